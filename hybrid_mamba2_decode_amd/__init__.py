@@ -1,0 +1,229 @@
+"""Python binding of libnhmamba (the Nemotron-H Mamba2 mixer block on MI355X / gfx950).
+
+Argument marshalling only: every step of the block runs in the library's HIP kernels.
+Functions carry the names of the C entry points in include/nhmamba.h and take torch
+tensors (device memory) or raw integer addresses; PyTorch supplies memory and streams.
+
+The library must be built first (``__graft_entry__.build()`` or
+``python hybrid_mamba2_decode_amd/build.py``); importing this package without it raises.
+There is no fallback path of any kind.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnhmamba.so")
+
+NH_OK = 0
+NH_ERR_INVALID_ARGUMENT = 1
+NH_ERR_UNSUPPORTED_SHAPE = 2
+NH_ERR_MISALIGNED = 3
+NH_ERR_WORKSPACE_TOO_SMALL = 4
+NH_ERR_HIP = 5
+NH_BF16 = 0
+NH_F32 = 1
+NH_MODE_STEP = 0
+NH_MODE_SEQ = 1
+
+# Entry points declared in include/nhmamba.h.
+EXPORTS = (
+    "nh_last_error", "nh_version", "nh_hybrid_pattern", "nh_w4_gemv", "nh_w4_gemm_workspace_bytes",
+    "nh_w4_gemm", "nh_rmsnorm", "nh_conv1d_step", "nh_conv1d_seq", "nh_ssm_step", "nh_ssd_chunk_scan",
+    "nh_rmsnorm_gated", "nh_block_workspace_bytes", "nh_mamba_block_step", "nh_mamba_block_seq",
+    "nh_mamba_stack",
+)
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
+                      "(hipcc --offload-arch=gfx950); there is no fallback implementation")
+lib = C.CDLL(LIB_PATH)
+
+
+class NhError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"nh status {status}: {message}")
+        self.status = status
+        self.message = message
+
+
+class nh_mamba_dims(C.Structure):
+    _fields_ = [("hidden", C.c_int), ("n_heads", C.c_int), ("head_dim", C.c_int),
+                ("d_state", C.c_int), ("n_groups", C.c_int), ("conv_k", C.c_int),
+                ("chunk", C.c_int), ("eps", C.c_float)]
+
+
+class nh_w4_matrix(C.Structure):
+    _fields_ = [("qweight", C.c_void_p), ("scales", C.c_void_p), ("biases", C.c_void_p),
+                ("n_out", C.c_int), ("k_in", C.c_int), ("group_size", C.c_int)]
+
+
+class nh_mamba_weights(C.Structure):
+    _fields_ = [("norm_w", C.c_void_p), ("in_proj", nh_w4_matrix), ("conv_w", C.c_void_p),
+                ("conv_b", C.c_void_p), ("dt_bias", C.c_void_p), ("A_log", C.c_void_p),
+                ("D", C.c_void_p), ("gnorm_w", C.c_void_p), ("out_proj", nh_w4_matrix)]
+
+
+class nh_mamba_state(C.Structure):
+    _fields_ = [("conv_state", C.c_void_p), ("ssm_state", C.c_void_p)]
+
+
+_vp, _i, _l, _sz = C.c_void_p, C.c_int, C.c_long, C.c_size_t
+_sigs = {
+    "nh_last_error": (C.c_char_p, []),
+    "nh_version": (C.c_char_p, []),
+    "nh_hybrid_pattern": (C.c_char_p, []),
+    "nh_w4_gemv": (_i, [_vp, _vp, _i, _vp, _i, _vp, _i, _vp]),
+    "nh_w4_gemm_workspace_bytes": (_sz, [_i, _i]),
+    "nh_w4_gemm": (_i, [_vp, _vp, _i, _vp, _i, _vp, _i, _vp, _sz, _vp]),
+    "nh_rmsnorm": (_i, [_vp, _i, _vp, _vp, _i, _i, C.c_float, _vp]),
+    "nh_conv1d_step": (_i, [_vp, _l, _vp, _vp, _vp, _vp, _i, _i, _i, _vp]),
+    "nh_conv1d_seq": (_i, [_vp, _l, _i, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp]),
+    "nh_ssm_step": (_i, [_vp, _vp, _vp, _l, _vp, _vp, _vp, _vp, _vp, _i, _i, _vp]),
+    "nh_ssd_chunk_scan": (_i, [_vp, _vp, _vp, _l, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _vp]),
+    "nh_rmsnorm_gated": (_i, [_vp, _vp, _l, _vp, _vp, _i, _i, _i, C.c_float, _vp]),
+    "nh_block_workspace_bytes": (_sz, [_vp, _i, _i, _i]),
+    "nh_mamba_block_step": (_i, [_vp, _vp, _vp, _vp, _i, _vp, _i, _i, _vp, _sz, _vp]),
+    "nh_mamba_block_seq": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _i, _i, _vp, _sz, _vp]),
+    "nh_mamba_stack": (_i, [_vp, _vp, _vp, _i, _i, _vp, _i, _i, _vp, _i, _vp, _sz, _vp]),
+}
+for _name, (_res, _args) in _sigs.items():
+    _f = getattr(lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+
+# ------------------------------------------------------------------ marshalling
+
+def _ptr(t):
+    """Device address of a torch tensor, an int address, a ctypes struct, or None."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if isinstance(t, C.Structure):
+        return C.addressof(t)
+    if isinstance(t, C.Array):
+        return C.addressof(t)
+    return t.data_ptr()
+
+
+def _stream(s):
+    if s is not None:
+        return s if isinstance(s, int) else s.cuda_stream
+    import torch
+    if torch.cuda.is_available():
+        return torch.cuda.current_stream().cuda_stream
+    return None
+
+
+def _check(rc: int):
+    if rc != NH_OK:
+        raise NhError(rc, lib.nh_last_error().decode())
+
+
+def dims(chunk: int = 128, eps: float = 1e-5, hidden: int = 4480, n_heads: int = 128,
+         head_dim: int = 80, d_state: int = 128, n_groups: int = 8, conv_k: int = 4) -> nh_mamba_dims:
+    return nh_mamba_dims(hidden, n_heads, head_dim, d_state, n_groups, conv_k, chunk, eps)
+
+
+def w4_matrix(qweight, scales, biases, n_out: int, k_in: int, group_size: int = 64) -> nh_w4_matrix:
+    m = nh_w4_matrix(_ptr(qweight), _ptr(scales), _ptr(biases), n_out, k_in, group_size)
+    m._keep = (qweight, scales, biases)
+    return m
+
+
+def mamba_weights(norm_w, in_proj: nh_w4_matrix, conv_w, conv_b, dt_bias, A_log, D, gnorm_w,
+                  out_proj: nh_w4_matrix) -> nh_mamba_weights:
+    w = nh_mamba_weights(_ptr(norm_w), in_proj, _ptr(conv_w), _ptr(conv_b), _ptr(dt_bias),
+                         _ptr(A_log), _ptr(D), _ptr(gnorm_w), out_proj)
+    w._keep = (norm_w, in_proj, conv_w, conv_b, dt_bias, A_log, D, gnorm_w, out_proj)
+    return w
+
+
+def mamba_state(conv_state, ssm_state) -> nh_mamba_state:
+    s = nh_mamba_state(_ptr(conv_state), _ptr(ssm_state))
+    s._keep = (conv_state, ssm_state)
+    return s
+
+
+def version() -> str:
+    return lib.nh_version().decode()
+
+
+def hybrid_pattern() -> str:
+    return lib.nh_hybrid_pattern().decode()
+
+
+# ------------------------------------------------------------------ entry points
+
+def nh_w4_gemv(W, x, batch, residual, res_dtype, y, y_dtype, stream=None):
+    _check(lib.nh_w4_gemv(C.byref(W), _ptr(x), batch, _ptr(residual), res_dtype, _ptr(y), y_dtype,
+                          _stream(stream)))
+
+
+def nh_w4_gemm_workspace_bytes(M, k_in) -> int:
+    return lib.nh_w4_gemm_workspace_bytes(M, k_in)
+
+
+def nh_w4_gemm(W, X, M, residual, res_dtype, Y, y_dtype, ws, ws_bytes, stream=None):
+    _check(lib.nh_w4_gemm(C.byref(W), _ptr(X), M, _ptr(residual), res_dtype, _ptr(Y), y_dtype,
+                          _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def nh_rmsnorm(x, x_dtype, w, u, rows, d, eps, stream=None):
+    _check(lib.nh_rmsnorm(_ptr(x), x_dtype, _ptr(w), _ptr(u), rows, d, eps, _stream(stream)))
+
+
+def nh_conv1d_step(xbc, ld, conv_state, w, b, out, batch, channels, k=4, stream=None):
+    _check(lib.nh_conv1d_step(_ptr(xbc), ld, _ptr(conv_state), _ptr(w), _ptr(b), _ptr(out), batch,
+                              channels, k, _stream(stream)))
+
+
+def nh_conv1d_seq(xbc, ld, T, state_in, state_out, w, b, out, batch, channels, k=4, stream=None):
+    _check(lib.nh_conv1d_seq(_ptr(xbc), ld, T, _ptr(state_in), _ptr(state_out), _ptr(w), _ptr(b),
+                             _ptr(out), batch, channels, k, _stream(stream)))
+
+
+def nh_ssm_step(d, xc, dt_raw, ld_dt, dt_bias, A_log, D, ssm_state, y, y_dtype, batch, stream=None):
+    _check(lib.nh_ssm_step(C.byref(d), _ptr(xc), _ptr(dt_raw), ld_dt, _ptr(dt_bias), _ptr(A_log),
+                           _ptr(D), _ptr(ssm_state), _ptr(y), y_dtype, batch, _stream(stream)))
+
+
+def nh_ssd_chunk_scan(d, xc, dt_raw, ld_dt, T, dt_bias, A_log, D, h0, h_final, y, y_dtype, batch,
+                      stream=None):
+    _check(lib.nh_ssd_chunk_scan(C.byref(d), _ptr(xc), _ptr(dt_raw), ld_dt, T, _ptr(dt_bias),
+                                 _ptr(A_log), _ptr(D), _ptr(h0), _ptr(h_final), _ptr(y), y_dtype,
+                                 batch, _stream(stream)))
+
+
+def nh_rmsnorm_gated(y, z, ld_z, w, out, rows, d, group, eps, stream=None):
+    _check(lib.nh_rmsnorm_gated(_ptr(y), _ptr(z), ld_z, _ptr(w), _ptr(out), rows, d, group, eps,
+                                _stream(stream)))
+
+
+def nh_block_workspace_bytes(d, batch, T, mode) -> int:
+    return lib.nh_block_workspace_bytes(C.byref(d), batch, T, mode)
+
+
+def nh_mamba_block_step(d, w, state, x, x_dtype, out, out_dtype, batch, ws, ws_bytes, stream=None):
+    _check(lib.nh_mamba_block_step(C.byref(d), C.byref(w), C.byref(state), _ptr(x), x_dtype,
+                                   _ptr(out), out_dtype, batch, _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def nh_mamba_block_seq(d, w, init, final_state, x, x_dtype, T, out, out_dtype, batch, ws, ws_bytes,
+                       stream=None):
+    _check(lib.nh_mamba_block_seq(C.byref(d), C.byref(w), None if init is None else C.byref(init),
+                                  None if final_state is None else C.byref(final_state), _ptr(x),
+                                  x_dtype, T, _ptr(out), out_dtype, batch, _ptr(ws), ws_bytes,
+                                  _stream(stream)))
+
+
+def nh_mamba_stack(d, weights, states, n_layers, mode, x, x_dtype, T, outs, batch, ws, ws_bytes,
+                   stream=None):
+    """weights / states: sequences of nh_mamba_weights / nh_mamba_state (or None for states)."""
+    warr = (nh_mamba_weights * n_layers)(*weights)
+    sarr = None if states is None else (nh_mamba_state * n_layers)(*states)
+    _check(lib.nh_mamba_stack(C.byref(d), warr, sarr, n_layers, mode, _ptr(x), x_dtype, T, _ptr(outs),
+                              batch, _ptr(ws), ws_bytes, _stream(stream)))

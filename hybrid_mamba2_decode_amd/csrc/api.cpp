@@ -1,0 +1,507 @@
+// api.cpp -- the C ABI of libnhmamba: argument validation, workspace layout, launches.
+//
+// Every entry point validates all of its arguments before it enqueues anything, so a call
+// that returns an error has no side effect.  Nothing here allocates device memory or
+// synchronises the host.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/nhmamba.h"
+#include "nh_device.hpp"
+#include "nh_kernels.hpp"
+
+using namespace nh;
+
+namespace {
+
+thread_local std::string g_err;
+
+nh_status fail(nh_status s, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+nh_status ok()
+{
+    g_err.clear();
+    return NH_OK;
+}
+
+nh_status hip_status(hipError_t e, const char *what)
+{
+    if (e != hipSuccess) return fail(NH_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+#define NH_TRY(expr)                         \
+    do {                                     \
+        nh_status s__ = (expr);              \
+        if (s__ != NH_OK) return s__;        \
+    } while (0)
+
+#define NH_HIP(expr, what)                                          \
+    do {                                                            \
+        hipError_t e__ = (expr);                                    \
+        if (e__ != hipSuccess) return hip_status(e__, what);        \
+    } while (0)
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+nh_status need_ptr(const void *p, const char *name)
+{
+    if (!p) return fail(NH_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+    if (!aligned16(p)) return fail(NH_ERR_MISALIGNED, "%s is not 16-byte aligned", name);
+    return NH_OK;
+}
+
+nh_status opt_ptr(const void *p, const char *name)
+{
+    if (p && !aligned16(p)) return fail(NH_ERR_MISALIGNED, "%s is not 16-byte aligned", name);
+    return NH_OK;
+}
+
+nh_status need_dtype(int t, const char *name)
+{
+    if (t != NH_BF16 && t != NH_F32) return fail(NH_ERR_INVALID_ARGUMENT, "%s: unknown dtype %d", name, t);
+    return NH_OK;
+}
+
+nh_status check_w4(const nh_w4_matrix *W, const char *name)
+{
+    if (!W) return fail(NH_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+    NH_TRY(need_ptr(W->qweight, "qweight"));
+    NH_TRY(need_ptr(W->scales, "scales"));
+    NH_TRY(need_ptr(W->biases, "biases"));
+    if (W->group_size != 64)
+        return fail(NH_ERR_UNSUPPORTED_SHAPE, "%s: group_size %d (only 64)", name, W->group_size);
+    if (W->n_out < 1 || W->k_in < 64 || W->k_in % 64 != 0 || W->k_in > 16384)
+        return fail(NH_ERR_UNSUPPORTED_SHAPE, "%s: n_out %d, k_in %d (need n_out >= 1, k_in %% 64 == 0, "
+                    "64 <= k_in <= 16384)", name, W->n_out, W->k_in);
+    return NH_OK;
+}
+
+W4 view(const nh_w4_matrix *W) { return W4{W->qweight, W->scales, W->biases, W->n_out, W->k_in}; }
+
+nh_status check_dims(const nh_mamba_dims *d, bool need_chunk)
+{
+    if (!d) return fail(NH_ERR_INVALID_ARGUMENT, "dims is NULL");
+    if (d->hidden != HIDDEN || d->n_heads != NHEADS || d->head_dim != HDIM || d->d_state != DSTATE ||
+        d->n_groups != NGROUPS || d->conv_k != CONVK)
+        return fail(NH_ERR_UNSUPPORTED_SHAPE,
+                    "dims (%d,%d,%d,%d,%d,%d) differ from the supported Nemotron-H mixer "
+                    "(4480,128,80,128,8,4)", d->hidden, d->n_heads, d->head_dim, d->d_state,
+                    d->n_groups, d->conv_k);
+    if (!(d->eps > 0.f) || !std::isfinite(d->eps))
+        return fail(NH_ERR_INVALID_ARGUMENT, "eps must be positive and finite");
+    if (need_chunk && (d->chunk < 1 || d->chunk > QMAX))
+        return fail(NH_ERR_UNSUPPORTED_SHAPE, "chunk %d outside 1..%d", d->chunk, QMAX);
+    return NH_OK;
+}
+
+nh_status check_weights(const nh_mamba_weights *w)
+{
+    if (!w) return fail(NH_ERR_INVALID_ARGUMENT, "weights is NULL");
+    NH_TRY(need_ptr(w->norm_w, "norm_w"));
+    NH_TRY(check_w4(&w->in_proj, "in_proj"));
+    NH_TRY(need_ptr(w->conv_w, "conv_w"));
+    NH_TRY(need_ptr(w->conv_b, "conv_b"));
+    NH_TRY(need_ptr(w->dt_bias, "dt_bias"));
+    NH_TRY(need_ptr(w->A_log, "A_log"));
+    NH_TRY(need_ptr(w->D, "D"));
+    NH_TRY(need_ptr(w->gnorm_w, "gnorm_w"));
+    NH_TRY(check_w4(&w->out_proj, "out_proj"));
+    if (w->in_proj.n_out != NIN || w->in_proj.k_in != HIDDEN)
+        return fail(NH_ERR_UNSUPPORTED_SHAPE, "in_proj is %dx%d, expected %dx%d", w->in_proj.n_out,
+                    w->in_proj.k_in, NIN, HIDDEN);
+    if (w->out_proj.n_out != HIDDEN || w->out_proj.k_in != DINNER)
+        return fail(NH_ERR_UNSUPPORTED_SHAPE, "out_proj is %dx%d, expected %dx%d", w->out_proj.n_out,
+                    w->out_proj.k_in, HIDDEN, DINNER);
+    return NH_OK;
+}
+
+// ---------------------------------------------------------------- workspace layout
+struct Carve {
+    char *base;
+    size_t off = 0;
+    template <class T>
+    T *take(size_t count)
+    {
+        off = (off + 255) & ~size_t(255);
+        T *p = base ? reinterpret_cast<T *>(base + off) : nullptr;
+        off += count * sizeof(T);
+        return p;
+    }
+};
+
+struct StepWs {
+    uint16_t *z, *xc, *dtr, *y, *o;
+    float *part;
+    uint32_t *cnt;
+};
+
+StepWs carve_step(void *ws, int B, size_t *bytes)
+{
+    Carve c{reinterpret_cast<char *>(ws)};
+    StepWs s;
+    s.z = c.take<uint16_t>((size_t)B * DINNER);
+    s.xc = c.take<uint16_t>((size_t)B * CONVDIM);
+    s.dtr = c.take<uint16_t>((size_t)B * NHEADS);
+    s.y = c.take<uint16_t>((size_t)B * DINNER);
+    s.o = c.take<uint16_t>((size_t)B * DINNER);
+    s.part = c.take<float>((size_t)B * NHEADS * 2);
+    s.cnt = c.take<uint32_t>((size_t)B * NGROUPS);
+    *bytes = c.off;
+    return s;
+}
+
+struct SeqWs {
+    uint16_t *u, *zx, *xc, *y, *o, *cs;
+    float *su_u, *su_o;
+};
+
+SeqWs carve_seq(void *ws, int B, int T, size_t *bytes)
+{
+    const size_t M = (size_t)B * T;
+    Carve c{reinterpret_cast<char *>(ws)};
+    SeqWs s;
+    s.u = c.take<uint16_t>(M * HIDDEN);
+    s.su_u = c.take<float>(M * (HIDDEN / 64));
+    s.zx = c.take<uint16_t>(M * NIN);
+    s.xc = c.take<uint16_t>(M * CONVDIM);
+    s.y = c.take<uint16_t>(M * DINNER);
+    s.o = c.take<uint16_t>(M * DINNER);
+    s.su_o = c.take<float>(M * (DINNER / 64));
+    s.cs = c.take<uint16_t>((size_t)B * (CONVK - 1) * CONVDIM);
+    *bytes = c.off;
+    return s;
+}
+
+size_t step_bytes(int B)
+{
+    size_t n;
+    carve_step(nullptr, B, &n);
+    return n;
+}
+
+size_t seq_bytes(int B, int T)
+{
+    size_t n;
+    carve_seq(nullptr, B, T, &n);
+    return n;
+}
+
+hipStream_t S(void *stream) { return reinterpret_cast<hipStream_t>(stream); }
+
+// The block bodies, called after validation.
+nh_status block_step(const nh_mamba_dims *d, const nh_mamba_weights *w, nh_mamba_state *st,
+                     const void *x, int x_t, void *out, int out_t, int B, void *ws, hipStream_t s)
+{
+    size_t nb;
+    StepWs k = carve_step(ws, B, &nb);
+    NH_HIP(launch_inproj_step(view(&w->in_proj), x, x_t, w->norm_w, d->eps, B, k.z, k.xc, k.dtr,
+                              st->conv_state, w->conv_w, w->conv_b, k.cnt, B * NGROUPS, s),
+           "in_proj step");
+    NH_HIP(launch_ssm_step_gnorm(k.xc, k.dtr, NHEADS, w->dt_bias, w->A_log, w->D, st->ssm_state,
+                                 k.y, k.z, w->gnorm_w, d->eps, k.part, k.cnt, k.o, B, s),
+           "ssm step");
+    NH_HIP(launch_gemv(view(&w->out_proj), k.o, B, x, x_t, out, out_t, s), "out_proj step");
+    return ok();
+}
+
+nh_status block_seq(const nh_mamba_dims *d, const nh_mamba_weights *w, const nh_mamba_state *init,
+                    nh_mamba_state *fin, const void *x, int x_t, int T, void *out, int out_t, int B,
+                    void *ws, hipStream_t s)
+{
+    size_t nb;
+    SeqWs k = carve_seq(ws, B, T, &nb);
+    const int M = B * T;
+    NH_HIP(launch_rmsnorm(x, x_t, w->norm_w, k.u, 1, k.su_u, M, HIDDEN, d->eps, s), "pre-norm");
+    NH_HIP(launch_w4_gemm(view(&w->in_proj), k.u, k.su_u, M, nullptr, BF16, k.zx, BF16, s), "in_proj");
+    const uint16_t *cs_in = init ? init->conv_state : nullptr;
+    uint16_t *cs_out = fin ? fin->conv_state : nullptr;
+    if (cs_in && cs_out == cs_in) {
+        NH_HIP(hipMemcpyAsync(k.cs, cs_in, (size_t)B * (CONVK - 1) * CONVDIM * 2, hipMemcpyDeviceToDevice, s),
+               "conv state copy");
+        cs_in = k.cs;
+    }
+    NH_HIP(launch_conv_seq(k.zx + DINNER, NIN, T, cs_in, cs_out, w->conv_w, w->conv_b, k.xc, B, CONVDIM, s),
+           "conv");
+    NH_HIP(launch_ssd_scan(k.xc, k.zx + DINNER + CONVDIM, NIN, T, d->chunk, w->dt_bias, w->A_log, w->D,
+                           init ? init->ssm_state : nullptr, fin ? fin->ssm_state : nullptr, k.y, BF16, B, s),
+           "scan");
+    NH_HIP(launch_rmsnorm_gated(k.y, k.zx, NIN, w->gnorm_w, k.o, 1, k.su_o, M, DINNER, GNORM, d->eps, s),
+           "gated norm");
+    NH_HIP(launch_w4_gemm(view(&w->out_proj), k.o, k.su_o, M, x, x_t, out, out_t, s), "out_proj");
+    return ok();
+}
+
+nh_status check_state(const nh_mamba_state *st, const char *name, bool required)
+{
+    if (!st) {
+        if (required) return fail(NH_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+        return NH_OK;
+    }
+    NH_TRY(need_ptr(st->conv_state, "conv_state"));
+    NH_TRY(need_ptr(st->ssm_state, "ssm_state"));
+    return NH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *nh_last_error(void) { return g_err.c_str(); }
+
+const char *nh_version(void) { return "libnhmamba 0.1 (gfx950)"; }
+
+const char *nh_hybrid_pattern(void)
+{
+    // text_config.hybrid_override_pattern (issue page, section "config.json").
+    return "M-M-M-MM-M-M-M*-M-M-M*-M-M-M-M*-M-M-M-M*-M-MM-M-M-M-M-M-";
+}
+
+nh_status nh_w4_gemv(const nh_w4_matrix *W, const uint16_t *x, int batch, const void *residual,
+                     nh_dtype res_dtype, void *y, nh_dtype y_dtype, void *stream)
+{
+    NH_TRY(check_w4(W, "W"));
+    NH_TRY(need_ptr(x, "x"));
+    NH_TRY(need_ptr(y, "y"));
+    NH_TRY(opt_ptr(residual, "residual"));
+    NH_TRY(need_dtype(y_dtype, "y_dtype"));
+    if (residual) NH_TRY(need_dtype(res_dtype, "res_dtype"));
+    if (batch < 1 || batch > 4) return fail(NH_ERR_UNSUPPORTED_SHAPE, "batch %d outside 1..4", batch);
+    NH_HIP(launch_gemv(view(W), x, batch, residual, res_dtype, y, y_dtype, S(stream)), "gemv");
+    return ok();
+}
+
+size_t nh_w4_gemm_workspace_bytes(int M, int k_in)
+{
+    if (M < 1 || k_in < 64 || k_in % 64) return 0;
+    Carve c{nullptr};
+    c.take<uint16_t>((size_t)M * k_in);
+    c.take<float>((size_t)M * (k_in / 64));
+    return c.off;
+}
+
+nh_status nh_w4_gemm(const nh_w4_matrix *W, const uint16_t *X, int M, const void *residual,
+                     nh_dtype res_dtype, void *Y, nh_dtype y_dtype, void *ws, size_t ws_bytes, void *stream)
+{
+    NH_TRY(check_w4(W, "W"));
+    NH_TRY(need_ptr(X, "X"));
+    NH_TRY(need_ptr(Y, "Y"));
+    NH_TRY(opt_ptr(residual, "residual"));
+    NH_TRY(need_dtype(y_dtype, "y_dtype"));
+    if (residual) NH_TRY(need_dtype(res_dtype, "res_dtype"));
+    if (M < 1) return fail(NH_ERR_UNSUPPORTED_SHAPE, "M %d < 1", M);
+    NH_TRY(need_ptr(ws, "ws"));
+    const size_t need = nh_w4_gemm_workspace_bytes(M, W->k_in);
+    if (ws_bytes < need) return fail(NH_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
+    Carve c{reinterpret_cast<char *>(ws)};
+    uint16_t *xh = c.take<uint16_t>((size_t)M * W->k_in);
+    float *su = c.take<float>((size_t)M * (W->k_in / 64));
+    NH_HIP(launch_to_f16(X, xh, su, M, W->k_in, S(stream)), "gemm staging");
+    NH_HIP(launch_w4_gemm(view(W), xh, su, M, residual, res_dtype, Y, y_dtype, S(stream)), "gemm");
+    return ok();
+}
+
+nh_status nh_rmsnorm(const void *x, nh_dtype x_dtype, const uint16_t *w, uint16_t *u, int rows, int d,
+                     float eps, void *stream)
+{
+    NH_TRY(need_ptr(x, "x"));
+    NH_TRY(need_ptr(w, "w"));
+    NH_TRY(need_ptr(u, "u"));
+    NH_TRY(need_dtype(x_dtype, "x_dtype"));
+    if (rows < 1 || d < 8 || d % 8 || d > 8192)
+        return fail(NH_ERR_UNSUPPORTED_SHAPE, "rows %d, d %d (need rows >= 1, d %% 8 == 0, d <= 8192)", rows, d);
+    if (!(eps > 0.f) || !std::isfinite(eps)) return fail(NH_ERR_INVALID_ARGUMENT, "eps must be positive");
+    NH_HIP(launch_rmsnorm(x, x_dtype, w, u, 0, nullptr, rows, d, eps, S(stream)), "rmsnorm");
+    return ok();
+}
+
+nh_status nh_conv1d_step(const uint16_t *xbc, long ld, uint16_t *conv_state, const uint16_t *w,
+                         const uint16_t *b, uint16_t *out, int batch, int channels, int k, void *stream)
+{
+    NH_TRY(need_ptr(xbc, "xbc"));
+    NH_TRY(need_ptr(conv_state, "conv_state"));
+    NH_TRY(need_ptr(w, "w"));
+    NH_TRY(need_ptr(b, "b"));
+    NH_TRY(need_ptr(out, "out"));
+    if (k != CONVK) return fail(NH_ERR_UNSUPPORTED_SHAPE, "conv kernel %d (only 4)", k);
+    if (batch < 1 || channels < 1 || ld < channels)
+        return fail(NH_ERR_UNSUPPORTED_SHAPE, "batch %d, channels %d, ld %ld", batch, channels, ld);
+    NH_HIP(launch_conv_step(xbc, ld, conv_state, w, b, out, batch, channels, S(stream)), "conv step");
+    return ok();
+}
+
+nh_status nh_conv1d_seq(const uint16_t *xbc, long ld, int T, const uint16_t *state_in, uint16_t *state_out,
+                        const uint16_t *w, const uint16_t *b, uint16_t *out, int batch, int channels, int k,
+                        void *stream)
+{
+    NH_TRY(need_ptr(xbc, "xbc"));
+    NH_TRY(opt_ptr(state_in, "state_in"));
+    NH_TRY(opt_ptr(state_out, "state_out"));
+    NH_TRY(need_ptr(w, "w"));
+    NH_TRY(need_ptr(b, "b"));
+    NH_TRY(need_ptr(out, "out"));
+    if (k != CONVK) return fail(NH_ERR_UNSUPPORTED_SHAPE, "conv kernel %d (only 4)", k);
+    if (batch < 1 || channels < 1 || ld < channels || T < 1)
+        return fail(NH_ERR_UNSUPPORTED_SHAPE, "batch %d, channels %d, ld %ld, T %d", batch, channels, ld, T);
+    if (state_in && state_in == state_out)
+        return fail(NH_ERR_INVALID_ARGUMENT, "state_out may not alias state_in");
+    NH_HIP(launch_conv_seq(xbc, ld, T, state_in, state_out, w, b, out, batch, channels, S(stream)), "conv seq");
+    return ok();
+}
+
+nh_status nh_ssm_step(const nh_mamba_dims *d, const uint16_t *xc, const uint16_t *dt_raw, long ld_dt,
+                      const float *dt_bias, const float *A_log, const float *D, float *ssm_state, void *y,
+                      nh_dtype y_dtype, int batch, void *stream)
+{
+    NH_TRY(check_dims(d, false));
+    NH_TRY(need_ptr(xc, "xc"));
+    if (!dt_raw) return fail(NH_ERR_INVALID_ARGUMENT, "dt_raw is NULL");
+    NH_TRY(need_ptr(dt_bias, "dt_bias"));
+    NH_TRY(need_ptr(A_log, "A_log"));
+    NH_TRY(need_ptr(D, "D"));
+    NH_TRY(need_ptr(ssm_state, "ssm_state"));
+    NH_TRY(need_ptr(y, "y"));
+    NH_TRY(need_dtype(y_dtype, "y_dtype"));
+    if (batch < 1 || batch > 64) return fail(NH_ERR_UNSUPPORTED_SHAPE, "batch %d outside 1..64", batch);
+    if (batch > 1 && ld_dt < NHEADS) return fail(NH_ERR_UNSUPPORTED_SHAPE, "ld_dt %ld < n_heads", ld_dt);
+    NH_HIP(launch_ssm_step(xc, dt_raw, ld_dt, dt_bias, A_log, D, ssm_state, y, y_dtype, batch, S(stream)),
+           "ssm step");
+    return ok();
+}
+
+nh_status nh_ssd_chunk_scan(const nh_mamba_dims *d, const uint16_t *xc, const uint16_t *dt_raw, long ld_dt,
+                            int T, const float *dt_bias, const float *A_log, const float *D, const float *h0,
+                            float *h_final, void *y, nh_dtype y_dtype, int batch, void *stream)
+{
+    NH_TRY(check_dims(d, true));
+    NH_TRY(need_ptr(xc, "xc"));
+    if (!dt_raw) return fail(NH_ERR_INVALID_ARGUMENT, "dt_raw is NULL");
+    NH_TRY(need_ptr(dt_bias, "dt_bias"));
+    NH_TRY(need_ptr(A_log, "A_log"));
+    NH_TRY(need_ptr(D, "D"));
+    NH_TRY(opt_ptr(h0, "h0"));
+    NH_TRY(opt_ptr(h_final, "h_final"));
+    NH_TRY(need_ptr(y, "y"));
+    NH_TRY(need_dtype(y_dtype, "y_dtype"));
+    if (batch < 1 || T < 1) return fail(NH_ERR_UNSUPPORTED_SHAPE, "batch %d, T %d", batch, T);
+    if (ld_dt < 1 || (T * (long)batch > 1 && ld_dt < NHEADS))
+        return fail(NH_ERR_UNSUPPORTED_SHAPE, "ld_dt %ld < n_heads", ld_dt);
+    NH_HIP(launch_ssd_scan(xc, dt_raw, ld_dt, T, d->chunk, dt_bias, A_log, D, h0, h_final, y, y_dtype, batch,
+                           S(stream)),
+           "ssd scan");
+    return ok();
+}
+
+nh_status nh_rmsnorm_gated(const uint16_t *y, const uint16_t *z, long ld_z, const uint16_t *w, uint16_t *out,
+                           int rows, int d, int group, float eps, void *stream)
+{
+    NH_TRY(need_ptr(y, "y"));
+    NH_TRY(need_ptr(z, "z"));
+    NH_TRY(need_ptr(w, "w"));
+    NH_TRY(need_ptr(out, "out"));
+    if (rows < 1 || group < 8 || group % 8 || d % group || group > 8192 || ld_z < d || ld_z % 8)
+        return fail(NH_ERR_UNSUPPORTED_SHAPE, "rows %d, d %d, group %d, ld_z %ld", rows, d, group, ld_z);
+    if (!(eps > 0.f) || !std::isfinite(eps)) return fail(NH_ERR_INVALID_ARGUMENT, "eps must be positive");
+    NH_HIP(launch_rmsnorm_gated(y, z, ld_z, w, out, 0, nullptr, rows, d, group, eps, S(stream)), "gated norm");
+    return ok();
+}
+
+size_t nh_block_workspace_bytes(const nh_mamba_dims *d, int batch, int T, int mode)
+{
+    if (!d || batch < 1) return 0;
+    if (mode == NH_MODE_STEP) return batch <= 4 ? step_bytes(batch) : 0;
+    if (mode == NH_MODE_SEQ) return T >= 1 ? seq_bytes(batch, T) : 0;
+    return 0;
+}
+
+nh_status nh_mamba_block_step(const nh_mamba_dims *d, const nh_mamba_weights *w, nh_mamba_state *state,
+                              const void *x, nh_dtype x_dtype, void *out, nh_dtype out_dtype, int batch,
+                              void *ws, size_t ws_bytes, void *stream)
+{
+    NH_TRY(check_dims(d, false));
+    NH_TRY(check_weights(w));
+    NH_TRY(check_state(state, "state", true));
+    NH_TRY(need_ptr(x, "x"));
+    NH_TRY(need_ptr(out, "out"));
+    NH_TRY(need_dtype(x_dtype, "x_dtype"));
+    NH_TRY(need_dtype(out_dtype, "out_dtype"));
+    if (batch < 1 || batch > 4) return fail(NH_ERR_UNSUPPORTED_SHAPE, "batch %d outside 1..4", batch);
+    if (x == out) return fail(NH_ERR_INVALID_ARGUMENT, "out may not alias x");
+    NH_TRY(need_ptr(ws, "ws"));
+    const size_t need = step_bytes(batch);
+    if (ws_bytes < need) return fail(NH_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
+    return block_step(d, w, state, x, x_dtype, out, out_dtype, batch, ws, S(stream));
+}
+
+nh_status nh_mamba_block_seq(const nh_mamba_dims *d, const nh_mamba_weights *w, const nh_mamba_state *init,
+                             nh_mamba_state *final_state, const void *x, nh_dtype x_dtype, int T, void *out,
+                             nh_dtype out_dtype, int batch, void *ws, size_t ws_bytes, void *stream)
+{
+    NH_TRY(check_dims(d, true));
+    NH_TRY(check_weights(w));
+    NH_TRY(check_state(init, "init", false));
+    NH_TRY(check_state(final_state, "final_state", false));
+    NH_TRY(need_ptr(x, "x"));
+    NH_TRY(need_ptr(out, "out"));
+    NH_TRY(need_dtype(x_dtype, "x_dtype"));
+    NH_TRY(need_dtype(out_dtype, "out_dtype"));
+    if (batch < 1 || T < 1) return fail(NH_ERR_UNSUPPORTED_SHAPE, "batch %d, T %d", batch, T);
+    if ((long)batch * T > (1L << 24)) return fail(NH_ERR_UNSUPPORTED_SHAPE, "batch*T too large");
+    if (x == out) return fail(NH_ERR_INVALID_ARGUMENT, "out may not alias x");
+    NH_TRY(need_ptr(ws, "ws"));
+    const size_t need = seq_bytes(batch, T);
+    if (ws_bytes < need) return fail(NH_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
+    return block_seq(d, w, init, final_state, x, x_dtype, T, out, out_dtype, batch, ws, S(stream));
+}
+
+nh_status nh_mamba_stack(const nh_mamba_dims *d, const nh_mamba_weights *weights, nh_mamba_state *states,
+                         int n_layers, int mode, const void *x, nh_dtype x_dtype, int T, float *outs, int batch,
+                         void *ws, size_t ws_bytes, void *stream)
+{
+    if (mode != NH_MODE_STEP && mode != NH_MODE_SEQ) return fail(NH_ERR_INVALID_ARGUMENT, "mode %d", mode);
+    NH_TRY(check_dims(d, mode == NH_MODE_SEQ));
+    if (!weights || n_layers < 1) return fail(NH_ERR_INVALID_ARGUMENT, "weights NULL or n_layers %d", n_layers);
+    if (mode == NH_MODE_STEP && !states) return fail(NH_ERR_INVALID_ARGUMENT, "states is NULL");
+    for (int i = 0; i < n_layers; ++i) {
+        NH_TRY(check_weights(&weights[i]));
+        if (states) NH_TRY(check_state(&states[i], "state", true));
+    }
+    NH_TRY(need_ptr(x, "x"));
+    NH_TRY(need_ptr(outs, "outs"));
+    NH_TRY(need_dtype(x_dtype, "x_dtype"));
+    if (batch < 1 || T < 1) return fail(NH_ERR_UNSUPPORTED_SHAPE, "batch %d, T %d", batch, T);
+    if (mode == NH_MODE_STEP && (T != 1 || batch > 4))
+        return fail(NH_ERR_UNSUPPORTED_SHAPE, "step mode needs T == 1 and batch <= 4");
+    if (x == (const void *)outs) return fail(NH_ERR_INVALID_ARGUMENT, "outs may not alias x");
+    NH_TRY(need_ptr(ws, "ws"));
+    const size_t need = mode == NH_MODE_STEP ? step_bytes(batch) : seq_bytes(batch, T);
+    if (ws_bytes < need) return fail(NH_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
+    const size_t per = (size_t)batch * T * HIDDEN;
+    for (int i = 0; i < n_layers; ++i) {
+        const void *xi = i == 0 ? x : (const void *)(outs + (i - 1) * per);
+        const int xt = i == 0 ? x_dtype : NH_F32;
+        nh_status s;
+        if (mode == NH_MODE_STEP)
+            s = block_step(d, &weights[i], &states[i], xi, xt, outs + i * per, NH_F32, batch, ws, S(stream));
+        else
+            s = block_seq(d, &weights[i], states ? &states[i] : nullptr, states ? &states[i] : nullptr, xi, xt, T,
+                          outs + i * per, NH_F32, batch, ws, S(stream));
+        if (s != NH_OK) return s;
+    }
+    return ok();
+}
+
+}  // extern "C"

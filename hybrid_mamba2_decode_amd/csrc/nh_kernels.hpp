@@ -1,0 +1,66 @@
+// nh_kernels.hpp -- host-side launchers of the libnhmamba kernels (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace nh {
+
+enum DT { BF16 = 0, F32 = 1 };
+
+struct W4 {
+    const uint32_t *q;
+    const uint16_t *s;
+    const uint16_t *b;
+    int n, k;
+};
+
+// ---- step mode (step.hip)
+hipError_t launch_gemv(const W4 &W, const uint16_t *x, int batch, const void *res, int res_t,
+                       void *y, int y_t, hipStream_t st);
+// Fused: RMSNorm(x) -> in_proj GEMV -> split; xBC rows go through the conv step (state
+// updated in place), z and dt_raw rows are stored.  Also zeroes `nzero` words at zero_ptr.
+hipError_t launch_inproj_step(const W4 &W, const void *x, int x_t, const uint16_t *norm_w,
+                              float eps, int batch, uint16_t *z, uint16_t *xc, uint16_t *dtr,
+                              uint16_t *conv_state, const uint16_t *conv_w,
+                              const uint16_t *conv_b, uint32_t *zero_ptr, int nzero,
+                              hipStream_t st);
+hipError_t launch_ssm_step(const uint16_t *xc, const uint16_t *dtr, long ld_dt,
+                           const float *dt_bias, const float *A_log, const float *D, float *S,
+                           void *y, int y_t, int batch, hipStream_t st);
+// SSM step fused with the gated RMSNorm: y (bf16) goes to y_ws, the normalised output to o.
+hipError_t launch_ssm_step_gnorm(const uint16_t *xc, const uint16_t *dtr, long ld_dt,
+                                 const float *dt_bias, const float *A_log, const float *D,
+                                 float *S, uint16_t *y_ws, const uint16_t *z, const uint16_t *gw,
+                                 float eps, float *part, uint32_t *cnt, uint16_t *o, int batch,
+                                 hipStream_t st);
+hipError_t launch_conv_step(const uint16_t *xbc, long ld, uint16_t *state, const uint16_t *w,
+                            const uint16_t *b, uint16_t *out, int batch, int channels,
+                            hipStream_t st);
+
+// ---- row kernels (rows.hip)
+// u = bf16(RMSNorm(x) * w); out_kind 0: bf16 bits, 1: fp16 bits of the same value (the
+// matrix-core operand format); su (nullable): per-64-group sums of u, [rows][d/64].
+hipError_t launch_rmsnorm(const void *x, int x_t, const uint16_t *w, uint16_t *u, int out_kind,
+                          float *su, int rows, int d, float eps, hipStream_t st);
+hipError_t launch_rmsnorm_gated(const uint16_t *y, const uint16_t *z, long ld_z,
+                                const uint16_t *w, uint16_t *out, int out_kind, float *su,
+                                int rows, int d, int group, float eps, hipStream_t st);
+hipError_t launch_conv_seq(const uint16_t *xbc, long ld, int T, const uint16_t *state_in,
+                           uint16_t *state_out, const uint16_t *w, const uint16_t *b,
+                           uint16_t *out, int batch, int channels, hipStream_t st);
+// bf16 [M][K] -> fp16 bits [M][K] plus per-64-group sums [M][K/64].
+hipError_t launch_to_f16(const uint16_t *x, uint16_t *xh, float *su, int M, int K,
+                         hipStream_t st);
+
+// ---- seq mode (gemm.hip, scan.hip)
+// Y = Xh W^T (+ res); Xh holds fp16 bits, su the per-group row sums of Xh.
+hipError_t launch_w4_gemm(const W4 &W, const uint16_t *Xh, const float *su, int M,
+                          const void *res, int res_t, void *Y, int y_t, hipStream_t st);
+hipError_t launch_ssd_scan(const uint16_t *xc, const uint16_t *dtr, long ld_dt, int T, int Q,
+                           const float *dt_bias, const float *A_log, const float *D,
+                           const float *h0, float *hT, void *y, int y_t, int batch,
+                           hipStream_t st);
+
+}  // namespace nh

@@ -1,0 +1,276 @@
+// rows.hip -- row-wise kernels of the sequence (full-history) path on gfx950:
+// RMSNorm, gated RMSNorm, the causal conv over T positions and the bf16 -> fp16 staging
+// of matrix-core operands.  All are HBM-streaming kernels with 128-bit accesses.
+#include "nh_device.hpp"
+#include "nh_kernels.hpp"
+
+namespace nh {
+
+// Sum over the 8 lanes that hold one 64-element quantisation group (8 values each).
+__device__ __forceinline__ float group8_sum(float v)
+{
+    v += __shfl_xor(v, 1, 64);
+    v += __shfl_xor(v, 2, 64);
+    v += __shfl_xor(v, 4, 64);
+    return v;
+}
+
+__device__ __forceinline__ float block_sum256(float v, float *red)
+{
+    v = wave_sum(v);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    const float t = (red[0] + red[1]) + (red[2] + red[3]);
+    __syncthreads();
+    return t;
+}
+
+// Store eight values that are already bf16-exact, as bf16 bits (kind 0) or as fp16 bits
+// (kind 1, the matrix-core operand format), plus their group sum.
+__device__ __forceinline__ void store8(uint16_t *dst, const float *v, int kind)
+{
+    uint4 o;
+    if (kind == 0) {
+        o.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+        o.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+        o.z = (uint32_t)f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16);
+        o.w = (uint32_t)f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16);
+    } else {
+        o.x = pack_f16x2(v[0], v[1]);
+        o.y = pack_f16x2(v[2], v[3]);
+        o.z = pack_f16x2(v[4], v[5]);
+        o.w = pack_f16x2(v[6], v[7]);
+    }
+    *reinterpret_cast<uint4 *>(dst) = o;
+}
+
+template <int XT>
+__device__ __forceinline__ void ld8(const void *x, size_t e, float *v)
+{
+    if (XT == BF16) {
+        uint4 w = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(x) + e);
+        v[0] = bf16lo(w.x); v[1] = bf16hi(w.x); v[2] = bf16lo(w.y); v[3] = bf16hi(w.y);
+        v[4] = bf16lo(w.z); v[5] = bf16hi(w.z); v[6] = bf16lo(w.w); v[7] = bf16hi(w.w);
+    } else {
+        const float4 *p = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(x) + e);
+        float4 a = p[0], c = p[1];
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = c.x; v[5] = c.y; v[6] = c.z; v[7] = c.w;
+    }
+}
+
+// ---------------------------------------------------------------- RMSNorm
+// One work-group per row; d % 64 == 0, d <= 256*8*MAXV.
+constexpr int RN_MAXV = 4;
+
+template <int XT>
+__global__ __launch_bounds__(256) void k_rmsnorm(const void *__restrict__ x,
+                                                 const uint16_t *__restrict__ w,
+                                                 uint16_t *__restrict__ u, int kind,
+                                                 float *__restrict__ su, int d, float eps)
+{
+    __shared__ float red[4];
+    const size_t row = blockIdx.x;
+    const int nv = d >> 3;
+    float v[RN_MAXV][8];
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < RN_MAXV; ++i) {
+        const int vi = threadIdx.x + 256 * i;
+        if (vi < nv) {
+            ld8<XT>(x, row * d + 8 * vi, v[i]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss += v[i][e] * v[i][e];
+        }
+    }
+    ss = block_sum256(ss, red);
+    const float r = 1.0f / sqrtf(ss / (float)d + eps);
+#pragma unroll
+    for (int i = 0; i < RN_MAXV; ++i) {
+        const int vi = threadIdx.x + 256 * i;
+        float s = 0.f;
+        if (vi < nv) {
+            uint4 ww = *reinterpret_cast<const uint4 *>(w + 8 * vi);
+            const float w8[8] = {bf16lo(ww.x), bf16hi(ww.x), bf16lo(ww.y), bf16hi(ww.y),
+                                 bf16lo(ww.z), bf16hi(ww.z), bf16lo(ww.w), bf16hi(ww.w)};
+            float o[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                o[e] = round_bf16(v[i][e] * r * w8[e]);
+                s += o[e];
+            }
+            store8(u + row * d + 8 * vi, o, kind);
+        }
+        // 256 is a multiple of 8, so the 8 lanes of a group share the same i.
+        s = group8_sum(s);
+        if (su && vi < nv && (vi & 7) == 0) su[row * (d >> 6) + (vi >> 3)] = s;
+    }
+}
+
+hipError_t launch_rmsnorm(const void *x, int x_t, const uint16_t *w, uint16_t *u, int out_kind,
+                          float *su, int rows, int d, float eps, hipStream_t st)
+{
+    if (rows <= 0) return hipSuccess;
+    dim3 grid(rows), block(256);
+    if (x_t == BF16)
+        k_rmsnorm<BF16><<<grid, block, 0, st>>>(x, w, u, out_kind, su, d, eps);
+    else
+        k_rmsnorm<F32><<<grid, block, 0, st>>>(x, w, u, out_kind, su, d, eps);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------- gated RMSNorm
+// One work-group per (row, group of channels).  g = y * silu(z); out = g / rms(g) * w.
+__global__ __launch_bounds__(256) void k_rmsnorm_gated(const uint16_t *__restrict__ y,
+                                                       const uint16_t *__restrict__ z, long ld_z,
+                                                       const uint16_t *__restrict__ w,
+                                                       uint16_t *__restrict__ out, int kind,
+                                                       float *__restrict__ su, int d, int group,
+                                                       float eps)
+{
+    __shared__ float red[4];
+    const size_t row = blockIdx.x;
+    const int j = blockIdx.y;
+    const int nv = group >> 3;
+    const size_t base = (size_t)j * group;
+    float gv[RN_MAXV][8];
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < RN_MAXV; ++i) {
+        const int vi = threadIdx.x + 256 * i;
+        if (vi < nv) {
+            const uint4 yy = *reinterpret_cast<const uint4 *>(y + row * d + base + 8 * vi);
+            const uint4 zz = *reinterpret_cast<const uint4 *>(z + row * ld_z + base + 8 * vi);
+            const uint32_t ya[4] = {yy.x, yy.y, yy.z, yy.w}, za[4] = {zz.x, zz.y, zz.z, zz.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                gv[i][2 * e] = bf16lo(ya[e]) * silu(bf16lo(za[e]));
+                gv[i][2 * e + 1] = bf16hi(ya[e]) * silu(bf16hi(za[e]));
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss += gv[i][e] * gv[i][e];
+        }
+    }
+    ss = block_sum256(ss, red);
+    const float r = 1.0f / sqrtf(ss / (float)group + eps);
+#pragma unroll
+    for (int i = 0; i < RN_MAXV; ++i) {
+        const int vi = threadIdx.x + 256 * i;
+        float s = 0.f;
+        if (vi < nv) {
+            const uint4 ww = *reinterpret_cast<const uint4 *>(w + base + 8 * vi);
+            const float w8[8] = {bf16lo(ww.x), bf16hi(ww.x), bf16lo(ww.y), bf16hi(ww.y),
+                                 bf16lo(ww.z), bf16hi(ww.z), bf16lo(ww.w), bf16hi(ww.w)};
+            float o[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                o[e] = round_bf16(gv[i][e] * r * w8[e]);
+                s += o[e];
+            }
+            store8(out + row * d + base + 8 * vi, o, kind);
+        }
+        s = group8_sum(s);
+        if (su && vi < nv && (vi & 7) == 0) su[row * (d >> 6) + ((base >> 6) + (vi >> 3))] = s;
+    }
+}
+
+hipError_t launch_rmsnorm_gated(const uint16_t *y, const uint16_t *z, long ld_z,
+                                const uint16_t *w, uint16_t *out, int out_kind, float *su,
+                                int rows, int d, int group, float eps, hipStream_t st)
+{
+    if (rows <= 0) return hipSuccess;
+    dim3 grid(rows, d / group), block(256);
+    k_rmsnorm_gated<<<grid, block, 0, st>>>(y, z, ld_z, w, out, out_kind, su, d, group, eps);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------- conv over T
+// Thread per (sequence, channel, block of CT positions): causal depthwise conv, kernel 4,
+// tap 3 on the newest input, left context from the carried state (row 0 oldest) or zeros.
+constexpr int CT = 16;
+
+__global__ __launch_bounds__(256) void k_conv_seq(const uint16_t *__restrict__ xbc, long ld, int T,
+                                                  const uint16_t *__restrict__ s_in,
+                                                  uint16_t *__restrict__ s_out,
+                                                  const uint16_t *__restrict__ w,
+                                                  const uint16_t *__restrict__ bias,
+                                                  uint16_t *__restrict__ out, int channels)
+{
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    const int t0 = blockIdx.y * CT;
+    const int b = blockIdx.z;
+    if (c >= channels) return;
+    const uint16_t *xb = xbc + (size_t)b * T * ld;
+    const uint16_t *si = s_in ? s_in + (size_t)b * (CONVK - 1) * channels : nullptr;
+    auto in = [&](int tau) -> float {
+        if (tau >= 0) return bf16_to_f32(xb[(size_t)tau * ld + c]);
+        return si ? bf16_to_f32(si[(size_t)(tau + CONVK - 1) * channels + c]) : 0.f;
+    };
+    const uint2 wv = *reinterpret_cast<const uint2 *>(w + 4 * (size_t)c);
+    const float w0 = bf16lo(wv.x), w1 = bf16hi(wv.x), w2 = bf16lo(wv.y), w3 = bf16hi(wv.y);
+    const float bb = bf16_to_f32(bias[c]);
+    float x0 = in(t0 - 3), x1 = in(t0 - 2), x2 = in(t0 - 1);
+    const int tend = min(T, t0 + CT);
+    for (int t = t0; t < tend; ++t) {
+        const float x3 = bf16_to_f32(xb[(size_t)t * ld + c]);
+        float a = fmaf(w0, x0, bb);
+        a = fmaf(w1, x1, a);
+        a = fmaf(w2, x2, a);
+        a = fmaf(w3, x3, a);
+        out[((size_t)b * T + t) * channels + c] = f32_to_bf16(silu(a));
+        x0 = x1; x1 = x2; x2 = x3;
+    }
+    if (s_out && tend == T) {
+        uint16_t *so = s_out + (size_t)b * (CONVK - 1) * channels;
+        for (int r = 0; r < CONVK - 1; ++r) {
+            const int tau = T - (CONVK - 1) + r;
+            uint16_t v;
+            if (tau >= 0)
+                v = xb[(size_t)tau * ld + c];
+            else
+                v = si ? si[(size_t)(tau + CONVK - 1) * channels + c] : (uint16_t)0;
+            so[(size_t)r * channels + c] = v;
+        }
+    }
+}
+
+hipError_t launch_conv_seq(const uint16_t *xbc, long ld, int T, const uint16_t *state_in,
+                           uint16_t *state_out, const uint16_t *w, const uint16_t *b,
+                           uint16_t *out, int batch, int channels, hipStream_t st)
+{
+    dim3 grid((channels + 255) / 256, (T + CT - 1) / CT, batch), block(256);
+    k_conv_seq<<<grid, block, 0, st>>>(xbc, ld, T, state_in, state_out, w, b, out, channels);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------- bf16 -> fp16 bits
+__global__ __launch_bounds__(256) void k_to_f16(const uint16_t *__restrict__ x,
+                                                uint16_t *__restrict__ xh, float *__restrict__ su,
+                                                size_t nvec, int kvec)
+{
+    const size_t v = (size_t)blockIdx.x * 256 + threadIdx.x;
+    float s = 0.f;
+    if (v < nvec) {
+        const uint4 w = *reinterpret_cast<const uint4 *>(x + 8 * v);
+        uint4 o;
+        o.x = bf16x2_to_f16x2(w.x);
+        o.y = bf16x2_to_f16x2(w.y);
+        o.z = bf16x2_to_f16x2(w.z);
+        o.w = bf16x2_to_f16x2(w.w);
+        *reinterpret_cast<uint4 *>(xh + 8 * v) = o;
+        s = sum_bf16x8(w);
+    }
+    s = group8_sum(s);
+    // kvec % 8 == 0, so a group never straddles two rows
+    if (v < nvec && (v & 7) == 0) su[v >> 3] = s;
+    (void)kvec;
+}
+
+hipError_t launch_to_f16(const uint16_t *x, uint16_t *xh, float *su, int M, int K, hipStream_t st)
+{
+    const size_t nvec = (size_t)M * K / 8;
+    dim3 grid((unsigned)((nvec + 255) / 256)), block(256);
+    k_to_f16<<<grid, block, 0, st>>>(x, xh, su, nvec, K / 8);
+    return hipGetLastError();
+}
+
+}  // namespace nh

@@ -1,0 +1,234 @@
+/*
+ * nhmamba.h -- C ABI of libnhmamba, the Nemotron-H Mamba2 mixer block on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  The mixer block of the Nemotron-H language model whose
+ * configuration is printed on the issue page "feat(nemotron_voicechat): load
+ * the VoiceChat checkpoint and run offline duplex inference ... #1374",
+ * section "config.json" (text_config: hidden_size 4480, mamba_num_heads 128,
+ * mamba_head_dim 80, ssm_state_size 128, n_groups 8, conv_kernel 4,
+ * use_conv_bias true, mamba_proj_bias false, layer_norm_epsilon 1e-5, and the
+ * 4-bit group-64 quantization of the mixer projections).  The block is
+ *     out = x + out_proj( RMSNormGated( SSM( silu(conv1d(xBC)) ), z ) ),
+ *     [z | xBC | dt_raw] = in_proj( RMSNorm(x) ),
+ * the standard Mamba2 mixer (Dao & Gu 2024, "Transformers are SSMs").  Two
+ * modes are exported, which the docs page "Nemotron VoiceChat", section
+ * "Offline timeline", says give the same tokens: a cached per-position step
+ * and a full-history recompute (here a chunked SSD scan).
+ *
+ * Conventions for every entry point.
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    allocates nothing; scratch memory is a caller-provided workspace whose
+ *    size is returned by nh_*_workspace_bytes.
+ *  - bf16 tensors are passed as uint16_t bit patterns; fp32 as float.
+ *  - Tensor pointers must be 16-byte aligned (NH_ERR_MISALIGNED otherwise);
+ *    row strides ("ld", in elements) must keep every row 16-byte aligned.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
+ *    work; they never synchronise the host.
+ *  - Arguments are validated before anything is enqueued.  On failure the
+ *    call returns a non-zero nh_status, enqueues nothing and changes nothing;
+ *    nh_last_error() then returns a message (thread-local).  NH_ERR_HIP means
+ *    a launch failed; device memory may then be partially written.
+ *  - Weights are read-only and may be shared by concurrent calls.  A state
+ *    (nh_mamba_state) and a workspace must not be used by two calls that can
+ *    run at the same time.
+ *  - Results are deterministic for fixed inputs on a fixed device (no
+ *    floating-point atomics).
+ *  - Internal matrix-core operands are fp16: activations entering the
+ *    chunked scan and the W4 GEMM must lie within the fp16 range
+ *    (|v| < 65504); magnitudes below 2^-14 are carried with fp16 subnormal
+ *    precision.  The block's own activations (normalised, SiLU-bounded) are
+ *    far inside this range.
+ */
+#ifndef NHMAMBA_H
+#define NHMAMBA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    NH_OK = 0,
+    NH_ERR_INVALID_ARGUMENT = 1,   /* NULL pointer, negative size, bad enum */
+    NH_ERR_UNSUPPORTED_SHAPE = 2,  /* dims outside the supported set */
+    NH_ERR_MISALIGNED = 3,         /* pointer or stride not 16-byte aligned */
+    NH_ERR_WORKSPACE_TOO_SMALL = 4,
+    NH_ERR_HIP = 5                 /* a HIP launch reported an error */
+} nh_status;
+
+typedef enum { NH_BF16 = 0, NH_F32 = 1 } nh_dtype;
+
+/* Block dimensions.  Supported set: hidden 4480, n_heads 128, head_dim 80,
+ * d_state 128, n_groups 8, conv_k 4 (text_config, issue page "config.json");
+ * chunk (scan chunk length Q) 1..256; eps > 0 (1e-5 in text_config). */
+typedef struct {
+    int hidden, n_heads, head_dim, d_state, n_groups, conv_k, chunk;
+    float eps;
+} nh_mamba_dims;
+
+/* Affine 4-bit weight matrix in the MLX layout (issue page "config.json":
+ * group_size 64, bits 4; a quantized linear carries .scales).
+ *   W[n][k] = scales[n][k/64] * q[n][k] + biases[n][k/64],
+ *   q[n][k] = (qweight[n][k/8] >> 4*(k%8)) & 15   (lowest nibble first).
+ * qweight: u32 [n_out][k_in/8]; scales, biases: bf16 [n_out][k_in/64].
+ * Requirements: group_size == 64, k_in % 64 == 0, k_in <= 16384. */
+typedef struct {
+    const uint32_t *qweight;
+    const uint16_t *scales;
+    const uint16_t *biases;
+    int n_out, k_in, group_size;
+} nh_w4_matrix;
+
+/* Weights of one block (mamba_proj_bias false: the projections have no bias). */
+typedef struct {
+    const uint16_t *norm_w;   /* bf16 [hidden]: pre-norm weight */
+    nh_w4_matrix in_proj;     /* [2*d_inner + 2*G*N + H][hidden] = [22656][4480] */
+    const uint16_t *conv_w;   /* bf16 [conv_dim][conv_k], tap conv_k-1 multiplies the newest
+                                 input (the [channels, 4, 1] layout of the issue page,
+                                 "Network 2", flattened) */
+    const uint16_t *conv_b;   /* bf16 [conv_dim] (use_conv_bias true) */
+    const float *dt_bias;     /* f32 [n_heads] */
+    const float *A_log;       /* f32 [n_heads]; A = -exp(A_log) */
+    const float *D;           /* f32 [n_heads] */
+    const uint16_t *gnorm_w;  /* bf16 [d_inner]: gated-norm weight */
+    nh_w4_matrix out_proj;    /* [hidden][d_inner] = [4480][10240] */
+} nh_mamba_weights;
+
+/* Per-sequence recurrent state of one block (the "Mamba2 state" a session
+ * keeps per position, docs page "Nemotron VoiceChat", "Online session"). */
+typedef struct {
+    uint16_t *conv_state; /* bf16 [batch][conv_k-1][conv_dim]; row 0 oldest */
+    float *ssm_state;     /* f32 [batch][n_heads][head_dim][d_state], d_state fastest */
+} nh_mamba_state;
+
+/* ------------------------------------------------------------- library */
+
+const char *nh_last_error(void);
+const char *nh_version(void);
+/* The hybrid_override_pattern of text_config: 'M' Mamba2, '*' attention, '-' MLP. */
+const char *nh_hybrid_pattern(void);
+
+/* ---------------------------------------------------------- primitives */
+
+/* y = W x (+ residual): the W4 dequantising matrix-vector product for small
+ * batches (per-position decode).  x: bf16 [batch][k_in]; residual: nullable,
+ * [batch][n_out] of res_dtype; y: [batch][n_out] of y_dtype (fp32
+ * accumulation, one rounding at the end).  batch 1..4. */
+nh_status nh_w4_gemv(const nh_w4_matrix *W, const uint16_t *x, int batch,
+                     const void *residual, nh_dtype res_dtype,
+                     void *y, nh_dtype y_dtype, void *stream);
+
+/* Y = X W^T (+ residual): the W4 matrix product for whole sequences.
+ * X: bf16 [M][k_in]; residual: nullable [M][n_out] of res_dtype;
+ * Y: [M][n_out] of y_dtype.  M >= 1.  Needs nh_w4_gemm_workspace_bytes(M, k_in)
+ * bytes of workspace.  Matrix-core arithmetic; W is dequantised exactly. */
+size_t nh_w4_gemm_workspace_bytes(int M, int k_in);
+nh_status nh_w4_gemm(const nh_w4_matrix *W, const uint16_t *X, int M,
+                     const void *residual, nh_dtype res_dtype,
+                     void *Y, nh_dtype y_dtype, void *ws, size_t ws_bytes, void *stream);
+
+/* u = RMSNorm(x) * w, rounded to bf16.  x: [rows][d] of x_dtype; w, u: bf16.
+ * RMS over the d values of a row, eps inside the square root. */
+nh_status nh_rmsnorm(const void *x, nh_dtype x_dtype, const uint16_t *w, uint16_t *u,
+                     int rows, int d, float eps, void *stream);
+
+/* One position of the causal depthwise conv1d (kernel k, with bias) + SiLU.
+ * xbc: bf16, row b at xbc + b*ld (channels values); conv_state: bf16
+ * [batch][k-1][channels], row 0 oldest, updated in place (shifted by one,
+ * the new input appended); w: bf16 [channels][k], tap k-1 newest; b: bf16
+ * [channels]; out: bf16 [batch][channels].  k == 4. */
+nh_status nh_conv1d_step(const uint16_t *xbc, long ld, uint16_t *conv_state,
+                         const uint16_t *w, const uint16_t *b, uint16_t *out,
+                         int batch, int channels, int k, void *stream);
+
+/* The same conv over T positions.  xbc row (b, t) at xbc + (b*T + t)*ld;
+ * state_in: nullable bf16 [batch][k-1][channels] (NULL = zeros);
+ * state_out: nullable, receives the last k-1 pre-conv rows (may not alias
+ * state_in); out: bf16 [batch][T][channels]. */
+nh_status nh_conv1d_seq(const uint16_t *xbc, long ld, int T, const uint16_t *state_in,
+                        uint16_t *state_out, const uint16_t *w, const uint16_t *b,
+                        uint16_t *out, int batch, int channels, int k, void *stream);
+
+/* One position of the selective SSM.  xc: bf16 [batch][conv_dim], the
+ * post-conv x | B | C; dt_raw: bf16, row b at dt_raw + b*ld_dt (n_heads
+ * values).  dt = softplus(dt_raw + dt_bias), A = -exp(A_log); for head h
+ * (group g = h / (n_heads/n_groups)):
+ *   S[h][p][:] = exp(dt*A) * S[h][p][:] + dt * x[h*P+p] * B[g][:]
+ *   y[h*P+p]   = C[g][:] . S[h][p][:] + D[h] * x[h*P+p]
+ * ssm_state: f32 [batch][H][P][N], updated in place; y: [batch][d_inner] of
+ * y_dtype.  batch 1..64. */
+nh_status nh_ssm_step(const nh_mamba_dims *d, const uint16_t *xc, const uint16_t *dt_raw,
+                      long ld_dt, const float *dt_bias, const float *A_log, const float *D,
+                      float *ssm_state, void *y, nh_dtype y_dtype, int batch, void *stream);
+
+/* The same recurrence over T positions, computed as a chunked SSD scan with
+ * chunk length d->chunk (intra-chunk quadratic form, chunk states, sequential
+ * state passing; Dao & Gu 2024).  Equals the per-position recurrence up to
+ * rounding for every chunk length.
+ * xc: bf16 [batch][T][conv_dim]; dt_raw: bf16, row (b, t) at
+ * dt_raw + (b*T + t)*ld_dt; h0: nullable f32 [batch][H][P][N] (NULL = zero
+ * state); h_final: nullable, receives the state after position T-1 (may
+ * alias h0); y: [batch][T][d_inner] of y_dtype. */
+nh_status nh_ssd_chunk_scan(const nh_mamba_dims *d, const uint16_t *xc, const uint16_t *dt_raw,
+                            long ld_dt, int T, const float *dt_bias, const float *A_log,
+                            const float *D, const float *h0, float *h_final, void *y,
+                            nh_dtype y_dtype, int batch, void *stream);
+
+/* Gated RMSNorm: g = y * silu(z); every block of `group` channels is
+ * normalised by its own RMS (eps inside the root) and multiplied by its
+ * slice of w.  y: bf16 [rows][d]; z: bf16, row r at z + r*ld_z; w: bf16 [d];
+ * out: bf16 [rows][d].  d % group == 0, group % 8 == 0. */
+nh_status nh_rmsnorm_gated(const uint16_t *y, const uint16_t *z, long ld_z, const uint16_t *w,
+                           uint16_t *out, int rows, int d, int group, float eps, void *stream);
+
+/* -------------------------------------------------------------- blocks */
+
+#define NH_MODE_STEP 0
+#define NH_MODE_SEQ 1
+
+/* Workspace bytes for nh_mamba_block_step (mode NH_MODE_STEP, T ignored) or
+ * nh_mamba_block_seq (NH_MODE_SEQ) at this batch and T; 0 on bad arguments. */
+size_t nh_block_workspace_bytes(const nh_mamba_dims *d, int batch, int T, int mode);
+
+/* One position of the whole block for `batch` independent sequences:
+ * out = x + mixer(RMSNorm(x)), state updated in place.
+ * x: [batch][hidden] of x_dtype; out: [batch][hidden] of out_dtype (may not
+ * alias x).  Storage points: the normalised input, the in_proj output, the
+ * conv output, y and the gated-norm output are rounded to bf16; dt, the
+ * state and the out_proj accumulator are fp32.  batch 1..4. */
+nh_status nh_mamba_block_step(const nh_mamba_dims *d, const nh_mamba_weights *w,
+                              nh_mamba_state *state, const void *x, nh_dtype x_dtype,
+                              void *out, nh_dtype out_dtype, int batch,
+                              void *ws, size_t ws_bytes, void *stream);
+
+/* The whole block over T positions (full-history recompute) with the same
+ * storage points.  init: nullable (NULL = zero conv and SSM state);
+ * final_state: nullable, receives the state after position T-1 (its
+ * buffers may be init's).  x: [batch][T][hidden]; out: [batch][T][hidden]. */
+nh_status nh_mamba_block_seq(const nh_mamba_dims *d, const nh_mamba_weights *w,
+                             const nh_mamba_state *init, nh_mamba_state *final_state,
+                             const void *x, nh_dtype x_dtype, int T, void *out,
+                             nh_dtype out_dtype, int batch, void *ws, size_t ws_bytes,
+                             void *stream);
+
+/* A stack of n_layers Mamba2 blocks applied in order (the M layers of the
+ * hybrid pattern; attention and MLP layers are not part of this library and
+ * act as identity between them).  The residual stream between blocks is
+ * fp32: layer i reads layer i-1's output and writes
+ * outs + i*batch*T*hidden (f32).  weights, states: host arrays of n_layers
+ * entries (states[i] is used in place by the step, and as init/final by the
+ * seq mode; a NULL states pointer in seq mode means zero initial state and
+ * no write-back).  mode NH_MODE_STEP requires T == 1. */
+nh_status nh_mamba_stack(const nh_mamba_dims *d, const nh_mamba_weights *weights,
+                         nh_mamba_state *states, int n_layers, int mode,
+                         const void *x, nh_dtype x_dtype, int T, float *outs, int batch,
+                         void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NHMAMBA_H */

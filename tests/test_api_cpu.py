@@ -1,0 +1,116 @@
+"""The C ABI without a GPU: the library loads, exports every entry point that
+include/nhmamba.h declares, and rejects bad arguments before touching the device
+(no compute call is made here)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nhmamba.h")
+
+
+@pytest.fixture(scope="module")
+def nh():
+    import hybrid_mamba2_decode_amd as m
+    return m
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(nh_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_binding_exports(nh):
+    assert _declared() == sorted(nh.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(nh):
+    for name in _declared():
+        assert hasattr(nh.lib, name), name
+
+
+def test_info_strings(nh):
+    assert "gfx950" in nh.version()
+    p = nh.hybrid_pattern()
+    assert len(p) == 56 and p.count("M") == 27 and p.count("*") == 4 and p.count("-") == 25
+
+
+def _fake_w4(n=64, k=128, gs=64, base=0x10000):
+    return nh_w4(base, base + 0x1000, base + 0x2000, n, k, gs)
+
+
+def nh_w4(q, s, b, n, k, gs):
+    import hybrid_mamba2_decode_amd as m
+    return m.nh_w4_matrix(q, s, b, n, k, gs)
+
+
+def _status(fn):
+    import hybrid_mamba2_decode_amd as m
+    with pytest.raises(m.NhError) as e:
+        fn()
+    return e.value.status
+
+
+def test_gemv_rejects_bad_arguments(nh):
+    A = 0x20000  # aligned fake addresses: validation fails before any use
+    assert _status(lambda: nh.nh_w4_gemv(_fake_w4(gs=32), A, 1, None, 0, A, 0, 0)) == nh.NH_ERR_UNSUPPORTED_SHAPE
+    assert _status(lambda: nh.nh_w4_gemv(_fake_w4(k=96), A, 1, None, 0, A, 0, 0)) == nh.NH_ERR_UNSUPPORTED_SHAPE
+    assert _status(lambda: nh.nh_w4_gemv(_fake_w4(), None, 1, None, 0, A, 0, 0)) == nh.NH_ERR_INVALID_ARGUMENT
+    assert _status(lambda: nh.nh_w4_gemv(_fake_w4(), A + 2, 1, None, 0, A, 0, 0)) == nh.NH_ERR_MISALIGNED
+    assert _status(lambda: nh.nh_w4_gemv(_fake_w4(), A, 5, None, 0, A, 0, 0)) == nh.NH_ERR_UNSUPPORTED_SHAPE
+    assert _status(lambda: nh.nh_w4_gemv(_fake_w4(), A, 1, None, 0, A, 7, 0)) == nh.NH_ERR_INVALID_ARGUMENT
+    assert "batch" in nh.lib.nh_last_error().decode() or "dtype" in nh.lib.nh_last_error().decode()
+
+
+def test_gemm_workspace_check(nh):
+    A = 0x20000
+    need = nh.nh_w4_gemm_workspace_bytes(100, 128)
+    assert need >= 100 * 128 * 2
+    assert _status(lambda: nh.nh_w4_gemm(_fake_w4(), A, 100, None, 0, A, 0, A, need - 1, 0)) == \
+        nh.NH_ERR_WORKSPACE_TOO_SMALL
+    assert _status(lambda: nh.nh_w4_gemm(_fake_w4(), A, 0, None, 0, A, 0, A, need, 0)) == \
+        nh.NH_ERR_UNSUPPORTED_SHAPE
+
+
+def test_block_dims_and_workspace_checks(nh):
+    A = 0x40000
+    d = nh.dims(chunk=128)
+    lw = nh.mamba_weights(A, _fake_w4(22656, 4480), A, A, A, A, A, A, _fake_w4(4480, 10240))
+    st = nh.mamba_state(A, A)
+    step_ws = nh.nh_block_workspace_bytes(d, 1, 1, nh.NH_MODE_STEP)
+    seq_ws = nh.nh_block_workspace_bytes(d, 2, 100, nh.NH_MODE_SEQ)
+    assert step_ws > 0 and seq_ws > step_ws
+    assert nh.nh_block_workspace_bytes(d, 5, 1, nh.NH_MODE_STEP) == 0
+    bad = nh.dims(chunk=128, head_dim=64)
+    assert _status(lambda: nh.nh_mamba_block_step(bad, lw, st, A, 0, A + 0x100, 0, 1, A, step_ws, 0)) == \
+        nh.NH_ERR_UNSUPPORTED_SHAPE
+    assert _status(lambda: nh.nh_mamba_block_step(d, lw, st, A, 0, A + 0x100, 0, 1, A, step_ws - 1, 0)) == \
+        nh.NH_ERR_WORKSPACE_TOO_SMALL
+    assert _status(lambda: nh.nh_mamba_block_step(d, lw, st, A, 0, A, 0, 1, A, step_ws, 0)) == \
+        nh.NH_ERR_INVALID_ARGUMENT  # out aliases x
+    wrong = nh.mamba_weights(A, _fake_w4(22656, 4416), A, A, A, A, A, A, _fake_w4(4480, 10240))
+    assert _status(lambda: nh.nh_mamba_block_step(d, wrong, st, A, 0, A + 0x100, 0, 1, A, step_ws, 0)) == \
+        nh.NH_ERR_UNSUPPORTED_SHAPE
+    for q in (0, 257):
+        assert _status(lambda: nh.nh_mamba_block_seq(nh.dims(chunk=q), lw, None, None, A, 0, 100, A + 0x100,
+                                                     0, 2, A, seq_ws, 0)) == nh.NH_ERR_UNSUPPORTED_SHAPE
+    assert _status(lambda: nh.nh_mamba_block_seq(d, lw, None, None, A, 0, 100, A + 0x100, 0, 2, A,
+                                                 seq_ws - 1, 0)) == nh.NH_ERR_WORKSPACE_TOO_SMALL
+    assert _status(lambda: nh.nh_mamba_stack(d, [lw], [st], 1, nh.NH_MODE_STEP, A, 0, 2, A + 0x100, 1, A,
+                                             step_ws, 0)) == nh.NH_ERR_UNSUPPORTED_SHAPE
+
+
+def test_primitive_checks(nh):
+    A = 0x40000
+    d = nh.dims(chunk=64)
+    assert _status(lambda: nh.nh_conv1d_step(A, 16, A, A, A, A, 1, 16, 3, 0)) == nh.NH_ERR_UNSUPPORTED_SHAPE
+    assert _status(lambda: nh.nh_conv1d_seq(A, 16, 4, A, A, A, A, A, 1, 16, 4, 0)) == nh.NH_ERR_INVALID_ARGUMENT
+    assert _status(lambda: nh.nh_ssm_step(d, A, A, 128, A, A, A, A, A, 0, 0, 0)) == nh.NH_ERR_UNSUPPORTED_SHAPE
+    assert _status(lambda: nh.nh_ssd_chunk_scan(d, A, A, 22656, 0, A, A, A, None, None, A, 0, 1, 0)) == \
+        nh.NH_ERR_UNSUPPORTED_SHAPE
+    assert _status(lambda: nh.nh_rmsnorm_gated(A, A, 10240, A, A, 1, 10240, 1000, 1e-5, 0)) == \
+        nh.NH_ERR_UNSUPPORTED_SHAPE
+    assert _status(lambda: nh.nh_rmsnorm(A, 0, A, A, 1, 4480, 0.0, 0)) == nh.NH_ERR_INVALID_ARGUMENT
