@@ -1,0 +1,389 @@
+#!/usr/bin/env python3
+"""Benchmark of libnhmamba (the Nemotron-H Mamba2 mixer block) on one MI355X.
+
+Headline (the JSON line's `value`): the cached per-position block step at batch 1 with a
+pre-filled state (config 1), in microseconds per layer-step, against the HBM roofline.  The
+timed loop rotates over `--copies` independent weight + state sets (8 x 93.7 MB by default,
+well beyond the 256 MB last-level cache), so every step streams its weights from HBM; a
+single-copy (cache-resident) figure is reported separately and labelled as such.
+
+Also measured in the same run, each in its own object of the JSON line:
+  * the chunked SSD scan at the config-4 shape (batch 2, T = 3750, chunk 256, 27 layers'
+    parameters), in position-layers per second against the matrix-core and HBM rooflines;
+  * the 27-layer stack stepwise over T = 413 (config 3) and the 27-layer full-history stack
+    at batch 2, T = 3750 (config 4);
+  * the CPU oracle on the host cores (a bounded sample of config 1), as a reported baseline.
+
+Per-kernel durations come from HIP events recorded around each kernel on the stream it runs
+on (the library's nh_profile_events hook for the three kernels of the block step).
+All inputs are seeded synthetic data (synth package); nothing is read from disk except the
+committed HBM-traffic counter summary under profiles/.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes as C
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # B/s, MI355X HBM3E
+MFMA_F16_PEAK = 2.5e15     # flop/s, dense bf16/fp16 matrix cores
+H, P, N, G, HID = 128, 80, 128, 8, 4480
+DI, CD, NIN = 10240, 12288, 22656
+
+
+# ------------------------------------------------------- algorithmic work
+
+def w4_bytes(n, k):
+    return n * k // 2 + 2 * 2 * n * (k // 64)   # packed nibbles + bf16 scales + bf16 biases
+
+
+def step_kernel_bytes(B=1, out_bytes=4):
+    """Algorithmic HBM bytes of the three kernels of one block step (batch B)."""
+    k1 = (w4_bytes(NIN, HID) + 2 * HID            # weights, norm weight
+          + B * 2 * HID                           # x (bf16)
+          + 12288 * 4 * 2 + 12288 * 2             # conv weight, bias
+          + B * 2 * 3 * CD * 2                    # conv state read + write
+          + B * 2 * (DI + CD + H))                # z, xc, dt_raw written
+    k2 = (B * H * P * N * 4 * 2                   # fp32 state read + write
+          + B * 2 * (2 * 1024 + DI)               # B, C, x (bf16)
+          + B * 2 * H + 4 * 3 * H                 # dt_raw, dt_bias, A_log, D
+          + B * 2 * DI * 3 + 2 * DI)              # y written, z read, o written, gated-norm weight
+    k3 = (w4_bytes(HID, DI) + B * 2 * DI          # weights, o
+          + B * 2 * HID + B * out_bytes * HID)    # residual x, output
+    return k1, k2, k3
+
+
+def scan_bytes_per_position():
+    return 2 * CD + 2 * H + 2 * DI                # xc + dt_raw read, y written (bf16)
+
+
+def scan_flops_per_position(Q):
+    """Causal-count flops per position of the chunked scan (all heads), chunk Q."""
+    hpg = H // G
+    per_head = ((Q + 1) / 2 * P * 2            # Y_diag = (G o L) X
+                + P * N * 2                    # chunk state
+                + N * P * 2                    # state -> output
+                + (Q + 1) / 2 * N * 2 / hpg)   # C B^T, once per group
+    return per_head * H
+
+
+# ------------------------------------------------------------- HIP events
+
+class Hip:
+    def __init__(self):
+        self.lib = C.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.lib.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [C.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [C.c_void_p]
+
+    def event(self):
+        e = C.c_void_p()
+        assert self.lib.hipEventCreate(C.byref(e)) == 0
+        return e.value
+
+    def record(self, e, stream):
+        assert self.lib.hipEventRecord(e, stream) == 0
+
+    def ms(self, a, b):
+        self.lib.hipEventSynchronize(b)
+        f = C.c_float()
+        assert self.lib.hipEventElapsedTime(C.byref(f), a, b) == 0
+        return f.value
+
+    def destroy(self, e):
+        self.lib.hipEventDestroy(e)
+
+
+# ------------------------------------------------------ counter summaries
+
+def _source_sha(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "hybrid_mamba2_decode_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kernel: str, source: str):
+    """HBM bytes per dispatch from the committed PMC summary, or None when absent or when
+    the kernel's source changed after the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        f = line.split()
+        if len(f) >= 4 and f[0] == kernel:
+            sha, nbytes = f[1], float(f[2])
+            return nbytes if sha == _source_sha(source) else None
+    return None
+
+
+# ------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000, help="timed block steps (config 1)")
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--copies", type=int, default=8, help="rotating weight+state sets")
+    ap.add_argument("--skip-seq", action="store_true", help="skip the config-4 scan and stack")
+    ap.add_argument("--skip-stack", action="store_true", help="skip the 27-layer stacks")
+    ap.add_argument("--skip-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); the block "
+              "has no multi-GPU path here", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import synth
+    import hybrid_mamba2_decode_amd as nh
+    from tests import gpu_util as gu
+
+    assert torch.cuda.is_available(), "no GPU visible"
+    hip = Hip()
+    stream = torch.cuda.current_stream().cuda_stream
+    log = lambda *a: print("[bench]", *a, file=sys.stderr, flush=True)  # noqa: E731
+
+    n_layers = 27
+    need_layers = n_layers if not (args.skip_stack and args.skip_seq) else args.copies
+    t0 = time.time()
+    host_layers = [synth.layer_weights(l) for l in range(max(need_layers, args.copies))]
+    dev_layers = [gu.layer_dev(lw) for lw in host_layers]
+    log(f"weights for {len(dev_layers)} layers ready in {time.time() - t0:.1f} s")
+
+    d128 = nh.dims(chunk=128)
+    out = {"metric": "Mamba2 block step us/layer (% HBM peak); SSD scan positions/s (% MFMA peak)"}
+
+    # ---------------------------------------------------------- config 1
+    B = 1
+    x1 = gu.to_dev(synth.block_input(1, B, 1)[:, 0])
+    cs0, ss0 = synth.prefilled_state(1, B)
+    states = [gu.state_dev(cs0, ss0) for _ in range(args.copies)]
+    ws_step = gu.workspace(nh.nh_block_workspace_bytes(d128, B, 1, nh.NH_MODE_STEP))
+    o1 = gu.empty_f32(B, HID)
+
+    def step(i):
+        nh.nh_mamba_block_step(d128, dev_layers[i], states[i][0], x1, nh.NH_BF16, o1, nh.NH_F32, B,
+                               ws_step, ws_step.numel(), stream)
+
+    for i in range(args.warmup):
+        step(i % args.copies)
+    torch.cuda.synchronize()
+    e0, e1 = hip.event(), hip.event()
+    hip.record(e0, stream)
+    t_wall = time.perf_counter()
+    for i in range(args.steps):
+        step(i % args.copies)
+    hip.record(e1, stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t_wall) * 1e3
+    ms_total = hip.ms(e0, e1)
+    us_layer = ms_total * 1e3 / args.steps
+    log(f"config 1 step: {us_layer:.2f} us/layer ({args.copies} rotating copies), host wall {wall_ms:.1f} ms")
+
+    # per-kernel durations of the block step (events between its three kernels)
+    nprof = min(args.steps, 400)
+    evs = [[hip.event() for _ in range(4)] for _ in range(nprof)]
+    for i in range(nprof):
+        nh.nh_profile_events(evs[i])
+        step(i % args.copies)
+    nh.nh_profile_events(None)
+    torch.cuda.synchronize()
+    kt = np.array([[hip.ms(e[j], e[j + 1]) for j in range(3)] for e in evs]) * 1e3  # us
+    k_avg = kt.mean(axis=0)
+    k_med = np.median(kt, axis=0)
+    for e in evs:
+        for x in e:
+            hip.destroy(x)
+    kb = step_kernel_bytes(B)
+    names = ["k_inproj_step", "k_ssm_step<gnorm>", "k_gemv<5,1> (out_proj)"]
+    kernels = [{"kernel": names[j], "avg_us": round(float(k_avg[j]), 3), "median_us": round(float(k_med[j]), 3),
+                "algorithmic_bytes": int(kb[j]), "GBps": round(kb[j] / (k_avg[j] * 1e-6) / 1e9, 1),
+                "hbm_frac": round(kb[j] / (k_avg[j] * 1e-6) / HBM_PEAK, 4)} for j in range(3)]
+    log("kernels:", kernels)
+
+    # cache-resident (single copy) figure, labelled
+    for i in range(args.warmup):
+        step(0)
+    hip.record(e0, stream)
+    for i in range(args.steps):
+        step(0)
+    hip.record(e1, stream)
+    torch.cuda.synchronize()
+    us_hot = hip.ms(e0, e1) * 1e3 / args.steps
+
+    total_bytes = sum(kb)
+    out.update({
+        "value": round(us_layer, 3), "unit": "us/layer", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(us_layer / 1e3, 6), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; pages' shapes and distributions)",
+        "config": {"workload": "config 1: one Mamba2 block, batch 1, one cached decode step with a pre-filled "
+                               "state, 1000 timed repeats over rotating weight/state copies",
+                   "batch": B, "hidden": HID, "heads": H, "head_dim": P, "d_state": N, "groups": G,
+                   "weights": "W4 group-64 affine (in_proj 22656x4480, out_proj 4480x10240)",
+                   "rotating_copies": args.copies},
+        "hbm_frac": round(total_bytes / (us_layer * 1e-6) / HBM_PEAK, 4),
+        "step_algorithmic_bytes": int(total_bytes),
+        "step_us_cache_resident": round(us_hot, 3),
+        "kernels": kernels,
+    })
+    dom = 0
+    out["roofline"] = {
+        "kernel": names[dom], "bound": "hbm",
+        "achieved": round(kb[dom] / (k_avg[dom] * 1e-6) / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+        "frac": round(kb[dom] / (k_avg[dom] * 1e-6) / HBM_PEAK, 4),
+        "traffic": traffic_from_profile(names[dom], "step.hip"),
+        "bytes_per_launch": int(kb[dom]), "avg_launch_us": round(float(k_avg[dom]), 3),
+    }
+
+    # ---------------------------------------------------------- config 3
+    if not args.skip_stack:
+        T3 = 413
+        x3 = gu.to_dev(synth.block_input(3, 1, T3))
+        st3 = [gu.state_dev(np.zeros((1, 3, CD), np.uint16), np.zeros((1, H, P, N), np.float32))
+               for _ in range(n_layers)]
+        outs3 = gu.empty_f32(n_layers, 1, HID)
+        s3 = [s[0] for s in st3]
+        xs = [x3[:, t].contiguous() for t in range(T3)]
+        torch.cuda.synchronize()
+        hip.record(e0, stream)
+        for t in range(T3):
+            nh.nh_mamba_stack(d128, dev_layers[:n_layers], s3, n_layers, nh.NH_MODE_STEP, xs[t], nh.NH_BF16, 1,
+                              outs3, 1, ws_step, ws_step.numel(), stream)
+        hip.record(e1, stream)
+        torch.cuda.synchronize()
+        ms3 = hip.ms(e0, e1)
+        out["stack_step"] = {
+            "workload": "config 3: 27 Mamba2 blocks, batch 1, stepwise over T=413 carrying conv+SSM state",
+            "total_ms": round(ms3, 3), "us_per_layer_step": round(ms3 * 1e3 / (T3 * n_layers), 3),
+            "hbm_frac": round(total_bytes / (ms3 * 1e-3 / (T3 * n_layers)) / HBM_PEAK, 4),
+        }
+        log("config 3:", out["stack_step"])
+        del st3, outs3
+
+    # ---------------------------------------------------------- config 4
+    if not args.skip_seq:
+        B4, T4, Q4 = 2, 3750, 256
+        d256 = nh.dims(chunk=Q4)
+        rng = np.random.default_rng(4004)
+        sets = []
+        for _ in range(3):   # rotating inputs: 3 x 184 MB, beyond the last-level cache
+            xc = synth.f32_to_bf16(rng.normal(0, 0.6, (B4, T4, CD)).astype(np.float32))
+            dtr = synth.f32_to_bf16(rng.normal(0, 1.25, (B4, T4, H)).astype(np.float32))
+            sets.append((gu.to_dev(xc), gu.to_dev(dtr)))
+        y4 = gu.empty_u16(B4, T4, DI)
+        hT = gu.empty_f32(B4, H, P, N)
+
+        def scan(l):
+            xcd, dtd = sets[l % 3]
+            lw = dev_layers[l % len(dev_layers)]
+            nh.nh_ssd_chunk_scan(d256, xcd, dtd, H, T4, lw.dt_bias, lw.A_log, lw.D, None, hT, y4, nh.NH_BF16,
+                                 B4, stream)
+
+        for l in range(3):
+            scan(l)
+        sev = [hip.event() for _ in range(n_layers + 1)]
+        hip.record(sev[0], stream)
+        for l in range(n_layers):
+            scan(l)
+            hip.record(sev[l + 1], stream)
+        torch.cuda.synchronize()
+        per = np.array([hip.ms(sev[l], sev[l + 1]) for l in range(n_layers)])
+        for e in sev:
+            hip.destroy(e)
+        pos = B4 * T4
+        sec = per.sum() * 1e-3
+        pps = pos * n_layers / sec
+        fl = scan_flops_per_position(Q4)
+        by = scan_bytes_per_position()
+        out["scan"] = {
+            "workload": "config 4 scan: chunked SSD scan, batch 2, T=3750, chunk 256, 27 layers' parameters, "
+                        "3 rotating input sets",
+            "metric": "SSD scan positions/s", "value": round(pps, 1), "unit": "position-layers/s",
+            "avg_launch_us": round(float(per.mean() * 1e3), 2),
+            "mfma_frac": round(pps * fl / MFMA_F16_PEAK, 4),
+            "hbm_frac": round(pps * by / HBM_PEAK, 4),
+            "roofline": {"kernel": "k_ssd_scan", "bound": "hbm", "achieved": round(pps * by / 1e9, 1),
+                         "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": round(pps * by / HBM_PEAK, 4),
+                         "traffic": traffic_from_profile("k_ssd_scan", "scan.hip"),
+                         "flops_per_position": round(fl), "bytes_per_position": by,
+                         "achieved_tflops": round(pps * fl / 1e12, 1), "mfma_peak_tflops": MFMA_F16_PEAK / 1e12},
+        }
+        log("config 4 scan:", out["scan"])
+        del sets
+
+        if not args.skip_stack:
+            x4 = gu.to_dev(synth.block_input(4, B4, T4))
+            ws4 = gu.workspace(nh.nh_block_workspace_bytes(d256, B4, T4, nh.NH_MODE_SEQ))
+            outs4 = gu.empty_f32(n_layers, B4, T4, HID)
+
+            def stack4():
+                nh.nh_mamba_stack(d256, dev_layers[:n_layers], None, n_layers, nh.NH_MODE_SEQ, x4, nh.NH_BF16,
+                                  T4, outs4, B4, ws4, ws4.numel(), stream)
+
+            stack4()
+            torch.cuda.synchronize()
+            reps = 2
+            hip.record(e0, stream)
+            for _ in range(reps):
+                stack4()
+            hip.record(e1, stream)
+            torch.cuda.synchronize()
+            ms4 = hip.ms(e0, e1) / reps
+            gemm_flops = 2 * pos * (NIN * HID + HID * DI) * n_layers
+            out["stack_seq"] = {
+                "workload": "config 4: 27 Mamba2 blocks, batch 2, full-history T=3750, chunk 256",
+                "ms": round(ms4, 2), "position_layers_per_s": round(pos * n_layers / (ms4 * 1e-3), 1),
+                "w4_gemm_tflops": round(gemm_flops / (ms4 * 1e-3) / 1e12, 1),
+            }
+            log("config 4 stack:", out["stack_seq"])
+            del outs4, ws4
+
+    if args.calib_copy_mib > 0:
+        a = torch.empty(args.calib_copy_mib * (1 << 20), dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        out["calib_copy_bytes"] = a.numel()
+
+    # ------------------------------------------------- CPU oracle baseline
+    if not args.skip_cpu:
+        import oracle
+        oracle.build(force=False)
+        xh = gu.bf16_bits_to_f64(synth.block_input(1, 1, 1))
+        csh = gu.bf16_bits_to_f64(cs0)
+        lw0 = host_layers[0]
+        reps, t_cpu = 0, 0.0
+        while t_cpu < args.cpu_seconds or reps < 2:
+            ts = time.perf_counter()
+            oracle.block(synth.REAL, lw0, xh, csh, ss0, mode=oracle.CONTRACT, stepwise=True)
+            t_cpu += time.perf_counter() - ts
+            reps += 1
+        out["cpu_baseline"] = {
+            "value": round(t_cpu / reps * 1e6, 1), "unit": "us/layer", "cores": oracle.lib().nho_max_threads(),
+            "kind": "oracle",
+            "sample": f"config 1 block step (batch 1, pre-filled state), fp64 oracle, {reps} repeats, "
+                      f"{t_cpu:.1f} s of host time",
+        }
+        log("cpu baseline:", out["cpu_baseline"])
+
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -32,7 +32,7 @@ EXPORTS = (
     "nh_last_error", "nh_version", "nh_hybrid_pattern", "nh_w4_gemv", "nh_w4_gemm_workspace_bytes",
     "nh_w4_gemm", "nh_rmsnorm", "nh_conv1d_step", "nh_conv1d_seq", "nh_ssm_step", "nh_ssd_chunk_scan",
     "nh_rmsnorm_gated", "nh_block_workspace_bytes", "nh_mamba_block_step", "nh_mamba_block_seq",
-    "nh_mamba_stack",
+    "nh_mamba_stack", "nh_profile_events",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -87,6 +87,7 @@ _sigs = {
     "nh_mamba_block_step": (_i, [_vp, _vp, _vp, _vp, _i, _vp, _i, _i, _vp, _sz, _vp]),
     "nh_mamba_block_seq": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _i, _i, _vp, _sz, _vp]),
     "nh_mamba_stack": (_i, [_vp, _vp, _vp, _i, _i, _vp, _i, _i, _vp, _i, _vp, _sz, _vp]),
+    "nh_profile_events": (_i, [_vp, _i]),
 }
 for _name, (_res, _args) in _sigs.items():
     _f = getattr(lib, _name)
@@ -227,3 +228,12 @@ def nh_mamba_stack(d, weights, states, n_layers, mode, x, x_dtype, T, outs, batc
     sarr = None if states is None else (nh_mamba_state * n_layers)(*states)
     _check(lib.nh_mamba_stack(C.byref(d), warr, sarr, n_layers, mode, _ptr(x), x_dtype, T, _ptr(outs),
                               batch, _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def nh_profile_events(events):
+    """events: None (off) or a sequence of 4 hipEvent_t handles (ints)."""
+    if events is None:
+        _check(lib.nh_profile_events(None, 0))
+    else:
+        arr = (C.c_void_p * len(events))(*events)
+        _check(lib.nh_profile_events(arr, len(events)))

@@ -19,6 +19,10 @@ using namespace nh;
 namespace {
 
 thread_local std::string g_err;
+thread_local hipEvent_t g_prof_ev[4];
+thread_local int g_prof_on = 0;
+
+hipError_t prof_mark(int i, hipStream_t s) { return g_prof_on ? hipEventRecord(g_prof_ev[i], s) : hipSuccess; }
 
 nh_status fail(nh_status s, const char *fmt, ...)
 {
@@ -208,13 +212,17 @@ nh_status block_step(const nh_mamba_dims *d, const nh_mamba_weights *w, nh_mamba
 {
     size_t nb;
     StepWs k = carve_step(ws, B, &nb);
+    NH_HIP(prof_mark(0, s), "profile event");
     NH_HIP(launch_inproj_step(view(&w->in_proj), x, x_t, w->norm_w, d->eps, B, k.z, k.xc, k.dtr,
                               st->conv_state, w->conv_w, w->conv_b, k.cnt, B * NGROUPS, s),
            "in_proj step");
+    NH_HIP(prof_mark(1, s), "profile event");
     NH_HIP(launch_ssm_step_gnorm(k.xc, k.dtr, NHEADS, w->dt_bias, w->A_log, w->D, st->ssm_state,
                                  k.y, k.z, w->gnorm_w, d->eps, k.part, k.cnt, k.o, B, s),
            "ssm step");
+    NH_HIP(prof_mark(2, s), "profile event");
     NH_HIP(launch_gemv(view(&w->out_proj), k.o, B, x, x_t, out, out_t, s), "out_proj step");
+    NH_HIP(prof_mark(3, s), "profile event");
     return ok();
 }
 
@@ -263,6 +271,21 @@ extern "C" {
 const char *nh_last_error(void) { return g_err.c_str(); }
 
 const char *nh_version(void) { return "libnhmamba 0.1 (gfx950)"; }
+
+nh_status nh_profile_events(void *const *events, int n)
+{
+    if (!events) {
+        g_prof_on = 0;
+        return ok();
+    }
+    if (n < 4) return fail(NH_ERR_INVALID_ARGUMENT, "need 4 events, got %d", n);
+    for (int i = 0; i < 4; ++i) {
+        if (!events[i]) return fail(NH_ERR_INVALID_ARGUMENT, "event %d is NULL", i);
+        g_prof_ev[i] = reinterpret_cast<hipEvent_t>(events[i]);
+    }
+    g_prof_on = 1;
+    return ok();
+}
 
 const char *nh_hybrid_pattern(void)
 {

@@ -111,6 +111,14 @@ const char *nh_version(void);
 /* The hybrid_override_pattern of text_config: 'M' Mamba2, '*' attention, '-' MLP. */
 const char *nh_hybrid_pattern(void);
 
+/* Measurement hook.  events: NULL (off) or an array of n >= 4 hipEvent_t
+ * created by the caller.  While set, every nh_mamba_block_step call on this
+ * thread records events[0] before its first kernel and events[i] after its
+ * i-th kernel (i = 1..3: fused pre-norm/in_proj/conv, SSM step + gated norm,
+ * out_proj + residual) on the call's stream, so the caller can read each
+ * kernel's duration with hipEventElapsedTime. */
+nh_status nh_profile_events(void *const *events, int n);
+
 /* ---------------------------------------------------------- primitives */
 
 /* y = W x (+ residual): the W4 dequantising matrix-vector product for small
