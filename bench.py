@@ -78,7 +78,13 @@ def scan_flops_per_position(Q):
 
 class Hip:
     def __init__(self):
-        self.lib = C.CDLL("libamdhip64.so")
+        # bind to the HIP runtime already mapped by torch (one runtime per process)
+        path = "libamdhip64.so"
+        for line in open("/proc/self/maps"):
+            if "libamdhip64" in line:
+                path = line.split()[-1]
+                break
+        self.lib = C.CDLL(path)
         self.lib.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
         self.lib.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
         self.lib.hipEventSynchronize.argtypes = [C.c_void_p]

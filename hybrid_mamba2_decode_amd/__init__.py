@@ -13,6 +13,10 @@ from __future__ import annotations
 import ctypes as C
 import os
 
+# PyTorch provides device memory and streams; load it first so that this library binds to
+# the same HIP runtime instance (a second runtime would not see torch's allocations).
+import torch  # noqa: F401
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libnhmamba.so")
 

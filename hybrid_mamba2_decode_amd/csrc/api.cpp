@@ -148,9 +148,8 @@ struct Carve {
 };
 
 struct StepWs {
-    uint16_t *z, *xc, *dtr, *y, *o;
+    uint16_t *z, *xc, *dtr, *y;
     float *part;
-    uint32_t *cnt;
 };
 
 StepWs carve_step(void *ws, int B, size_t *bytes)
@@ -161,9 +160,7 @@ StepWs carve_step(void *ws, int B, size_t *bytes)
     s.xc = c.take<uint16_t>((size_t)B * CONVDIM);
     s.dtr = c.take<uint16_t>((size_t)B * NHEADS);
     s.y = c.take<uint16_t>((size_t)B * DINNER);
-    s.o = c.take<uint16_t>((size_t)B * DINNER);
     s.part = c.take<float>((size_t)B * NHEADS * 2);
-    s.cnt = c.take<uint32_t>((size_t)B * NGROUPS);
     *bytes = c.off;
     return s;
 }
@@ -214,14 +211,15 @@ nh_status block_step(const nh_mamba_dims *d, const nh_mamba_weights *w, nh_mamba
     StepWs k = carve_step(ws, B, &nb);
     NH_HIP(prof_mark(0, s), "profile event");
     NH_HIP(launch_inproj_step(view(&w->in_proj), x, x_t, w->norm_w, d->eps, B, k.z, k.xc, k.dtr,
-                              st->conv_state, w->conv_w, w->conv_b, k.cnt, B * NGROUPS, s),
+                              st->conv_state, w->conv_w, w->conv_b, nullptr, 0, s),
            "in_proj step");
     NH_HIP(prof_mark(1, s), "profile event");
-    NH_HIP(launch_ssm_step_gnorm(k.xc, k.dtr, NHEADS, w->dt_bias, w->A_log, w->D, st->ssm_state,
-                                 k.y, k.z, w->gnorm_w, d->eps, k.part, k.cnt, k.o, B, s),
+    NH_HIP(launch_ssm_step_part(k.xc, k.dtr, NHEADS, w->dt_bias, w->A_log, w->D, st->ssm_state, k.y, k.z,
+                                k.part, B, s),
            "ssm step");
     NH_HIP(prof_mark(2, s), "profile event");
-    NH_HIP(launch_gemv(view(&w->out_proj), k.o, B, x, x_t, out, out_t, s), "out_proj step");
+    NH_HIP(launch_outproj_step(view(&w->out_proj), k.y, k.z, w->gnorm_w, k.part, d->eps, B, x, x_t, out, out_t, s),
+           "out_proj step");
     NH_HIP(prof_mark(3, s), "profile event");
     return ok();
 }

@@ -1,0 +1,579 @@
+// gemv.hip -- W4 dequantising matrix-vector products of the per-position block on gfx950.
+//
+// The per-position block streams 82.9 MB of packed 4-bit weights per layer and does a few
+// hundred MFLOP, so it is bound by HBM; the aim is every weight byte read exactly once with
+// 128-bit loads, enough bytes in flight per CU to cover HBM latency, and a dequantisation
+// cheap enough in VALU issue slots to hide under the loads.
+//
+// Layout.  LPR lanes own one output row (LPR = 32 or 64), so a wave works on 64/LPR rows at
+// a time; lane li of a row handles 16-byte chunks (32 nibbles, half a quantisation group)
+// c = li, li + LPR, ...  Its activations are the same for every row it visits, so they are
+// staged once per work-group in LDS and then held in registers for the whole kernel.
+//
+// Dequantisation.  For a packed word w (nibbles q0..q7 of k = 8j .. 8j+7), with the fp16
+// magic 0x6400 (1024.0, whose unit in the last place is 1):
+//   (w      & 0x000F000F) | 0x64006400 = fp16 pair (1024 + q0,    1024 + q4)
+//   (w      & 0x00F000F0) | 0x64006400 = fp16 pair (1024 + 16 q1, 1024 + 16 q5)
+//   (w >> 8 & 0x000F000F) | 0x64006400 = fp16 pair (1024 + q2,    1024 + q6)
+//   (w >> 8 & 0x00F000F0) | 0x64006400 = fp16 pair (1024 + 16 q3, 1024 + 16 q7)
+// i.e. one shift and four v_and_or_b32 per word; v_dot2_f32_f16 multiplies each pair with the
+// matching activation pair (fp16 holds the bf16 activations exactly).  With dA collecting the
+// even k and dB the odd k of a chunk,
+//   sum_k q_k x_k = dA + dB / 16 - (1024 sum_even x + 64 sum_odd x)
+// and the affine map W = s q + b of the chunk's group adds s * that + b * sum x.
+// Every product is exact and accumulation is fp32.
+#include "nh_device.hpp"
+#include "nh_kernels.hpp"
+
+namespace nh {
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c)
+{
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(c));
+    return r;
+}
+
+__device__ __forceinline__ float dot2h(uint32_t a, uint32_t b, float c)
+{
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
+}
+
+// Cross-lane sums with DPP inside rows of 16 lanes (quad swaps, half-row and row mirrors),
+// then LDS permutes for the 32- and 64-lane steps.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+template <int LPR>
+__device__ __forceinline__ float row_sum(float v)
+{
+    v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp_mov<0x141>(v);  // row_half_mirror
+    v += dpp_mov<0x140>(v);  // row_mirror
+    if (LPR >= 32) v += __shfl_xor(v, 16, 64);
+    if (LPR >= 64) v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
+// Activations of one 16-byte chunk: 16 fp16 pairs (k, k+4) in extraction order, the offset
+// 1024 sum_even + 64 sum_odd, and the plain sum.
+struct ActChunk {
+    uint32_t p[16];
+    float off, sum;
+};
+constexpr int ACT_WORDS = 18;
+
+// Build one chunk from 32 bf16-exact floats v[0..31].
+__device__ __forceinline__ void make_chunk(const float *v, uint32_t *dst)
+{
+    float se = 0.f, so = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float lo = v[8 * j + e], hi = v[8 * j + e + 4];
+            dst[4 * j + e] = pack_f16x2(lo, hi);
+            if (e & 1) so += lo + hi; else se += lo + hi;
+        }
+    dst[16] = __float_as_uint(fmaf(1024.f, se, 64.f * so));
+    dst[17] = __float_as_uint(se + so);
+}
+
+template <int LPR>
+struct GemvShape {
+    static constexpr int RPG = 64 / LPR;  // rows per wave-instruction
+};
+
+struct EpiPre {
+    uint32_t a, b, c, d;
+};
+
+// y[b][n] = acc + res[b][n]
+struct EpiStore {
+    void *y;
+    const void *res;
+    int y_t, res_t, n;
+    __device__ __forceinline__ EpiPre prefetch(int row, int b) const
+    {
+        EpiPre p{0u, 0u, 0u, 0u};
+        if (res) {
+            const size_t i = (size_t)b * n + row;
+            p.a = res_t == BF16 ? (uint32_t)reinterpret_cast<const uint16_t *>(res)[i] << 16
+                                : __float_as_uint(reinterpret_cast<const float *>(res)[i]);
+        }
+        return p;
+    }
+    __device__ __forceinline__ void operator()(int row, int b, float v, const EpiPre &p) const
+    {
+        const size_t i = (size_t)b * n + row;
+        v += __uint_as_float(p.a);
+        if (y_t == BF16)
+            reinterpret_cast<uint16_t *>(y)[i] = f32_to_bf16(v);
+        else
+            reinterpret_cast<float *>(y)[i] = v;
+    }
+};
+
+// in_proj rows of the per-position block: z | xBC | dt_raw.  The in_proj output is a bf16
+// storage point; xBC channels immediately run the causal conv step (state row 0 oldest,
+// tap 3 newest) and SiLU, and the conv state shifts by one position.  The conv state, taps
+// and bias of a row are prefetched together with the row's weights.
+struct EpiInProjStep {
+    uint16_t *z, *xc, *dtr, *cs;
+    const uint16_t *cw, *cb;
+    __device__ __forceinline__ EpiPre prefetch(int n, int b) const
+    {
+        const int c = min(max(n - DINNER, 0), CONVDIM - 1);
+        const uint16_t *st = cs + (size_t)b * (CONVK - 1) * CONVDIM + c;
+        const uint2 w = *reinterpret_cast<const uint2 *>(cw + 4 * (size_t)c);
+        EpiPre p;
+        p.a = (uint32_t)st[0] | ((uint32_t)st[CONVDIM] << 16);
+        p.b = (uint32_t)st[2 * CONVDIM] | ((uint32_t)cb[c] << 16);
+        p.c = w.x;
+        p.d = w.y;
+        return p;
+    }
+    __device__ __forceinline__ void operator()(int n, int b, float acc, const EpiPre &p) const
+    {
+        const uint16_t vb = f32_to_bf16(acc);
+        if (n < DINNER) {
+            z[(size_t)b * DINNER + n] = vb;
+        } else if (n < DINNER + CONVDIM) {
+            const int c = n - DINNER;
+            uint16_t *st = cs + (size_t)b * (CONVK - 1) * CONVDIM + c;
+            float a = bf16hi(p.b);
+            a = fmaf(bf16lo(p.c), bf16lo(p.a), a);
+            a = fmaf(bf16hi(p.c), bf16hi(p.a), a);
+            a = fmaf(bf16lo(p.d), bf16lo(p.b), a);
+            a = fmaf(bf16hi(p.d), bf16_to_f32(vb), a);
+            xc[(size_t)b * CONVDIM + c] = f32_to_bf16(silu(a));
+            st[0] = (uint16_t)(p.a >> 16);
+            st[CONVDIM] = (uint16_t)(p.b & 0xFFFFu);
+            st[2 * CONVDIM] = vb;
+        } else {
+            dtr[(size_t)b * NHEADS + (n - DINNER - CONVDIM)] = vb;
+        }
+    }
+};
+
+// One pipeline stage: RG row groups of 64/LPR rows, CPL chunks per lane.
+template <int RG, int CPL>
+struct Stage {
+    uint4 q[RG][CPL];
+    uint32_t s[RG][CPL], b[RG][CPL];
+};
+
+template <int RG, int CPL>
+__device__ __forceinline__ void load_stage(Stage<RG, CPL> &st, __amdgpu_buffer_rsrc_t rq,
+                                           __amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rb,
+                                           const uint32_t *qoff, const uint32_t *soff, uint32_t row0,
+                                           uint32_t rpg, uint32_t rowbytes, uint32_t kg2)
+{
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+        const uint32_t row = row0 + r * rpg;
+        const uint32_t qb = row * rowbytes, sb = row * kg2;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            st.q[r][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, qoff[i] + qb, 0, 0));
+            st.s[r][i] = __builtin_amdgcn_raw_buffer_load_b16(rs, soff[i] + sb, 0, 0);
+            st.b[r][i] = __builtin_amdgcn_raw_buffer_load_b16(rb, soff[i] + sb, 0, 0);
+        }
+    }
+}
+
+template <int LPR, int CPL, int NB, int RG, class Epi>
+__device__ __forceinline__ void compute_stage(const Stage<RG, CPL> &st, const ActChunk (&a)[NB][CPL],
+                                              const Epi &epi, const EpiPre &pre, int row0, int n_out,
+                                              int li, uint32_t mlo, uint32_t mhi, uint32_t magic)
+{
+    constexpr int RPG = GemvShape<LPR>::RPG;
+    float acc[RG][NB];
+#pragma unroll
+    for (int r = 0; r < RG; ++r)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            float s = 0.f;
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) {
+                const uint32_t wq[4] = {st.q[r][i].x, st.q[r][i].y, st.q[r][i].z, st.q[r][i].w};
+                float dA = 0.f, dB = 0.f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t w = wq[j], wh = w >> 8;
+                    dA = dot2h(and_or(w, mlo, magic), a[b][i].p[4 * j + 0], dA);
+                    dB = dot2h(and_or(w, mhi, magic), a[b][i].p[4 * j + 1], dB);
+                    dA = dot2h(and_or(wh, mlo, magic), a[b][i].p[4 * j + 2], dA);
+                    dB = dot2h(and_or(wh, mhi, magic), a[b][i].p[4 * j + 3], dB);
+                }
+                const float t = fmaf(dB, 0.0625f, dA) - a[b][i].off;
+                const float sc = __uint_as_float(st.s[r][i] << 16), bi = __uint_as_float(st.b[r][i] << 16);
+                s = fmaf(sc, t, fmaf(bi, a[b][i].sum, s));
+            }
+            acc[r][b] = row_sum<LPR>(s);
+        }
+    // lane li = r*NB + b of each row finishes (row, b); rows are row0 + r*RPG
+    float v = 0.f;
+#pragma unroll
+    for (int r = 0; r < RG; ++r)
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+            if (li == r * NB + b) v = acc[r][b];
+    const int er = li / NB, eb = li % NB;
+    const int row = row0 + er * RPG;
+    if (li < RG * NB && row < n_out) epi(row, eb, v, pre);
+}
+
+// Activations staged in LDS: [NB][nch][ACT_WORDS] words.
+template <int LPR, int CPL, int NB>
+__device__ __forceinline__ void act_from_lds(ActChunk (&a)[NB][CPL], const uint32_t *lds, int nch, int li)
+{
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = li + LPR * i;
+            if (c < nch) {
+                const uint32_t *src = lds + ((size_t)b * nch + c) * ACT_WORDS;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) a[b][i].p[j] = src[j];
+                a[b][i].off = __uint_as_float(src[16]);
+                a[b][i].sum = __uint_as_float(src[17]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) a[b][i].p[j] = 0u;
+                a[b][i].off = 0.f;
+                a[b][i].sum = 0.f;
+            }
+        }
+}
+
+// The streaming loop.  Construction issues the first stage's loads, so a kernel can build
+// its activations (LDS staging, pre-norm, gated norm) while those loads are in flight.
+template <int LPR, int CPL, int NB, int RG, class Epi>
+struct GemvRunner {
+    static constexpr int RPG = GemvShape<LPR>::RPG;
+    static constexpr int ROWS = RG * RPG;  // rows per wave per stage
+    const W4 W;
+    const Epi epi;
+    int sub, li, er, eb, stride, n0;
+    uint32_t rowbytes, kg2, qoff[CPL], soff[CPL];
+    __amdgpu_buffer_rsrc_t rq, rs, rb;
+    Stage<RG, CPL> A, B;
+    EpiPre pa, pb;
+
+    __device__ __forceinline__ GemvRunner(const W4 &W_, const Epi &epi_) : W(W_), epi(epi_)
+    {
+        const int lane = threadIdx.x & 63;
+        sub = lane / LPR;
+        li = lane % LPR;
+        // waves numbered across work-groups first, so the leftover rows of an uneven split land
+        // one per work-group instead of piling onto the first work-groups
+        const int wave = __builtin_amdgcn_readfirstlane((int)((threadIdx.x >> 6) * gridDim.x + blockIdx.x));
+        const int nwaves = gridDim.x * (blockDim.x >> 6);
+        const int nch = W.k >> 5;
+        rowbytes = (uint32_t)W.k / 2;
+        kg2 = (uint32_t)(W.k >> 6) * 2;
+        rq = __builtin_amdgcn_make_buffer_rsrc((void *)W.q, 0, (int)((uint32_t)W.n * rowbytes), 0x00020000);
+        rs = __builtin_amdgcn_make_buffer_rsrc((void *)W.s, 0, (int)((uint32_t)W.n * kg2), 0x00020000);
+        rb = __builtin_amdgcn_make_buffer_rsrc((void *)W.b, 0, (int)((uint32_t)W.n * kg2), 0x00020000);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const uint32_t c = (uint32_t)min(li + LPR * i, nch - 1);
+            qoff[i] = sub * rowbytes + 16u * c;
+            soff[i] = sub * kg2 + 2u * (c >> 1);
+        }
+        er = min(li / NB, RG - 1);
+        eb = li % NB;
+        stride = nwaves * ROWS;
+        n0 = wave * ROWS;
+        if (n0 < W.n) {
+            load_stage<RG, CPL>(A, rq, rs, rb, qoff, soff, (uint32_t)n0, RPG, rowbytes, kg2);
+            pa = epi.prefetch(min(n0 + er * RPG + sub, W.n - 1), eb);
+        }
+    }
+
+    __device__ __forceinline__ void run(const ActChunk (&a)[NB][CPL])
+    {
+        const uint32_t mlo = 0x000F000Fu, mhi = 0x00F000F0u, magic = 0x64006400u;
+        if (n0 >= W.n) return;
+        while (true) {
+            const int n1 = n0 + stride;
+            if (n1 < W.n) {
+                load_stage<RG, CPL>(B, rq, rs, rb, qoff, soff, (uint32_t)n1, RPG, rowbytes, kg2);
+                pb = epi.prefetch(min(n1 + er * RPG + sub, W.n - 1), eb);
+            }
+            compute_stage<LPR, CPL, NB, RG>(A, a, epi, pa, n0 + sub, W.n, li, mlo, mhi, magic);
+            if (n1 >= W.n) break;
+            const int n2 = n1 + stride;
+            if (n2 < W.n) {
+                load_stage<RG, CPL>(A, rq, rs, rb, qoff, soff, (uint32_t)n2, RPG, rowbytes, kg2);
+                pa = epi.prefetch(min(n2 + er * RPG + sub, W.n - 1), eb);
+            }
+            compute_stage<LPR, CPL, NB, RG>(B, a, epi, pb, n1 + sub, W.n, li, mlo, mhi, magic);
+            if (n2 >= W.n) break;
+            n0 = n2;
+        }
+    }
+};
+
+// ------------------------------------------------------------------ kernels
+
+template <int LPR, int CPL, int NB, int RG>
+__global__ __launch_bounds__(256, (NB == 1 ? (CPL <= 3 ? 3 : 2) : 1)) void k_gemv(W4 W, const uint16_t *__restrict__ x, EpiStore epi)
+{
+    GemvRunner<LPR, CPL, NB, RG, EpiStore> run(W, epi);
+    extern __shared__ uint32_t act_lds[];
+    const int nch = W.k >> 5;
+    for (int it = threadIdx.x; it < NB * nch; it += blockDim.x) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(x + (size_t)it * 32);  // [b][c] = b*nch + c
+        float v[32];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint4 w = src[j];
+            v[8 * j + 0] = bf16lo(w.x); v[8 * j + 1] = bf16hi(w.x); v[8 * j + 2] = bf16lo(w.y);
+            v[8 * j + 3] = bf16hi(w.y); v[8 * j + 4] = bf16lo(w.z); v[8 * j + 5] = bf16hi(w.z);
+            v[8 * j + 6] = bf16lo(w.w); v[8 * j + 7] = bf16hi(w.w);
+        }
+        make_chunk(v, act_lds + (size_t)it * ACT_WORDS);
+    }
+    __syncthreads();
+    ActChunk a[NB][CPL];
+    act_from_lds<LPR, CPL, NB>(a, act_lds, nch, (threadIdx.x & 63) % LPR);
+    run.run(a);
+}
+
+// Fused pre-norm + in_proj + conv step: the work-group normalises the input rows into LDS
+// (u = bf16(x / rms(x) * w)), then streams its share of in_proj rows.
+template <int NB, int XT>
+__global__ __launch_bounds__(256, (NB == 1 ? 3 : 1)) void k_inproj_step(W4 W, const void *__restrict__ x,
+                                                                    const uint16_t *__restrict__ nw, float eps,
+                                                                    EpiInProjStep epi, uint32_t *zero_ptr,
+                                                                    int nzero)
+{
+    constexpr int LPR = 64, CPL = (HIDDEN / 32 + LPR - 1) / LPR, RG = (NB == 1 ? 2 : 1);
+    constexpr int NCH = HIDDEN / 32;
+    GemvRunner<LPR, CPL, NB, RG, EpiInProjStep> run(W, epi);
+    extern __shared__ uint32_t act_lds[];
+    __shared__ float red[NB][4];
+    if (blockIdx.x == 0 && (int)threadIdx.x < nzero) zero_ptr[threadIdx.x] = 0u;
+    auto ld32 = [&](int b, int c, float *v) {
+        if (XT == BF16) {
+            const uint4 *src = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(x) +
+                                                               (size_t)b * HIDDEN + 32 * c);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint4 w = src[j];
+                v[8 * j + 0] = bf16lo(w.x); v[8 * j + 1] = bf16hi(w.x); v[8 * j + 2] = bf16lo(w.y);
+                v[8 * j + 3] = bf16hi(w.y); v[8 * j + 4] = bf16lo(w.z); v[8 * j + 5] = bf16hi(w.z);
+                v[8 * j + 6] = bf16lo(w.w); v[8 * j + 7] = bf16hi(w.w);
+            }
+        } else {
+            const float4 *src = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(x) +
+                                                                 (size_t)b * HIDDEN + 32 * c);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float4 f = src[j];
+                v[4 * j] = f.x; v[4 * j + 1] = f.y; v[4 * j + 2] = f.z; v[4 * j + 3] = f.w;
+            }
+        }
+    };
+    // pass 1: sum of squares per batch row (each thread owns at most one chunk per row)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        float ss = 0.f;
+        if ((int)threadIdx.x < NCH) {
+            float v[32];
+            ld32(b, threadIdx.x, v);
+#pragma unroll
+            for (int e = 0; e < 32; ++e) ss += v[e] * v[e];
+        }
+        ss = wave_sum(ss);
+        if ((threadIdx.x & 63) == 0) red[b][threadIdx.x >> 6] = ss;
+    }
+    __syncthreads();
+    // pass 2: normalised, bf16-rounded chunks
+    if ((int)threadIdx.x < NCH) {
+        const int c = threadIdx.x;
+        float w[32];
+        const uint4 *wsrc = reinterpret_cast<const uint4 *>(nw + 32 * c);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint4 q = wsrc[j];
+            w[8 * j + 0] = bf16lo(q.x); w[8 * j + 1] = bf16hi(q.x); w[8 * j + 2] = bf16lo(q.y);
+            w[8 * j + 3] = bf16hi(q.y); w[8 * j + 4] = bf16lo(q.z); w[8 * j + 5] = bf16hi(q.z);
+            w[8 * j + 6] = bf16lo(q.w); w[8 * j + 7] = bf16hi(q.w);
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const float tot = (red[b][0] + red[b][1]) + (red[b][2] + red[b][3]);
+            const float r = 1.0f / sqrtf(tot / (float)HIDDEN + eps);
+            float v[32];
+            ld32(b, c, v);
+#pragma unroll
+            for (int e = 0; e < 32; ++e) v[e] = round_bf16(v[e] * r * w[e]);
+            make_chunk(v, act_lds + ((size_t)b * NCH + c) * ACT_WORDS);
+        }
+    }
+    __syncthreads();
+    ActChunk a[NB][CPL];
+    act_from_lds<LPR, CPL, NB>(a, act_lds, NCH, (threadIdx.x & 63) % LPR);
+    run.run(a);
+}
+
+// Fused gated RMSNorm + out_proj + residual for the per-position block.  The work-group forms
+// o = bf16(RMSNorm_group(y * silu(z)) * w) straight into the LDS activation format from y,
+// z and the per-(head, half) sums of squares left by the SSM step, while the first stage of
+// out_proj weights is already in flight; o never goes to memory.
+template <int NB>
+__global__ __launch_bounds__(NB == 1 ? 512 : 256, 1) void k_outproj_step(W4 W, const uint16_t *__restrict__ y,
+                                                         const uint16_t *__restrict__ z,
+                                                         const uint16_t *__restrict__ gw,
+                                                         const float *__restrict__ part, float eps,
+                                                         EpiStore epi)
+{
+    constexpr int LPR = 64, NCH = DINNER / 32, CPL = NCH / LPR, RG = 1;
+    GemvRunner<LPR, CPL, NB, RG, EpiStore> run(W, epi);
+    extern __shared__ uint32_t act_lds[];
+    __shared__ float rstd[NB][NGROUPS];
+    if ((int)threadIdx.x < NB * NGROUPS) {
+        const int b = threadIdx.x / NGROUPS, g = threadIdx.x % NGROUPS;
+        const float *pg = part + ((size_t)b * NHEADS + g * HPG) * 2;
+        float t = 0.f;
+        for (int i = 0; i < 2 * HPG; ++i) t += pg[i];
+        rstd[b][g] = 1.0f / sqrtf(t / (float)GNORM + eps);
+    }
+    __syncthreads();
+    for (int it = threadIdx.x; it < NB * NCH; it += blockDim.x) {
+        const int b = it / NCH, c = it % NCH;
+        const float r = rstd[b][(32 * c) / GNORM];
+        const uint4 *yp = reinterpret_cast<const uint4 *>(y + (size_t)b * DINNER + 32 * c);
+        const uint4 *zp = reinterpret_cast<const uint4 *>(z + (size_t)b * DINNER + 32 * c);
+        const uint4 *wp = reinterpret_cast<const uint4 *>(gw + 32 * c);
+        float v[32];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint4 yy = yp[j], zz = zp[j], ww = wp[j];
+            const uint32_t ya[4] = {yy.x, yy.y, yy.z, yy.w}, za[4] = {zz.x, zz.y, zz.z, zz.w};
+            const uint32_t wa[4] = {ww.x, ww.y, ww.z, ww.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[8 * j + 2 * e] = round_bf16(bf16lo(ya[e]) * silu(bf16lo(za[e])) * r * bf16lo(wa[e]));
+                v[8 * j + 2 * e + 1] = round_bf16(bf16hi(ya[e]) * silu(bf16hi(za[e])) * r * bf16hi(wa[e]));
+            }
+        }
+        make_chunk(v, act_lds + (size_t)it * ACT_WORDS);
+    }
+    __syncthreads();
+    ActChunk a[NB][CPL];
+    act_from_lds<LPR, CPL, NB>(a, act_lds, NCH, (threadIdx.x & 63) % LPR);
+    run.run(a);
+}
+
+// ------------------------------------------------------------------ launchers
+
+static int cu_count()
+{
+    static int cus = 0;
+    if (!cus) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+    }
+    return cus;
+}
+
+// Persistent grid: at most two work-groups of four waves per CU, each wave walking stages.
+static int gemv_grid(int n, int rows_per_stage, int wgs_per_cu)
+{
+    const int stages = (n + rows_per_stage - 1) / rows_per_stage;
+    const int g = (stages + 3) / 4;
+    const int cap = wgs_per_cu * cu_count();
+    return g < cap ? g : cap;
+}
+
+template <int LPR, int CPL, int NB, int RG>
+static hipError_t run_gemv(const W4 &W, const uint16_t *x, EpiStore e, hipStream_t st)
+{
+    const size_t lds = (size_t)NB * (W.k >> 5) * ACT_WORDS * 4;
+    const int grid = gemv_grid(W.n, RG * (64 / LPR), NB == 1 ? (CPL <= 3 ? 3 : 2) : 1);
+    k_gemv<LPR, CPL, NB, RG><<<dim3(grid), dim3(256), lds, st>>>(W, x, e);
+    return hipGetLastError();
+}
+
+template <int NB>
+static hipError_t gemv_nb(const W4 &W, const uint16_t *x, EpiStore e, hipStream_t st)
+{
+    const int nch = W.k >> 5;
+    if (nch <= 32) return run_gemv<32, 1, NB, 2>(W, x, e, st);
+    if (nch <= 64) return run_gemv<64, 1, NB, 2>(W, x, e, st);
+    if (nch <= 128) return run_gemv<64, 2, NB, 2>(W, x, e, st);
+    if (nch <= 192) return run_gemv<64, 3, NB, (NB == 1 ? 2 : 1)>(W, x, e, st);
+    if (nch <= 256) return run_gemv<64, 4, NB, 1>(W, x, e, st);
+    if (nch <= 320) return run_gemv<64, 5, NB, 1>(W, x, e, st);
+    return run_gemv<64, 8, NB, 1>(W, x, e, st);
+}
+
+hipError_t launch_gemv(const W4 &W, const uint16_t *x, int batch, const void *res, int res_t,
+                       void *y, int y_t, hipStream_t st)
+{
+    EpiStore e{y, res, y_t, res_t, W.n};
+    switch (batch) {
+    case 1: return gemv_nb<1>(W, x, e, st);
+    case 2: return gemv_nb<2>(W, x, e, st);
+    case 3: return gemv_nb<3>(W, x, e, st);
+    default: return gemv_nb<4>(W, x, e, st);
+    }
+}
+
+hipError_t launch_outproj_step(const W4 &W, const uint16_t *y, const uint16_t *z, const uint16_t *gw,
+                               const float *part, float eps, int batch, const void *res, int res_t,
+                               void *out, int out_t, hipStream_t st)
+{
+    EpiStore e{out, res, out_t, res_t, W.n};
+    const size_t lds = (size_t)batch * (DINNER / 32) * ACT_WORDS * 4;
+    // one work-group per CU: 8 waves at batch 1; 4 waves (more registers each) above
+    const int grid = min(cu_count(), (W.n + 7) / 8);
+    switch (batch) {
+    case 1: k_outproj_step<1><<<dim3(grid), dim3(512), lds, st>>>(W, y, z, gw, part, eps, e); break;
+    case 2: k_outproj_step<2><<<dim3(grid), dim3(256), lds, st>>>(W, y, z, gw, part, eps, e); break;
+    case 3: k_outproj_step<3><<<dim3(grid), dim3(256), lds, st>>>(W, y, z, gw, part, eps, e); break;
+    default: k_outproj_step<4><<<dim3(grid), dim3(256), lds, st>>>(W, y, z, gw, part, eps, e); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_inproj_step(const W4 &W, const void *x, int x_t, const uint16_t *norm_w,
+                              float eps, int batch, uint16_t *z, uint16_t *xc, uint16_t *dtr,
+                              uint16_t *conv_state, const uint16_t *conv_w,
+                              const uint16_t *conv_b, uint32_t *zero_ptr, int nzero,
+                              hipStream_t st)
+{
+    EpiInProjStep e{z, xc, dtr, conv_state, conv_w, conv_b};
+    const size_t lds = (size_t)batch * (HIDDEN / 32) * ACT_WORDS * 4;
+#define NH_LAUNCH(NB)                                                                                      \
+    {                                                                                                      \
+        const int grid = gemv_grid(W.n, (NB == 1 ? 2 : 1), NB == 1 ? 3 : 1);                                \
+        if (x_t == BF16)                                                                                   \
+            k_inproj_step<NB, BF16><<<dim3(grid), dim3(256), lds, st>>>(W, x, norm_w, eps, e, zero_ptr, nzero); \
+        else                                                                                               \
+            k_inproj_step<NB, F32><<<dim3(grid), dim3(256), lds, st>>>(W, x, norm_w, eps, e, zero_ptr, nzero);  \
+    }
+    switch (batch) {
+    case 1: NH_LAUNCH(1); break;
+    case 2: NH_LAUNCH(2); break;
+    case 3: NH_LAUNCH(3); break;
+    default: NH_LAUNCH(4); break;
+    }
+#undef NH_LAUNCH
+    return hipGetLastError();
+}
+
+}  // namespace nh

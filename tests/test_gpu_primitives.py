@@ -89,7 +89,8 @@ def test_gemv_residual_bf16_out(env):
     nh.nh_w4_gemv(gu.w4_dev(W), gu.to_dev(x), 2, gu.to_dev(res), nh.NH_F32, y, nh.NH_BF16)
     ref = oracle.w4_matvec(W, gu.bf16_bits_to_f64(x)) + res
     got = gu.bf16_bits_to_f64(gu.from_dev_u16(y))
-    assert np.all(np.abs(got - ref) <= np.abs(ref) * 2 ** -8 + 1e-6)
+    # half a bf16 unit of the value plus the fp32 accumulation error (a rounding-boundary flip)
+    assert np.all(np.abs(got - ref) <= np.abs(ref) * 2 ** -8 + 2e-5 * np.abs(ref).max())
 
 
 # ------------------------------------------------------------------------ GEMM
