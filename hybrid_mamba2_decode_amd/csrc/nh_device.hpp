@@ -33,13 +33,15 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_floa
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// Round to nearest bf16, ties to even.  NaN stays NaN.
-__device__ __forceinline__ uint16_t f32_to_bf16(float f)
+// Round to nearest bf16, ties to even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+// Two floats -> packed bf16 pair (low half = lo), round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    typedef __bf16 bf16x2n __attribute__((ext_vector_type(2)));
+    const bf16x2n v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ float round_bf16(float f) { return bf16_to_f32(f32_to_bf16(f)); }

@@ -8,40 +8,76 @@
 //   S_out     = exp(cum_{L-1}) S_in + sum_j exp(cum_{L-1} - cum_j) dt_j x_j (outer) B_j
 //   y         = Y_off + Y_diag + D x
 //
-// Work decomposition: one work-group (4 waves) per (sequence, head) walks the chunks in order,
-// keeping the head's 80 x 128 fp32 state in registers as the accumulator of the state MFMA.
-// Work-groups are numbered so that the 16 heads sharing a B/C group land on the same XCD
-// (work-group i runs on XCD i mod 8) and read B and C through one L2.  Per chunk:
-//   1. dt = softplus(dt_raw + dt_bias), the log2-scaled cumulative sum of dt*A (block scan);
-//   2. B (L x 128) and x (as x^T, 80 x L) staged in LDS as fp16, S_in as fp16;
-//   3. each wave takes 16-row blocks {w, 7-w, 8+w, 15-w} (balanced causal work): C rows are
-//      loaded once into registers and serve both as the A operand of C S_in^T and as the B
-//      operand of B C^T, whose D layout is exactly the A-operand layout that
-//      (G o decay) X needs, so the intra-chunk product never leaves registers;
-//   4. each wave updates its two 16-column slices of the state.
-// Operands are fp16 (B, C, x are bf16-exact; the scaled operands round once, relative error
-// 2^-11); all accumulation is fp32.  Chunks shorter than 16/32 rows are zero-padded in LDS.
+// Decomposition.  One work-group of 8 waves per (sequence, head) walks the chunks in order and
+// keeps the head's 80 x 128 fp32 state in registers as the accumulator of the state MFMA (wave
+// w owns state columns 16w .. 16w+15).  Work-group i runs on XCD i mod 8, so the 16 heads that
+// share a B/C group are numbered to land on one XCD and read B and C through one L2.
+//
+// Per chunk:
+//   1. the chunk's B and x (prefetched into registers during the previous chunk) go to LDS as
+//      row-major fp16 tiles; dt = softplus(dt_raw + dt_bias) and the log2-scaled cumulative
+//      sum of dt A (256-wide block scan); S_in as fp16;
+//   2. (after step 3) the next chunk's B, x, dt_raw and C rows are issued to registers;
+//   3. wave w takes 16-row output blocks {w, 15-w} (equal causal work): its C rows, already in
+//      registers, are the A operand of C S_in^T and the B operand of B C^T, whose D layout is
+//      exactly the A-operand layout that (G o decay) X needs, so the intra-chunk product never
+//      leaves registers;
+//   4. x is scaled in place by w_j = exp(cum_{L-1} - cum_j) dt_j;
+//   5. each wave adds (w x)^T B to its state columns.
+// Operands with k = chunk position (x, w x, B in the state update) are read with
+// ds_read_b64_tr_b16, which transposes 4 x 16-bit elements across each group of 16 lanes, so
+// both tiles stay row-major in LDS.  Matrix-core operands are fp16 (B, C, x are bf16-exact;
+// computed operands round once, 2^-11 relative); accumulation is fp32.  Chunks shorter than
+// 32 rows are zero-padded.
 #include "nh_device.hpp"
 #include "nh_kernels.hpp"
 
 namespace nh {
 
-constexpr int BS_LD = DSTATE + 8;  // Bs row (fp16): 272 B
-constexpr int XT_LD = QMAX + 8;    // Xt row (fp16): 528 B
-constexpr int SI_LD = DSTATE + 8;  // Si row (fp16): 272 B
+constexpr int SC_THREADS = 512;
+constexpr int SC_WAVES = SC_THREADS / 64;
+constexpr int BS_LD = DSTATE + 16;  // B rows: 288 B (transposed reads conflict-free)
+constexpr int XS_LD = HDIM;         // x rows: 160 B (transposed reads conflict-free)
+constexpr int SI_LD = DSTATE + 8;   // S_in rows: 272 B
 
 struct ScanSmem {
     uint16_t Bs[QMAX * BS_LD];  // B of the chunk, [j][n]
-    uint16_t Xt[HDIM * XT_LD];  // x of the chunk transposed, [p][j]
+    uint16_t Xs[QMAX * XS_LD];  // x of the chunk, [j][p]; scaled by w_j before the state update
     uint16_t Si[HDIM * SI_LD];  // state at chunk start, [p][n]
     float cum[QMAX];            // log2-scaled cumulative dt*A
     float dtv[QMAX];            // dt
+    float Fv[QMAX];             // exp(cum_end(block of j) - cum_j) dt_j
     float wsum[4];
 };
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+
+// Transposed read: lane (group g = lane/16, s = lane%16) addresses row r0 + s/4, columns
+// c0 + 4*(s%4) .. +3 of a row-major fp16 tile; lane g*16 + i receives, for e = 0..3, element
+// [r0 + e][c0 + i] where r0 is the group's own base row.
+__device__ __forceinline__ uint2 ld_tr(const uint16_t *tile, int ld, int r0, int c0)
+{
+    const int s = threadIdx.x & 15;
+    const uint16_t *p = tile + (r0 + (s >> 2)) * ld + c0 + 4 * (s & 3);
+    const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)p);
+    return __builtin_bit_cast(uint2, v);
+}
 
 __device__ __forceinline__ half8 ld_half8(const uint16_t *p)
 {
     return __builtin_bit_cast(half8, *reinterpret_cast<const uint4 *>(p));
+}
+
+__device__ __forceinline__ half8 cat(uint2 a, uint2 b)
+{
+    return __builtin_bit_cast(half8, make_uint4(a.x, a.y, b.x, b.y));
+}
+
+// value of the neighbouring lane (lanes 2k and 2k+1 swap)
+__device__ __forceinline__ float dpp_swap1(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
 }
 
 __device__ __forceinline__ uint32_t pack_rne(float a, float b)
@@ -50,23 +86,48 @@ __device__ __forceinline__ uint32_t pack_rne(float a, float b)
     return __builtin_bit_cast(uint32_t, v);
 }
 
+__device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 w)
+{
+    return make_uint4(bf16x2_to_f16x2(w.x), bf16x2_to_f16x2(w.y), bf16x2_to_f16x2(w.z), bf16x2_to_f16x2(w.w));
+}
+
+constexpr int PB_VEC = QMAX * (DSTATE / 8) / SC_THREADS;  // 8 B vectors per thread
+constexpr int PX_VEC = QMAX * (HDIM / 8) / SC_THREADS;    // 5 x vectors per thread
+constexpr uint32_t OOB = 0x80000000u;                     // buffer offset that reads as zero
+
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+// Registers holding the next chunk while the current one is computed.
+struct Prefetch {
+    uint4 b[PB_VEC];
+    uint4 x[PX_VEC];
+    uint4 c[2][4];
+    uint32_t dt;
+};
+
 template <int YT>
-__global__ __launch_bounds__(256) void k_ssd_scan(const uint16_t *__restrict__ xc,
-                                                  const uint16_t *__restrict__ dtr, long ld_dt,
-                                                  int T, int Q, const float *__restrict__ dt_bias,
-                                                  const float *__restrict__ A_log,
-                                                  const float *__restrict__ Dp,
-                                                  const float *h0, float *hT,
-                                                  void *__restrict__ y)
+__global__ __launch_bounds__(SC_THREADS, 1) void k_ssd_scan(const uint16_t *__restrict__ xc,
+                                                            const uint16_t *__restrict__ dtr, long ld_dt,
+                                                            int T, int Q, const float *__restrict__ dt_bias,
+                                                            const float *__restrict__ A_log,
+                                                            const float *__restrict__ Dp, const float *h0,
+                                                            float *hT, void *__restrict__ y)
 {
     extern __shared__ __attribute__((aligned(16))) char smem_raw[];
     ScanSmem &sm = *reinterpret_cast<ScanSmem *>(smem_raw);
+    constexpr int YB = YT == BF16 ? 2 : 4;
 
     const int g = blockIdx.x % NGROUPS;
     const int rr = blockIdx.x / NGROUPS;
     const int h = g * HPG + rr % HPG;
     const int b = rr / HPG;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, q4 = lane >> 4;
 
     const float LOG2E = 1.4426950408889634f;
@@ -74,31 +135,73 @@ __global__ __launch_bounds__(256) void k_ssd_scan(const uint16_t *__restrict__ x
     const float dtb = dt_bias[h];
     const float Dh = Dp[h];
 
-    const uint16_t *xcb = xc + (size_t)b * T * CONVDIM;
-    const uint16_t *dtb_ptr = dtr + (size_t)b * T * ld_dt + h;
+    // Buffers over this sequence's rows: rows at or beyond T read as zero and are not stored.
+    const uint32_t XROW = CONVDIM * 2, YROW = DINNER * YB, DROW = (uint32_t)ld_dt * 2;
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(xc + (size_t)b * T * CONVDIM), 0, (int)((uint32_t)T * XROW), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(dtr + (size_t)b * T * ld_dt), 0, (int)((uint32_t)T * DROW), 0x00020000);
+    const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(reinterpret_cast<char *>(y) + (size_t)b * T * YROW), 0, (int)((uint32_t)T * YROW), 0x00020000);
 
-    // State registers: st[pb][nb] holds S[16pb + 4q4 + r][16(2 wave + nb) + l16], r = 0..3.
-    floatx4 st[5][2];
-    float *Sg = hT ? hT + ((size_t)b * NHEADS + h) * HDIM * DSTATE : nullptr;
-    const float *S0 = h0 ? h0 + ((size_t)b * NHEADS + h) * HDIM * DSTATE : nullptr;
+    // output blocks of this wave
+    const int I0 = wave, I1 = 15 - wave;
+    // per-thread load offsets (chunk-relative rows; rows >= Q are never needed)
+    uint32_t ob[PB_VEC], ox[PX_VEC], oc[2][4];
 #pragma unroll
-    for (int pb = 0; pb < 5; ++pb)
+    for (int i = 0; i < PB_VEC; ++i) {
+        const int v = tid + SC_THREADS * i, j = v >> 4, nv = v & 15;
+        ob[i] = j < Q ? j * XROW + (OFF_B + g * DSTATE + 8 * nv) * 2 : OOB;
+    }
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+    for (int i = 0; i < PX_VEC; ++i) {
+        const int v = tid + SC_THREADS * i, j = v / (HDIM / 8), pv = v % (HDIM / 8);
+        ox[i] = j < Q ? j * XROW + (h * HDIM + 8 * pv) * 2 : OOB;
+    }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int p = 16 * pb + 4 * q4 + r, n = 16 * (2 * wave + nb) + l16;
-                st[pb][nb][r] = S0 ? S0[p * DSTATE + n] : 0.f;
-            }
+    for (int bi = 0; bi < 2; ++bi) {
+        const int i = 16 * (bi == 0 ? I0 : I1) + l16;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            oc[bi][ks] = i < Q ? i * XROW + (OFF_C + g * DSTATE + 32 * ks + 8 * q4) * 2 : OOB;
+    }
+    const uint32_t odt = tid < Q ? tid * DROW + h * 2 : OOB;
+
+    auto prefetch = [&](Prefetch &pf, int t0) {
+        const uint32_t sx = (uint32_t)t0 * XROW;
+#pragma unroll
+        for (int i = 0; i < PB_VEC; ++i) pf.b[i] = bload16(rx, ob[i], sx);
+#pragma unroll
+        for (int i = 0; i < PX_VEC; ++i) pf.x[i] = bload16(rx, ox[i], sx);
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) pf.c[bi][ks] = bload16(rx, oc[bi][ks], sx);
+        pf.dt = __builtin_amdgcn_raw_buffer_load_b16(rd, odt, (uint32_t)t0 * DROW, 0);
+    };
+
+    // State: st[pb] holds S[16pb + 4q4 + r][16 wave + l16], r = 0..3.
+    floatx4 st[5];
+    {
+        const float *S0 = h0 ? h0 + ((size_t)b * NHEADS + h) * HDIM * DSTATE : nullptr;
+#pragma unroll
+        for (int pb = 0; pb < 5; ++pb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                st[pb][r] = S0 ? S0[(16 * pb + 4 * q4 + r) * DSTATE + 16 * wave + l16] : 0.f;
+    }
+
+    Prefetch pf;
+    prefetch(pf, 0);
 
     for (int t0 = 0; t0 < T; t0 += Q) {
         const int L = min(Q, T - t0);
         const int LR = (L + 31) & ~31;
 
-        // ---- 1. discretisation and cumulative sum (inclusive, 256-wide block scan)
+        // ---- 1. chunk to LDS; discretisation, cumulative sum, decay table; S_in
         float dtt = 0.f, a = 0.f;
         if (tid < L) {
-            dtt = softplus(bf16_to_f32(dtb_ptr[(size_t)(t0 + tid) * ld_dt]) + dtb);
+            dtt = softplus(bf16_to_f32((uint16_t)pf.dt) + dtb);
             a = dtt * A2;
         }
         float v = a;
@@ -107,72 +210,46 @@ __global__ __launch_bounds__(256) void k_ssd_scan(const uint16_t *__restrict__ x
             const float nbv = __shfl_up(v, o, 64);
             if (lane >= o) v += nbv;
         }
-        if (lane == 63) sm.wsum[wave] = v;
-        __syncthreads();
-        for (int w = 0; w < wave; ++w) v += sm.wsum[w];
-        sm.cum[tid] = v;
-        sm.dtv[tid] = dtt;
-
-        // ---- 2. stage B [j][n], x^T [p][j] and S_in [p][n] as fp16
-        for (int vi = tid; vi < LR * (DSTATE / 8); vi += 256) {
-            const int j = vi >> 4, nv = vi & 15;
-            uint4 o = make_uint4(0u, 0u, 0u, 0u);
-            if (j < L) {
-                const uint4 w = *reinterpret_cast<const uint4 *>(
-                    xcb + (size_t)(t0 + j) * CONVDIM + OFF_B + g * DSTATE + 8 * nv);
-                o.x = bf16x2_to_f16x2(w.x);
-                o.y = bf16x2_to_f16x2(w.y);
-                o.z = bf16x2_to_f16x2(w.z);
-                o.w = bf16x2_to_f16x2(w.w);
-            }
-            *reinterpret_cast<uint4 *>(&sm.Bs[j * BS_LD + 8 * nv]) = o;
-        }
-        for (int vi = tid; vi < LR * (HDIM / 8); vi += 256) {
-            const int j = vi / (HDIM / 8), pv = vi % (HDIM / 8);
-            uint4 w = make_uint4(0u, 0u, 0u, 0u);
-            if (j < L)
-                w = *reinterpret_cast<const uint4 *>(xcb + (size_t)(t0 + j) * CONVDIM + h * HDIM + 8 * pv);
-            const uint32_t wa[4] = {w.x, w.y, w.z, w.w};
+        if (lane == 63 && wave < 4) sm.wsum[wave] = v;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t f = bf16x2_to_f16x2(wa[e]);
-                sm.Xt[(8 * pv + 2 * e) * XT_LD + j] = (uint16_t)(f & 0xFFFFu);
-                sm.Xt[(8 * pv + 2 * e + 1) * XT_LD + j] = (uint16_t)(f >> 16);
-            }
+        for (int i = 0; i < PB_VEC; ++i) {
+            const int vv = tid + SC_THREADS * i, j = vv >> 4, nv = vv & 15;
+            *reinterpret_cast<uint4 *>(&sm.Bs[j * BS_LD + 8 * nv]) = bf16x8_to_f16x8(pf.b[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < PX_VEC; ++i) {
+            const int vv = tid + SC_THREADS * i, j = vv / (HDIM / 8), pv = vv % (HDIM / 8);
+            *reinterpret_cast<uint4 *>(&sm.Xs[j * XS_LD + 8 * pv]) = bf16x8_to_f16x8(pf.x[i]);
         }
 #pragma unroll
         for (int pb = 0; pb < 5; ++pb)
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int p = 16 * pb + 4 * q4 + r, n = 16 * (2 * wave + nb) + l16;
-                    sm.Si[p * SI_LD + n] = __builtin_bit_cast(uint16_t, (_Float16)st[pb][nb][r]);
-                }
+            for (int r = 0; r < 4; ++r)
+                sm.Si[(16 * pb + 4 * q4 + r) * SI_LD + 16 * wave + l16] =
+                    __builtin_bit_cast(uint16_t, (_Float16)st[pb][r]);
+        __syncthreads();
+        if (tid < QMAX) {
+            for (int w = 0; w < wave; ++w) v += sm.wsum[w];
+            // cumulative value at the end of this lane's 16-row block
+            const float cend = __shfl(v, lane | 15, 64);
+            sm.cum[tid] = v;
+            sm.dtv[tid] = dtt;
+            sm.Fv[tid] = __builtin_amdgcn_exp2f(cend - v) * dtt;
+        }
+        const int t1 = t0 + Q;
         __syncthreads();
 
-        // ---- 3. outputs, 16-row blocks per wave
+        // ---- 3. outputs of blocks I0, I1
         const int nblk = (L + 15) >> 4;
-        const int blocks[4] = {wave, 7 - wave, 8 + wave, 15 - wave};
-        for (int bi = 0; bi < 4; ++bi) {
-            const int I = blocks[bi];
+#pragma unroll 1
+        for (int bi = 0; bi < 2; ++bi) {
+            const int I = bi == 0 ? I0 : I1;
             if (I >= nblk) continue;
-            const int ia = 16 * I + l16;  // row of this lane in A/B operand layouts
-            half8 cf[4];
+            half8 cfb[4];
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                uint4 w = make_uint4(0u, 0u, 0u, 0u);
-                if (ia < L)
-                    w = *reinterpret_cast<const uint4 *>(xcb + (size_t)(t0 + ia) * CONVDIM + OFF_C +
-                                                         g * DSTATE + 32 * ks + 8 * q4);
-                uint4 f;
-                f.x = bf16x2_to_f16x2(w.x);
-                f.y = bf16x2_to_f16x2(w.y);
-                f.z = bf16x2_to_f16x2(w.z);
-                f.w = bf16x2_to_f16x2(w.w);
-                cf[ks] = __builtin_bit_cast(half8, f);
-            }
-            // Y_off = C S_in^T, then rows scaled by exp(cum_i)
+            for (int ks = 0; ks < 4; ++ks)
+                cfb[ks] = __builtin_bit_cast(half8, bf16x8_to_f16x8(bi == 0 ? pf.c[0][ks] : pf.c[1][ks]));
+            const int ia = 16 * I + l16;
             floatx4 acc[5];
 #pragma unroll
             for (int pb = 0; pb < 5; ++pb) {
@@ -180,7 +257,7 @@ __global__ __launch_bounds__(256) void k_ssd_scan(const uint16_t *__restrict__ x
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks)
                     acc[pb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                        cf[ks], ld_half8(&sm.Si[(16 * pb + l16) * SI_LD + 32 * ks + 8 * q4]), acc[pb], 0, 0, 0);
+                        cfb[ks], ld_half8(&sm.Si[(16 * pb + l16) * SI_LD + 32 * ks + 8 * q4]), acc[pb], 0, 0, 0);
             }
             float ei[4];
 #pragma unroll
@@ -190,122 +267,143 @@ __global__ __launch_bounds__(256) void k_ssd_scan(const uint16_t *__restrict__ x
 #pragma unroll
                 for (int r = 0; r < 4; ++r) acc[pb][r] *= ei[r];
 
-            // Y_diag: pairs of 16-column blocks (32 keys per MFMA)
             const float ci = sm.cum[ia];
-            for (int jp = 0; 2 * jp <= I; ++jp) {
-                float m[8];
+            // G^T tile: gt[r] = G[i = ia][j = 16J + 4q4 + r]
+            auto gtile = [&](int J) {
+                floatx4 gt = {0.f, 0.f, 0.f, 0.f};
+                const uint16_t *src = &sm.Bs[(16 * J + l16) * BS_LD + 8 * q4];
 #pragma unroll
-                for (int hb = 0; hb < 2; ++hb) {
-                    const int J = 2 * jp + hb;
-                    if (J <= I) {
-                        floatx4 gt = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int ks = 0; ks < 4; ++ks)
-                            gt = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                                ld_half8(&sm.Bs[(16 * J + l16) * BS_LD + 32 * ks + 8 * q4]), cf[ks], gt, 0, 0, 0);
-                        // gt[r] = G[i = ia][j = 16J + 4q4 + r]
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int j = 16 * J + 4 * q4 + r;
-                            const bool ok = (j <= ia) && (j < L);
-                            m[4 * hb + r] = ok ? gt[r] * __builtin_amdgcn_exp2f(ci - sm.cum[j]) * sm.dtv[j] : 0.f;
-                        }
-                    } else {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) m[4 * hb + r] = 0.f;
-                    }
-                }
-                uint4 mp;
-                mp.x = pack_rne(m[0], m[1]);
-                mp.y = pack_rne(m[2], m[3]);
-                mp.z = pack_rne(m[4], m[5]);
-                mp.w = pack_rne(m[6], m[7]);
-                const half8 mf = __builtin_bit_cast(half8, mp);
-#pragma unroll
-                for (int pb = 0; pb < 5; ++pb) {
-                    const uint16_t *xr = &sm.Xt[(16 * pb + l16) * XT_LD + 32 * jp + 4 * q4];
-                    const uint2 lo = *reinterpret_cast<const uint2 *>(xr);
-                    const uint2 hi = *reinterpret_cast<const uint2 *>(xr + 16);
-                    const half8 xf = __builtin_bit_cast(half8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-                    acc[pb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(mf, xf, acc[pb], 0, 0, 0);
-                }
-            }
-            // y = Y_off + Y_diag + D x
-#pragma unroll
-            for (int pb = 0; pb < 5; ++pb)
+                for (int ks = 0; ks < 4; ++ks)
+                    gt = __builtin_amdgcn_mfma_f32_16x16x32_f16(ld_half8(src + 32 * ks), cfb[ks], gt, 0, 0, 0);
+                return gt;
+            };
+            // below the diagonal: exp(cum_i - cum_j) = exp(cum_i - cum_end(J)) exp(cum_end(J) - cum_j)
+            auto offdiag = [&](int J, float *m) {
+                const floatx4 gt = gtile(J);
+                const float eJ = __builtin_amdgcn_exp2f(ci - sm.cum[16 * J + 15]);
+                const float4 F = *reinterpret_cast<const float4 *>(&sm.Fv[16 * J + 4 * q4]);
+                m[0] = gt[0] * eJ * F.x;
+                m[1] = gt[1] * eJ * F.y;
+                m[2] = gt[2] * eJ * F.z;
+                m[3] = gt[3] * eJ * F.w;
+            };
+            // the diagonal block: causal mask j <= i, and the skip term D x_i on j == i
+            auto diag = [&](float *m) {
+                const floatx4 gt = gtile(I);
+                const float4 cj = *reinterpret_cast<const float4 *>(&sm.cum[16 * I + 4 * q4]);
+                const float4 dj = *reinterpret_cast<const float4 *>(&sm.dtv[16 * I + 4 * q4]);
+                const float cja[4] = {cj.x, cj.y, cj.z, cj.w}, dja[4] = {dj.x, dj.y, dj.z, dj.w};
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int i = 16 * I + 4 * q4 + r, p = 16 * pb + l16;
-                    if (i < L) {
-                        const float xv = f16_to_f32(sm.Xt[p * XT_LD + i]);
-                        const float yv = fmaf(Dh, xv, acc[pb][r]);
-                        const size_t o = ((size_t)b * T + t0 + i) * DINNER + h * HDIM + p;
+                    const int jl = 4 * q4 + r;  // j - 16 I
+                    const float e = __builtin_amdgcn_exp2f(fminf(ci - cja[r], 0.f));
+                    const float v = jl <= l16 ? gt[r] * e * dja[r] : 0.f;
+                    m[r] = jl == l16 ? v + Dh : v;
+                }
+            };
+            auto apply = [&](int jp, const float *m) {
+                const half8 mf = __builtin_bit_cast(half8, make_uint4(pack_rne(m[0], m[1]), pack_rne(m[2], m[3]),
+                                                                      pack_rne(m[4], m[5]), pack_rne(m[6], m[7])));
+                // B operand X[j][p] with j = 32jp + 4q4 + e (e < 4) and 32jp + 16 + 4q4 + (e - 4)
+#pragma unroll
+                for (int pb = 0; pb < 5; ++pb) {
+                    const half8 xf = cat(ld_tr(sm.Xs, XS_LD, 32 * jp + 4 * q4, 16 * pb),
+                                         ld_tr(sm.Xs, XS_LD, 32 * jp + 16 + 4 * q4, 16 * pb));
+                    acc[pb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(mf, xf, acc[pb], 0, 0, 0);
+                }
+            };
+            // pairs of 16-column blocks strictly below the diagonal
+            for (int jp = 0; jp < I / 2; ++jp) {
+                float m[8];
+                offdiag(2 * jp, m);
+                offdiag(2 * jp + 1, m + 4);
+                apply(jp, m);
+            }
+            // the pair that holds the diagonal block
+            {
+                float m[8];
+                if (I & 1) {
+                    offdiag(I - 1, m);
+                    diag(m + 4);
+                } else {
+                    diag(m);
+#pragma unroll
+                    for (int r = 4; r < 8; ++r) m[r] = 0.f;
+                }
+                apply(I >> 1, m);
+            }
+            // store y = acc (the skip term is in the diagonal); neighbouring columns are paired
+            // across lanes for 2-column stores
+            const uint32_t soff = (uint32_t)t0 * YROW;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * I + 4 * q4 + r;
+                const uint32_t rowoff = (uint32_t)i * YROW + (uint32_t)(h * HDIM) * YB;
+#pragma unroll
+                for (int pb = 0; pb < 5; ++pb) {
+                    const int p = 16 * pb + l16;
+                    const float yv = acc[pb][r];
+                    const float yn = dpp_swap1(yv);
+                    if (!(l16 & 1)) {
                         if (YT == BF16)
-                            reinterpret_cast<uint16_t *>(y)[o] = f32_to_bf16(yv);
-                        else
-                            reinterpret_cast<float *>(y)[o] = yv;
+                            __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(yv, yn), ry, rowoff + p * YB, soff, 0);
+                        else {
+                            typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+                            const u32x2v w2 = {__float_as_uint(yv), __float_as_uint(yn)};
+                            __builtin_amdgcn_raw_buffer_store_b64(w2, ry, rowoff + p * YB, soff, 0);
+                        }
                     }
                 }
+            }
         }
+        // ---- 2. the next chunk into registers (free once this chunk's outputs are done;
+        // the loads land during steps 4 and 5)
+        if (t1 < T) prefetch(pf, t1);
+        __syncthreads();
 
-        // ---- 4. state update: S = exp(cum_last) S + (w x)^T B, w_j = exp(cum_last - cum_j) dt_j
+        // ---- 4. x <- w x, w_j = exp(cum_{L-1} - cum_j) dt_j (rows >= L hold zeros)
         const float cl = sm.cum[L - 1];
+        for (int vv = tid; vv < LR * (HDIM / 8); vv += SC_THREADS) {
+            const int j = vv / (HDIM / 8), pv = vv % (HDIM / 8);
+            const float wj = __builtin_amdgcn_exp2f(cl - sm.cum[j]) * sm.dtv[j];
+            uint4 *px = reinterpret_cast<uint4 *>(&sm.Xs[j * XS_LD + 8 * pv]);
+            const uint4 xv = *px;
+            const uint32_t xa[4] = {xv.x, xv.y, xv.z, xv.w};
+            uint32_t o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const half2v hv = __builtin_bit_cast(half2v, xa[e]);
+                o[e] = pack_rne((float)hv[0] * wj, (float)hv[1] * wj);
+            }
+            *px = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+        __syncthreads();
+
+        // ---- 5. state: S = exp(cum_{L-1}) S + (w x)^T B over this wave's 16 columns
         const float dec = __builtin_amdgcn_exp2f(cl);
 #pragma unroll
         for (int pb = 0; pb < 5; ++pb)
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) st[pb][nb][r] *= dec;
+            for (int r = 0; r < 4; ++r) st[pb][r] *= dec;
         for (int ks = 0; ks < (LR >> 5); ++ks) {
-            const int jb = 32 * ks + 8 * q4;
-            float wj[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) wj[e] = __builtin_amdgcn_exp2f(cl - sm.cum[jb + e]) * sm.dtv[jb + e];
-            half8 bfr[2];
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-                const int n = 16 * (2 * wave + nb) + l16;
-                uint16_t t8[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) t8[e] = sm.Bs[(jb + e) * BS_LD + n];
-                uint4 pk;
-                pk.x = (uint32_t)t8[0] | ((uint32_t)t8[1] << 16);
-                pk.y = (uint32_t)t8[2] | ((uint32_t)t8[3] << 16);
-                pk.z = (uint32_t)t8[4] | ((uint32_t)t8[5] << 16);
-                pk.w = (uint32_t)t8[6] | ((uint32_t)t8[7] << 16);
-                bfr[nb] = __builtin_bit_cast(half8, pk);
-            }
+            const int j0 = 32 * ks + 8 * q4;
+            const half8 bfr = cat(ld_tr(sm.Bs, BS_LD, j0, 16 * wave), ld_tr(sm.Bs, BS_LD, j0 + 4, 16 * wave));
 #pragma unroll
             for (int pb = 0; pb < 5; ++pb) {
-                const uint4 xw = *reinterpret_cast<const uint4 *>(&sm.Xt[(16 * pb + l16) * XT_LD + jb]);
-                const uint32_t xa[4] = {xw.x, xw.y, xw.z, xw.w};
-                uint4 ap;
-                uint32_t *apw = &ap.x;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const half2v hv = __builtin_bit_cast(half2v, xa[e]);
-                    apw[e] = pack_rne((float)hv[0] * wj[2 * e], (float)hv[1] * wj[2 * e + 1]);
-                }
-                const half8 af = __builtin_bit_cast(half8, ap);
-#pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
-                    st[pb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bfr[nb], st[pb][nb], 0, 0, 0);
+                const half8 af = cat(ld_tr(sm.Xs, XS_LD, j0, 16 * pb), ld_tr(sm.Xs, XS_LD, j0 + 4, 16 * pb));
+                st[pb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bfr, st[pb], 0, 0, 0);
             }
         }
         __syncthreads();
     }
 
-    if (Sg)
+    if (hT) {
+        float *Sg = hT + ((size_t)b * NHEADS + h) * HDIM * DSTATE;
 #pragma unroll
         for (int pb = 0; pb < 5; ++pb)
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int p = 16 * pb + 4 * q4 + r, n = 16 * (2 * wave + nb) + l16;
-                    Sg[p * DSTATE + n] = st[pb][nb][r];
-                }
+            for (int r = 0; r < 4; ++r) Sg[(16 * pb + 4 * q4 + r) * DSTATE + 16 * wave + l16] = st[pb][r];
+    }
 }
 
 hipError_t launch_ssd_scan(const uint16_t *xc, const uint16_t *dtr, long ld_dt, int T, int Q,
@@ -315,7 +413,7 @@ hipError_t launch_ssd_scan(const uint16_t *xc, const uint16_t *dtr, long ld_dt, 
 {
     const size_t smem = sizeof(ScanSmem);
     static bool attr_set[2] = {false, false};
-    dim3 grid(batch * NHEADS), block(256);
+    dim3 grid(batch * NHEADS), block(SC_THREADS);
     if (y_t == BF16) {
         if (!attr_set[0]) {
             hipError_t e = hipFuncSetAttribute((const void *)k_ssd_scan<BF16>,
