@@ -22,13 +22,19 @@
 //      registers, are the A operand of C S_in^T and the B operand of B C^T, whose D layout is
 //      exactly the A-operand layout that (G o decay) X needs, so the intra-chunk product never
 //      leaves registers;
-//   4. x is scaled in place by w_j = exp(cum_{L-1} - cum_j) dt_j;
-//   5. each wave adds (w x)^T B to its state columns.
+//   4. each wave adds x^T (w B) to its state columns, w_j = exp(cum_{L-1} - cum_j) dt_j taken
+//      from an fp16 table and multiplied into the B fragment in registers (steps 3 and 4 only
+//      read LDS, so no barrier separates them).
 // Operands with k = chunk position (x, w x, B in the state update) are read with
 // ds_read_b64_tr_b16, which transposes 4 x 16-bit elements across each group of 16 lanes, so
 // both tiles stay row-major in LDS.  Matrix-core operands are fp16 (B, C, x are bf16-exact;
 // computed operands round once, 2^-11 relative); accumulation is fp32.  Chunks shorter than
 // 32 rows are zero-padded.
+//
+// Global memory is addressed through buffer resources whose base is the chunk's first row and
+// whose size covers the chunk's valid rows only, so the hardware range check makes rows at or
+// beyond min(Q, T - t0) read as zero and drops their stores; offsets are per lane and
+// chunk-relative (the scalar offset operand is always 0).
 #include "nh_device.hpp"
 #include "nh_kernels.hpp"
 
@@ -47,6 +53,7 @@ struct ScanSmem {
     float cum[QMAX];            // log2-scaled cumulative dt*A
     float dtv[QMAX];            // dt
     float Fv[QMAX];             // exp(cum_end(block of j) - cum_j) dt_j
+    _Float16 Wh[QMAX];          // w_j = exp(cum_{L-1} - cum_j) dt_j (state-update weights)
     float wsum[4];
 };
 
@@ -93,7 +100,6 @@ __device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 w)
 
 constexpr int PB_VEC = QMAX * (DSTATE / 8) / SC_THREADS;  // 8 B vectors per thread
 constexpr int PX_VEC = QMAX * (HDIM / 8) / SC_THREADS;    // 5 x vectors per thread
-constexpr uint32_t OOB = 0x80000000u;                     // buffer offset that reads as zero
 
 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 
@@ -135,49 +141,39 @@ __global__ __launch_bounds__(SC_THREADS, 1) void k_ssd_scan(const uint16_t *__re
     const float dtb = dt_bias[h];
     const float Dh = Dp[h];
 
-    // Buffers over this sequence's rows: rows at or beyond T read as zero and are not stored.
+    // Rows of this sequence; a chunk's buffer resource starts at its first row.
     const uint32_t XROW = CONVDIM * 2, YROW = DINNER * YB, DROW = (uint32_t)ld_dt * 2;
-    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(xc + (size_t)b * T * CONVDIM), 0, (int)((uint32_t)T * XROW), 0x00020000);
-    const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(dtr + (size_t)b * T * ld_dt), 0, (int)((uint32_t)T * DROW), 0x00020000);
-    const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(reinterpret_cast<char *>(y) + (size_t)b * T * YROW), 0, (int)((uint32_t)T * YROW), 0x00020000);
+    const char *xseq = reinterpret_cast<const char *>(xc + (size_t)b * T * CONVDIM);
+    const char *dseq = reinterpret_cast<const char *>(dtr + (size_t)b * T * ld_dt);
+    char *yseq = reinterpret_cast<char *>(y) + (size_t)b * T * YROW;
+    auto rsrc = [](const char *p, uint32_t bytes) {
+        return __builtin_amdgcn_make_buffer_rsrc((void *)p, 0, (int)bytes, 0x00020000);
+    };
 
     // output blocks of this wave
     const int I0 = wave, I1 = 15 - wave;
-    // per-thread load offsets (chunk-relative rows; rows >= Q are never needed)
-    uint32_t ob[PB_VEC], ox[PX_VEC], oc[2][4];
-#pragma unroll
-    for (int i = 0; i < PB_VEC; ++i) {
-        const int v = tid + SC_THREADS * i, j = v >> 4, nv = v & 15;
-        ob[i] = j < Q ? j * XROW + (OFF_B + g * DSTATE + 8 * nv) * 2 : OOB;
-    }
-#pragma unroll
-    for (int i = 0; i < PX_VEC; ++i) {
-        const int v = tid + SC_THREADS * i, j = v / (HDIM / 8), pv = v % (HDIM / 8);
-        ox[i] = j < Q ? j * XROW + (h * HDIM + 8 * pv) * 2 : OOB;
-    }
-#pragma unroll
-    for (int bi = 0; bi < 2; ++bi) {
-        const int i = 16 * (bi == 0 ? I0 : I1) + l16;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            oc[bi][ks] = i < Q ? i * XROW + (OFF_C + g * DSTATE + 32 * ks + 8 * q4) * 2 : OOB;
-    }
-    const uint32_t odt = tid < Q ? tid * DROW + h * 2 : OOB;
+    // per-lane offsets inside a chunk: B row (tid/16) + 32i, 16 B piece tid%16; x row tid/2,
+    // half row tid%2 as 5 x 16 B; C rows of blocks I0, I1; dt row tid
+    const uint32_t vb = (uint32_t)(tid >> 4) * XROW + (OFF_B + g * DSTATE + 8 * (tid & 15)) * 2;
+    const uint32_t vx = (uint32_t)(tid >> 1) * XROW + (h * HDIM + 40 * (tid & 1)) * 2;
+    const uint32_t vc0 = (uint32_t)(16 * I0 + l16) * XROW + (OFF_C + g * DSTATE + 8 * q4) * 2;
+    const uint32_t vc1 = (uint32_t)(16 * I1 + l16) * XROW + (OFF_C + g * DSTATE + 8 * q4) * 2;
+    const uint32_t vdt = (uint32_t)tid * DROW + h * 2;
 
     auto prefetch = [&](Prefetch &pf, int t0) {
-        const uint32_t sx = (uint32_t)t0 * XROW;
+        const uint32_t rows = (uint32_t)min(Q, T - t0);
+        const __amdgpu_buffer_rsrc_t rx = rsrc(xseq + (size_t)t0 * XROW, rows * XROW);
+        const __amdgpu_buffer_rsrc_t rd = rsrc(dseq + (size_t)t0 * DROW, rows * DROW);
 #pragma unroll
-        for (int i = 0; i < PB_VEC; ++i) pf.b[i] = bload16(rx, ob[i], sx);
+        for (int i = 0; i < PB_VEC; ++i) pf.b[i] = bload16(rx, vb + (uint32_t)i * 32 * XROW, 0);
 #pragma unroll
-        for (int i = 0; i < PX_VEC; ++i) pf.x[i] = bload16(rx, ox[i], sx);
+        for (int e = 0; e < PX_VEC; ++e) pf.x[e] = bload16(rx, vx + 16 * e, 0);
 #pragma unroll
-        for (int bi = 0; bi < 2; ++bi)
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) pf.c[bi][ks] = bload16(rx, oc[bi][ks], sx);
-        pf.dt = __builtin_amdgcn_raw_buffer_load_b16(rd, odt, (uint32_t)t0 * DROW, 0);
+        for (int ks = 0; ks < 4; ++ks) {
+            pf.c[0][ks] = bload16(rx, vc0 + 64 * ks, 0);
+            pf.c[1][ks] = bload16(rx, vc1 + 64 * ks, 0);
+        }
+        pf.dt = __builtin_amdgcn_raw_buffer_load_b16(rd, vdt, 0, 0);
     };
 
     // State: st[pb] holds S[16pb + 4q4 + r][16 wave + l16], r = 0..3.
@@ -212,15 +208,13 @@ __global__ __launch_bounds__(SC_THREADS, 1) void k_ssd_scan(const uint16_t *__re
         }
         if (lane == 63 && wave < 4) sm.wsum[wave] = v;
 #pragma unroll
-        for (int i = 0; i < PB_VEC; ++i) {
-            const int vv = tid + SC_THREADS * i, j = vv >> 4, nv = vv & 15;
-            *reinterpret_cast<uint4 *>(&sm.Bs[j * BS_LD + 8 * nv]) = bf16x8_to_f16x8(pf.b[i]);
-        }
+        for (int i = 0; i < PB_VEC; ++i)
+            *reinterpret_cast<uint4 *>(&sm.Bs[((tid >> 4) + 32 * i) * BS_LD + 8 * (tid & 15)]) =
+                bf16x8_to_f16x8(pf.b[i]);
 #pragma unroll
-        for (int i = 0; i < PX_VEC; ++i) {
-            const int vv = tid + SC_THREADS * i, j = vv / (HDIM / 8), pv = vv % (HDIM / 8);
-            *reinterpret_cast<uint4 *>(&sm.Xs[j * XS_LD + 8 * pv]) = bf16x8_to_f16x8(pf.x[i]);
-        }
+        for (int e = 0; e < PX_VEC; ++e)
+            *reinterpret_cast<uint4 *>(&sm.Xs[(tid >> 1) * XS_LD + 40 * (tid & 1) + 8 * e]) =
+                bf16x8_to_f16x8(pf.x[e]);
 #pragma unroll
         for (int pb = 0; pb < 5; ++pb)
 #pragma unroll
@@ -228,6 +222,8 @@ __global__ __launch_bounds__(SC_THREADS, 1) void k_ssd_scan(const uint16_t *__re
                 sm.Si[(16 * pb + 4 * q4 + r) * SI_LD + 16 * wave + l16] =
                     __builtin_bit_cast(uint16_t, (_Float16)st[pb][r]);
         __syncthreads();
+        // cumulative value at the chunk end (a_j = 0 for j >= L)
+        const float cl = (sm.wsum[0] + sm.wsum[1]) + (sm.wsum[2] + sm.wsum[3]);
         if (tid < QMAX) {
             for (int w = 0; w < wave; ++w) v += sm.wsum[w];
             // cumulative value at the end of this lane's 16-row block
@@ -235,12 +231,14 @@ __global__ __launch_bounds__(SC_THREADS, 1) void k_ssd_scan(const uint16_t *__re
             sm.cum[tid] = v;
             sm.dtv[tid] = dtt;
             sm.Fv[tid] = __builtin_amdgcn_exp2f(cend - v) * dtt;
+            sm.Wh[tid] = (_Float16)(__builtin_amdgcn_exp2f(cl - v) * dtt);
         }
         const int t1 = t0 + Q;
         __syncthreads();
 
         // ---- 3. outputs of blocks I0, I1
         const int nblk = (L + 15) >> 4;
+        const __amdgpu_buffer_rsrc_t ry = rsrc(yseq + (size_t)t0 * YROW, (uint32_t)L * YROW);
 #pragma unroll 1
         for (int bi = 0; bi < 2; ++bi) {
             const int I = bi == 0 ? I0 : I1;
@@ -334,7 +332,6 @@ __global__ __launch_bounds__(SC_THREADS, 1) void k_ssd_scan(const uint16_t *__re
             }
             // store y = acc (the skip term is in the diagonal); neighbouring columns are paired
             // across lanes for 2-column stores
-            const uint32_t soff = (uint32_t)t0 * YROW;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = 16 * I + 4 * q4 + r;
@@ -346,40 +343,21 @@ __global__ __launch_bounds__(SC_THREADS, 1) void k_ssd_scan(const uint16_t *__re
                     const float yn = dpp_swap1(yv);
                     if (!(l16 & 1)) {
                         if (YT == BF16)
-                            __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(yv, yn), ry, rowoff + p * YB, soff, 0);
+                            __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(yv, yn), ry, rowoff + p * YB, 0, 0);
                         else {
                             typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
                             const u32x2v w2 = {__float_as_uint(yv), __float_as_uint(yn)};
-                            __builtin_amdgcn_raw_buffer_store_b64(w2, ry, rowoff + p * YB, soff, 0);
+                            __builtin_amdgcn_raw_buffer_store_b64(w2, ry, rowoff + p * YB, 0, 0);
                         }
                     }
                 }
             }
         }
         // ---- 2. the next chunk into registers (free once this chunk's outputs are done;
-        // the loads land during steps 4 and 5)
+        // the loads land during step 4)
         if (t1 < T) prefetch(pf, t1);
-        __syncthreads();
 
-        // ---- 4. x <- w x, w_j = exp(cum_{L-1} - cum_j) dt_j (rows >= L hold zeros)
-        const float cl = sm.cum[L - 1];
-        for (int vv = tid; vv < LR * (HDIM / 8); vv += SC_THREADS) {
-            const int j = vv / (HDIM / 8), pv = vv % (HDIM / 8);
-            const float wj = __builtin_amdgcn_exp2f(cl - sm.cum[j]) * sm.dtv[j];
-            uint4 *px = reinterpret_cast<uint4 *>(&sm.Xs[j * XS_LD + 8 * pv]);
-            const uint4 xv = *px;
-            const uint32_t xa[4] = {xv.x, xv.y, xv.z, xv.w};
-            uint32_t o[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const half2v hv = __builtin_bit_cast(half2v, xa[e]);
-                o[e] = pack_rne((float)hv[0] * wj, (float)hv[1] * wj);
-            }
-            *px = make_uint4(o[0], o[1], o[2], o[3]);
-        }
-        __syncthreads();
-
-        // ---- 5. state: S = exp(cum_{L-1}) S + (w x)^T B over this wave's 16 columns
+        // ---- 4. state: S = exp(cum_{L-1}) S + x^T (w B) over this wave's 16 columns
         const float dec = __builtin_amdgcn_exp2f(cl);
 #pragma unroll
         for (int pb = 0; pb < 5; ++pb)
@@ -387,7 +365,8 @@ __global__ __launch_bounds__(SC_THREADS, 1) void k_ssd_scan(const uint16_t *__re
             for (int r = 0; r < 4; ++r) st[pb][r] *= dec;
         for (int ks = 0; ks < (LR >> 5); ++ks) {
             const int j0 = 32 * ks + 8 * q4;
-            const half8 bfr = cat(ld_tr(sm.Bs, BS_LD, j0, 16 * wave), ld_tr(sm.Bs, BS_LD, j0 + 4, 16 * wave));
+            half8 bfr = cat(ld_tr(sm.Bs, BS_LD, j0, 16 * wave), ld_tr(sm.Bs, BS_LD, j0 + 4, 16 * wave));
+            bfr *= *reinterpret_cast<const half8 *>(&sm.Wh[j0]);
 #pragma unroll
             for (int pb = 0; pb < 5; ++pb) {
                 const half8 af = cat(ld_tr(sm.Xs, XS_LD, j0, 16 * pb), ld_tr(sm.Xs, XS_LD, j0 + 4, 16 * pb));

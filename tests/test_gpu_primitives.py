@@ -262,6 +262,29 @@ def test_scan_bf16_output_and_alias(env):
     assert gu.rel_l2(Sd.cpu().numpy()[0], rS) < 1e-3
 
 
+@pytest.mark.parametrize("T,Q", [(413, 128), (29, 256), (7, 4)])
+def test_scan_stores_stay_inside_the_sequence(env, T, Q):
+    """Rows past T in the last, partial chunk are computed as padding and must never be stored:
+    the memory right after y (and before it) keeps its contents."""
+    nh, oracle, gu, torch = env
+    _say("scan bounds", T, Q)
+    rng = np.random.default_rng(5 + T)
+    lw = synth.layer_weights(3)
+    xc, dtr = _scan_inputs(rng, 1, T)
+    pad = 64
+    buf = torch.full(((T + 2 * pad) * 10240,), 0x7E5A, dtype=torch.int16, device="cuda")
+    y = buf[pad * 10240:(pad + T) * 10240]
+    nh.nh_ssd_chunk_scan(nh.dims(chunk=Q), gu.to_dev(xc), gu.to_dev(dtr), 128, T, gu.to_dev(lw.dt_bias),
+                         gu.to_dev(lw.A_log), gu.to_dev(lw.D), None, None, y, nh.NH_BF16, 1)
+    torch.cuda.synchronize()
+    host = buf.cpu().numpy()
+    assert np.all(host[:pad * 10240] == 0x7E5A)
+    assert np.all(host[(pad + T) * 10240:] == 0x7E5A)
+    ry, _ = _oracle_scan(oracle, gu, lw, xc[0], dtr[0], np.zeros((128, 80, 128)))
+    got = gu.bf16_bits_to_f64(host[pad * 10240:(pad + T) * 10240].view(np.uint16).reshape(T, 10240))
+    assert gu.rel_l2(got, ry) < 4e-3
+
+
 # ---------------------------------------------------------------------- norms
 
 def test_rmsnorm_and_gated_norm(env):
