@@ -294,12 +294,14 @@ def main():
             sets.append((gu.to_dev(xc), gu.to_dev(dtr)))
         y4 = gu.empty_u16(B4, T4, DI)
         hT = gu.empty_f32(B4, H, P, N)
+        sws_n = nh.nh_ssd_scan_workspace_bytes(d256, B4, T4)
+        sws = gu.workspace(sws_n)
 
         def scan(l):
             xcd, dtd = sets[l % 3]
             lw = dev_layers[l % len(dev_layers)]
             nh.nh_ssd_chunk_scan(d256, xcd, dtd, H, T4, lw.dt_bias, lw.A_log, lw.D, None, hT, y4, nh.NH_BF16,
-                                 B4, stream)
+                                 B4, sws, sws_n, stream)
 
         for l in range(3):
             scan(l)

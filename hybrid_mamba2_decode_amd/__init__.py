@@ -34,7 +34,8 @@ NH_MODE_SEQ = 1
 # Entry points declared in include/nhmamba.h.
 EXPORTS = (
     "nh_last_error", "nh_version", "nh_hybrid_pattern", "nh_w4_gemv", "nh_w4_gemm_workspace_bytes",
-    "nh_w4_gemm", "nh_rmsnorm", "nh_conv1d_step", "nh_conv1d_seq", "nh_ssm_step", "nh_ssd_chunk_scan",
+    "nh_w4_gemm", "nh_rmsnorm", "nh_conv1d_step", "nh_conv1d_seq", "nh_ssm_step", "nh_ssd_scan_workspace_bytes",
+    "nh_ssd_chunk_scan",
     "nh_rmsnorm_gated", "nh_block_workspace_bytes", "nh_mamba_block_step", "nh_mamba_block_seq",
     "nh_mamba_stack", "nh_profile_events",
 )
@@ -85,7 +86,8 @@ _sigs = {
     "nh_conv1d_step": (_i, [_vp, _l, _vp, _vp, _vp, _vp, _i, _i, _i, _vp]),
     "nh_conv1d_seq": (_i, [_vp, _l, _i, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp]),
     "nh_ssm_step": (_i, [_vp, _vp, _vp, _l, _vp, _vp, _vp, _vp, _vp, _i, _i, _vp]),
-    "nh_ssd_chunk_scan": (_i, [_vp, _vp, _vp, _l, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _vp]),
+    "nh_ssd_scan_workspace_bytes": (_sz, [_vp, _i, _i]),
+    "nh_ssd_chunk_scan": (_i, [_vp, _vp, _vp, _l, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _sz, _vp]),
     "nh_rmsnorm_gated": (_i, [_vp, _vp, _l, _vp, _vp, _i, _i, _i, C.c_float, _vp]),
     "nh_block_workspace_bytes": (_sz, [_vp, _i, _i, _i]),
     "nh_mamba_block_step": (_i, [_vp, _vp, _vp, _vp, _i, _vp, _i, _i, _vp, _sz, _vp]),
@@ -196,11 +198,15 @@ def nh_ssm_step(d, xc, dt_raw, ld_dt, dt_bias, A_log, D, ssm_state, y, y_dtype, 
                            _ptr(D), _ptr(ssm_state), _ptr(y), y_dtype, batch, _stream(stream)))
 
 
+def nh_ssd_scan_workspace_bytes(d, batch, T) -> int:
+    return lib.nh_ssd_scan_workspace_bytes(C.byref(d), batch, T)
+
+
 def nh_ssd_chunk_scan(d, xc, dt_raw, ld_dt, T, dt_bias, A_log, D, h0, h_final, y, y_dtype, batch,
-                      stream=None):
+                      ws, ws_bytes, stream=None):
     _check(lib.nh_ssd_chunk_scan(C.byref(d), _ptr(xc), _ptr(dt_raw), ld_dt, T, _ptr(dt_bias),
                                  _ptr(A_log), _ptr(D), _ptr(h0), _ptr(h_final), _ptr(y), y_dtype,
-                                 batch, _stream(stream)))
+                                 batch, _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def nh_rmsnorm_gated(y, z, ld_z, w, out, rows, d, group, eps, stream=None):

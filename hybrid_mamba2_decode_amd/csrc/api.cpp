@@ -242,8 +242,13 @@ nh_status block_seq(const nh_mamba_dims *d, const nh_mamba_weights *w, const nh_
     }
     NH_HIP(launch_conv_seq(k.zx + DINNER, NIN, T, cs_in, cs_out, w->conv_w, w->conv_b, k.xc, B, CONVDIM, s),
            "conv");
+    // the scan's C.B^T tiles (at most 4 KiB per position) reuse the normalised input, which
+    // in_proj has consumed
+    if (ssd_scan_ws_bytes(B, T, d->chunk) > (size_t)M * HIDDEN * sizeof(uint16_t))
+        return fail(NH_ERR_INVALID_ARGUMENT, "internal: scan tiles exceed their workspace region");
     NH_HIP(launch_ssd_scan(k.xc, k.zx + DINNER + CONVDIM, NIN, T, d->chunk, w->dt_bias, w->A_log, w->D,
-                           init ? init->ssm_state : nullptr, fin ? fin->ssm_state : nullptr, k.y, BF16, B, s),
+                           init ? init->ssm_state : nullptr, fin ? fin->ssm_state : nullptr, k.y, BF16, B,
+                           k.u, s),
            "scan");
     NH_HIP(launch_rmsnorm_gated(k.y, k.zx, NIN, w->gnorm_w, k.o, 1, k.su_o, M, DINNER, GNORM, d->eps, s),
            "gated norm");
@@ -403,9 +408,16 @@ nh_status nh_ssm_step(const nh_mamba_dims *d, const uint16_t *xc, const uint16_t
     return ok();
 }
 
+size_t nh_ssd_scan_workspace_bytes(const nh_mamba_dims *d, int batch, int T)
+{
+    if (!d || batch < 1 || T < 1 || d->chunk < 1 || d->chunk > QMAX) return 0;
+    return ssd_scan_ws_bytes(batch, T, d->chunk);
+}
+
 nh_status nh_ssd_chunk_scan(const nh_mamba_dims *d, const uint16_t *xc, const uint16_t *dt_raw, long ld_dt,
                             int T, const float *dt_bias, const float *A_log, const float *D, const float *h0,
-                            float *h_final, void *y, nh_dtype y_dtype, int batch, void *stream)
+                            float *h_final, void *y, nh_dtype y_dtype, int batch, void *ws, size_t ws_bytes,
+                            void *stream)
 {
     NH_TRY(check_dims(d, true));
     NH_TRY(need_ptr(xc, "xc"));
@@ -420,8 +432,11 @@ nh_status nh_ssd_chunk_scan(const nh_mamba_dims *d, const uint16_t *xc, const ui
     if (batch < 1 || T < 1) return fail(NH_ERR_UNSUPPORTED_SHAPE, "batch %d, T %d", batch, T);
     if (ld_dt < 1 || (T * (long)batch > 1 && ld_dt < NHEADS))
         return fail(NH_ERR_UNSUPPORTED_SHAPE, "ld_dt %ld < n_heads", ld_dt);
+    NH_TRY(need_ptr(ws, "ws"));
+    const size_t need = ssd_scan_ws_bytes(batch, T, d->chunk);
+    if (ws_bytes < need) return fail(NH_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
     NH_HIP(launch_ssd_scan(xc, dt_raw, ld_dt, T, d->chunk, dt_bias, A_log, D, h0, h_final, y, y_dtype, batch,
-                           S(stream)),
+                           reinterpret_cast<uint16_t *>(ws), S(stream)),
            "ssd scan");
     return ok();
 }

@@ -62,9 +62,11 @@ hipError_t launch_to_f16(const uint16_t *x, uint16_t *xh, float *su, int M, int 
 // Y = Xh W^T (+ res); Xh holds fp16 bits, su the per-group row sums of Xh.
 hipError_t launch_w4_gemm(const W4 &W, const uint16_t *Xh, const float *su, int M,
                           const void *res, int res_t, void *Y, int y_t, hipStream_t st);
+// Workspace of the scan: the fp16 C.B^T tiles of every (sequence, chunk, group).
+size_t ssd_scan_ws_bytes(int batch, int T, int Q);
 hipError_t launch_ssd_scan(const uint16_t *xc, const uint16_t *dtr, long ld_dt, int T, int Q,
                            const float *dt_bias, const float *A_log, const float *D,
-                           const float *h0, float *hT, void *y, int y_t, int batch,
+                           const float *h0, float *hT, void *y, int y_t, int batch, uint16_t *Gws,
                            hipStream_t st);
 
 }  // namespace nh

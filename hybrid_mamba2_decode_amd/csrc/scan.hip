@@ -8,6 +8,14 @@
 //   S_out     = exp(cum_{L-1}) S_in + sum_j exp(cum_{L-1} - cum_j) dt_j x_j (outer) B_j
 //   y         = Y_off + Y_diag + D x
 //
+// C.B^T depends on the group only, so a pre-pass (k_ssd_cb) computes it once per (sequence,
+// chunk, group): bf16 matrix-core products of the bf16 inputs (exact products, fp32 sums),
+// stored as fp16 16 x 16 tiles of the causal lower triangle, tile (I, J <= I) at index
+// I(I+1)/2 + J, each in the lane order the scan reads it in (lane l = 16 q + i holds
+// G[16I + i][16J + 4q + r], r = 0..3), so a wave loads a tile with one 8-byte load per lane.
+// Workspace layout: chunk-major, then (sequence, group); a chunk of L rows holds
+// cb_tiles(L) tiles per (sequence, group), so the total is at most 4 KiB per position.
+//
 // Decomposition.  One work-group of 8 waves per (sequence, head) walks the chunks in order and
 // keeps the head's 80 x 128 fp32 state in registers as the accumulator of the state MFMA (wave
 // w owns state columns 16w .. 16w+15).  Work-group i runs on XCD i mod 8, so the 16 heads that
@@ -18,10 +26,11 @@
 //      row-major fp16 tiles; dt = softplus(dt_raw + dt_bias) and the log2-scaled cumulative
 //      sum of dt A (256-wide block scan); S_in as fp16;
 //   2. (after step 3) the next chunk's B, x, dt_raw and C rows are issued to registers;
-//   3. wave w takes 16-row output blocks {w, 15-w} (equal causal work): its C rows, already in
-//      registers, are the A operand of C S_in^T and the B operand of B C^T, whose D layout is
-//      exactly the A-operand layout that (G o decay) X needs, so the intra-chunk product never
-//      leaves registers;
+//   3. wave w takes 16-row output blocks {w, 15-w} (equal causal work) and computes them
+//      transposed, Y^T = S_in C^T + X^T (G o decay)^T: its C rows, already in registers, are the
+//      B operand of S_in C^T, and the block's G tiles come from the pre-pass in the B-operand
+//      layout, so the scaled tile never leaves registers; each lane ends with 4 consecutive
+//      columns of one output row (one 8-byte store per tile);
 //   4. each wave adds x^T (w B) to its state columns, w_j = exp(cum_{L-1} - cum_j) dt_j taken
 //      from an fp16 table and multiplied into the B fragment in registers (steps 3 and 4 only
 //      read LDS, so no barrier separates them).
@@ -46,15 +55,17 @@ constexpr int BS_LD = DSTATE + 16;  // B rows: 288 B (transposed reads conflict-
 constexpr int XS_LD = HDIM;         // x rows: 160 B (transposed reads conflict-free)
 constexpr int SI_LD = DSTATE + 8;   // S_in rows: 272 B
 
+// Member order keeps the tables, x and S_in below 64 KiB, so their reads take immediate
+// offsets from one base register.
 struct ScanSmem {
-    uint16_t Bs[QMAX * BS_LD];  // B of the chunk, [j][n]
-    uint16_t Xs[QMAX * XS_LD];  // x of the chunk, [j][p]; scaled by w_j before the state update
-    uint16_t Si[HDIM * SI_LD];  // state at chunk start, [p][n]
     float cum[QMAX];            // log2-scaled cumulative dt*A
     float dtv[QMAX];            // dt
     float Fv[QMAX];             // exp(cum_end(block of j) - cum_j) dt_j
     _Float16 Wh[QMAX];          // w_j = exp(cum_{L-1} - cum_j) dt_j (state-update weights)
     float wsum[4];
+    uint16_t Xs[QMAX * XS_LD];  // x of the chunk, [j][p]
+    uint16_t Si[HDIM * SI_LD];  // state at chunk start, [p][n]
+    uint16_t Bs[QMAX * BS_LD];  // B of the chunk, [j][n]
 };
 
 typedef short v4s __attribute__((ext_vector_type(4)));
@@ -102,6 +113,7 @@ constexpr int PB_VEC = QMAX * (DSTATE / 8) / SC_THREADS;  // 8 B vectors per thr
 constexpr int PX_VEC = QMAX * (HDIM / 8) / SC_THREADS;    // 5 x vectors per thread
 
 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
 {
@@ -116,13 +128,92 @@ struct Prefetch {
     uint32_t dt;
 };
 
+// ------------------------------------------------------------------ C.B^T pre-pass
+
+constexpr int CB_THREADS = 512;
+constexpr int CB_LD = DSTATE + 8;  // bf16 B rows in LDS: 272 B (16-byte row reads conflict-free)
+
+typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+
+__host__ __device__ constexpr int cb_tiles(int Q)
+{
+    return ((Q + 15) / 16) * ((Q + 15) / 16 + 1) / 2;
+}
+
+// first tile of (chunk ck of L rows, sequence b, group g)
+__device__ __forceinline__ size_t cb_base(int ck, int Q, int L, int batch, int b, int g)
+{
+    return ((size_t)ck * batch * NGROUPS * cb_tiles(Q) + (size_t)(b * NGROUPS + g) * cb_tiles(L)) * 256;
+}
+
+// One work-group per (chunk, group, sequence): B rows of the chunk to LDS; wave w takes row
+// blocks I = w and 15 - w (equal causal work when the chunk has 16 blocks) and for each J <= I
+// computes the tile D = B_J C_I^T (D lane layout: rows j = 16J + 4q + r, column
+// i = 16I + l16), which is the G layout the scan reads.
+__global__ __launch_bounds__(CB_THREADS) void k_ssd_cb(const uint16_t *__restrict__ xc, int T, int Q,
+                                                      uint16_t *__restrict__ Gw)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[QMAX * CB_LD];
+    const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, q4 = lane >> 4;
+    const int t0 = c * Q, L = min(Q, T - t0), nb = (L + 15) >> 4;
+    const uint32_t XROW = CONVDIM * 2;
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(xc + ((size_t)b * T + t0) * CONVDIM), 0, (int)((uint32_t)L * XROW), 0x00020000);
+
+    const int Ib[2] = {wave, 15 - wave};
+    uint4 cq[2][4];
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            cq[bi][ks] = bload16(rx, (uint32_t)(16 * Ib[bi] + l16) * XROW + (OFF_C + g * DSTATE + 32 * ks + 8 * q4) * 2, 0);
+    for (int v = tid; v < 16 * nb * 16; v += CB_THREADS) {
+        const int row = v >> 4, pc = v & 15;
+        *reinterpret_cast<uint4 *>(&Bs[row * CB_LD + 8 * pc]) =
+            bload16(rx, (uint32_t)row * XROW + (OFF_B + g * DSTATE + 8 * pc) * 2, 0);
+    }
+    __syncthreads();
+
+    uint16_t *Gc = Gw + cb_base(c, Q, L, gridDim.z, b, g) + lane * 4;
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi) {
+        const int I = Ib[bi];
+        if (I >= nb) continue;
+        uint16_t *gI = Gc + (I * (I + 1) / 2) * 256;
+        // two tiles per step: independent accumulation chains
+        for (int J = 0; J <= I; J += 2) {
+            const int J1 = min(J + 1, I);
+            floatx4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+            const uint16_t *s0 = &Bs[(16 * J + l16) * CB_LD + 8 * q4];
+            const uint16_t *s1 = &Bs[(16 * J1 + l16) * CB_LD + 8 * q4];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const bf16x8v cf = __builtin_bit_cast(bf16x8v, cq[bi][ks]);
+                a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8v, *reinterpret_cast<const uint4 *>(s0 + 32 * ks)), cf, a0, 0, 0, 0);
+                a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8v, *reinterpret_cast<const uint4 *>(s1 + 32 * ks)), cf, a1, 0, 0, 0);
+            }
+            *reinterpret_cast<uint2 *>(gI + J * 256) = make_uint2(pack_rne(a0[0], a0[1]), pack_rne(a0[2], a0[3]));
+            if (J + 1 <= I)
+                *reinterpret_cast<uint2 *>(gI + J1 * 256) = make_uint2(pack_rne(a1[0], a1[1]), pack_rne(a1[2], a1[3]));
+        }
+    }
+}
+
+// ------------------------------------------------------------------------- scan
+
 template <int YT>
 __global__ __launch_bounds__(SC_THREADS, 1) void k_ssd_scan(const uint16_t *__restrict__ xc,
                                                             const uint16_t *__restrict__ dtr, long ld_dt,
                                                             int T, int Q, const float *__restrict__ dt_bias,
                                                             const float *__restrict__ A_log,
                                                             const float *__restrict__ Dp, const float *h0,
-                                                            float *hT, void *__restrict__ y)
+                                                            float *hT, void *__restrict__ y,
+                                                            const uint16_t *__restrict__ Gw)
 {
     extern __shared__ __attribute__((aligned(16))) char smem_raw[];
     ScanSmem &sm = *reinterpret_cast<ScanSmem *>(smem_raw);
@@ -190,7 +281,7 @@ __global__ __launch_bounds__(SC_THREADS, 1) void k_ssd_scan(const uint16_t *__re
     Prefetch pf;
     prefetch(pf, 0);
 
-    for (int t0 = 0; t0 < T; t0 += Q) {
+    for (int t0 = 0, ck = 0; t0 < T; t0 += Q, ++ck) {
         const int L = min(Q, T - t0);
         const int LR = (L + 31) & ~31;
 
@@ -239,10 +330,19 @@ __global__ __launch_bounds__(SC_THREADS, 1) void k_ssd_scan(const uint16_t *__re
         // ---- 3. outputs of blocks I0, I1
         const int nblk = (L + 15) >> 4;
         const __amdgpu_buffer_rsrc_t ry = rsrc(yseq + (size_t)t0 * YROW, (uint32_t)L * YROW);
-#pragma unroll 1
+        const uint16_t *Gc = Gw + cb_base(ck, Q, L, gridDim.x / NHEADS, b, g) + lane * 4;
+#pragma unroll
         for (int bi = 0; bi < 2; ++bi) {
             const int I = bi == 0 ? I0 : I1;
             if (I >= nblk) continue;
+            // the block's G tiles J = 0..I, loaded three pairs ahead of their use (the first
+            // three while C S_in^T runs; loads past I re-read tile I and are unused)
+            const uint16_t *gI = Gc + (I * (I + 1) / 2) * 256;
+            uint2 gq[16];
+            auto gload = [&](int J) { gq[J] = *reinterpret_cast<const uint2 *>(gI + min(J, I) * 256); };
+#pragma unroll
+            for (int J = 0; J < 6; ++J) gload(J);
+            __builtin_amdgcn_sched_barrier(0);
             half8 cfb[4];
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
@@ -255,39 +355,36 @@ __global__ __launch_bounds__(SC_THREADS, 1) void k_ssd_scan(const uint16_t *__re
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks)
                     acc[pb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                        cfb[ks], ld_half8(&sm.Si[(16 * pb + l16) * SI_LD + 32 * ks + 8 * q4]), acc[pb], 0, 0, 0);
+                        ld_half8(&sm.Si[(16 * pb + l16) * SI_LD + 32 * ks + 8 * q4]), cfb[ks], acc[pb], 0, 0, 0);
             }
-            float ei[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) ei[r] = __builtin_amdgcn_exp2f(sm.cum[16 * I + 4 * q4 + r]);
+            // acc[pb][r] = Y^T[p = 16pb + 4q4 + r][i = ia]
+            const float ci = sm.cum[ia];
+            const float ei = __builtin_amdgcn_exp2f(ci);
 #pragma unroll
             for (int pb = 0; pb < 5; ++pb)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[pb][r] *= ei[r];
+                for (int r = 0; r < 4; ++r) acc[pb][r] *= ei;
 
-            const float ci = sm.cum[ia];
-            // G^T tile: gt[r] = G[i = ia][j = 16J + 4q4 + r]
-            auto gtile = [&](int J) {
-                floatx4 gt = {0.f, 0.f, 0.f, 0.f};
-                const uint16_t *src = &sm.Bs[(16 * J + l16) * BS_LD + 8 * q4];
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
-                    gt = __builtin_amdgcn_mfma_f32_16x16x32_f16(ld_half8(src + 32 * ks), cfb[ks], gt, 0, 0, 0);
-                return gt;
+            // gt[r] = G[i = ia][j = 16J + 4q4 + r]
+            auto gtile = [&](const uint2 gv) {
+                const half2v lo = __builtin_bit_cast(half2v, gv.x), hi = __builtin_bit_cast(half2v, gv.y);
+                return floatx4{(float)lo[0], (float)lo[1], (float)hi[0], (float)hi[1]};
             };
-            // below the diagonal: exp(cum_i - cum_j) = exp(cum_i - cum_end(J)) exp(cum_end(J) - cum_j)
-            auto offdiag = [&](int J, float *m) {
-                const floatx4 gt = gtile(J);
+            // below the diagonal: exp(cum_i - cum_j) = exp(cum_i - cum_end(J)) exp(cum_end(J) - cum_j);
+            // the factor is rounded to fp16 and multiplied into the fp16 tile (packed)
+            auto offdiag = [&](int J, const uint2 gv) {
                 const float eJ = __builtin_amdgcn_exp2f(ci - sm.cum[16 * J + 15]);
                 const float4 F = *reinterpret_cast<const float4 *>(&sm.Fv[16 * J + 4 * q4]);
-                m[0] = gt[0] * eJ * F.x;
-                m[1] = gt[1] * eJ * F.y;
-                m[2] = gt[2] * eJ * F.z;
-                m[3] = gt[3] * eJ * F.w;
+                const half2v f01 = __builtin_bit_cast(half2v, pack_rne(eJ * F.x, eJ * F.y));
+                const half2v f23 = __builtin_bit_cast(half2v, pack_rne(eJ * F.z, eJ * F.w));
+                const half2v m01 = __builtin_bit_cast(half2v, gv.x) * f01;
+                const half2v m23 = __builtin_bit_cast(half2v, gv.y) * f23;
+                return make_uint2(__builtin_bit_cast(uint32_t, m01), __builtin_bit_cast(uint32_t, m23));
             };
             // the diagonal block: causal mask j <= i, and the skip term D x_i on j == i
-            auto diag = [&](float *m) {
-                const floatx4 gt = gtile(I);
+            auto diag = [&](const uint2 gv) {
+                const floatx4 gt = gtile(gv);
+                float m[4];
                 const float4 cj = *reinterpret_cast<const float4 *>(&sm.cum[16 * I + 4 * q4]);
                 const float4 dj = *reinterpret_cast<const float4 *>(&sm.dtv[16 * I + 4 * q4]);
                 const float cja[4] = {cj.x, cj.y, cj.z, cj.w}, dja[4] = {dj.x, dj.y, dj.z, dj.w};
@@ -298,58 +395,49 @@ __global__ __launch_bounds__(SC_THREADS, 1) void k_ssd_scan(const uint16_t *__re
                     const float v = jl <= l16 ? gt[r] * e * dja[r] : 0.f;
                     m[r] = jl == l16 ? v + Dh : v;
                 }
+                return make_uint2(pack_rne(m[0], m[1]), pack_rne(m[2], m[3]));
             };
-            auto apply = [&](int jp, const float *m) {
-                const half8 mf = __builtin_bit_cast(half8, make_uint4(pack_rne(m[0], m[1]), pack_rne(m[2], m[3]),
-                                                                      pack_rne(m[4], m[5]), pack_rne(m[6], m[7])));
-                // B operand X[j][p] with j = 32jp + 4q4 + e (e < 4) and 32jp + 16 + 4q4 + (e - 4)
+            // m: the scaled tiles 2jp, 2jp + 1, B operand (column i, k = j); the A operand is
+            // X^T[p][j] with j = 32jp + 4q4 + e (e < 4) and 32jp + 16 + 4q4 + (e - 4)
+            auto apply = [&](int jp, const uint2 ma, const uint2 mb) {
+                const half8 mf = __builtin_bit_cast(half8, make_uint4(ma.x, ma.y, mb.x, mb.y));
 #pragma unroll
                 for (int pb = 0; pb < 5; ++pb) {
                     const half8 xf = cat(ld_tr(sm.Xs, XS_LD, 32 * jp + 4 * q4, 16 * pb),
                                          ld_tr(sm.Xs, XS_LD, 32 * jp + 16 + 4 * q4, 16 * pb));
-                    acc[pb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(mf, xf, acc[pb], 0, 0, 0);
+                    acc[pb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xf, mf, acc[pb], 0, 0, 0);
                 }
             };
-            // pairs of 16-column blocks strictly below the diagonal
-            for (int jp = 0; jp < I / 2; ++jp) {
-                float m[8];
-                offdiag(2 * jp, m);
-                offdiag(2 * jp + 1, m + 4);
-                apply(jp, m);
-            }
-            // the pair that holds the diagonal block
-            {
-                float m[8];
-                if (I & 1) {
-                    offdiag(I - 1, m);
-                    diag(m + 4);
-                } else {
-                    diag(m);
+            // pairs of 16-column blocks: strictly below the diagonal, then the pair holding it
+            // (unrolled so that every tile has its own registers; the scheduling barriers keep
+            // each pair's LDS reads inside its own step)
+            const int npair = I >> 1;
 #pragma unroll
-                    for (int r = 4; r < 8; ++r) m[r] = 0.f;
+            for (int jp = 0; jp < 8; ++jp) {
+                if (jp > npair) break;
+                if (jp + 3 < 8) {
+                    gload(2 * jp + 6);
+                    gload(2 * jp + 7);
                 }
-                apply(I >> 1, m);
+                if (jp < npair)
+                    apply(jp, offdiag(2 * jp, gq[2 * jp]), offdiag(2 * jp + 1, gq[2 * jp + 1]));
+                else if (I & 1)
+                    apply(jp, offdiag(2 * jp, gq[2 * jp]), diag(gq[2 * jp + 1]));
+                else
+                    apply(jp, diag(gq[2 * jp]), make_uint2(0u, 0u));
+                __builtin_amdgcn_sched_barrier(0);
             }
-            // store y = acc (the skip term is in the diagonal); neighbouring columns are paired
-            // across lanes for 2-column stores
+            // store y: row ia, columns 16pb + 4q4 .. +3 (the skip term is in the diagonal)
+            const uint32_t rowoff = (uint32_t)ia * YROW + (uint32_t)(h * HDIM + 4 * q4) * YB;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * I + 4 * q4 + r;
-                const uint32_t rowoff = (uint32_t)i * YROW + (uint32_t)(h * HDIM) * YB;
-#pragma unroll
-                for (int pb = 0; pb < 5; ++pb) {
-                    const int p = 16 * pb + l16;
-                    const float yv = acc[pb][r];
-                    const float yn = dpp_swap1(yv);
-                    if (!(l16 & 1)) {
-                        if (YT == BF16)
-                            __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(yv, yn), ry, rowoff + p * YB, 0, 0);
-                        else {
-                            typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
-                            const u32x2v w2 = {__float_as_uint(yv), __float_as_uint(yn)};
-                            __builtin_amdgcn_raw_buffer_store_b64(w2, ry, rowoff + p * YB, 0, 0);
-                        }
-                    }
+            for (int pb = 0; pb < 5; ++pb) {
+                if (YT == BF16) {
+                    const u32x2v w2 = {pack_bf16x2(acc[pb][0], acc[pb][1]), pack_bf16x2(acc[pb][2], acc[pb][3])};
+                    __builtin_amdgcn_raw_buffer_store_b64(w2, ry, rowoff + 16 * pb * YB, 0, 0);
+                } else {
+                    const u32x4v w4 = {__float_as_uint(acc[pb][0]), __float_as_uint(acc[pb][1]),
+                                       __float_as_uint(acc[pb][2]), __float_as_uint(acc[pb][3])};
+                    __builtin_amdgcn_raw_buffer_store_b128(w4, ry, rowoff + 16 * pb * YB, 0, 0);
                 }
             }
         }
@@ -385,11 +473,20 @@ __global__ __launch_bounds__(SC_THREADS, 1) void k_ssd_scan(const uint16_t *__re
     }
 }
 
+size_t ssd_scan_ws_bytes(int batch, int T, int Q)
+{
+    const int full = T / Q, last = T - full * Q;
+    const size_t tiles = (size_t)full * cb_tiles(Q) + (last ? cb_tiles(last) : 0);
+    return (size_t)batch * NGROUPS * tiles * 256 * sizeof(uint16_t);
+}
+
 hipError_t launch_ssd_scan(const uint16_t *xc, const uint16_t *dtr, long ld_dt, int T, int Q,
                            const float *dt_bias, const float *A_log, const float *D,
-                           const float *h0, float *hT, void *y, int y_t, int batch,
+                           const float *h0, float *hT, void *y, int y_t, int batch, uint16_t *Gws,
                            hipStream_t st)
 {
+    const int nch = (T + Q - 1) / Q;
+    k_ssd_cb<<<dim3(nch, NGROUPS, batch), CB_THREADS, 0, st>>>(xc, T, Q, Gws);
     const size_t smem = sizeof(ScanSmem);
     static bool attr_set[2] = {false, false};
     dim3 grid(batch * NHEADS), block(SC_THREADS);
@@ -400,7 +497,7 @@ hipError_t launch_ssd_scan(const uint16_t *xc, const uint16_t *dtr, long ld_dt, 
             if (e != hipSuccess) return e;
             attr_set[0] = true;
         }
-        k_ssd_scan<BF16><<<grid, block, smem, st>>>(xc, dtr, ld_dt, T, Q, dt_bias, A_log, D, h0, hT, y);
+        k_ssd_scan<BF16><<<grid, block, smem, st>>>(xc, dtr, ld_dt, T, Q, dt_bias, A_log, D, h0, hT, y, Gws);
     } else {
         if (!attr_set[1]) {
             hipError_t e = hipFuncSetAttribute((const void *)k_ssd_scan<F32>,
@@ -408,7 +505,7 @@ hipError_t launch_ssd_scan(const uint16_t *xc, const uint16_t *dtr, long ld_dt, 
             if (e != hipSuccess) return e;
             attr_set[1] = true;
         }
-        k_ssd_scan<F32><<<grid, block, smem, st>>>(xc, dtr, ld_dt, T, Q, dt_bias, A_log, D, h0, hT, y);
+        k_ssd_scan<F32><<<grid, block, smem, st>>>(xc, dtr, ld_dt, T, Q, dt_bias, A_log, D, h0, hT, y, Gws);
     }
     return hipGetLastError();
 }

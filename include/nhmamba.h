@@ -179,11 +179,18 @@ nh_status nh_ssm_step(const nh_mamba_dims *d, const uint16_t *xc, const uint16_t
  * xc: bf16 [batch][T][conv_dim]; dt_raw: bf16, row (b, t) at
  * dt_raw + (b*T + t)*ld_dt; h0: nullable f32 [batch][H][P][N] (NULL = zero
  * state); h_final: nullable, receives the state after position T-1 (may
- * alias h0); y: [batch][T][d_inner] of y_dtype. */
+ * alias h0); y: [batch][T][d_inner] of y_dtype.
+ * ws: caller-owned device workspace of at least
+ * nh_ssd_scan_workspace_bytes(d, batch, T) bytes (16-byte aligned), which
+ * receives the per-group C.B^T tiles of every chunk (at most 4 KiB per
+ * position); its contents on return are unspecified.  A smaller ws fails with
+ * NH_ERR_WORKSPACE_TOO_SMALL before any launch. */
+size_t nh_ssd_scan_workspace_bytes(const nh_mamba_dims *d, int batch, int T);
 nh_status nh_ssd_chunk_scan(const nh_mamba_dims *d, const uint16_t *xc, const uint16_t *dt_raw,
                             long ld_dt, int T, const float *dt_bias, const float *A_log,
                             const float *D, const float *h0, float *h_final, void *y,
-                            nh_dtype y_dtype, int batch, void *stream);
+                            nh_dtype y_dtype, int batch, void *ws, size_t ws_bytes,
+                            void *stream);
 
 /* Gated RMSNorm: g = y * silu(z); every block of `group` channels is
  * normalised by its own RMS (eps inside the root) and multiplied by its

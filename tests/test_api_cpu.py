@@ -109,7 +109,7 @@ def test_primitive_checks(nh):
     assert _status(lambda: nh.nh_conv1d_step(A, 16, A, A, A, A, 1, 16, 3, 0)) == nh.NH_ERR_UNSUPPORTED_SHAPE
     assert _status(lambda: nh.nh_conv1d_seq(A, 16, 4, A, A, A, A, A, 1, 16, 4, 0)) == nh.NH_ERR_INVALID_ARGUMENT
     assert _status(lambda: nh.nh_ssm_step(d, A, A, 128, A, A, A, A, A, 0, 0, 0)) == nh.NH_ERR_UNSUPPORTED_SHAPE
-    assert _status(lambda: nh.nh_ssd_chunk_scan(d, A, A, 22656, 0, A, A, A, None, None, A, 0, 1, 0)) == \
+    assert _status(lambda: nh.nh_ssd_chunk_scan(d, A, A, 22656, 0, A, A, A, None, None, A, 0, 1, A, 1 << 20, 0)) == \
         nh.NH_ERR_UNSUPPORTED_SHAPE
     assert _status(lambda: nh.nh_rmsnorm_gated(A, A, 10240, A, A, 1, 10240, 1000, 1e-5, 0)) == \
         nh.NH_ERR_UNSUPPORTED_SHAPE

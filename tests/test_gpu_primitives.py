@@ -222,6 +222,12 @@ def test_ssm_step_matches_oracle(env, B):
 
 # ----------------------------------------------------------------------- scan
 
+def _scan_ws(nh, gu, Q, B, T):
+    n = nh.nh_ssd_scan_workspace_bytes(nh.dims(chunk=Q), B, T)
+    assert 0 < n <= 4096 * B * T
+    return gu.workspace(n), n
+
+
 @pytest.mark.parametrize("T,Q,h0,B", [(1, 128, False, 1), (5, 4, True, 1), (16, 128, False, 1), (17, 16, True, 2),
                                       (40, 7, False, 1), (129, 128, True, 1), (300, 256, False, 1),
                                       (413, 128, False, 1), (413, 256, True, 2), (64, 1, False, 1)])
@@ -236,7 +242,7 @@ def test_scan_matches_recurrence(env, T, Q, h0, B):
     hT = gu.empty_f32(B, 128, 80, 128)
     nh.nh_ssd_chunk_scan(nh.dims(chunk=Q), gu.to_dev(xc), gu.to_dev(dtr), 128, T, gu.to_dev(lw.dt_bias),
                          gu.to_dev(lw.A_log), gu.to_dev(lw.D), None if S0 is None else gu.to_dev(S0), hT, y,
-                         nh.NH_F32, B)
+                         nh.NH_F32, B, *_scan_ws(nh, gu, Q, B, T))
     yg, Sg = y.cpu().numpy(), hT.cpu().numpy()
     for b in range(B):
         s0 = np.zeros((128, 80, 128)) if S0 is None else S0[b].astype(np.float64)
@@ -256,7 +262,7 @@ def test_scan_bf16_output_and_alias(env):
     Sd = gu.to_dev(S0)
     y = gu.empty_u16(1, T, 10240)
     nh.nh_ssd_chunk_scan(nh.dims(chunk=32), gu.to_dev(xc), gu.to_dev(dtr), 128, T, gu.to_dev(lw.dt_bias),
-                         gu.to_dev(lw.A_log), gu.to_dev(lw.D), Sd, Sd, y, nh.NH_BF16, 1)
+                         gu.to_dev(lw.A_log), gu.to_dev(lw.D), Sd, Sd, y, nh.NH_BF16, 1, *_scan_ws(nh, gu, 32, 1, T))
     ry, rS = _oracle_scan(oracle, gu, lw, xc[0], dtr[0], S0[0].astype(np.float64))
     assert gu.rel_l2(gu.bf16_bits_to_f64(gu.from_dev_u16(y)[0]), ry) < 4e-3
     assert gu.rel_l2(Sd.cpu().numpy()[0], rS) < 1e-3
@@ -275,7 +281,7 @@ def test_scan_stores_stay_inside_the_sequence(env, T, Q):
     buf = torch.full(((T + 2 * pad) * 10240,), 0x7E5A, dtype=torch.int16, device="cuda")
     y = buf[pad * 10240:(pad + T) * 10240]
     nh.nh_ssd_chunk_scan(nh.dims(chunk=Q), gu.to_dev(xc), gu.to_dev(dtr), 128, T, gu.to_dev(lw.dt_bias),
-                         gu.to_dev(lw.A_log), gu.to_dev(lw.D), None, None, y, nh.NH_BF16, 1)
+                         gu.to_dev(lw.A_log), gu.to_dev(lw.D), None, None, y, nh.NH_BF16, 1, *_scan_ws(nh, gu, Q, 1, T))
     torch.cuda.synchronize()
     host = buf.cpu().numpy()
     assert np.all(host[:pad * 10240] == 0x7E5A)
