@@ -68,6 +68,17 @@ __device__ __forceinline__ float silu(float v) { return v / (1.0f + __expf(-v));
 
 __device__ __forceinline__ float softplus(float v) { return fmaxf(v, 0.0f) + log1pf(__expf(-fabsf(v))); }
 
+// softplus with a short log1p: max(v, 0) + log1p(y), y = exp(-|v|) in (0, 1]; below 2^-6 a
+// 4-term series (truncation < y^5 / 5), above it the hardware logarithm of 1 + y (whose
+// argument is then >= 1.0156, so its absolute error is a small relative one).  About 1e-6
+// relative; used where dt is computed per position in bulk.
+__device__ __forceinline__ float softplus_fast(float v)
+{
+    const float y = __expf(-fabsf(v));
+    const float ser = y * (1.0f - y * (0.5f - y * (1.0f / 3.0f - 0.25f * y)));
+    return fmaxf(v, 0.0f) + (y < 0.015625f ? ser : __logf(1.0f + y));
+}
+
 __device__ __forceinline__ float wave_sum(float v)
 {
 #pragma unroll

@@ -92,10 +92,11 @@ __device__ __forceinline__ half8 cat(uint2 a, uint2 b)
     return __builtin_bit_cast(half8, make_uint4(a.x, a.y, b.x, b.y));
 }
 
-// value of the neighbouring lane (lanes 2k and 2k+1 swap)
-__device__ __forceinline__ float dpp_swap1(float v)
+// DPP move of v (lanes whose source is invalid or whose row is masked off read 0)
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f(float v)
 {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, false));
 }
 
 __device__ __forceinline__ uint32_t pack_rne(float a, float b)
@@ -149,7 +150,8 @@ __device__ __forceinline__ size_t cb_base(int ck, int Q, int L, int batch, int b
 // One work-group per (chunk, group, sequence): B rows of the chunk to LDS; wave w takes row
 // blocks I = w and 15 - w (equal causal work when the chunk has 16 blocks) and for each J <= I
 // computes the tile D = B_J C_I^T (D lane layout: rows j = 16J + 4q + r, column
-// i = 16I + l16), which is the G layout the scan reads.
+// i = 16I + l16), which is the G layout the scan reads.  Diagonal tiles hold 0 above the
+// diagonal (j > i): the causal mask.
 __global__ __launch_bounds__(CB_THREADS) void k_ssd_cb(const uint16_t *__restrict__ xc, int T, int Q,
                                                       uint16_t *__restrict__ Gw)
 {
@@ -197,6 +199,12 @@ __global__ __launch_bounds__(CB_THREADS) void k_ssd_cb(const uint16_t *__restric
                 a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                     __builtin_bit_cast(bf16x8v, *reinterpret_cast<const uint4 *>(s1 + 32 * ks)), cf, a1, 0, 0, 0);
             }
+            if (J == I)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) a0[r] = 4 * q4 + r > l16 ? 0.f : a0[r];
+            if (J1 == I)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) a1[r] = 4 * q4 + r > l16 ? 0.f : a1[r];
             *reinterpret_cast<uint2 *>(gI + J * 256) = make_uint2(pack_rne(a0[0], a0[1]), pack_rne(a0[2], a0[3]));
             if (J + 1 <= I)
                 *reinterpret_cast<uint2 *>(gI + J1 * 256) = make_uint2(pack_rne(a1[0], a1[1]), pack_rne(a1[2], a1[3]));
@@ -231,6 +239,10 @@ __global__ __launch_bounds__(SC_THREADS, 1) void k_ssd_scan(const uint16_t *__re
     const float A2 = -expf(A_log[h]) * LOG2E;  // dt*A in log2 units
     const float dtb = dt_bias[h];
     const float Dh = Dp[h];
+    // D on the diagonal of the diagonal tile: lane (i = l16, j = 4q4 + r) holds D where j == i
+    float dsel[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dsel[r] = 4 * q4 + r == l16 ? Dh : 0.f;
 
     // Rows of this sequence; a chunk's buffer resource starts at its first row.
     const uint32_t XROW = CONVDIM * 2, YROW = DINNER * YB, DROW = (uint32_t)ld_dt * 2;
@@ -288,15 +300,18 @@ __global__ __launch_bounds__(SC_THREADS, 1) void k_ssd_scan(const uint16_t *__re
         // ---- 1. chunk to LDS; discretisation, cumulative sum, decay table; S_in
         float dtt = 0.f, a = 0.f;
         if (tid < L) {
-            dtt = softplus(bf16_to_f32((uint16_t)pf.dt) + dtb);
+            dtt = softplus_fast(bf16_to_f32((uint16_t)pf.dt) + dtb);
             a = dtt * A2;
         }
+        // inclusive prefix sum over the wave: row shifts within 16-lane rows, then the row ends
+        // broadcast into the following rows
         float v = a;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const float nbv = __shfl_up(v, o, 64);
-            if (lane >= o) v += nbv;
-        }
+        v += dpp_f<0x111, 0xF>(v);  // row_shr:1
+        v += dpp_f<0x112, 0xF>(v);  // row_shr:2
+        v += dpp_f<0x114, 0xF>(v);  // row_shr:4
+        v += dpp_f<0x118, 0xF>(v);  // row_shr:8
+        v += dpp_f<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+        v += dpp_f<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
         if (lane == 63 && wave < 4) sm.wsum[wave] = v;
 #pragma unroll
         for (int i = 0; i < PB_VEC; ++i)
@@ -331,17 +346,16 @@ __global__ __launch_bounds__(SC_THREADS, 1) void k_ssd_scan(const uint16_t *__re
         const int nblk = (L + 15) >> 4;
         const __amdgpu_buffer_rsrc_t ry = rsrc(yseq + (size_t)t0 * YROW, (uint32_t)L * YROW);
         const uint16_t *Gc = Gw + cb_base(ck, Q, L, gridDim.x / NHEADS, b, g) + lane * 4;
-#pragma unroll
+#pragma unroll 1
         for (int bi = 0; bi < 2; ++bi) {
             const int I = bi == 0 ? I0 : I1;
             if (I >= nblk) continue;
             // the block's G tiles J = 0..I, loaded three pairs ahead of their use (the first
             // three while C S_in^T runs; loads past I re-read tile I and are unused)
             const uint16_t *gI = Gc + (I * (I + 1) / 2) * 256;
-            uint2 gq[16];
-            auto gload = [&](int J) { gq[J] = *reinterpret_cast<const uint2 *>(gI + min(J, I) * 256); };
-#pragma unroll
-            for (int J = 0; J < 6; ++J) gload(J);
+            auto gload = [&](int J) { return *reinterpret_cast<const uint2 *>(gI + min(J, I) * 256); };
+            // window of pairs jp, jp + 1, jp + 2
+            uint2 g0a = gload(0), g0b = gload(1), g1a = gload(2), g1b = gload(3), g2a = gload(4), g2b = gload(5);
             __builtin_amdgcn_sched_barrier(0);
             half8 cfb[4];
 #pragma unroll
@@ -381,7 +395,8 @@ __global__ __launch_bounds__(SC_THREADS, 1) void k_ssd_scan(const uint16_t *__re
                 const half2v m23 = __builtin_bit_cast(half2v, gv.y) * f23;
                 return make_uint2(__builtin_bit_cast(uint32_t, m01), __builtin_bit_cast(uint32_t, m23));
             };
-            // the diagonal block: causal mask j <= i, and the skip term D x_i on j == i
+            // the diagonal block (its tile is already 0 for j > i, where the clamped exponent
+            // keeps the factor finite), plus the skip term D x_i on j == i
             auto diag = [&](const uint2 gv) {
                 const floatx4 gt = gtile(gv);
                 float m[4];
@@ -389,12 +404,8 @@ __global__ __launch_bounds__(SC_THREADS, 1) void k_ssd_scan(const uint16_t *__re
                 const float4 dj = *reinterpret_cast<const float4 *>(&sm.dtv[16 * I + 4 * q4]);
                 const float cja[4] = {cj.x, cj.y, cj.z, cj.w}, dja[4] = {dj.x, dj.y, dj.z, dj.w};
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int jl = 4 * q4 + r;  // j - 16 I
-                    const float e = __builtin_amdgcn_exp2f(fminf(ci - cja[r], 0.f));
-                    const float v = jl <= l16 ? gt[r] * e * dja[r] : 0.f;
-                    m[r] = jl == l16 ? v + Dh : v;
-                }
+                for (int r = 0; r < 4; ++r)
+                    m[r] = gt[r] * __builtin_amdgcn_exp2f(fminf(ci - cja[r], 0.f)) * dja[r] + dsel[r];
                 return make_uint2(pack_rne(m[0], m[1]), pack_rne(m[2], m[3]));
             };
             // m: the scaled tiles 2jp, 2jp + 1, B operand (column i, k = j); the A operand is
@@ -408,25 +419,24 @@ __global__ __launch_bounds__(SC_THREADS, 1) void k_ssd_scan(const uint16_t *__re
                     acc[pb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xf, mf, acc[pb], 0, 0, 0);
                 }
             };
-            // pairs of 16-column blocks: strictly below the diagonal, then the pair holding it
-            // (unrolled so that every tile has its own registers; the scheduling barriers keep
-            // each pair's LDS reads inside its own step)
+            // pairs of 16-column blocks strictly below the diagonal
             const int npair = I >> 1;
-#pragma unroll
-            for (int jp = 0; jp < 8; ++jp) {
-                if (jp > npair) break;
-                if (jp + 3 < 8) {
-                    gload(2 * jp + 6);
-                    gload(2 * jp + 7);
-                }
-                if (jp < npair)
-                    apply(jp, offdiag(2 * jp, gq[2 * jp]), offdiag(2 * jp + 1, gq[2 * jp + 1]));
-                else if (I & 1)
-                    apply(jp, offdiag(2 * jp, gq[2 * jp]), diag(gq[2 * jp + 1]));
-                else
-                    apply(jp, diag(gq[2 * jp]), make_uint2(0u, 0u));
-                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll 1
+            for (int jp = 0; jp < npair; ++jp) {
+                const uint2 na = gload(2 * jp + 6), nb = gload(2 * jp + 7);
+                apply(jp, offdiag(2 * jp, g0a), offdiag(2 * jp + 1, g0b));
+                g0a = g1a;
+                g0b = g1b;
+                g1a = g2a;
+                g1b = g2b;
+                g2a = na;
+                g2b = nb;
             }
+            // the pair that holds the diagonal block
+            if (I & 1)
+                apply(npair, offdiag(I - 1, g0a), diag(g0b));
+            else
+                apply(npair, diag(g0a), make_uint2(0u, 0u));
             // store y: row ia, columns 16pb + 4q4 .. +3 (the skip term is in the diagonal)
             const uint32_t rowoff = (uint32_t)ia * YROW + (uint32_t)(h * HDIM + 4 * q4) * YB;
 #pragma unroll
