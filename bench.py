@@ -2,20 +2,24 @@
 """Benchmark of libnhmamba (the Nemotron-H Mamba2 mixer block) on one MI355X.
 
 Headline (the JSON line's `value`): the cached per-position block step at batch 1 with a
-pre-filled state (config 1), in microseconds per layer-step, against the HBM roofline.  The
+pre-filled state, in microseconds per layer-step, against the HBM roofline.  The
 timed loop rotates over `--copies` independent weight + state sets (8 x 93.7 MB by default,
 well beyond the 256 MB last-level cache), so every step streams its weights from HBM; a
 single-copy (cache-resident) figure is reported separately and labelled as such.
 
 Also measured in the same run, each in its own object of the JSON line:
-  * the chunked SSD scan at the config-4 shape (batch 2, T = 3750, chunk 256, 27 layers'
-    parameters), in position-layers per second against the matrix-core and HBM rooflines;
-  * the 27-layer stack stepwise over T = 413 (config 3) and the 27-layer full-history stack
-    at batch 2, T = 3750 (config 4);
-  * the CPU oracle on the host cores (a bounded sample of config 1), as a reported baseline.
+  * the chunked SSD scan at batch 2, T = 3750, chunk 256 (27 layers' parameters), in
+    position-layers per second against the matrix-core roofline (and the HBM one);
+  * the 27-layer stack stepwise over T = 413 at batch 1, and the 27-layer full-history
+    stack at batch 2, T = 3750, chunk 256;
+  * the CPU oracle on the host cores (a bounded sample of the batch-1 block step), as a
+    reported baseline.
 
-Per-kernel durations come from HIP events recorded around each kernel on the stream it runs
-on (the library's nh_profile_events hook for the three kernels of the block step).
+The roofline's kernel (the fused pre-norm / in_proj / conv step, 61% of the step's bytes) is
+timed alone: back-to-back launches of nh_inproj_conv_step over the same rotating copies, with
+two HIP events on the launch stream around the loop.  The per-kernel split of the block step
+comes from the library's nh_profile_events hook (an event recorded before each kernel, and
+one stamped at its end), so each of those figures also holds that kernel's dispatch.
 All inputs are seeded synthetic data (synth package); nothing is read from disk except the
 committed HBM-traffic counter summary under profiles/.
 """
@@ -119,17 +123,18 @@ def _source_sha(*names):
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(kernel: str, source: str):
+def traffic_from_profile(kernel: str, *sources: str):
     """HBM bytes per dispatch from the committed PMC summary, or None when absent or when
     the kernel's source changed after the counters were taken."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
     if not os.path.exists(path):
         return None
+    key = kernel.replace(" ", "")
     for line in open(path):
         f = line.split()
-        if len(f) >= 4 and f[0] == kernel:
+        if len(f) >= 4 and f[0] == key:
             sha, nbytes = f[1], float(f[2])
-            return nbytes if sha == _source_sha(source) else None
+            return nbytes if sha == _source_sha(*sources) else None
     return None
 
 
@@ -138,10 +143,10 @@ def traffic_from_profile(kernel: str, source: str):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=1000, help="timed block steps (config 1)")
+    ap.add_argument("--steps", type=int, default=1000, help="timed batch-1 block steps")
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--copies", type=int, default=8, help="rotating weight+state sets")
-    ap.add_argument("--skip-seq", action="store_true", help="skip the config-4 scan and stack")
+    ap.add_argument("--skip-seq", action="store_true", help="skip the batch-2 T=3750 scan and stack")
     ap.add_argument("--skip-stack", action="store_true", help="skip the 27-layer stacks")
     ap.add_argument("--skip-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -174,7 +179,7 @@ def main():
     d128 = nh.dims(chunk=128)
     out = {"metric": "Mamba2 block step us/layer (% HBM peak); SSD scan positions/s (% MFMA peak)"}
 
-    # ---------------------------------------------------------- config 1
+    # ------------------------------------- block step, batch 1, pre-filled state
     B = 1
     x1 = gu.to_dev(synth.block_input(1, B, 1)[:, 0])
     cs0, ss0 = synth.prefilled_state(1, B)
@@ -199,28 +204,45 @@ def main():
     wall_ms = (time.perf_counter() - t_wall) * 1e3
     ms_total = hip.ms(e0, e1)
     us_layer = ms_total * 1e3 / args.steps
-    log(f"config 1 step: {us_layer:.2f} us/layer ({args.copies} rotating copies), host wall {wall_ms:.1f} ms")
+    log(f"block step: {us_layer:.2f} us/layer ({args.copies} rotating copies), host wall {wall_ms:.1f} ms")
 
     # per-kernel durations of the block step (events between its three kernels)
     nprof = min(args.steps, 400)
-    evs = [[hip.event() for _ in range(4)] for _ in range(nprof)]
+    evs = [[hip.event() for _ in range(6)] for _ in range(nprof)]
     for i in range(nprof):
         nh.nh_profile_events(evs[i])
         step(i % args.copies)
     nh.nh_profile_events(None)
     torch.cuda.synchronize()
-    kt = np.array([[hip.ms(e[j], e[j + 1]) for j in range(3)] for e in evs]) * 1e3  # us
+    kt = np.array([[hip.ms(e[2 * j], e[2 * j + 1]) for j in range(3)] for e in evs]) * 1e3  # us
     k_avg = kt.mean(axis=0)
     k_med = np.median(kt, axis=0)
     for e in evs:
         for x in e:
             hip.destroy(x)
     kb = step_kernel_bytes(B)
-    names = ["k_inproj_step", "k_ssm_step<gnorm>", "k_gemv<5,1> (out_proj)"]
+    names = ["k_inproj_step<1, 0>", "k_ssm_step<true, 0>", "k_outproj_step<1>"]  # batch 1, bf16 input
     kernels = [{"kernel": names[j], "avg_us": round(float(k_avg[j]), 3), "median_us": round(float(k_med[j]), 3),
                 "algorithmic_bytes": int(kb[j]), "GBps": round(kb[j] / (k_avg[j] * 1e-6) / 1e9, 1),
                 "hbm_frac": round(kb[j] / (k_avg[j] * 1e-6) / HBM_PEAK, 4)} for j in range(3)]
     log("kernels:", kernels)
+
+    # the dominant kernel alone (fused pre-norm / in_proj / conv step): back-to-back launches
+    # over the same rotating weight + state copies, two events around the loop
+    zb, xcb, dtb = gu.empty_u16(B, DI), gu.empty_u16(B, CD), gu.empty_u16(B, H)
+
+    def inproj(i):
+        nh.nh_inproj_conv_step(d128, dev_layers[i], states[i][0], x1, nh.NH_BF16, zb, xcb, dtb, B, stream)
+
+    for i in range(args.warmup):
+        inproj(i % args.copies)
+    hip.record(e0, stream)
+    for i in range(args.steps):
+        inproj(i % args.copies)
+    hip.record(e1, stream)
+    torch.cuda.synchronize()
+    dom_us = hip.ms(e0, e1) * 1e3 / args.steps
+    log(f"k_inproj_step alone: {dom_us:.2f} us per launch")
 
     # cache-resident (single copy) figure, labelled
     for i in range(args.warmup):
@@ -238,8 +260,8 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(us_layer / 1e3, 6), "higher_is_better": False,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded; pages' shapes and distributions)",
-        "config": {"workload": "config 1: one Mamba2 block, batch 1, one cached decode step with a pre-filled "
-                               "state, 1000 timed repeats over rotating weight/state copies",
+        "config": {"workload": "one Mamba2 block (hidden 4480, 128 heads x 80, state 128), batch 1, one "
+                               "cached step with a pre-filled state, timed over rotating weight/state copies",
                    "batch": B, "hidden": HID, "heads": H, "head_dim": P, "d_state": N, "groups": G,
                    "weights": "W4 group-64 affine (in_proj 22656x4480, out_proj 4480x10240)",
                    "rotating_copies": args.copies},
@@ -251,13 +273,15 @@ def main():
     dom = 0
     out["roofline"] = {
         "kernel": names[dom], "bound": "hbm",
-        "achieved": round(kb[dom] / (k_avg[dom] * 1e-6) / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-        "frac": round(kb[dom] / (k_avg[dom] * 1e-6) / HBM_PEAK, 4),
-        "traffic": traffic_from_profile(names[dom], "step.hip"),
-        "bytes_per_launch": int(kb[dom]), "avg_launch_us": round(float(k_avg[dom]), 3),
+        "achieved": round(kb[dom] / (dom_us * 1e-6) / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+        "frac": round(kb[dom] / (dom_us * 1e-6) / HBM_PEAK, 4),
+        "traffic": traffic_from_profile(names[dom], "gemv.hip", "nh_device.hpp"),
+        "bytes_per_launch": int(kb[dom]), "avg_launch_us": round(dom_us, 3),
+        "timing": f"{args.steps} back-to-back launches over {args.copies} rotating weight/state copies, "
+                  "two HIP events on the launch stream",
     }
 
-    # ---------------------------------------------------------- config 3
+    # ------------------------------- 27-layer stack, batch 1, stepwise over T=413
     if not args.skip_stack:
         T3 = 413
         x3 = gu.to_dev(synth.block_input(3, 1, T3))
@@ -275,14 +299,14 @@ def main():
         torch.cuda.synchronize()
         ms3 = hip.ms(e0, e1)
         out["stack_step"] = {
-            "workload": "config 3: 27 Mamba2 blocks, batch 1, stepwise over T=413 carrying conv+SSM state",
+            "workload": "27 Mamba2 blocks, batch 1, stepwise over T=413 carrying conv+SSM state",
             "total_ms": round(ms3, 3), "us_per_layer_step": round(ms3 * 1e3 / (T3 * n_layers), 3),
             "hbm_frac": round(total_bytes / (ms3 * 1e-3 / (T3 * n_layers)) / HBM_PEAK, 4),
         }
-        log("config 3:", out["stack_step"])
+        log("stack steps:", out["stack_step"])
         del st3, outs3
 
-    # ---------------------------------------------------------- config 4
+    # ------------------------- scan and 27-layer stack, batch 2, T=3750, chunk 256
     if not args.skip_seq:
         B4, T4, Q4 = 2, 3750, 256
         d256 = nh.dims(chunk=Q4)
@@ -320,19 +344,20 @@ def main():
         fl = scan_flops_per_position(Q4)
         by = scan_bytes_per_position()
         out["scan"] = {
-            "workload": "config 4 scan: chunked SSD scan, batch 2, T=3750, chunk 256, 27 layers' parameters, "
-                        "3 rotating input sets",
+            "workload": "chunked SSD scan (C.B^T pre-pass + scan), batch 2, T=3750, chunk 256, 27 layers' "
+                        "parameters, 3 rotating input sets",
             "metric": "SSD scan positions/s", "value": round(pps, 1), "unit": "position-layers/s",
             "avg_launch_us": round(float(per.mean() * 1e3), 2),
             "mfma_frac": round(pps * fl / MFMA_F16_PEAK, 4),
             "hbm_frac": round(pps * by / HBM_PEAK, 4),
-            "roofline": {"kernel": "k_ssd_scan", "bound": "hbm", "achieved": round(pps * by / 1e9, 1),
-                         "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": round(pps * by / HBM_PEAK, 4),
-                         "traffic": traffic_from_profile("k_ssd_scan", "scan.hip"),
+            "roofline": {"kernel": "k_ssd_scan + k_ssd_cb", "bound": "mfma",
+                         "achieved": round(pps * fl / 1e12, 1), "peak": MFMA_F16_PEAK / 1e12, "unit": "TFLOP/s",
+                         "frac": round(pps * fl / MFMA_F16_PEAK, 4),
+                         "traffic": traffic_from_profile("k_ssd_scan", "scan.hip", "nh_device.hpp"),
                          "flops_per_position": round(fl), "bytes_per_position": by,
-                         "achieved_tflops": round(pps * fl / 1e12, 1), "mfma_peak_tflops": MFMA_F16_PEAK / 1e12},
+                         "achieved_GBps": round(pps * by / 1e9, 1), "hbm_peak_GBps": HBM_PEAK / 1e9},
         }
-        log("config 4 scan:", out["scan"])
+        log("scan:", out["scan"])
         del sets
 
         if not args.skip_stack:
@@ -355,11 +380,11 @@ def main():
             ms4 = hip.ms(e0, e1) / reps
             gemm_flops = 2 * pos * (NIN * HID + HID * DI) * n_layers
             out["stack_seq"] = {
-                "workload": "config 4: 27 Mamba2 blocks, batch 2, full-history T=3750, chunk 256",
+                "workload": "27 Mamba2 blocks, batch 2, full-history T=3750, chunk 256",
                 "ms": round(ms4, 2), "position_layers_per_s": round(pos * n_layers / (ms4 * 1e-3), 1),
                 "w4_gemm_tflops": round(gemm_flops / (ms4 * 1e-3) / 1e12, 1),
             }
-            log("config 4 stack:", out["stack_seq"])
+            log("stack seq:", out["stack_seq"])
             del outs4, ws4
 
     if args.calib_copy_mib > 0:
@@ -385,7 +410,7 @@ def main():
         out["cpu_baseline"] = {
             "value": round(t_cpu / reps * 1e6, 1), "unit": "us/layer", "cores": oracle.lib().nho_max_threads(),
             "kind": "oracle",
-            "sample": f"config 1 block step (batch 1, pre-filled state), fp64 oracle, {reps} repeats, "
+            "sample": f"one batch-1 block step with a pre-filled state, fp64 oracle, {reps} repeats, "
                       f"{t_cpu:.1f} s of host time",
         }
         log("cpu baseline:", out["cpu_baseline"])

@@ -33,11 +33,11 @@ NH_MODE_SEQ = 1
 
 # Entry points declared in include/nhmamba.h.
 EXPORTS = (
-    "nh_last_error", "nh_version", "nh_hybrid_pattern", "nh_w4_gemv", "nh_w4_gemm_workspace_bytes",
-    "nh_w4_gemm", "nh_rmsnorm", "nh_conv1d_step", "nh_conv1d_seq", "nh_ssm_step", "nh_ssd_scan_workspace_bytes",
-    "nh_ssd_chunk_scan",
+    "nh_last_error", "nh_version", "nh_hybrid_pattern", "nh_profile_events",
+    "nh_w4_gemv", "nh_w4_gemm_workspace_bytes", "nh_w4_gemm", "nh_rmsnorm", "nh_inproj_conv_step",
+    "nh_conv1d_step", "nh_conv1d_seq", "nh_ssm_step", "nh_ssd_scan_workspace_bytes", "nh_ssd_chunk_scan",
     "nh_rmsnorm_gated", "nh_block_workspace_bytes", "nh_mamba_block_step", "nh_mamba_block_seq",
-    "nh_mamba_stack", "nh_profile_events",
+    "nh_mamba_stack",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -83,6 +83,7 @@ _sigs = {
     "nh_w4_gemm_workspace_bytes": (_sz, [_i, _i]),
     "nh_w4_gemm": (_i, [_vp, _vp, _i, _vp, _i, _vp, _i, _vp, _sz, _vp]),
     "nh_rmsnorm": (_i, [_vp, _i, _vp, _vp, _i, _i, C.c_float, _vp]),
+    "nh_inproj_conv_step": (_i, [_vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _vp]),
     "nh_conv1d_step": (_i, [_vp, _l, _vp, _vp, _vp, _vp, _i, _i, _i, _vp]),
     "nh_conv1d_seq": (_i, [_vp, _l, _i, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp]),
     "nh_ssm_step": (_i, [_vp, _vp, _vp, _l, _vp, _vp, _vp, _vp, _vp, _i, _i, _vp]),
@@ -216,6 +217,11 @@ def nh_rmsnorm_gated(y, z, ld_z, w, out, rows, d, group, eps, stream=None):
 
 def nh_block_workspace_bytes(d, batch, T, mode) -> int:
     return lib.nh_block_workspace_bytes(C.byref(d), batch, T, mode)
+
+
+def nh_inproj_conv_step(d, w, state, x, x_dtype, z, xc, dt_raw, batch, stream=None):
+    _check(lib.nh_inproj_conv_step(C.byref(d), C.byref(w), C.byref(state), _ptr(x), x_dtype, _ptr(z), _ptr(xc),
+                                   _ptr(dt_raw), batch, _stream(stream)))
 
 
 def nh_mamba_block_step(d, w, state, x, x_dtype, out, out_dtype, batch, ws, ws_bytes, stream=None):

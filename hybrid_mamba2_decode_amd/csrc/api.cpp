@@ -16,13 +16,25 @@
 
 using namespace nh;
 
+namespace nh {
+ProfEvents &prof_next()
+{
+    static thread_local ProfEvents p;
+    return p;
+}
+}  // namespace nh
+
 namespace {
 
 thread_local std::string g_err;
-thread_local hipEvent_t g_prof_ev[4];
+thread_local hipEvent_t g_prof_ev[6];
 thread_local int g_prof_on = 0;
 
-hipError_t prof_mark(int i, hipStream_t s) { return g_prof_on ? hipEventRecord(g_prof_ev[i], s) : hipSuccess; }
+// arm the start/stop events of the step's kernel i (0 in_proj, 1 SSM, 2 out_proj)
+void prof_arm(int i)
+{
+    if (g_prof_on) prof_next() = ProfEvents{g_prof_ev[2 * i], g_prof_ev[2 * i + 1]};
+}
 
 nh_status fail(nh_status s, const char *fmt, ...)
 {
@@ -209,18 +221,18 @@ nh_status block_step(const nh_mamba_dims *d, const nh_mamba_weights *w, nh_mamba
 {
     size_t nb;
     StepWs k = carve_step(ws, B, &nb);
-    NH_HIP(prof_mark(0, s), "profile event");
+    prof_arm(0);
     NH_HIP(launch_inproj_step(view(&w->in_proj), x, x_t, w->norm_w, d->eps, B, k.z, k.xc, k.dtr,
                               st->conv_state, w->conv_w, w->conv_b, nullptr, 0, s),
            "in_proj step");
-    NH_HIP(prof_mark(1, s), "profile event");
+    prof_arm(1);
     NH_HIP(launch_ssm_step_part(k.xc, k.dtr, NHEADS, w->dt_bias, w->A_log, w->D, st->ssm_state, k.y, k.z,
                                 k.part, B, s),
            "ssm step");
-    NH_HIP(prof_mark(2, s), "profile event");
+    prof_arm(2);
     NH_HIP(launch_outproj_step(view(&w->out_proj), k.y, k.z, w->gnorm_w, k.part, d->eps, B, x, x_t, out, out_t, s),
            "out_proj step");
-    NH_HIP(prof_mark(3, s), "profile event");
+    prof_next() = ProfEvents{};
     return ok();
 }
 
@@ -281,8 +293,8 @@ nh_status nh_profile_events(void *const *events, int n)
         g_prof_on = 0;
         return ok();
     }
-    if (n < 4) return fail(NH_ERR_INVALID_ARGUMENT, "need 4 events, got %d", n);
-    for (int i = 0; i < 4; ++i) {
+    if (n < 6) return fail(NH_ERR_INVALID_ARGUMENT, "need 6 events, got %d", n);
+    for (int i = 0; i < 6; ++i) {
         if (!events[i]) return fail(NH_ERR_INVALID_ARGUMENT, "event %d is NULL", i);
         g_prof_ev[i] = reinterpret_cast<hipEvent_t>(events[i]);
     }
@@ -480,6 +492,27 @@ nh_status nh_mamba_block_step(const nh_mamba_dims *d, const nh_mamba_weights *w,
     const size_t need = step_bytes(batch);
     if (ws_bytes < need) return fail(NH_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
     return block_step(d, w, state, x, x_dtype, out, out_dtype, batch, ws, S(stream));
+}
+
+nh_status nh_inproj_conv_step(const nh_mamba_dims *d, const nh_mamba_weights *w, nh_mamba_state *state,
+                              const void *x, nh_dtype x_dtype, uint16_t *z, uint16_t *xc, uint16_t *dt_raw,
+                              int batch, void *stream)
+{
+    NH_TRY(check_dims(d, false));
+    NH_TRY(check_weights(w));
+    NH_TRY(check_state(state, "state", true));
+    NH_TRY(need_ptr(x, "x"));
+    NH_TRY(need_ptr(z, "z"));
+    NH_TRY(need_ptr(xc, "xc"));
+    NH_TRY(need_ptr(dt_raw, "dt_raw"));
+    NH_TRY(need_dtype(x_dtype, "x_dtype"));
+    if (batch < 1 || batch > 4) return fail(NH_ERR_UNSUPPORTED_SHAPE, "batch %d outside 1..4", batch);
+    if (x == (const void *)z || x == (const void *)xc || x == (const void *)dt_raw)
+        return fail(NH_ERR_INVALID_ARGUMENT, "outputs may not alias x");
+    NH_HIP(launch_inproj_step(view(&w->in_proj), x, x_dtype, w->norm_w, d->eps, batch, z, xc, dt_raw,
+                              state->conv_state, w->conv_w, w->conv_b, nullptr, 0, S(stream)),
+           "in_proj step");
+    return ok();
 }
 
 nh_status nh_mamba_block_seq(const nh_mamba_dims *d, const nh_mamba_weights *w, const nh_mamba_state *init,

@@ -262,7 +262,7 @@ struct GemvRunner {
     static constexpr int ROWS = RG * RPG;  // rows per wave per stage
     const W4 W;
     const Epi epi;
-    int sub, li, er, eb, stride, n0;
+    int sub, li, er, eb, stride, n0, nlim;
     uint32_t rowbytes, kg2, qoff[CPL], soff[CPL];
     __amdgpu_buffer_rsrc_t rq, rs, rb;
     Stage<RG, CPL> A, B;
@@ -273,10 +273,17 @@ struct GemvRunner {
         const int lane = threadIdx.x & 63;
         sub = lane / LPR;
         li = lane % LPR;
-        // waves numbered across work-groups first, so the leftover rows of an uneven split land
-        // one per work-group instead of piling onto the first work-groups
-        const int wave = __builtin_amdgcn_readfirstlane((int)((threadIdx.x >> 6) * gridDim.x + blockIdx.x));
-        const int nwaves = gridDim.x * (blockDim.x >> 6);
+        // Rows are split into one contiguous slab per XCD (work-group i runs on XCD i mod 8), so
+        // the cache lines that neighbouring rows share (row boundaries of the packed weights and
+        // of the 140-byte scale rows) are fetched by one L2 only.  Inside a slab the XCD's waves
+        // are numbered across work-groups first, so the leftover rows of an uneven split land one
+        // per work-group.
+        const int nx = (gridDim.x & 7) == 0 ? 8 : 1;
+        const int xcd = blockIdx.x % nx;
+        const int wave = __builtin_amdgcn_readfirstlane(
+            (int)((threadIdx.x >> 6) * (gridDim.x / nx) + blockIdx.x / nx));
+        const int nwaves = (gridDim.x / nx) * (blockDim.x >> 6);
+        const int slab = (((W.n + nx - 1) / nx + ROWS - 1) / ROWS) * ROWS;
         const int nch = W.k >> 5;
         rowbytes = (uint32_t)W.k / 2;
         kg2 = (uint32_t)(W.k >> 6) * 2;
@@ -292,8 +299,9 @@ struct GemvRunner {
         er = min(li / NB, RG - 1);
         eb = li % NB;
         stride = nwaves * ROWS;
-        n0 = wave * ROWS;
-        if (n0 < W.n) {
+        n0 = xcd * slab + wave * ROWS;
+        nlim = min(W.n, (xcd + 1) * slab);
+        if (n0 < nlim) {
             load_stage<RG, CPL>(A, rq, rs, rb, qoff, soff, (uint32_t)n0, RPG, rowbytes, kg2);
             pa = epi.prefetch(min(n0 + er * RPG + sub, W.n - 1), eb);
         }
@@ -302,22 +310,22 @@ struct GemvRunner {
     __device__ __forceinline__ void run(const ActChunk (&a)[NB][CPL])
     {
         const uint32_t mlo = 0x000F000Fu, mhi = 0x00F000F0u, magic = 0x64006400u;
-        if (n0 >= W.n) return;
+        if (n0 >= nlim) return;
         while (true) {
             const int n1 = n0 + stride;
-            if (n1 < W.n) {
+            if (n1 < nlim) {
                 load_stage<RG, CPL>(B, rq, rs, rb, qoff, soff, (uint32_t)n1, RPG, rowbytes, kg2);
                 pb = epi.prefetch(min(n1 + er * RPG + sub, W.n - 1), eb);
             }
-            compute_stage<LPR, CPL, NB, RG>(A, a, epi, pa, n0 + sub, W.n, li, mlo, mhi, magic);
-            if (n1 >= W.n) break;
+            compute_stage<LPR, CPL, NB, RG>(A, a, epi, pa, n0 + sub, nlim, li, mlo, mhi, magic);
+            if (n1 >= nlim) break;
             const int n2 = n1 + stride;
-            if (n2 < W.n) {
+            if (n2 < nlim) {
                 load_stage<RG, CPL>(A, rq, rs, rb, qoff, soff, (uint32_t)n2, RPG, rowbytes, kg2);
                 pa = epi.prefetch(min(n2 + er * RPG + sub, W.n - 1), eb);
             }
-            compute_stage<LPR, CPL, NB, RG>(B, a, epi, pb, n1 + sub, W.n, li, mlo, mhi, magic);
-            if (n2 >= W.n) break;
+            compute_stage<LPR, CPL, NB, RG>(B, a, epi, pb, n1 + sub, nlim, li, mlo, mhi, magic);
+            if (n2 >= nlim) break;
             n0 = n2;
         }
     }
@@ -542,10 +550,10 @@ hipError_t launch_outproj_step(const W4 &W, const uint16_t *y, const uint16_t *z
     // one work-group per CU: 8 waves at batch 1; 4 waves (more registers each) above
     const int grid = min(cu_count(), (W.n + 7) / 8);
     switch (batch) {
-    case 1: k_outproj_step<1><<<dim3(grid), dim3(512), lds, st>>>(W, y, z, gw, part, eps, e); break;
-    case 2: k_outproj_step<2><<<dim3(grid), dim3(256), lds, st>>>(W, y, z, gw, part, eps, e); break;
-    case 3: k_outproj_step<3><<<dim3(grid), dim3(256), lds, st>>>(W, y, z, gw, part, eps, e); break;
-    default: k_outproj_step<4><<<dim3(grid), dim3(256), lds, st>>>(W, y, z, gw, part, eps, e); break;
+    case 1: launch_k(k_outproj_step<1>, dim3(grid), dim3(512), lds, st, W, y, z, gw, part, eps, e); break;
+    case 2: launch_k(k_outproj_step<2>, dim3(grid), dim3(256), lds, st, W, y, z, gw, part, eps, e); break;
+    case 3: launch_k(k_outproj_step<3>, dim3(grid), dim3(256), lds, st, W, y, z, gw, part, eps, e); break;
+    default: launch_k(k_outproj_step<4>, dim3(grid), dim3(256), lds, st, W, y, z, gw, part, eps, e); break;
     }
     return hipGetLastError();
 }
@@ -562,9 +570,11 @@ hipError_t launch_inproj_step(const W4 &W, const void *x, int x_t, const uint16_
     {                                                                                                      \
         const int grid = gemv_grid(W.n, (NB == 1 ? 2 : 1), NB == 1 ? 3 : 1);                                \
         if (x_t == BF16)                                                                                   \
-            k_inproj_step<NB, BF16><<<dim3(grid), dim3(256), lds, st>>>(W, x, norm_w, eps, e, zero_ptr, nzero); \
+            launch_k(k_inproj_step<NB, BF16>, dim3(grid), dim3(256), lds, st, W, x, norm_w, eps, e, zero_ptr, \
+                     nzero);                                                                               \
         else                                                                                               \
-            k_inproj_step<NB, F32><<<dim3(grid), dim3(256), lds, st>>>(W, x, norm_w, eps, e, zero_ptr, nzero);  \
+            launch_k(k_inproj_step<NB, F32>, dim3(grid), dim3(256), lds, st, W, x, norm_w, eps, e, zero_ptr,  \
+                     nzero);                                                                               \
     }
     switch (batch) {
     case 1: NH_LAUNCH(1); break;

@@ -1,11 +1,34 @@
 // nh_kernels.hpp -- host-side launchers of the libnhmamba kernels (internal).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace nh {
+
+// Profiling hook: start/stop events for the next kernel launch of this thread.  When set, the
+// start event is recorded on the stream just before the launch (it completes once the
+// preceding work has finished) and the launch goes through hipExtLaunchKernelGGL with the
+// stop event, which is stamped at the kernel's own end; the slot is then cleared.
+struct ProfEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+ProfEvents &prof_next();
+
+template <typename... P, typename... Args>
+inline void launch_k(void (*k)(P...), dim3 grid, dim3 block, uint32_t lds, hipStream_t st, Args... args)
+{
+    ProfEvents &p = prof_next();
+    if (p.start) {
+        hipEventRecord(p.start, st);
+        hipExtLaunchKernelGGL(k, grid, block, lds, st, nullptr, p.stop, 0, static_cast<P>(args)...);
+        p = ProfEvents{};
+    } else {
+        hipLaunchKernelGGL(k, grid, block, lds, st, static_cast<P>(args)...);
+    }
+}
 
 enum DT { BF16 = 0, F32 = 1 };
 

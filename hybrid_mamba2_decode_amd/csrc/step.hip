@@ -129,7 +129,7 @@ hipError_t launch_ssm_step_part(const uint16_t *xc, const uint16_t *dtr, long ld
                                 hipStream_t st)
 {
     dim3 grid(batch * NHEADS * 2), block(256);
-    k_ssm_step<true, BF16><<<grid, block, 0, st>>>(xc, dtr, ld_dt, dt_bias, A_log, D, S, y_ws, z, part);
+    launch_k(k_ssm_step<true, BF16>, grid, block, 0, st, xc, dtr, ld_dt, dt_bias, A_log, D, S, y_ws, z, part);
     return hipGetLastError();
 }
 

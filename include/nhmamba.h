@@ -111,12 +111,14 @@ const char *nh_version(void);
 /* The hybrid_override_pattern of text_config: 'M' Mamba2, '*' attention, '-' MLP. */
 const char *nh_hybrid_pattern(void);
 
-/* Measurement hook.  events: NULL (off) or an array of n >= 4 hipEvent_t
+/* Measurement hook.  events: NULL (off) or an array of n >= 6 hipEvent_t
  * created by the caller.  While set, every nh_mamba_block_step call on this
- * thread records events[0] before its first kernel and events[i] after its
- * i-th kernel (i = 1..3: fused pre-norm/in_proj/conv, SSM step + gated norm,
- * out_proj + residual) on the call's stream, so the caller can read each
- * kernel's duration with hipEventElapsedTime. */
+ * thread records events[2i] on its stream right before kernel i (0: fused
+ * pre-norm/in_proj/conv, 1: SSM step + gated-norm partial sums, 2: gated
+ * norm/out_proj/residual) and launches that kernel with events[2i+1] stamped
+ * at its own end (hipExtLaunchKernelGGL), so hipEventElapsedTime(events[2i],
+ * events[2i+1]) is the kernel's duration plus its dispatch.  Returns NH_ERR_INVALID_ARGUMENT for n < 6 or a
+ * NULL event. */
 nh_status nh_profile_events(void *const *events, int n);
 
 /* ---------------------------------------------------------- primitives */
@@ -142,6 +144,19 @@ nh_status nh_w4_gemm(const nh_w4_matrix *W, const uint16_t *X, int M,
  * RMS over the d values of a row, eps inside the square root. */
 nh_status nh_rmsnorm(const void *x, nh_dtype x_dtype, const uint16_t *w, uint16_t *u,
                      int rows, int d, float eps, void *stream);
+
+/* The front of one block step as one fused kernel: u = RMSNorm(x) * norm_w
+ * (bf16), zxbcdt = in_proj(u) (W4 GEMV, fp32 sums), split into z | xBC | dt_raw
+ * (Nemotron-H issue page, section "config.json": d_inner 10240, 8 groups x
+ * state 128, 128 heads); xBC goes through the conv step (as nh_conv1d_step,
+ * state shifted in place) and SiLU.  x: [batch][hidden] of x_dtype; outputs
+ * bf16: z [batch][d_inner], xc [batch][conv_dim] (x | B | C after conv and
+ * SiLU), dt_raw [batch][n_heads].  Uses w->norm_w, in_proj, conv_w, conv_b
+ * and state->conv_state only.  batch 1..4; outputs may not alias x. */
+nh_status nh_inproj_conv_step(const nh_mamba_dims *d, const nh_mamba_weights *w,
+                              nh_mamba_state *state, const void *x, nh_dtype x_dtype,
+                              uint16_t *z, uint16_t *xc, uint16_t *dt_raw, int batch,
+                              void *stream);
 
 /* One position of the causal depthwise conv1d (kernel k, with bias) + SiLU.
  * xbc: bf16, row b at xbc + b*ld (channels values); conv_state: bf16

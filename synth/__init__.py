@@ -22,8 +22,8 @@ Distributions (the workload recipe, identical for every consumer):
   pre-filled SSM state ~ N(0, 0.1^2) (float32).
 
 Random streams: numpy PCG64 seeded by SeedSequence([seed, layer, tensor_id])
-for weights and SeedSequence([seed, 1000 + config, tensor_id]) for inputs, so
-any tensor can be regenerated on its own.
+for weights and SeedSequence([seed, 1000 + stream, tensor_id]) for inputs (stream: a
+small integer naming the input draw), so any tensor can be regenerated on its own.
 """
 from __future__ import annotations
 
@@ -148,17 +148,17 @@ def layer_weights(layer: int, seed: int = 0, d: Dims = REAL) -> LayerWeights:
     return LayerWeights(norm_w, in_proj, conv_w, conv_b, dt_bias, A_log, D, gnorm_w, out_proj)
 
 
-def block_input(config: int, batch: int, T: int, seed: int = 0, d: Dims = REAL) -> np.ndarray:
+def block_input(stream: int, batch: int, T: int, seed: int = 0, d: Dims = REAL) -> np.ndarray:
     """x ~ N(0, 1) rounded to bf16, layout [batch][T][hidden] (uint16 bits)."""
-    x = rng(seed, 1000 + config, _I_X).normal(0.0, 1.0, (batch, T, d.hidden)).astype(np.float32)
+    x = rng(seed, 1000 + stream, _I_X).normal(0.0, 1.0, (batch, T, d.hidden)).astype(np.float32)
     return f32_to_bf16(x)
 
 
-def prefilled_state(config: int, batch: int, seed: int = 0, d: Dims = REAL):
+def prefilled_state(stream: int, batch: int, seed: int = 0, d: Dims = REAL):
     """Pre-filled decode state: conv [batch][K-1][conv_dim] bf16 ~ N(0,1), SSM [batch][H][P][N] f32 ~ N(0, 0.1^2)."""
-    cs = rng(seed, 1000 + config, _I_CONV_STATE).normal(
+    cs = rng(seed, 1000 + stream, _I_CONV_STATE).normal(
         0.0, 1.0, (batch, d.conv_k - 1, d.conv_dim)).astype(np.float32)
-    ss = rng(seed, 1000 + config, _I_SSM_STATE).normal(
+    ss = rng(seed, 1000 + stream, _I_SSM_STATE).normal(
         0.0, 0.1, (batch, d.n_heads, d.head_dim, d.d_state)).astype(np.float32)
     return f32_to_bf16(cs), ss
 

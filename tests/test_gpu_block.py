@@ -6,8 +6,8 @@ fp32 block output before any output rounding (a bf16 output near |4| has a unit 
 place of 0.03125, so a single rounding-boundary flip would break max-abs 3e-2 on bf16 bits);
 the fp32 SSM state rel-L2 <= 1e-3.  The bf16 output is also checked by rel-L2 and its
 rounding flips are counted.
-Workloads: one block with seeded synthetic weights (the layer-0 draw), batch 1, T = 16 both
-ways (config 0), one prefilled step (config 1), T = 413 with chunk 128 (config 2)."""
+Workloads: one block with seeded synthetic weights (the layer-0 draw): batch 1, T = 16 both
+ways; one step from a prefilled state; batch 1, T = 413 with chunk 128."""
 import numpy as np
 import pytest
 
@@ -45,9 +45,9 @@ def _check_state(gu, got, ref, what):
     assert r <= STATE_REL, r
 
 
-def test_block_step_prefilled_config1(env):
+def test_block_step_prefilled_b1(env):
     nh, oracle, gu, torch, lw, W = env
-    _say("block step, config 1")
+    _say("block step, batch 1, prefilled state")
     B = 1
     x = synth.block_input(1, B, 1)
     cs0, ss0 = synth.prefilled_state(1, B)
@@ -58,11 +58,38 @@ def test_block_step_prefilled_config1(env):
     nh.nh_mamba_block_step(d, W, st, gu.to_dev(x[:, 0]), nh.NH_BF16, out, nh.NH_F32, B, ws, ws.numel())
     ref = oracle.block(synth.REAL, lw, gu.bf16_bits_to_f64(x), gu.bf16_bits_to_f64(cs0), ss0,
                        mode=oracle.CONTRACT, stepwise=True)
-    _check_out(gu, out.cpu().numpy(), ref.out[:, 0], "step c1")
-    _check_state(gu, ssd.cpu().numpy(), ref.ssm_state, "step c1")
+    _check_out(gu, out.cpu().numpy(), ref.out[:, 0], "step b1")
+    _check_state(gu, ssd.cpu().numpy(), ref.ssm_state, "step b1")
     cs_got = gu.bf16_bits_to_f64(gu.from_dev_u16(csd))
     assert np.array_equal(cs_got[:, :2], gu.bf16_bits_to_f64(cs0)[:, 1:])   # shifted rows are copies
     assert gu.rel_l2(cs_got, ref.conv_state) < 4e-3                     # new row: bf16 in_proj output
+
+
+@pytest.mark.parametrize("B", [1, 2])
+def test_inproj_conv_step_matches_oracle(env, B):
+    """The fused front of the step (pre-norm, in_proj, split, conv step + SiLU) against the
+    oracle's storage points of the same step (z and dt_raw from zxbcdt, xc after the conv)."""
+    nh, oracle, gu, torch, lw, W = env
+    _say("in_proj + conv step, batch", B)
+    x = synth.block_input(11, B, 1)
+    cs0, ss0 = synth.prefilled_state(11, B)
+    st, csd, ssd = gu.state_dev(cs0, ss0)
+    z, xc, dtr = gu.empty_u16(B, 10240), gu.empty_u16(B, synth.CONV_DIM), gu.empty_u16(B, 128)
+    nh.nh_inproj_conv_step(nh.dims(), W, st, gu.to_dev(x[:, 0]), nh.NH_BF16, z, xc, dtr, B)
+    ref = oracle.block(synth.REAL, lw, gu.bf16_bits_to_f64(x), gu.bf16_bits_to_f64(cs0), ss0,
+                       mode=oracle.CONTRACT, stepwise=True, debug=True)
+    zx = ref.debug["zxbcdt"][:, 0]
+    for name, got, want in [("z", z, zx[:, :10240]), ("dt_raw", dtr, zx[:, 22528:]),
+                            ("xc", xc, ref.debug["xc"][:, 0])]:
+        g = gu.bf16_bits_to_f64(gu.from_dev_u16(got))
+        r = gu.rel_l2(g, want)
+        print(f"[inproj step b{B}] {name} rel-L2 {r:.3e} flips {gu.bf16_ulp_flips(gu.from_dev_u16(got), want)}",
+              flush=True)
+        assert r < 4e-3, (name, r)
+    cs_got = gu.bf16_bits_to_f64(gu.from_dev_u16(csd))
+    assert np.array_equal(cs_got[:, :2], gu.bf16_bits_to_f64(cs0)[:, 1:])
+    assert gu.rel_l2(cs_got, ref.conv_state) < 4e-3
+    assert np.array_equal(ssd.cpu().numpy(), ss0)                         # the SSM state is not touched
 
 
 def test_block_step_batch2_bf16_out(env):
@@ -86,9 +113,9 @@ def test_block_step_batch2_bf16_out(env):
 
 
 @pytest.mark.parametrize("Q", [128, 4, 8])
-def test_block_seq_and_step_config0(env, Q):
+def test_block_seq_and_step_b1_t16(env, Q):
     nh, oracle, gu, torch, lw, W = env
-    _say("block config 0, Q", Q)
+    _say("block batch 1, T=16, Q", Q)
     B, T = 1, 16
     x = synth.block_input(0, B, T)
     xf = gu.bf16_bits_to_f64(x)
@@ -100,8 +127,8 @@ def test_block_seq_and_step_config0(env, Q):
     out = gu.empty_f32(B, T, 4480)
     nh.nh_mamba_block_seq(d, W, None, fin, gu.to_dev(x), nh.NH_BF16, T, out, nh.NH_F32, B, ws, ws.numel())
     seq_out = out.cpu().numpy()
-    _check_out(gu, seq_out, ref.out, f"seq c0 Q={Q}")
-    _check_state(gu, fss.cpu().numpy(), ref.ssm_state, f"seq c0 Q={Q}")
+    _check_out(gu, seq_out, ref.out, f"seq t16 Q={Q}")
+    _check_state(gu, fss.cpu().numpy(), ref.ssm_state, f"seq t16 Q={Q}")
     assert gu.rel_l2(gu.bf16_bits_to_f64(gu.from_dev_u16(fcs)), ref.conv_state) < 4e-3
     # cached per-position steps from zero state
     st, csd, ssd = gu.state_dev(np.zeros((B, 3, synth.CONV_DIM), np.uint16), np.zeros((B, 128, 80, 128), np.float32))
@@ -112,15 +139,15 @@ def test_block_seq_and_step_config0(env, Q):
     for t in range(T):
         nh.nh_mamba_block_step(d, W, st, xd[:, t].contiguous(), nh.NH_BF16, o1, nh.NH_F32, B, wss, wss.numel())
         step_out[:, t] = o1.cpu().numpy()
-    _check_out(gu, step_out, ref.out, "step c0")
-    _check_state(gu, ssd.cpu().numpy(), ref.ssm_state, "step c0")
+    _check_out(gu, step_out, ref.out, "step t16")
+    _check_state(gu, ssd.cpu().numpy(), ref.ssm_state, "step t16")
     # the two GPU modes agree with each other (the pages' cached == full-history claim)
     assert gu.rel_l2(step_out, seq_out) <= OUT_REL
 
 
-def test_block_seq_config2_t413(env):
+def test_block_seq_b1_t413_q128(env):
     nh, oracle, gu, torch, lw, W = env
-    _say("block config 2: T=413, Q=128")
+    _say("block batch 1, T=413, Q=128")
     B, T = 1, 413
     x = synth.block_input(2, B, T)
     d = nh.dims(chunk=128)
@@ -130,8 +157,8 @@ def test_block_seq_config2_t413(env):
     nh.nh_mamba_block_seq(d, W, None, fin, gu.to_dev(x), nh.NH_BF16, T, out, nh.NH_F32, B, ws, ws.numel())
     ref = oracle.block(synth.REAL, lw, gu.bf16_bits_to_f64(x), np.zeros((B, 3, synth.CONV_DIM)), None,
                        mode=oracle.CONTRACT)
-    _check_out(gu, out.cpu().numpy(), ref.out, "seq c2")
-    _check_state(gu, fss.cpu().numpy(), ref.ssm_state, "seq c2")
+    _check_out(gu, out.cpu().numpy(), ref.out, "seq t413")
+    _check_state(gu, fss.cpu().numpy(), ref.ssm_state, "seq t413")
 
 
 def test_block_resume_seq_then_steps(env):
