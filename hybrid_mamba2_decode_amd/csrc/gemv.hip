@@ -360,12 +360,12 @@ __global__ __launch_bounds__(256, (NB == 1 ? (CPL <= 3 ? 3 : 2) : 1)) void k_gem
 // Fused pre-norm + in_proj + conv step: the work-group normalises the input rows into LDS
 // (u = bf16(x / rms(x) * w)), then streams its share of in_proj rows.
 template <int NB, int XT>
-__global__ __launch_bounds__(256, (NB == 1 ? 3 : 1)) void k_inproj_step(W4 W, const void *__restrict__ x,
+__global__ __launch_bounds__(256, (NB == 1 ? 4 : 1)) void k_inproj_step(W4 W, const void *__restrict__ x,
                                                                     const uint16_t *__restrict__ nw, float eps,
                                                                     EpiInProjStep epi, uint32_t *zero_ptr,
                                                                     int nzero)
 {
-    constexpr int LPR = 64, CPL = (HIDDEN / 32 + LPR - 1) / LPR, RG = (NB == 1 ? 2 : 1);
+    constexpr int LPR = 64, CPL = (HIDDEN / 32 + LPR - 1) / LPR, RG = 1;
     constexpr int NCH = HIDDEN / 32;
     GemvRunner<LPR, CPL, NB, RG, EpiInProjStep> run(W, epi);
     extern __shared__ uint32_t act_lds[];
@@ -392,41 +392,45 @@ __global__ __launch_bounds__(256, (NB == 1 ? 3 : 1)) void k_inproj_step(W4 W, co
             }
         }
     };
-    // pass 1: sum of squares per batch row (each thread owns at most one chunk per row)
+    // one round trip: the thread's x chunk (every batch row) and norm-weight chunk are loaded
+    // together and kept in registers for the second pass
+    float xv[NB][32], w[32];
+    const bool own = (int)threadIdx.x < NCH;
+    if (own) {
+        const uint4 *wsrc = reinterpret_cast<const uint4 *>(nw + 32 * threadIdx.x);
+        uint4 wq[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) wq[j] = wsrc[j];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) ld32(b, threadIdx.x, xv[b]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            w[8 * j + 0] = bf16lo(wq[j].x); w[8 * j + 1] = bf16hi(wq[j].x); w[8 * j + 2] = bf16lo(wq[j].y);
+            w[8 * j + 3] = bf16hi(wq[j].y); w[8 * j + 4] = bf16lo(wq[j].z); w[8 * j + 5] = bf16hi(wq[j].z);
+            w[8 * j + 6] = bf16lo(wq[j].w); w[8 * j + 7] = bf16hi(wq[j].w);
+        }
+    }
+    // sum of squares per batch row
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
         float ss = 0.f;
-        if ((int)threadIdx.x < NCH) {
-            float v[32];
-            ld32(b, threadIdx.x, v);
+        if (own)
 #pragma unroll
-            for (int e = 0; e < 32; ++e) ss += v[e] * v[e];
-        }
+            for (int e = 0; e < 32; ++e) ss += xv[b][e] * xv[b][e];
         ss = wave_sum(ss);
         if ((threadIdx.x & 63) == 0) red[b][threadIdx.x >> 6] = ss;
     }
     __syncthreads();
-    // pass 2: normalised, bf16-rounded chunks
-    if ((int)threadIdx.x < NCH) {
-        const int c = threadIdx.x;
-        float w[32];
-        const uint4 *wsrc = reinterpret_cast<const uint4 *>(nw + 32 * c);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint4 q = wsrc[j];
-            w[8 * j + 0] = bf16lo(q.x); w[8 * j + 1] = bf16hi(q.x); w[8 * j + 2] = bf16lo(q.y);
-            w[8 * j + 3] = bf16hi(q.y); w[8 * j + 4] = bf16lo(q.z); w[8 * j + 5] = bf16hi(q.z);
-            w[8 * j + 6] = bf16lo(q.w); w[8 * j + 7] = bf16hi(q.w);
-        }
+    // normalised, bf16-rounded chunks
+    if (own) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             const float tot = (red[b][0] + red[b][1]) + (red[b][2] + red[b][3]);
             const float r = 1.0f / sqrtf(tot / (float)HIDDEN + eps);
             float v[32];
-            ld32(b, c, v);
 #pragma unroll
-            for (int e = 0; e < 32; ++e) v[e] = round_bf16(v[e] * r * w[e]);
-            make_chunk(v, act_lds + ((size_t)b * NCH + c) * ACT_WORDS);
+            for (int e = 0; e < 32; ++e) v[e] = round_bf16(xv[b][e] * r * w[e]);
+            make_chunk(v, act_lds + ((size_t)b * NCH + threadIdx.x) * ACT_WORDS);
         }
     }
     __syncthreads();
@@ -498,7 +502,7 @@ static int cu_count()
     return cus;
 }
 
-// Persistent grid: at most two work-groups of four waves per CU, each wave walking stages.
+// Persistent grid: at most wgs_per_cu work-groups of four waves per CU, each wave walking stages.
 static int gemv_grid(int n, int rows_per_stage, int wgs_per_cu)
 {
     const int stages = (n + rows_per_stage - 1) / rows_per_stage;
@@ -568,7 +572,7 @@ hipError_t launch_inproj_step(const W4 &W, const void *x, int x_t, const uint16_
     const size_t lds = (size_t)batch * (HIDDEN / 32) * ACT_WORDS * 4;
 #define NH_LAUNCH(NB)                                                                                      \
     {                                                                                                      \
-        const int grid = gemv_grid(W.n, (NB == 1 ? 2 : 1), NB == 1 ? 3 : 1);                                \
+        const int grid = gemv_grid(W.n, 1, NB == 1 ? 4 : 1);                                                 \
         if (x_t == BF16)                                                                                   \
             launch_k(k_inproj_step<NB, BF16>, dim3(grid), dim3(256), lds, st, W, x, norm_w, eps, e, zero_ptr, \
                      nzero);                                                                               \
