@@ -160,8 +160,8 @@ struct Carve {
 };
 
 struct StepWs {
-    uint16_t *z, *xc, *dtr, *y;
-    float *part;
+    uint16_t *z, *xc, *dtr;
+    float *gate, *part;
 };
 
 StepWs carve_step(void *ws, int B, size_t *bytes)
@@ -171,7 +171,7 @@ StepWs carve_step(void *ws, int B, size_t *bytes)
     s.z = c.take<uint16_t>((size_t)B * DINNER);
     s.xc = c.take<uint16_t>((size_t)B * CONVDIM);
     s.dtr = c.take<uint16_t>((size_t)B * NHEADS);
-    s.y = c.take<uint16_t>((size_t)B * DINNER);
+    s.gate = c.take<float>((size_t)B * DINNER);
     s.part = c.take<float>((size_t)B * NHEADS * 2);
     *bytes = c.off;
     return s;
@@ -226,11 +226,11 @@ nh_status block_step(const nh_mamba_dims *d, const nh_mamba_weights *w, nh_mamba
                               st->conv_state, w->conv_w, w->conv_b, nullptr, 0, s),
            "in_proj step");
     prof_arm(1);
-    NH_HIP(launch_ssm_step_part(k.xc, k.dtr, NHEADS, w->dt_bias, w->A_log, w->D, st->ssm_state, k.y, k.z,
+    NH_HIP(launch_ssm_step_part(k.xc, k.dtr, NHEADS, w->dt_bias, w->A_log, w->D, st->ssm_state, k.gate, k.z,
                                 k.part, B, s),
            "ssm step");
     prof_arm(2);
-    NH_HIP(launch_outproj_step(view(&w->out_proj), k.y, k.z, w->gnorm_w, k.part, d->eps, B, x, x_t, out, out_t, s),
+    NH_HIP(launch_outproj_step(view(&w->out_proj), k.gate, w->gnorm_w, k.part, d->eps, B, x, x_t, out, out_t, s),
            "out_proj step");
     prof_next() = ProfEvents{};
     return ok();

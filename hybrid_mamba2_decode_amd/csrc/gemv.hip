@@ -440,12 +440,11 @@ __global__ __launch_bounds__(256, (NB == 1 ? 4 : 1)) void k_inproj_step(W4 W, co
 }
 
 // Fused gated RMSNorm + out_proj + residual for the per-position block.  The work-group forms
-// o = bf16(RMSNorm_group(y * silu(z)) * w) straight into the LDS activation format from y,
-// z and the per-(head, half) sums of squares left by the SSM step, while the first stage of
-// out_proj weights is already in flight; o never goes to memory.
+// o = bf16(RMSNorm_group(g) * w) straight into the LDS activation format from the gate product
+// g = bf16(y) * silu(z) and the per-(head, half) sums of squares, both left by the SSM step,
+// while the first stage of out_proj weights is already in flight; o never goes to memory.
 template <int NB>
-__global__ __launch_bounds__(NB == 1 ? 512 : 256, 1) void k_outproj_step(W4 W, const uint16_t *__restrict__ y,
-                                                         const uint16_t *__restrict__ z,
+__global__ __launch_bounds__(NB == 1 ? 512 : 256, 1) void k_outproj_step(W4 W, const float *__restrict__ gate,
                                                          const uint16_t *__restrict__ gw,
                                                          const float *__restrict__ part, float eps,
                                                          EpiStore epi)
@@ -465,19 +464,24 @@ __global__ __launch_bounds__(NB == 1 ? 512 : 256, 1) void k_outproj_step(W4 W, c
     for (int it = threadIdx.x; it < NB * NCH; it += blockDim.x) {
         const int b = it / NCH, c = it % NCH;
         const float r = rstd[b][(32 * c) / GNORM];
-        const uint4 *yp = reinterpret_cast<const uint4 *>(y + (size_t)b * DINNER + 32 * c);
-        const uint4 *zp = reinterpret_cast<const uint4 *>(z + (size_t)b * DINNER + 32 * c);
+        const float4 *gp = reinterpret_cast<const float4 *>(gate + (size_t)b * DINNER + 32 * c);
         const uint4 *wp = reinterpret_cast<const uint4 *>(gw + 32 * c);
+        float4 gv[8];
+        uint4 wv[4];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) gv[j] = gp[j];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) wv[j] = wp[j];
         float v[32];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const uint4 yy = yp[j], zz = zp[j], ww = wp[j];
-            const uint32_t ya[4] = {yy.x, yy.y, yy.z, yy.w}, za[4] = {zz.x, zz.y, zz.z, zz.w};
-            const uint32_t wa[4] = {ww.x, ww.y, ww.z, ww.w};
+            const uint32_t wa[4] = {wv[j].x, wv[j].y, wv[j].z, wv[j].w};
+            const float ga[8] = {gv[2 * j].x, gv[2 * j].y, gv[2 * j].z, gv[2 * j].w,
+                                 gv[2 * j + 1].x, gv[2 * j + 1].y, gv[2 * j + 1].z, gv[2 * j + 1].w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                v[8 * j + 2 * e] = round_bf16(bf16lo(ya[e]) * silu(bf16lo(za[e])) * r * bf16lo(wa[e]));
-                v[8 * j + 2 * e + 1] = round_bf16(bf16hi(ya[e]) * silu(bf16hi(za[e])) * r * bf16hi(wa[e]));
+                v[8 * j + 2 * e] = round_bf16(ga[2 * e] * r * bf16lo(wa[e]));
+                v[8 * j + 2 * e + 1] = round_bf16(ga[2 * e + 1] * r * bf16hi(wa[e]));
             }
         }
         make_chunk(v, act_lds + (size_t)it * ACT_WORDS);
@@ -545,19 +549,19 @@ hipError_t launch_gemv(const W4 &W, const uint16_t *x, int batch, const void *re
     }
 }
 
-hipError_t launch_outproj_step(const W4 &W, const uint16_t *y, const uint16_t *z, const uint16_t *gw,
-                               const float *part, float eps, int batch, const void *res, int res_t,
-                               void *out, int out_t, hipStream_t st)
+hipError_t launch_outproj_step(const W4 &W, const float *gate, const uint16_t *gw, const float *part,
+                               float eps, int batch, const void *res, int res_t, void *out, int out_t,
+                               hipStream_t st)
 {
     EpiStore e{out, res, out_t, res_t, W.n};
     const size_t lds = (size_t)batch * (DINNER / 32) * ACT_WORDS * 4;
     // one work-group per CU: 8 waves at batch 1; 4 waves (more registers each) above
     const int grid = min(cu_count(), (W.n + 7) / 8);
     switch (batch) {
-    case 1: launch_k(k_outproj_step<1>, dim3(grid), dim3(512), lds, st, W, y, z, gw, part, eps, e); break;
-    case 2: launch_k(k_outproj_step<2>, dim3(grid), dim3(256), lds, st, W, y, z, gw, part, eps, e); break;
-    case 3: launch_k(k_outproj_step<3>, dim3(grid), dim3(256), lds, st, W, y, z, gw, part, eps, e); break;
-    default: launch_k(k_outproj_step<4>, dim3(grid), dim3(256), lds, st, W, y, z, gw, part, eps, e); break;
+    case 1: launch_k(k_outproj_step<1>, dim3(grid), dim3(512), lds, st, W, gate, gw, part, eps, e); break;
+    case 2: launch_k(k_outproj_step<2>, dim3(grid), dim3(256), lds, st, W, gate, gw, part, eps, e); break;
+    case 3: launch_k(k_outproj_step<3>, dim3(grid), dim3(256), lds, st, W, gate, gw, part, eps, e); break;
+    default: launch_k(k_outproj_step<4>, dim3(grid), dim3(256), lds, st, W, gate, gw, part, eps, e); break;
     }
     return hipGetLastError();
 }

@@ -52,16 +52,16 @@ hipError_t launch_inproj_step(const W4 &W, const void *x, int x_t, const uint16_
 hipError_t launch_ssm_step(const uint16_t *xc, const uint16_t *dtr, long ld_dt,
                            const float *dt_bias, const float *A_log, const float *D, float *S,
                            void *y, int y_t, int batch, hipStream_t st);
-// SSM step that stores y (bf16) and, per (sequence, head, half head), the sum of squares of
-// y * silu(z) for the gated RMSNorm.
+// SSM step that stores the gate product g = bf16(y) * silu(z) (fp32, [batch][d_inner]) and,
+// per (sequence, head, half head), the sum of squares of g for the gated RMSNorm.
 hipError_t launch_ssm_step_part(const uint16_t *xc, const uint16_t *dtr, long ld_dt,
                                 const float *dt_bias, const float *A_log, const float *D,
-                                float *S, uint16_t *y_ws, const uint16_t *z, float *part, int batch,
+                                float *S, float *gate, const uint16_t *z, float *part, int batch,
                                 hipStream_t st);
-// Gated RMSNorm (from y, z and the SSM step's partial sums) fused into out_proj + residual.
-hipError_t launch_outproj_step(const W4 &W, const uint16_t *y, const uint16_t *z, const uint16_t *gw,
-                               const float *part, float eps, int batch, const void *res, int res_t,
-                               void *out, int out_t, hipStream_t st);
+// Gated RMSNorm (from g and the SSM step's partial sums) fused into out_proj + residual.
+hipError_t launch_outproj_step(const W4 &W, const float *gate, const uint16_t *gw, const float *part,
+                               float eps, int batch, const void *res, int res_t, void *out, int out_t,
+                               hipStream_t st);
 hipError_t launch_conv_step(const uint16_t *xbc, long ld, uint16_t *state, const uint16_t *w,
                             const uint16_t *b, uint16_t *out, int batch, int channels,
                             hipStream_t st);

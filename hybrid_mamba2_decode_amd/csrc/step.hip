@@ -85,8 +85,9 @@ __global__ __launch_bounds__(256) void k_ssm_step(const uint16_t *__restrict__ x
         return;
     }
 
-    // ---- y (bf16) and this work-group's sum of squares of y * silu(z), consumed by the
-    // gated RMSNorm in the out_proj kernel.
+    // ---- the gate product g = bf16(y) * silu(z) (fp32; y is rounded to bf16 first, its
+    // storage point) and this work-group's sum of squares of g, both consumed by the gated
+    // RMSNorm in the out_proj kernel, which so needs neither y nor z.
     __shared__ float red[8];
     float ss = 0.f;
     if (nl == 0)
@@ -94,9 +95,8 @@ __global__ __launch_bounds__(256) void k_ssm_step(const uint16_t *__restrict__ x
         for (int it = 0; it < SSM_IT; ++it) {
             const int p = half * SSM_ROWS + slot + 8 * it;
             const size_t i = (size_t)b * DINNER + h * HDIM + p;
-            const uint16_t yb = f32_to_bf16(yv[it]);
-            reinterpret_cast<uint16_t *>(y)[i] = yb;
-            const float gm = bf16_to_f32(yb) * silu(bf16_to_f32(z[i]));
+            const float gm = round_bf16(yv[it]) * silu(bf16_to_f32(z[i]));
+            reinterpret_cast<float *>(y)[i] = gm;
             ss += gm * gm;
         }
     if (nl == 0) red[slot] = ss;
@@ -125,11 +125,11 @@ hipError_t launch_ssm_step(const uint16_t *xc, const uint16_t *dtr, long ld_dt,
 
 hipError_t launch_ssm_step_part(const uint16_t *xc, const uint16_t *dtr, long ld_dt,
                                 const float *dt_bias, const float *A_log, const float *D,
-                                float *S, uint16_t *y_ws, const uint16_t *z, float *part, int batch,
+                                float *S, float *gate, const uint16_t *z, float *part, int batch,
                                 hipStream_t st)
 {
     dim3 grid(batch * NHEADS * 2), block(256);
-    launch_k(k_ssm_step<true, BF16>, grid, block, 0, st, xc, dtr, ld_dt, dt_bias, A_log, D, S, y_ws, z, part);
+    launch_k(k_ssm_step<true, F32>, grid, block, 0, st, xc, dtr, ld_dt, dt_bias, A_log, D, S, gate, z, part);
     return hipGetLastError();
 }
 
