@@ -221,7 +221,7 @@ def main():
         for x in e:
             hip.destroy(x)
     kb = step_kernel_bytes(B)
-    names = ["k_inproj_step<1, 0>", "k_ssm_step<true, 0>", "k_outproj_step<1>"]  # batch 1, bf16 input
+    names = ["k_inproj_step<1, 0>", "k_ssm_step<true, 1>", "k_outproj_step<1>"]  # batch 1, bf16 input
     kernels = [{"kernel": names[j], "avg_us": round(float(k_avg[j]), 3), "median_us": round(float(k_med[j]), 3),
                 "algorithmic_bytes": int(kb[j]), "GBps": round(kb[j] / (k_avg[j] * 1e-6) / 1e9, 1),
                 "hbm_frac": round(kb[j] / (k_avg[j] * 1e-6) / HBM_PEAK, 4)} for j in range(3)]
