@@ -98,7 +98,8 @@ __global__ __launch_bounds__(256) void k_w4_gemm(W4 W, const uint16_t *__restric
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             if (nok[j]) {
-                wq[j] = ld_nt(reinterpret_cast<const uint4 *>(W.q + (size_t)nrow[j] * kw + 8 * g) + kh);
+                // cached load: the 128-byte line serves the next three groups and every row tile
+                wq[j] = *(reinterpret_cast<const uint4 *>(W.q + (size_t)nrow[j] * kw + 8 * g) + kh);
                 sc[j] = bf16_to_f32(W.s[(size_t)nrow[j] * kg + g]);
                 bb[j] = bf16_to_f32(W.b[(size_t)nrow[j] * kg + g]);
             } else {
