@@ -114,3 +114,43 @@ def test_primitive_checks(nh):
     assert _status(lambda: nh.nh_rmsnorm_gated(A, A, 10240, A, A, 1, 10240, 1000, 1e-5, 0)) == \
         nh.NH_ERR_UNSUPPORTED_SHAPE
     assert _status(lambda: nh.nh_rmsnorm(A, 0, A, A, 1, 4480, 0.0, 0)) == nh.NH_ERR_INVALID_ARGUMENT
+
+
+def test_scan_workspace_size_and_checks(nh):
+    A = 0x40000
+    # chunk 256: 136 causal 16 x 16 tiles of fp16 per (chunk, sequence, group); a partial last
+    # chunk of L rows holds ceil(L/16)(ceil(L/16)+1)/2 tiles
+    d256 = nh.dims(chunk=256)
+    assert nh.nh_ssd_scan_workspace_bytes(d256, 2, 3750) == 2 * 8 * 512 * (14 * 136 + 66)  # last chunk: 166 rows
+    assert nh.nh_ssd_scan_workspace_bytes(d256, 1, 1) == 8 * 512
+    for B, T, Q in [(1, 1, 1), (2, 413, 128), (3, 17, 16), (1, 300, 7), (2, 3750, 256)]:
+        n = nh.nh_ssd_scan_workspace_bytes(nh.dims(chunk=Q), B, T)
+        assert 0 < n <= 4096 * B * T        # the block reuses 8960 B per position for it
+    assert nh.nh_ssd_scan_workspace_bytes(nh.dims(chunk=0), 1, 10) == 0
+    assert nh.nh_ssd_scan_workspace_bytes(nh.dims(chunk=257), 1, 10) == 0
+    assert nh.nh_ssd_scan_workspace_bytes(d256, 0, 10) == 0
+    n = nh.nh_ssd_scan_workspace_bytes(d256, 1, 100)
+    assert _status(lambda: nh.nh_ssd_chunk_scan(d256, A, A, 128, 100, A, A, A, None, None, A, 0, 1, A, n - 1, 0)) == \
+        nh.NH_ERR_WORKSPACE_TOO_SMALL
+    assert _status(lambda: nh.nh_ssd_chunk_scan(d256, A, A, 128, 100, A, A, A, None, None, A, 0, 1, None, n, 0)) == \
+        nh.NH_ERR_INVALID_ARGUMENT
+    assert _status(lambda: nh.nh_ssd_chunk_scan(d256, A, A, 128, 100, A, A, A, None, None, A, 0, 1, A + 2, n, 0)) == \
+        nh.NH_ERR_MISALIGNED
+
+
+def test_inproj_conv_step_checks(nh):
+    A = 0x40000
+    d = nh.dims()
+    lw = nh.mamba_weights(A, _fake_w4(22656, 4480), A, A, A, A, A, A, _fake_w4(4480, 10240))
+    st = nh.mamba_state(A, A)
+    assert _status(lambda: nh.nh_inproj_conv_step(d, lw, st, A, 0, A + 0x100, A + 0x200, A + 0x300, 5, 0)) == \
+        nh.NH_ERR_UNSUPPORTED_SHAPE
+    assert _status(lambda: nh.nh_inproj_conv_step(d, lw, st, A, 0, A, A + 0x200, A + 0x300, 1, 0)) == \
+        nh.NH_ERR_INVALID_ARGUMENT  # z aliases x
+    assert _status(lambda: nh.nh_inproj_conv_step(d, lw, st, A, 0, None, A + 0x200, A + 0x300, 1, 0)) == \
+        nh.NH_ERR_INVALID_ARGUMENT
+    assert _status(lambda: nh.nh_inproj_conv_step(d, lw, st, A, 0, A + 0x100, A + 0x208, A + 0x300, 1, 0)) == \
+        nh.NH_ERR_MISALIGNED
+    wrong = nh.mamba_weights(A, _fake_w4(22656, 4416), A, A, A, A, A, A, _fake_w4(4480, 10240))
+    assert _status(lambda: nh.nh_inproj_conv_step(d, wrong, st, A, 0, A + 0x100, A + 0x200, A + 0x300, 1, 0)) == \
+        nh.NH_ERR_UNSUPPORTED_SHAPE
