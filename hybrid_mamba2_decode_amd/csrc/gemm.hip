@@ -12,16 +12,17 @@
 // accumulation is fp32 inside v_mfma_f32_32x32x16_f16.
 //
 // Tiling: 128 x 128 output tile per work-group of 4 waves (2 x 2), each wave 64 x 64 as
-// 2 x 2 MFMA 32x32 tiles, K advanced one 64-wide quantisation group at a time.  The X tile is
-// staged through LDS (double-buffered, padded rows); each wave reads its W rows straight from
-// global memory into registers, one group ahead.
+// 2 x 2 MFMA 32x32 tiles, K advanced two 64-wide quantisation groups per pipeline step.  The X
+// tile is staged through LDS (double-buffered, padded rows); each wave reads its W rows straight
+// from global memory into registers, one step ahead.
 #include "nh_device.hpp"
 #include "nh_kernels.hpp"
 
 namespace nh {
 
 constexpr int GBM = 128, GBN = 128, GBK = 64;
-constexpr int GALD = GBK + 8;  // LDS row of the X tile, in fp16 elements (144 B: conflict-free)
+constexpr int GKS = 2;                  // quantisation groups per pipeline step
+constexpr int GALD = GKS * GBK + 8;     // LDS row of the X tile, in fp16 elements (272 B)
 
 // Eight fp16 values in pair order (0,4) (1,5) (2,6) (3,7), matching the nibble extraction.
 __device__ __forceinline__ uint4 pair_order16(uint4 v)
@@ -56,8 +57,12 @@ struct GemmEpi {
     int y_t, res_t;
 };
 
-__global__ __launch_bounds__(256) void k_w4_gemm(W4 W, const uint16_t *__restrict__ Xh,
-                                                 const float *__restrict__ su, int M, GemmEpi ep)
+// One pipeline step covers GKS quantisation groups (K = 128): the X tile of the step is in
+// LDS (double-buffered), the W words and scales of the step are in registers (double-buffered),
+// and the next step's loads are in flight while this step's 32 MFMAs per wave run.  The W words
+// are dequantised just before their MFMA step.
+__global__ __launch_bounds__(256, 2) void k_w4_gemm(W4 W, const uint16_t *__restrict__ Xh,
+                                                    const float *__restrict__ su, int M, GemmEpi ep)
 {
     __shared__ __attribute__((aligned(16))) uint16_t As[2][GBM * GALD];
 
@@ -67,10 +72,11 @@ __global__ __launch_bounds__(256) void k_w4_gemm(W4 W, const uint16_t *__restric
     const int mt = blockIdx.x % mtiles, nt = blockIdx.x / mtiles;
     const int m0 = mt * GBM, n0 = nt * GBN;
     const int K = W.k, kw = K >> 3, kg = K >> 6;
+    const int nsteps = (kg + GKS - 1) / GKS;
     const int l32 = lane & 31, kh = lane >> 5;
 
-    // X tile staging: thread -> (row tid/2, 32 values at column 32*(tid&1)).
-    const int srow = tid >> 1, scol = 32 * (tid & 1);
+    // X tile staging: thread -> (row tid/2, 64 values at column 64*(tid&1) of the step)
+    const int srow = tid >> 1, scol = 64 * (tid & 1);
     const bool srow_ok = (m0 + srow) < M;
     const uint16_t *xsrc = Xh + (size_t)(srow_ok ? m0 + srow : 0) * K + scol;
 
@@ -83,31 +89,37 @@ __global__ __launch_bounds__(256) void k_w4_gemm(W4 W, const uint16_t *__restric
         nok[j] = nrow[j] < W.n;
     }
 
-    auto load_x = [&](int g, uint4 *v) {
+    // the step's X columns: group 2*st + (tid & 1); a missing second group (odd kg) reads zero.
+    // Staged in two halves of 32 columns (h = 0, 1) to keep fewer values in flight in registers.
+    auto load_x = [&](int st, int h, uint4 *v) {
+        const bool ok = srow_ok && (GKS * st + (tid & 1)) < kg;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            v[i] = srow_ok ? *reinterpret_cast<const uint4 *>(xsrc + (size_t)g * GBK + 8 * i)
-                           : make_uint4(0u, 0u, 0u, 0u);
+            v[i] = ok ? *reinterpret_cast<const uint4 *>(xsrc + (size_t)st * GKS * GBK + 32 * h + 8 * i)
+                      : make_uint4(0u, 0u, 0u, 0u);
     };
-    auto store_x = [&](int buf, const uint4 *v) {
-        uint16_t *dst = &As[buf][srow * GALD + scol];
+    auto store_x = [&](int buf, int h, const uint4 *v) {
+        uint16_t *dst = &As[buf][srow * GALD + scol + 32 * h];
 #pragma unroll
         for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4 *>(dst + 8 * i) = pair_order16(v[i]);
     };
-    auto load_w = [&](int g, uint4 *wq, float *sc, float *bb) {
+    auto load_w = [&](int st, uint4 (*wq)[GKS], float (*sc)[GKS], float (*bb)[GKS]) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            if (nok[j]) {
-                // cached load: the 128-byte line serves the next three groups and every row tile
-                wq[j] = *(reinterpret_cast<const uint4 *>(W.q + (size_t)nrow[j] * kw + 8 * g) + kh);
-                sc[j] = bf16_to_f32(W.s[(size_t)nrow[j] * kg + g]);
-                bb[j] = bf16_to_f32(W.b[(size_t)nrow[j] * kg + g]);
-            } else {
-                wq[j] = make_uint4(0u, 0u, 0u, 0u);
-                sc[j] = 0.f;
-                bb[j] = 0.f;
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int gg = 0; gg < GKS; ++gg) {
+                const int g = GKS * st + gg;
+                if (nok[j] && g < kg) {
+                    // cached load: the 128-byte line serves the next groups and every row tile
+                    wq[j][gg] = *(reinterpret_cast<const uint4 *>(W.q + (size_t)nrow[j] * kw + 8 * g) + kh);
+                    sc[j][gg] = bf16_to_f32(W.s[(size_t)nrow[j] * kg + g]);
+                    bb[j][gg] = bf16_to_f32(W.b[(size_t)nrow[j] * kg + g]);
+                } else {
+                    wq[j][gg] = make_uint4(0u, 0u, 0u, 0u);
+                    sc[j][gg] = 0.f;
+                    bb[j][gg] = 0.f;
+                }
             }
-        }
     };
 
     floatx16 acc[2][2];
@@ -119,66 +131,79 @@ __global__ __launch_bounds__(256) void k_w4_gemm(W4 W, const uint16_t *__restric
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     uint4 xv[4];
-    uint4 wq[2], wq_n[2];
-    float sc[2], bb[2], sc_n[2], bb_n[2];
-    load_x(0, xv);
+    uint4 wq[2][GKS], wq_n[2][GKS];
+    float sc[2][GKS], bb[2][GKS], sc_n[2][GKS], bb_n[2][GKS];
     load_w(0, wq, sc, bb);
-    store_x(0, xv);
+    load_x(0, 0, xv);
+    store_x(0, 0, xv);
+    load_x(0, 1, xv);
+    store_x(0, 1, xv);
     __syncthreads();
 
-    for (int g = 0; g < kg; ++g) {
-        const int cur = g & 1;
-        const bool more = g + 1 < kg;
+    for (int st = 0; st < nsteps; ++st) {
+        const int cur = st & 1;
+        const bool more = st + 1 < nsteps;
         if (more) {
-            load_x(g + 1, xv);
-            load_w(g + 1, wq_n, sc_n, bb_n);
-        }
-        // B fragments: word ks of this lane's 4-word slice <-> MFMA step ks.
-        half8 bf[2][4];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const half2v s2 = {(_Float16)sc[j], (_Float16)sc[j]};
-            const uint32_t ww[4] = {wq[j].x, wq[j].y, wq[j].z, wq[j].w};
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) bf[j][ks] = dequant_word(ww[ks], s2);
+            load_x(st + 1, 0, xv);
+            load_w(st + 1, wq_n, sc_n, bb_n);
         }
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            half8 af[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const uint16_t *src = &As[cur][(64 * wm + 32 * i + l32) * GALD + 8 * (4 * kh + ks)];
-                af[i] = __builtin_bit_cast(half8, *reinterpret_cast<const uint4 *>(src));
+        for (int gg = 0; gg < GKS; ++gg) {
+            const int g = GKS * st + gg;
+            if (gg == 1 && more) {
+                // first half of the next step's X to the other buffer, then the second half in flight
+                store_x(cur ^ 1, 0, xv);
+                load_x(st + 1, 1, xv);
             }
+            half2v s2[2];
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int j = 0; j < 2; ++j) s2[j] = half2v{(_Float16)sc[j][gg], (_Float16)sc[j][gg]};
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j][ks], acc[i][j], 0, 0, 0);
-        }
-        // Asymmetric groups: add (beta + 8 s) * (group sum of the X row).
-        float bpp[2];
+            for (int ks = 0; ks < 4; ++ks) {
+                half8 bf[2], af[2];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) bpp[j] = fmaf(8.f, sc[j], bb[j]);
-        if (__builtin_amdgcn_ballot_w64(bpp[0] != 0.f || bpp[1] != 0.f) != 0ull) {
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int m = m0 + 64 * wm + 32 * i + 8 * (r >> 2) + 4 * kh + (r & 3);
-                    const float s = m < M ? su[(size_t)m * kg + g] : 0.f;
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) acc[i][j][r] = fmaf(bpp[j], s, acc[i][j][r]);
+                for (int j = 0; j < 2; ++j) {
+                    const uint32_t ww[4] = {wq[j][gg].x, wq[j][gg].y, wq[j][gg].z, wq[j][gg].w};
+                    bf[j] = dequant_word(ww[ks], s2[j]);
                 }
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const uint16_t *src = &As[cur][(64 * wm + 32 * i + l32) * GALD + GBK * gg + 8 * (4 * kh + ks)];
+                    af[i] = __builtin_bit_cast(half8, *reinterpret_cast<const uint4 *>(src));
+                }
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // Asymmetric groups: add (beta + 8 s) * (group sum of the X row).
+            float bpp[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) bpp[j] = fmaf(8.f, sc[j][gg], bb[j][gg]);
+            if (g < kg && __builtin_amdgcn_ballot_w64(bpp[0] != 0.f || bpp[1] != 0.f) != 0ull) {
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int m = m0 + 64 * wm + 32 * i + 8 * (r >> 2) + 4 * kh + (r & 3);
+                        const float s = m < M ? su[(size_t)m * kg + g] : 0.f;
+#pragma unroll
+                        for (int j = 0; j < 2; ++j) acc[i][j][r] = fmaf(bpp[j], s, acc[i][j][r]);
+                    }
+            }
         }
         if (more) {
-            store_x(cur ^ 1, xv);
+            store_x(cur ^ 1, 1, xv);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                wq[j] = wq_n[j];
-                sc[j] = sc_n[j];
-                bb[j] = bb_n[j];
-            }
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int gg = 0; gg < GKS; ++gg) {
+                    wq[j][gg] = wq_n[j][gg];
+                    sc[j][gg] = sc_n[j][gg];
+                    bb[j][gg] = bb_n[j][gg];
+                }
         }
         __syncthreads();
     }
