@@ -453,25 +453,18 @@ __global__ __launch_bounds__(NB == 1 ? 512 : 256, 1) void k_outproj_step(W4 W, c
     GemvRunner<LPR, CPL, NB, RG, EpiStore> run(W, epi);
     extern __shared__ uint32_t act_lds[];
     __shared__ float rstd[NB][NGROUPS];
-    if ((int)threadIdx.x < NB * NGROUPS) {
-        const int b = threadIdx.x / NGROUPS, g = threadIdx.x % NGROUPS;
-        const float *pg = part + ((size_t)b * NHEADS + g * HPG) * 2;
-        float t = 0.f;
-        for (int i = 0; i < 2 * HPG; ++i) t += pg[i];
-        rstd[b][g] = 1.0f / sqrtf(t / (float)GNORM + eps);
-    }
-    __syncthreads();
-    for (int it = threadIdx.x; it < NB * NCH; it += blockDim.x) {
+    auto load = [&](int it, float4 *gv, uint4 *wv) {
         const int b = it / NCH, c = it % NCH;
-        const float r = rstd[b][(32 * c) / GNORM];
         const float4 *gp = reinterpret_cast<const float4 *>(gate + (size_t)b * DINNER + 32 * c);
         const uint4 *wp = reinterpret_cast<const uint4 *>(gw + 32 * c);
-        float4 gv[8];
-        uint4 wv[4];
 #pragma unroll
         for (int j = 0; j < 8; ++j) gv[j] = gp[j];
 #pragma unroll
         for (int j = 0; j < 4; ++j) wv[j] = wp[j];
+    };
+    auto build = [&](int it, const float4 *gv, const uint4 *wv) {
+        const int b = it / NCH, c = it % NCH;
+        const float r = rstd[b][(32 * c) / GNORM];
         float v[32];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -485,6 +478,31 @@ __global__ __launch_bounds__(NB == 1 ? 512 : 256, 1) void k_outproj_step(W4 W, c
             }
         }
         make_chunk(v, act_lds + (size_t)it * ACT_WORDS);
+    };
+    // With at most one chunk per thread (batch 1: 320 chunks, 512 threads) the chunk's gate
+    // and weight loads are issued before the group sums are reduced, so the two global round
+    // trips overlap.
+    constexpr bool ONE = NB * NCH <= (NB == 1 ? 512 : 256);
+    float4 gv0[8];
+    uint4 wv0[4];
+    if (ONE && (int)threadIdx.x < NB * NCH) load(threadIdx.x, gv0, wv0);
+    if ((int)threadIdx.x < NB * NGROUPS) {
+        const int b = threadIdx.x / NGROUPS, g = threadIdx.x % NGROUPS;
+        const float *pg = part + ((size_t)b * NHEADS + g * HPG) * 2;
+        float t = 0.f;
+        for (int i = 0; i < 2 * HPG; ++i) t += pg[i];
+        rstd[b][g] = 1.0f / sqrtf(t / (float)GNORM + eps);
+    }
+    __syncthreads();
+    if (ONE) {
+        if ((int)threadIdx.x < NB * NCH) build(threadIdx.x, gv0, wv0);
+    } else {
+        for (int it = threadIdx.x; it < NB * NCH; it += blockDim.x) {
+            float4 gv[8];
+            uint4 wv[4];
+            load(it, gv, wv);
+            build(it, gv, wv);
+        }
     }
     __syncthreads();
     ActChunk a[NB][CPL];
