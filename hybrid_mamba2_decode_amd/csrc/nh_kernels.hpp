@@ -22,7 +22,8 @@ inline void launch_k(void (*k)(P...), dim3 grid, dim3 block, uint32_t lds, hipSt
 {
     ProfEvents &p = prof_next();
     if (p.start) {
-        hipEventRecord(p.start, st);
+        // a failure here is the runtime's last error, which every launcher returns after launching
+        (void)hipEventRecord(p.start, st);
         hipExtLaunchKernelGGL(k, grid, block, lds, st, nullptr, p.stop, 0, static_cast<P>(args)...);
         p = ProfEvents{};
     } else {
