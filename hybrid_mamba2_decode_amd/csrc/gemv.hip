@@ -90,8 +90,11 @@ struct GemvShape {
     static constexpr int RPG = 64 / LPR;  // rows per wave-instruction
 };
 
+// Values an epilogue loads one stage ahead, kept exactly as loaded: any arithmetic on them at
+// load time would make the wave wait for every load issued before them, the next stage's
+// weights included.
 struct EpiPre {
-    uint32_t a, b, c, d;
+    uint32_t a, b, c, d, e, f;
 };
 
 // y[b][n] = acc + res[b][n]
@@ -101,10 +104,10 @@ struct EpiStore {
     int y_t, res_t, n;
     __device__ __forceinline__ EpiPre prefetch(int row, int b) const
     {
-        EpiPre p{0u, 0u, 0u, 0u};
+        EpiPre p{0u, 0u, 0u, 0u, 0u, 0u};
         if (res) {
             const size_t i = (size_t)b * n + row;
-            p.a = res_t == BF16 ? (uint32_t)reinterpret_cast<const uint16_t *>(res)[i] << 16
+            p.a = res_t == BF16 ? (uint32_t)reinterpret_cast<const uint16_t *>(res)[i]
                                 : __float_as_uint(reinterpret_cast<const float *>(res)[i]);
         }
         return p;
@@ -112,7 +115,7 @@ struct EpiStore {
     __device__ __forceinline__ void operator()(int row, int b, float v, const EpiPre &p) const
     {
         const size_t i = (size_t)b * n + row;
-        v += __uint_as_float(p.a);
+        v += res_t == BF16 ? __uint_as_float(p.a << 16) : __uint_as_float(p.a);
         if (y_t == BF16)
             reinterpret_cast<uint16_t *>(y)[i] = f32_to_bf16(v);
         else
@@ -133,10 +136,12 @@ struct EpiInProjStep {
         const uint16_t *st = cs + (size_t)b * (CONVK - 1) * CONVDIM + c;
         const uint2 w = *reinterpret_cast<const uint2 *>(cw + 4 * (size_t)c);
         EpiPre p;
-        p.a = (uint32_t)st[0] | ((uint32_t)st[CONVDIM] << 16);
-        p.b = (uint32_t)st[2 * CONVDIM] | ((uint32_t)cb[c] << 16);
-        p.c = w.x;
-        p.d = w.y;
+        p.a = st[0];
+        p.b = st[CONVDIM];
+        p.c = st[2 * CONVDIM];
+        p.d = cb[c];
+        p.e = w.x;
+        p.f = w.y;
         return p;
     }
     __device__ __forceinline__ void operator()(int n, int b, float acc, const EpiPre &p) const
@@ -147,14 +152,14 @@ struct EpiInProjStep {
         } else if (n < DINNER + CONVDIM) {
             const int c = n - DINNER;
             uint16_t *st = cs + (size_t)b * (CONVK - 1) * CONVDIM + c;
-            float a = bf16hi(p.b);
-            a = fmaf(bf16lo(p.c), bf16lo(p.a), a);
-            a = fmaf(bf16hi(p.c), bf16hi(p.a), a);
-            a = fmaf(bf16lo(p.d), bf16lo(p.b), a);
-            a = fmaf(bf16hi(p.d), bf16_to_f32(vb), a);
+            float a = bf16lo(p.d);
+            a = fmaf(bf16lo(p.e), bf16lo(p.a), a);
+            a = fmaf(bf16hi(p.e), bf16lo(p.b), a);
+            a = fmaf(bf16lo(p.f), bf16lo(p.c), a);
+            a = fmaf(bf16hi(p.f), bf16_to_f32(vb), a);
             xc[(size_t)b * CONVDIM + c] = f32_to_bf16(silu(a));
-            st[0] = (uint16_t)(p.a >> 16);
-            st[CONVDIM] = (uint16_t)(p.b & 0xFFFFu);
+            st[0] = (uint16_t)p.b;
+            st[CONVDIM] = (uint16_t)p.c;
             st[2 * CONVDIM] = vb;
         } else {
             dtr[(size_t)b * NHEADS + (n - DINNER - CONVDIM)] = vb;
@@ -268,7 +273,9 @@ struct GemvRunner {
     Stage<RG, CPL> A, B;
     EpiPre pa, pb;
 
-    __device__ __forceinline__ GemvRunner(const W4 &W_, const Epi &epi_) : W(W_), epi(epi_)
+    // threads: the work-group size, a compile-time constant at every call site (blockDim would
+    // be a load from the dispatch arguments whose wait also covers every load issued before it)
+    __device__ __forceinline__ GemvRunner(const W4 &W_, const Epi &epi_, int threads) : W(W_), epi(epi_)
     {
         const int lane = threadIdx.x & 63;
         sub = lane / LPR;
@@ -282,7 +289,7 @@ struct GemvRunner {
         const int xcd = blockIdx.x % nx;
         const int wave = __builtin_amdgcn_readfirstlane(
             (int)((threadIdx.x >> 6) * (gridDim.x / nx) + blockIdx.x / nx));
-        const int nwaves = (gridDim.x / nx) * (blockDim.x >> 6);
+        const int nwaves = (gridDim.x / nx) * (threads >> 6);
         const int slab = (((W.n + nx - 1) / nx + ROWS - 1) / ROWS) * ROWS;
         const int nch = W.k >> 5;
         rowbytes = (uint32_t)W.k / 2;
@@ -336,10 +343,10 @@ struct GemvRunner {
 template <int LPR, int CPL, int NB, int RG>
 __global__ __launch_bounds__(256, (NB == 1 ? (CPL <= 3 ? 3 : 2) : 1)) void k_gemv(W4 W, const uint16_t *__restrict__ x, EpiStore epi)
 {
-    GemvRunner<LPR, CPL, NB, RG, EpiStore> run(W, epi);
+    GemvRunner<LPR, CPL, NB, RG, EpiStore> run(W, epi, 256);
     extern __shared__ uint32_t act_lds[];
     const int nch = W.k >> 5;
-    for (int it = threadIdx.x; it < NB * nch; it += blockDim.x) {
+    for (int it = threadIdx.x; it < NB * nch; it += 256) {
         const uint4 *src = reinterpret_cast<const uint4 *>(x + (size_t)it * 32);  // [b][c] = b*nch + c
         float v[32];
 #pragma unroll
@@ -360,55 +367,58 @@ __global__ __launch_bounds__(256, (NB == 1 ? (CPL <= 3 ? 3 : 2) : 1)) void k_gem
 // Fused pre-norm + in_proj + conv step: the work-group normalises the input rows into LDS
 // (u = bf16(x / rms(x) * w)), then streams its share of in_proj rows.
 template <int NB, int XT>
-__global__ __launch_bounds__(256, (NB == 1 ? 4 : 1)) void k_inproj_step(W4 W, const void *__restrict__ x,
+__global__ __launch_bounds__(256, (NB == 1 ? 3 : 1)) void k_inproj_step(W4 W, const void *__restrict__ x,
                                                                     const uint16_t *__restrict__ nw, float eps,
                                                                     EpiInProjStep epi, uint32_t *zero_ptr,
                                                                     int nzero)
 {
     constexpr int LPR = 64, CPL = (HIDDEN / 32 + LPR - 1) / LPR, RG = 1;
     constexpr int NCH = HIDDEN / 32;
-    GemvRunner<LPR, CPL, NB, RG, EpiInProjStep> run(W, epi);
     extern __shared__ uint32_t act_lds[];
     __shared__ float red[NB][4];
     if (blockIdx.x == 0 && (int)threadIdx.x < nzero) zero_ptr[threadIdx.x] = 0u;
-    auto ld32 = [&](int b, int c, float *v) {
-        if (XT == BF16) {
-            const uint4 *src = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(x) +
-                                                               (size_t)b * HIDDEN + 32 * c);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint4 w = src[j];
-                v[8 * j + 0] = bf16lo(w.x); v[8 * j + 1] = bf16hi(w.x); v[8 * j + 2] = bf16lo(w.y);
-                v[8 * j + 3] = bf16hi(w.y); v[8 * j + 4] = bf16lo(w.z); v[8 * j + 5] = bf16hi(w.z);
-                v[8 * j + 6] = bf16lo(w.w); v[8 * j + 7] = bf16hi(w.w);
-            }
-        } else {
-            const float4 *src = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(x) +
-                                                                 (size_t)b * HIDDEN + 32 * c);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float4 f = src[j];
-                v[4 * j] = f.x; v[4 * j + 1] = f.y; v[4 * j + 2] = f.z; v[4 * j + 3] = f.w;
-            }
-        }
-    };
-    // one round trip: the thread's x chunk (every batch row) and norm-weight chunk are loaded
-    // together and kept in registers for the second pass
-    float xv[NB][32], w[32];
+    // Raw loads of the thread's x chunk (every batch row) and norm-weight chunk, issued before
+    // the first weight stage: a wave's loads complete in issue order, so the pre-norm then
+    // waits only for these.  Values are widened after the weight loads are in flight.
+    constexpr int XW = XT == BF16 ? 4 : 8;  // 16-byte words per 32 values
     const bool own = (int)threadIdx.x < NCH;
+    uint4 xr[NB][XW], wq[4];
     if (own) {
         const uint4 *wsrc = reinterpret_cast<const uint4 *>(nw + 32 * threadIdx.x);
-        uint4 wq[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) wq[j] = wsrc[j];
 #pragma unroll
-        for (int b = 0; b < NB; ++b) ld32(b, threadIdx.x, xv[b]);
+        for (int b = 0; b < NB; ++b) {
+            const uint4 *src = XT == BF16
+                ? reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(x) + (size_t)b * HIDDEN + 32 * threadIdx.x)
+                : reinterpret_cast<const uint4 *>(reinterpret_cast<const float *>(x) + (size_t)b * HIDDEN + 32 * threadIdx.x);
+#pragma unroll
+            for (int j = 0; j < XW; ++j) xr[b][j] = src[j];
+        }
+    }
+    GemvRunner<LPR, CPL, NB, RG, EpiInProjStep> run(W, epi, 256);
+    float xv[NB][32], w[32];
+    if (own) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             w[8 * j + 0] = bf16lo(wq[j].x); w[8 * j + 1] = bf16hi(wq[j].x); w[8 * j + 2] = bf16lo(wq[j].y);
             w[8 * j + 3] = bf16hi(wq[j].y); w[8 * j + 4] = bf16lo(wq[j].z); w[8 * j + 5] = bf16hi(wq[j].z);
             w[8 * j + 6] = bf16lo(wq[j].w); w[8 * j + 7] = bf16hi(wq[j].w);
         }
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int j = 0; j < XW; ++j) {
+                const uint4 r = xr[b][j];
+                if (XT == BF16) {
+                    xv[b][8 * j + 0] = bf16lo(r.x); xv[b][8 * j + 1] = bf16hi(r.x); xv[b][8 * j + 2] = bf16lo(r.y);
+                    xv[b][8 * j + 3] = bf16hi(r.y); xv[b][8 * j + 4] = bf16lo(r.z); xv[b][8 * j + 5] = bf16hi(r.z);
+                    xv[b][8 * j + 6] = bf16lo(r.w); xv[b][8 * j + 7] = bf16hi(r.w);
+                } else {
+                    xv[b][4 * j + 0] = __uint_as_float(r.x); xv[b][4 * j + 1] = __uint_as_float(r.y);
+                    xv[b][4 * j + 2] = __uint_as_float(r.z); xv[b][4 * j + 3] = __uint_as_float(r.w);
+                }
+            }
     }
     // sum of squares per batch row
 #pragma unroll
@@ -449,8 +459,8 @@ __global__ __launch_bounds__(NB == 1 ? 512 : 256, 1) void k_outproj_step(W4 W, c
                                                          const float *__restrict__ part, float eps,
                                                          EpiStore epi)
 {
-    constexpr int LPR = 64, NCH = DINNER / 32, CPL = NCH / LPR, RG = 1;
-    GemvRunner<LPR, CPL, NB, RG, EpiStore> run(W, epi);
+    constexpr int LPR = 64, NCH = DINNER / 32, CPL = NCH / LPR, RG = 1, NT = NB == 1 ? 512 : 256;
+    GemvRunner<LPR, CPL, NB, RG, EpiStore> run(W, epi, NT);
     extern __shared__ uint32_t act_lds[];
     __shared__ float rstd[NB][NGROUPS];
     auto load = [&](int it, float4 *gv, uint4 *wv) {
@@ -482,7 +492,7 @@ __global__ __launch_bounds__(NB == 1 ? 512 : 256, 1) void k_outproj_step(W4 W, c
     // With at most one chunk per thread (batch 1: 320 chunks, 512 threads) the chunk's gate
     // and weight loads are issued before the group sums are reduced, so the two global round
     // trips overlap.
-    constexpr bool ONE = NB * NCH <= (NB == 1 ? 512 : 256);
+    constexpr bool ONE = NB * NCH <= NT;
     float4 gv0[8];
     uint4 wv0[4];
     if (ONE && (int)threadIdx.x < NB * NCH) load(threadIdx.x, gv0, wv0);
@@ -497,7 +507,7 @@ __global__ __launch_bounds__(NB == 1 ? 512 : 256, 1) void k_outproj_step(W4 W, c
     if (ONE) {
         if ((int)threadIdx.x < NB * NCH) build(threadIdx.x, gv0, wv0);
     } else {
-        for (int it = threadIdx.x; it < NB * NCH; it += blockDim.x) {
+        for (int it = threadIdx.x; it < NB * NCH; it += NT) {
             float4 gv[8];
             uint4 wv[4];
             load(it, gv, wv);
@@ -594,7 +604,7 @@ hipError_t launch_inproj_step(const W4 &W, const void *x, int x_t, const uint16_
     const size_t lds = (size_t)batch * (HIDDEN / 32) * ACT_WORDS * 4;
 #define NH_LAUNCH(NB)                                                                                      \
     {                                                                                                      \
-        const int grid = gemv_grid(W.n, 1, NB == 1 ? 4 : 1);                                                 \
+        const int grid = gemv_grid(W.n, 1, NB == 1 ? 3 : 1);                                                 \
         if (x_t == BF16)                                                                                   \
             launch_k(k_inproj_step<NB, BF16>, dim3(grid), dim3(256), lds, st, W, x, norm_w, eps, e, zero_ptr, \
                      nzero);                                                                               \

@@ -50,7 +50,6 @@
 namespace nh {
 
 constexpr int SC_THREADS = 512;
-constexpr int SC_WAVES = SC_THREADS / 64;
 constexpr int BS_LD = DSTATE + 16;  // B rows: 288 B (transposed reads conflict-free)
 constexpr int XS_LD = HDIM;         // x rows: 160 B (transposed reads conflict-free)
 constexpr int SI_LD = DSTATE + 8;   // S_in rows: 272 B
