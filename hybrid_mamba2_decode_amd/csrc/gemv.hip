@@ -90,11 +90,14 @@ struct GemvShape {
     static constexpr int RPG = 64 / LPR;  // rows per wave-instruction
 };
 
-// Values an epilogue loads one stage ahead, kept exactly as loaded: any arithmetic on them at
-// load time would make the wave wait for every load issued before them, the next stage's
-// weights included.
+// Values an epilogue loads one stage ahead, kept exactly as loaded (16-bit values as 16-bit
+// values, so not even a zero-extension is attached to the load): arithmetic on them before their
+// stage is computed would make the wave wait for every load issued before them, the next
+// stage's weights included.  Loads are unconditional for the same reason (a branch would make
+// the compiler's waits conservative where the paths join).
 struct EpiPre {
-    uint32_t a, b, c, d, e, f;
+    uint16_t h[4];
+    uint32_t w[2];
 };
 
 // y[b][n] = acc + res[b][n]
@@ -102,20 +105,24 @@ struct EpiStore {
     void *y;
     const void *res;
     int y_t, res_t, n;
+    // The residual is read through one buffer resource per dtype; the one not in use (and both
+    // when there is no residual) has no records, so its load returns zero without touching memory.
     __device__ __forceinline__ EpiPre prefetch(int row, int b) const
     {
-        EpiPre p{0u, 0u, 0u, 0u, 0u, 0u};
-        if (res) {
-            const size_t i = (size_t)b * n + row;
-            p.a = res_t == BF16 ? (uint32_t)reinterpret_cast<const uint16_t *>(res)[i]
-                                : __float_as_uint(reinterpret_cast<const float *>(res)[i]);
-        }
+        const uint32_t i = (uint32_t)(b * n + row);
+        const auto r16 = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(res), 0,
+                                                           (res && res_t == BF16) ? 0x7FFFFFFF : 0, 0x00020000);
+        const auto r32 = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(res), 0,
+                                                           (res && res_t != BF16) ? 0x7FFFFFFF : 0, 0x00020000);
+        EpiPre p;
+        p.h[0] = __builtin_amdgcn_raw_buffer_load_b16(r16, 2u * i, 0, 0);
+        p.w[0] = __builtin_amdgcn_raw_buffer_load_b32(r32, 4u * i, 0, 0);
         return p;
     }
     __device__ __forceinline__ void operator()(int row, int b, float v, const EpiPre &p) const
     {
         const size_t i = (size_t)b * n + row;
-        v += res_t == BF16 ? __uint_as_float(p.a << 16) : __uint_as_float(p.a);
+        v += res_t == BF16 ? bf16lo(p.h[0]) : __uint_as_float(p.w[0]);
         if (y_t == BF16)
             reinterpret_cast<uint16_t *>(y)[i] = f32_to_bf16(v);
         else
@@ -136,12 +143,12 @@ struct EpiInProjStep {
         const uint16_t *st = cs + (size_t)b * (CONVK - 1) * CONVDIM + c;
         const uint2 w = *reinterpret_cast<const uint2 *>(cw + 4 * (size_t)c);
         EpiPre p;
-        p.a = st[0];
-        p.b = st[CONVDIM];
-        p.c = st[2 * CONVDIM];
-        p.d = cb[c];
-        p.e = w.x;
-        p.f = w.y;
+        p.h[0] = st[0];
+        p.h[1] = st[CONVDIM];
+        p.h[2] = st[2 * CONVDIM];
+        p.h[3] = cb[c];
+        p.w[0] = w.x;
+        p.w[1] = w.y;
         return p;
     }
     __device__ __forceinline__ void operator()(int n, int b, float acc, const EpiPre &p) const
@@ -152,14 +159,14 @@ struct EpiInProjStep {
         } else if (n < DINNER + CONVDIM) {
             const int c = n - DINNER;
             uint16_t *st = cs + (size_t)b * (CONVK - 1) * CONVDIM + c;
-            float a = bf16lo(p.d);
-            a = fmaf(bf16lo(p.e), bf16lo(p.a), a);
-            a = fmaf(bf16hi(p.e), bf16lo(p.b), a);
-            a = fmaf(bf16lo(p.f), bf16lo(p.c), a);
-            a = fmaf(bf16hi(p.f), bf16_to_f32(vb), a);
+            float a = bf16lo(p.h[3]);
+            a = fmaf(bf16lo(p.w[0]), bf16lo(p.h[0]), a);
+            a = fmaf(bf16hi(p.w[0]), bf16lo(p.h[1]), a);
+            a = fmaf(bf16lo(p.w[1]), bf16lo(p.h[2]), a);
+            a = fmaf(bf16hi(p.w[1]), bf16_to_f32(vb), a);
             xc[(size_t)b * CONVDIM + c] = f32_to_bf16(silu(a));
-            st[0] = (uint16_t)p.b;
-            st[CONVDIM] = (uint16_t)p.c;
+            st[0] = p.h[1];
+            st[CONVDIM] = p.h[2];
             st[2 * CONVDIM] = vb;
         } else {
             dtr[(size_t)b * NHEADS + (n - DINNER - CONVDIM)] = vb;
@@ -171,7 +178,7 @@ struct EpiInProjStep {
 template <int RG, int CPL>
 struct Stage {
     uint4 q[RG][CPL];
-    uint32_t s[RG][CPL], b[RG][CPL];
+    uint16_t s[RG][CPL], b[RG][CPL];  // bf16 bits, widened where used
 };
 
 template <int RG, int CPL>
@@ -193,6 +200,25 @@ __device__ __forceinline__ void load_stage(Stage<RG, CPL> &st, __amdgpu_buffer_r
     }
 }
 
+// One 16-byte chunk of a row against its activations: acc + s * (q . a) + b * sum(a).
+__device__ __forceinline__ float chunk_dot(uint4 q, uint32_t sbits, uint32_t bbits, const ActChunk &a, float acc,
+                                           uint32_t mlo, uint32_t mhi, uint32_t magic)
+{
+    const uint32_t wq[4] = {q.x, q.y, q.z, q.w};
+    float dA = 0.f, dB = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t w = wq[j], wh = w >> 8;
+        dA = dot2h(and_or(w, mlo, magic), a.p[4 * j + 0], dA);
+        dB = dot2h(and_or(w, mhi, magic), a.p[4 * j + 1], dB);
+        dA = dot2h(and_or(wh, mlo, magic), a.p[4 * j + 2], dA);
+        dB = dot2h(and_or(wh, mhi, magic), a.p[4 * j + 3], dB);
+    }
+    const float t = fmaf(dB, 0.0625f, dA) - a.off;
+    const float sc = __uint_as_float(sbits << 16), bi = __uint_as_float(bbits << 16);
+    return fmaf(sc, t, fmaf(bi, a.sum, acc));
+}
+
 template <int LPR, int CPL, int NB, int RG, class Epi>
 __device__ __forceinline__ void compute_stage(const Stage<RG, CPL> &st, const ActChunk (&a)[NB][CPL],
                                               const Epi &epi, const EpiPre &pre, int row0, int n_out,
@@ -206,21 +232,8 @@ __device__ __forceinline__ void compute_stage(const Stage<RG, CPL> &st, const Ac
         for (int b = 0; b < NB; ++b) {
             float s = 0.f;
 #pragma unroll
-            for (int i = 0; i < CPL; ++i) {
-                const uint32_t wq[4] = {st.q[r][i].x, st.q[r][i].y, st.q[r][i].z, st.q[r][i].w};
-                float dA = 0.f, dB = 0.f;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint32_t w = wq[j], wh = w >> 8;
-                    dA = dot2h(and_or(w, mlo, magic), a[b][i].p[4 * j + 0], dA);
-                    dB = dot2h(and_or(w, mhi, magic), a[b][i].p[4 * j + 1], dB);
-                    dA = dot2h(and_or(wh, mlo, magic), a[b][i].p[4 * j + 2], dA);
-                    dB = dot2h(and_or(wh, mhi, magic), a[b][i].p[4 * j + 3], dB);
-                }
-                const float t = fmaf(dB, 0.0625f, dA) - a[b][i].off;
-                const float sc = __uint_as_float(st.s[r][i] << 16), bi = __uint_as_float(st.b[r][i] << 16);
-                s = fmaf(sc, t, fmaf(bi, a[b][i].sum, s));
-            }
+            for (int i = 0; i < CPL; ++i)
+                s = chunk_dot(st.q[r][i], st.s[r][i], st.b[r][i], a[b][i], s, mlo, mhi, magic);
             acc[r][b] = row_sum<LPR>(s);
         }
     // lane li = r*NB + b of each row finishes (row, b); rows are row0 + r*RPG
@@ -308,32 +321,172 @@ struct GemvRunner {
         stride = nwaves * ROWS;
         n0 = xcd * slab + wave * ROWS;
         nlim = min(W.n, (xcd + 1) * slab);
-        if (n0 < nlim) {
-            load_stage<RG, CPL>(A, rq, rs, rb, qoff, soff, (uint32_t)n0, RPG, rowbytes, kg2);
-            pa = epi.prefetch(min(n0 + er * RPG + sub, W.n - 1), eb);
-        }
+        // unconditional (rows past the matrix read zero through the buffer range check): a
+        // branch here would make the compiler's wait before the first use of any earlier load
+        // also cover this stage's loads
+        load_stage<RG, CPL>(A, rq, rs, rb, qoff, soff, (uint32_t)min(n0, W.n), RPG, rowbytes, kg2);
+        pa = epi.prefetch(min(n0 + er * RPG + sub, W.n - 1), eb);
     }
 
     __device__ __forceinline__ void run(const ActChunk (&a)[NB][CPL])
     {
         const uint32_t mlo = 0x000F000Fu, mhi = 0x00F000F0u, magic = 0x64006400u;
         if (n0 >= nlim) return;
-        while (true) {
-            const int n1 = n0 + stride;
-            if (n1 < nlim) {
-                load_stage<RG, CPL>(B, rq, rs, rb, qoff, soff, (uint32_t)n1, RPG, rowbytes, kg2);
-                pb = epi.prefetch(min(n1 + er * RPG + sub, W.n - 1), eb);
+        auto ld = [&](Stage<RG, CPL> &st, EpiPre &pe, int n) {
+            load_stage<RG, CPL>(st, rq, rs, rb, qoff, soff, (uint32_t)n, RPG, rowbytes, kg2);
+            pe = epi.prefetch(min(n + er * RPG + sub, W.n - 1), eb);
+        };
+        // The loop body holds no conditional load: the compiler's wait before a stage's first use
+        // then counts exactly the next stage's loads (where a conditional load's path joins, it
+        // would wait for everything).  Scheduling barriers keep those first uses inside the
+        // compute blocks.  The last one or two stages are peeled.
+        const int nst = (nlim - n0 + stride - 1) / stride;  // stages of this wave, A holds the first
+        int n = n0, i = 0;
+        for (; i + 2 < nst; i += 2, n += 2 * stride) {
+            ld(B, pb, n + stride);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_stage<LPR, CPL, NB, RG>(A, a, epi, pa, n + sub, nlim, li, mlo, mhi, magic);
+            ld(A, pa, n + 2 * stride);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_stage<LPR, CPL, NB, RG>(B, a, epi, pb, n + stride + sub, nlim, li, mlo, mhi, magic);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (i + 1 < nst) {
+            ld(B, pb, n + stride);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_stage<LPR, CPL, NB, RG>(A, a, epi, pa, n + sub, nlim, li, mlo, mhi, magic);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_stage<LPR, CPL, NB, RG>(B, a, epi, pb, n + stride + sub, nlim, li, mlo, mhi, magic);
+        } else {
+            compute_stage<LPR, CPL, NB, RG>(A, a, epi, pa, n + sub, nlim, li, mlo, mhi, magic);
+        }
+    }
+};
+
+// The in_proj rows have K = 4480, i.e. 140 chunks, which do not split evenly over 64 lanes.
+// Lane l covers chunks l and l + 64 of every row (128 chunks); the remaining 12 chunks of R
+// rows are covered by one further load in which lane l takes chunk 128 + l % 12 of row l / 12
+// (lanes 12 R .. 63 idle, with zero activations).  A stage of R rows thus needs 2R + 1 loads
+// per lane instead of 3R, and its R results leave through one epilogue pass.
+#ifndef IP_R1
+#define IP_R1 2
+#endif
+#ifndef IP_WGS1
+#define IP_WGS1 3
+#endif
+constexpr int IP_NCH = HIDDEN / 32;       // 140
+constexpr int IP_TAIL = IP_NCH - 128;     // 12
+constexpr uint32_t IP_ROWB = HIDDEN / 2;  // packed bytes per row
+constexpr uint32_t IP_GRPB = HIDDEN / 32; // scale bytes per row (70 bf16)
+
+template <int R>
+struct IpStage {
+    uint4 q[R][2], qt;
+    uint16_t s[R][2], b[R][2], st, bt;  // bf16 bits, widened where used
+};
+
+template <int R, int NB>
+struct InProjRunner {
+    static_assert(IP_TAIL * R <= 64, "tail chunks of a stage must fit one wave");
+    const EpiInProjStep epi;
+    int li, stride, n0, nlim, nmax, rt;
+    uint32_t toff, tsoff;
+    __amdgpu_buffer_rsrc_t rq, rs, rb;
+    IpStage<R> A, B;
+    EpiPre pa, pb;
+
+    __device__ __forceinline__ void load(IpStage<R> &st, EpiPre &pe, int n) const
+    {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const uint32_t row = (uint32_t)min(n + r, nmax);  // wave-uniform
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                st.q[r][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                    rq, 16u * (li + 64 * i), row * IP_ROWB, 0));
+                st.s[r][i] = __builtin_amdgcn_raw_buffer_load_b16(rs, 2u * ((li + 64 * i) >> 1), row * IP_GRPB, 0);
+                st.b[r][i] = __builtin_amdgcn_raw_buffer_load_b16(rb, 2u * ((li + 64 * i) >> 1), row * IP_GRPB, 0);
             }
-            compute_stage<LPR, CPL, NB, RG>(A, a, epi, pa, n0 + sub, nlim, li, mlo, mhi, magic);
-            if (n1 >= nlim) break;
-            const int n2 = n1 + stride;
-            if (n2 < nlim) {
-                load_stage<RG, CPL>(A, rq, rs, rb, qoff, soff, (uint32_t)n2, RPG, rowbytes, kg2);
-                pa = epi.prefetch(min(n2 + er * RPG + sub, W.n - 1), eb);
+        }
+        const uint32_t trow = (uint32_t)min(n + rt, nmax);
+        st.qt = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, trow * IP_ROWB + toff, 0, 0));
+        st.st = __builtin_amdgcn_raw_buffer_load_b16(rs, trow * IP_GRPB + tsoff, 0, 0);
+        st.bt = __builtin_amdgcn_raw_buffer_load_b16(rb, trow * IP_GRPB + tsoff, 0, 0);
+        pe = epi.prefetch(min(n + min(li / NB, R - 1), nmax), li % NB);
+    }
+
+    __device__ __forceinline__ void compute(const IpStage<R> &st, const EpiPre &pe, int n,
+                                            const ActChunk (&am)[NB][2], const ActChunk (&at)[NB]) const
+    {
+        const uint32_t mlo = 0x000F000Fu, mhi = 0x00F000F0u, magic = 0x64006400u;
+        float tail[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) tail[b] = chunk_dot(st.qt, st.st, st.bt, at[b], 0.f, mlo, mhi, magic);
+        float v = 0.f;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                float s = rt == r ? tail[b] : 0.f;
+                s = chunk_dot(st.q[r][0], st.s[r][0], st.b[r][0], am[b][0], s, mlo, mhi, magic);
+                s = chunk_dot(st.q[r][1], st.s[r][1], st.b[r][1], am[b][1], s, mlo, mhi, magic);
+                s = row_sum<64>(s);
+                if (li == r * NB + b) v = s;
             }
-            compute_stage<LPR, CPL, NB, RG>(B, a, epi, pb, n1 + sub, nlim, li, mlo, mhi, magic);
-            if (n2 >= nlim) break;
-            n0 = n2;
+        const int row = n + li / NB;
+        if (li < R * NB && row < nlim) epi(row, li % NB, v, pe);
+    }
+
+    // Row distribution as in GemvRunner: one contiguous slab of rows per XCD, R rows per wave
+    // and stage.  The first stage is issued here.
+    __device__ __forceinline__ InProjRunner(const W4 &W, const EpiInProjStep &e, int threads) : epi(e)
+    {
+        li = threadIdx.x & 63;
+        const int nx = (gridDim.x & 7) == 0 ? 8 : 1;
+        const int xcd = blockIdx.x % nx;
+        const int wave = __builtin_amdgcn_readfirstlane(
+            (int)((threadIdx.x >> 6) * (gridDim.x / nx) + blockIdx.x / nx));
+        const int nwaves = (gridDim.x / nx) * (threads >> 6);
+        const int slab = (((W.n + nx - 1) / nx + R - 1) / R) * R;
+        rq = __builtin_amdgcn_make_buffer_rsrc((void *)W.q, 0, (int)((uint32_t)W.n * IP_ROWB), 0x00020000);
+        rs = __builtin_amdgcn_make_buffer_rsrc((void *)W.s, 0, (int)((uint32_t)W.n * IP_GRPB), 0x00020000);
+        rb = __builtin_amdgcn_make_buffer_rsrc((void *)W.b, 0, (int)((uint32_t)W.n * IP_GRPB), 0x00020000);
+        rt = min(li / IP_TAIL, R - 1);
+        const uint32_t tc = 128u + (uint32_t)(li % IP_TAIL);
+        toff = 16u * tc;
+        tsoff = 2u * (tc >> 1);
+        stride = nwaves * R;
+        n0 = xcd * slab + wave * R;
+        nlim = min(W.n, (xcd + 1) * slab);
+        nmax = W.n - 1;
+        // unconditional (rows are clamped): a branch here would make the compiler's wait before
+        // the first use of any earlier load also cover this stage's loads
+        load(A, pa, n0);
+    }
+
+    __device__ __forceinline__ void run(const ActChunk (&am)[NB][2], const ActChunk (&at)[NB])
+    {
+        if (n0 >= nlim) return;
+        // No conditional load in the loop body, as in GemvRunner::run.
+        const int nst = (nlim - n0 + stride - 1) / stride;
+        int n = n0, i = 0;
+        for (; i + 2 < nst; i += 2, n += 2 * stride) {
+            load(B, pb, n + stride);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(A, pa, n, am, at);
+            load(A, pa, n + 2 * stride);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(B, pb, n + stride, am, at);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (i + 1 < nst) {
+            load(B, pb, n + stride);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(A, pa, n, am, at);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(B, pb, n + stride, am, at);
+        } else {
+            compute(A, pa, n, am, at);
         }
     }
 };
@@ -366,14 +519,19 @@ __global__ __launch_bounds__(256, (NB == 1 ? (CPL <= 3 ? 3 : 2) : 1)) void k_gem
 
 // Fused pre-norm + in_proj + conv step: the work-group normalises the input rows into LDS
 // (u = bf16(x / rms(x) * w)), then streams its share of in_proj rows.
+template <int NB>
+struct InProjShape {
+    static constexpr int R = NB == 1 ? IP_R1 : 1;      // rows per wave and stage
+    static constexpr int WGS = NB == 1 ? IP_WGS1 : 1;  // work-groups per CU
+};
+
 template <int NB, int XT>
-__global__ __launch_bounds__(256, (NB == 1 ? 3 : 1)) void k_inproj_step(W4 W, const void *__restrict__ x,
+__global__ __launch_bounds__(256, InProjShape<NB>::WGS) void k_inproj_step(W4 W, const void *__restrict__ x,
                                                                     const uint16_t *__restrict__ nw, float eps,
                                                                     EpiInProjStep epi, uint32_t *zero_ptr,
                                                                     int nzero)
 {
-    constexpr int LPR = 64, CPL = (HIDDEN / 32 + LPR - 1) / LPR, RG = 1;
-    constexpr int NCH = HIDDEN / 32;
+    constexpr int NCH = HIDDEN / 32, R = InProjShape<NB>::R;
     extern __shared__ uint32_t act_lds[];
     __shared__ float red[NB][4];
     if (blockIdx.x == 0 && (int)threadIdx.x < nzero) zero_ptr[threadIdx.x] = 0u;
@@ -396,7 +554,8 @@ __global__ __launch_bounds__(256, (NB == 1 ? 3 : 1)) void k_inproj_step(W4 W, co
             for (int j = 0; j < XW; ++j) xr[b][j] = src[j];
         }
     }
-    GemvRunner<LPR, CPL, NB, RG, EpiInProjStep> run(W, epi, 256);
+    __builtin_amdgcn_sched_barrier(0);
+    InProjRunner<R, NB> run(W, epi, 256);
     float xv[NB][32], w[32];
     if (own) {
 #pragma unroll
@@ -444,9 +603,27 @@ __global__ __launch_bounds__(256, (NB == 1 ? 3 : 1)) void k_inproj_step(W4 W, co
         }
     }
     __syncthreads();
-    ActChunk a[NB][CPL];
-    act_from_lds<LPR, CPL, NB>(a, act_lds, NCH, (threadIdx.x & 63) % LPR);
-    run.run(a);
+    // activations of the lane's chunks: l and l + 64 of every row, and its tail chunk
+    ActChunk am[NB][2], at[NB];
+    const int l = threadIdx.x & 63;
+    const bool tail = l < IP_TAIL * R;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const uint32_t *src = act_lds + ((size_t)b * NCH + l + 64 * i) * ACT_WORDS;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) am[b][i].p[j] = src[j];
+            am[b][i].off = __uint_as_float(src[16]);
+            am[b][i].sum = __uint_as_float(src[17]);
+        }
+        const uint32_t *src = act_lds + ((size_t)b * NCH + 128 + l % IP_TAIL) * ACT_WORDS;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) at[b].p[j] = tail ? src[j] : 0u;
+        at[b].off = tail ? __uint_as_float(src[16]) : 0.f;
+        at[b].sum = tail ? __uint_as_float(src[17]) : 0.f;
+    }
+    run.run(am, at);
 }
 
 // Fused gated RMSNorm + out_proj + residual for the per-position block.  The work-group forms
@@ -460,7 +637,6 @@ __global__ __launch_bounds__(NB == 1 ? 512 : 256, 1) void k_outproj_step(W4 W, c
                                                          EpiStore epi)
 {
     constexpr int LPR = 64, NCH = DINNER / 32, CPL = NCH / LPR, RG = 1, NT = NB == 1 ? 512 : 256;
-    GemvRunner<LPR, CPL, NB, RG, EpiStore> run(W, epi, NT);
     extern __shared__ uint32_t act_lds[];
     __shared__ float rstd[NB][NGROUPS];
     auto load = [&](int it, float4 *gv, uint4 *wv) {
@@ -489,19 +665,28 @@ __global__ __launch_bounds__(NB == 1 ? 512 : 256, 1) void k_outproj_step(W4 W, c
         }
         make_chunk(v, act_lds + (size_t)it * ACT_WORDS);
     };
-    // With at most one chunk per thread (batch 1: 320 chunks, 512 threads) the chunk's gate
-    // and weight loads are issued before the group sums are reduced, so the two global round
-    // trips overlap.
+    // The prologue's loads go out before the first weight stage (a wave's loads complete in
+    // issue order): one per-(head, half) sum of squares per thread, 32 of which make a group,
+    // and, with at most one chunk per thread (batch 1: 320 chunks, 512 threads), the chunk's
+    // gate and norm-weight values.
     constexpr bool ONE = NB * NCH <= NT;
+    constexpr int NPART = NHEADS * 2;  // per batch row
     float4 gv0[8];
     uint4 wv0[4];
+    float pv[(NB * NPART + NT - 1) / NT];
+#pragma unroll
+    for (int i = 0; i < (NB * NPART + NT - 1) / NT; ++i) {
+        const int t = threadIdx.x + NT * i;
+        pv[i] = t < NB * NPART ? part[t] : 0.f;
+    }
     if (ONE && (int)threadIdx.x < NB * NCH) load(threadIdx.x, gv0, wv0);
-    if ((int)threadIdx.x < NB * NGROUPS) {
-        const int b = threadIdx.x / NGROUPS, g = threadIdx.x % NGROUPS;
-        const float *pg = part + ((size_t)b * NHEADS + g * HPG) * 2;
-        float t = 0.f;
-        for (int i = 0; i < 2 * HPG; ++i) t += pg[i];
-        rstd[b][g] = 1.0f / sqrtf(t / (float)GNORM + eps);
+    __builtin_amdgcn_sched_barrier(0);
+    GemvRunner<LPR, CPL, NB, RG, EpiStore> run(W, epi, NT);
+#pragma unroll
+    for (int i = 0; i < (NB * NPART + NT - 1) / NT; ++i) {
+        const int t = threadIdx.x + NT * i;  // 32 consecutive entries = one group of one row
+        const float tot = row_sum<32>(pv[i]);
+        if (t < NB * NPART && (t & 31) == 0) rstd[t / NPART][(t % NPART) / 32] = 1.0f / sqrtf(tot / (float)GNORM + eps);
     }
     __syncthreads();
     if (ONE) {
@@ -604,7 +789,7 @@ hipError_t launch_inproj_step(const W4 &W, const void *x, int x_t, const uint16_
     const size_t lds = (size_t)batch * (HIDDEN / 32) * ACT_WORDS * 4;
 #define NH_LAUNCH(NB)                                                                                      \
     {                                                                                                      \
-        const int grid = gemv_grid(W.n, 1, NB == 1 ? 3 : 1);                                                 \
+        const int grid = gemv_grid(W.n, InProjShape<NB>::R, InProjShape<NB>::WGS);                             \
         if (x_t == BF16)                                                                                   \
             launch_k(k_inproj_step<NB, BF16>, dim3(grid), dim3(256), lds, st, W, x, norm_w, eps, e, zero_ptr, \
                      nzero);                                                                               \

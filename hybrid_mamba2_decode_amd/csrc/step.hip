@@ -36,26 +36,34 @@ __global__ __launch_bounds__(256) void k_ssm_step(const uint16_t *__restrict__ x
     const int g = h / HPG;
     const int nl = threadIdx.x & 31, slot = threadIdx.x >> 5;
 
-    const float dt = softplus(bf16_to_f32(dtr[(size_t)b * ld_dt + h]) + dt_bias[h]);
-    const float A = -expf(A_log[h]);
-    const float dA = expf(dt * A);
-    const float Dh = Dp[h];
-
+    // Every load is issued before any arithmetic: the small parameter loads first, then the
+    // state rows.  A wave's loads complete in issue order, so the discretisation (which needs
+    // dt) then waits only for the parameters while the 20 KB of state are still in flight.
     const uint16_t *xb = xc + (size_t)b * CONVDIM;
+    const uint16_t dtb = dtr[(size_t)b * ld_dt + h];
     const uint2 bw = *reinterpret_cast<const uint2 *>(xb + OFF_B + g * DSTATE + 4 * nl);
     const uint2 cw = *reinterpret_cast<const uint2 *>(xb + OFF_C + g * DSTATE + 4 * nl);
-    const float B0 = bf16lo(bw.x), B1 = bf16hi(bw.x), B2 = bf16lo(bw.y), B3 = bf16hi(bw.y);
-    const float C0 = bf16lo(cw.x), C1 = bf16hi(cw.x), C2 = bf16lo(cw.y), C3 = bf16hi(cw.y);
-
+    uint16_t xr[SSM_IT];
+#pragma unroll
+    for (int it = 0; it < SSM_IT; ++it) xr[it] = xb[h * HDIM + half * SSM_ROWS + slot + 8 * it];
+    __builtin_amdgcn_sched_barrier(0);
     float4 *Sh = reinterpret_cast<float4 *>(S + ((size_t)b * NHEADS + h) * HDIM * DSTATE);
     float4 s[SSM_IT];
-    float xp[SSM_IT];
 #pragma unroll
     for (int it = 0; it < SSM_IT; ++it) {
         const int p = half * SSM_ROWS + slot + 8 * it;
         s[it] = ld_nt(Sh + p * (DSTATE / 4) + nl);
-        xp[it] = bf16_to_f32(xb[h * HDIM + p]);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    const float dt = softplus(bf16_to_f32(dtb) + dt_bias[h]);
+    const float A = -expf(A_log[h]);
+    const float dA = expf(dt * A);
+    const float Dh = Dp[h];
+    const float B0 = bf16lo(bw.x), B1 = bf16hi(bw.x), B2 = bf16lo(bw.y), B3 = bf16hi(bw.y);
+    const float C0 = bf16lo(cw.x), C1 = bf16hi(cw.x), C2 = bf16lo(cw.y), C3 = bf16hi(cw.y);
+    float xp[SSM_IT];
+#pragma unroll
+    for (int it = 0; it < SSM_IT; ++it) xp[it] = bf16_to_f32(xr[it]);
     float yv[SSM_IT];
 #pragma unroll
     for (int it = 0; it < SSM_IT; ++it) {
