@@ -367,13 +367,13 @@ struct GemvRunner {
 // Lane l covers chunks l and l + 64 of every row (128 chunks); the remaining 12 chunks of R
 // rows are covered by one further load in which lane l takes chunk 128 + l % 12 of row l / 12
 // (lanes 12 R .. 63 idle, with zero activations).  A stage of R rows thus needs 2R + 1 loads
-// per lane instead of 3R, and its R results leave through one epilogue pass.
-#ifndef IP_R1
-#define IP_R1 2
-#endif
-#ifndef IP_WGS1
-#define IP_WGS1 3
-#endif
+// per lane instead of 3R.
+//
+// Each wave owns one contiguous block of RW = R NS rows (NS stages, fully unrolled, two stages
+// in flight).  Row results collect in lanes (one lane per row and batch row), and the
+// epilogue, with its conv-state prefetch, runs once per wave at the end: no stores sit among
+// the streaming loads, and the epilogue's branches are uniform (block boundaries are multiples
+// of 8, as are the z | xBC | dt_raw boundaries).
 constexpr int IP_NCH = HIDDEN / 32;       // 140
 constexpr int IP_TAIL = IP_NCH - 128;     // 12
 constexpr uint32_t IP_ROWB = HIDDEN / 2;  // packed bytes per row
@@ -385,109 +385,113 @@ struct IpStage {
     uint16_t s[R][2], b[R][2], st, bt;  // bf16 bits, widened where used
 };
 
-template <int R, int NB>
-struct InProjRunner {
-    static_assert(IP_TAIL * R <= 64, "tail chunks of a stage must fit one wave");
-    const EpiInProjStep epi;
-    int li, stride, n0, nlim, nmax, rt;
-    uint32_t toff, tsoff;
-    __amdgpu_buffer_rsrc_t rq, rs, rb;
-    IpStage<R> A, B;
-    EpiPre pa, pb;
+template <int NB>
+struct InProjShape {
+    static constexpr int R = NB == 1 ? 2 : 1;        // rows per stage
+    static constexpr int NS = NB == 1 ? 4 : 8;       // stages per wave
+    static constexpr int RW = R * NS;                // rows per wave
+    static constexpr int NT = NB == 1 ? 768 : 256;   // threads per work-group
+    static_assert(IP_TAIL * R <= 64 && RW * NB <= 64, "stage or block too large for one wave");
+};
 
-    __device__ __forceinline__ void load(IpStage<R> &st, EpiPre &pe, int n) const
+// Work-groups run on XCD (index mod 8); the blocks are split into one contiguous range per XCD.
+template <int NB>
+static inline int inproj_grid(int n)
+{
+    using S = InProjShape<NB>;
+    const int nblk = (n + S::RW - 1) / S::RW, bx = (nblk + 7) / 8, wpg = S::NT / 64;
+    return 8 * ((bx + wpg - 1) / wpg);
+}
+
+template <int NB>
+struct InProjBlock {
+    using S = InProjShape<NB>;
+    static constexpr int R = S::R, NS = S::NS, RW = S::RW;
+    const EpiInProjStep epi;
+    int li, rb, nmax, rt;
+    bool active;
+    uint32_t toff, tsoff;
+    __amdgpu_buffer_rsrc_t rq, rs, rbias;
+    IpStage<R> st[2];
+    EpiPre pe;
+
+    __device__ __forceinline__ void load(IpStage<R> &g, int n) const
     {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const uint32_t row = (uint32_t)min(n + r, nmax);  // wave-uniform
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                st.q[r][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                g.q[r][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                     rq, 16u * (li + 64 * i), row * IP_ROWB, 0));
-                st.s[r][i] = __builtin_amdgcn_raw_buffer_load_b16(rs, 2u * ((li + 64 * i) >> 1), row * IP_GRPB, 0);
-                st.b[r][i] = __builtin_amdgcn_raw_buffer_load_b16(rb, 2u * ((li + 64 * i) >> 1), row * IP_GRPB, 0);
+                g.s[r][i] = __builtin_amdgcn_raw_buffer_load_b16(rs, 2u * ((li + 64 * i) >> 1), row * IP_GRPB, 0);
+                g.b[r][i] = __builtin_amdgcn_raw_buffer_load_b16(rbias, 2u * ((li + 64 * i) >> 1), row * IP_GRPB, 0);
             }
         }
         const uint32_t trow = (uint32_t)min(n + rt, nmax);
-        st.qt = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, trow * IP_ROWB + toff, 0, 0));
-        st.st = __builtin_amdgcn_raw_buffer_load_b16(rs, trow * IP_GRPB + tsoff, 0, 0);
-        st.bt = __builtin_amdgcn_raw_buffer_load_b16(rb, trow * IP_GRPB + tsoff, 0, 0);
-        pe = epi.prefetch(min(n + min(li / NB, R - 1), nmax), li % NB);
+        g.qt = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, trow * IP_ROWB + toff, 0, 0));
+        g.st = __builtin_amdgcn_raw_buffer_load_b16(rs, trow * IP_GRPB + tsoff, 0, 0);
+        g.bt = __builtin_amdgcn_raw_buffer_load_b16(rbias, trow * IP_GRPB + tsoff, 0, 0);
     }
 
-    __device__ __forceinline__ void compute(const IpStage<R> &st, const EpiPre &pe, int n,
-                                            const ActChunk (&am)[NB][2], const ActChunk (&at)[NB]) const
+    // stage k of the block: its R row sums go to lanes (k R + r) NB + b
+    __device__ __forceinline__ void compute(const IpStage<R> &g, int k, const ActChunk (&am)[NB][2],
+                                            const ActChunk (&at)[NB], float &v) const
     {
         const uint32_t mlo = 0x000F000Fu, mhi = 0x00F000F0u, magic = 0x64006400u;
         float tail[NB];
 #pragma unroll
-        for (int b = 0; b < NB; ++b) tail[b] = chunk_dot(st.qt, st.st, st.bt, at[b], 0.f, mlo, mhi, magic);
-        float v = 0.f;
+        for (int b = 0; b < NB; ++b) tail[b] = chunk_dot(g.qt, g.st, g.bt, at[b], 0.f, mlo, mhi, magic);
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
                 float s = rt == r ? tail[b] : 0.f;
-                s = chunk_dot(st.q[r][0], st.s[r][0], st.b[r][0], am[b][0], s, mlo, mhi, magic);
-                s = chunk_dot(st.q[r][1], st.s[r][1], st.b[r][1], am[b][1], s, mlo, mhi, magic);
+                s = chunk_dot(g.q[r][0], g.s[r][0], g.b[r][0], am[b][0], s, mlo, mhi, magic);
+                s = chunk_dot(g.q[r][1], g.s[r][1], g.b[r][1], am[b][1], s, mlo, mhi, magic);
                 s = row_sum<64>(s);
-                if (li == r * NB + b) v = s;
+                if (li == (k * R + r) * NB + b) v = s;
             }
-        const int row = n + li / NB;
-        if (li < R * NB && row < nlim) epi(row, li % NB, v, pe);
     }
 
-    // Row distribution as in GemvRunner: one contiguous slab of rows per XCD, R rows per wave
-    // and stage.  The first stage is issued here.
-    __device__ __forceinline__ InProjRunner(const W4 &W, const EpiInProjStep &e, int threads) : epi(e)
+    // Issues the epilogue prefetch and the first stage (unconditionally, rows clamped: a
+    // branch here would make the compiler's wait before the first use of any earlier load
+    // also cover these loads; idle waves read the last row, which the cache holds).
+    __device__ __forceinline__ InProjBlock(const W4 &W, const EpiInProjStep &e) : epi(e)
     {
         li = threadIdx.x & 63;
-        const int nx = (gridDim.x & 7) == 0 ? 8 : 1;
-        const int xcd = blockIdx.x % nx;
+        const int xcd = blockIdx.x & 7;
         const int wave = __builtin_amdgcn_readfirstlane(
-            (int)((threadIdx.x >> 6) * (gridDim.x / nx) + blockIdx.x / nx));
-        const int nwaves = (gridDim.x / nx) * (threads >> 6);
-        const int slab = (((W.n + nx - 1) / nx + R - 1) / R) * R;
+            (int)((threadIdx.x >> 6) * (gridDim.x >> 3) + (blockIdx.x >> 3)));
+        const int nblk = (W.n + RW - 1) / RW, bx = (nblk + 7) / 8;
+        const int blk = xcd * bx + wave;
+        active = wave < bx && blk < nblk;
+        rb = min(blk, nblk - 1) * RW;
+        nmax = W.n - 1;
         rq = __builtin_amdgcn_make_buffer_rsrc((void *)W.q, 0, (int)((uint32_t)W.n * IP_ROWB), 0x00020000);
         rs = __builtin_amdgcn_make_buffer_rsrc((void *)W.s, 0, (int)((uint32_t)W.n * IP_GRPB), 0x00020000);
-        rb = __builtin_amdgcn_make_buffer_rsrc((void *)W.b, 0, (int)((uint32_t)W.n * IP_GRPB), 0x00020000);
+        rbias = __builtin_amdgcn_make_buffer_rsrc((void *)W.b, 0, (int)((uint32_t)W.n * IP_GRPB), 0x00020000);
         rt = min(li / IP_TAIL, R - 1);
         const uint32_t tc = 128u + (uint32_t)(li % IP_TAIL);
         toff = 16u * tc;
         tsoff = 2u * (tc >> 1);
-        stride = nwaves * R;
-        n0 = xcd * slab + wave * R;
-        nlim = min(W.n, (xcd + 1) * slab);
-        nmax = W.n - 1;
-        // unconditional (rows are clamped): a branch here would make the compiler's wait before
-        // the first use of any earlier load also cover this stage's loads
-        load(A, pa, n0);
+        load(st[0], rb);
+        pe = epi.prefetch(min(rb + min(li / NB, RW - 1), nmax), li % NB);
     }
 
     __device__ __forceinline__ void run(const ActChunk (&am)[NB][2], const ActChunk (&at)[NB])
     {
-        if (n0 >= nlim) return;
-        // No conditional load in the loop body, as in GemvRunner::run.
-        const int nst = (nlim - n0 + stride - 1) / stride;
-        int n = n0, i = 0;
-        for (; i + 2 < nst; i += 2, n += 2 * stride) {
-            load(B, pb, n + stride);
+        if (!active) return;
+        float v = 0.f;
+#pragma unroll
+        for (int k = 0; k < NS; ++k) {
+            if (k + 1 < NS) load(st[(k + 1) & 1], rb + (k + 1) * R);
             __builtin_amdgcn_sched_barrier(0);
-            compute(A, pa, n, am, at);
-            load(A, pa, n + 2 * stride);
-            __builtin_amdgcn_sched_barrier(0);
-            compute(B, pb, n + stride, am, at);
+            compute(st[k & 1], k, am, at, v);
             __builtin_amdgcn_sched_barrier(0);
         }
-        if (i + 1 < nst) {
-            load(B, pb, n + stride);
-            __builtin_amdgcn_sched_barrier(0);
-            compute(A, pa, n, am, at);
-            __builtin_amdgcn_sched_barrier(0);
-            compute(B, pb, n + stride, am, at);
-        } else {
-            compute(A, pa, n, am, at);
-        }
+        const int row = rb + li / NB;
+        if (li < RW * NB && row <= nmax) epi(row, li % NB, v, pe);
     }
 };
 
@@ -519,21 +523,15 @@ __global__ __launch_bounds__(256, (NB == 1 ? (CPL <= 3 ? 3 : 2) : 1)) void k_gem
 
 // Fused pre-norm + in_proj + conv step: the work-group normalises the input rows into LDS
 // (u = bf16(x / rms(x) * w)), then streams its share of in_proj rows.
-template <int NB>
-struct InProjShape {
-    static constexpr int R = NB == 1 ? IP_R1 : 1;      // rows per wave and stage
-    static constexpr int WGS = NB == 1 ? IP_WGS1 : 1;  // work-groups per CU
-};
-
 template <int NB, int XT>
-__global__ __launch_bounds__(256, InProjShape<NB>::WGS) void k_inproj_step(W4 W, const void *__restrict__ x,
+__global__ __launch_bounds__(InProjShape<NB>::NT, 1) void k_inproj_step(W4 W, const void *__restrict__ x,
                                                                     const uint16_t *__restrict__ nw, float eps,
                                                                     EpiInProjStep epi, uint32_t *zero_ptr,
                                                                     int nzero)
 {
-    constexpr int NCH = HIDDEN / 32, R = InProjShape<NB>::R;
+    constexpr int NCH = HIDDEN / 32, R = InProjShape<NB>::R, NW = InProjShape<NB>::NT / 64;
     extern __shared__ uint32_t act_lds[];
-    __shared__ float red[NB][4];
+    __shared__ float red[NB][NW];
     if (blockIdx.x == 0 && (int)threadIdx.x < nzero) zero_ptr[threadIdx.x] = 0u;
     // Raw loads of the thread's x chunk (every batch row) and norm-weight chunk, issued before
     // the first weight stage: a wave's loads complete in issue order, so the pre-norm then
@@ -555,7 +553,7 @@ __global__ __launch_bounds__(256, InProjShape<NB>::WGS) void k_inproj_step(W4 W,
         }
     }
     __builtin_amdgcn_sched_barrier(0);
-    InProjRunner<R, NB> run(W, epi, 256);
+    InProjBlock<NB> run(W, epi);
     float xv[NB][32], w[32];
     if (own) {
 #pragma unroll
@@ -594,7 +592,9 @@ __global__ __launch_bounds__(256, InProjShape<NB>::WGS) void k_inproj_step(W4 W,
     if (own) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            const float tot = (red[b][0] + red[b][1]) + (red[b][2] + red[b][3]);
+            float tot = 0.f;
+#pragma unroll
+            for (int i = 0; i < NW; ++i) tot += red[b][i];
             const float r = 1.0f / sqrtf(tot / (float)HIDDEN + eps);
             float v[32];
 #pragma unroll
@@ -789,13 +789,12 @@ hipError_t launch_inproj_step(const W4 &W, const void *x, int x_t, const uint16_
     const size_t lds = (size_t)batch * (HIDDEN / 32) * ACT_WORDS * 4;
 #define NH_LAUNCH(NB)                                                                                      \
     {                                                                                                      \
-        const int grid = gemv_grid(W.n, InProjShape<NB>::R, InProjShape<NB>::WGS);                             \
+        const int grid = inproj_grid<NB>(W.n);                                                             \
+        const dim3 blk(InProjShape<NB>::NT);                                                               \
         if (x_t == BF16)                                                                                   \
-            launch_k(k_inproj_step<NB, BF16>, dim3(grid), dim3(256), lds, st, W, x, norm_w, eps, e, zero_ptr, \
-                     nzero);                                                                               \
+            launch_k(k_inproj_step<NB, BF16>, dim3(grid), blk, lds, st, W, x, norm_w, eps, e, zero_ptr, nzero); \
         else                                                                                               \
-            launch_k(k_inproj_step<NB, F32>, dim3(grid), dim3(256), lds, st, W, x, norm_w, eps, e, zero_ptr,  \
-                     nzero);                                                                               \
+            launch_k(k_inproj_step<NB, F32>, dim3(grid), blk, lds, st, W, x, norm_w, eps, e, zero_ptr, nzero);  \
     }
     switch (batch) {
     case 1: NH_LAUNCH(1); break;
