@@ -665,8 +665,9 @@ __global__ __launch_bounds__(NB == 1 ? 512 : 256, 1) void k_outproj_step(W4 W, c
         }
         make_chunk(v, act_lds + (size_t)it * ACT_WORDS);
     };
-    // The prologue's loads go out before the first weight stage (a wave's loads complete in
-    // issue order): one per-(head, half) sum of squares per thread, 32 of which make a group,
+    // The prologue's loads go out alone, and the weight stream starts only once the work-group
+    // has them (after the first barrier; issued together, they would queue behind every wave's
+    // weight loads): one per-(head, half) sum of squares per thread, 32 of which make a group,
     // and, with at most one chunk per thread (batch 1: 320 chunks, 512 threads), the chunk's
     // gate and norm-weight values.
     constexpr bool ONE = NB * NCH <= NT;
@@ -680,15 +681,15 @@ __global__ __launch_bounds__(NB == 1 ? 512 : 256, 1) void k_outproj_step(W4 W, c
         pv[i] = t < NB * NPART ? part[t] : 0.f;
     }
     if (ONE && (int)threadIdx.x < NB * NCH) load(threadIdx.x, gv0, wv0);
-    __builtin_amdgcn_sched_barrier(0);
-    GemvRunner<LPR, CPL, NB, RG, EpiStore> run(W, epi, NT);
 #pragma unroll
     for (int i = 0; i < (NB * NPART + NT - 1) / NT; ++i) {
         const int t = threadIdx.x + NT * i;  // 32 consecutive entries = one group of one row
         const float tot = row_sum<32>(pv[i]);
         if (t < NB * NPART && (t & 31) == 0) rstd[t / NPART][(t % NPART) / 32] = 1.0f / sqrtf(tot / (float)GNORM + eps);
     }
+    __builtin_amdgcn_s_waitcnt(0);  // the gate and norm-weight loads too
     __syncthreads();
+    GemvRunner<LPR, CPL, NB, RG, EpiStore> run(W, epi, NT);
     if (ONE) {
         if ((int)threadIdx.x < NB * NCH) build(threadIdx.x, gv0, wv0);
     } else {
