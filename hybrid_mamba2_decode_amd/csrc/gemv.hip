@@ -67,22 +67,26 @@ struct ActChunk {
     uint32_t p[16];
     float off, sum;
 };
-constexpr int ACT_WORDS = 18;
+constexpr int ACT_WORDS = 20;  // 80-byte slots: 16-byte reads, conflict-free across lanes
 
-// Build one chunk from 32 bf16-exact floats v[0..31].
+// Build one chunk from 32 bf16-exact floats v[0..31] into its 80-byte LDS slot (16-byte
+// aligned: five 16-byte writes).
 __device__ __forceinline__ void make_chunk(const float *v, uint32_t *dst)
 {
     float se = 0.f, so = 0.f;
+    uint32_t w[16];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float lo = v[8 * j + e], hi = v[8 * j + e + 4];
-            dst[4 * j + e] = pack_f16x2(lo, hi);
+            w[4 * j + e] = pack_f16x2(lo, hi);
             if (e & 1) so += lo + hi; else se += lo + hi;
         }
-    dst[16] = __float_as_uint(fmaf(1024.f, se, 64.f * so));
-    dst[17] = __float_as_uint(se + so);
+    uint4 *d4 = reinterpret_cast<uint4 *>(dst);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) d4[j] = make_uint4(w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]);
+    d4[4] = make_uint4(__float_as_uint(fmaf(1024.f, se, 64.f * so)), __float_as_uint(se + so), 0u, 0u);
 }
 
 template <int LPR>
@@ -248,6 +252,23 @@ __device__ __forceinline__ void compute_stage(const Stage<RG, CPL> &st, const Ac
     if (li < RG * NB && row < n_out) epi(row, eb, v, pre);
 }
 
+// One activation chunk from its 80-byte LDS slot (five 16-byte reads).
+__device__ __forceinline__ void chunk_from_lds(ActChunk &a, const uint32_t *src)
+{
+    const uint4 *s4 = reinterpret_cast<const uint4 *>(src);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint4 w = s4[j];
+        a.p[4 * j] = w.x;
+        a.p[4 * j + 1] = w.y;
+        a.p[4 * j + 2] = w.z;
+        a.p[4 * j + 3] = w.w;
+    }
+    const uint4 t = s4[4];
+    a.off = __uint_as_float(t.x);
+    a.sum = __uint_as_float(t.y);
+}
+
 // Activations staged in LDS: [NB][nch][ACT_WORDS] words.
 template <int LPR, int CPL, int NB>
 __device__ __forceinline__ void act_from_lds(ActChunk (&a)[NB][CPL], const uint32_t *lds, int nch, int li)
@@ -258,11 +279,7 @@ __device__ __forceinline__ void act_from_lds(ActChunk (&a)[NB][CPL], const uint3
         for (int i = 0; i < CPL; ++i) {
             const int c = li + LPR * i;
             if (c < nch) {
-                const uint32_t *src = lds + ((size_t)b * nch + c) * ACT_WORDS;
-#pragma unroll
-                for (int j = 0; j < 16; ++j) a[b][i].p[j] = src[j];
-                a[b][i].off = __uint_as_float(src[16]);
-                a[b][i].sum = __uint_as_float(src[17]);
+                chunk_from_lds(a[b][i], lds + ((size_t)b * nch + c) * ACT_WORDS);
             } else {
 #pragma unroll
                 for (int j = 0; j < 16; ++j) a[b][i].p[j] = 0u;
@@ -501,7 +518,7 @@ template <int LPR, int CPL, int NB, int RG>
 __global__ __launch_bounds__(256, (NB == 1 ? (CPL <= 3 ? 3 : 2) : 1)) void k_gemv(W4 W, const uint16_t *__restrict__ x, EpiStore epi)
 {
     GemvRunner<LPR, CPL, NB, RG, EpiStore> run(W, epi, 256);
-    extern __shared__ uint32_t act_lds[];
+    extern __shared__ __attribute__((aligned(16))) uint32_t act_lds[];
     const int nch = W.k >> 5;
     for (int it = threadIdx.x; it < NB * nch; it += 256) {
         const uint4 *src = reinterpret_cast<const uint4 *>(x + (size_t)it * 32);  // [b][c] = b*nch + c
@@ -530,7 +547,7 @@ __global__ __launch_bounds__(InProjShape<NB>::NT, 1) void k_inproj_step(W4 W, co
                                                                     int nzero)
 {
     constexpr int NCH = HIDDEN / 32, R = InProjShape<NB>::R, NW = InProjShape<NB>::NT / 64;
-    extern __shared__ uint32_t act_lds[];
+    extern __shared__ __attribute__((aligned(16))) uint32_t act_lds[];
     __shared__ float red[NB][NW];
     if (blockIdx.x == 0 && (int)threadIdx.x < nzero) zero_ptr[threadIdx.x] = 0u;
     // Raw loads of the thread's x chunk (every batch row) and norm-weight chunk, issued before
@@ -611,17 +628,15 @@ __global__ __launch_bounds__(InProjShape<NB>::NT, 1) void k_inproj_step(W4 W, co
     for (int b = 0; b < NB; ++b) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const uint32_t *src = act_lds + ((size_t)b * NCH + l + 64 * i) * ACT_WORDS;
-#pragma unroll
-            for (int j = 0; j < 16; ++j) am[b][i].p[j] = src[j];
-            am[b][i].off = __uint_as_float(src[16]);
-            am[b][i].sum = __uint_as_float(src[17]);
+            chunk_from_lds(am[b][i], act_lds + ((size_t)b * NCH + l + 64 * i) * ACT_WORDS);
         }
-        const uint32_t *src = act_lds + ((size_t)b * NCH + 128 + l % IP_TAIL) * ACT_WORDS;
+        chunk_from_lds(at[b], act_lds + ((size_t)b * NCH + 128 + l % IP_TAIL) * ACT_WORDS);
+        if (!tail) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) at[b].p[j] = tail ? src[j] : 0u;
-        at[b].off = tail ? __uint_as_float(src[16]) : 0.f;
-        at[b].sum = tail ? __uint_as_float(src[17]) : 0.f;
+            for (int j = 0; j < 16; ++j) at[b].p[j] = 0u;
+            at[b].off = 0.f;
+            at[b].sum = 0.f;
+        }
     }
     run.run(am, at);
 }
@@ -637,7 +652,7 @@ __global__ __launch_bounds__(NB == 1 ? 512 : 256, 1) void k_outproj_step(W4 W, c
                                                          EpiStore epi)
 {
     constexpr int LPR = 64, NCH = DINNER / 32, CPL = NCH / LPR, RG = 1, NT = NB == 1 ? 512 : 256;
-    extern __shared__ uint32_t act_lds[];
+    extern __shared__ __attribute__((aligned(16))) uint32_t act_lds[];
     __shared__ float rstd[NB][NGROUPS];
     auto load = [&](int it, float4 *gv, uint4 *wv) {
         const int b = it / NCH, c = it % NCH;
