@@ -262,7 +262,7 @@ __global__ __launch_bounds__(SC_THREADS, 1) void k_ssd_scan(const uint16_t *__re
     const uint32_t vc1 = (uint32_t)(16 * I1 + l16) * XROW + (OFF_C + g * DSTATE + 8 * q4) * 2;
     const uint32_t vdt = (uint32_t)tid * DROW + h * 2;
 
-    auto prefetch = [&](Prefetch &pf, int t0) {
+    auto prefetch_bx = [&](Prefetch &pf, int t0) {
         const uint32_t rows = (uint32_t)min(Q, T - t0);
         const __amdgpu_buffer_rsrc_t rx = rsrc(xseq + (size_t)t0 * XROW, rows * XROW);
         const __amdgpu_buffer_rsrc_t rd = rsrc(dseq + (size_t)t0 * DROW, rows * DROW);
@@ -270,12 +270,20 @@ __global__ __launch_bounds__(SC_THREADS, 1) void k_ssd_scan(const uint16_t *__re
         for (int i = 0; i < PB_VEC; ++i) pf.b[i] = bload16(rx, vb + (uint32_t)i * 32 * XROW, 0);
 #pragma unroll
         for (int e = 0; e < PX_VEC; ++e) pf.x[e] = bload16(rx, vx + 16 * e, 0);
+        pf.dt = __builtin_amdgcn_raw_buffer_load_b16(rd, vdt, 0, 0);
+    };
+    auto prefetch_c = [&](Prefetch &pf, int t0) {
+        const uint32_t rows = (uint32_t)min(Q, T - t0);
+        const __amdgpu_buffer_rsrc_t rx = rsrc(xseq + (size_t)t0 * XROW, rows * XROW);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             pf.c[0][ks] = bload16(rx, vc0 + 64 * ks, 0);
             pf.c[1][ks] = bload16(rx, vc1 + 64 * ks, 0);
         }
-        pf.dt = __builtin_amdgcn_raw_buffer_load_b16(rd, vdt, 0, 0);
+    };
+    auto prefetch = [&](Prefetch &pf, int t0) {
+        prefetch_bx(pf, t0);
+        prefetch_c(pf, t0);
     };
 
     // State: st[pb] holds S[16pb + 4q4 + r][16 wave + l16], r = 0..3.
@@ -340,6 +348,8 @@ __global__ __launch_bounds__(SC_THREADS, 1) void k_ssd_scan(const uint16_t *__re
         }
         const int t1 = t0 + Q;
         __syncthreads();
+        // the next chunk's B, x and dt rows (their registers were consumed by step 1)
+        if (t1 < T) prefetch_bx(pf, t1);
 
         // ---- 3. outputs of blocks I0, I1
         const int nblk = (L + 15) >> 4;
@@ -452,7 +462,7 @@ __global__ __launch_bounds__(SC_THREADS, 1) void k_ssd_scan(const uint16_t *__re
         }
         // ---- 2. the next chunk into registers (free once this chunk's outputs are done;
         // the loads land during step 4)
-        if (t1 < T) prefetch(pf, t1);
+        if (t1 < T) prefetch_c(pf, t1);
 
         // ---- 4. state: S = exp(cum_{L-1}) S + x^T (w B) over this wave's 16 columns
         const float dec = __builtin_amdgcn_exp2f(cl);
