@@ -11,18 +11,17 @@
 // Activations arrive as fp16 bits (bf16-exact values), so every product is exact and the
 // accumulation is fp32 inside v_mfma_f32_32x32x16_f16.
 //
-// Tiling: 128 x 128 output tile per work-group of 4 waves (2 x 2), each wave 64 x 64 as
-// 2 x 2 MFMA 32x32 tiles, K advanced two 64-wide quantisation groups per pipeline step.  The X
-// tile is staged through LDS (double-buffered, padded rows); each wave reads its W rows straight
-// from global memory into registers, one step ahead.
+// Tiling: a 256 x 128 output tile per work-group of 8 waves with split roles.  Waves 4-7 load:
+// one quantisation group (K = 64) of the X tile and of the W tile per step, from global memory
+// into registers three steps ahead of use; they dequantise W to fp16 and write both tiles into
+// a ring of three LDS slots.  Waves 0-3 compute: each owns a 128 x 64 block of the tile (4 x 2
+// MFMA 32x32 tiles) and only reads LDS and issues MFMAs.  One barrier per step: at step k the
+// compute waves read slot k mod 3 while the loaders fill slot (k + 2) mod 3, which the compute
+// waves left at step k - 1.
 #include "nh_device.hpp"
 #include "nh_kernels.hpp"
 
 namespace nh {
-
-constexpr int GBM = 128, GBN = 128, GBK = 64;
-constexpr int GKS = 2;                  // quantisation groups per pipeline step
-constexpr int GALD = GKS * GBK + 8;     // LDS row of the X tile, in fp16 elements (272 B)
 
 // Eight fp16 values in pair order (0,4) (1,5) (2,6) (3,7), matching the nibble extraction.
 __device__ __forceinline__ uint4 pair_order16(uint4 v)
@@ -57,168 +56,174 @@ struct GemmEpi {
     int y_t, res_t;
 };
 
-// One pipeline step covers GKS quantisation groups (K = 128): the X tile of the step is in
-// LDS (double-buffered), the W words and scales of the step are in registers (double-buffered),
-// and the next step's loads are in flight while this step's 32 MFMAs per wave run.  The W words
-// are dequantised just before their MFMA step.
-__global__ __launch_bounds__(256, 2) void k_w4_gemm(W4 W, const uint16_t *__restrict__ Xh,
-                                                    const float *__restrict__ su, int M, GemmEpi ep)
+constexpr int WS_BM = 256, WS_BN = 128, WS_SLOTS = 3, WS_THREADS = 512;
+
+// One LDS slot: the operands of one step (one quantisation group of the tile).
+struct WsSlot {
+    uint4 x[WS_BM * 8];  // fp16 X tile, [row][chunk], pair order inside a chunk
+    uint4 w[WS_BN * 8];  // fp16 s (q - 8) tile, [column][chunk], pair order inside a chunk
+    float bpp[WS_BN];    // beta + 8 s per column (zero for symmetric groups)
+    float su[WS_BM];     // group sum of each X row
+};
+
+// An LDS tile row is 8 chunks of 16 bytes; chunk c of row r sits at position
+// c ^ (r mod 8) ^ (r / 8 mod 2), so 16-byte accesses by 16 lanes to one chunk of 16 consecutive
+// rows, or to all chunks of 2 rows, touch each of the 64 banks once.
+__device__ __forceinline__ int ws_sw(int row, int c) { return row * 8 + (c ^ (row & 7) ^ ((row >> 3) & 1)); }
+
+// A loader lane's global loads for one step: 8 x 16 bytes of X (rows 32 i + lane / 8, chunk
+// lane mod 8), 16 bytes of packed W (column lane / 2, half lane mod 2), the column's scale and
+// bias, and the group sum of X row lane.
+struct WsRegs {
+    uint4 x[8];
+    uint4 w;
+    uint16_t s, b;
+    float su;
+};
+
+// Work-group i runs on XCD i mod 8; each XCD takes a contiguous range of tiles in row-major
+// tile order, so the work-groups resident on one XCD share the X rows of their tiles in its L2.
+__global__ __launch_bounds__(WS_THREADS, 1) void k_w4_gemm(W4 W, const uint16_t *__restrict__ Xh,
+                                                           const float *__restrict__ su, int M, GemmEpi ep)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][GBM * GALD];
+    extern __shared__ __attribute__((aligned(16))) char ws_smem[];
+    WsSlot *slots = reinterpret_cast<WsSlot *>(ws_smem);
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int mtiles = (M + GBM - 1) / GBM;
-    const int mt = blockIdx.x % mtiles, nt = blockIdx.x / mtiles;
-    const int m0 = mt * GBM, n0 = nt * GBN;
     const int K = W.k, kw = K >> 3, kg = K >> 6;
-    const int nsteps = (kg + GKS - 1) / GKS;
-    const int l32 = lane & 31, kh = lane >> 5;
+    const int ntiles = (W.n + WS_BN - 1) / WS_BN, mtiles = (M + WS_BM - 1) / WS_BM;
+    const int tiles = ntiles * mtiles, per = (tiles + 7) / 8;
+    const int tile = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    if (tile >= tiles) return;
+    const int m0 = (tile / ntiles) * WS_BM, n0 = (tile % ntiles) * WS_BN;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nsteps = kg, nloop = (nsteps + 2) / 3 * 3;
 
-    // X tile staging: thread -> (row tid/2, 64 values at column 64*(tid&1) of the step)
-    const int srow = tid >> 1, scol = 64 * (tid & 1);
-    const bool srow_ok = (m0 + srow) < M;
-    const uint16_t *xsrc = Xh + (size_t)(srow_ok ? m0 + srow : 0) * K + scol;
-
-    // W rows of this lane: one per 32-column MFMA tile.
-    int nrow[2];
-    bool nok[2];
+    if (wave >= 4) {
+        // ------------------------------------------------------------ loaders
+        const int lid = tid - 256;
+        const int xc = lid & 7, n = lid >> 1, h = lid & 1;
+        const uint16_t *xr[8];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        nrow[j] = n0 + 64 * wn + 32 * j + l32;
-        nok[j] = nrow[j] < W.n;
+        for (int i = 0; i < 8; ++i)
+            xr[i] = Xh + (size_t)min(m0 + 32 * i + (lid >> 3), M - 1) * K + 8 * xc;
+        const int nr = min(n0 + n, W.n - 1);
+        const uint32_t *wr = W.q + (size_t)nr * kw + 4 * h;
+        const uint16_t *sr = W.s + (size_t)nr * kg, *br = W.b + (size_t)nr * kg;
+        const float *sur = su + (size_t)min(m0 + lid, M - 1) * kg;
+        auto issue = [&](WsRegs &R, int st) {
+            const int g = min(st, kg - 1);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) R.x[i] = *reinterpret_cast<const uint4 *>(xr[i] + 64 * g);
+            R.w = *reinterpret_cast<const uint4 *>(wr + 8 * g);
+            R.s = sr[g];
+            R.b = br[g];
+            R.su = sur[g];
+        };
+        auto store = [&](const WsRegs &R, int slot) {
+            WsSlot &sl = slots[slot];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) sl.x[ws_sw(32 * i + (lid >> 3), xc)] = pair_order16(R.x[i]);
+            const float sc = bf16_to_f32(R.s);
+            const half2v s2 = {(_Float16)sc, (_Float16)sc};
+            const uint32_t ww[4] = {R.w.x, R.w.y, R.w.z, R.w.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j)  // the two lanes of a column write in different bank orders
+                sl.w[ws_sw(n, 4 * h + (j ^ h))] = __builtin_bit_cast(uint4, dequant_word(ww[j ^ h], s2));
+            if (h == 0) sl.bpp[n] = fmaf(8.f, sc, bf16_to_f32(R.b));
+            sl.su[lid] = R.su;
+        };
+        // stage s travels in register set s mod 3 and LDS slot s mod 3; it is loaded at step
+        // s - 5 and written to LDS at step s - 2.  Loads past the last group re-read it (no
+        // branch around a load) and the slots they fill are never read.
+        WsRegs r0, r1, r2;
+        issue(r0, 0);
+        issue(r1, 1);
+        issue(r2, 2);
+        store(r0, 0);
+        issue(r0, 3);
+        store(r1, 1);
+        issue(r1, 4);
+        for (int k = 0; k < nloop; k += 3) {
+            __syncthreads();
+            store(r2, 2);
+            issue(r2, k + 5);
+            __syncthreads();
+            store(r0, 0);
+            issue(r0, k + 6);
+            __syncthreads();
+            store(r1, 1);
+            issue(r1, k + 7);
+        }
+        return;
     }
 
-    // the step's X columns: group 2*st + (tid & 1); a missing second group (odd kg) reads zero.
-    // Staged in two halves of 32 columns (h = 0, 1) to keep fewer values in flight in registers.
-    auto load_x = [&](int st, int h, uint4 *v) {
-        const bool ok = srow_ok && (GKS * st + (tid & 1)) < kg;
+    // ---------------------------------------------------------------- compute
+    const int lane = tid & 63, l32 = lane & 31, kh = lane >> 5;
+    const int wm = wave >> 1, wn = wave & 1;  // rows 128 wm .. +127, columns 64 wn .. +63
+    floatx16 acc[4][2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            v[i] = ok ? *reinterpret_cast<const uint4 *>(xsrc + (size_t)st * GKS * GBK + 32 * h + 8 * i)
-                      : make_uint4(0u, 0u, 0u, 0u);
-    };
-    auto store_x = [&](int buf, int h, const uint4 *v) {
-        uint16_t *dst = &As[buf][srow * GALD + scol + 32 * h];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4 *>(dst + 8 * i) = pair_order16(v[i]);
-    };
-    auto load_w = [&](int st, uint4 (*wq)[GKS], float (*sc)[GKS], float (*bb)[GKS]) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int gg = 0; gg < GKS; ++gg) {
-                const int g = GKS * st + gg;
-                if (nok[j] && g < kg) {
-                    // cached load: the 128-byte line serves the next groups and every row tile
-                    wq[j][gg] = *(reinterpret_cast<const uint4 *>(W.q + (size_t)nrow[j] * kw + 8 * g) + kh);
-                    sc[j][gg] = bf16_to_f32(W.s[(size_t)nrow[j] * kg + g]);
-                    bb[j][gg] = bf16_to_f32(W.b[(size_t)nrow[j] * kg + g]);
-                } else {
-                    wq[j][gg] = make_uint4(0u, 0u, 0u, 0u);
-                    sc[j][gg] = 0.f;
-                    bb[j][gg] = 0.f;
-                }
-            }
-    };
-
-    floatx16 acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    uint4 xv[4];
-    uint4 wq[2][GKS], wq_n[2][GKS];
-    float sc[2][GKS], bb[2][GKS], sc_n[2][GKS], bb_n[2][GKS];
-    load_w(0, wq, sc, bb);
-    load_x(0, 0, xv);
-    store_x(0, 0, xv);
-    load_x(0, 1, xv);
-    store_x(0, 1, xv);
-    __syncthreads();
-
-    for (int st = 0; st < nsteps; ++st) {
-        const int cur = st & 1;
-        const bool more = st + 1 < nsteps;
-        if (more) {
-            load_x(st + 1, 0, xv);
-            load_w(st + 1, wq_n, sc_n, bb_n);
-        }
-#pragma unroll
-        for (int gg = 0; gg < GKS; ++gg) {
-            const int g = GKS * st + gg;
-            if (gg == 1 && more) {
-                // first half of the next step's X to the other buffer, then the second half in flight
-                store_x(cur ^ 1, 0, xv);
-                load_x(st + 1, 1, xv);
-            }
-            half2v s2[2];
-#pragma unroll
-            for (int j = 0; j < 2; ++j) s2[j] = half2v{(_Float16)sc[j][gg], (_Float16)sc[j][gg]};
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                half8 bf[2], af[2];
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const uint32_t ww[4] = {wq[j][gg].x, wq[j][gg].y, wq[j][gg].z, wq[j][gg].w};
-                    bf[j] = dequant_word(ww[ks], s2[j]);
-                }
-#pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const uint16_t *src = &As[cur][(64 * wm + 32 * i + l32) * GALD + GBK * gg + 8 * (4 * kh + ks)];
-                    af[i] = __builtin_bit_cast(half8, *reinterpret_cast<const uint4 *>(src));
-                }
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int j = 0; j < 2; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            // Asymmetric groups: add (beta + 8 s) * (group sum of the X row).
-            float bpp[2];
-#pragma unroll
-            for (int j = 0; j < 2; ++j) bpp[j] = fmaf(8.f, sc[j][gg], bb[j][gg]);
-            if (g < kg && __builtin_amdgcn_ballot_w64(bpp[0] != 0.f || bpp[1] != 0.f) != 0ull) {
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int m = m0 + 64 * wm + 32 * i + 8 * (r >> 2) + 4 * kh + (r & 3);
-                        const float s = m < M ? su[(size_t)m * kg + g] : 0.f;
-#pragma unroll
-                        for (int j = 0; j < 2; ++j) acc[i][j][r] = fmaf(bpp[j], s, acc[i][j][r]);
-                    }
-            }
-        }
-        if (more) {
-            store_x(cur ^ 1, 1, xv);
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int gg = 0; gg < GKS; ++gg) {
-                    wq[j][gg] = wq_n[j][gg];
-                    sc[j][gg] = sc_n[j][gg];
-                    bb[j][gg] = bb_n[j][gg];
-                }
-        }
+    auto step = [&](int k, int slot) {
         __syncthreads();
+        if (k >= nsteps) return;
+        const WsSlot &sl = slots[slot];
+        // operands of k-step ks + 1 are read while the MFMAs of k-step ks run
+        half8 af[2][4], bf[2][2];
+        auto rd = [&](int ks, half8 (&a)[4], half8 (&b)[2]) {
+            const int c = 2 * ks + kh;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = __builtin_bit_cast(half8, sl.x[ws_sw(128 * wm + 32 * i + l32, c)]);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) b[j] = __builtin_bit_cast(half8, sl.w[ws_sw(64 * wn + 32 * j + l32, c)]);
+        };
+        rd(0, af[0], bf[0]);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            if (ks + 1 < 4) rd(ks + 1, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ks & 1][i], bf[ks & 1][j], acc[i][j], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // asymmetric groups: add (beta + 8 s) * (group sum of the X row) as a rank-1 fp32
+        // matrix-core update (K = 2 with the second k zero)
+        float bq[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) bq[j] = sl.bpp[64 * wn + 32 * j + l32];
+        if (__builtin_amdgcn_ballot_w64(bq[0] != 0.f || bq[1] != 0.f) != 0ull) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float a = kh ? 0.f : sl.su[128 * wm + 32 * i + l32];
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, kh ? 0.f : bq[j], acc[i][j], 0, 0, 0);
+            }
+        }
+    };
+    for (int k = 0; k < nloop; k += 3) {
+        step(k, 0);
+        step(k + 1, 1);
+        step(k + 2, 2);
     }
 
-    // Epilogue: D layout of the 32x32 MFMA: lane l, register r -> row 8*(r/4) + 4*(l/32) + r%4,
-    // column l%32.
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const int n = nrow[j];
-            if (!nok[j]) continue;
+            const int n = n0 + 64 * wn + 32 * j + l32;
+            if (n >= W.n) continue;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int m = m0 + 64 * wm + 32 * i + 8 * (r >> 2) + 4 * kh + (r & 3);
+                const int m = m0 + 128 * wm + 32 * i + 8 * (r >> 2) + 4 * kh + (r & 3);
                 if (m >= M) continue;
                 const size_t o = (size_t)m * W.n + n;
                 float v = acc[i][j][r];
@@ -237,9 +242,17 @@ hipError_t launch_w4_gemm(const W4 &W, const uint16_t *Xh, const float *su, int 
                           const void *res, int res_t, void *Y, int y_t, hipStream_t st)
 {
     if (M <= 0) return hipSuccess;
-    const int mtiles = (M + GBM - 1) / GBM, ntiles = (W.n + GBN - 1) / GBN;
+    static bool attr = false;
+    const size_t smem = WS_SLOTS * sizeof(WsSlot);
+    if (!attr) {
+        hipError_t e = hipFuncSetAttribute((const void *)k_w4_gemm,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        if (e != hipSuccess) return e;
+        attr = true;
+    }
+    const int tiles = ((M + WS_BM - 1) / WS_BM) * ((W.n + WS_BN - 1) / WS_BN);
     GemmEpi ep{Y, res, y_t, res_t};
-    k_w4_gemm<<<dim3(mtiles * ntiles), dim3(256), 0, st>>>(W, Xh, su, M, ep);
+    k_w4_gemm<<<dim3(8 * ((tiles + 7) / 8)), dim3(WS_THREADS), smem, st>>>(W, Xh, su, M, ep);
     return hipGetLastError();
 }
 
