@@ -110,7 +110,7 @@ __global__ __launch_bounds__(WS_THREADS, 1) void k_w4_gemm(W4 W, const uint16_t 
         const int nr = min(n0 + n, W.n - 1);
         const uint32_t *wr = W.q + (size_t)nr * kw + 4 * h;
         const uint16_t *sr = W.s + (size_t)nr * kg, *br = W.b + (size_t)nr * kg;
-        const float *sur = su + (size_t)min(m0 + lid, M - 1) * kg;
+        const float *sur = su + min(m0 + lid, M - 1);
         auto issue = [&](WsRegs &R, int st) {
             const int g = min(st, kg - 1);
 #pragma unroll
@@ -118,7 +118,7 @@ __global__ __launch_bounds__(WS_THREADS, 1) void k_w4_gemm(W4 W, const uint16_t 
             R.w = *reinterpret_cast<const uint4 *>(wr + 8 * g);
             R.s = sr[g];
             R.b = br[g];
-            R.su = sur[g];
+            R.su = sur[(size_t)g * M];
         };
         auto store = [&](const WsRegs &R, int slot) {
             WsSlot &sl = slots[slot];

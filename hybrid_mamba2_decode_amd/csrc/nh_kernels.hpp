@@ -69,7 +69,7 @@ hipError_t launch_conv_step(const uint16_t *xbc, long ld, uint16_t *state, const
 
 // ---- row kernels (rows.hip)
 // u = bf16(RMSNorm(x) * w); out_kind 0: bf16 bits, 1: fp16 bits of the same value (the
-// matrix-core operand format); su (nullable): per-64-group sums of u, [rows][d/64].
+// matrix-core operand format); su (nullable): per-64-group sums of u, [d/64][rows].
 hipError_t launch_rmsnorm(const void *x, int x_t, const uint16_t *w, uint16_t *u, int out_kind,
                           float *su, int rows, int d, float eps, hipStream_t st);
 hipError_t launch_rmsnorm_gated(const uint16_t *y, const uint16_t *z, long ld_z,
@@ -78,12 +78,12 @@ hipError_t launch_rmsnorm_gated(const uint16_t *y, const uint16_t *z, long ld_z,
 hipError_t launch_conv_seq(const uint16_t *xbc, long ld, int T, const uint16_t *state_in,
                            uint16_t *state_out, const uint16_t *w, const uint16_t *b,
                            uint16_t *out, int batch, int channels, hipStream_t st);
-// bf16 [M][K] -> fp16 bits [M][K] plus per-64-group sums [M][K/64].
+// bf16 [M][K] -> fp16 bits [M][K] plus per-64-group sums [K/64][M].
 hipError_t launch_to_f16(const uint16_t *x, uint16_t *xh, float *su, int M, int K,
                          hipStream_t st);
 
 // ---- seq mode (gemm.hip, scan.hip)
-// Y = Xh W^T (+ res); Xh holds fp16 bits, su the per-group row sums of Xh.
+// Y = Xh W^T (+ res); Xh holds fp16 bits, su the per-group row sums of Xh as [K/64][M].
 hipError_t launch_w4_gemm(const W4 &W, const uint16_t *Xh, const float *su, int M,
                           const void *res, int res_t, void *Y, int y_t, hipStream_t st);
 // Workspace of the scan: the fp16 C.B^T tiles of every (sequence, chunk, group).

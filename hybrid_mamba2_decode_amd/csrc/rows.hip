@@ -102,7 +102,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const void *__restrict__ x,
         }
         // 256 is a multiple of 8, so the 8 lanes of a group share the same i.
         s = group8_sum(s);
-        if (su && vi < nv && (vi & 7) == 0) su[row * (d >> 6) + (vi >> 3)] = s;
+        if (su && vi < nv && (vi & 7) == 0) su[(size_t)(vi >> 3) * gridDim.x + row] = s;
     }
 }
 
@@ -169,7 +169,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm_gated(const uint16_t *__restric
             store8(out + row * d + base + 8 * vi, o, kind);
         }
         s = group8_sum(s);
-        if (su && vi < nv && (vi & 7) == 0) su[row * (d >> 6) + ((base >> 6) + (vi >> 3))] = s;
+        if (su && vi < nv && (vi & 7) == 0) su[(size_t)((base >> 6) + (vi >> 3)) * gridDim.x + row] = s;
     }
 }
 
@@ -260,9 +260,11 @@ __global__ __launch_bounds__(256) void k_to_f16(const uint16_t *__restrict__ x,
         s = sum_bf16x8(w);
     }
     s = group8_sum(s);
-    // kvec % 8 == 0, so a group never straddles two rows
-    if (v < nvec && (v & 7) == 0) su[v >> 3] = s;
-    (void)kvec;
+    // kvec % 8 == 0, so a group never straddles two rows; su is [group][row]
+    if (v < nvec && (v & 7) == 0) {
+        const size_t gi = v >> 3, kg = (size_t)kvec >> 3;
+        su[(gi % kg) * (nvec / kvec) + gi / kg] = s;
+    }
 }
 
 hipError_t launch_to_f16(const uint16_t *x, uint16_t *xh, float *su, int M, int K, hipStream_t st)
