@@ -10,11 +10,13 @@
 //
 // C.B^T depends on the group only, so a pre-pass (k_ssd_cb) computes it once per (sequence,
 // chunk, group): bf16 matrix-core products of the bf16 inputs (exact products, fp32 sums),
-// stored as fp16 16 x 16 tiles of the causal lower triangle, tile (I, J <= I) at index
-// I(I+1)/2 + J, each in the lane order the scan reads it in (lane l = 16 q + i holds
-// G[16I + i][16J + 4q + r], r = 0..3), so a wave loads a tile with one 8-byte load per lane.
+// stored as fp16 16 x 16 tiles of the causal lower triangle in the lane order the scan reads
+// them in (lane l = 16 q + i holds G[16I + i][16J + 4q + r], r = 0..3).  Tiles 2jp and 2jp + 1
+// of row block I form a pair stored lane-interleaved (lane l's 4 values of one, then its 4 of
+// the other), so a wave loads a pair with one 16-byte load per lane; row block I holds
+// ceil((I + 1) / 2) pairs (the last one half used when I is even).
 // Workspace layout: chunk-major, then (sequence, group); a chunk of L rows holds
-// cb_tiles(L) tiles per (sequence, group), so the total is at most 4 KiB per position.
+// cb_pairs(L) pairs per (sequence, group), at most 8 KiB per position (chunks under 17 rows).
 //
 // Decomposition.  One work-group of 8 waves per (sequence, head) walks the chunks in order and
 // keeps the head's 80 x 128 fp32 state in registers as the accumulator of the state MFMA (wave
@@ -30,7 +32,8 @@
 //      transposed, Y^T = S_in C^T + X^T (G o decay)^T: its C rows, already in registers, are the
 //      B operand of S_in C^T, and the block's G tiles come from the pre-pass in the B-operand
 //      layout, so the scaled tile never leaves registers; each lane ends with 4 consecutive
-//      columns of one output row (one 8-byte store per tile);
+//      columns of one output row, and the block goes through the wave's LDS rows so that each
+//      16-byte store covers 8 consecutive columns of one row;
 //   4. each wave adds x^T (w B) to its state columns, w_j = exp(cum_{L-1} - cum_j) dt_j taken
 //      from an fp16 table and multiplied into the B fragment in registers (steps 3 and 4 only
 //      read LDS, so no barrier separates them).
@@ -53,6 +56,7 @@ constexpr int SC_THREADS = 512;
 constexpr int BS_LD = DSTATE + 16;  // B rows: 288 B (transposed reads conflict-free)
 constexpr int XS_LD = HDIM;         // x rows: 160 B (transposed reads conflict-free)
 constexpr int SI_LD = DSTATE + 8;   // S_in rows: 272 B
+constexpr int YS_LD = HDIM + 8;     // staged output rows: 176 B (16-byte aligned, writes conflict-free)
 
 // Member order keeps the tables, x and S_in below 64 KiB, so their reads take immediate
 // offsets from one base register.
@@ -65,6 +69,7 @@ struct ScanSmem {
     uint16_t Xs[QMAX * XS_LD];  // x of the chunk, [j][p]
     uint16_t Si[HDIM * SI_LD];  // state at chunk start, [p][n]
     uint16_t Bs[QMAX * BS_LD];  // B of the chunk, [j][n]
+    uint16_t Ys[8][16 * YS_LD]; // per wave: one 16-row bf16 output block, [i][p]
 };
 
 typedef short v4s __attribute__((ext_vector_type(4)));
@@ -135,15 +140,18 @@ constexpr int CB_LD = DSTATE + 8;  // bf16 B rows in LDS: 272 B (16-byte row rea
 
 typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
 
-__host__ __device__ constexpr int cb_tiles(int Q)
+// Tile pairs (2jp, 2jp + 1) of the row blocks I < nb: row block I holds ceil((I + 1) / 2) pairs.
+__host__ __device__ constexpr int cb_pairs_before(int nb)
 {
-    return ((Q + 15) / 16) * ((Q + 15) / 16 + 1) / 2;
+    return (nb & 1) ? ((nb + 1) / 2) * ((nb + 1) / 2) : (nb / 2) * (nb / 2 + 1);
 }
+
+__host__ __device__ constexpr int cb_pairs(int Q) { return cb_pairs_before((Q + 15) / 16); }
 
 // first tile of (chunk ck of L rows, sequence b, group g)
 __device__ __forceinline__ size_t cb_base(int ck, int Q, int L, int batch, int b, int g)
 {
-    return ((size_t)ck * batch * NGROUPS * cb_tiles(Q) + (size_t)(b * NGROUPS + g) * cb_tiles(L)) * 256;
+    return ((size_t)ck * batch * NGROUPS * cb_pairs(Q) + (size_t)(b * NGROUPS + g) * cb_pairs(L)) * 512;
 }
 
 // One work-group per (chunk, group, sequence): B rows of the chunk to LDS; wave w takes row
@@ -178,12 +186,12 @@ __global__ __launch_bounds__(CB_THREADS) void k_ssd_cb(const uint16_t *__restric
     }
     __syncthreads();
 
-    uint16_t *Gc = Gw + cb_base(c, Q, L, gridDim.z, b, g) + lane * 4;
+    uint16_t *Gc = Gw + cb_base(c, Q, L, gridDim.z, b, g) + lane * 8;
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi) {
         const int I = Ib[bi];
         if (I >= nb) continue;
-        uint16_t *gI = Gc + (I * (I + 1) / 2) * 256;
+        uint16_t *gI = Gc + cb_pairs_before(I) * 512;
         // two tiles per step: independent accumulation chains
         for (int J = 0; J <= I; J += 2) {
             const int J1 = min(J + 1, I);
@@ -204,9 +212,12 @@ __global__ __launch_bounds__(CB_THREADS) void k_ssd_cb(const uint16_t *__restric
             if (J1 == I)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) a1[r] = 4 * q4 + r > l16 ? 0.f : a1[r];
-            *reinterpret_cast<uint2 *>(gI + J * 256) = make_uint2(pack_rne(a0[0], a0[1]), pack_rne(a0[2], a0[3]));
+            // pair J / 2: lane l's 4 values of tile J, then its 4 values of tile J + 1
             if (J + 1 <= I)
-                *reinterpret_cast<uint2 *>(gI + J1 * 256) = make_uint2(pack_rne(a1[0], a1[1]), pack_rne(a1[2], a1[3]));
+                *reinterpret_cast<uint4 *>(gI + (J >> 1) * 512) =
+                    make_uint4(pack_rne(a0[0], a0[1]), pack_rne(a0[2], a0[3]), pack_rne(a1[0], a1[1]), pack_rne(a1[2], a1[3]));
+            else
+                *reinterpret_cast<uint2 *>(gI + (J >> 1) * 512) = make_uint2(pack_rne(a0[0], a0[1]), pack_rne(a0[2], a0[3]));
         }
     }
 }
@@ -354,17 +365,17 @@ __global__ __launch_bounds__(SC_THREADS, 1) void k_ssd_scan(const uint16_t *__re
         // ---- 3. outputs of blocks I0, I1
         const int nblk = (L + 15) >> 4;
         const __amdgpu_buffer_rsrc_t ry = rsrc(yseq + (size_t)t0 * YROW, (uint32_t)L * YROW);
-        const uint16_t *Gc = Gw + cb_base(ck, Q, L, gridDim.x / NHEADS, b, g) + lane * 4;
+        const uint16_t *Gc = Gw + cb_base(ck, Q, L, gridDim.x / NHEADS, b, g) + lane * 8;
 #pragma unroll 1
         for (int bi = 0; bi < 2; ++bi) {
             const int I = bi == 0 ? I0 : I1;
             if (I >= nblk) continue;
             // the block's G tiles J = 0..I, loaded three pairs ahead of their use (the first
             // three while C S_in^T runs; loads past I re-read tile I and are unused)
-            const uint16_t *gI = Gc + (I * (I + 1) / 2) * 256;
-            auto gload = [&](int J) { return *reinterpret_cast<const uint2 *>(gI + min(J, I) * 256); };
+            const uint16_t *gI = Gc + cb_pairs_before(I) * 512;
+            auto gload = [&](int jp) { return *reinterpret_cast<const uint4 *>(gI + min(jp, I >> 1) * 512); };
             // window of pairs jp, jp + 1, jp + 2
-            uint2 g0a = gload(0), g0b = gload(1), g1a = gload(2), g1b = gload(3), g2a = gload(4), g2b = gload(5);
+            uint4 g0 = gload(0), g1 = gload(1), g2 = gload(2);
             __builtin_amdgcn_sched_barrier(0);
             half8 cfb[4];
 #pragma unroll
@@ -432,28 +443,39 @@ __global__ __launch_bounds__(SC_THREADS, 1) void k_ssd_scan(const uint16_t *__re
             const int npair = I >> 1;
 #pragma unroll 1
             for (int jp = 0; jp < npair; ++jp) {
-                const uint2 na = gload(2 * jp + 6), nb = gload(2 * jp + 7);
-                apply(jp, offdiag(2 * jp, g0a), offdiag(2 * jp + 1, g0b));
-                g0a = g1a;
-                g0b = g1b;
-                g1a = g2a;
-                g1b = g2b;
-                g2a = na;
-                g2b = nb;
+                const uint4 nx = gload(jp + 3);
+                apply(jp, offdiag(2 * jp, make_uint2(g0.x, g0.y)), offdiag(2 * jp + 1, make_uint2(g0.z, g0.w)));
+                g0 = g1;
+                g1 = g2;
+                g2 = nx;
             }
             // the pair that holds the diagonal block
             if (I & 1)
-                apply(npair, offdiag(I - 1, g0a), diag(g0b));
+                apply(npair, offdiag(I - 1, make_uint2(g0.x, g0.y)), diag(make_uint2(g0.z, g0.w)));
             else
-                apply(npair, diag(g0a), make_uint2(0u, 0u));
-            // store y: row ia, columns 16pb + 4q4 .. +3 (the skip term is in the diagonal)
-            const uint32_t rowoff = (uint32_t)ia * YROW + (uint32_t)(h * HDIM + 4 * q4) * YB;
+                apply(npair, diag(make_uint2(g0.x, g0.y)), make_uint2(0u, 0u));
+            // store y (the skip term is in the diagonal).  bf16 output goes through the wave's
+            // LDS block so that each 16-byte store covers consecutive columns of one row.
+            if (YT == BF16) {
+                uint16_t *ys = sm.Ys[wave];
 #pragma unroll
-            for (int pb = 0; pb < 5; ++pb) {
-                if (YT == BF16) {
-                    const u32x2v w2 = {pack_bf16x2(acc[pb][0], acc[pb][1]), pack_bf16x2(acc[pb][2], acc[pb][3])};
-                    __builtin_amdgcn_raw_buffer_store_b64(w2, ry, rowoff + 16 * pb * YB, 0, 0);
-                } else {
+                for (int pb = 0; pb < 5; ++pb)
+                    *reinterpret_cast<uint2 *>(&ys[l16 * YS_LD + 16 * pb + 4 * q4]) =
+                        make_uint2(pack_bf16x2(acc[pb][0], acc[pb][1]), pack_bf16x2(acc[pb][2], acc[pb][3]));
+#pragma unroll
+                for (int e = 0; e < 3; ++e) {
+                    const int c = lane + 64 * e;  // 16-byte piece: row c / 10, columns 8 (c % 10) ..
+                    if (c < 160) {
+                        const int ri = c / 10, cc = c - 10 * ri;
+                        const uint4 v = *reinterpret_cast<const uint4 *>(&ys[ri * YS_LD + 8 * cc]);
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4v, v), ry,
+                            (uint32_t)(16 * I + ri) * YROW + (uint32_t)(h * HDIM + 8 * cc) * 2, 0, 0);
+                    }
+                }
+            } else {
+                const uint32_t rowoff = (uint32_t)ia * YROW + (uint32_t)(h * HDIM + 4 * q4) * YB;
+#pragma unroll
+                for (int pb = 0; pb < 5; ++pb) {
                     const u32x4v w4 = {__float_as_uint(acc[pb][0]), __float_as_uint(acc[pb][1]),
                                        __float_as_uint(acc[pb][2]), __float_as_uint(acc[pb][3])};
                     __builtin_amdgcn_raw_buffer_store_b128(w4, ry, rowoff + 16 * pb * YB, 0, 0);
@@ -495,8 +517,8 @@ __global__ __launch_bounds__(SC_THREADS, 1) void k_ssd_scan(const uint16_t *__re
 size_t ssd_scan_ws_bytes(int batch, int T, int Q)
 {
     const int full = T / Q, last = T - full * Q;
-    const size_t tiles = (size_t)full * cb_tiles(Q) + (last ? cb_tiles(last) : 0);
-    return (size_t)batch * NGROUPS * tiles * 256 * sizeof(uint16_t);
+    const size_t pairs = (size_t)full * cb_pairs(Q) + (last ? cb_pairs(last) : 0);
+    return (size_t)batch * NGROUPS * pairs * 512 * sizeof(uint16_t);
 }
 
 hipError_t launch_ssd_scan(const uint16_t *xc, const uint16_t *dtr, long ld_dt, int T, int Q,

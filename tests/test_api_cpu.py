@@ -118,14 +118,15 @@ def test_primitive_checks(nh):
 
 def test_scan_workspace_size_and_checks(nh):
     A = 0x40000
-    # chunk 256: 136 causal 16 x 16 tiles of fp16 per (chunk, sequence, group); a partial last
-    # chunk of L rows holds ceil(L/16)(ceil(L/16)+1)/2 tiles
+    # chunk 256: the causal 16 x 16 fp16 tiles of C.B^T per (chunk, sequence, group) in pairs of
+    # 2 x 512 B; row block I holds ceil((I+1)/2) pairs, 72 for 16 row blocks; a partial last
+    # chunk of 166 rows has 11 row blocks, 36 pairs
     d256 = nh.dims(chunk=256)
-    assert nh.nh_ssd_scan_workspace_bytes(d256, 2, 3750) == 2 * 8 * 512 * (14 * 136 + 66)  # last chunk: 166 rows
-    assert nh.nh_ssd_scan_workspace_bytes(d256, 1, 1) == 8 * 512
+    assert nh.nh_ssd_scan_workspace_bytes(d256, 2, 3750) == 2 * 8 * 1024 * (14 * 72 + 36)
+    assert nh.nh_ssd_scan_workspace_bytes(d256, 1, 1) == 8 * 1024
     for B, T, Q in [(1, 1, 1), (2, 413, 128), (3, 17, 16), (1, 300, 7), (2, 3750, 256)]:
         n = nh.nh_ssd_scan_workspace_bytes(nh.dims(chunk=Q), B, T)
-        assert 0 < n <= 4096 * B * T        # the block reuses 8960 B per position for it
+        assert 0 < n <= 8192 * B * T        # the block reuses 8960 B per position for it
     assert nh.nh_ssd_scan_workspace_bytes(nh.dims(chunk=0), 1, 10) == 0
     assert nh.nh_ssd_scan_workspace_bytes(nh.dims(chunk=257), 1, 10) == 0
     assert nh.nh_ssd_scan_workspace_bytes(d256, 0, 10) == 0
