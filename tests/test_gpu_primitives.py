@@ -112,7 +112,10 @@ def test_gemm_identity_probe_is_bit_exact(env, asym):
 
 
 @pytest.mark.parametrize("M,n,k,asym", [(1, 300, 4480, False), (16, 300, 4480, True), (130, 260, 4480, False),
-                                        (413, 4480, 10240, True), (257, 64, 128, False)])
+                                        (413, 4480, 10240, True), (257, 64, 128, False),
+                                        # one, three and five groups of 64 (fewer groups than the
+                                        # loaders' three-step lead), several tiles in both directions
+                                        (37, 129, 64, True), (300, 520, 192, False), (600, 1000, 320, True)])
 def test_gemm_matches_oracle(env, M, n, k, asym):
     nh, oracle, gu, torch = env
     _say("gemm", M, n, k, asym)
