@@ -190,6 +190,29 @@ def test_conv_step_and_seq(env):
         assert np.array_equal(gu.bf16_bits_to_f64(gu.from_dev_u16(std)[bb]), ref_st)
 
 
+@pytest.mark.parametrize("C,ld,T", [(100, 103, 40), (96, 96, 64), (12288, 22656, 33)])
+def test_conv_seq_other_shapes(env, C, ld, T):
+    # channel counts and row strides that are not multiples of 8 take the one-channel kernel;
+    # the others the 8-channel one, here with a full and a one-position last block
+    nh, oracle, gu, torch = env
+    _say("conv seq shape", C, ld, T)
+    rng = np.random.default_rng(C + T)
+    w = synth.f32_to_bf16(rng.normal(0, 0.25, (C, 4)).astype(np.float32))
+    b = synth.f32_to_bf16(rng.normal(0, 0.1, C).astype(np.float32))
+    for with_state in [False, True]:
+        xbc = synth.f32_to_bf16(rng.normal(0, 1.2, (1, T, ld)).astype(np.float32))
+        st = synth.f32_to_bf16(rng.normal(0, 1, (1, 3, C)).astype(np.float32)) if with_state else None
+        out = gu.empty_u16(1, T, C)
+        so = gu.empty_u16(1, 3, C)
+        nh.nh_conv1d_seq(gu.to_dev(xbc), ld, T, None if st is None else gu.to_dev(st), so,
+                         gu.to_dev(w), gu.to_dev(b), out, 1, C)
+        got = gu.bf16_bits_to_f64(gu.from_dev_u16(out))[0]
+        ref, ref_st = oracle.conv1d(gu.bf16_bits_to_f64(xbc[0, :, :C]), w, b,
+                                    None if st is None else gu.bf16_bits_to_f64(st[0]))
+        assert np.all(np.abs(got - ref) <= np.abs(ref) * 2 ** -8 + 1e-6)
+        assert np.array_equal(gu.bf16_bits_to_f64(gu.from_dev_u16(so)[0]), ref_st)
+
+
 # ------------------------------------------------------------------- SSM step
 
 def _scan_inputs(rng, B, T):
