@@ -92,6 +92,25 @@ def test_inproj_conv_step_matches_oracle(env, B):
     assert np.array_equal(ssd.cpu().numpy(), ss0)                         # the SSM state is not touched
 
 
+@pytest.mark.parametrize("B", [3, 4])
+def test_block_step_batch3_4(env, B):
+    # the step kernels are specialised per batch size up to 4
+    nh, oracle, gu, torch, lw, W = env
+    _say("block step, batch", B)
+    x = synth.block_input(9, B, 1)
+    cs0, ss0 = synth.prefilled_state(9, B)
+    st, csd, ssd = gu.state_dev(cs0, ss0)
+    d = nh.dims()
+    ws = gu.workspace(nh.nh_block_workspace_bytes(d, B, 1, nh.NH_MODE_STEP))
+    out = gu.empty_f32(B, 4480)
+    nh.nh_mamba_block_step(d, W, st, gu.to_dev(x[:, 0]), nh.NH_BF16, out, nh.NH_F32, B, ws, ws.numel())
+    ref = oracle.block(synth.REAL, lw, gu.bf16_bits_to_f64(x), gu.bf16_bits_to_f64(cs0), ss0,
+                       mode=oracle.CONTRACT, stepwise=True)
+    _check_out(gu, out.cpu().numpy(), ref.out[:, 0], f"step b{B}")
+    _check_state(gu, ssd.cpu().numpy(), ref.ssm_state, f"step b{B}")
+    assert gu.rel_l2(gu.bf16_bits_to_f64(gu.from_dev_u16(csd)), ref.conv_state) < 4e-3
+
+
 def test_block_step_batch2_bf16_out(env):
     nh, oracle, gu, torch, lw, W = env
     _say("block step, batch 2, bf16 out")
