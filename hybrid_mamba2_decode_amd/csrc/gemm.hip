@@ -13,7 +13,7 @@
 //
 // Tiling: a 256 x 128 output tile per work-group of 8 waves with split roles.  Waves 4-7 load:
 // one quantisation group (K = 64) of the X tile and of the W tile per step, from global memory
-// into registers three steps ahead of use; they dequantise W to fp16 and write both tiles into
+// into registers four steps ahead of use; they dequantise W to fp16 and write both tiles into
 // a ring of three LDS slots.  Waves 0-3 compute: each owns a 128 x 64 block of the tile (4 x 2
 // MFMA 32x32 tiles) and only reads LDS and issues MFMAs.  One barrier per step: at step k the
 // compute waves read slot k mod 3 while the loaders fill slot (k + 2) mod 3, which the compute
@@ -97,28 +97,36 @@ __global__ __launch_bounds__(WS_THREADS, 1) void k_w4_gemm(W4 W, const uint16_t 
     const int m0 = (tile / ntiles) * WS_BM, n0 = (tile % ntiles) * WS_BN;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int nsteps = kg, nloop = (nsteps + 2) / 3 * 3;
+    const int nsteps = kg, nloop = (nsteps + 11) / 12 * 12;
 
     if (wave >= 4) {
         // ------------------------------------------------------------ loaders
         const int lid = tid - 256;
         const int xc = lid & 7, n = lid >> 1, h = lid & 1;
-        const uint16_t *xr[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            xr[i] = Xh + (size_t)min(m0 + 32 * i + (lid >> 3), M - 1) * K + 8 * xc;
-        const int nr = min(n0 + n, W.n - 1);
-        const uint32_t *wr = W.q + (size_t)nr * kw + 4 * h;
-        const uint16_t *sr = W.s + (size_t)nr * kg, *br = W.b + (size_t)nr * kg;
-        const float *sur = su + min(m0 + lid, M - 1);
+        // Buffer resources based at the tile's first row and covering only the tile's rows, so
+        // rows past the end of X or W read 0 (every offset is in the per-lane operand, the scalar
+        // offset operand stays 0, so the range check covers the whole offset).
+        auto rsrc = [](const void *p, uint32_t bytes) {
+            return __builtin_amdgcn_make_buffer_rsrc((void *)p, 0, (int)bytes, 0x00020000);
+        };
+        const uint32_t mrows = (uint32_t)min(M - m0, WS_BM), nrows = (uint32_t)min(W.n - n0, WS_BN);
+        const __amdgpu_buffer_rsrc_t rx = rsrc(Xh + (size_t)m0 * K, mrows * (uint32_t)K * 2);
+        const __amdgpu_buffer_rsrc_t rw = rsrc(W.q + (size_t)n0 * kw, nrows * (uint32_t)kw * 4);
+        const __amdgpu_buffer_rsrc_t rs = rsrc(W.s + (size_t)n0 * kg, nrows * (uint32_t)kg * 2);
+        const __amdgpu_buffer_rsrc_t rb = rsrc(W.b + (size_t)n0 * kg, nrows * (uint32_t)kg * 2);
+        const uint32_t vx = ((uint32_t)(lid >> 3) * K + 8 * xc) * 2, vw = ((uint32_t)n * kw + 4 * h) * 4;
+        const uint32_t vs = (uint32_t)n * kg * 2, vu = (uint32_t)lid * 4;
         auto issue = [&](WsRegs &R, int st) {
             const int g = min(st, kg - 1);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) R.x[i] = *reinterpret_cast<const uint4 *>(xr[i] + 64 * g);
-            R.w = *reinterpret_cast<const uint4 *>(wr + 8 * g);
-            R.s = sr[g];
-            R.b = br[g];
-            R.su = sur[(size_t)g * M];
+            for (int i = 0; i < 8; ++i)
+                R.x[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, vx + (uint32_t)(32 * i * K * 2 + 128 * g), 0, 0));
+            R.w = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, vw + (uint32_t)(32 * g), 0, 0));
+            R.s = __builtin_amdgcn_raw_buffer_load_b16(rs, vs + (uint32_t)(2 * g), 0, 0);
+            R.b = __builtin_amdgcn_raw_buffer_load_b16(rb, vs + (uint32_t)(2 * g), 0, 0);
+            // group g's sums of the tile's rows (su is [group][row])
+            const __amdgpu_buffer_rsrc_t ru = rsrc(su + (size_t)g * M + m0, mrows * 4);
+            R.su = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ru, vu, 0, 0));
         };
         auto store = [&](const WsRegs &R, int slot) {
             WsSlot &sl = slots[slot];
@@ -133,27 +141,23 @@ __global__ __launch_bounds__(WS_THREADS, 1) void k_w4_gemm(W4 W, const uint16_t 
             if (h == 0) sl.bpp[n] = fmaf(8.f, sc, bf16_to_f32(R.b));
             sl.su[lid] = R.su;
         };
-        // stage s travels in register set s mod 3 and LDS slot s mod 3; it is loaded at step
-        // s - 5 and written to LDS at step s - 2.  Loads past the last group re-read it (no
-        // branch around a load) and the slots they fill are never read.
-        WsRegs r0, r1, r2;
-        issue(r0, 0);
-        issue(r1, 1);
-        issue(r2, 2);
-        store(r0, 0);
-        issue(r0, 3);
-        store(r1, 1);
-        issue(r1, 4);
-        for (int k = 0; k < nloop; k += 3) {
-            __syncthreads();
-            store(r2, 2);
-            issue(r2, k + 5);
-            __syncthreads();
-            store(r0, 0);
-            issue(r0, k + 6);
-            __syncthreads();
-            store(r1, 1);
-            issue(r1, k + 7);
+        // stage s: register set s mod 4, LDS slot s mod 3; loaded at step s - 6, stored at step
+        // s - 2.  Loads past the last group re-read it (no branch around a load) and the slots
+        // they fill are never read.
+        WsRegs rr[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) issue(rr[j], j);
+        store(rr[0], 0);
+        issue(rr[0], 4);
+        store(rr[1], 1);
+        issue(rr[1], 5);
+        for (int k = 0; k < nloop; k += 12) {
+#pragma unroll
+            for (int j = 0; j < 12; ++j) {
+                __syncthreads();
+                store(rr[(j + 2) & 3], (j + 2) % 3);
+                issue(rr[(j + 2) & 3], k + j + 6);
+            }
         }
         return;
     }
