@@ -154,8 +154,8 @@ def main():
                     help="also run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); the block "
-              "has no multi-GPU path here", file=sys.stderr)
+        print(f"bench.py: the library runs on one GPU only (asked for --gpus {args.gpus}); the block "
+              "has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
