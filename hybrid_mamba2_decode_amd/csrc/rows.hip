@@ -173,13 +173,80 @@ __global__ __launch_bounds__(256) void k_rmsnorm_gated(const uint16_t *__restric
     }
 }
 
+// The same with one wave per (row, group) for groups of at most 2048 channels: the group's
+// sum of squares is a wave reduction (no LDS, no barrier), and a work-group of four waves
+// takes four consecutive (row, group) units.  Same products and rounding points as above; the
+// sum of squares is accumulated in another order.
+constexpr int RG_MAXI = 4;  // 16-byte vectors per lane: group <= 64 * 8 * RG_MAXI
+
+__global__ __launch_bounds__(256) void k_rmsnorm_gated_w(const uint16_t *__restrict__ y,
+                                                         const uint16_t *__restrict__ z, long ld_z,
+                                                         const uint16_t *__restrict__ w,
+                                                         uint16_t *__restrict__ out, int kind,
+                                                         float *__restrict__ su, int rows, int d,
+                                                         int group, float eps)
+{
+    const int ng = d / group;
+    const int unit = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+    if ((long)unit >= (long)rows * ng) return;  // wave-uniform; the kernel has no barrier
+    const size_t row = unit / ng;
+    const int j = unit - (int)row * ng, lane = threadIdx.x & 63, nv = group >> 3;
+    const size_t base = (size_t)j * group;
+    float gv[RG_MAXI][8];
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < RG_MAXI; ++i) {
+        const int vi = lane + 64 * i;
+        if (vi < nv) {
+            const uint4 yy = *reinterpret_cast<const uint4 *>(y + row * d + base + 8 * vi);
+            const uint4 zz = *reinterpret_cast<const uint4 *>(z + row * ld_z + base + 8 * vi);
+            const uint32_t ya[4] = {yy.x, yy.y, yy.z, yy.w}, za[4] = {zz.x, zz.y, zz.z, zz.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                gv[i][2 * e] = bf16lo(ya[e]) * silu(bf16lo(za[e]));
+                gv[i][2 * e + 1] = bf16hi(ya[e]) * silu(bf16hi(za[e]));
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss += gv[i][e] * gv[i][e];
+        }
+    }
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / (float)group + eps);
+#pragma unroll
+    for (int i = 0; i < RG_MAXI; ++i) {
+        const int vi = lane + 64 * i;
+        float s = 0.f;
+        if (vi < nv) {
+            const uint4 ww = *reinterpret_cast<const uint4 *>(w + base + 8 * vi);
+            const float w8[8] = {bf16lo(ww.x), bf16hi(ww.x), bf16lo(ww.y), bf16hi(ww.y),
+                                 bf16lo(ww.z), bf16hi(ww.z), bf16lo(ww.w), bf16hi(ww.w)};
+            float o[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                o[e] = round_bf16(gv[i][e] * r * w8[e]);
+                s += o[e];
+            }
+            store8(out + row * d + base + 8 * vi, o, kind);
+        }
+        // 64 is a multiple of 8, so the 8 lanes of a 64-channel group share the same i
+        s = group8_sum(s);
+        if (su && vi < nv && (vi & 7) == 0) su[(size_t)((base >> 6) + (vi >> 3)) * rows + row] = s;
+    }
+}
+
 hipError_t launch_rmsnorm_gated(const uint16_t *y, const uint16_t *z, long ld_z,
                                 const uint16_t *w, uint16_t *out, int out_kind, float *su,
                                 int rows, int d, int group, float eps, hipStream_t st)
 {
     if (rows <= 0) return hipSuccess;
-    dim3 grid(rows, d / group), block(256);
-    k_rmsnorm_gated<<<grid, block, 0, st>>>(y, z, ld_z, w, out, out_kind, su, d, group, eps);
+    if (group <= 64 * 8 * RG_MAXI) {
+        const long units = (long)rows * (d / group);
+        k_rmsnorm_gated_w<<<dim3((unsigned)((units + 3) / 4)), dim3(256), 0, st>>>(y, z, ld_z, w, out, out_kind, su,
+                                                                                 rows, d, group, eps);
+    } else {
+        dim3 grid(rows, d / group), block(256);
+        k_rmsnorm_gated<<<grid, block, 0, st>>>(y, z, ld_z, w, out, out_kind, su, d, group, eps);
+    }
     return hipGetLastError();
 }
 

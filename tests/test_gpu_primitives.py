@@ -341,3 +341,21 @@ def test_rmsnorm_and_gated_norm(env):
     ref = oracle.rmsnorm_gated(gu.bf16_bits_to_f64(y), gu.bf16_bits_to_f64(z)[:, :10240], gw, 1280, 1e-5)
     got = gu.bf16_bits_to_f64(gu.from_dev_u16(o))
     assert np.all(np.abs(got - ref) <= np.abs(ref) * 2 ** -8 + 1e-7)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("rows,d,group,ld_z", [(5, 8192, 4096, 8200), (7, 96, 8, 96), (3, 2048, 2048, 2048)])
+def test_gated_norm_other_groups(env, rows, d, group, ld_z):
+    # groups above 2048 channels take the work-group-per-group kernel, the rest the
+    # wave-per-group one; ragged 16-byte tails (group / 8 not a multiple of 64) included
+    nh, oracle, gu, torch = env
+    rng = np.random.default_rng(rows * 31 + group)
+    _say(f"gated norm rows={rows} d={d} group={group}")
+    y = synth.f32_to_bf16(rng.normal(size=(rows, d)).astype(np.float32))
+    z = synth.f32_to_bf16(rng.normal(size=(rows, ld_z)).astype(np.float32))
+    gw = synth.f32_to_bf16((1 + 0.05 * rng.normal(size=d)).astype(np.float32))
+    o = gu.empty_u16(rows, d)
+    nh.nh_rmsnorm_gated(gu.to_dev(y), gu.to_dev(z), ld_z, gu.to_dev(gw), o, rows, d, group, 1e-5)
+    ref = oracle.rmsnorm_gated(gu.bf16_bits_to_f64(y), gu.bf16_bits_to_f64(z)[:, :d], gw, group, 1e-5)
+    got = gu.bf16_bits_to_f64(gu.from_dev_u16(o))
+    assert np.all(np.abs(got - ref) <= np.abs(ref) * 2 ** -8 + 1e-7)
