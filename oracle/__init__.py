@@ -5,7 +5,7 @@ Only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 its Python binding) never imports, links or runs anything under ``oracle/``.
 
 The arithmetic lives in ``nh_oracle.c`` (plain C, fp64); this module builds it
-with gcc, wraps it with ctypes and adds two numpy-level pieces:
+with gcc, wraps it with ctypes and adds these numpy-level pieces:
 
 * ``ssd_chunked`` -- the chunked state-space-duality form of the same scan
   (Dao & Gu 2024, "Transformers are SSMs", the SSD algorithm: intra-chunk
@@ -13,6 +13,8 @@ with gcc, wraps it with ctypes and adds two numpy-level pieces:
   is not used to produce expected values; it is pinned against the recurrence
   for many chunk lengths and documents the decomposition the GPU scan uses.
 * ``stack`` -- composition of blocks over the hybrid layer pattern.
+* ``head`` and ``greedy_ids`` -- the final norm, one 4-bit output head and the
+  greedy id (smallest index of the largest logit, NaN never chosen).
 
 Readings of the pages that the oracle fixes (no mixer equations are printed
 on the pages; see the header of nh_oracle.c):
@@ -184,6 +186,38 @@ def rmsnorm(x, w_bf16, eps: float) -> np.ndarray:
     lib().nho_rmsnorm(_p(x2, C.c_double), x2.shape[0], x2.shape[1], _p(w, C.c_uint16), eps,
                       _p(out, C.c_double))
     return out.reshape(x.shape)
+
+
+def greedy_ids(logits) -> np.ndarray:
+    """Greedy choice per row of logits [m][n]: the smallest index among those holding the
+    largest value.  NaN entries never win; a row of NaN only gives -1."""
+    l = _d(logits)
+    l2 = l.reshape(-1, l.shape[-1])
+    ids = np.full(l2.shape[0], -1, dtype=np.int64)
+    for r in range(l2.shape[0]):
+        ok = ~np.isnan(l2[r])
+        if ok.any():
+            best = l2[r][ok].max()
+            ids[r] = int(np.flatnonzero(ok & (l2[r] == best))[0])
+    return ids
+
+
+def head(W, x, norm_w, eps: float, mode: int = CONTRACT):
+    """Final norm and one greedy output head of the language model.
+
+    The issue page "feat(nemotron_voicechat): ... offline duplex inference #1374", section
+    "Network 2": after the last layer the hidden state goes through norm_f, then through
+    lm_head and function_head, both 4-bit [4480 -> 131072] matrices without a linear bias,
+    and the text and function ids are the argmax of the last position (no sampling).
+    h = x / rms(x) * norm_w (rounded to bf16 in CONTRACT mode, the point where the GPU
+    kernel stores it); logits = dequant(W) h in fp64; ids = greedy_ids(logits).
+    x: [m][k_in] doubles.  Returns (logits [m][n_out], ids [m])."""
+    x2 = _d(x).reshape(-1, W.k_in)
+    h = rmsnorm(x2, norm_w, eps)
+    if mode == CONTRACT:
+        h = round_bf16(h)
+    logits = w4_matvec(W, h)
+    return logits, greedy_ids(logits)
 
 
 def rmsnorm_gated(y, z, w_bf16, group: int, eps: float) -> np.ndarray:

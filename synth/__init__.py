@@ -19,7 +19,9 @@ Distributions (the workload recipe, identical for every consumer):
   conv weight ~ N(0, 0.25^2), conv bias ~ N(0, 0.1^2), both norm weights
       1 + N(0, 0.05^2) (all bf16);
   block input x ~ N(0, 1) (bf16); pre-filled conv state ~ N(0, 1) (bf16);
-  pre-filled SSM state ~ N(0, 0.1^2) (float32).
+  pre-filled SSM state ~ N(0, 0.1^2) (float32);
+  output heads (lm_head, function_head, 131072 x 4480 each, the vocab_size of the
+      same config): drawn like in_proj; norm_f ~ 1 + N(0, 0.05^2) (bf16).
 
 Random streams: numpy PCG64 seeded by SeedSequence([seed, layer, tensor_id])
 for weights and SeedSequence([seed, 1000 + stream, tensor_id]) for inputs (stream: a
@@ -48,6 +50,11 @@ EPS = 1e-5
 _T_NORM_W, _T_IN_Q, _T_IN_S, _T_CONV_W, _T_CONV_B = 0, 1, 2, 3, 4
 _T_DT_BIAS, _T_A_LOG, _T_D, _T_GNORM_W, _T_OUT_Q, _T_OUT_S = 5, 6, 7, 8, 9, 10
 _I_X, _I_CONV_STATE, _I_SSM_STATE = 0, 1, 2
+# The final norm and the two output heads sit outside the 56 layers; they draw from
+# pseudo-layer HEADS_LAYER with their own tensor ids.
+HEADS_LAYER = 100
+_T_NORM_F, _T_LMH_Q, _T_LMH_S, _T_FNH_Q, _T_FNH_S = 11, 12, 13, 14, 15
+VOCAB = 131072
 
 
 @dataclass
@@ -146,6 +153,22 @@ def layer_weights(layer: int, seed: int = 0, d: Dims = REAL) -> LayerWeights:
     gnorm_w = f32_to_bf16(1.0 + g(_T_GNORM_W).normal(0.0, 0.05, d.d_inner).astype(f32))
     out_proj = w4_random(seed, layer, _T_OUT_Q, _T_OUT_S, d.hidden, d.d_inner, d.group_size)
     return LayerWeights(norm_w, in_proj, conv_w, conv_b, dt_bias, A_log, D, gnorm_w, out_proj)
+
+
+@dataclass
+class HeadWeights:
+    norm_f: np.ndarray          # bf16 [hidden]
+    lm_head: W4Matrix           # [n_out][hidden]
+    function_head: W4Matrix     # [n_out][hidden]
+
+
+def head_weights(seed: int = 0, n_out: int = VOCAB, d: Dims = REAL) -> HeadWeights:
+    """norm_f ~ 1 + N(0, 0.05^2) (bf16); both heads drawn like the mixer projections."""
+    g = rng(seed, HEADS_LAYER, _T_NORM_F)
+    norm_f = f32_to_bf16(1.0 + g.normal(0.0, 0.05, d.hidden).astype(np.float32))
+    lm = w4_random(seed, HEADS_LAYER, _T_LMH_Q, _T_LMH_S, n_out, d.hidden, d.group_size)
+    fn = w4_random(seed, HEADS_LAYER, _T_FNH_Q, _T_FNH_S, n_out, d.hidden, d.group_size)
+    return HeadWeights(norm_f, lm, fn)
 
 
 def block_input(stream: int, batch: int, T: int, seed: int = 0, d: Dims = REAL) -> np.ndarray:

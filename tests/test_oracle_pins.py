@@ -147,6 +147,64 @@ def test_gemv_one_hot_and_library_matmul(oracle_lib):
     assert np.allclose(oracle_lib.w4_matvec(W, x), x @ Wd.T, rtol=1e-13, atol=1e-12)
 
 
+# ----------------------------------------------------------- output head
+
+def test_greedy_ids_brute_force_rules(oracle_lib):
+    # small integer-valued rows full of ties, with NaN and infinities mixed in
+    rng = np.random.default_rng(11)
+    rows = rng.integers(-3, 4, size=(200, 9)).astype(np.float64)
+    rows[rng.random(rows.shape) < 0.15] = np.nan
+    rows[rng.random(rows.shape) < 0.05] = -np.inf
+    rows[rng.random(rows.shape) < 0.02] = np.inf
+    rows[0] = np.nan
+    rows[1] = -np.inf
+    got = oracle_lib.greedy_ids(rows)
+    for r, row in enumerate(rows):
+        best, bi = None, -1
+        for i, v in enumerate(row):
+            if math.isnan(v):
+                continue
+            if best is None or v > best:
+                best, bi = v, i
+        assert got[r] == bi, (r, row)
+    assert got[0] == -1 and got[1] == 0
+
+
+def test_head_planted_maximum_closed_form(oracle_lib):
+    # every nibble 9 and bias -8 s: row r of W is the constant s_r; a constant positive x
+    # normalises to 1/sqrt(1 + eps/c^2), which rounds to 1.0 in bf16 for c = 3
+    n, k, eps = 40, 4480, 1e-5
+    q = np.full((n, k // 8), 0x99999999, dtype=np.uint32)
+    s32 = np.linspace(0.002, 0.006, n).astype(np.float32)
+    s32[[7, 23]] = np.float32(0.0075)                    # tied largest rows: 7 wins
+    sb = synth.f32_to_bf16(np.repeat(s32[:, None], k // 64, axis=1))
+    bb = synth.f32_to_bf16(synth.bf16_to_f32(sb) * np.float32(-8.0))
+    W = synth.W4Matrix(q, sb, bb, n, k)
+    sd = synth.bf16_to_f32(sb[:, 0]).astype(np.float64)
+    x = np.full((2, k), 3.0)
+    x[1] *= -1.0                                          # negative x: h = -1, smallest s wins
+    wn = synth.f32_to_bf16(np.ones(k, dtype=np.float32))
+    logits, ids = oracle_lib.head(W, x, wn, eps)
+    assert np.allclose(logits[0], k * sd, rtol=1e-14) and np.allclose(logits[1], -k * sd, rtol=1e-14)
+    assert ids[0] == 7 and ids[1] == int(np.argmin(sd))
+    ex, _ = oracle_lib.head(W, x, wn, eps, mode=oracle_lib.EXACT)
+    assert np.allclose(ex[0], k * sd / math.sqrt(1 + eps / 9.0), rtol=1e-14)
+
+
+def test_head_matches_library_pieces(oracle_lib):
+    # EXACT mode is torch's rms_norm followed by a matmul with the byte-split dequantised W
+    rng = np.random.default_rng(12)
+    W = synth.w4_random(5, 2, 1, 2, 96, 4480)
+    _, Wd = _byte_split_dequant(W)
+    x = rng.normal(size=(3, 4480))
+    wn = synth.f32_to_bf16((1 + 0.05 * rng.normal(size=4480)).astype(np.float32))
+    wd = torch.from_numpy(synth.bf16_to_f32(wn).astype(np.float64))
+    h = F.rms_norm(torch.from_numpy(x), (4480,), weight=wd, eps=1e-5).numpy()
+    logits, ids = oracle_lib.head(W, x, wn, 1e-5, mode=oracle_lib.EXACT)
+    assert np.allclose(logits, h @ Wd.T, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(ids, np.argmax(h @ Wd.T, axis=1))
+
+
 # ---------------------------------------------------------------- norms
 
 def test_rmsnorm_constant_vector_closed_form(oracle_lib):
