@@ -40,6 +40,7 @@ HBM_PEAK = 8.0e12          # B/s, MI355X HBM3E
 MFMA_F16_PEAK = 2.5e15     # flop/s, dense bf16/fp16 matrix cores
 H, P, N, G, HID = 128, 80, 128, 8, 4480
 DI, CD, NIN = 10240, 12288, 22656
+VOCAB = 131072             # vocab_size: rows of each output head
 
 
 # ------------------------------------------------------- algorithmic work
@@ -149,6 +150,7 @@ def main():
     ap.add_argument("--skip-seq", action="store_true", help="skip the batch-2 T=3750 scan and stack")
     ap.add_argument("--skip-stack", action="store_true", help="skip the 27-layer stacks")
     ap.add_argument("--skip-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--skip-heads", action="store_true", help="skip the final norm + two output heads")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
@@ -305,6 +307,44 @@ def main():
         }
         log("stack steps:", out["stack_step"])
         del st3, outs3
+
+    # ----------- final norm + lm_head + function_head + greedy ids, batch 1, vocab 131072
+    if not args.skip_heads:
+        heads = []
+        for seed in range(2):   # two rotating sets of both heads: 1.3 GB, beyond the last-level cache
+            hw = synth.head_weights(seed=seed)
+            heads.append((gu.to_dev(hw.norm_f), gu.w4_dev(hw.lm_head), gu.w4_dev(hw.function_head)))
+            del hw
+        xh1 = gu.to_dev(np.random.default_rng(77).normal(0, 1, (1, HID)).astype(np.float32))
+        hws_n = nh.nh_head_workspace_bytes(1)
+        hws = gu.workspace(hws_n)
+        ids = [torch.empty(1, dtype=torch.int32, device="cuda") for _ in range(2)]
+
+        def head_pair(i):
+            nf, lm, fn = heads[i % 2]
+            nh.nh_head_argmax(lm, xh1, nh.NH_F32, nf, 1e-5, 1, None, ids[0], hws, hws_n, stream)
+            nh.nh_head_argmax(fn, xh1, nh.NH_F32, nf, 1e-5, 1, None, ids[1], hws, hws_n, stream)
+
+        for i in range(4):
+            head_pair(i)
+        reps = 100
+        hip.record(e0, stream)
+        for i in range(reps):
+            head_pair(i)
+        hip.record(e1, stream)
+        torch.cuda.synchronize()
+        pair_us = hip.ms(e0, e1) * 1e3 / reps
+        head_bytes = w4_bytes(VOCAB, HID) + HID * 4 + HID * 2
+        out["heads"] = {
+            "workload": "final norm + lm_head + function_head (W4 131072x4480 each) + greedy ids, batch 1, "
+                        "two rotating sets",
+            "us_per_position": round(pair_us, 2), "us_per_head": round(pair_us / 2, 2),
+            "algorithmic_bytes_per_head": int(head_bytes),
+            "hbm_frac": round(2 * head_bytes / (pair_us * 1e-6) / HBM_PEAK, 4),
+            "timing": f"{reps} back-to-back pairs of calls (head kernel + id kernel each), two HIP events",
+        }
+        log("heads:", out["heads"])
+        del heads
 
     # ------------------------- scan and 27-layer stack, batch 2, T=3750, chunk 256
     if not args.skip_seq:

@@ -37,7 +37,7 @@ EXPORTS = (
     "nh_w4_gemv", "nh_w4_gemm_workspace_bytes", "nh_w4_gemm", "nh_rmsnorm", "nh_inproj_conv_step",
     "nh_conv1d_step", "nh_conv1d_seq", "nh_ssm_step", "nh_ssd_scan_workspace_bytes", "nh_ssd_chunk_scan",
     "nh_rmsnorm_gated", "nh_block_workspace_bytes", "nh_mamba_block_step", "nh_mamba_block_seq",
-    "nh_mamba_stack",
+    "nh_mamba_stack", "nh_head_workspace_bytes", "nh_head_argmax",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -95,6 +95,8 @@ _sigs = {
     "nh_mamba_block_seq": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _i, _i, _vp, _sz, _vp]),
     "nh_mamba_stack": (_i, [_vp, _vp, _vp, _i, _i, _vp, _i, _i, _vp, _i, _vp, _sz, _vp]),
     "nh_profile_events": (_i, [_vp, _i]),
+    "nh_head_workspace_bytes": (_sz, [_i]),
+    "nh_head_argmax": (_i, [_vp, _vp, _i, _vp, C.c_float, _i, _vp, _vp, _vp, _sz, _vp]),
 }
 for _name, (_res, _args) in _sigs.items():
     _f = getattr(lib, _name)
@@ -169,6 +171,15 @@ def hybrid_pattern() -> str:
 def nh_w4_gemv(W, x, batch, residual, res_dtype, y, y_dtype, stream=None):
     _check(lib.nh_w4_gemv(C.byref(W), _ptr(x), batch, _ptr(residual), res_dtype, _ptr(y), y_dtype,
                           _stream(stream)))
+
+
+def nh_head_workspace_bytes(batch) -> int:
+    return lib.nh_head_workspace_bytes(batch)
+
+
+def nh_head_argmax(W, x, x_dtype, norm_w, eps, batch, logits, ids, ws, ws_bytes, stream=None):
+    _check(lib.nh_head_argmax(C.byref(W), _ptr(x), x_dtype, _ptr(norm_w), eps, batch, _ptr(logits),
+                              _ptr(ids), _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def nh_w4_gemm_workspace_bytes(M, k_in) -> int:

@@ -103,6 +103,10 @@ nh_status check_w4(const nh_w4_matrix *W, const char *name)
     if (W->n_out < 1 || W->k_in < 64 || W->k_in % 64 != 0 || W->k_in > 16384)
         return fail(NH_ERR_UNSUPPORTED_SHAPE, "%s: n_out %d, k_in %d (need n_out >= 1, k_in %% 64 == 0, "
                     "64 <= k_in <= 16384)", name, W->n_out, W->k_in);
+    // the kernels address the packed matrix through one 32-bit buffer range
+    if ((long long)W->n_out * (W->k_in / 2) >= (1LL << 31))
+        return fail(NH_ERR_UNSUPPORTED_SHAPE, "%s: packed matrix of %d x %d is 2 GiB or more", name,
+                    W->n_out, W->k_in);
     return NH_OK;
 }
 
@@ -319,6 +323,34 @@ nh_status nh_w4_gemv(const nh_w4_matrix *W, const uint16_t *x, int batch, const 
     if (residual) NH_TRY(need_dtype(res_dtype, "res_dtype"));
     if (batch < 1 || batch > 4) return fail(NH_ERR_UNSUPPORTED_SHAPE, "batch %d outside 1..4", batch);
     NH_HIP(launch_gemv(view(W), x, batch, residual, res_dtype, y, y_dtype, S(stream)), "gemv");
+    return ok();
+}
+
+size_t nh_head_workspace_bytes(int batch)
+{
+    if (batch < 1 || batch > 4) return 0;
+    return head_ws_bytes(batch);
+}
+
+nh_status nh_head_argmax(const nh_w4_matrix *W, const void *x, nh_dtype x_dtype, const uint16_t *norm_w,
+                         float eps, int batch, float *logits, int32_t *ids, void *ws, size_t ws_bytes,
+                         void *stream)
+{
+    NH_TRY(check_w4(W, "W"));
+    if (W->k_in != HIDDEN || W->n_out > (1 << 19))
+        return fail(NH_ERR_UNSUPPORTED_SHAPE, "head %d x %d (need k_in == %d, n_out <= 524288)", W->n_out,
+                    W->k_in, HIDDEN);
+    NH_TRY(need_ptr(x, "x"));
+    NH_TRY(need_dtype(x_dtype, "x_dtype"));
+    NH_TRY(need_ptr(norm_w, "norm_w"));
+    NH_TRY(opt_ptr(logits, "logits"));
+    NH_TRY(need_ptr(ids, "ids"));
+    NH_TRY(need_ptr(ws, "ws"));
+    if (!(eps > 0.f) || !std::isfinite(eps)) return fail(NH_ERR_INVALID_ARGUMENT, "eps must be positive");
+    if (batch < 1 || batch > 4) return fail(NH_ERR_UNSUPPORTED_SHAPE, "batch %d outside 1..4", batch);
+    if (ws_bytes < head_ws_bytes(batch))
+        return fail(NH_ERR_WORKSPACE_TOO_SMALL, "head workspace %zu < %zu bytes", ws_bytes, head_ws_bytes(batch));
+    NH_HIP(launch_head(view(W), x, x_dtype, norm_w, eps, batch, logits, ids, ws, S(stream)), "head");
     return ok();
 }
 

@@ -420,17 +420,26 @@ static inline int inproj_grid(int n)
     return 8 * ((bx + wpg - 1) / wpg);
 }
 
-template <int NB>
-struct InProjBlock {
-    using S = InProjShape<NB>;
-    static constexpr int R = S::R, NS = S::NS, RW = S::RW;
-    const EpiInProjStep epi;
-    int li, rb, nmax, rt;
-    bool active;
+// Loads and row sums of R-row stages in the K = 4480 chunk layout above.  Rows past the
+// matrix are clamped to its last row (a branch would make the compiler's waits conservative).
+template <int R>
+struct IpRows {
+    int li, nmax, rt;
     uint32_t toff, tsoff;
     __amdgpu_buffer_rsrc_t rq, rs, rbias;
-    IpStage<R> st[2];
-    EpiPre pe;
+
+    __device__ __forceinline__ void init(const W4 &W)
+    {
+        li = threadIdx.x & 63;
+        nmax = W.n - 1;
+        rq = __builtin_amdgcn_make_buffer_rsrc((void *)W.q, 0, (int)((uint32_t)W.n * IP_ROWB), 0x00020000);
+        rs = __builtin_amdgcn_make_buffer_rsrc((void *)W.s, 0, (int)((uint32_t)W.n * IP_GRPB), 0x00020000);
+        rbias = __builtin_amdgcn_make_buffer_rsrc((void *)W.b, 0, (int)((uint32_t)W.n * IP_GRPB), 0x00020000);
+        rt = min(li / IP_TAIL, R - 1);
+        const uint32_t tc = 128u + (uint32_t)(li % IP_TAIL);
+        toff = 16u * tc;
+        tsoff = 2u * (tc >> 1);
+    }
 
     __device__ __forceinline__ void load(IpStage<R> &g, int n) const
     {
@@ -451,9 +460,10 @@ struct InProjBlock {
         g.bt = __builtin_amdgcn_raw_buffer_load_b16(rbias, trow * IP_GRPB + tsoff, 0, 0);
     }
 
-    // stage k of the block: its R row sums go to lanes (k R + r) NB + b
-    __device__ __forceinline__ void compute(const IpStage<R> &g, int k, const ActChunk (&am)[NB][2],
-                                            const ActChunk (&at)[NB], float &v) const
+    // the R row sums of a stage for every batch row, complete in every lane
+    template <int NB>
+    __device__ __forceinline__ void sums(const IpStage<R> &g, const ActChunk (&am)[NB][2],
+                                         const ActChunk (&at)[NB], float (&out)[R][NB]) const
     {
         const uint32_t mlo = 0x000F000Fu, mhi = 0x00F000F0u, magic = 0x64006400u;
         float tail[NB];
@@ -466,9 +476,33 @@ struct InProjBlock {
                 float s = rt == r ? tail[b] : 0.f;
                 s = chunk_dot(g.q[r][0], g.s[r][0], g.b[r][0], am[b][0], s, mlo, mhi, magic);
                 s = chunk_dot(g.q[r][1], g.s[r][1], g.b[r][1], am[b][1], s, mlo, mhi, magic);
-                s = row_sum<64>(s);
-                if (li == (k * R + r) * NB + b) v = s;
+                out[r][b] = row_sum<64>(s);
             }
+    }
+};
+
+template <int NB>
+struct InProjBlock {
+    using S = InProjShape<NB>;
+    static constexpr int R = S::R, NS = S::NS, RW = S::RW;
+    const EpiInProjStep epi;
+    IpRows<R> io;
+    int rb;
+    bool active;
+    IpStage<R> st[2];
+    EpiPre pe;
+
+    // stage k of the block: its R row sums go to lanes (k R + r) NB + b
+    __device__ __forceinline__ void compute(const IpStage<R> &g, int k, const ActChunk (&am)[NB][2],
+                                            const ActChunk (&at)[NB], float &v) const
+    {
+        float sm[R][NB];
+        io.template sums<NB>(g, am, at, sm);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                if (io.li == (k * R + r) * NB + b) v = sm[r][b];
     }
 
     // Issues the epilogue prefetch and the first stage (unconditionally, rows clamped: a
@@ -476,7 +510,7 @@ struct InProjBlock {
     // also cover these loads; idle waves read the last row, which the cache holds).
     __device__ __forceinline__ InProjBlock(const W4 &W, const EpiInProjStep &e) : epi(e)
     {
-        li = threadIdx.x & 63;
+        io.init(W);
         const int xcd = blockIdx.x & 7;
         const int wave = __builtin_amdgcn_readfirstlane(
             (int)((threadIdx.x >> 6) * (gridDim.x >> 3) + (blockIdx.x >> 3)));
@@ -484,16 +518,8 @@ struct InProjBlock {
         const int blk = xcd * bx + wave;
         active = wave < bx && blk < nblk;
         rb = min(blk, nblk - 1) * RW;
-        nmax = W.n - 1;
-        rq = __builtin_amdgcn_make_buffer_rsrc((void *)W.q, 0, (int)((uint32_t)W.n * IP_ROWB), 0x00020000);
-        rs = __builtin_amdgcn_make_buffer_rsrc((void *)W.s, 0, (int)((uint32_t)W.n * IP_GRPB), 0x00020000);
-        rbias = __builtin_amdgcn_make_buffer_rsrc((void *)W.b, 0, (int)((uint32_t)W.n * IP_GRPB), 0x00020000);
-        rt = min(li / IP_TAIL, R - 1);
-        const uint32_t tc = 128u + (uint32_t)(li % IP_TAIL);
-        toff = 16u * tc;
-        tsoff = 2u * (tc >> 1);
-        load(st[0], rb);
-        pe = epi.prefetch(min(rb + min(li / NB, RW - 1), nmax), li % NB);
+        io.load(st[0], rb);
+        pe = epi.prefetch(min(rb + min(io.li / NB, RW - 1), io.nmax), io.li % NB);
     }
 
     __device__ __forceinline__ void run(const ActChunk (&am)[NB][2], const ActChunk (&at)[NB])
@@ -502,15 +528,123 @@ struct InProjBlock {
         float v = 0.f;
 #pragma unroll
         for (int k = 0; k < NS; ++k) {
-            if (k + 1 < NS) load(st[(k + 1) & 1], rb + (k + 1) * R);
+            if (k + 1 < NS) io.load(st[(k + 1) & 1], rb + (k + 1) * R);
             __builtin_amdgcn_sched_barrier(0);
             compute(st[k & 1], k, am, at, v);
             __builtin_amdgcn_sched_barrier(0);
         }
-        const int row = rb + li / NB;
-        if (li < RW * NB && row <= nmax) epi(row, li % NB, v, pe);
+        const int row = rb + io.li / NB;
+        if (io.li < RW * NB && row <= io.nmax) epi(row, io.li % NB, v, pe);
     }
 };
+
+// Pre-norm of the per-position kernels whose K is the hidden size.  Thread t < 140 owns the
+// 32-value chunk t of x (every batch row) and of the norm weight.  issue() sends the raw loads
+// (a wave's loads complete in issue order, so issued before the caller's first weight stage
+// they are all the pre-norm waits for); finish() widens them, sums the squares over the
+// work-group and writes u = bf16(x / rms(x) * w) to LDS in the activation format.
+template <int NB, int XT, int NT>
+struct PreNorm {
+    static constexpr int NCH = HIDDEN / 32, NW = NT / 64;
+    static constexpr int XW = XT == BF16 ? 4 : 8;  // 16-byte words per 32 values
+    bool own;
+    uint4 xr[NB][XW], wq[4];
+
+    __device__ __forceinline__ void issue(const void *x, const uint16_t *nw)
+    {
+        own = (int)threadIdx.x < NCH;
+        if (own) {
+            const uint4 *wsrc = reinterpret_cast<const uint4 *>(nw + 32 * threadIdx.x);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) wq[j] = wsrc[j];
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const uint4 *src = XT == BF16
+                    ? reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(x) + (size_t)b * HIDDEN + 32 * threadIdx.x)
+                    : reinterpret_cast<const uint4 *>(reinterpret_cast<const float *>(x) + (size_t)b * HIDDEN + 32 * threadIdx.x);
+#pragma unroll
+                for (int j = 0; j < XW; ++j) xr[b][j] = src[j];
+            }
+        }
+    }
+
+    __device__ __forceinline__ void finish(float eps, uint32_t *act_lds, float (&red)[NB][NW])
+    {
+        float xv[NB][32], w[32];
+        if (own) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                w[8 * j + 0] = bf16lo(wq[j].x); w[8 * j + 1] = bf16hi(wq[j].x); w[8 * j + 2] = bf16lo(wq[j].y);
+                w[8 * j + 3] = bf16hi(wq[j].y); w[8 * j + 4] = bf16lo(wq[j].z); w[8 * j + 5] = bf16hi(wq[j].z);
+                w[8 * j + 6] = bf16lo(wq[j].w); w[8 * j + 7] = bf16hi(wq[j].w);
+            }
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int j = 0; j < XW; ++j) {
+                    const uint4 r = xr[b][j];
+                    if (XT == BF16) {
+                        xv[b][8 * j + 0] = bf16lo(r.x); xv[b][8 * j + 1] = bf16hi(r.x); xv[b][8 * j + 2] = bf16lo(r.y);
+                        xv[b][8 * j + 3] = bf16hi(r.y); xv[b][8 * j + 4] = bf16lo(r.z); xv[b][8 * j + 5] = bf16hi(r.z);
+                        xv[b][8 * j + 6] = bf16lo(r.w); xv[b][8 * j + 7] = bf16hi(r.w);
+                    } else {
+                        xv[b][4 * j + 0] = __uint_as_float(r.x); xv[b][4 * j + 1] = __uint_as_float(r.y);
+                        xv[b][4 * j + 2] = __uint_as_float(r.z); xv[b][4 * j + 3] = __uint_as_float(r.w);
+                    }
+                }
+        }
+        // sum of squares per batch row
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            float ss = 0.f;
+            if (own)
+#pragma unroll
+                for (int e = 0; e < 32; ++e) ss += xv[b][e] * xv[b][e];
+            ss = wave_sum(ss);
+            if ((threadIdx.x & 63) == 0) red[b][threadIdx.x >> 6] = ss;
+        }
+        __syncthreads();
+        // normalised, bf16-rounded chunks
+        if (own) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                float tot = 0.f;
+#pragma unroll
+                for (int i = 0; i < NW; ++i) tot += red[b][i];
+                const float r = 1.0f / sqrtf(tot / (float)HIDDEN + eps);
+                float v[32];
+#pragma unroll
+                for (int e = 0; e < 32; ++e) v[e] = round_bf16(xv[b][e] * r * w[e]);
+                make_chunk(v, act_lds + ((size_t)b * NCH + threadIdx.x) * ACT_WORDS);
+            }
+        }
+        __syncthreads();
+    }
+};
+
+// Activations of the lane's chunks in the K = 4480 layout: l and l + 64 of every row, and
+// its tail chunk 128 + l % 12 (zero for lanes beyond the R rows' tails).
+template <int NB, int R>
+__device__ __forceinline__ void act_hidden(ActChunk (&am)[NB][2], ActChunk (&at)[NB], const uint32_t *act_lds)
+{
+    constexpr int NCH = HIDDEN / 32;
+    const int l = threadIdx.x & 63;
+    const bool tail = l < IP_TAIL * R;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            chunk_from_lds(am[b][i], act_lds + ((size_t)b * NCH + l + 64 * i) * ACT_WORDS);
+        }
+        chunk_from_lds(at[b], act_lds + ((size_t)b * NCH + 128 + l % IP_TAIL) * ACT_WORDS);
+        if (!tail) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) at[b].p[j] = 0u;
+            at[b].off = 0.f;
+            at[b].sum = 0.f;
+        }
+    }
+}
 
 // ------------------------------------------------------------------ kernels
 
@@ -546,98 +680,17 @@ __global__ __launch_bounds__(InProjShape<NB>::NT, 1) void k_inproj_step(W4 W, co
                                                                     EpiInProjStep epi, uint32_t *zero_ptr,
                                                                     int nzero)
 {
-    constexpr int NCH = HIDDEN / 32, R = InProjShape<NB>::R, NW = InProjShape<NB>::NT / 64;
+    constexpr int NT = InProjShape<NB>::NT, R = InProjShape<NB>::R;
     extern __shared__ __attribute__((aligned(16))) uint32_t act_lds[];
-    __shared__ float red[NB][NW];
+    __shared__ float red[NB][NT / 64];
     if (blockIdx.x == 0 && (int)threadIdx.x < nzero) zero_ptr[threadIdx.x] = 0u;
-    // Raw loads of the thread's x chunk (every batch row) and norm-weight chunk, issued before
-    // the first weight stage: a wave's loads complete in issue order, so the pre-norm then
-    // waits only for these.  Values are widened after the weight loads are in flight.
-    constexpr int XW = XT == BF16 ? 4 : 8;  // 16-byte words per 32 values
-    const bool own = (int)threadIdx.x < NCH;
-    uint4 xr[NB][XW], wq[4];
-    if (own) {
-        const uint4 *wsrc = reinterpret_cast<const uint4 *>(nw + 32 * threadIdx.x);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) wq[j] = wsrc[j];
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            const uint4 *src = XT == BF16
-                ? reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(x) + (size_t)b * HIDDEN + 32 * threadIdx.x)
-                : reinterpret_cast<const uint4 *>(reinterpret_cast<const float *>(x) + (size_t)b * HIDDEN + 32 * threadIdx.x);
-#pragma unroll
-            for (int j = 0; j < XW; ++j) xr[b][j] = src[j];
-        }
-    }
+    PreNorm<NB, XT, NT> pn;
+    pn.issue(x, nw);
     __builtin_amdgcn_sched_barrier(0);
     InProjBlock<NB> run(W, epi);
-    float xv[NB][32], w[32];
-    if (own) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            w[8 * j + 0] = bf16lo(wq[j].x); w[8 * j + 1] = bf16hi(wq[j].x); w[8 * j + 2] = bf16lo(wq[j].y);
-            w[8 * j + 3] = bf16hi(wq[j].y); w[8 * j + 4] = bf16lo(wq[j].z); w[8 * j + 5] = bf16hi(wq[j].z);
-            w[8 * j + 6] = bf16lo(wq[j].w); w[8 * j + 7] = bf16hi(wq[j].w);
-        }
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-            for (int j = 0; j < XW; ++j) {
-                const uint4 r = xr[b][j];
-                if (XT == BF16) {
-                    xv[b][8 * j + 0] = bf16lo(r.x); xv[b][8 * j + 1] = bf16hi(r.x); xv[b][8 * j + 2] = bf16lo(r.y);
-                    xv[b][8 * j + 3] = bf16hi(r.y); xv[b][8 * j + 4] = bf16lo(r.z); xv[b][8 * j + 5] = bf16hi(r.z);
-                    xv[b][8 * j + 6] = bf16lo(r.w); xv[b][8 * j + 7] = bf16hi(r.w);
-                } else {
-                    xv[b][4 * j + 0] = __uint_as_float(r.x); xv[b][4 * j + 1] = __uint_as_float(r.y);
-                    xv[b][4 * j + 2] = __uint_as_float(r.z); xv[b][4 * j + 3] = __uint_as_float(r.w);
-                }
-            }
-    }
-    // sum of squares per batch row
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-        float ss = 0.f;
-        if (own)
-#pragma unroll
-            for (int e = 0; e < 32; ++e) ss += xv[b][e] * xv[b][e];
-        ss = wave_sum(ss);
-        if ((threadIdx.x & 63) == 0) red[b][threadIdx.x >> 6] = ss;
-    }
-    __syncthreads();
-    // normalised, bf16-rounded chunks
-    if (own) {
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            float tot = 0.f;
-#pragma unroll
-            for (int i = 0; i < NW; ++i) tot += red[b][i];
-            const float r = 1.0f / sqrtf(tot / (float)HIDDEN + eps);
-            float v[32];
-#pragma unroll
-            for (int e = 0; e < 32; ++e) v[e] = round_bf16(xv[b][e] * r * w[e]);
-            make_chunk(v, act_lds + ((size_t)b * NCH + threadIdx.x) * ACT_WORDS);
-        }
-    }
-    __syncthreads();
-    // activations of the lane's chunks: l and l + 64 of every row, and its tail chunk
+    pn.finish(eps, act_lds, red);
     ActChunk am[NB][2], at[NB];
-    const int l = threadIdx.x & 63;
-    const bool tail = l < IP_TAIL * R;
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            chunk_from_lds(am[b][i], act_lds + ((size_t)b * NCH + l + 64 * i) * ACT_WORDS);
-        }
-        chunk_from_lds(at[b], act_lds + ((size_t)b * NCH + 128 + l % IP_TAIL) * ACT_WORDS);
-        if (!tail) {
-#pragma unroll
-            for (int j = 0; j < 16; ++j) at[b].p[j] = 0u;
-            at[b].off = 0.f;
-            at[b].sum = 0.f;
-        }
-    }
+    act_hidden<NB, R>(am, at, act_lds);
     run.run(am, at);
 }
 
@@ -719,6 +772,165 @@ __global__ __launch_bounds__(NB == 1 ? 512 : 256, 1) void k_outproj_step(W4 W, c
     ActChunk a[NB][CPL];
     act_from_lds<LPR, CPL, NB>(a, act_lds, NCH, (threadIdx.x & 63) % LPR);
     run.run(a);
+}
+
+// Final norm + one W4 output head + greedy id.  The head has K = hidden, so it shares the
+// in_proj chunk layout and pre-norm; its 131072 rows are R-row stages split into one
+// contiguous range per XCD and, inside it, one contiguous range per wave (so rows that share
+// scale cache lines stay in one L2).  A wave streams its range with two stages in flight,
+// keeps the best (logit, row) of each batch row, and the work-group's best goes to
+// part_v / part_i [NB][gridDim.x] for k_head_finish.  Logits are stored only on request.
+//
+// Greedy order: (v, n) beats (bv, bn) when v is not NaN and (bn < 0 or v > bv or
+// (v == bv and n < bn)); it is a total order on the candidates, so any reduction tree gives
+// the smallest row among those with the largest logit.
+__device__ __forceinline__ bool greedy_better(float v, int n, float bv, int bn)
+{
+    return n >= 0 && v == v && (bn < 0 || v > bv || (v == bv && n < bn));
+}
+
+constexpr int HEAD_WGS = 256;  // work-groups of the head kernel: 32 per XCD
+
+template <int NB, int XT>
+__global__ __launch_bounds__(InProjShape<NB>::NT, 1) void k_head_step(W4 W, const void *__restrict__ x,
+                                                                  const uint16_t *__restrict__ nw, float eps,
+                                                                  float *__restrict__ logits,
+                                                                  float *__restrict__ part_v,
+                                                                  int *__restrict__ part_i)
+{
+    constexpr int NT = InProjShape<NB>::NT, R = InProjShape<NB>::R, NW = NT / 64;
+    extern __shared__ __attribute__((aligned(16))) uint32_t act_lds[];
+    __shared__ float red[NB][NW];
+    __shared__ float wv[NB][NW];
+    __shared__ int wi[NB][NW];
+    PreNorm<NB, XT, NT> pn;
+    pn.issue(x, nw);
+    __builtin_amdgcn_sched_barrier(0);
+    IpRows<R> io;
+    io.init(W);
+    // this wave's stages [s0, s1): an even split per XCD, then per wave inside the XCD
+    const long nst = (W.n + R - 1) / R;
+    const int xcd = blockIdx.x & 7, nwx = (int)(gridDim.x >> 3) * NW;
+    const int wx = __builtin_amdgcn_readfirstlane((int)((blockIdx.x >> 3) * NW + (threadIdx.x >> 6)));
+    const long xs = nst * xcd / 8, xn = nst * (xcd + 1) / 8 - xs;
+    const int s0 = (int)(xs + xn * wx / nwx), s1 = (int)(xs + xn * (wx + 1) / nwx);
+    IpStage<R> A, B;
+    io.load(A, min(s0, (int)nst - 1) * R);
+    pn.finish(eps, act_lds, red);
+    ActChunk am[NB][2], at[NB];
+    act_hidden<NB, R>(am, at, act_lds);
+
+    float bv[NB];
+    int bi[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        bv[b] = -INFINITY;
+        bi[b] = -1;
+    }
+    auto step = [&](const IpStage<R> &g, int s) {
+        float sm[R][NB];
+        io.template sums<NB>(g, am, at, sm);
+        float mine = 0.f;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const int n = s * R + r;
+                const float v = sm[r][b];
+                if (n < W.n && greedy_better(v, n, bv[b], bi[b])) {
+                    bv[b] = v;
+                    bi[b] = n;
+                }
+                if (io.li == r * NB + b) mine = v;
+            }
+        const int n = s * R + io.li / NB;
+        if (logits && io.li < R * NB && n < W.n) logits[(size_t)(io.li % NB) * W.n + n] = mine;
+    };
+    // no conditional load in the loop (see GemvRunner::run); the last one or two stages peeled
+    const int cnt = s1 - s0;
+    if (cnt > 0) {
+        int s = s0, i = 0;
+        for (; i + 2 < cnt; i += 2, s += 2) {
+            io.load(B, (s + 1) * R);
+            __builtin_amdgcn_sched_barrier(0);
+            step(A, s);
+            io.load(A, (s + 2) * R);
+            __builtin_amdgcn_sched_barrier(0);
+            step(B, s + 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (i + 1 < cnt) {
+            io.load(B, (s + 1) * R);
+            __builtin_amdgcn_sched_barrier(0);
+            step(A, s);
+            __builtin_amdgcn_sched_barrier(0);
+            step(B, s + 1);
+        } else {
+            step(A, s);
+        }
+    }
+    const int wave = threadIdx.x >> 6;
+    if (io.li == 0)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            wv[b][wave] = bv[b];
+            wi[b][wave] = bi[b];
+        }
+    __syncthreads();
+    if ((int)threadIdx.x < NB) {
+        const int b = threadIdx.x;
+        float v = wv[b][0];
+        int n = wi[b][0];
+        for (int w = 1; w < NW; ++w)
+            if (greedy_better(wv[b][w], wi[b][w], v, n)) {
+                v = wv[b][w];
+                n = wi[b][w];
+            }
+        part_v[b * gridDim.x + blockIdx.x] = v;
+        part_i[b * gridDim.x + blockIdx.x] = n;
+    }
+}
+
+// The greedy id of each batch row from the work-groups' partial results: one work-group of
+// 256 threads, one partial per thread, then wave and work-group reductions in greedy order.
+__global__ __launch_bounds__(256) void k_head_finish(const float *__restrict__ part_v,
+                                                     const int *__restrict__ part_i, int nparts,
+                                                     int batch, int *__restrict__ ids)
+{
+    __shared__ float sv[4];
+    __shared__ int si[4];
+    for (int b = 0; b < batch; ++b) {
+        float v = -INFINITY;
+        int n = -1;
+        for (int t = threadIdx.x; t < nparts; t += 256)
+            if (greedy_better(part_v[b * nparts + t], part_i[b * nparts + t], v, n)) {
+                v = part_v[b * nparts + t];
+                n = part_i[b * nparts + t];
+            }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+            const float ov = __shfl_xor(v, o, 64);
+            const int on = __shfl_xor(n, o, 64);
+            if (greedy_better(ov, on, v, n)) {
+                v = ov;
+                n = on;
+            }
+        }
+        if ((threadIdx.x & 63) == 0) {
+            sv[threadIdx.x >> 6] = v;
+            si[threadIdx.x >> 6] = n;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            for (int w = 1; w < 4; ++w)
+                if (greedy_better(sv[w], si[w], v, n)) {
+                    v = sv[w];
+                    n = si[w];
+                }
+            ids[b] = n;
+        }
+        __syncthreads();
+    }
 }
 
 // ------------------------------------------------------------------ launchers
@@ -819,6 +1031,35 @@ hipError_t launch_inproj_step(const W4 &W, const void *x, int x_t, const uint16_
     default: NH_LAUNCH(4); break;
     }
 #undef NH_LAUNCH
+    return hipGetLastError();
+}
+
+size_t head_ws_bytes(int batch) { return (size_t)batch * HEAD_WGS * (sizeof(float) + sizeof(int)); }
+
+hipError_t launch_head(const W4 &W, const void *x, int x_t, const uint16_t *norm_w, float eps, int batch,
+                       float *logits, int *ids, void *ws, hipStream_t st)
+{
+    float *pv = reinterpret_cast<float *>(ws);
+    int *pi = reinterpret_cast<int *>(pv + (size_t)batch * HEAD_WGS);
+    const size_t lds = (size_t)batch * (HIDDEN / 32) * ACT_WORDS * 4;
+#define NH_LAUNCH(NB)                                                                                   \
+    {                                                                                                   \
+        const dim3 blk(InProjShape<NB>::NT);                                                            \
+        if (x_t == BF16)                                                                                \
+            launch_k(k_head_step<NB, BF16>, dim3(HEAD_WGS), blk, lds, st, W, x, norm_w, eps, logits, pv, pi); \
+        else                                                                                            \
+            launch_k(k_head_step<NB, F32>, dim3(HEAD_WGS), blk, lds, st, W, x, norm_w, eps, logits, pv, pi);  \
+    }
+    switch (batch) {
+    case 1: NH_LAUNCH(1); break;
+    case 2: NH_LAUNCH(2); break;
+    case 3: NH_LAUNCH(3); break;
+    default: NH_LAUNCH(4); break;
+    }
+#undef NH_LAUNCH
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    k_head_finish<<<dim3(1), dim3(256), 0, st>>>(pv, pi, HEAD_WGS, batch, ids);
     return hipGetLastError();
 }
 

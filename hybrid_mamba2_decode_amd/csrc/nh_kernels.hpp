@@ -50,6 +50,11 @@ hipError_t launch_inproj_step(const W4 &W, const void *x, int x_t, const uint16_
                               uint16_t *conv_state, const uint16_t *conv_w,
                               const uint16_t *conv_b, uint32_t *zero_ptr, int nzero,
                               hipStream_t st);
+// Final norm + one W4 head (k = HIDDEN) + greedy id per batch row; logits optional.  Two
+// kernels; ws holds head_ws_bytes(batch) bytes of per-work-group partial results.
+size_t head_ws_bytes(int batch);
+hipError_t launch_head(const W4 &W, const void *x, int x_t, const uint16_t *norm_w, float eps, int batch,
+                       float *logits, int *ids, void *ws, hipStream_t st);
 hipError_t launch_ssm_step(const uint16_t *xc, const uint16_t *dtr, long ld_dt,
                            const float *dt_bias, const float *A_log, const float *D, float *S,
                            void *y, int y_t, int batch, hipStream_t st);

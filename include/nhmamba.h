@@ -74,7 +74,8 @@ typedef struct {
  *   W[n][k] = scales[n][k/64] * q[n][k] + biases[n][k/64],
  *   q[n][k] = (qweight[n][k/8] >> 4*(k%8)) & 15   (lowest nibble first).
  * qweight: u32 [n_out][k_in/8]; scales, biases: bf16 [n_out][k_in/64].
- * Requirements: group_size == 64, k_in % 64 == 0, k_in <= 16384. */
+ * Requirements: group_size == 64, k_in % 64 == 0, k_in <= 16384, and the
+ * packed matrix under 2 GiB (n_out * k_in / 2 < 2^31 bytes). */
 typedef struct {
     const uint32_t *qweight;
     const uint16_t *scales;
@@ -214,6 +215,33 @@ nh_status nh_ssd_chunk_scan(const nh_mamba_dims *d, const uint16_t *xc, const ui
  * out: bf16 [rows][d].  d % group == 0, group % 8 == 0. */
 nh_status nh_rmsnorm_gated(const uint16_t *y, const uint16_t *z, long ld_z, const uint16_t *w,
                            uint16_t *out, int rows, int d, int group, float eps, void *stream);
+
+/* ----------------------------------------------------------- model top */
+
+/* Final norm, one output head and the greedy id for `batch` positions
+ * (issue page, section "Network 2": after the last layer the hidden state
+ * goes through norm_f, then through lm_head and function_head, both 4-bit
+ * [4480 -> 131072] matrices without a linear bias; the text and function ids
+ * are the argmax of the last position, with no sampling).  Call it once per
+ * head.
+ *   h = bf16(x / rms(x) * norm_w)   (RMS over the 4480 values, eps inside
+ *                                    the root)
+ *   logits[b][n] = W[n] . h[b]      (fp32 accumulation)
+ *   ids[b] = the smallest n holding the largest logits[b][n]; NaN logits
+ *            are never chosen, and a row of NaN logits gives -1.
+ * W: k_in == 4480, n_out 1 .. 524288; x: [batch][4480] of x_dtype; norm_w:
+ * bf16 [4480]; logits: nullable f32 [batch][n_out] (NULL: not stored);
+ * ids: int32 [batch]; ws: caller-owned device workspace of at least
+ * nh_head_workspace_bytes(batch) bytes, contents on return unspecified.
+ * batch 1..4.  Every pointer 16-byte aligned.  Two kernels on `stream`; the
+ * ids are bitwise deterministic.  Errors (checked before any launch):
+ * NH_ERR_UNSUPPORTED_SHAPE for k_in, n_out or batch outside these ranges,
+ * NH_ERR_WORKSPACE_TOO_SMALL, NH_ERR_MISALIGNED, NH_ERR_INVALID_ARGUMENT for
+ * NULL pointers, an unknown dtype or eps <= 0. */
+size_t nh_head_workspace_bytes(int batch);
+nh_status nh_head_argmax(const nh_w4_matrix *W, const void *x, nh_dtype x_dtype,
+                         const uint16_t *norm_w, float eps, int batch, float *logits,
+                         int32_t *ids, void *ws, size_t ws_bytes, void *stream);
 
 /* -------------------------------------------------------------- blocks */
 

@@ -65,6 +65,37 @@ def test_gemv_rejects_bad_arguments(nh):
     assert "batch" in nh.lib.nh_last_error().decode() or "dtype" in nh.lib.nh_last_error().decode()
 
 
+def test_packed_matrix_over_2gib_rejected(nh):
+    A = 0x20000
+    big = nh_w4(A, A + 0x1000, A + 0x2000, 1 << 18, 16384, 64)   # 2 GiB of packed words
+    assert _status(lambda: nh.nh_w4_gemv(big, A, 1, None, 0, A, 0, 0)) == nh.NH_ERR_UNSUPPORTED_SHAPE
+    assert "2 GiB" in nh.lib.nh_last_error().decode()
+
+
+def test_head_rejects_bad_arguments(nh):
+    A = 0x20000
+    ws = nh.nh_head_workspace_bytes(1)
+    assert ws == 256 * 8 and nh.nh_head_workspace_bytes(4) == 4 * 256 * 8
+    assert nh.nh_head_workspace_bytes(0) == 0 and nh.nh_head_workspace_bytes(5) == 0
+    W = _fake_w4(n=131072, k=4480)
+    ok = dict(W=W, x=A, x_dtype=0, norm_w=A, eps=1e-5, batch=1, logits=None, ids=A, ws=A, ws_bytes=ws)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return _status(lambda: nh.nh_head_argmax(a["W"], a["x"], a["x_dtype"], a["norm_w"], a["eps"],
+                                                 a["batch"], a["logits"], a["ids"], a["ws"], a["ws_bytes"], 0))
+    assert call(W=_fake_w4(n=1000, k=4096)) == nh.NH_ERR_UNSUPPORTED_SHAPE        # k_in != hidden
+    assert call(W=_fake_w4(n=(1 << 19) + 1, k=4480)) == nh.NH_ERR_UNSUPPORTED_SHAPE
+    assert call(batch=0) == nh.NH_ERR_UNSUPPORTED_SHAPE
+    assert call(batch=5) == nh.NH_ERR_UNSUPPORTED_SHAPE
+    assert call(ws_bytes=ws - 1) == nh.NH_ERR_WORKSPACE_TOO_SMALL
+    assert call(ids=None) == nh.NH_ERR_INVALID_ARGUMENT
+    assert call(norm_w=A + 2) == nh.NH_ERR_MISALIGNED
+    assert call(logits=A + 4) == nh.NH_ERR_MISALIGNED
+    assert call(x_dtype=3) == nh.NH_ERR_INVALID_ARGUMENT
+    assert call(eps=0.0) == nh.NH_ERR_INVALID_ARGUMENT
+
+
 def test_gemm_workspace_check(nh):
     A = 0x20000
     need = nh.nh_w4_gemm_workspace_bytes(100, 128)

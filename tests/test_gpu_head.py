@@ -1,0 +1,133 @@
+"""GPU parity of the final norm + one W4 output head + greedy id (nh_head_argmax) against
+the CPU oracle, through the C ABI.
+
+Logits: the kernel's fp32 sums of exact products against the oracle's fp64 sums over the
+same bf16 normalised input h, apart from rare one-unit bf16 flips of h where the fp32 norm
+lands on a rounding boundary; a flip moves a logit by about s |q - 8| |h| 2^-8 (below 2e-4
+for these weights), so |gpu - oracle| <= 2e-3 on logits of spread about 1.3.
+Ids: rows whose logits lie within that tolerance of the maximum could be ordered either way
+by rounding, so the test checks what is unique -- the GPU id is the greedy id of the GPU's
+own logits (smallest row of the largest value, NaN never chosen) -- and that the oracle's
+logit of that row is within twice the tolerance of the oracle's maximum."""
+import numpy as np
+import pytest
+
+import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    import hybrid_mamba2_decode_amd as nh
+    import oracle
+    from tests import gpu_util as gu
+    oracle.build(force=False)
+    assert torch.cuda.is_available()
+    return nh, oracle, gu, torch
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _x(seed, batch, f32):
+    x = synth.rng(seed, 2000, 0).normal(0.0, 1.0, (batch, 4480)).astype(np.float32)
+    if f32:
+        return x, x.astype(np.float64)
+    xb = synth.f32_to_bf16(x)
+    return xb, synth.bf16_to_f32(xb).astype(np.float64)
+
+
+def _run(env, W, norm_f, x, f32, batch, with_logits=True):
+    nh, oracle, gu, torch = env
+    ws = gu.workspace(nh.nh_head_workspace_bytes(batch))
+    logits = gu.empty_f32(batch, W.n_out) if with_logits else None
+    ids = torch.full((batch,), -7, dtype=torch.int32, device=gu.DEV)
+    nh.nh_head_argmax(gu.w4_dev(W), gu.to_dev(x), nh.NH_F32 if f32 else nh.NH_BF16, gu.to_dev(norm_f),
+                      1e-5, batch, logits, ids, ws, ws.numel())
+    torch.cuda.synchronize()
+    return (None if logits is None else logits.cpu().numpy().astype(np.float64)), ids.cpu().numpy()
+
+
+def _check(oracle, got_l, got_ids, ref_l):
+    assert np.all(np.abs(got_l - ref_l) <= TOL), np.abs(got_l - ref_l).max()
+    assert np.array_equal(got_ids, oracle.greedy_ids(got_l))
+    for b, i in enumerate(got_ids):
+        assert ref_l[b, i] >= ref_l[b].max() - 2 * TOL
+
+
+@pytest.mark.parametrize("n_out", [1, 7, 1001])
+@pytest.mark.parametrize("batch", [1, 2, 3, 4])
+@pytest.mark.parametrize("f32", [False, True])
+def test_head_small_and_ragged(env, n_out, batch, f32):
+    # fewer rows than waves (most waves empty), an odd last stage, every batch width
+    nh, oracle, gu, torch = env
+    _say("head", n_out, batch, f32)
+    hw = synth.head_weights(seed=3, n_out=n_out)
+    x, xd = _x(n_out + 10 * batch, batch, f32)
+    got_l, got_ids = _run(env, hw.lm_head, hw.norm_f, x, f32, batch)
+    ref_l, _ = oracle.head(hw.lm_head, xd, hw.norm_f, 1e-5)
+    _check(oracle, got_l, got_ids, ref_l)
+
+
+@pytest.mark.slow
+def test_head_full_vocab_both_heads(env):
+    # the model's two heads at vocab_size 131072, batch 1, in the launch configuration timed
+    # by the benchmark; ids with and without the logits stored
+    nh, oracle, gu, torch = env
+    hw = synth.head_weights()
+    x, xd = _x(0, 1, True)
+    for name, W in (("lm_head", hw.lm_head), ("function_head", hw.function_head)):
+        _say("head full", name)
+        got_l, got_ids = _run(env, W, hw.norm_f, x, True, 1)
+        ref_l, _ = oracle.head(W, xd, hw.norm_f, 1e-5)
+        _check(oracle, got_l, got_ids, ref_l)
+        _, ids_only = _run(env, W, hw.norm_f, x, True, 1, with_logits=False)
+        assert np.array_equal(ids_only, got_ids)
+
+
+def _pack(qv):
+    """Nibbles [n][k] (0..15) into the packed words [n][k/8], lowest nibble first."""
+    qv = np.asarray(qv, dtype=np.uint32).reshape(qv.shape[0], -1, 8)
+    return (qv << (4 * np.arange(8, dtype=np.uint32))).sum(axis=2, dtype=np.uint32)
+
+
+@pytest.mark.parametrize("batch", [1, 2])
+def test_head_tie_takes_lowest_row(env, batch):
+    # For batch row b the rows pairs[b] hold identical words q_k = 8 + 7 sign(x_b[k]), so their
+    # logits (7 s sum |h|) tie far above every random row; both rows of a pair have the same
+    # parity (the same lane layout), so their fp32 sums are bit-identical.
+    nh, oracle, gu, torch = env
+    _say("head tie", batch)
+    pairs = [(500, 900), (1500, 2500)][:batch]
+    hw = synth.head_weights(seed=4, n_out=3000)
+    W = hw.lm_head
+    x, xd = _x(5, batch, False)
+    q = W.qweight.copy()
+    for b, (i, j) in enumerate(pairs):
+        q[i] = q[j] = _pack((8 + 7 * np.sign(xd[b])).astype(np.int64)[None, :])[0]
+        # the same scale and bias too
+        W.scales[j], W.biases[j] = W.scales[i], W.biases[i]
+    Wt = synth.W4Matrix(q, W.scales, W.biases, W.n_out, W.k_in)
+    ref_l, ref_ids = oracle.head(Wt, xd, hw.norm_f, 1e-5)
+    got_l, got_ids = _run(env, Wt, hw.norm_f, x, False, batch)
+    _check(oracle, got_l, got_ids, ref_l)
+    for b, (i, j) in enumerate(pairs):
+        assert got_l[b, i] == got_l[b, j] and ref_ids[b] == i
+        assert got_ids[b] == i
+
+
+def test_head_nan_input_gives_minus_one(env):
+    nh, oracle, gu, torch = env
+    _say("head nan")
+    hw = synth.head_weights(seed=5, n_out=300)
+    x, xd = _x(6, 2, True)
+    x[1, 17] = np.nan
+    got_l, got_ids = _run(env, hw.lm_head, hw.norm_f, x, True, 2)
+    assert np.isnan(got_l[1]).all() and got_ids[1] == -1
+    ref_l, _ = oracle.head(hw.lm_head, xd[:1], hw.norm_f, 1e-5)
+    _check(oracle, got_l[:1], got_ids[:1], ref_l)
