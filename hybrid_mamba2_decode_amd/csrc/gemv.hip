@@ -420,6 +420,13 @@ static inline int inproj_grid(int n)
     return 8 * ((bx + wpg - 1) / wpg);
 }
 
+// Cache policy of the packed-weight loads of the K = 4480 kernels: non-temporal.  Each weight
+// byte is read once per call.  Measured over working sets well beyond the 256 MB last-level
+// cache (27 layers, 2.4 GB; four heads, 2.6 GB): in_proj 4% and the head 8% faster than with
+// the plain policy.  Over smaller rotations the gain looks larger (the cache then keeps part
+// of the rotation), which is not the per-position decode's case.
+constexpr int NT_LOAD = 2;  // the nt bit of the buffer instructions' cache-policy operand
+
 // Loads and row sums of R-row stages in the K = 4480 chunk layout above.  Rows past the
 // matrix are clamped to its last row (a branch would make the compiler's waits conservative).
 template <int R>
@@ -449,13 +456,13 @@ struct IpRows {
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 g.q[r][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                    rq, 16u * (li + 64 * i), row * IP_ROWB, 0));
+                    rq, 16u * (li + 64 * i), row * IP_ROWB, NT_LOAD));
                 g.s[r][i] = __builtin_amdgcn_raw_buffer_load_b16(rs, 2u * ((li + 64 * i) >> 1), row * IP_GRPB, 0);
                 g.b[r][i] = __builtin_amdgcn_raw_buffer_load_b16(rbias, 2u * ((li + 64 * i) >> 1), row * IP_GRPB, 0);
             }
         }
         const uint32_t trow = (uint32_t)min(n + rt, nmax);
-        g.qt = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, trow * IP_ROWB + toff, 0, 0));
+        g.qt = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, trow * IP_ROWB + toff, 0, NT_LOAD));
         g.st = __builtin_amdgcn_raw_buffer_load_b16(rs, trow * IP_GRPB + tsoff, 0, 0);
         g.bt = __builtin_amdgcn_raw_buffer_load_b16(rbias, trow * IP_GRPB + tsoff, 0, 0);
     }
