@@ -15,6 +15,8 @@ with gcc, wraps it with ctypes and adds these numpy-level pieces:
 * ``stack`` -- composition of blocks over the hybrid layer pattern.
 * ``head`` and ``greedy_ids`` -- the final norm, one 4-bit output head and the
   greedy id (smallest index of the largest logit, NaN never chosen).
+* ``fused_embedding`` -- the language model's input row: two 4-bit embedding rows
+  and the audio frame.
 
 Readings of the pages that the oracle fixes (no mixer equations are printed
 on the pages; see the header of nh_oracle.c):
@@ -200,6 +202,36 @@ def greedy_ids(logits) -> np.ndarray:
             best = l2[r][ok].max()
             ids[r] = int(np.flatnonzero(ok & (l2[r] == best))[0])
     return ids
+
+
+def fused_embedding(E, text_ids, function_ids, audio, function_weight: float = 2.0) -> np.ndarray:
+    """The language model's input row per position, in fp64.
+
+    The issue page "feat(nemotron_voicechat): ... offline duplex inference #1374", section
+    "Network 2": the input at a timeline position is the 4-bit embed_tokens row of the
+    previous text id, plus the projected audio frame, plus function_channel_weight (2.0 in
+    the config) times the embed_tokens row of the previous function id; the LLM then runs on
+    it with no lookup of its own.  E[id][k] = s q + b (the W4 affine map).
+    text_ids, function_ids: [m] ints; audio: [m][k_in] doubles.  An id outside 0..n_out-1
+    gives a row of NaN (a reading: the pages never feed such ids)."""
+    a = _d(audio).reshape(-1, E.k_in)
+    t = np.asarray(text_ids, dtype=np.int64).reshape(-1)
+    f = np.asarray(function_ids, dtype=np.int64).reshape(-1)
+    out = np.empty_like(a)
+    for r in range(a.shape[0]):
+        if not (0 <= t[r] < E.n_out and 0 <= f[r] < E.n_out):
+            out[r] = np.nan
+            continue
+        et = _w4_row(E, int(t[r]))
+        ef = _w4_row(E, int(f[r]))
+        out[r] = et + a[r] + function_weight * ef
+    return out
+
+
+def _w4_row(E, n: int) -> np.ndarray:
+    """Row n of dequant(E), through the oracle's W4 decode."""
+    sub = type(E)(E.qweight[n:n + 1], E.scales[n:n + 1], E.biases[n:n + 1], 1, E.k_in, E.group_size)
+    return w4_dequant(sub)[0]
 
 
 def head(W, x, norm_w, eps: float, mode: int = CONTRACT):

@@ -21,7 +21,9 @@ Distributions (the workload recipe, identical for every consumer):
   block input x ~ N(0, 1) (bf16); pre-filled conv state ~ N(0, 1) (bf16);
   pre-filled SSM state ~ N(0, 0.1^2) (float32);
   output heads (lm_head, function_head, 131072 x 4480 each, the vocab_size of the
-      same config): drawn like in_proj; norm_f ~ 1 + N(0, 0.05^2) (bf16).
+      same config) and the input embedding embed_tokens (same shape): drawn like in_proj;
+      norm_f ~ 1 + N(0, 0.05^2) (bf16); previous text / function ids ~ U{0..131071};
+      projected audio frame ~ N(0, 1) (float32).
 
 Random streams: numpy PCG64 seeded by SeedSequence([seed, layer, tensor_id])
 for weights and SeedSequence([seed, 1000 + stream, tensor_id]) for inputs (stream: a
@@ -54,6 +56,8 @@ _I_X, _I_CONV_STATE, _I_SSM_STATE = 0, 1, 2
 # pseudo-layer HEADS_LAYER with their own tensor ids.
 HEADS_LAYER = 100
 _T_NORM_F, _T_LMH_Q, _T_LMH_S, _T_FNH_Q, _T_FNH_S = 11, 12, 13, 14, 15
+_T_EMB_Q, _T_EMB_S = 16, 17
+_I_AUDIO, _I_IDS = 3, 4
 VOCAB = 131072
 
 
@@ -169,6 +173,19 @@ def head_weights(seed: int = 0, n_out: int = VOCAB, d: Dims = REAL) -> HeadWeigh
     lm = w4_random(seed, HEADS_LAYER, _T_LMH_Q, _T_LMH_S, n_out, d.hidden, d.group_size)
     fn = w4_random(seed, HEADS_LAYER, _T_FNH_Q, _T_FNH_S, n_out, d.hidden, d.group_size)
     return HeadWeights(norm_f, lm, fn)
+
+
+def embed_tokens(seed: int = 0, n_out: int = VOCAB, d: Dims = REAL) -> W4Matrix:
+    """The 4-bit input embedding [n_out][hidden], drawn like in_proj."""
+    return w4_random(seed, HEADS_LAYER, _T_EMB_Q, _T_EMB_S, n_out, d.hidden, d.group_size)
+
+
+def embed_inputs(stream: int, batch: int, n_out: int = VOCAB, seed: int = 0, d: Dims = REAL):
+    """Per position: previous text id and function id ~ U{0..n_out-1} (int32) and the projected
+    audio frame ~ N(0, 1) (float32, [batch][hidden])."""
+    ids = rng(seed, 1000 + stream, _I_IDS).integers(0, n_out, size=(2, batch)).astype(np.int32)
+    audio = rng(seed, 1000 + stream, _I_AUDIO).normal(0.0, 1.0, (batch, d.hidden)).astype(np.float32)
+    return ids[0], ids[1], audio
 
 
 def block_input(stream: int, batch: int, T: int, seed: int = 0, d: Dims = REAL) -> np.ndarray:

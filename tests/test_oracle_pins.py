@@ -205,6 +205,36 @@ def test_head_matches_library_pieces(oracle_lib):
     assert np.array_equal(ids, np.argmax(h @ Wd.T, axis=1))
 
 
+def test_fused_embedding_handpacked_closed_form(oracle_lib):
+    # row 0: every word 0x76543210 (q = k % 8), scale 0.25, bias -2 -> 0.25 (k % 8) - 2;
+    # row 1: every word 0xFEDCBA98 (q = 8 + k % 8), scale 0.5, bias 1 -> 0.5 (8 + k % 8) + 1
+    k = 128
+    qw = np.array([[0x76543210] * 16, [0xFEDCBA98] * 16], dtype=np.uint32)
+    s = synth.f32_to_bf16(np.array([[0.25, 0.25], [0.5, 0.5]], dtype=np.float32))
+    b = synth.f32_to_bf16(np.array([[-2.0, -2.0], [1.0, 1.0]], dtype=np.float32))
+    E = synth.W4Matrix(qw, s, b, 2, k)
+    kk = np.arange(k)
+    e0, e1 = 0.25 * (kk % 8) - 2.0, 0.5 * (8 + kk % 8) + 1.0
+    audio = np.stack([np.linspace(-1, 1, k), np.full(k, 0.5), np.zeros(k)])
+    got = oracle_lib.fused_embedding(E, [0, 1, 1], [1, 0, 1], audio, 2.0)
+    assert np.array_equal(got[0], e0 + audio[0] + 2 * e1)
+    assert np.array_equal(got[1], e1 + audio[1] + 2 * e0)
+    assert np.array_equal(got[2], 3 * e1)
+    assert np.array_equal(oracle_lib.fused_embedding(E, [1], [0], audio[:1], 0.0)[0], e1 + audio[0])
+
+
+def test_fused_embedding_independent_decode_and_bad_ids(oracle_lib):
+    rng = np.random.default_rng(13)
+    E = synth.w4_random(9, 3, 1, 2, 50, 4480)
+    _, Ed = _byte_split_dequant(E)
+    t, f = np.array([0, 49, 12, 7]), np.array([12, 0, 49, 7])
+    audio = rng.normal(size=(4, 4480))
+    got = oracle_lib.fused_embedding(E, t, f, audio)
+    assert np.allclose(got, Ed[t] + audio + 2.0 * Ed[f], rtol=0, atol=1e-15)
+    bad = oracle_lib.fused_embedding(E, [-1, 3, 50], [3, 50, 3], audio[:3])
+    assert np.isnan(bad).all()
+
+
 # ---------------------------------------------------------------- norms
 
 def test_rmsnorm_constant_vector_closed_form(oracle_lib):
