@@ -13,7 +13,8 @@ Also measured in the same run, each in its own object of the JSON line:
     position-layers per second against the matrix-core roofline (and the HBM one);
   * the 27-layer stack stepwise over T = 413 at batch 1, and the 27-layer full-history
     stack at batch 2, T = 3750, chunk 256;
-  * the final norm + both output heads (W4 131072 x 4480 each) + greedy ids at batch 1;
+  * the final norm + both output heads (W4 131072 x 4480 each) + greedy ids at batch 1,
+    and the fused input row (two W4 embedding rows + the audio frame);
   * the CPU oracle on the host cores (a bounded sample of the batch-1 block step), as a
     reported baseline.
 
@@ -349,6 +350,33 @@ def main():
         }
         log("heads:", out["heads"])
         del heads
+
+        # the fused input row at batch 1: two random rows of the W4 embedding table + audio
+        E = gu.w4_dev(synth.embed_tokens())
+        nemb = 1000
+        ids_t = [torch.tensor(synth.embed_inputs(100 + i, 1)[0], device="cuda") for i in range(16)]
+        ids_f = [torch.tensor(synth.embed_inputs(100 + i, 1)[1], device="cuda") for i in range(16)]
+        aud = gu.to_dev(synth.embed_inputs(99, 1)[2])
+        emb = gu.empty_f32(1, HID)
+
+        def embed(i):
+            nh.nh_fused_embedding(E, ids_t[i % 16], ids_f[i % 16], aud, nh.NH_F32, 2.0, 1, emb, stream)
+
+        for i in range(100):
+            embed(i)
+        hip.record(e0, stream)
+        for i in range(nemb):
+            embed(i)
+        hip.record(e1, stream)
+        torch.cuda.synchronize()
+        out["embedding"] = {
+            "workload": "fused input row E[text] + audio + 2 E[function] (W4 table 131072x4480), batch 1",
+            "us_per_position": round(hip.ms(e0, e1) * 1e3 / nemb, 3),
+            "bound": "latency (two 2.5 KB table rows, 36 KB in all)",
+            "timing": f"{nemb} back-to-back calls over 16 id pairs, two HIP events",
+        }
+        log("embedding:", out["embedding"])
+        del E
 
     # ------------------------- scan and 27-layer stack, batch 2, T=3750, chunk 256
     if not args.skip_seq:

@@ -37,7 +37,7 @@ EXPORTS = (
     "nh_w4_gemv", "nh_w4_gemm_workspace_bytes", "nh_w4_gemm", "nh_rmsnorm", "nh_inproj_conv_step",
     "nh_conv1d_step", "nh_conv1d_seq", "nh_ssm_step", "nh_ssd_scan_workspace_bytes", "nh_ssd_chunk_scan",
     "nh_rmsnorm_gated", "nh_block_workspace_bytes", "nh_mamba_block_step", "nh_mamba_block_seq",
-    "nh_mamba_stack", "nh_head_workspace_bytes", "nh_head_argmax",
+    "nh_mamba_stack", "nh_head_workspace_bytes", "nh_head_argmax", "nh_fused_embedding",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -97,6 +97,7 @@ _sigs = {
     "nh_profile_events": (_i, [_vp, _i]),
     "nh_head_workspace_bytes": (_sz, [_i]),
     "nh_head_argmax": (_i, [_vp, _vp, _i, _vp, C.c_float, _i, _vp, _vp, _vp, _sz, _vp]),
+    "nh_fused_embedding": (_i, [_vp, _vp, _vp, _vp, _i, C.c_float, _i, _vp, _vp]),
 }
 for _name, (_res, _args) in _sigs.items():
     _f = getattr(lib, _name)
@@ -171,6 +172,12 @@ def hybrid_pattern() -> str:
 def nh_w4_gemv(W, x, batch, residual, res_dtype, y, y_dtype, stream=None):
     _check(lib.nh_w4_gemv(C.byref(W), _ptr(x), batch, _ptr(residual), res_dtype, _ptr(y), y_dtype,
                           _stream(stream)))
+
+
+def nh_fused_embedding(E, text_ids, function_ids, audio, audio_dtype, function_weight, batch, out,
+                       stream=None):
+    _check(lib.nh_fused_embedding(C.byref(E), _ptr(text_ids), _ptr(function_ids), _ptr(audio), audio_dtype,
+                                  function_weight, batch, _ptr(out), _stream(stream)))
 
 
 def nh_head_workspace_bytes(batch) -> int:

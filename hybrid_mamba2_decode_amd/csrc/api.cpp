@@ -326,6 +326,24 @@ nh_status nh_w4_gemv(const nh_w4_matrix *W, const uint16_t *x, int batch, const 
     return ok();
 }
 
+nh_status nh_fused_embedding(const nh_w4_matrix *E, const int32_t *text_ids, const int32_t *function_ids,
+                             const void *audio, nh_dtype audio_dtype, float function_weight, int batch,
+                             float *out, void *stream)
+{
+    NH_TRY(check_w4(E, "E"));
+    NH_TRY(need_ptr(text_ids, "text_ids"));
+    NH_TRY(need_ptr(function_ids, "function_ids"));
+    NH_TRY(need_ptr(audio, "audio"));
+    NH_TRY(need_dtype(audio_dtype, "audio_dtype"));
+    NH_TRY(need_ptr(out, "out"));
+    if (!std::isfinite(function_weight)) return fail(NH_ERR_INVALID_ARGUMENT, "function_weight must be finite");
+    if (batch < 1 || batch > 4096) return fail(NH_ERR_UNSUPPORTED_SHAPE, "batch %d outside 1..4096", batch);
+    NH_HIP(launch_fused_embed(view(E), text_ids, function_ids, audio, audio_dtype, function_weight, batch, out,
+                              S(stream)),
+           "fused embedding");
+    return ok();
+}
+
 size_t nh_head_workspace_bytes(int batch)
 {
     if (batch < 1 || batch > 4) return 0;

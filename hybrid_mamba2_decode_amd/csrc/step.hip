@@ -176,4 +176,61 @@ hipError_t launch_conv_step(const uint16_t *xbc, long ld, uint16_t *state, const
     return hipGetLastError();
 }
 
+// ====================================================================== fused input row
+//
+// out[b] = E[text_ids[b]] + audio[b] + wf E[function_ids[b]], E the W4 embedding table.  One
+// thread per packed word (8 values) of a row: the two rows' words, their group scales and
+// biases, 8 audio values, and 32 bytes of fp32 output.  E rows are dequantised as
+// fmaf(s, q, b) (s q is exact; one rounding), then (e_t + a) and fmaf(wf, e_f, .) in that
+// order.  An id outside the table writes NaN and reads row 0 instead.
+template <int AT>
+__global__ __launch_bounds__(64) void k_fused_embed(W4 E, const int *__restrict__ tid,
+                                                    const int *__restrict__ fid,
+                                                    const void *__restrict__ audio, float wf,
+                                                    float *__restrict__ out)
+{
+    const int b = blockIdx.y, nw = E.k >> 3;
+    const int w = blockIdx.x * 64 + threadIdx.x;
+    if (w >= nw) return;
+    const int t = tid[b], f = fid[b];
+    const bool ok = t >= 0 && t < E.n && f >= 0 && f < E.n;
+    const size_t rt = ok ? (size_t)t : 0, rf = ok ? (size_t)f : 0;
+    const int kg = E.k >> 6;
+    const uint32_t qt = E.q[rt * nw + w], qf = E.q[rf * nw + w];
+    const float st = bf16_to_f32(E.s[rt * kg + (w >> 3)]), bt = bf16_to_f32(E.b[rt * kg + (w >> 3)]);
+    const float sf = bf16_to_f32(E.s[rf * kg + (w >> 3)]), bf = bf16_to_f32(E.b[rf * kg + (w >> 3)]);
+    float a[8];
+    if (AT == BF16) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(audio) + (size_t)b * E.k + 8 * w);
+        a[0] = bf16lo(v.x); a[1] = bf16hi(v.x); a[2] = bf16lo(v.y); a[3] = bf16hi(v.y);
+        a[4] = bf16lo(v.z); a[5] = bf16hi(v.z); a[6] = bf16lo(v.w); a[7] = bf16hi(v.w);
+    } else {
+        const float4 *src = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(audio) + (size_t)b * E.k + 8 * w);
+        const float4 v0 = src[0], v1 = src[1];
+        a[0] = v0.x; a[1] = v0.y; a[2] = v0.z; a[3] = v0.w;
+        a[4] = v1.x; a[5] = v1.y; a[6] = v1.z; a[7] = v1.w;
+    }
+    float o[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float et = fmaf(st, (float)((qt >> (4 * j)) & 15u), bt);
+        const float ef = fmaf(sf, (float)((qf >> (4 * j)) & 15u), bf);
+        o[j] = ok ? fmaf(wf, ef, et + a[j]) : __builtin_nanf("");
+    }
+    float4 *dst = reinterpret_cast<float4 *>(out + (size_t)b * E.k + 8 * w);
+    dst[0] = make_float4(o[0], o[1], o[2], o[3]);
+    dst[1] = make_float4(o[4], o[5], o[6], o[7]);
+}
+
+hipError_t launch_fused_embed(const W4 &E, const int *text_ids, const int *function_ids, const void *audio,
+                              int audio_t, float wf, int batch, float *out, hipStream_t st)
+{
+    dim3 grid(((E.k >> 3) + 63) / 64, batch), block(64);
+    if (audio_t == BF16)
+        k_fused_embed<BF16><<<grid, block, 0, st>>>(E, text_ids, function_ids, audio, wf, out);
+    else
+        k_fused_embed<F32><<<grid, block, 0, st>>>(E, text_ids, function_ids, audio, wf, out);
+    return hipGetLastError();
+}
+
 }  // namespace nh

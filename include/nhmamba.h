@@ -218,6 +218,24 @@ nh_status nh_rmsnorm_gated(const uint16_t *y, const uint16_t *z, long ld_z, cons
 
 /* ----------------------------------------------------------- model top */
 
+/* The language model's input row for `batch` positions (issue page, section
+ * "Network 2": embed_tokens row of the previous text id, plus the projected
+ * audio frame, plus function_channel_weight (2.0 in the config) times the
+ * embed_tokens row of the previous function id):
+ *   out[b] = E[text_ids[b]] + audio[b] + function_weight * E[function_ids[b]]
+ * with E rows dequantised to fp32 (E[n][k] = s q + b, one rounding) and the
+ * sums taken in fp32 in that order.  E: any W4 matrix (k_in = the hidden
+ * size for the model); text_ids, function_ids: int32 [batch] device arrays;
+ * audio: [batch][k_in] of audio_dtype; out: f32 [batch][k_in].  An id
+ * outside 0 .. n_out-1 gives a row of NaN (no out-of-table read).
+ * batch 1 .. 4096; every pointer 16-byte aligned; function_weight finite.
+ * Errors before any launch: NH_ERR_UNSUPPORTED_SHAPE, NH_ERR_MISALIGNED,
+ * NH_ERR_INVALID_ARGUMENT. */
+nh_status nh_fused_embedding(const nh_w4_matrix *E, const int32_t *text_ids,
+                             const int32_t *function_ids, const void *audio,
+                             nh_dtype audio_dtype, float function_weight, int batch,
+                             float *out, void *stream);
+
 /* Final norm, one output head and the greedy id for `batch` positions
  * (issue page, section "Network 2": after the last layer the hidden state
  * goes through norm_f, then through lm_head and function_head, both 4-bit

@@ -96,6 +96,24 @@ def test_head_rejects_bad_arguments(nh):
     assert call(eps=0.0) == nh.NH_ERR_INVALID_ARGUMENT
 
 
+def test_fused_embedding_rejects_bad_arguments(nh):
+    A = 0x20000
+    E = _fake_w4(n=131072, k=4480)
+
+    def call(**kw):
+        a = dict(E=E, t=A, f=A, audio=A, at=0, w=2.0, batch=1, out=A)
+        a.update(kw)
+        return _status(lambda: nh.nh_fused_embedding(a["E"], a["t"], a["f"], a["audio"], a["at"], a["w"],
+                                                     a["batch"], a["out"], 0))
+    assert call(batch=0) == nh.NH_ERR_UNSUPPORTED_SHAPE
+    assert call(batch=4097) == nh.NH_ERR_UNSUPPORTED_SHAPE
+    assert call(t=None) == nh.NH_ERR_INVALID_ARGUMENT
+    assert call(f=A + 4) == nh.NH_ERR_MISALIGNED
+    assert call(at=2) == nh.NH_ERR_INVALID_ARGUMENT
+    assert call(w=float("nan")) == nh.NH_ERR_INVALID_ARGUMENT
+    assert call(E=_fake_w4(gs=32)) == nh.NH_ERR_UNSUPPORTED_SHAPE
+
+
 def test_gemm_workspace_check(nh):
     A = 0x20000
     need = nh.nh_w4_gemm_workspace_bytes(100, 128)

@@ -1,5 +1,9 @@
-"""GPU parity of the final norm + one W4 output head + greedy id (nh_head_argmax) against
-the CPU oracle, through the C ABI.
+"""GPU parity of the model top against the CPU oracle, through the C ABI: the fused input
+row (nh_fused_embedding) and the final norm + one W4 output head + greedy id
+(nh_head_argmax).
+
+Fused input row: E rows dequantised with one fp32 rounding and two fp32 additions against the
+oracle's exact fp64, so |gpu - oracle| <= 2^-21 (|E[t]| + |audio| + |w E[f]|) elementwise.
 
 Logits: the kernel's fp32 sums of exact products against the oracle's fp64 sums over the
 same bf16 normalised input h, apart from rare one-unit bf16 flips of h where the fp32 norm
@@ -131,3 +135,68 @@ def test_head_nan_input_gives_minus_one(env):
     assert np.isnan(got_l[1]).all() and got_ids[1] == -1
     ref_l, _ = oracle.head(hw.lm_head, xd[:1], hw.norm_f, 1e-5)
     _check(oracle, got_l[:1], got_ids[:1], ref_l)
+
+
+# ------------------------------------------------------------ fused input row
+
+def _embed_run(env, E, t, f, audio, f32, w=2.0):
+    nh, oracle, gu, torch = env
+    batch = len(t)
+    out = gu.empty_f32(batch, E.k_in)
+    td = torch.tensor(np.asarray(t, dtype=np.int32), device=gu.DEV)
+    fd = torch.tensor(np.asarray(f, dtype=np.int32), device=gu.DEV)
+    a = audio if f32 else synth.f32_to_bf16(audio)
+    nh.nh_fused_embedding(gu.w4_dev(E), td, fd, gu.to_dev(a), nh.NH_F32 if f32 else nh.NH_BF16, w, batch, out)
+    torch.cuda.synchronize()
+    ad = audio.astype(np.float64) if f32 else synth.bf16_to_f32(a).astype(np.float64)
+    return out.cpu().numpy().astype(np.float64), ad
+
+
+def _embed_check(oracle, E, t, f, ad, got, w=2.0):
+    ref = oracle.fused_embedding(E, t, f, ad, w)
+    z = np.zeros_like(ad)
+    ok = [(0 <= a < E.n_out) and (0 <= b < E.n_out) for a, b in zip(t, f)]
+    for r, good in enumerate(ok):
+        if not good:
+            assert np.isnan(got[r]).all()
+            continue
+        et = oracle.fused_embedding(E, [t[r]], [t[r]], z[r:r + 1], 0.0)[0]
+        ef = oracle.fused_embedding(E, [f[r]], [f[r]], z[r:r + 1], 0.0)[0]
+        bound = 2.0 ** -21 * (np.abs(et) + np.abs(ad[r]) + abs(w) * np.abs(ef)) + 1e-30
+        assert np.all(np.abs(got[r] - ref[r]) <= bound), np.abs(got[r] - ref[r]).max()
+
+
+@pytest.mark.parametrize("batch", [1, 3, 5])
+@pytest.mark.parametrize("f32", [False, True])
+def test_fused_embedding_small(env, batch, f32):
+    # the first and last rows of the table, repeated ids, both audio dtypes
+    nh, oracle, gu, torch = env
+    _say("fused embedding", batch, f32)
+    E = synth.embed_tokens(seed=2, n_out=1000)
+    t = np.array([0, 999, 12, 500, 12][:batch])
+    f = np.array([999, 0, 12, 7, 3][:batch])
+    audio = synth.rng(3, 3000 + batch, 0).normal(0.0, 1.0, (batch, 4480)).astype(np.float32)
+    got, ad = _embed_run(env, E, t, f, audio, f32)
+    _embed_check(oracle, E, t, f, ad, got)
+
+
+def test_fused_embedding_bad_ids_and_weight(env):
+    nh, oracle, gu, torch = env
+    _say("fused embedding bad ids")
+    E = synth.embed_tokens(seed=2, n_out=1000)
+    t = np.array([-1, 5, 1000, 6])
+    f = np.array([3, 1000, 3, 6])
+    audio = synth.rng(3, 3100, 0).normal(0.0, 1.0, (4, 4480)).astype(np.float32)
+    got, ad = _embed_run(env, E, t, f, audio, True, w=-0.5)
+    _embed_check(oracle, E, t, f, ad, got, w=-0.5)
+    assert not np.isnan(got[3]).any()
+
+
+def test_fused_embedding_full_table(env):
+    # the model's table (131072 x 4480), two positions drawn like the benchmark's
+    nh, oracle, gu, torch = env
+    _say("fused embedding full table")
+    E = synth.embed_tokens()
+    t, f, audio = synth.embed_inputs(5, 2)
+    got, ad = _embed_run(env, E, t, f, audio, True)
+    _embed_check(oracle, E, t, f, ad, got)
