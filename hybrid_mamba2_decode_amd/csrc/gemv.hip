@@ -653,6 +653,150 @@ __device__ __forceinline__ void act_hidden(ActChunk (&am)[NB][2], ActChunk (&at)
     }
 }
 
+// ---------------------------------------------- batched rows on the matrix cores
+//
+// For 2 to 4 batch rows the dot products go to v_mfma_f32_4x4x4_16b_f16, which runs 16
+// independent 4x4x4 products: for block b (lanes 4b .. 4b+3) lane 4b+i supplies row i of A
+// (4 values of K), lane 4b+j column j of B, and lane 4b+j receives column j of D (register v
+// holding row v).  Here block b is a K-range -- chunks b, b + 16, ... (32 K each; 140 per row,
+// so blocks 12-15 have 8 and the rest 9) -- A's rows are the batch rows (lane 4b+i holds batch
+// row i's activations, zero for i >= NB) and B's columns are 4 weight rows (lane 4b+j holds
+// row j's packed words).  A stage is thus 4 rows, and the dequantisation (one shift and four
+// v_and_or per word) is shared by all batch rows instead of repeated per row.
+//
+// Per chunk: D gathers the even nibbles (1024 + q) and D' the odd ones (1024 + 16 q) as in
+// chunk_dot, and acc += s (D + D'/16).  The activation constants of the magic offset and of
+// the bias are per (chunk, batch row) and live in the A lanes, so they enter through two
+// v_mfma_f32_4x4x1_16b_f32: E += sum_x b and E += (-off) s.  After the 9 chunks the 16
+// blocks' partials are summed across lanes (DPP row rotations, then two shuffles).
+constexpr int MF_CH = 9;    // chunks per lane and row
+constexpr int MF_WGS = 256;  // work-groups of the batched in_proj: one per CU, 32 per XCD
+
+struct MfStage {
+    uint4 q[MF_CH];
+    uint16_t s[MF_CH], b[MF_CH];
+    EpiPre pe;
+};
+
+typedef _Float16 h4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ h4v h4_of(uint32_t lo, uint32_t hi)
+{
+    return __builtin_bit_cast(h4v, make_uint2(lo, hi));
+}
+
+template <int NB, int XT>
+__global__ __launch_bounds__(256, 1) void k_inproj_step_mf(W4 W, const void *__restrict__ x,
+                                                          const uint16_t *__restrict__ nw, float eps,
+                                                          EpiInProjStep epi, uint32_t *zero_ptr, int nzero)
+{
+    constexpr int NT = 256, NW = NT / 64, NCH = HIDDEN / 32;
+    extern __shared__ __attribute__((aligned(16))) uint32_t act_lds[];
+    __shared__ float red[NB][NW];
+    if (blockIdx.x == 0 && (int)threadIdx.x < nzero) zero_ptr[threadIdx.x] = 0u;
+    PreNorm<NB, XT, NT> pn;
+    pn.issue(x, nw);
+    __builtin_amdgcn_sched_barrier(0);
+
+    const int lane = threadIdx.x & 63, kb = lane >> 2, q4 = lane & 3;
+    const int nmax = W.n - 1;
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void *)W.q, 0, (int)((uint32_t)W.n * IP_ROWB), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)W.s, 0, (int)((uint32_t)W.n * IP_GRPB), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rbi = __builtin_amdgcn_make_buffer_rsrc((void *)W.b, 0, (int)((uint32_t)W.n * IP_GRPB), 0x00020000);
+    // this wave's 4-row stages [s0, s1): an even split per XCD, then per wave inside the XCD
+    const int nst = (W.n + 3) / 4;
+    const int xcd = blockIdx.x & 7, nwx = (int)(gridDim.x >> 3) * NW;
+    const int wx = __builtin_amdgcn_readfirstlane((int)((blockIdx.x >> 3) * NW + (threadIdx.x >> 6)));
+    const int xs = (int)((long)nst * xcd / 8), xn = (int)((long)nst * (xcd + 1) / 8) - xs;
+    const int s0 = xs + (int)((long)xn * wx / nwx), s1 = xs + (int)((long)xn * (wx + 1) / nwx);
+    // lanes 0-15 finish (row 4 s + (lane & 3), batch lane >> 2) of each stage
+    const int eb = min(lane >> 2, NB - 1);
+    // the row differs between the four lanes of a block, so the whole offset goes in the
+    // per-lane operand (a per-lane scalar offset would become a loop over its values)
+    auto load = [&](MfStage &g, int st) {
+        const uint32_t row = (uint32_t)min(4 * st + q4, nmax);
+#pragma unroll
+        for (int t = 0; t < MF_CH; ++t) {
+            const uint32_t c = (uint32_t)min(kb + 16 * t, NCH - 1);
+            g.q[t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, row * IP_ROWB + 16u * c, 0, NT_LOAD));
+            g.s[t] = __builtin_amdgcn_raw_buffer_load_b16(rs, row * IP_GRPB + 2u * (c >> 1), 0, 0);
+            g.b[t] = __builtin_amdgcn_raw_buffer_load_b16(rbi, row * IP_GRPB + 2u * (c >> 1), 0, 0);
+        }
+        g.pe = epi.prefetch(min(4 * st + q4, nmax), eb);
+    };
+    // the first stage is issued after the pre-norm: issued before it, its registers overlap
+    // the pre-norm's NB x 32 widened values and the allocation spills at batch 4
+    pn.finish(eps, act_lds, red);
+    MfStage A, B;
+    load(A, min(s0, nst - 1));
+    // activations: batch row q4 (zero beyond NB), chunks kb + 16 t (zero beyond the row);
+    // the offset constant is kept negated for the f32 products
+    ActChunk a[MF_CH];
+#pragma unroll
+    for (int t = 0; t < MF_CH; ++t) {
+        const int c = kb + 16 * t;
+        if (q4 < NB && c < NCH) {
+            chunk_from_lds(a[t], act_lds + ((size_t)q4 * NCH + c) * ACT_WORDS);
+            a[t].off = -a[t].off;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) a[t].p[j] = 0u;
+            a[t].off = 0.f;
+            a[t].sum = 0.f;
+        }
+    }
+    auto step = [&](const MfStage &g, int st) {
+        const uint32_t mlo = 0x000F000Fu, mhi = 0x00F000F0u, magic = 0x64006400u;
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f}, E = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < MF_CH; ++t) {
+            floatx4 D = {0.f, 0.f, 0.f, 0.f}, D2 = {0.f, 0.f, 0.f, 0.f};
+            const uint32_t wq[4] = {g.q[t].x, g.q[t].y, g.q[t].z, g.q[t].w};
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t wd = wq[w], wh = wd >> 8;
+                const uint32_t d0 = and_or(wd, mlo, magic), d1 = and_or(wd, mhi, magic);
+                const uint32_t d2 = and_or(wh, mlo, magic), d3 = and_or(wh, mhi, magic);
+                D = __builtin_amdgcn_mfma_f32_4x4x4f16(h4_of(a[t].p[4 * w], a[t].p[4 * w + 2]), h4_of(d0, d2), D, 0, 0, 0);
+                D2 = __builtin_amdgcn_mfma_f32_4x4x4f16(h4_of(a[t].p[4 * w + 1], a[t].p[4 * w + 3]), h4_of(d1, d3), D2, 0, 0, 0);
+            }
+            const float sc = __uint_as_float((uint32_t)g.s[t] << 16), bi = __uint_as_float((uint32_t)g.b[t] << 16);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[v] = fmaf(sc, fmaf(D2[v], 0.0625f, D[v]), acc[v]);
+            E = __builtin_amdgcn_mfma_f32_4x4x1f32(a[t].sum, bi, E, 0, 0, 0);
+            E = __builtin_amdgcn_mfma_f32_4x4x1f32(a[t].off, sc, E, 0, 0, 0);
+        }
+        float tot[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            float u = acc[v] + E[v];
+            u += dpp_mov<0x124>(u);  // row_ror:4
+            u += dpp_mov<0x128>(u);  // row_ror:8
+            u += __shfl_xor(u, 16, 64);
+            u += __shfl_xor(u, 32, 64);
+            tot[v] = u;
+        }
+        const int bsel = lane >> 2;
+        const float mine = bsel == 0 ? tot[0] : bsel == 1 ? tot[1] : bsel == 2 ? tot[2] : tot[3];
+        const int row = 4 * st + q4;
+        if (lane < 4 * NB && row <= nmax) epi(row, bsel, mine, g.pe);
+    };
+    // two stages per iteration with no conditional load: loads past the wave's last stage
+    // re-read that stage (the cache holds it), and only the second compute is conditional
+    if (s1 > s0) {
+        const int last = s1 - 1;
+        for (int st = s0; st < s1; st += 2) {
+            load(B, min(st + 1, last));
+            __builtin_amdgcn_sched_barrier(0);
+            step(A, st);
+            load(A, min(st + 2, last));
+            __builtin_amdgcn_sched_barrier(0);
+            if (st + 1 < s1) step(B, st + 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
 // ------------------------------------------------------------------ kernels
 
 template <int LPR, int CPL, int NB, int RG>
@@ -1031,13 +1175,22 @@ hipError_t launch_inproj_step(const W4 &W, const void *x, int x_t, const uint16_
         else                                                                                               \
             launch_k(k_inproj_step<NB, F32>, dim3(grid), blk, lds, st, W, x, norm_w, eps, e, zero_ptr, nzero);  \
     }
+#define NH_LAUNCH_MF(NB)                                                                                   \
+    {                                                                                                      \
+        if (x_t == BF16)                                                                                   \
+            launch_k(k_inproj_step_mf<NB, BF16>, dim3(MF_WGS), dim3(256), lds, st, W, x, norm_w, eps, e, zero_ptr, nzero); \
+        else                                                                                               \
+            launch_k(k_inproj_step_mf<NB, F32>, dim3(MF_WGS), dim3(256), lds, st, W, x, norm_w, eps, e, zero_ptr, nzero);  \
+    }
+    // the matrix-core kernel from batch 3 on (at batch 2 the per-row kernel is 1 us faster)
     switch (batch) {
     case 1: NH_LAUNCH(1); break;
     case 2: NH_LAUNCH(2); break;
-    case 3: NH_LAUNCH(3); break;
-    default: NH_LAUNCH(4); break;
+    case 3: NH_LAUNCH_MF(3); break;
+    default: NH_LAUNCH_MF(4); break;
     }
 #undef NH_LAUNCH
+#undef NH_LAUNCH_MF
     return hipGetLastError();
 }
 

@@ -65,7 +65,7 @@ def test_block_step_prefilled_b1(env):
     assert gu.rel_l2(cs_got, ref.conv_state) < 4e-3                     # new row: bf16 in_proj output
 
 
-@pytest.mark.parametrize("B", [1, 2])
+@pytest.mark.parametrize("B", [1, 2, 3, 4])
 def test_inproj_conv_step_matches_oracle(env, B):
     """The fused front of the step (pre-norm, in_proj, split, conv step + SiLU) against the
     oracle's storage points of the same step (z and dt_raw from zxbcdt, xc after the conv)."""
@@ -83,6 +83,9 @@ def test_inproj_conv_step_matches_oracle(env, B):
                             ("xc", xc, ref.debug["xc"][:, 0])]:
         g = gu.bf16_bits_to_f64(gu.from_dev_u16(got))
         r = gu.rel_l2(g, want)
+        for b in range(B):
+            print(f"[inproj step b{B}] {name} row {b}: rel-L2 {gu.rel_l2(g[b], want[b]):.3e} "
+                  f"non-finite {int((~np.isfinite(g[b])).sum())}", flush=True)
         print(f"[inproj step b{B}] {name} rel-L2 {r:.3e} flips {gu.bf16_ulp_flips(gu.from_dev_u16(got), want)}",
               flush=True)
         assert r < 4e-3, (name, r)
