@@ -13,6 +13,7 @@ Also measured in the same run, each in its own object of the JSON line:
     position-layers per second against the matrix-core roofline (and the HBM one);
   * the 27-layer stack stepwise over T = 413 at batch 1, and the 27-layer full-history
     stack at batch 2, T = 3750, chunk 256;
+  * the block step with 4 sessions sharing one weight stream;
   * the final norm + both output heads (W4 131072 x 4480 each) + greedy ids at batch 1,
     and the fused input row (two W4 embedding rows + the audio frame);
   * the CPU oracle on the host cores (a bounded sample of the batch-1 block step), as a
@@ -286,6 +287,37 @@ def main():
         "timing": f"{args.steps} back-to-back launches over {args.copies} rotating weight/state copies, "
                   "two HIP events on the launch stream",
     }
+
+    # --------------- batched step: 4 sessions share one weight stream (27 rotating copies)
+    B4s = 4
+    x4s = gu.to_dev(synth.block_input(1, B4s, 1)[:, 0])
+    cs4, ss4 = synth.prefilled_state(1, B4s)
+    st4 = [gu.state_dev(cs4, ss4) for _ in range(args.copies)]
+    ws4s = gu.workspace(nh.nh_block_workspace_bytes(d128, B4s, 1, nh.NH_MODE_STEP))
+    o4s = gu.empty_f32(B4s, HID)
+
+    def step4(i):
+        nh.nh_mamba_block_step(d128, dev_layers[i], st4[i][0], x4s, nh.NH_BF16, o4s, nh.NH_F32, B4s, ws4s,
+                               ws4s.numel(), stream)
+
+    for i in range(args.warmup):
+        step4(i % args.copies)
+    nb4 = max(args.steps // 4, 50)
+    hip.record(e0, stream)
+    for i in range(nb4):
+        step4(i % args.copies)
+    hip.record(e1, stream)
+    torch.cuda.synchronize()
+    us4 = hip.ms(e0, e1) * 1e3 / nb4
+    b4 = sum(step_kernel_bytes(B4s))
+    out["step_batch4"] = {
+        "workload": f"one Mamba2 block, {B4s} independent sessions per step (pre-filled states), "
+                    f"{args.copies} rotating weight/state copies",
+        "us_per_layer_step": round(us4, 3), "us_per_session_layer": round(us4 / B4s, 3),
+        "algorithmic_bytes": int(b4), "hbm_frac": round(b4 / (us4 * 1e-6) / HBM_PEAK, 4),
+    }
+    log("batch-4 step:", out["step_batch4"])
+    del st4, ws4s
 
     # ------------------------------- 27-layer stack, batch 1, stepwise over T=413
     if not args.skip_stack:
