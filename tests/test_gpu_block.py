@@ -65,17 +65,19 @@ def test_block_step_prefilled_b1(env):
     assert gu.rel_l2(cs_got, ref.conv_state) < 4e-3                     # new row: bf16 in_proj output
 
 
-@pytest.mark.parametrize("B", [1, 2, 3, 4])
-def test_inproj_conv_step_matches_oracle(env, B):
+@pytest.mark.parametrize("B,xf32", [(1, False), (2, False), (3, False), (4, False), (1, True), (4, True)])
+def test_inproj_conv_step_matches_oracle(env, B, xf32):
     """The fused front of the step (pre-norm, in_proj, split, conv step + SiLU) against the
-    oracle's storage points of the same step (z and dt_raw from zxbcdt, xc after the conv)."""
+    oracle's storage points of the same step (z and dt_raw from zxbcdt, xc after the conv).
+    Batch 3 and 4 run the matrix-core kernel; an fp32 input is the residual stream of a stack."""
     nh, oracle, gu, torch, lw, W = env
-    _say("in_proj + conv step, batch", B)
+    _say("in_proj + conv step, batch", B, "fp32 x" if xf32 else "bf16 x")
     x = synth.block_input(11, B, 1)
     cs0, ss0 = synth.prefilled_state(11, B)
     st, csd, ssd = gu.state_dev(cs0, ss0)
     z, xc, dtr = gu.empty_u16(B, 10240), gu.empty_u16(B, synth.CONV_DIM), gu.empty_u16(B, 128)
-    nh.nh_inproj_conv_step(nh.dims(), W, st, gu.to_dev(x[:, 0]), nh.NH_BF16, z, xc, dtr, B)
+    xin = gu.to_dev(gu.bf16_bits_to_f64(x[:, 0]).astype(np.float32)) if xf32 else gu.to_dev(x[:, 0])
+    nh.nh_inproj_conv_step(nh.dims(), W, st, xin, nh.NH_F32 if xf32 else nh.NH_BF16, z, xc, dtr, B)
     ref = oracle.block(synth.REAL, lw, gu.bf16_bits_to_f64(x), gu.bf16_bits_to_f64(cs0), ss0,
                        mode=oracle.CONTRACT, stepwise=True, debug=True)
     zx = ref.debug["zxbcdt"][:, 0]
