@@ -231,10 +231,10 @@ nh_status block_step(const nh_mamba_dims *d, const nh_mamba_weights *w, nh_mamba
            "in_proj step");
     prof_arm(1);
     NH_HIP(launch_ssm_step_part(k.xc, k.dtr, NHEADS, w->dt_bias, w->A_log, w->D, st->ssm_state, k.gate, k.z,
-                                k.part, B, s),
+                                w->gnorm_w, k.part, B, s),
            "ssm step");
     prof_arm(2);
-    NH_HIP(launch_outproj_step(view(&w->out_proj), k.gate, w->gnorm_w, k.part, d->eps, B, x, x_t, out, out_t, s),
+    NH_HIP(launch_outproj_step(view(&w->out_proj), k.gate, k.part, d->eps, B, x, x_t, out, out_t, s),
            "out_proj step");
     prof_next() = ProfEvents{};
     return ok();
@@ -258,7 +258,7 @@ nh_status block_seq(const nh_mamba_dims *d, const nh_mamba_weights *w, const nh_
     }
     NH_HIP(launch_conv_seq(k.zx + DINNER, NIN, T, cs_in, cs_out, w->conv_w, w->conv_b, k.xc, B, CONVDIM, s),
            "conv");
-    // the scan's C.B^T tiles (at most 4 KiB per position) reuse the normalised input, which
+    // the scan's C.B^T tiles (at most 8 KiB per position) reuse the normalised input, which
     // in_proj has consumed
     if (ssd_scan_ws_bytes(B, T, d->chunk) > (size_t)M * HIDDEN * sizeof(uint16_t))
         return fail(NH_ERR_INVALID_ARGUMENT, "internal: scan tiles exceed their workspace region");

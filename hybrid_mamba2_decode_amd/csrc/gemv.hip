@@ -846,41 +846,34 @@ __global__ __launch_bounds__(InProjShape<NB>::NT, 1) void k_inproj_step(W4 W, co
 }
 
 // Fused gated RMSNorm + out_proj + residual for the per-position block.  The work-group forms
-// o = bf16(RMSNorm_group(g) * w) straight into the LDS activation format from the gate product
-// g = bf16(y) * silu(z) and the per-(head, half) sums of squares, both left by the SSM step,
-// while the first stage of out_proj weights is already in flight; o never goes to memory.
+// o = bf16((g w) / rms_group(g)) straight into the LDS activation format from g w (the gate
+// product g = bf16(y) * silu(z) times the norm weight) and the per-(head, half) sums of squares
+// of g, both left by the SSM step, while the first stage of out_proj weights is already in
+// flight; o never goes to memory.
 template <int NB>
 __global__ __launch_bounds__(NB == 1 ? 512 : 256, 1) void k_outproj_step(W4 W, const float *__restrict__ gate,
-                                                         const uint16_t *__restrict__ gw,
                                                          const float *__restrict__ part, float eps,
                                                          EpiStore epi)
 {
     constexpr int LPR = 64, NCH = DINNER / 32, CPL = NCH / LPR, RG = 1, NT = NB == 1 ? 512 : 256;
     extern __shared__ __attribute__((aligned(16))) uint32_t act_lds[];
     __shared__ float rstd[NB][NGROUPS];
-    auto load = [&](int it, float4 *gv, uint4 *wv) {
+    auto load = [&](int it, float4 *gv) {
         const int b = it / NCH, c = it % NCH;
         const float4 *gp = reinterpret_cast<const float4 *>(gate + (size_t)b * DINNER + 32 * c);
-        const uint4 *wp = reinterpret_cast<const uint4 *>(gw + 32 * c);
 #pragma unroll
         for (int j = 0; j < 8; ++j) gv[j] = gp[j];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) wv[j] = wp[j];
     };
-    auto build = [&](int it, const float4 *gv, const uint4 *wv) {
+    auto build = [&](int it, const float4 *gv) {
         const int b = it / NCH, c = it % NCH;
         const float r = rstd[b][(32 * c) / GNORM];
         float v[32];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t wa[4] = {wv[j].x, wv[j].y, wv[j].z, wv[j].w};
-            const float ga[8] = {gv[2 * j].x, gv[2 * j].y, gv[2 * j].z, gv[2 * j].w,
-                                 gv[2 * j + 1].x, gv[2 * j + 1].y, gv[2 * j + 1].z, gv[2 * j + 1].w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                v[8 * j + 2 * e] = round_bf16(ga[2 * e] * r * bf16lo(wa[e]));
-                v[8 * j + 2 * e + 1] = round_bf16(ga[2 * e + 1] * r * bf16hi(wa[e]));
-            }
+        for (int j = 0; j < 8; ++j) {
+            v[4 * j] = round_bf16(gv[j].x * r);
+            v[4 * j + 1] = round_bf16(gv[j].y * r);
+            v[4 * j + 2] = round_bf16(gv[j].z * r);
+            v[4 * j + 3] = round_bf16(gv[j].w * r);
         }
         make_chunk(v, act_lds + (size_t)it * ACT_WORDS);
     };
@@ -888,35 +881,33 @@ __global__ __launch_bounds__(NB == 1 ? 512 : 256, 1) void k_outproj_step(W4 W, c
     // has them (after the first barrier; issued together, they would queue behind every wave's
     // weight loads): one per-(head, half) sum of squares per thread, 32 of which make a group,
     // and, with at most one chunk per thread (batch 1: 320 chunks, 512 threads), the chunk's
-    // gate and norm-weight values.
+    // g w values.
     constexpr bool ONE = NB * NCH <= NT;
     constexpr int NPART = NHEADS * 2;  // per batch row
     float4 gv0[8];
-    uint4 wv0[4];
     float pv[(NB * NPART + NT - 1) / NT];
 #pragma unroll
     for (int i = 0; i < (NB * NPART + NT - 1) / NT; ++i) {
         const int t = threadIdx.x + NT * i;
         pv[i] = t < NB * NPART ? part[t] : 0.f;
     }
-    if (ONE && (int)threadIdx.x < NB * NCH) load(threadIdx.x, gv0, wv0);
+    if (ONE && (int)threadIdx.x < NB * NCH) load(threadIdx.x, gv0);
 #pragma unroll
     for (int i = 0; i < (NB * NPART + NT - 1) / NT; ++i) {
         const int t = threadIdx.x + NT * i;  // 32 consecutive entries = one group of one row
         const float tot = row_sum<32>(pv[i]);
         if (t < NB * NPART && (t & 31) == 0) rstd[t / NPART][(t % NPART) / 32] = 1.0f / sqrtf(tot / (float)GNORM + eps);
     }
-    __builtin_amdgcn_s_waitcnt(0);  // the gate and norm-weight loads too
+    __builtin_amdgcn_s_waitcnt(0);  // the g w loads too
     __syncthreads();
     GemvRunner<LPR, CPL, NB, RG, EpiStore> run(W, epi, NT);
     if (ONE) {
-        if ((int)threadIdx.x < NB * NCH) build(threadIdx.x, gv0, wv0);
+        if ((int)threadIdx.x < NB * NCH) build(threadIdx.x, gv0);
     } else {
         for (int it = threadIdx.x; it < NB * NCH; it += NT) {
             float4 gv[8];
-            uint4 wv[4];
-            load(it, gv, wv);
-            build(it, gv, wv);
+            load(it, gv);
+            build(it, gv);
         }
     }
     __syncthreads();
@@ -1141,7 +1132,7 @@ hipError_t launch_gemv(const W4 &W, const uint16_t *x, int batch, const void *re
     }
 }
 
-hipError_t launch_outproj_step(const W4 &W, const float *gate, const uint16_t *gw, const float *part,
+hipError_t launch_outproj_step(const W4 &W, const float *gate, const float *part,
                                float eps, int batch, const void *res, int res_t, void *out, int out_t,
                                hipStream_t st)
 {
@@ -1150,10 +1141,10 @@ hipError_t launch_outproj_step(const W4 &W, const float *gate, const uint16_t *g
     // one work-group per CU: 8 waves at batch 1; 4 waves (more registers each) above
     const int grid = min(cu_count(), (W.n + 7) / 8);
     switch (batch) {
-    case 1: launch_k(k_outproj_step<1>, dim3(grid), dim3(512), lds, st, W, gate, gw, part, eps, e); break;
-    case 2: launch_k(k_outproj_step<2>, dim3(grid), dim3(256), lds, st, W, gate, gw, part, eps, e); break;
-    case 3: launch_k(k_outproj_step<3>, dim3(grid), dim3(256), lds, st, W, gate, gw, part, eps, e); break;
-    default: launch_k(k_outproj_step<4>, dim3(grid), dim3(256), lds, st, W, gate, gw, part, eps, e); break;
+    case 1: launch_k(k_outproj_step<1>, dim3(grid), dim3(512), lds, st, W, gate, part, eps, e); break;
+    case 2: launch_k(k_outproj_step<2>, dim3(grid), dim3(256), lds, st, W, gate, part, eps, e); break;
+    case 3: launch_k(k_outproj_step<3>, dim3(grid), dim3(256), lds, st, W, gate, part, eps, e); break;
+    default: launch_k(k_outproj_step<4>, dim3(grid), dim3(256), lds, st, W, gate, part, eps, e); break;
     }
     return hipGetLastError();
 }

@@ -61,14 +61,15 @@ hipError_t launch_head(const W4 &W, const void *x, int x_t, const uint16_t *norm
 hipError_t launch_ssm_step(const uint16_t *xc, const uint16_t *dtr, long ld_dt,
                            const float *dt_bias, const float *A_log, const float *D, float *S,
                            void *y, int y_t, int batch, hipStream_t st);
-// SSM step that stores the gate product g = bf16(y) * silu(z) (fp32, [batch][d_inner]) and,
-// per (sequence, head, half head), the sum of squares of g for the gated RMSNorm.
+// SSM step that stores g w, the gate product g = bf16(y) * silu(z) times the gated-norm
+// weight (fp32, [batch][d_inner]), and, per (sequence, head, half head), the sum of squares of
+// g for the gated RMSNorm.
 hipError_t launch_ssm_step_part(const uint16_t *xc, const uint16_t *dtr, long ld_dt,
                                 const float *dt_bias, const float *A_log, const float *D,
-                                float *S, float *gate, const uint16_t *z, float *part, int batch,
+                                float *S, float *gate, const uint16_t *z, const uint16_t *gw, float *part, int batch,
                                 hipStream_t st);
-// Gated RMSNorm (from g and the SSM step's partial sums) fused into out_proj + residual.
-hipError_t launch_outproj_step(const W4 &W, const float *gate, const uint16_t *gw, const float *part,
+// Gated RMSNorm (from g w and the SSM step's partial sums of g) fused into out_proj + residual.
+hipError_t launch_outproj_step(const W4 &W, const float *gate, const float *part,
                                float eps, int batch, const void *res, int res_t, void *out, int out_t,
                                hipStream_t st);
 hipError_t launch_conv_step(const uint16_t *xbc, long ld, uint16_t *state, const uint16_t *w,

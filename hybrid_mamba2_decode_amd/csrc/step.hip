@@ -28,6 +28,7 @@ __global__ __launch_bounds__(256) void k_ssm_step(const uint16_t *__restrict__ x
                                                   const float *__restrict__ Dp,
                                                   float *__restrict__ S, void *__restrict__ y,
                                                   const uint16_t *__restrict__ z,
+                                                  const uint16_t *__restrict__ gw,
                                                   float *__restrict__ part)
 {
     const int half = blockIdx.x & 1;
@@ -94,8 +95,9 @@ __global__ __launch_bounds__(256) void k_ssm_step(const uint16_t *__restrict__ x
     }
 
     // ---- the gate product g = bf16(y) * silu(z) (fp32; y is rounded to bf16 first, its
-    // storage point) and this work-group's sum of squares of g, both consumed by the gated
-    // RMSNorm in the out_proj kernel, which so needs neither y nor z.
+    // storage point) times the gated-norm weight, and this work-group's sum of squares of g,
+    // both consumed by the gated RMSNorm in the out_proj kernel, which so needs neither y, z
+    // nor the norm weight: o = bf16((g w) / rms(g)).
     __shared__ float red[8];
     float ss = 0.f;
     if (nl == 0)
@@ -104,7 +106,7 @@ __global__ __launch_bounds__(256) void k_ssm_step(const uint16_t *__restrict__ x
             const int p = half * SSM_ROWS + slot + 8 * it;
             const size_t i = (size_t)b * DINNER + h * HDIM + p;
             const float gm = round_bf16(yv[it]) * silu(bf16_to_f32(z[i]));
-            reinterpret_cast<float *>(y)[i] = gm;
+            reinterpret_cast<float *>(y)[i] = gm * bf16_to_f32(gw[h * HDIM + p]);
             ss += gm * gm;
         }
     if (nl == 0) red[slot] = ss;
@@ -124,20 +126,20 @@ hipError_t launch_ssm_step(const uint16_t *xc, const uint16_t *dtr, long ld_dt,
     dim3 grid(batch * NHEADS * 2), block(256);
     if (y_t == BF16)
         k_ssm_step<false, BF16><<<grid, block, 0, st>>>(xc, dtr, ld_dt, dt_bias, A_log, D, S, y,
-                                                        nullptr, nullptr);
+                                                        nullptr, nullptr, nullptr);
     else
         k_ssm_step<false, F32><<<grid, block, 0, st>>>(xc, dtr, ld_dt, dt_bias, A_log, D, S, y,
-                                                       nullptr, nullptr);
+                                                       nullptr, nullptr, nullptr);
     return hipGetLastError();
 }
 
 hipError_t launch_ssm_step_part(const uint16_t *xc, const uint16_t *dtr, long ld_dt,
                                 const float *dt_bias, const float *A_log, const float *D,
-                                float *S, float *gate, const uint16_t *z, float *part, int batch,
-                                hipStream_t st)
+                                float *S, float *gate, const uint16_t *z, const uint16_t *gw, float *part,
+                                int batch, hipStream_t st)
 {
     dim3 grid(batch * NHEADS * 2), block(256);
-    launch_k(k_ssm_step<true, F32>, grid, block, 0, st, xc, dtr, ld_dt, dt_bias, A_log, D, S, gate, z, part);
+    launch_k(k_ssm_step<true, F32>, grid, block, 0, st, xc, dtr, ld_dt, dt_bias, A_log, D, S, gate, z, gw, part);
     return hipGetLastError();
 }
 
