@@ -44,9 +44,19 @@ __global__ __launch_bounds__(256) void k_ssm_step(const uint16_t *__restrict__ x
     const uint16_t dtb = dtr[(size_t)b * ld_dt + h];
     const uint2 bw = *reinterpret_cast<const uint2 *>(xb + OFF_B + g * DSTATE + 4 * nl);
     const uint2 cw = *reinterpret_cast<const uint2 *>(xb + OFF_C + g * DSTATE + 4 * nl);
-    uint16_t xr[SSM_IT];
+    uint16_t xr[SSM_IT], zr[SSM_IT], wr[SSM_IT];
 #pragma unroll
     for (int it = 0; it < SSM_IT; ++it) xr[it] = xb[h * HDIM + half * SSM_ROWS + slot + 8 * it];
+    // the gate's z and the gated-norm weight, loaded with the rest (every lane of a row loads
+    // the same value): the epilogue then makes no round trip to memory
+    if constexpr (GN) {
+#pragma unroll
+        for (int it = 0; it < SSM_IT; ++it) {
+            const int p = half * SSM_ROWS + slot + 8 * it;
+            zr[it] = z[(size_t)b * DINNER + h * HDIM + p];
+            wr[it] = gw[h * HDIM + p];
+        }
+    }
     __builtin_amdgcn_sched_barrier(0);
     float4 *Sh = reinterpret_cast<float4 *>(S + ((size_t)b * NHEADS + h) * HDIM * DSTATE);
     float4 s[SSM_IT];
@@ -105,8 +115,8 @@ __global__ __launch_bounds__(256) void k_ssm_step(const uint16_t *__restrict__ x
         for (int it = 0; it < SSM_IT; ++it) {
             const int p = half * SSM_ROWS + slot + 8 * it;
             const size_t i = (size_t)b * DINNER + h * HDIM + p;
-            const float gm = round_bf16(yv[it]) * silu(bf16_to_f32(z[i]));
-            reinterpret_cast<float *>(y)[i] = gm * bf16_to_f32(gw[h * HDIM + p]);
+            const float gm = round_bf16(yv[it]) * silu(bf16_to_f32(zr[it]));
+            reinterpret_cast<float *>(y)[i] = gm * bf16_to_f32(wr[it]);
             ss += gm * gm;
         }
     if (nl == 0) red[slot] = ss;
