@@ -17,6 +17,8 @@ with gcc, wraps it with ctypes and adds these numpy-level pieces:
   greedy id (smallest index of the largest logit, NaN never chosen).
 * ``fused_embedding`` -- the language model's input row: two 4-bit embedding rows
   and the audio frame.
+* ``mlp`` -- one MLP layer of the hybrid stack (pre-norm, 4-bit up, squared ReLU,
+  4-bit down, residual).
 
 Readings of the pages that the oracle fixes (no mixer equations are printed
 on the pages; see the header of nh_oracle.c):
@@ -202,6 +204,26 @@ def greedy_ids(logits) -> np.ndarray:
             best = l2[r][ok].max()
             ids[r] = int(np.flatnonzero(ok & (l2[r] == best))[0])
     return ids
+
+
+def mlp(x, norm_w, W_up, W_down, eps: float, mode: int = CONTRACT) -> np.ndarray:
+    """One MLP layer of the hybrid stack: out = x + down(relu(up(u))^2), u = RMSNorm(x) w.
+
+    The issue page "feat(nemotron_voicechat): ... offline duplex inference #1374", section
+    "config.json": the '-' layers of hybrid_override_pattern are MLPs with intermediate_size
+    15680 and mlp_bias false, quantized like the mixer projections; the pages do not name the
+    activation, and the squared ReLU of the Nemotron-H architecture is the reading taken here.
+    CONTRACT rounds u and the activation h = relu(up(u))^2 to bf16 (the storage points the GPU
+    kernels use); sums are fp64.  x: [m][hidden] doubles.  Returns out [m][hidden]."""
+    x2 = _d(x).reshape(-1, W_up.k_in)
+    u = rmsnorm(x2, norm_w, eps)
+    if mode == CONTRACT:
+        u = round_bf16(u)
+    a = w4_matvec(W_up, u)
+    h = np.maximum(a, 0.0) ** 2
+    if mode == CONTRACT:
+        h = round_bf16(h)
+    return x2 + w4_matvec(W_down, h)
 
 
 def fused_embedding(E, text_ids, function_ids, audio, function_weight: float = 2.0) -> np.ndarray:

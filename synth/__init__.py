@@ -57,6 +57,9 @@ _I_X, _I_CONV_STATE, _I_SSM_STATE = 0, 1, 2
 HEADS_LAYER = 100
 _T_NORM_F, _T_LMH_Q, _T_LMH_S, _T_FNH_Q, _T_FNH_S = 11, 12, 13, 14, 15
 _T_EMB_Q, _T_EMB_S = 16, 17
+# MLP layers use their own layer index of the hybrid pattern and these tensor ids
+_T_MLP_NORM, _T_UP_Q, _T_UP_S, _T_DOWN_Q, _T_DOWN_S = 20, 21, 22, 23, 24
+MLP_INTER = 15680
 _I_AUDIO, _I_IDS = 3, 4
 VOCAB = 131072
 
@@ -173,6 +176,27 @@ def head_weights(seed: int = 0, n_out: int = VOCAB, d: Dims = REAL) -> HeadWeigh
     lm = w4_random(seed, HEADS_LAYER, _T_LMH_Q, _T_LMH_S, n_out, d.hidden, d.group_size)
     fn = w4_random(seed, HEADS_LAYER, _T_FNH_Q, _T_FNH_S, n_out, d.hidden, d.group_size)
     return HeadWeights(norm_f, lm, fn)
+
+
+@dataclass
+class MlpWeights:
+    norm_w: np.ndarray      # bf16 [hidden]
+    up: W4Matrix            # [15680][hidden]
+    down: W4Matrix          # [hidden][15680]
+
+
+def mlp_weights(layer: int, seed: int = 0, inter: int = MLP_INTER, d: Dims = REAL) -> MlpWeights:
+    """norm weight 1 + N(0, 0.05^2); up and down drawn like in_proj.  The down scales are
+    divided by 8 (U(0.00025, 0.00075)): the squared-ReLU activations reach tens, and the
+    mixer's scale range would make each MLP layer add O(100) to the residual stream."""
+    g = rng(seed, layer, _T_MLP_NORM)
+    norm_w = f32_to_bf16(1.0 + g.normal(0.0, 0.05, d.hidden).astype(np.float32))
+    up = w4_random(seed, layer, _T_UP_Q, _T_UP_S, inter, d.hidden, d.group_size)
+    dq = rng(seed, layer, _T_DOWN_Q).integers(0, 1 << 32, size=(d.hidden, inter // 8), dtype=np.uint32)
+    s32 = rng(seed, layer, _T_DOWN_S).uniform(0.00025, 0.00075, size=(d.hidden, inter // d.group_size)).astype(np.float32)
+    sb = f32_to_bf16(s32)
+    bb = f32_to_bf16(bf16_to_f32(sb) * np.float32(-8.0))
+    return MlpWeights(norm_w, up, W4Matrix(dq, sb, bb, d.hidden, inter, d.group_size))
 
 
 def embed_tokens(seed: int = 0, n_out: int = VOCAB, d: Dims = REAL) -> W4Matrix:

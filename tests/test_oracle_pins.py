@@ -235,6 +235,48 @@ def test_fused_embedding_independent_decode_and_bad_ids(oracle_lib):
     assert np.isnan(bad).all()
 
 
+def _const_w4(vals, k):
+    """Rows of constant value v (every nibble 9, bias -8 s, scale s = v): W[n][k] = v_n."""
+    n = len(vals)
+    q = np.full((n, k // 8), 0x99999999, dtype=np.uint32)
+    sb = synth.f32_to_bf16(np.repeat(np.asarray(vals, np.float32)[:, None], k // 64, axis=1))
+    bb = synth.f32_to_bf16(synth.bf16_to_f32(sb) * np.float32(-8.0))
+    return synth.W4Matrix(q, sb, bb, n, k)
+
+
+def test_mlp_closed_form(oracle_lib):
+    # up rows: +0.25 (kept) and -0.25 (cut by the ReLU); down rows constant 0.5 and -1;
+    # x = 3 everywhere normalises to h0 = 1/sqrt(1 + eps/9) (EXACT mode)
+    k, inter, eps = 128, 192, 1e-5
+    up = _const_w4([0.25] * 100 + [-0.25] * 92, k)
+    down = _const_w4([0.5] * 64 + [-1.0] * 64, inter)
+    wn = synth.f32_to_bf16(np.ones(k, dtype=np.float32))
+    x = np.full((1, k), 3.0)
+    h0 = 1.0 / math.sqrt(1 + eps / 9.0)
+    a = 0.25 * k * h0                      # each kept unit
+    m = 100 * a * a                        # sum over the kept units of relu(a)^2
+    got = oracle_lib.mlp(x, wn, up, down, eps, mode=oracle_lib.EXACT)[0]
+    want = np.r_[np.full(64, 3.0 + 0.5 * m), np.full(64, 3.0 - m)]
+    assert np.allclose(got, want, rtol=1e-13)
+
+
+def test_mlp_matches_library_pieces(oracle_lib):
+    # EXACT mode is torch's rms_norm, two independently decoded matmuls and relu^2
+    rng = np.random.default_rng(14)
+    up = synth.w4_random(4, 5, 1, 2, 192, 256)
+    down = synth.w4_random(4, 5, 3, 4, 256, 192)
+    _, Ud = _byte_split_dequant(up)
+    _, Dd = _byte_split_dequant(down)
+    x = rng.normal(size=(3, 256))
+    wn = synth.f32_to_bf16((1 + 0.05 * rng.normal(size=256)).astype(np.float32))
+    wd = torch.from_numpy(synth.bf16_to_f32(wn).astype(np.float64))
+    u = F.rms_norm(torch.from_numpy(x), (256,), weight=wd, eps=1e-5)
+    h = torch.relu(u @ torch.from_numpy(Ud).T) ** 2
+    want = (torch.from_numpy(x) + h @ torch.from_numpy(Dd).T).numpy()
+    got = oracle_lib.mlp(x, wn, up, down, 1e-5, mode=oracle_lib.EXACT)
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
 # ---------------------------------------------------------------- norms
 
 def test_rmsnorm_constant_vector_closed_form(oracle_lib):
