@@ -14,6 +14,7 @@ Also measured in the same run, each in its own object of the JSON line:
   * the 27-layer stack stepwise over T = 413 at batch 1, and the 27-layer full-history
     stack at batch 2, T = 3750, chunk 256;
   * the block step with 4 sessions sharing one weight stream;
+  * one MLP layer step (the hybrid stack's other layer kind), over the 25 MLP layers' weights;
   * the final norm + both output heads (W4 131072 x 4480 each) + greedy ids at batch 1,
     and the fused input row (two W4 embedding rows + the audio frame);
   * the CPU oracle on the host cores (a bounded sample of the batch-1 block step), as a
@@ -48,6 +49,12 @@ VOCAB = 131072             # vocab_size: rows of each output head
 
 
 # ------------------------------------------------------- algorithmic work
+
+def pattern_layers(kind: str):
+    """Layer indices of one kind in the hybrid pattern, read from the library."""
+    import hybrid_mamba2_decode_amd as nh
+    return [i for i, c in enumerate(nh.hybrid_pattern()) if c == kind]
+
 
 def w4_bytes(n, k):
     return n * k // 2 + 2 * 2 * n * (k // 64)   # packed nibbles + bf16 scales + bf16 biases
@@ -155,7 +162,8 @@ def main():
     ap.add_argument("--skip-seq", action="store_true", help="skip the batch-2 T=3750 scan and stack")
     ap.add_argument("--skip-stack", action="store_true", help="skip the 27-layer stacks")
     ap.add_argument("--skip-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--skip-heads", action="store_true", help="skip the final norm + two output heads")
+    ap.add_argument("--skip-heads", action="store_true",
+                    help="skip the legs outside the block: MLP layer, output heads, input row")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
@@ -318,6 +326,43 @@ def main():
     }
     log("batch-4 step:", out["step_batch4"])
     del st4, ws4s
+
+    # ----------------------- MLP layer step, batch 1, over the model's 25 MLP layers' weights
+    if not args.skip_heads:
+        t0 = time.time()
+        mlps = []
+        for l in pattern_layers("-"):
+            mw = synth.mlp_weights(l)
+            mlps.append((gu.to_dev(mw.norm_w), gu.w4_dev(mw.up), gu.w4_dev(mw.down)))
+            del mw
+        log(f"{len(mlps)} MLP layers ready in {time.time() - t0:.1f} s")
+        wsm_n = nh.nh_mlp_workspace_bytes(synth.MLP_INTER, 1)
+        wsm = gu.workspace(wsm_n)
+        xm = gu.to_dev(np.random.default_rng(78).normal(0, 1, (1, HID)).astype(np.float32))
+        om = gu.empty_f32(1, HID)
+
+        def mlp_step(i):
+            nw_, up_, dn_ = mlps[i % len(mlps)]
+            nh.nh_mlp_step(nw_, up_, dn_, 1e-5, xm, nh.NH_F32, om, nh.NH_F32, 1, wsm, wsm_n, stream)
+
+        for i in range(100):
+            mlp_step(i)
+        nm = 500
+        hip.record(e0, stream)
+        for i in range(nm):
+            mlp_step(i)
+        hip.record(e1, stream)
+        torch.cuda.synchronize()
+        us_m = hip.ms(e0, e1) * 1e3 / nm
+        mb = w4_bytes(synth.MLP_INTER, HID) + w4_bytes(HID, synth.MLP_INTER) + 2 * HID + 4 * HID * 2 + 2 * synth.MLP_INTER * 2
+        out["mlp_step"] = {
+            "workload": f"one MLP layer (pre-norm, W4 up 4480->15680, squared ReLU, W4 down 15680->4480, residual), "
+                        f"batch 1, rotating over the {len(mlps)} MLP layers' weights",
+            "us_per_layer_step": round(us_m, 3), "algorithmic_bytes": int(mb),
+            "hbm_frac": round(mb / (us_m * 1e-6) / HBM_PEAK, 4),
+        }
+        log("mlp step:", out["mlp_step"])
+        del mlps
 
     # ------------------------------- 27-layer stack, batch 1, stepwise over T=413
     if not args.skip_stack:

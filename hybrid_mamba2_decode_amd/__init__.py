@@ -38,6 +38,7 @@ EXPORTS = (
     "nh_conv1d_step", "nh_conv1d_seq", "nh_ssm_step", "nh_ssd_scan_workspace_bytes", "nh_ssd_chunk_scan",
     "nh_rmsnorm_gated", "nh_block_workspace_bytes", "nh_mamba_block_step", "nh_mamba_block_seq",
     "nh_mamba_stack", "nh_head_workspace_bytes", "nh_head_argmax", "nh_fused_embedding",
+    "nh_mlp_workspace_bytes", "nh_mlp_step",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -98,6 +99,8 @@ _sigs = {
     "nh_head_workspace_bytes": (_sz, [_i]),
     "nh_head_argmax": (_i, [_vp, _vp, _i, _vp, C.c_float, _i, _vp, _vp, _vp, _sz, _vp]),
     "nh_fused_embedding": (_i, [_vp, _vp, _vp, _vp, _i, C.c_float, _i, _vp, _vp]),
+    "nh_mlp_workspace_bytes": (_sz, [_i, _i]),
+    "nh_mlp_step": (_i, [_vp, _vp, _vp, C.c_float, _vp, _i, _vp, _i, _i, _vp, _sz, _vp]),
 }
 for _name, (_res, _args) in _sigs.items():
     _f = getattr(lib, _name)
@@ -172,6 +175,15 @@ def hybrid_pattern() -> str:
 def nh_w4_gemv(W, x, batch, residual, res_dtype, y, y_dtype, stream=None):
     _check(lib.nh_w4_gemv(C.byref(W), _ptr(x), batch, _ptr(residual), res_dtype, _ptr(y), y_dtype,
                           _stream(stream)))
+
+
+def nh_mlp_workspace_bytes(inter, batch) -> int:
+    return lib.nh_mlp_workspace_bytes(inter, batch)
+
+
+def nh_mlp_step(norm_w, up, down, eps, x, x_dtype, out, out_dtype, batch, ws, ws_bytes, stream=None):
+    _check(lib.nh_mlp_step(_ptr(norm_w), C.byref(up), C.byref(down), eps, _ptr(x), x_dtype, _ptr(out),
+                           out_dtype, batch, _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def nh_fused_embedding(E, text_ids, function_ids, audio, audio_dtype, function_weight, batch, out,

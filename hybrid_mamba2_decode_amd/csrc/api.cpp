@@ -326,6 +326,37 @@ nh_status nh_w4_gemv(const nh_w4_matrix *W, const uint16_t *x, int batch, const 
     return ok();
 }
 
+size_t nh_mlp_workspace_bytes(int inter, int batch)
+{
+    if (inter < 64 || inter % 64 || inter > 16384 || batch < 1 || batch > 4) return 0;
+    return ((size_t)batch * inter * sizeof(uint16_t) + 255) / 256 * 256;
+}
+
+nh_status nh_mlp_step(const uint16_t *norm_w, const nh_w4_matrix *up, const nh_w4_matrix *down, float eps,
+                      const void *x, nh_dtype x_dtype, void *out, nh_dtype out_dtype, int batch, void *ws,
+                      size_t ws_bytes, void *stream)
+{
+    NH_TRY(need_ptr(norm_w, "norm_w"));
+    NH_TRY(check_w4(up, "up"));
+    NH_TRY(check_w4(down, "down"));
+    if (up->k_in != HIDDEN || down->n_out != HIDDEN || down->k_in != up->n_out)
+        return fail(NH_ERR_UNSUPPORTED_SHAPE, "up %d x %d, down %d x %d (need up [inter][%d], down [%d][inter])",
+                    up->n_out, up->k_in, down->n_out, down->k_in, HIDDEN, HIDDEN);
+    NH_TRY(need_ptr(x, "x"));
+    NH_TRY(need_dtype(x_dtype, "x_dtype"));
+    NH_TRY(need_ptr(out, "out"));
+    NH_TRY(need_dtype(out_dtype, "out_dtype"));
+    NH_TRY(need_ptr(ws, "ws"));
+    if (!(eps > 0.f) || !std::isfinite(eps)) return fail(NH_ERR_INVALID_ARGUMENT, "eps must be positive");
+    if (batch < 1 || batch > 4) return fail(NH_ERR_UNSUPPORTED_SHAPE, "batch %d outside 1..4", batch);
+    const size_t need = nh_mlp_workspace_bytes(up->n_out, batch);
+    if (ws_bytes < need) return fail(NH_ERR_WORKSPACE_TOO_SMALL, "mlp workspace %zu < %zu bytes", ws_bytes, need);
+    uint16_t *h = reinterpret_cast<uint16_t *>(ws);
+    NH_HIP(launch_mlp_up_step(view(up), x, x_dtype, norm_w, eps, batch, h, S(stream)), "mlp up");
+    NH_HIP(launch_gemv(view(down), h, batch, x, x_dtype, out, out_dtype, S(stream)), "mlp down");
+    return ok();
+}
+
 nh_status nh_fused_embedding(const nh_w4_matrix *E, const int32_t *text_ids, const int32_t *function_ids,
                              const void *audio, nh_dtype audio_dtype, float function_weight, int batch,
                              float *out, void *stream)

@@ -178,6 +178,18 @@ struct EpiInProjStep {
     }
 };
 
+// MLP up projection: h[b][n] = bf16(relu(acc)^2), the activation between the two projections.
+struct EpiReluSq {
+    uint16_t *h;
+    int n;
+    __device__ __forceinline__ EpiPre prefetch(int, int) const { return EpiPre{}; }
+    __device__ __forceinline__ void operator()(int row, int b, float acc, const EpiPre &) const
+    {
+        const float r = fmaxf(acc, 0.f);
+        h[(size_t)b * n + row] = f32_to_bf16(r * r);
+    }
+};
+
 // One pipeline stage: RG row groups of 64/LPR rows, CPL chunks per lane.
 template <int RG, int CPL>
 struct Stage {
@@ -488,11 +500,11 @@ struct IpRows {
     }
 };
 
-template <int NB>
+template <int NB, class Epi = EpiInProjStep>
 struct InProjBlock {
     using S = InProjShape<NB>;
     static constexpr int R = S::R, NS = S::NS, RW = S::RW;
-    const EpiInProjStep epi;
+    const Epi epi;
     IpRows<R> io;
     int rb;
     bool active;
@@ -515,7 +527,7 @@ struct InProjBlock {
     // Issues the epilogue prefetch and the first stage (unconditionally, rows clamped: a
     // branch here would make the compiler's wait before the first use of any earlier load
     // also cover these loads; idle waves read the last row, which the cache holds).
-    __device__ __forceinline__ InProjBlock(const W4 &W, const EpiInProjStep &e) : epi(e)
+    __device__ __forceinline__ InProjBlock(const W4 &W, const Epi &e) : epi(e)
     {
         io.init(W);
         const int xcd = blockIdx.x & 7;
@@ -916,6 +928,26 @@ __global__ __launch_bounds__(NB == 1 ? 512 : 256, 1) void k_outproj_step(W4 W, c
     run.run(a);
 }
 
+// Pre-norm + MLP up projection (K = hidden) + squared ReLU: the in_proj kernel's structure
+// with the activation as its epilogue.
+template <int NB, int XT>
+__global__ __launch_bounds__(InProjShape<NB>::NT, 1) void k_mlp_up_step(W4 W, const void *__restrict__ x,
+                                                                    const uint16_t *__restrict__ nw, float eps,
+                                                                    EpiReluSq epi)
+{
+    constexpr int NT = InProjShape<NB>::NT, R = InProjShape<NB>::R;
+    extern __shared__ __attribute__((aligned(16))) uint32_t act_lds[];
+    __shared__ float red[NB][NT / 64];
+    PreNorm<NB, XT, NT> pn;
+    pn.issue(x, nw);
+    __builtin_amdgcn_sched_barrier(0);
+    InProjBlock<NB, EpiReluSq> run(W, epi);
+    pn.finish(eps, act_lds, red);
+    ActChunk am[NB][2], at[NB];
+    act_hidden<NB, R>(am, at, act_lds);
+    run.run(am, at);
+}
+
 // Final norm + one W4 output head + greedy id.  The head has K = hidden, so it shares the
 // in_proj chunk layout and pre-norm; its 131072 rows are R-row stages split into one
 // contiguous range per XCD and, inside it, one contiguous range per wave (so rows that share
@@ -1182,6 +1214,30 @@ hipError_t launch_inproj_step(const W4 &W, const void *x, int x_t, const uint16_
     }
 #undef NH_LAUNCH
 #undef NH_LAUNCH_MF
+    return hipGetLastError();
+}
+
+hipError_t launch_mlp_up_step(const W4 &W, const void *x, int x_t, const uint16_t *norm_w, float eps, int batch,
+                              uint16_t *h, hipStream_t st)
+{
+    EpiReluSq e{h, W.n};
+    const size_t lds = (size_t)batch * (HIDDEN / 32) * ACT_WORDS * 4;
+#define NH_LAUNCH(NB)                                                                                      \
+    {                                                                                                      \
+        const int grid = inproj_grid<NB>(W.n);                                                             \
+        const dim3 blk(InProjShape<NB>::NT);                                                               \
+        if (x_t == BF16)                                                                                   \
+            launch_k(k_mlp_up_step<NB, BF16>, dim3(grid), blk, lds, st, W, x, norm_w, eps, e);             \
+        else                                                                                               \
+            launch_k(k_mlp_up_step<NB, F32>, dim3(grid), blk, lds, st, W, x, norm_w, eps, e);              \
+    }
+    switch (batch) {
+    case 1: NH_LAUNCH(1); break;
+    case 2: NH_LAUNCH(2); break;
+    case 3: NH_LAUNCH(3); break;
+    default: NH_LAUNCH(4); break;
+    }
+#undef NH_LAUNCH
     return hipGetLastError();
 }
 

@@ -50,6 +50,9 @@ hipError_t launch_inproj_step(const W4 &W, const void *x, int x_t, const uint16_
                               uint16_t *conv_state, const uint16_t *conv_w,
                               const uint16_t *conv_b, uint32_t *zero_ptr, int nzero,
                               hipStream_t st);
+// Pre-norm + MLP up projection (k = HIDDEN) + squared ReLU into h (bf16 [batch][W.n]).
+hipError_t launch_mlp_up_step(const W4 &W, const void *x, int x_t, const uint16_t *norm_w, float eps, int batch,
+                              uint16_t *h, hipStream_t st);
 // The language model's input row: E[text_id] + audio + wf E[function_id] (fp32 out).
 hipError_t launch_fused_embed(const W4 &E, const int *text_ids, const int *function_ids, const void *audio,
                               int audio_t, float wf, int batch, float *out, hipStream_t st);

@@ -218,6 +218,22 @@ nh_status nh_rmsnorm_gated(const uint16_t *y, const uint16_t *z, long ld_z, cons
 
 /* ----------------------------------------------------------- model top */
 
+/* One MLP layer of the hybrid stack, per position, for `batch` sequences
+ * (issue page, section "config.json": the '-' layers of hybrid_override_pattern
+ * are MLPs with intermediate_size 15680 and mlp_bias false, quantized like the
+ * mixer projections; the pages do not name the activation, and squared ReLU,
+ * Nemotron-H's, is the reading taken):
+ *   u = bf16(RMSNorm(x) * norm_w), h = bf16(relu(up u)^2), out = x + down h
+ * with fp32 sums.  up: [inter][4480], down: [4480][inter], inter % 64 == 0
+ * and <= 16384; x: [batch][4480] of x_dtype; out: [batch][4480] of out_dtype
+ * (may not alias x).  ws: at least nh_mlp_workspace_bytes(inter, batch)
+ * bytes (holds h).  batch 1..4; every pointer 16-byte aligned.  Errors
+ * before any launch as for the other entry points. */
+size_t nh_mlp_workspace_bytes(int inter, int batch);
+nh_status nh_mlp_step(const uint16_t *norm_w, const nh_w4_matrix *up, const nh_w4_matrix *down, float eps,
+                      const void *x, nh_dtype x_dtype, void *out, nh_dtype out_dtype, int batch,
+                      void *ws, size_t ws_bytes, void *stream);
+
 /* The language model's input row for `batch` positions (issue page, section
  * "Network 2": embed_tokens row of the previous text id, plus the projected
  * audio frame, plus function_channel_weight (2.0 in the config) times the

@@ -114,6 +114,26 @@ def test_fused_embedding_rejects_bad_arguments(nh):
     assert call(E=_fake_w4(gs=32)) == nh.NH_ERR_UNSUPPORTED_SHAPE
 
 
+def test_mlp_rejects_bad_arguments(nh):
+    A = 0x20000
+    assert nh.nh_mlp_workspace_bytes(15680, 1) == 31488 and nh.nh_mlp_workspace_bytes(15680, 5) == 0
+    assert nh.nh_mlp_workspace_bytes(100, 1) == 0
+    up, down = _fake_w4(n=15680, k=4480), _fake_w4(n=4480, k=15680)
+    ws = nh.nh_mlp_workspace_bytes(15680, 1)
+
+    def call(**kw):
+        a = dict(up=up, down=down, batch=1, ws_bytes=ws, x=A, xt=0)
+        a.update(kw)
+        return _status(lambda: nh.nh_mlp_step(A, a["up"], a["down"], 1e-5, a["x"], a["xt"], A, 0, a["batch"], A,
+                                              a["ws_bytes"], 0))
+    assert call(down=_fake_w4(n=4480, k=15616)) == nh.NH_ERR_UNSUPPORTED_SHAPE   # inner sizes differ
+    assert call(up=_fake_w4(n=15680, k=4096)) == nh.NH_ERR_UNSUPPORTED_SHAPE
+    assert call(batch=5) == nh.NH_ERR_UNSUPPORTED_SHAPE
+    assert call(ws_bytes=ws - 1) == nh.NH_ERR_WORKSPACE_TOO_SMALL
+    assert call(x=A + 8) == nh.NH_ERR_MISALIGNED
+    assert call(xt=5) == nh.NH_ERR_INVALID_ARGUMENT
+
+
 def test_gemm_workspace_check(nh):
     A = 0x20000
     need = nh.nh_w4_gemm_workspace_bytes(100, 128)
