@@ -809,10 +809,15 @@ __global__ __launch_bounds__(256, 1) void k_inproj_step_mf(W4 W, const void *__r
     }
 }
 
+// Work-groups of four waves per CU for the generic GEMV: three or two at batch 1 while the
+// activations (CPL chunks of 18 registers per lane) leave room, one above: with 8 chunks per
+// lane (K above 10240, e.g. an MLP down projection of K = 15680) two per CU spilled.
+constexpr int gemv_wgs_per_cu(int nb, int cpl) { return nb == 1 ? (cpl <= 3 ? 3 : cpl <= 5 ? 2 : 1) : 1; }
+
 // ------------------------------------------------------------------ kernels
 
 template <int LPR, int CPL, int NB, int RG>
-__global__ __launch_bounds__(256, (NB == 1 ? (CPL <= 3 ? 3 : 2) : 1)) void k_gemv(W4 W, const uint16_t *__restrict__ x, EpiStore epi)
+__global__ __launch_bounds__(256, gemv_wgs_per_cu(NB, CPL)) void k_gemv(W4 W, const uint16_t *__restrict__ x, EpiStore epi)
 {
     GemvRunner<LPR, CPL, NB, RG, EpiStore> run(W, epi, 256);
     extern __shared__ __attribute__((aligned(16))) uint32_t act_lds[];
@@ -1134,7 +1139,7 @@ template <int LPR, int CPL, int NB, int RG>
 static hipError_t run_gemv(const W4 &W, const uint16_t *x, EpiStore e, hipStream_t st)
 {
     const size_t lds = (size_t)NB * (W.k >> 5) * ACT_WORDS * 4;
-    const int grid = gemv_grid(W.n, RG * (64 / LPR), NB == 1 ? (CPL <= 3 ? 3 : 2) : 1);
+    const int grid = gemv_grid(W.n, RG * (64 / LPR), gemv_wgs_per_cu(NB, CPL));
     k_gemv<LPR, CPL, NB, RG><<<dim3(grid), dim3(256), lds, st>>>(W, x, e);
     return hipGetLastError();
 }
