@@ -14,7 +14,8 @@ Also measured in the same run, each in its own object of the JSON line:
   * the 27-layer stack stepwise over T = 413 at batch 1, and the 27-layer full-history
     stack at batch 2, T = 3750, chunk 256;
   * the block step with 4 sessions sharing one weight stream;
-  * one MLP layer step (the hybrid stack's other layer kind), over the 25 MLP layers' weights;
+  * one MLP layer step (the hybrid stack's other layer kind), over the 25 MLP layers' weights,
+    and one whole language-model position (input row, Mamba2 and MLP layers, both heads);
   * the final norm + both output heads (W4 131072 x 4480 each) + greedy ids at batch 1,
     and the fused input row (two W4 embedding rows + the audio frame);
   * the CPU oracle on the host cores (a bounded sample of the batch-1 block step), as a
@@ -362,7 +363,44 @@ def main():
             "hbm_frac": round(mb / (us_m * 1e-6) / HBM_PEAK, 4),
         }
         log("mlp step:", out["mlp_step"])
-        del mlps
+
+        # one language-model position: input row, 27 Mamba2 + 25 MLP layers in pattern order
+        # (attention layers pass the stream through), norm_f, both heads and greedy ids
+        hw = synth.head_weights(seed=9)
+        lmw = nh.lm_weights(gu.w4_dev(synth.embed_tokens(seed=9)), dev_layers[:n_layers],
+                            [nh.mlp_weights(*m) for m in mlps], gu.to_dev(hw.norm_f), gu.w4_dev(hw.lm_head),
+                            gu.w4_dev(hw.function_head), 2.0)
+        del hw
+        st_lm = [gu.state_dev(np.zeros((1, 3, CD), np.uint16), np.zeros((1, H, P, N), np.float32))[0]
+                 for _ in range(n_layers)]
+        wsl_n = nh.nh_lm_workspace_bytes(d128, synth.MLP_INTER, 1)
+        wsl = gu.workspace(wsl_n)
+        ti, fi, au = synth.embed_inputs(200, 1)
+        ti, fi, au = (torch.tensor(ti, device="cuda"), torch.tensor(fi, device="cuda"), gu.to_dev(au))
+        ot, of = (torch.empty(1, dtype=torch.int32, device="cuda") for _ in range(2))
+
+        def lm_pos():
+            nh.nh_lm_step(d128, lmw, st_lm, ti, fi, au, nh.NH_F32, 1, None, ot, of, wsl, wsl_n, stream)
+
+        for _ in range(5):
+            lm_pos()
+        npos = 50
+        hip.record(e0, stream)
+        for _ in range(npos):
+            lm_pos()
+        hip.record(e1, stream)
+        torch.cuda.synchronize()
+        us_lm = hip.ms(e0, e1) * 1e3 / npos
+        lm_bytes = (n_layers * sum(step_kernel_bytes(1)) + len(mlps) * mb + 2 * (w4_bytes(VOCAB, HID) + 6 * HID))
+        out["lm_step"] = {
+            "workload": "one language-model position at batch 1: input row, 27 Mamba2 blocks and 25 MLP layers in "
+                        "pattern order (the 4 attention layers not part of the library), norm_f, lm_head + "
+                        "function_head (W4 131072x4480) and greedy ids",
+            "ms_per_position": round(us_lm / 1e3, 4), "algorithmic_bytes": int(lm_bytes),
+            "hbm_frac": round(lm_bytes / (us_lm * 1e-6) / HBM_PEAK, 4),
+        }
+        log("lm step:", out["lm_step"])
+        del mlps, lmw, st_lm
 
     # ------------------------------- 27-layer stack, batch 1, stepwise over T=413
     if not args.skip_stack:

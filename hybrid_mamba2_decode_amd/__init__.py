@@ -38,7 +38,7 @@ EXPORTS = (
     "nh_conv1d_step", "nh_conv1d_seq", "nh_ssm_step", "nh_ssd_scan_workspace_bytes", "nh_ssd_chunk_scan",
     "nh_rmsnorm_gated", "nh_block_workspace_bytes", "nh_mamba_block_step", "nh_mamba_block_seq",
     "nh_mamba_stack", "nh_head_workspace_bytes", "nh_head_argmax", "nh_fused_embedding",
-    "nh_mlp_workspace_bytes", "nh_mlp_step",
+    "nh_mlp_workspace_bytes", "nh_mlp_step", "nh_lm_workspace_bytes", "nh_lm_step",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -75,6 +75,16 @@ class nh_mamba_state(C.Structure):
     _fields_ = [("conv_state", C.c_void_p), ("ssm_state", C.c_void_p)]
 
 
+class nh_mlp_weights(C.Structure):
+    _fields_ = [("norm_w", C.c_void_p), ("up", nh_w4_matrix), ("down", nh_w4_matrix)]
+
+
+class nh_lm_weights(C.Structure):
+    _fields_ = [("embed", nh_w4_matrix), ("mamba", C.POINTER(nh_mamba_weights)),
+                ("mlp", C.POINTER(nh_mlp_weights)), ("norm_f", C.c_void_p), ("lm_head", nh_w4_matrix),
+                ("function_head", nh_w4_matrix), ("function_weight", C.c_float)]
+
+
 _vp, _i, _l, _sz = C.c_void_p, C.c_int, C.c_long, C.c_size_t
 _sigs = {
     "nh_last_error": (C.c_char_p, []),
@@ -101,6 +111,8 @@ _sigs = {
     "nh_fused_embedding": (_i, [_vp, _vp, _vp, _vp, _i, C.c_float, _i, _vp, _vp]),
     "nh_mlp_workspace_bytes": (_sz, [_i, _i]),
     "nh_mlp_step": (_i, [_vp, _vp, _vp, C.c_float, _vp, _i, _vp, _i, _i, _vp, _sz, _vp]),
+    "nh_lm_workspace_bytes": (_sz, [_vp, _i, _i]),
+    "nh_lm_step": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
 }
 for _name, (_res, _args) in _sigs.items():
     _f = getattr(lib, _name)
@@ -174,6 +186,34 @@ def hybrid_pattern() -> str:
 
 def nh_w4_gemv(W, x, batch, residual, res_dtype, y, y_dtype, stream=None):
     _check(lib.nh_w4_gemv(C.byref(W), _ptr(x), batch, _ptr(residual), res_dtype, _ptr(y), y_dtype,
+                          _stream(stream)))
+
+
+def mlp_weights(norm_w, up: nh_w4_matrix, down: nh_w4_matrix) -> nh_mlp_weights:
+    w = nh_mlp_weights(_ptr(norm_w), up, down)
+    w._keep = (norm_w, up, down)
+    return w
+
+
+def lm_weights(embed: nh_w4_matrix, mamba: list, mlp: list, norm_f, lm_head: nh_w4_matrix,
+               function_head: nh_w4_matrix, function_weight: float = 2.0) -> nh_lm_weights:
+    """mamba: nh_mamba_weights per 'M' layer; mlp: nh_mlp_weights per '-' layer (pattern order)."""
+    ma = (nh_mamba_weights * len(mamba))(*mamba)
+    ml = (nh_mlp_weights * len(mlp))(*mlp)
+    w = nh_lm_weights(embed, ma, ml, _ptr(norm_f), lm_head, function_head, function_weight)
+    w._keep = (embed, mamba, mlp, ma, ml, norm_f, lm_head, function_head)
+    return w
+
+
+def nh_lm_workspace_bytes(d, inter, batch) -> int:
+    return lib.nh_lm_workspace_bytes(C.byref(d), inter, batch)
+
+
+def nh_lm_step(d, w, states, text_ids, function_ids, audio, audio_dtype, batch, hidden_out, text_out,
+               function_out, ws, ws_bytes, stream=None):
+    st = (nh_mamba_state * len(states))(*states)
+    _check(lib.nh_lm_step(C.byref(d), C.byref(w), st, _ptr(text_ids), _ptr(function_ids), _ptr(audio), audio_dtype,
+                          batch, _ptr(hidden_out), _ptr(text_out), _ptr(function_out), _ptr(ws), ws_bytes,
                           _stream(stream)))
 
 

@@ -5,6 +5,7 @@
 // synchronises the host.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -651,6 +652,99 @@ nh_status nh_mamba_stack(const nh_mamba_dims *d, const nh_mamba_weights *weights
                           outs + i * per, NH_F32, batch, ws, S(stream));
         if (s != NH_OK) return s;
     }
+    return ok();
+}
+
+static const int NH_N_MAMBA = 27, NH_N_MLP = 25;
+
+size_t nh_lm_workspace_bytes(const nh_mamba_dims *d, int inter, int batch)
+{
+    if (!d || batch < 1 || batch > 4 || nh_mlp_workspace_bytes(inter, batch) == 0) return 0;
+    size_t scratch = step_bytes(batch);
+    scratch = std::max(scratch, nh_mlp_workspace_bytes(inter, batch));
+    scratch = std::max(scratch, head_ws_bytes(batch));
+    Carve c{nullptr};
+    c.take<float>((size_t)batch * HIDDEN);
+    c.take<float>((size_t)batch * HIDDEN);
+    c.take<char>(scratch);
+    return c.off;
+}
+
+nh_status nh_lm_step(const nh_mamba_dims *d, const nh_lm_weights *w, nh_mamba_state *states,
+                     const int32_t *text_ids, const int32_t *function_ids, const void *audio, nh_dtype audio_dtype,
+                     int batch, float *hidden_out, int32_t *text_out, int32_t *function_out, void *ws,
+                     size_t ws_bytes, void *stream)
+{
+    NH_TRY(check_dims(d, false));
+    if (!w || !w->mamba || !w->mlp || !states)
+        return fail(NH_ERR_INVALID_ARGUMENT, "weights, their layer arrays and states must be non-NULL");
+    NH_TRY(check_w4(&w->embed, "embed"));
+    NH_TRY(check_w4(&w->lm_head, "lm_head"));
+    NH_TRY(check_w4(&w->function_head, "function_head"));
+    if (w->embed.k_in != HIDDEN || w->lm_head.k_in != HIDDEN || w->function_head.k_in != HIDDEN ||
+        w->lm_head.n_out > (1 << 19) || w->function_head.n_out > (1 << 19))
+        return fail(NH_ERR_UNSUPPORTED_SHAPE, "embedding and heads need k_in == %d and heads n_out <= 524288", HIDDEN);
+    NH_TRY(need_ptr(w->norm_f, "norm_f"));
+    if (!std::isfinite(w->function_weight)) return fail(NH_ERR_INVALID_ARGUMENT, "function_weight must be finite");
+    for (int i = 0; i < NH_N_MAMBA; ++i) {
+        NH_TRY(check_weights(&w->mamba[i]));
+        NH_TRY(check_state(&states[i], "state", true));
+    }
+    const int inter = w->mlp[0].up.n_out;
+    for (int i = 0; i < NH_N_MLP; ++i) {
+        const nh_mlp_weights &m = w->mlp[i];
+        NH_TRY(need_ptr(m.norm_w, "mlp norm_w"));
+        NH_TRY(check_w4(&m.up, "mlp up"));
+        NH_TRY(check_w4(&m.down, "mlp down"));
+        if (m.up.k_in != HIDDEN || m.down.n_out != HIDDEN || m.up.n_out != inter || m.down.k_in != inter)
+            return fail(NH_ERR_UNSUPPORTED_SHAPE, "mlp layer %d: up %d x %d, down %d x %d", i, m.up.n_out, m.up.k_in,
+                        m.down.n_out, m.down.k_in);
+    }
+    NH_TRY(need_ptr(text_ids, "text_ids"));
+    NH_TRY(need_ptr(function_ids, "function_ids"));
+    NH_TRY(need_ptr(audio, "audio"));
+    NH_TRY(need_dtype(audio_dtype, "audio_dtype"));
+    NH_TRY(opt_ptr(hidden_out, "hidden_out"));
+    NH_TRY(need_ptr(text_out, "text_out"));
+    NH_TRY(need_ptr(function_out, "function_out"));
+    NH_TRY(need_ptr(ws, "ws"));
+    if (batch < 1 || batch > 4) return fail(NH_ERR_UNSUPPORTED_SHAPE, "batch %d outside 1..4", batch);
+    const size_t need = nh_lm_workspace_bytes(d, inter, batch);
+    if (need == 0) return fail(NH_ERR_UNSUPPORTED_SHAPE, "mlp width %d", inter);
+    if (ws_bytes < need) return fail(NH_ERR_WORKSPACE_TOO_SMALL, "lm workspace %zu < %zu bytes", ws_bytes, need);
+
+    Carve c{reinterpret_cast<char *>(ws)};
+    float *cur = c.take<float>((size_t)batch * HIDDEN);
+    float *nxt = c.take<float>((size_t)batch * HIDDEN);
+    void *scratch = c.take<char>(1);
+    const hipStream_t s = S(stream);
+    NH_HIP(launch_fused_embed(view(&w->embed), text_ids, function_ids, audio, audio_dtype, w->function_weight, batch,
+                              cur, s),
+           "input row");
+    const char *pat = nh_hybrid_pattern();
+    int mi = 0, li = 0;
+    for (const char *p = pat; *p; ++p) {
+        if (*p == 'M') {
+            NH_TRY(block_step(d, &w->mamba[mi], &states[mi], cur, NH_F32, nxt, NH_F32, batch, scratch, s));
+            ++mi;
+        } else if (*p == '-') {
+            const nh_mlp_weights &m = w->mlp[li++];
+            uint16_t *h = reinterpret_cast<uint16_t *>(scratch);
+            NH_HIP(launch_mlp_up_step(view(&m.up), cur, F32, m.norm_w, d->eps, batch, h, s), "mlp up");
+            NH_HIP(launch_gemv(view(&m.down), h, batch, cur, F32, nxt, F32, s), "mlp down");
+        } else {
+            continue;  // attention: not part of this library, the stream passes through
+        }
+        std::swap(cur, nxt);
+    }
+    if (hidden_out)
+        NH_HIP(hipMemcpyAsync(hidden_out, cur, (size_t)batch * HIDDEN * sizeof(float), hipMemcpyDeviceToDevice, s),
+               "hidden copy");
+    NH_HIP(launch_head(view(&w->lm_head), cur, F32, w->norm_f, d->eps, batch, nullptr, text_out, scratch, s),
+           "lm_head");
+    NH_HIP(launch_head(view(&w->function_head), cur, F32, w->norm_f, d->eps, batch, nullptr, function_out, scratch,
+                       s),
+           "function_head");
     return ok();
 }
 

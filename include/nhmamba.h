@@ -252,6 +252,40 @@ nh_status nh_fused_embedding(const nh_w4_matrix *E, const int32_t *text_ids,
                              nh_dtype audio_dtype, float function_weight, int batch,
                              float *out, void *stream);
 
+/* One position of the language model (issue page, section "Network 2"): the
+ * fused input row, the layers of hybrid_override_pattern in order, norm_f,
+ * both heads and their greedy ids.  'M' layers run nh_mamba_block_step
+ * (state updated in place), '-' layers nh_mlp_step; the 4 attention layers
+ * ('*') are not part of this library and pass the stream through unchanged.
+ * The residual stream between layers is fp32. */
+typedef struct {
+    const uint16_t *norm_w;   /* bf16 [hidden] */
+    nh_w4_matrix up;          /* [inter][hidden] */
+    nh_w4_matrix down;        /* [hidden][inter] */
+} nh_mlp_weights;
+
+typedef struct {
+    nh_w4_matrix embed;                 /* [vocab][hidden]: embed_tokens */
+    const nh_mamba_weights *mamba;      /* host array, one per 'M' of the pattern (27) */
+    const nh_mlp_weights *mlp;          /* host array, one per '-' of the pattern (25) */
+    const uint16_t *norm_f;             /* bf16 [hidden] */
+    nh_w4_matrix lm_head, function_head; /* [vocab][hidden] each */
+    float function_weight;              /* function_channel_weight, 2.0 in the config */
+} nh_lm_weights;
+
+/* Workspace bytes of nh_lm_step for MLP width `inter` at this batch (0 on bad
+ * arguments). */
+size_t nh_lm_workspace_bytes(const nh_mamba_dims *d, int inter, int batch);
+/* states: host array, one per 'M' layer, updated in place.  text_ids,
+ * function_ids: int32 [batch] (the previous ids); audio: [batch][hidden] of
+ * audio_dtype; hidden_out: nullable f32 [batch][hidden] (the stream before
+ * norm_f); text_out, function_out: int32 [batch] (greedy ids as in
+ * nh_head_argmax).  batch 1..4; every pointer 16-byte aligned. */
+nh_status nh_lm_step(const nh_mamba_dims *d, const nh_lm_weights *w, nh_mamba_state *states,
+                     const int32_t *text_ids, const int32_t *function_ids, const void *audio,
+                     nh_dtype audio_dtype, int batch, float *hidden_out, int32_t *text_out,
+                     int32_t *function_out, void *ws, size_t ws_bytes, void *stream);
+
 /* Final norm, one output head and the greedy id for `batch` positions
  * (issue page, section "Network 2": after the last layer the hidden state
  * goes through norm_f, then through lm_head and function_head, both 4-bit

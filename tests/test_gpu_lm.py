@@ -1,0 +1,86 @@
+"""GPU parity of one language-model position (nh_lm_step) against a composition of the CPU
+oracle's functions, through the C ABI: the fused input row, the 27 Mamba2 blocks and 25 MLP
+layers in the order of the hybrid pattern (attention layers pass the stream through), norm_f
+and both heads with their greedy ids.  Two positions in a row, the second fed the first's
+ids as the pages' greedy loop does, so the carried block states are exercised too.
+
+Tolerances: the stream before norm_f is held to rel-L2 <= 5e-3 (the block bar; the 52 layers
+each add about 3e-5).  Ids are checked as in the head test: each GPU id must be the greedy id
+of the oracle's logits computed on the GPU's own stream, within 4e-3 of their maximum (a
+vocabulary of 1000 rows keeps the oracle heads quick)."""
+import numpy as np
+import pytest
+
+import synth
+
+pytestmark = pytest.mark.gpu
+
+VOCAB_T = 1000
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    import hybrid_mamba2_decode_amd as nh
+    import oracle
+    from tests import gpu_util as gu
+    oracle.build(force=False)
+    assert torch.cuda.is_available()
+    return nh, oracle, gu, torch
+
+
+def test_lm_step_two_positions(env):
+    nh, oracle, gu, torch = env
+    pat = nh.hybrid_pattern()
+    m_layers = [i for i, c in enumerate(pat) if c == "M"]
+    f_layers = [i for i, c in enumerate(pat) if c == "-"]
+    print("[case] lm step: layers", len(m_layers), "mamba", len(f_layers), "mlp", flush=True)
+    lws = [synth.layer_weights(l) for l in range(len(m_layers))]
+    mws = [synth.mlp_weights(l) for l in f_layers]
+    hw = synth.head_weights(seed=6, n_out=VOCAB_T)
+    E = synth.embed_tokens(seed=6, n_out=VOCAB_T)
+    mamba = [gu.layer_dev(lw) for lw in lws]
+    mlp = [nh.mlp_weights(gu.to_dev(mw.norm_w), gu.w4_dev(mw.up), gu.w4_dev(mw.down)) for mw in mws]
+    w = nh.lm_weights(gu.w4_dev(E), mamba, mlp, gu.to_dev(hw.norm_f), gu.w4_dev(hw.lm_head),
+                      gu.w4_dev(hw.function_head), 2.0)
+    d = nh.dims()
+    states = [gu.state_dev(np.zeros((1, 3, synth.CONV_DIM), np.uint16),
+                           np.zeros((1, 128, 80, 128), np.float32)) for _ in m_layers]
+    ws = gu.workspace(nh.nh_lm_workspace_bytes(d, synth.MLP_INTER, 1))
+    hid = gu.empty_f32(1, 4480)
+    t_out = torch.empty(1, dtype=torch.int32, device=gu.DEV)
+    f_out = torch.empty(1, dtype=torch.int32, device=gu.DEV)
+
+    o_cs = [np.zeros((1, 3, synth.CONV_DIM)) for _ in m_layers]
+    o_ss = [np.zeros((1, 128, 80, 128)) for _ in m_layers]
+    t_id, f_id = np.array([12], np.int32), np.array([12], np.int32)   # pad for the first position
+    for pos in range(2):
+        audio = synth.rng(6, 4000 + pos, 0).normal(0.0, 1.0, (1, 4480)).astype(np.float32)
+        nh.nh_lm_step(d, w, [s[0] for s in states], torch.tensor(t_id, device=gu.DEV),
+                      torch.tensor(f_id, device=gu.DEV), gu.to_dev(audio), nh.NH_F32, 1, hid, t_out, f_out,
+                      ws, ws.numel())
+        torch.cuda.synchronize()
+        # oracle: the same position through the oracle's functions, fp32 stream between layers
+        x = oracle.fused_embedding(E, t_id, f_id, audio.astype(np.float64)).astype(np.float32).astype(np.float64)
+        mi = li = 0
+        for c in pat:
+            if c == "M":
+                r = oracle.block(synth.REAL, lws[mi], x[:, None, :], o_cs[mi], o_ss[mi], stepwise=True)
+                o_cs[mi], o_ss[mi] = r.conv_state, r.ssm_state
+                x = r.out[:, 0].astype(np.float32).astype(np.float64)
+                mi += 1
+            elif c == "-":
+                x = oracle.mlp(x, mws[li].norm_w, mws[li].up, mws[li].down, 1e-5).astype(np.float32).astype(np.float64)
+                li += 1
+        got = hid.cpu().numpy().astype(np.float64)
+        r = gu.rel_l2(got, x)
+        print(f"[lm pos {pos}] stream rel-L2 {r:.3e}", flush=True)
+        assert r <= 5e-3
+        ids = []
+        for W, out in ((hw.lm_head, t_out), (hw.function_head, f_out)):
+            ref_l, _ = oracle.head(W, got, hw.norm_f, 1e-5)
+            gid = int(out.cpu().numpy()[0])
+            assert ref_l[0, gid] >= ref_l.max() - 4e-3, (gid, ref_l.max() - ref_l[0, gid])
+            ids.append(gid)
+        print(f"[lm pos {pos}] ids {ids}", flush=True)
+        t_id, f_id = np.array([ids[0]], np.int32), np.array([ids[1]], np.int32)
