@@ -84,3 +84,47 @@ def test_lm_step_two_positions(env):
             ids.append(gid)
         print(f"[lm pos {pos}] ids {ids}", flush=True)
         t_id, f_id = np.array([ids[0]], np.int32), np.array([ids[1]], np.int32)
+
+
+def test_lm_step_batch2_rows_match_batch1(env):
+    # two sessions in one call (batch-2 kernels) against each session alone (batch-1 kernels):
+    # both are held to the oracle bar, so the rows agree within twice it; ids must agree where
+    # the oracle's top two logits are apart by more than the head tolerance
+    nh, oracle, gu, torch = env
+    pat = nh.hybrid_pattern()
+    m_layers = [i for i, c in enumerate(pat) if c == "M"]
+    f_layers = [i for i, c in enumerate(pat) if c == "-"]
+    print("[case] lm step batch 2 vs batch 1", flush=True)
+    mamba = [gu.layer_dev(synth.layer_weights(l)) for l in range(len(m_layers))]
+    mws = [synth.mlp_weights(l) for l in f_layers]
+    mlp = [nh.mlp_weights(gu.to_dev(mw.norm_w), gu.w4_dev(mw.up), gu.w4_dev(mw.down)) for mw in mws]
+    hw = synth.head_weights(seed=7, n_out=VOCAB_T)
+    w = nh.lm_weights(gu.w4_dev(synth.embed_tokens(seed=7, n_out=VOCAB_T)), mamba, mlp, gu.to_dev(hw.norm_f),
+                      gu.w4_dev(hw.lm_head), gu.w4_dev(hw.function_head), 2.0)
+    d = nh.dims()
+    t_ids, f_ids, audio = synth.embed_inputs(8, 2, n_out=VOCAB_T)
+
+    def run(rows):
+        B = len(rows)
+        states = [gu.state_dev(np.zeros((B, 3, synth.CONV_DIM), np.uint16),
+                               np.zeros((B, 128, 80, 128), np.float32))[0] for _ in m_layers]
+        ws = gu.workspace(nh.nh_lm_workspace_bytes(d, synth.MLP_INTER, B))
+        hid = gu.empty_f32(B, 4480)
+        to = torch.empty(B, dtype=torch.int32, device=gu.DEV)
+        fo = torch.empty(B, dtype=torch.int32, device=gu.DEV)
+        nh.nh_lm_step(d, w, states, torch.tensor(t_ids[rows], device=gu.DEV), torch.tensor(f_ids[rows], device=gu.DEV),
+                      gu.to_dev(np.ascontiguousarray(audio[rows])), nh.NH_F32, B, hid, to, fo, ws, ws.numel())
+        torch.cuda.synchronize()
+        return hid.cpu().numpy().astype(np.float64), to.cpu().numpy(), fo.cpu().numpy()
+
+    h2, t2, f2 = run([0, 1])
+    for r in (0, 1):
+        h1, t1, f1 = run([r])
+        rel = gu.rel_l2(h2[r], h1[0])
+        print(f"[lm b2 row {r}] rel-L2 vs batch 1 {rel:.3e} ids {t2[r]},{f2[r]} vs {t1[0]},{f1[0]}", flush=True)
+        assert rel <= 1e-2
+        for W, a, b in ((hw.lm_head, t2[r], t1[0]), (hw.function_head, f2[r], f1[0])):
+            ref_l, _ = oracle.head(W, h1[:1], hw.norm_f, 1e-5)
+            top = np.sort(ref_l[0])[-2:]
+            if top[1] - top[0] > 8e-3:
+                assert a == b
