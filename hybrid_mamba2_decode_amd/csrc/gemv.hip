@@ -935,12 +935,19 @@ __global__ __launch_bounds__(NB == 1 ? 512 : 256, 1) void k_outproj_step(W4 W, c
 
 // Pre-norm + MLP up projection (K = hidden) + squared ReLU: the in_proj kernel's structure
 // with the activation as its epilogue.
+// At batch 1 the work-groups have 8 waves instead of in_proj's 12: the 15680 rows make 1960
+// blocks of 8, which 12-wave work-groups spread over only 168 CUs.
+template <int NB>
+struct MlpUpShape {
+    static constexpr int NT = NB == 1 ? 512 : InProjShape<NB>::NT;
+};
+
 template <int NB, int XT>
-__global__ __launch_bounds__(InProjShape<NB>::NT, 1) void k_mlp_up_step(W4 W, const void *__restrict__ x,
-                                                                    const uint16_t *__restrict__ nw, float eps,
-                                                                    EpiReluSq epi)
+__global__ __launch_bounds__(MlpUpShape<NB>::NT, 1) void k_mlp_up_step(W4 W, const void *__restrict__ x,
+                                                                   const uint16_t *__restrict__ nw, float eps,
+                                                                   EpiReluSq epi)
 {
-    constexpr int NT = InProjShape<NB>::NT, R = InProjShape<NB>::R;
+    constexpr int NT = MlpUpShape<NB>::NT, R = InProjShape<NB>::R;
     extern __shared__ __attribute__((aligned(16))) uint32_t act_lds[];
     __shared__ float red[NB][NT / 64];
     PreNorm<NB, XT, NT> pn;
@@ -1229,8 +1236,9 @@ hipError_t launch_mlp_up_step(const W4 &W, const void *x, int x_t, const uint16_
     const size_t lds = (size_t)batch * (HIDDEN / 32) * ACT_WORDS * 4;
 #define NH_LAUNCH(NB)                                                                                      \
     {                                                                                                      \
-        const int grid = inproj_grid<NB>(W.n);                                                             \
-        const dim3 blk(InProjShape<NB>::NT);                                                               \
+        constexpr int RW = InProjShape<NB>::RW, WPG = MlpUpShape<NB>::NT / 64;                             \
+        const int bx = ((W.n + RW - 1) / RW + 7) / 8, grid = 8 * ((bx + WPG - 1) / WPG);                   \
+        const dim3 blk(MlpUpShape<NB>::NT);                                                                \
         if (x_t == BF16)                                                                                   \
             launch_k(k_mlp_up_step<NB, BF16>, dim3(grid), blk, lds, st, W, x, norm_w, eps, e);             \
         else                                                                                               \
