@@ -134,6 +134,28 @@ def test_mlp_rejects_bad_arguments(nh):
     assert call(xt=5) == nh.NH_ERR_INVALID_ARGUMENT
 
 
+def test_lm_step_rejects_bad_arguments(nh):
+    A = 0x40000
+    d = nh.dims()
+    need = nh.nh_lm_workspace_bytes(d, 15680, 1)
+    assert need >= 2 * 4480 * 4 + nh.nh_mlp_workspace_bytes(15680, 1)
+    assert nh.nh_lm_workspace_bytes(d, 15680, 5) == 0 and nh.nh_lm_workspace_bytes(d, 100, 1) == 0
+    emb = _fake_w4(n=131072, k=4480)
+    m = nh.nh_mamba_weights(A, _fake_w4(n=22656, k=4480), A, A, A, A, A, A, _fake_w4(n=4480, k=10240))
+    f = nh.nh_mlp_weights(A, _fake_w4(n=15680, k=4480), _fake_w4(n=4480, k=15680))
+    w = nh.lm_weights(emb, [m] * 27, [f] * 25, A, emb, emb, 2.0)
+    st = [nh.nh_mamba_state(A, A)] * 27
+
+    def call(w=w, batch=1, ws_bytes=need, t=A):
+        return _status(lambda: nh.nh_lm_step(d, w, st, t, A, A, 0, batch, None, A, A, A, ws_bytes, 0))
+    assert call(batch=5) == nh.NH_ERR_UNSUPPORTED_SHAPE
+    assert call(ws_bytes=need - 1) == nh.NH_ERR_WORKSPACE_TOO_SMALL
+    assert call(t=None) == nh.NH_ERR_INVALID_ARGUMENT
+    bad_f = nh.nh_mlp_weights(A, _fake_w4(n=15680, k=4480), _fake_w4(n=4480, k=15616))
+    assert call(w=nh.lm_weights(emb, [m] * 27, [f] * 24 + [bad_f], A, emb, emb, 2.0)) == nh.NH_ERR_UNSUPPORTED_SHAPE
+    assert call(w=nh.lm_weights(emb, [m] * 27, [f] * 25, A, emb, emb, float("inf"))) == nh.NH_ERR_INVALID_ARGUMENT
+
+
 def test_gemm_workspace_check(nh):
     A = 0x20000
     need = nh.nh_w4_gemm_workspace_bytes(100, 128)
