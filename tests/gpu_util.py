@@ -72,3 +72,18 @@ def bf16_ulp_flips(gpu_bits: np.ndarray, ref: np.ndarray) -> int:
     """How many bf16 outputs differ from the oracle's value rounded to bf16."""
     import oracle
     return int(np.count_nonzero(np.asarray(gpu_bits, dtype=np.uint16) != oracle.to_bf16(ref)))
+
+
+def row_errors(got, ref, row: int = 80):
+    """Per-row view of a scan or block output, rows of `row` values (one (position, head) of
+    the scan's y, 80 channels).  Returns (worst row error relative to the row's own norm, with
+    the norm floored at a tenth of the RMS row norm so that near-zero rows do not divide by
+    ~0; max-abs error; max |ref|).  A wrong row gives a relative error near 1 here, whatever
+    the size of the tensor, where a whole-tensor rel-L2 would dilute it."""
+    g = np.asarray(got, dtype=np.float64).reshape(-1, row)
+    r = np.asarray(ref, dtype=np.float64).reshape(-1, row)
+    en = np.linalg.norm(g - r, axis=1)
+    rn = np.linalg.norm(r, axis=1)
+    floor = 0.1 * float(np.sqrt(np.mean(rn * rn)))
+    worst = float(np.max(en / np.maximum(rn, max(floor, 1e-300))))
+    return worst, float(np.max(np.abs(g - r))), float(np.max(np.abs(r)))
