@@ -160,6 +160,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--copies", type=int, default=27,
                     help="rotating weight+state sets (27: the stack's layers, 2.4 GB)")
+    ap.add_argument("--skip-step", action="store_true",
+                    help="skip the block-step legs (batch 1 and 4); the line then has no value (profiling runs)")
     ap.add_argument("--skip-seq", action="store_true", help="skip the batch-2 T=3750 scan and stack")
     ap.add_argument("--skip-stack", action="store_true", help="skip the 27-layer stacks")
     ap.add_argument("--skip-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -195,138 +197,142 @@ def main():
     d128 = nh.dims(chunk=128)
     out = {"metric": "Mamba2 block step us/layer (% HBM peak); SSD scan positions/s (% MFMA peak)"}
 
-    # ------------------------------------- block step, batch 1, pre-filled state
-    B = 1
-    x1 = gu.to_dev(synth.block_input(1, B, 1)[:, 0])
-    cs0, ss0 = synth.prefilled_state(1, B)
-    states = [gu.state_dev(cs0, ss0) for _ in range(args.copies)]
-    ws_step = gu.workspace(nh.nh_block_workspace_bytes(d128, B, 1, nh.NH_MODE_STEP))
-    o1 = gu.empty_f32(B, HID)
-
-    def step(i):
-        nh.nh_mamba_block_step(d128, dev_layers[i], states[i][0], x1, nh.NH_BF16, o1, nh.NH_F32, B,
-                               ws_step, ws_step.numel(), stream)
-
-    for i in range(args.warmup):
-        step(i % args.copies)
-    torch.cuda.synchronize()
     e0, e1 = hip.event(), hip.event()
-    hip.record(e0, stream)
-    t_wall = time.perf_counter()
-    for i in range(args.steps):
-        step(i % args.copies)
-    hip.record(e1, stream)
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t_wall) * 1e3
-    ms_total = hip.ms(e0, e1)
-    us_layer = ms_total * 1e3 / args.steps
-    log(f"block step: {us_layer:.2f} us/layer ({args.copies} rotating copies), host wall {wall_ms:.1f} ms")
+    B = 1
+    cs0, ss0 = synth.prefilled_state(1, B)           # the pre-filled state (also the CPU baseline's)
+    ws_step = gu.workspace(nh.nh_block_workspace_bytes(d128, B, 1, nh.NH_MODE_STEP))
+    total_bytes = sum(step_kernel_bytes(B))
+    if args.skip_step:
+        out["value"] = None
+    else:
+        # ------------------------------------- block step, batch 1, pre-filled state
+        x1 = gu.to_dev(synth.block_input(1, B, 1)[:, 0])
+        states = [gu.state_dev(cs0, ss0) for _ in range(args.copies)]
+        o1 = gu.empty_f32(B, HID)
 
-    # per-kernel durations of the block step (events between its three kernels)
-    nprof = min(args.steps, 400)
-    evs = [[hip.event() for _ in range(6)] for _ in range(nprof)]
-    for i in range(nprof):
-        nh.nh_profile_events(evs[i])
-        step(i % args.copies)
-    nh.nh_profile_events(None)
-    torch.cuda.synchronize()
-    kt = np.array([[hip.ms(e[2 * j], e[2 * j + 1]) for j in range(3)] for e in evs]) * 1e3  # us
-    k_avg = kt.mean(axis=0)
-    k_med = np.median(kt, axis=0)
-    for e in evs:
-        for x in e:
-            hip.destroy(x)
-    kb = step_kernel_bytes(B)
-    names = ["k_inproj_step<1, 0>", "k_ssm_step<true, 1>", "k_outproj_step<1>"]  # batch 1, bf16 input
-    kernels = [{"kernel": names[j], "avg_us": round(float(k_avg[j]), 3), "median_us": round(float(k_med[j]), 3),
-                "algorithmic_bytes": int(kb[j]), "GBps": round(kb[j] / (k_avg[j] * 1e-6) / 1e9, 1),
-                "hbm_frac": round(kb[j] / (k_avg[j] * 1e-6) / HBM_PEAK, 4)} for j in range(3)]
-    log("kernels:", kernels)
+        def step(i):
+            nh.nh_mamba_block_step(d128, dev_layers[i], states[i][0], x1, nh.NH_BF16, o1, nh.NH_F32, B,
+                                   ws_step, ws_step.numel(), stream)
 
-    # the dominant kernel alone (fused pre-norm / in_proj / conv step): back-to-back launches
-    # over the same rotating weight + state copies, two events around the loop
-    zb, xcb, dtb = gu.empty_u16(B, DI), gu.empty_u16(B, CD), gu.empty_u16(B, H)
+        for i in range(args.warmup):
+            step(i % args.copies)
+        torch.cuda.synchronize()
+        hip.record(e0, stream)
+        t_wall = time.perf_counter()
+        for i in range(args.steps):
+            step(i % args.copies)
+        hip.record(e1, stream)
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t_wall) * 1e3
+        ms_total = hip.ms(e0, e1)
+        us_layer = ms_total * 1e3 / args.steps
+        log(f"block step: {us_layer:.2f} us/layer ({args.copies} rotating copies), host wall {wall_ms:.1f} ms")
 
-    def inproj(i):
-        nh.nh_inproj_conv_step(d128, dev_layers[i], states[i][0], x1, nh.NH_BF16, zb, xcb, dtb, B, stream)
+        # per-kernel durations of the block step (events between its three kernels)
+        nprof = min(args.steps, 400)
+        evs = [[hip.event() for _ in range(6)] for _ in range(nprof)]
+        for i in range(nprof):
+            nh.nh_profile_events(evs[i])
+            step(i % args.copies)
+        nh.nh_profile_events(None)
+        torch.cuda.synchronize()
+        kt = np.array([[hip.ms(e[2 * j], e[2 * j + 1]) for j in range(3)] for e in evs]) * 1e3  # us
+        k_avg = kt.mean(axis=0)
+        k_med = np.median(kt, axis=0)
+        for e in evs:
+            for x in e:
+                hip.destroy(x)
+        kb = step_kernel_bytes(B)
+        names = ["k_inproj_step<1, 0>", "k_ssm_step<true, 1>", "k_outproj_step<1>"]  # batch 1, bf16 input
+        kernels = [{"kernel": names[j], "avg_us": round(float(k_avg[j]), 3), "median_us": round(float(k_med[j]), 3),
+                    "algorithmic_bytes": int(kb[j]), "GBps": round(kb[j] / (k_avg[j] * 1e-6) / 1e9, 1),
+                    "hbm_frac": round(kb[j] / (k_avg[j] * 1e-6) / HBM_PEAK, 4)} for j in range(3)]
+        log("kernels:", kernels)
 
-    for i in range(args.warmup):
-        inproj(i % args.copies)
-    hip.record(e0, stream)
-    for i in range(args.steps):
-        inproj(i % args.copies)
-    hip.record(e1, stream)
-    torch.cuda.synchronize()
-    dom_us = hip.ms(e0, e1) * 1e3 / args.steps
-    log(f"k_inproj_step alone: {dom_us:.2f} us per launch")
+        # the dominant kernel alone (fused pre-norm / in_proj / conv step): back-to-back launches
+        # over the same rotating weight + state copies, two events around the loop
+        zb, xcb, dtb = gu.empty_u16(B, DI), gu.empty_u16(B, CD), gu.empty_u16(B, H)
 
-    # cache-resident (single copy) figure, labelled
-    for i in range(args.warmup):
-        step(0)
-    hip.record(e0, stream)
-    for i in range(args.steps):
-        step(0)
-    hip.record(e1, stream)
-    torch.cuda.synchronize()
-    us_hot = hip.ms(e0, e1) * 1e3 / args.steps
+        def inproj(i):
+            nh.nh_inproj_conv_step(d128, dev_layers[i], states[i][0], x1, nh.NH_BF16, zb, xcb, dtb, B, stream)
 
-    total_bytes = sum(kb)
-    out.update({
-        "value": round(us_layer, 3), "unit": "us/layer", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(us_layer / 1e3, 6), "higher_is_better": False,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic (seeded; pages' shapes and distributions)",
-        "config": {"workload": "one Mamba2 block (hidden 4480, 128 heads x 80, state 128), batch 1, one "
-                               "cached step with a pre-filled state, timed over rotating weight/state copies",
-                   "batch": B, "hidden": HID, "heads": H, "head_dim": P, "d_state": N, "groups": G,
-                   "weights": "W4 group-64 affine (in_proj 22656x4480, out_proj 4480x10240)",
-                   "rotating_copies": args.copies},
-        "hbm_frac": round(total_bytes / (us_layer * 1e-6) / HBM_PEAK, 4),
-        "step_algorithmic_bytes": int(total_bytes),
-        "step_us_cache_resident": round(us_hot, 3),
-        "kernels": kernels,
-    })
-    dom = 0
-    out["roofline"] = {
-        "kernel": names[dom], "bound": "hbm",
-        "achieved": round(kb[dom] / (dom_us * 1e-6) / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-        "frac": round(kb[dom] / (dom_us * 1e-6) / HBM_PEAK, 4),
-        "traffic": traffic_from_profile(names[dom], "gemv.hip", "nh_device.hpp"),
-        "bytes_per_launch": int(kb[dom]), "avg_launch_us": round(dom_us, 3),
-        "timing": f"{args.steps} back-to-back launches over {args.copies} rotating weight/state copies, "
-                  "two HIP events on the launch stream",
-    }
+        for i in range(args.warmup):
+            inproj(i % args.copies)
+        hip.record(e0, stream)
+        for i in range(args.steps):
+            inproj(i % args.copies)
+        hip.record(e1, stream)
+        torch.cuda.synchronize()
+        dom_us = hip.ms(e0, e1) * 1e3 / args.steps
+        log(f"k_inproj_step alone: {dom_us:.2f} us per launch")
 
-    # --------------- batched step: 4 sessions share one weight stream (27 rotating copies)
-    B4s = 4
-    x4s = gu.to_dev(synth.block_input(1, B4s, 1)[:, 0])
-    cs4, ss4 = synth.prefilled_state(1, B4s)
-    st4 = [gu.state_dev(cs4, ss4) for _ in range(args.copies)]
-    ws4s = gu.workspace(nh.nh_block_workspace_bytes(d128, B4s, 1, nh.NH_MODE_STEP))
-    o4s = gu.empty_f32(B4s, HID)
+        # cache-resident (single copy) figure, labelled
+        for i in range(args.warmup):
+            step(0)
+        hip.record(e0, stream)
+        for i in range(args.steps):
+            step(0)
+        hip.record(e1, stream)
+        torch.cuda.synchronize()
+        us_hot = hip.ms(e0, e1) * 1e3 / args.steps
 
-    def step4(i):
-        nh.nh_mamba_block_step(d128, dev_layers[i], st4[i][0], x4s, nh.NH_BF16, o4s, nh.NH_F32, B4s, ws4s,
-                               ws4s.numel(), stream)
+        total_bytes = sum(kb)
+        out.update({
+            "value": round(us_layer, 3), "unit": "us/layer", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(us_layer / 1e3, 6), "higher_is_better": False,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded; pages' shapes and distributions)",
+            "config": {"workload": "one Mamba2 block (hidden 4480, 128 heads x 80, state 128), batch 1, one "
+                                   "cached step with a pre-filled state, timed over rotating weight/state copies",
+                       "batch": B, "hidden": HID, "heads": H, "head_dim": P, "d_state": N, "groups": G,
+                       "weights": "W4 group-64 affine (in_proj 22656x4480, out_proj 4480x10240)",
+                       "rotating_copies": args.copies},
+            "hbm_frac": round(total_bytes / (us_layer * 1e-6) / HBM_PEAK, 4),
+            "step_algorithmic_bytes": int(total_bytes),
+            "step_us_cache_resident": round(us_hot, 3),
+            "kernels": kernels,
+        })
+        dom = 0
+        out["roofline"] = {
+            "kernel": names[dom], "bound": "hbm",
+            "achieved": round(kb[dom] / (dom_us * 1e-6) / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+            "frac": round(kb[dom] / (dom_us * 1e-6) / HBM_PEAK, 4),
+            "traffic": traffic_from_profile(names[dom], "gemv.hip", "nh_device.hpp"),
+            "bytes_per_launch": int(kb[dom]), "avg_launch_us": round(dom_us, 3),
+            "timing": f"{args.steps} back-to-back launches over {args.copies} rotating weight/state copies, "
+                      "two HIP events on the launch stream",
+        }
 
-    for i in range(args.warmup):
-        step4(i % args.copies)
-    nb4 = max(args.steps // 4, 50)
-    hip.record(e0, stream)
-    for i in range(nb4):
-        step4(i % args.copies)
-    hip.record(e1, stream)
-    torch.cuda.synchronize()
-    us4 = hip.ms(e0, e1) * 1e3 / nb4
-    b4 = sum(step_kernel_bytes(B4s))
-    out["step_batch4"] = {
-        "workload": f"one Mamba2 block, {B4s} independent sessions per step (pre-filled states), "
-                    f"{args.copies} rotating weight/state copies",
-        "us_per_layer_step": round(us4, 3), "us_per_session_layer": round(us4 / B4s, 3),
-        "algorithmic_bytes": int(b4), "hbm_frac": round(b4 / (us4 * 1e-6) / HBM_PEAK, 4),
-    }
-    log("batch-4 step:", out["step_batch4"])
-    del st4, ws4s
+        # --------------- batched step: 4 sessions share one weight stream (27 rotating copies)
+        B4s = 4
+        x4s = gu.to_dev(synth.block_input(1, B4s, 1)[:, 0])
+        cs4, ss4 = synth.prefilled_state(1, B4s)
+        st4 = [gu.state_dev(cs4, ss4) for _ in range(args.copies)]
+        ws4s = gu.workspace(nh.nh_block_workspace_bytes(d128, B4s, 1, nh.NH_MODE_STEP))
+        o4s = gu.empty_f32(B4s, HID)
+
+        def step4(i):
+            nh.nh_mamba_block_step(d128, dev_layers[i], st4[i][0], x4s, nh.NH_BF16, o4s, nh.NH_F32, B4s, ws4s,
+                                   ws4s.numel(), stream)
+
+        for i in range(args.warmup):
+            step4(i % args.copies)
+        nb4 = max(args.steps // 4, 50)
+        hip.record(e0, stream)
+        for i in range(nb4):
+            step4(i % args.copies)
+        hip.record(e1, stream)
+        torch.cuda.synchronize()
+        us4 = hip.ms(e0, e1) * 1e3 / nb4
+        b4 = sum(step_kernel_bytes(B4s))
+        out["step_batch4"] = {
+            "workload": f"one Mamba2 block, {B4s} independent sessions per step (pre-filled states), "
+                        f"{args.copies} rotating weight/state copies",
+            "us_per_layer_step": round(us4, 3), "us_per_session_layer": round(us4 / B4s, 3),
+            "algorithmic_bytes": int(b4), "hbm_frac": round(b4 / (us4 * 1e-6) / HBM_PEAK, 4),
+        }
+        log("batch-4 step:", out["step_batch4"])
+        del st4, ws4s
 
     # ----------------------- MLP layer step, batch 1, over the model's 25 MLP layers' weights
     if not args.skip_heads:
