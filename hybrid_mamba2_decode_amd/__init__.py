@@ -36,7 +36,7 @@ EXPORTS = (
     "nh_last_error", "nh_version", "nh_hybrid_pattern", "nh_profile_events",
     "nh_w4_gemv", "nh_w4_gemm_workspace_bytes", "nh_w4_gemm", "nh_rmsnorm", "nh_inproj_conv_step",
     "nh_conv1d_step", "nh_conv1d_seq", "nh_ssm_step", "nh_ssd_scan_workspace_bytes", "nh_ssd_chunk_scan",
-    "nh_rmsnorm_gated", "nh_block_workspace_bytes", "nh_mamba_block_step", "nh_mamba_block_seq",
+    "nh_rmsnorm_gated", "nh_block_workspace_bytes", "nh_mamba_block_step", "nh_mamba_block_step_noalloc", "nh_mamba_block_seq",
     "nh_mamba_stack", "nh_head_workspace_bytes", "nh_head_argmax", "nh_fused_embedding",
     "nh_mlp_workspace_bytes", "nh_mlp_step", "nh_lm_workspace_bytes", "nh_lm_step",
 )
@@ -103,6 +103,7 @@ _sigs = {
     "nh_rmsnorm_gated": (_i, [_vp, _vp, _l, _vp, _vp, _i, _i, _i, C.c_float, _vp]),
     "nh_block_workspace_bytes": (_sz, [_vp, _i, _i, _i]),
     "nh_mamba_block_step": (_i, [_vp, _vp, _vp, _vp, _i, _vp, _i, _i, _vp, _sz, _vp]),
+    "nh_mamba_block_step_noalloc": (_i, [_vp, _vp, _vp, _vp, _i, _vp, _i, _i, _vp]),
     "nh_mamba_block_seq": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _i, _i, _vp, _sz, _vp]),
     "nh_mamba_stack": (_i, [_vp, _vp, _vp, _i, _i, _vp, _i, _i, _vp, _i, _vp, _sz, _vp]),
     "nh_profile_events": (_i, [_vp, _i]),
@@ -297,6 +298,11 @@ def nh_inproj_conv_step(d, w, state, x, x_dtype, z, xc, dt_raw, batch, stream=No
 def nh_mamba_block_step(d, w, state, x, x_dtype, out, out_dtype, batch, ws, ws_bytes, stream=None):
     _check(lib.nh_mamba_block_step(C.byref(d), C.byref(w), C.byref(state), _ptr(x), x_dtype,
                                    _ptr(out), out_dtype, batch, _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def nh_mamba_block_step_noalloc(d, w, state, x, x_dtype, out, out_dtype, batch, stream=None):
+    _check(lib.nh_mamba_block_step_noalloc(C.byref(d), C.byref(w), C.byref(state), _ptr(x), x_dtype,
+                                           _ptr(out), out_dtype, batch, _stream(stream)))
 
 
 def nh_mamba_block_seq(d, w, init, final_state, x, x_dtype, T, out, out_dtype, batch, ws, ws_bytes,

@@ -576,6 +576,30 @@ nh_status nh_mamba_block_step(const nh_mamba_dims *d, const nh_mamba_weights *w,
     return block_step(d, w, state, x, x_dtype, out, out_dtype, batch, ws, S(stream));
 }
 
+nh_status nh_mamba_block_step_noalloc(const nh_mamba_dims *d, const nh_mamba_weights *w, nh_mamba_state *state,
+                                      const void *x, nh_dtype x_dtype, void *out, nh_dtype out_dtype, int batch,
+                                      void *stream)
+{
+    NH_TRY(check_dims(d, false));
+    NH_TRY(check_weights(w));
+    NH_TRY(check_state(state, "state", true));
+    NH_TRY(need_ptr(x, "x"));
+    NH_TRY(need_ptr(out, "out"));
+    NH_TRY(need_dtype(x_dtype, "x_dtype"));
+    NH_TRY(need_dtype(out_dtype, "out_dtype"));
+    if (batch < 1 || batch > 4)
+        return fail(NH_ERR_UNSUPPORTED_SHAPE, "batch %d outside 1..4 (the allocation-free scratch holds the "
+                    "step workspace of at most 4 sequences)", batch);
+    if (x == out) return fail(NH_ERR_INVALID_ARGUMENT, "out may not alias x");
+    void *scr = nullptr;
+    size_t cap = 0;
+    NH_HIP(noalloc_scratch(&scr, &cap), "allocation-free scratch lookup");
+    if (step_bytes(batch) > cap)
+        return fail(NH_ERR_WORKSPACE_TOO_SMALL, "step workspace %zu exceeds the allocation-free scratch (%zu bytes)",
+                    step_bytes(batch), cap);
+    return block_step(d, w, state, x, x_dtype, out, out_dtype, batch, scr, S(stream));
+}
+
 nh_status nh_inproj_conv_step(const nh_mamba_dims *d, const nh_mamba_weights *w, nh_mamba_state *state,
                               const void *x, nh_dtype x_dtype, uint16_t *z, uint16_t *xc, uint16_t *dt_raw,
                               int batch, void *stream)

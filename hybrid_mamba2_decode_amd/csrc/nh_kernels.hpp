@@ -41,6 +41,9 @@ struct W4 {
 };
 
 // ---- step mode (step.hip)
+// Device address and size of this device's allocation-free scratch array (looked up once per
+// device with hipGetSymbolAddress; the current device is the caller's).
+hipError_t noalloc_scratch(void **ptr, size_t *bytes);
 hipError_t launch_gemv(const W4 &W, const uint16_t *x, int batch, const void *res, int res_t,
                        void *y, int y_t, hipStream_t st);
 // Fused: RMSNorm(x) -> in_proj GEMV -> split; xBC rows go through the conv step (state

@@ -5,10 +5,44 @@
 // hundred MFLOP.  The kernels therefore aim at coalesced 128-bit loads of every weight byte
 // exactly once, with the dequantisation folded into a packed bf16 dot product and all other
 // work (pre-norm, conv, discretisation, gated norm, residual) fused into the streaming kernels.
+#include <mutex>
+
 #include "nh_device.hpp"
 #include "nh_kernels.hpp"
 
 namespace nh {
+
+// ============================================================ allocation-free scratch
+//
+// The block step's workspace (z, xc, dt_raw, g w and the gated-norm partial sums) for callers
+// that cannot allocate: one file-scope device array, which every GPU the library runs on holds
+// until the process ends.  Host code never passes the array's name to a kernel (on the host it
+// is only a stand-in for the symbol): the device address comes from hipGetSymbolAddress, once
+// per device with that device current, and is kept per device.
+constexpr size_t NOALLOC_SCRATCH_BYTES = 352u << 10;  // >= the batch-4 step workspace
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+hipError_t noalloc_scratch(void **ptr, size_t *bytes)
+{
+    constexpr int MAXDEV = 64;
+    static std::mutex mu;
+    static void *addr[MAXDEV] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= MAXDEV) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    *bytes = NOALLOC_SCRATCH_BYTES;
+    return hipSuccess;
+}
 
 // ============================================================================ SSM step
 //

@@ -331,6 +331,22 @@ nh_status nh_mamba_block_step(const nh_mamba_dims *d, const nh_mamba_weights *w,
                               void *out, nh_dtype out_dtype, int batch,
                               void *ws, size_t ws_bytes, void *stream);
 
+/* nh_mamba_block_step for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Same computation, kernels and results as nh_mamba_block_step,
+ * but the step workspace is the library's own file-scope device array
+ * (352 KiB per GPU, held until the process ends), so no workspace argument
+ * is taken and nothing is allocated or freed.  Every call on one GPU shares
+ * that GPU's array: calls that can overlap on one GPU (two streams, two
+ * threads) race and must be serialised by the caller.  The array keeps the
+ * last call's contents; nothing in it has to start at zero.  batch 1..4
+ * (NH_ERR_UNSUPPORTED_SHAPE above that, the array's limit); other errors as
+ * nh_mamba_block_step; NH_ERR_HIP if the array's address cannot be looked up
+ * on the current device. */
+nh_status nh_mamba_block_step_noalloc(const nh_mamba_dims *d, const nh_mamba_weights *w,
+                                      nh_mamba_state *state, const void *x, nh_dtype x_dtype,
+                                      void *out, nh_dtype out_dtype, int batch, void *stream);
+
 /* The whole block over T positions (full-history recompute) with the same
  * storage points.  init: nullable (NULL = zero conv and SSM state);
  * final_state: nullable, receives the state after position T-1 (its

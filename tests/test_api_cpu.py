@@ -194,6 +194,24 @@ def test_block_dims_and_workspace_checks(nh):
                                              step_ws, 0)) == nh.NH_ERR_UNSUPPORTED_SHAPE
 
 
+def test_noalloc_step_checks(nh):
+    """The allocation-free step validates like the workspace step, and rejects batches beyond
+    its scratch array's limit, before any device call."""
+    A = 0x40000
+    d = nh.dims(chunk=128)
+    lw = nh.mamba_weights(A, _fake_w4(22656, 4480), A, A, A, A, A, A, _fake_w4(4480, 10240))
+    st = nh.mamba_state(A, A)
+    for b in (0, 5):
+        assert _status(lambda: nh.nh_mamba_block_step_noalloc(d, lw, st, A, 0, A + 0x100, 0, b, 0)) == \
+            nh.NH_ERR_UNSUPPORTED_SHAPE
+    assert _status(lambda: nh.nh_mamba_block_step_noalloc(d, lw, st, A, 0, A, 0, 1, 0)) == \
+        nh.NH_ERR_INVALID_ARGUMENT  # out aliases x
+    assert _status(lambda: nh.nh_mamba_block_step_noalloc(nh.dims(head_dim=64), lw, st, A, 0, A + 0x100, 0, 1,
+                                                          0)) == nh.NH_ERR_UNSUPPORTED_SHAPE
+    assert _status(lambda: nh.nh_mamba_block_step_noalloc(d, lw, st, A + 8, 0, A + 0x100, 0, 1, 0)) == \
+        nh.NH_ERR_MISALIGNED
+
+
 def test_primitive_checks(nh):
     A = 0x40000
     d = nh.dims(chunk=64)
