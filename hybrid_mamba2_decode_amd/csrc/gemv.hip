@@ -317,7 +317,10 @@ struct GemvRunner {
 
     // threads: the work-group size, a compile-time constant at every call site (blockDim would
     // be a load from the dispatch arguments whose wait also covers every load issued before it)
-    __device__ __forceinline__ GemvRunner(const W4 &W_, const Epi &epi_, int threads) : W(W_), epi(epi_)
+    // issue_now false: the first stage is left for issue_first() (a caller whose wave has other
+    // loads to receive first)
+    __device__ __forceinline__ GemvRunner(const W4 &W_, const Epi &epi_, int threads, bool issue_now = true)
+        : W(W_), epi(epi_)
     {
         const int lane = threadIdx.x & 63;
         sub = lane / LPR;
@@ -353,6 +356,11 @@ struct GemvRunner {
         // unconditional (rows past the matrix read zero through the buffer range check): a
         // branch here would make the compiler's wait before the first use of any earlier load
         // also cover this stage's loads
+        if (issue_now) issue_first();
+    }
+
+    __device__ __forceinline__ void issue_first()
+    {
         load_stage<RG, CPL>(A, rq, rs, rb, qoff, soff, (uint32_t)min(n0, W.n), RPG, rowbytes, kg2);
         pa = epi.prefetch(min(n0 + er * RPG + sub, W.n - 1), eb);
     }
@@ -894,43 +902,65 @@ __global__ __launch_bounds__(NB == 1 ? 512 : 256, 1) void k_outproj_step(W4 W, c
         }
         make_chunk(v, act_lds + (size_t)it * ACT_WORDS);
     };
-    // The prologue's loads go out alone, and the weight stream starts only once the work-group
-    // has them (after the first barrier; issued together, they would queue behind every wave's
-    // weight loads): one per-(head, half) sum of squares per thread, 32 of which make a group,
-    // and, with at most one chunk per thread (batch 1: 320 chunks, 512 threads), the chunk's
-    // g w values.
-    constexpr bool ONE = NB * NCH <= NT;
     constexpr int NPART = NHEADS * 2;  // per batch row
-    float4 gv0[8];
-    float pv[(NB * NPART + NT - 1) / NT];
+    if constexpr (NB == 1) {
+        // The prologue's loads go out alone on waves 0..3 (one per-(head, half) sum of squares
+        // per thread, 32 of which make a group, and the chunks' g w values: chunks t and t + 256);
+        // waves 4..7 issue their first weight stage at once, so their rows stream while the
+        // activations are built.  Waves 0..3 start streaming after the first barrier: issued
+        // together, the prologue loads would queue behind their weight loads.
+        constexpr int PW = 256, GC = (NCH + PW - 1) / PW;
+        const bool early = threadIdx.x >= PW;
+        GemvRunner<LPR, CPL, NB, RG, EpiStore> run(W, epi, NT, early);
+        float4 gv0[GC][8];
+        if (!early) {
+            const float pv = part[threadIdx.x];
 #pragma unroll
-    for (int i = 0; i < (NB * NPART + NT - 1) / NT; ++i) {
-        const int t = threadIdx.x + NT * i;
-        pv[i] = t < NB * NPART ? part[t] : 0.f;
-    }
-    if (ONE && (int)threadIdx.x < NB * NCH) load(threadIdx.x, gv0);
+            for (int k = 0; k < GC; ++k) load(min((int)threadIdx.x + PW * k, NCH - 1), gv0[k]);
+            const float tot = row_sum<32>(pv);  // 32 consecutive entries = one group
+            if ((threadIdx.x & 31) == 0) rstd[0][threadIdx.x / 32] = 1.0f / sqrtf(tot / (float)GNORM + eps);
+        }
+        __syncthreads();
+        if (!early) {
+            run.issue_first();
 #pragma unroll
-    for (int i = 0; i < (NB * NPART + NT - 1) / NT; ++i) {
-        const int t = threadIdx.x + NT * i;  // 32 consecutive entries = one group of one row
-        const float tot = row_sum<32>(pv[i]);
-        if (t < NB * NPART && (t & 31) == 0) rstd[t / NPART][(t % NPART) / 32] = 1.0f / sqrtf(tot / (float)GNORM + eps);
-    }
-    __builtin_amdgcn_s_waitcnt(0);  // the g w loads too
-    __syncthreads();
-    GemvRunner<LPR, CPL, NB, RG, EpiStore> run(W, epi, NT);
-    if (ONE) {
-        if ((int)threadIdx.x < NB * NCH) build(threadIdx.x, gv0);
+            for (int k = 0; k < GC; ++k)
+                if ((int)threadIdx.x + PW * k < NCH) build(threadIdx.x + PW * k, gv0[k]);
+        }
+        __syncthreads();
+        ActChunk a[NB][CPL];
+        act_from_lds<LPR, CPL, NB>(a, act_lds, NCH, (threadIdx.x & 63) % LPR);
+        run.run(a);
     } else {
+        // The prologue's loads go out alone, and the weight stream starts only once the
+        // work-group has them (after the first barrier; issued together, they would queue behind
+        // every wave's weight loads).
+        constexpr int NPI = (NB * NPART + NT - 1) / NT;
+        float pv[NPI];
+#pragma unroll
+        for (int i = 0; i < NPI; ++i) {
+            const int t = threadIdx.x + NT * i;
+            pv[i] = t < NB * NPART ? part[t] : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < NPI; ++i) {
+            const int t = threadIdx.x + NT * i;  // 32 consecutive entries = one group of one row
+            const float tot = row_sum<32>(pv[i]);
+            if (t < NB * NPART && (t & 31) == 0) rstd[t / NPART][(t % NPART) / 32] = 1.0f / sqrtf(tot / (float)GNORM + eps);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        GemvRunner<LPR, CPL, NB, RG, EpiStore> run(W, epi, NT);
         for (int it = threadIdx.x; it < NB * NCH; it += NT) {
             float4 gv[8];
             load(it, gv);
             build(it, gv);
         }
+        __syncthreads();
+        ActChunk a[NB][CPL];
+        act_from_lds<LPR, CPL, NB>(a, act_lds, NCH, (threadIdx.x & 63) % LPR);
+        run.run(a);
     }
-    __syncthreads();
-    ActChunk a[NB][CPL];
-    act_from_lds<LPR, CPL, NB>(a, act_lds, NCH, (threadIdx.x & 63) % LPR);
-    run.run(a);
 }
 
 // Pre-norm + MLP up projection (K = hidden) + squared ReLU: the in_proj kernel's structure
