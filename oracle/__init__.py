@@ -19,6 +19,9 @@ with gcc, wraps it with ctypes and adds these numpy-level pieces:
   and the audio frame.
 * ``mlp`` -- one MLP layer of the hybrid stack (pre-norm, 4-bit up, squared ReLU,
   4-bit down, residual).
+* ``attention_core`` and ``attention`` -- one grouped-query attention layer of the hybrid
+  stack at one position with its key/value cache (pre-norm, 4-bit q/k/v, softmax attention
+  over the cached and the new position, 4-bit o, residual).
 
 Readings of the pages that the oracle fixes (no mixer equations are printed
 on the pages; see the header of nh_oracle.c):
@@ -224,6 +227,62 @@ def mlp(x, norm_w, W_up, W_down, eps: float, mode: int = CONTRACT) -> np.ndarray
     if mode == CONTRACT:
         h = round_bf16(h)
     return x2 + w4_matvec(W_down, h)
+
+
+def attention_core(q, K, V, n_kv: int) -> np.ndarray:
+    """Softmax attention of one query position per head over T key/value positions, with
+    query heads grouped onto key/value heads (grouped-query attention).
+
+    The issue page "feat(nemotron_voicechat): ... offline duplex inference #1374", section
+    "config.json": num_attention_heads 40, num_key_value_heads 8, head_dim 128.  Query head h
+    reads key/value head h // (heads / n_kv) (consecutive query heads share one key/value
+    head), scores are q . k / sqrt(head_dim), and the weights are the softmax of the scores over
+    all T positions (the query sits at the last position, so every cached position is visible).
+    q: [heads][hd]; K, V: [n_kv][T][hd] (doubles).  Returns o [heads][hd] in fp64."""
+    q, K, V = _d(q), _d(K), _d(V)
+    heads, hd = q.shape
+    rep = heads // n_kv
+    o = np.empty((heads, hd))
+    for h in range(heads):
+        g = h // rep
+        s = K[g] @ q[h] / np.sqrt(hd)        # [T]
+        w = np.exp(s - s.max())
+        w /= w.sum()
+        o[h] = w @ V[g]
+    return o
+
+
+def attention(x, aw, k_cache, v_cache, eps: float, mode: int = CONTRACT):
+    """One attention layer of the hybrid stack at one position per sequence, with its cache.
+
+    The '*' layers of hybrid_override_pattern (issue page, section "config.json": attention at
+    layers 14, 21, 30, 39, attention_bias false; q/k/v/o are Nemotron-H mixer projections and
+    so 4-bit group-64 like the others).  No positional encoding enters (text_config names none):
+        u = RMSNorm(x) w,  q = W_q u,  k = W_k u,  v = W_v u,
+        o = attention_core(q, [K_cache; k], [V_cache; v]),  out = x + W_o o.
+    The docs page "Nemotron VoiceChat", section "Online session": the attention key/value
+    caches persist across positions; the new position's k and v are appended to them.
+    CONTRACT rounds u, q, k, v and o to bf16 (the points where the GPU kernels store them).
+    x: [m][hidden]; k_cache, v_cache: [m][n_kv][T][hd] doubles (T may be 0).
+    Returns (out [m][hidden], k_new [m][n_kv][hd], v_new [m][n_kv][hd])."""
+    x2 = _d(x).reshape(-1, aw.q_proj.k_in)
+    m = x2.shape[0]
+    kc, vc = _d(k_cache), _d(v_cache)
+    n_kv = kc.shape[1]
+    hd = kc.shape[3]
+    heads = aw.q_proj.n_out // hd
+    rnd = round_bf16 if mode == CONTRACT else (lambda a: a)
+    u = rnd(rmsnorm(x2, aw.norm_w, eps))
+    q = rnd(w4_matvec(aw.q_proj, u)).reshape(m, heads, hd)
+    k = rnd(w4_matvec(aw.k_proj, u)).reshape(m, n_kv, hd)
+    v = rnd(w4_matvec(aw.v_proj, u)).reshape(m, n_kv, hd)
+    o = np.empty((m, heads * hd))
+    for r in range(m):
+        K = np.concatenate([kc[r], k[r][:, None, :]], axis=1)
+        V = np.concatenate([vc[r], v[r][:, None, :]], axis=1)
+        o[r] = attention_core(q[r], K, V, n_kv).reshape(-1)
+    o = rnd(o)
+    return x2 + w4_matvec(aw.o_proj, o), k, v
 
 
 def fused_embedding(E, text_ids, function_ids, audio, function_weight: float = 2.0) -> np.ndarray:

@@ -20,6 +20,9 @@ Distributions (the workload recipe, identical for every consumer):
       1 + N(0, 0.05^2) (all bf16);
   block input x ~ N(0, 1) (bf16); pre-filled conv state ~ N(0, 1) (bf16);
   pre-filled SSM state ~ N(0, 0.1^2) (float32);
+  attention layers (the '*' layers): norm weight 1 + N(0, 0.05^2) (bf16); q_proj
+      (5120 x 4480), k_proj, v_proj (1024 x 4480 each) and o_proj (4480 x 5120) drawn like
+      in_proj; a pre-filled KV cache ~ N(0, 1.3^2) (bf16), the magnitude of k = W_k u;
   output heads (lm_head, function_head, 131072 x 4480 each, the vocab_size of the
       same config) and the input embedding embed_tokens (same shape): drawn like in_proj;
       norm_f ~ 1 + N(0, 0.05^2) (bf16); previous text / function ids ~ U{0..131071};
@@ -61,6 +64,10 @@ _T_EMB_Q, _T_EMB_S = 16, 17
 _T_MLP_NORM, _T_UP_Q, _T_UP_S, _T_DOWN_Q, _T_DOWN_S = 20, 21, 22, 23, 24
 MLP_INTER = 15680
 _I_AUDIO, _I_IDS = 3, 4
+# attention layers: 40 query heads and 8 key/value heads of 128 (text_config)
+ATT_HEADS, ATT_KV_HEADS, ATT_HEAD_DIM = 40, 8, 128
+_T_ATT_NORM, _T_Q_Q, _T_Q_S, _T_K_Q, _T_K_S, _T_V_Q, _T_V_S, _T_O_Q, _T_O_S = 30, 31, 32, 33, 34, 35, 36, 37, 38
+_I_KV = 5
 VOCAB = 131072
 
 
@@ -197,6 +204,38 @@ def mlp_weights(layer: int, seed: int = 0, inter: int = MLP_INTER, d: Dims = REA
     sb = f32_to_bf16(s32)
     bb = f32_to_bf16(bf16_to_f32(sb) * np.float32(-8.0))
     return MlpWeights(norm_w, up, W4Matrix(dq, sb, bb, d.hidden, inter, d.group_size))
+
+
+@dataclass
+class AttentionWeights:
+    norm_w: np.ndarray      # bf16 [hidden]
+    q_proj: W4Matrix        # [heads * head_dim][hidden]
+    k_proj: W4Matrix        # [kv_heads * head_dim][hidden]
+    v_proj: W4Matrix        # [kv_heads * head_dim][hidden]
+    o_proj: W4Matrix        # [hidden][heads * head_dim]
+
+
+def attention_weights(layer: int, seed: int = 0, d: Dims = REAL) -> AttentionWeights:
+    """One attention layer ('*' of the pattern): norm weight 1 + N(0, 0.05^2); q, k, v and o
+    projections drawn like in_proj (q U{0..15}, scales U(0.002, 0.006), bias -8 scale)."""
+    g = rng(seed, layer, _T_ATT_NORM)
+    norm_w = f32_to_bf16(1.0 + g.normal(0.0, 0.05, d.hidden).astype(np.float32))
+    qd, kd = ATT_HEADS * ATT_HEAD_DIM, ATT_KV_HEADS * ATT_HEAD_DIM
+    return AttentionWeights(norm_w,
+                            w4_random(seed, layer, _T_Q_Q, _T_Q_S, qd, d.hidden, d.group_size),
+                            w4_random(seed, layer, _T_K_Q, _T_K_S, kd, d.hidden, d.group_size),
+                            w4_random(seed, layer, _T_V_Q, _T_V_S, kd, d.hidden, d.group_size),
+                            w4_random(seed, layer, _T_O_Q, _T_O_S, d.hidden, qd, d.group_size))
+
+
+def kv_cache(stream: int, batch: int, T: int, seed: int = 0):
+    """A pre-filled KV cache of T positions: keys and values ~ N(0, 1.3^2) rounded to bf16,
+    layout [batch][kv_heads][T][head_dim] (uint16 bits) each."""
+    g = rng(seed, 1000 + stream, _I_KV)
+    shape = (batch, ATT_KV_HEADS, T, ATT_HEAD_DIM)
+    k = g.normal(0.0, 1.3, shape).astype(np.float32)
+    v = g.normal(0.0, 1.3, shape).astype(np.float32)
+    return f32_to_bf16(k), f32_to_bf16(v)
 
 
 def embed_tokens(seed: int = 0, n_out: int = VOCAB, d: Dims = REAL) -> W4Matrix:
