@@ -14,8 +14,9 @@ Also measured in the same run, each in its own object of the JSON line:
   * the 27-layer stack stepwise over T = 413 at batch 1, and the 27-layer full-history
     stack at batch 2, T = 3750, chunk 256;
   * the block step with 4 sessions sharing one weight stream;
-  * one MLP layer step (the hybrid stack's other layer kind), over the 25 MLP layers' weights,
-    and one whole language-model position (input row, Mamba2 and MLP layers, both heads);
+  * one MLP layer step and one attention layer step (the hybrid stack's other layer kinds),
+    over the 25 MLP and 4 attention layers' weights, and one whole language-model position
+    (input row, all 56 layers, both heads);
   * the final norm + both output heads (W4 131072 x 4480 each) + greedy ids at batch 1,
     and the fused input row (two W4 embedding rows + the audio frame);
   * the CPU oracle on the host cores (a bounded sample of the batch-1 block step), as a
@@ -370,15 +371,74 @@ def main():
         }
         log("mlp step:", out["mlp_step"])
 
-        # one language-model position: input row, 27 Mamba2 + 25 MLP layers in pattern order
-        # (attention layers pass the stream through), norm_f, both heads and greedy ids
+        # one attention layer at batch 1 over a cache of T_att earlier positions (the 33 s
+        # timeline, and the 5 min one), rotating over the 4 attention layers' weights and caches
+        t0 = time.time()
+        atts = []
+        for l in pattern_layers("*"):
+            aw = synth.attention_weights(l)
+            atts.append(nh.attention_weights(gu.to_dev(aw.norm_w), gu.w4_dev(aw.q_proj), gu.w4_dev(aw.k_proj),
+                                             gu.w4_dev(aw.v_proj), gu.w4_dev(aw.o_proj)))
+            del aw
+        log(f"{len(atts)} attention layers ready in {time.time() - t0:.1f} s")
+        att_w_bytes = w4_bytes(5120, HID) + 2 * w4_bytes(1024, HID) + w4_bytes(HID, 5120) + 2 * HID
+        wsa_n = nh.nh_attention_workspace_bytes(1)
+        wsa = gu.workspace(wsa_n)
+        xa = gu.to_dev(np.random.default_rng(79).normal(0, 1, (1, HID)).astype(np.float32))
+        oa = gu.empty_f32(1, HID)
+        att_out = {}
+        for T_att in (413, 3750):
+            caches = []
+            for a in range(len(atts)):
+                kk, vv = synth.kv_cache(40 + a, 1, T_att + 1)
+                caches.append(nh.kv_cache(gu.to_dev(kk), gu.to_dev(vv), T_att + 1))
+            pos_a = torch.tensor([T_att], dtype=torch.int32, device="cuda")
+
+            def att_step(i):
+                j = i % len(atts)
+                nh.nh_attention_step(atts[j], caches[j], pos_a, xa, nh.NH_F32, oa, nh.NH_F32, 1, 1e-5, wsa, wsa_n,
+                                     stream)
+
+            for i in range(50):
+                att_step(i)
+            na = 500
+            hip.record(e0, stream)
+            for i in range(na):
+                att_step(i)
+            hip.record(e1, stream)
+            torch.cuda.synchronize()
+            us_a = hip.ms(e0, e1) * 1e3 / na
+            ab = (att_w_bytes + 2 * (T_att + 1) * 8 * 128 * 2     # weights; k and v cache rows read
+                  + 2 * 8 * 128 * 2 + 4 * HID * 2)               # new k, v rows; x read, out written
+            att_out[f"cache_{T_att}"] = {
+                "us_per_layer_step": round(us_a, 3), "algorithmic_bytes": int(ab),
+                "hbm_frac": round(ab / (us_a * 1e-6) / HBM_PEAK, 4),
+            }
+            del caches
+        out["attention_step"] = {
+            "workload": "one attention layer (pre-norm, W4 q/k/v 4480->5120/1024/1024, k/v appended to the cache, "
+                        "40-head grouped-query attention over the 8 key/value heads of 128, W4 o_proj 5120->4480, "
+                        "residual), batch 1, over a cache of 413 and of 3750 earlier positions, rotating over the 4 "
+                        "attention layers' weights and caches",
+            **att_out,
+        }
+        log("attention step:", out["attention_step"])
+
+        # one language-model position: input row, all 56 layers in pattern order (27 Mamba2,
+        # 25 MLP, 4 attention over caches of 413 earlier positions), norm_f, both heads and ids
         hw = synth.head_weights(seed=9)
         lmw = nh.lm_weights(gu.w4_dev(synth.embed_tokens(seed=9)), dev_layers[:n_layers],
-                            [nh.mlp_weights(*m) for m in mlps], gu.to_dev(hw.norm_f), gu.w4_dev(hw.lm_head),
+                            [nh.mlp_weights(*m) for m in mlps], atts, gu.to_dev(hw.norm_f), gu.w4_dev(hw.lm_head),
                             gu.w4_dev(hw.function_head), 2.0)
         del hw
         st_lm = [gu.state_dev(np.zeros((1, 3, CD), np.uint16), np.zeros((1, H, P, N), np.float32))[0]
                  for _ in range(n_layers)]
+        T_lm = 413
+        kv_lm = []
+        for a in range(len(atts)):
+            kk, vv = synth.kv_cache(50 + a, 1, T_lm + 1)
+            kv_lm.append(nh.kv_cache(gu.to_dev(kk), gu.to_dev(vv), T_lm + 1))
+        pos_lm = torch.tensor([T_lm], dtype=torch.int32, device="cuda")
         wsl_n = nh.nh_lm_workspace_bytes(d128, synth.MLP_INTER, 1)
         wsl = gu.workspace(wsl_n)
         ti, fi, au = synth.embed_inputs(200, 1)
@@ -386,7 +446,8 @@ def main():
         ot, of = (torch.empty(1, dtype=torch.int32, device="cuda") for _ in range(2))
 
         def lm_pos():
-            nh.nh_lm_step(d128, lmw, st_lm, ti, fi, au, nh.NH_F32, 1, None, ot, of, wsl, wsl_n, stream)
+            nh.nh_lm_step(d128, lmw, st_lm, kv_lm, pos_lm, ti, fi, au, nh.NH_F32, 1, None, ot, of, wsl, wsl_n,
+                          stream)
 
         for _ in range(5):
             lm_pos()
@@ -397,16 +458,17 @@ def main():
         hip.record(e1, stream)
         torch.cuda.synchronize()
         us_lm = hip.ms(e0, e1) * 1e3 / npos
-        lm_bytes = (n_layers * sum(step_kernel_bytes(1)) + len(mlps) * mb + 2 * (w4_bytes(VOCAB, HID) + 6 * HID))
+        lm_bytes = (n_layers * sum(step_kernel_bytes(1)) + len(mlps) * mb + 2 * (w4_bytes(VOCAB, HID) + 6 * HID)
+                    + len(atts) * att_out["cache_413"]["algorithmic_bytes"])
         out["lm_step"] = {
-            "workload": "one language-model position at batch 1: input row, 27 Mamba2 blocks and 25 MLP layers in "
-                        "pattern order (the 4 attention layers not part of the library), norm_f, lm_head + "
-                        "function_head (W4 131072x4480) and greedy ids",
+            "workload": "one language-model position at batch 1: input row, all 56 layers in pattern order "
+                        "(27 Mamba2 blocks, 25 MLP layers, 4 attention layers over caches of 413 earlier "
+                        "positions), norm_f, lm_head + function_head (W4 131072x4480) and greedy ids",
             "ms_per_position": round(us_lm / 1e3, 4), "algorithmic_bytes": int(lm_bytes),
             "hbm_frac": round(lm_bytes / (us_lm * 1e-6) / HBM_PEAK, 4),
         }
         log("lm step:", out["lm_step"])
-        del mlps, lmw, st_lm
+        del mlps, lmw, st_lm, kv_lm, atts
 
     # ------------------------------- 27-layer stack, batch 1, stepwise over T=413
     if not args.skip_stack:

@@ -38,7 +38,9 @@ EXPORTS = (
     "nh_conv1d_step", "nh_conv1d_seq", "nh_ssm_step", "nh_ssd_scan_workspace_bytes", "nh_ssd_chunk_scan",
     "nh_rmsnorm_gated", "nh_block_workspace_bytes", "nh_mamba_block_step", "nh_mamba_block_step_noalloc", "nh_mamba_block_seq",
     "nh_mamba_stack", "nh_head_workspace_bytes", "nh_head_argmax", "nh_fused_embedding",
-    "nh_mlp_workspace_bytes", "nh_mlp_step", "nh_lm_workspace_bytes", "nh_lm_step",
+    "nh_mlp_workspace_bytes", "nh_mlp_step", "nh_attention_workspace_bytes", "nh_attention_step",
+    "nh_attention_decode_workspace_bytes", "nh_attention_decode",
+    "nh_lm_workspace_bytes", "nh_lm_step",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -79,9 +81,19 @@ class nh_mlp_weights(C.Structure):
     _fields_ = [("norm_w", C.c_void_p), ("up", nh_w4_matrix), ("down", nh_w4_matrix)]
 
 
+class nh_attention_weights(C.Structure):
+    _fields_ = [("norm_w", C.c_void_p), ("q_proj", nh_w4_matrix), ("k_proj", nh_w4_matrix),
+                ("v_proj", nh_w4_matrix), ("o_proj", nh_w4_matrix)]
+
+
+class nh_kv_cache(C.Structure):
+    _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("max_len", C.c_int)]
+
+
 class nh_lm_weights(C.Structure):
     _fields_ = [("embed", nh_w4_matrix), ("mamba", C.POINTER(nh_mamba_weights)),
-                ("mlp", C.POINTER(nh_mlp_weights)), ("norm_f", C.c_void_p), ("lm_head", nh_w4_matrix),
+                ("mlp", C.POINTER(nh_mlp_weights)), ("attn", C.POINTER(nh_attention_weights)),
+                ("norm_f", C.c_void_p), ("lm_head", nh_w4_matrix),
                 ("function_head", nh_w4_matrix), ("function_weight", C.c_float)]
 
 
@@ -113,7 +125,11 @@ _sigs = {
     "nh_mlp_workspace_bytes": (_sz, [_i, _i]),
     "nh_mlp_step": (_i, [_vp, _vp, _vp, C.c_float, _vp, _i, _vp, _i, _i, _vp, _sz, _vp]),
     "nh_lm_workspace_bytes": (_sz, [_vp, _i, _i]),
-    "nh_lm_step": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "nh_attention_workspace_bytes": (_sz, [_i]),
+    "nh_attention_step": (_i, [_vp, _vp, _vp, _vp, _i, _vp, _i, _i, C.c_float, _vp, _sz, _vp]),
+    "nh_attention_decode_workspace_bytes": (_sz, [_i]),
+    "nh_attention_decode": (_i, [_vp, _vp, _vp, _vp, _i, _vp, _sz, _vp]),
+    "nh_lm_step": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
 }
 for _name, (_res, _args) in _sigs.items():
     _f = getattr(lib, _name)
@@ -196,13 +212,28 @@ def mlp_weights(norm_w, up: nh_w4_matrix, down: nh_w4_matrix) -> nh_mlp_weights:
     return w
 
 
-def lm_weights(embed: nh_w4_matrix, mamba: list, mlp: list, norm_f, lm_head: nh_w4_matrix,
+def attention_weights(norm_w, q_proj: nh_w4_matrix, k_proj: nh_w4_matrix, v_proj: nh_w4_matrix,
+                      o_proj: nh_w4_matrix) -> nh_attention_weights:
+    w = nh_attention_weights(_ptr(norm_w), q_proj, k_proj, v_proj, o_proj)
+    w._keep = (norm_w, q_proj, k_proj, v_proj, o_proj)
+    return w
+
+
+def kv_cache(k, v, max_len: int) -> nh_kv_cache:
+    c = nh_kv_cache(_ptr(k), _ptr(v), max_len)
+    c._keep = (k, v)
+    return c
+
+
+def lm_weights(embed: nh_w4_matrix, mamba: list, mlp: list, attn: list, norm_f, lm_head: nh_w4_matrix,
                function_head: nh_w4_matrix, function_weight: float = 2.0) -> nh_lm_weights:
-    """mamba: nh_mamba_weights per 'M' layer; mlp: nh_mlp_weights per '-' layer (pattern order)."""
+    """mamba: nh_mamba_weights per 'M' layer; mlp: nh_mlp_weights per '-' layer; attn:
+    nh_attention_weights per '*' layer (pattern order)."""
     ma = (nh_mamba_weights * len(mamba))(*mamba)
     ml = (nh_mlp_weights * len(mlp))(*mlp)
-    w = nh_lm_weights(embed, ma, ml, _ptr(norm_f), lm_head, function_head, function_weight)
-    w._keep = (embed, mamba, mlp, ma, ml, norm_f, lm_head, function_head)
+    at = (nh_attention_weights * len(attn))(*attn)
+    w = nh_lm_weights(embed, ma, ml, at, _ptr(norm_f), lm_head, function_head, function_weight)
+    w._keep = (embed, mamba, mlp, attn, ma, ml, at, norm_f, lm_head, function_head)
     return w
 
 
@@ -210,12 +241,22 @@ def nh_lm_workspace_bytes(d, inter, batch) -> int:
     return lib.nh_lm_workspace_bytes(C.byref(d), inter, batch)
 
 
-def nh_lm_step(d, w, states, text_ids, function_ids, audio, audio_dtype, batch, hidden_out, text_out,
-               function_out, ws, ws_bytes, stream=None):
+def nh_lm_step(d, w, states, caches, positions, text_ids, function_ids, audio, audio_dtype, batch, hidden_out,
+               text_out, function_out, ws, ws_bytes, stream=None):
     st = (nh_mamba_state * len(states))(*states)
-    _check(lib.nh_lm_step(C.byref(d), C.byref(w), st, _ptr(text_ids), _ptr(function_ids), _ptr(audio), audio_dtype,
-                          batch, _ptr(hidden_out), _ptr(text_out), _ptr(function_out), _ptr(ws), ws_bytes,
-                          _stream(stream)))
+    kc = (nh_kv_cache * len(caches))(*caches)
+    _check(lib.nh_lm_step(C.byref(d), C.byref(w), st, kc, _ptr(positions), _ptr(text_ids), _ptr(function_ids),
+                          _ptr(audio), audio_dtype, batch, _ptr(hidden_out), _ptr(text_out), _ptr(function_out),
+                          _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def nh_attention_workspace_bytes(batch) -> int:
+    return lib.nh_attention_workspace_bytes(batch)
+
+
+def nh_attention_step(w, cache, positions, x, x_dtype, out, out_dtype, batch, eps, ws, ws_bytes, stream=None):
+    _check(lib.nh_attention_step(C.byref(w), C.byref(cache), _ptr(positions), _ptr(x), x_dtype, _ptr(out),
+                                 out_dtype, batch, eps, _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def nh_mlp_workspace_bytes(inter, batch) -> int:
@@ -329,3 +370,12 @@ def nh_profile_events(events):
     else:
         arr = (C.c_void_p * len(events))(*events)
         _check(lib.nh_profile_events(arr, len(events)))
+
+
+def nh_attention_decode_workspace_bytes(batch) -> int:
+    return lib.nh_attention_decode_workspace_bytes(batch)
+
+
+def nh_attention_decode(q, cache, positions, o, batch, ws, ws_bytes, stream=None):
+    _check(lib.nh_attention_decode(_ptr(q), C.byref(cache), _ptr(positions), _ptr(o), batch, _ptr(ws), ws_bytes,
+                                   _stream(stream)))

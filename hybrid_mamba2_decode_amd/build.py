@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libnhmamba.so")
-SOURCES = ["api.cpp", "gemv.hip", "step.hip", "rows.hip", "gemm.hip", "scan.hip"]
+SOURCES = ["api.cpp", "gemv.hip", "step.hip", "rows.hip", "gemm.hip", "scan.hip", "attn.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 VALU instructions are disabled for all device code.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",

@@ -284,6 +284,75 @@ nh_status check_state(const nh_mamba_state *st, const char *name, bool required)
     return NH_OK;
 }
 
+// ---------------------------------------------------------------- attention layers
+constexpr int ATT_Q = 40 * 128, ATT_KV = 8 * 128, ATT_MAX_LEN = 1 << 22;
+
+nh_status check_attention(const nh_attention_weights *w)
+{
+    if (!w) return fail(NH_ERR_INVALID_ARGUMENT, "attention weights are NULL");
+    NH_TRY(need_ptr(w->norm_w, "attention norm_w"));
+    NH_TRY(check_w4(&w->q_proj, "q_proj"));
+    NH_TRY(check_w4(&w->k_proj, "k_proj"));
+    NH_TRY(check_w4(&w->v_proj, "v_proj"));
+    NH_TRY(check_w4(&w->o_proj, "o_proj"));
+    if (w->q_proj.n_out != ATT_Q || w->q_proj.k_in != HIDDEN || w->k_proj.n_out != ATT_KV ||
+        w->k_proj.k_in != HIDDEN || w->v_proj.n_out != ATT_KV || w->v_proj.k_in != HIDDEN ||
+        w->o_proj.n_out != HIDDEN || w->o_proj.k_in != ATT_Q)
+        return fail(NH_ERR_UNSUPPORTED_SHAPE,
+                    "attention projections q %dx%d, k %dx%d, v %dx%d, o %dx%d (need q [%d][%d], k and v "
+                    "[%d][%d], o [%d][%d])",
+                    w->q_proj.n_out, w->q_proj.k_in, w->k_proj.n_out, w->k_proj.k_in, w->v_proj.n_out,
+                    w->v_proj.k_in, w->o_proj.n_out, w->o_proj.k_in, ATT_Q, HIDDEN, ATT_KV, HIDDEN, HIDDEN, ATT_Q);
+    return NH_OK;
+}
+
+nh_status check_cache(const nh_kv_cache *c)
+{
+    if (!c) return fail(NH_ERR_INVALID_ARGUMENT, "kv cache is NULL");
+    NH_TRY(need_ptr(c->k, "cache k"));
+    NH_TRY(need_ptr(c->v, "cache v"));
+    if (c->max_len < 1 || c->max_len > ATT_MAX_LEN)
+        return fail(NH_ERR_UNSUPPORTED_SHAPE, "cache max_len %d outside 1..%d", c->max_len, ATT_MAX_LEN);
+    return NH_OK;
+}
+
+struct AttWs {
+    uint16_t *q, *o;
+    float *part;
+};
+
+AttWs carve_attention(void *ws, int B, size_t *bytes)
+{
+    Carve c{reinterpret_cast<char *>(ws)};
+    AttWs a;
+    a.q = c.take<uint16_t>((size_t)B * ATT_Q);
+    a.o = c.take<uint16_t>((size_t)B * ATT_Q);
+    a.part = c.take<float>(attn_part_bytes(B) / sizeof(float));
+    *bytes = c.off;
+    return a;
+}
+
+size_t attention_bytes(int B)
+{
+    size_t n;
+    carve_attention(nullptr, B, &n);
+    return n;
+}
+
+// the four launches of one attention layer (arguments already checked)
+nh_status attention_step(const nh_attention_weights *w, const nh_kv_cache *c, const int32_t *pos, const void *x,
+                         int x_t, void *out, int out_t, int B, float eps, void *ws, hipStream_t s)
+{
+    size_t n;
+    const AttWs a = carve_attention(ws, B, &n);
+    NH_HIP(launch_attn_qkv(view(&w->q_proj), view(&w->k_proj), view(&w->v_proj), x, x_t, w->norm_w, eps, B, a.q,
+                           c->k, c->v, pos, c->max_len, s),
+           "attention q/k/v");
+    NH_HIP(launch_attn_decode(a.q, c->k, c->v, pos, c->max_len, B, a.part, a.o, s), "attention");
+    NH_HIP(launch_gemv(view(&w->o_proj), a.o, B, x, x_t, out, out_t, s), "attention o_proj");
+    return NH_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -679,7 +748,59 @@ nh_status nh_mamba_stack(const nh_mamba_dims *d, const nh_mamba_weights *weights
     return ok();
 }
 
-static const int NH_N_MAMBA = 27, NH_N_MLP = 25;
+size_t nh_attention_workspace_bytes(int batch)
+{
+    if (batch < 1 || batch > 4) return 0;
+    return attention_bytes(batch);
+}
+
+nh_status nh_attention_step(const nh_attention_weights *w, const nh_kv_cache *cache, const int32_t *positions,
+                            const void *x, nh_dtype x_dtype, void *out, nh_dtype out_dtype, int batch, float eps,
+                            void *ws, size_t ws_bytes, void *stream)
+{
+    NH_TRY(check_attention(w));
+    NH_TRY(check_cache(cache));
+    NH_TRY(need_ptr(positions, "positions"));
+    NH_TRY(need_ptr(x, "x"));
+    NH_TRY(need_dtype(x_dtype, "x_dtype"));
+    NH_TRY(need_ptr(out, "out"));
+    NH_TRY(need_dtype(out_dtype, "out_dtype"));
+    NH_TRY(need_ptr(ws, "ws"));
+    if (out == x) return fail(NH_ERR_INVALID_ARGUMENT, "out may not alias x");
+    if (!(eps > 0.f) || !std::isfinite(eps)) return fail(NH_ERR_INVALID_ARGUMENT, "eps must be positive");
+    if (batch < 1 || batch > 4) return fail(NH_ERR_UNSUPPORTED_SHAPE, "batch %d outside 1..4", batch);
+    const size_t need = attention_bytes(batch);
+    if (ws_bytes < need)
+        return fail(NH_ERR_WORKSPACE_TOO_SMALL, "attention workspace %zu < %zu bytes", ws_bytes, need);
+    NH_TRY(attention_step(w, cache, positions, x, x_dtype, out, out_dtype, batch, eps, ws, S(stream)));
+    return ok();
+}
+
+size_t nh_attention_decode_workspace_bytes(int batch)
+{
+    if (batch < 1 || batch > 64) return 0;
+    return attn_part_bytes(batch);
+}
+
+nh_status nh_attention_decode(const uint16_t *q, const nh_kv_cache *cache, const int32_t *positions, uint16_t *o,
+                              int batch, void *ws, size_t ws_bytes, void *stream)
+{
+    NH_TRY(need_ptr(q, "q"));
+    NH_TRY(check_cache(cache));
+    NH_TRY(need_ptr(positions, "positions"));
+    NH_TRY(need_ptr(o, "o"));
+    NH_TRY(need_ptr(ws, "ws"));
+    if (batch < 1 || batch > 64) return fail(NH_ERR_UNSUPPORTED_SHAPE, "batch %d outside 1..64", batch);
+    const size_t need = attn_part_bytes(batch);
+    if (ws_bytes < need)
+        return fail(NH_ERR_WORKSPACE_TOO_SMALL, "attention workspace %zu < %zu bytes", ws_bytes, need);
+    NH_HIP(launch_attn_decode(q, cache->k, cache->v, positions, cache->max_len, batch,
+                              reinterpret_cast<float *>(ws), o, S(stream)),
+           "attention");
+    return ok();
+}
+
+static const int NH_N_MAMBA = 27, NH_N_MLP = 25, NH_N_ATT = 4;
 
 size_t nh_lm_workspace_bytes(const nh_mamba_dims *d, int inter, int batch)
 {
@@ -687,6 +808,7 @@ size_t nh_lm_workspace_bytes(const nh_mamba_dims *d, int inter, int batch)
     size_t scratch = step_bytes(batch);
     scratch = std::max(scratch, nh_mlp_workspace_bytes(inter, batch));
     scratch = std::max(scratch, head_ws_bytes(batch));
+    scratch = std::max(scratch, attention_bytes(batch));
     Carve c{nullptr};
     c.take<float>((size_t)batch * HIDDEN);
     c.take<float>((size_t)batch * HIDDEN);
@@ -695,13 +817,14 @@ size_t nh_lm_workspace_bytes(const nh_mamba_dims *d, int inter, int batch)
 }
 
 nh_status nh_lm_step(const nh_mamba_dims *d, const nh_lm_weights *w, nh_mamba_state *states,
-                     const int32_t *text_ids, const int32_t *function_ids, const void *audio, nh_dtype audio_dtype,
-                     int batch, float *hidden_out, int32_t *text_out, int32_t *function_out, void *ws,
-                     size_t ws_bytes, void *stream)
+                     const nh_kv_cache *caches, const int32_t *positions, const int32_t *text_ids,
+                     const int32_t *function_ids, const void *audio, nh_dtype audio_dtype, int batch,
+                     float *hidden_out, int32_t *text_out, int32_t *function_out, void *ws, size_t ws_bytes,
+                     void *stream)
 {
     NH_TRY(check_dims(d, false));
-    if (!w || !w->mamba || !w->mlp || !states)
-        return fail(NH_ERR_INVALID_ARGUMENT, "weights, their layer arrays and states must be non-NULL");
+    if (!w || !w->mamba || !w->mlp || !w->attn || !states || !caches)
+        return fail(NH_ERR_INVALID_ARGUMENT, "weights, their layer arrays, states and caches must be non-NULL");
     NH_TRY(check_w4(&w->embed, "embed"));
     NH_TRY(check_w4(&w->lm_head, "lm_head"));
     NH_TRY(check_w4(&w->function_head, "function_head"));
@@ -724,6 +847,11 @@ nh_status nh_lm_step(const nh_mamba_dims *d, const nh_lm_weights *w, nh_mamba_st
             return fail(NH_ERR_UNSUPPORTED_SHAPE, "mlp layer %d: up %d x %d, down %d x %d", i, m.up.n_out, m.up.k_in,
                         m.down.n_out, m.down.k_in);
     }
+    for (int i = 0; i < NH_N_ATT; ++i) {
+        NH_TRY(check_attention(&w->attn[i]));
+        NH_TRY(check_cache(&caches[i]));
+    }
+    NH_TRY(need_ptr(positions, "positions"));
     NH_TRY(need_ptr(text_ids, "text_ids"));
     NH_TRY(need_ptr(function_ids, "function_ids"));
     NH_TRY(need_ptr(audio, "audio"));
@@ -746,7 +874,7 @@ nh_status nh_lm_step(const nh_mamba_dims *d, const nh_lm_weights *w, nh_mamba_st
                               cur, s),
            "input row");
     const char *pat = nh_hybrid_pattern();
-    int mi = 0, li = 0;
+    int mi = 0, li = 0, ai = 0;
     for (const char *p = pat; *p; ++p) {
         if (*p == 'M') {
             NH_TRY(block_step(d, &w->mamba[mi], &states[mi], cur, NH_F32, nxt, NH_F32, batch, scratch, s));
@@ -757,7 +885,9 @@ nh_status nh_lm_step(const nh_mamba_dims *d, const nh_lm_weights *w, nh_mamba_st
             NH_HIP(launch_mlp_up_step(view(&m.up), cur, F32, m.norm_w, d->eps, batch, h, s), "mlp up");
             NH_HIP(launch_gemv(view(&m.down), h, batch, cur, F32, nxt, F32, s), "mlp down");
         } else {
-            continue;  // attention: not part of this library, the stream passes through
+            NH_TRY(attention_step(&w->attn[ai], &caches[ai], positions, cur, F32, nxt, F32, batch, d->eps, scratch,
+                                  s));
+            ++ai;
         }
         std::swap(cur, nxt);
     }

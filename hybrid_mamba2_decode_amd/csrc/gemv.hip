@@ -508,9 +508,8 @@ struct IpRows {
     }
 };
 
-template <int NB, class Epi = EpiInProjStep>
+template <int NB, class Epi = EpiInProjStep, class S = InProjShape<NB>>
 struct InProjBlock {
-    using S = InProjShape<NB>;
     static constexpr int R = S::R, NS = S::NS, RW = S::RW;
     const Epi epi;
     IpRows<R> io;
@@ -545,6 +544,16 @@ struct InProjBlock {
         const int blk = xcd * bx + wave;
         active = wave < bx && blk < nblk;
         rb = min(blk, nblk - 1) * RW;
+        io.load(st[0], rb);
+        pe = epi.prefetch(min(rb + min(io.li / NB, RW - 1), io.nmax), io.li % NB);
+    }
+
+    // a block whose first row and activity the caller chose (rows past the matrix are clamped)
+    __device__ __forceinline__ InProjBlock(const W4 &W, const Epi &e, int row0, bool act) : epi(e)
+    {
+        io.init(W);
+        active = act;
+        rb = row0;
         io.load(st[0], rb);
         pe = epi.prefetch(min(rb + min(io.li / NB, RW - 1), io.nmax), io.li % NB);
     }
@@ -961,6 +970,107 @@ __global__ __launch_bounds__(NB == 1 ? 512 : 256, 1) void k_outproj_step(W4 W, c
         act_from_lds<LPR, CPL, NB>(a, act_lds, NCH, (threadIdx.x & 63) % LPR);
         run.run(a);
     }
+}
+
+// ----------------------------------------------------------------- attention q / k / v
+//
+// The q, k and v projections of an attention layer share one input, u = RMSNorm(x) w, so one
+// launch computes all three (5120 + 1024 + 1024 rows of K = hidden): the pre-norm and the
+// K = 4480 row layout of in_proj, 4-row blocks spread over 8-wave work-groups, each block inside
+// one of the three matrices.  The epilogue stores q (bf16) and
+// appends k and v (bf16) to the key/value cache, [batch][kv_heads][max_len][head_dim], at the
+// sequence's position; a position outside 0 .. max_len - 1 stores nothing (the attention
+// kernels then write NaN outputs for that sequence).
+constexpr int ATT_HEADS = 40, ATT_KV = 8, ATT_HD = 128;
+constexpr int ATT_QD = ATT_HEADS * ATT_HD, ATT_KD = ATT_KV * ATT_HD;  // 5120, 1024
+
+// Batch 1 and 2: 4-row blocks (1792 of them), so that 8-wave work-groups still cover 224 CUs.
+// Batch 3 and 4 need the registers of 4-wave work-groups: in_proj's 8-row blocks.
+template <int NB>
+struct AttnQkvShape {
+    static constexpr int R = NB == 1 ? 2 : 1, RW = NB <= 2 ? 4 : 8, NS = RW / R, NT = NB <= 2 ? 512 : 256;
+};
+
+struct EpiAttnQKV {
+    uint16_t *q, *kc, *vc;
+    const int *pos;
+    int max_len, base;  // base: the first global row (q | k | v) of the wave's matrix
+    __device__ __forceinline__ EpiPre prefetch(int, int b) const
+    {
+        EpiPre p;
+        p.w[0] = (uint32_t)pos[b];
+        return p;
+    }
+    __device__ __forceinline__ void operator()(int n, int b, float acc, const EpiPre &p) const
+    {
+        const uint16_t vb = f32_to_bf16(acc);
+        const int gn = base + n;
+        if (gn < ATT_QD) {
+            q[(size_t)b * ATT_QD + gn] = vb;
+            return;
+        }
+        const int t = (int)p.w[0];
+        if (t < 0 || t >= max_len) return;
+        const int r = (gn - ATT_QD) % ATT_KD, kvh = r / ATT_HD, d = r % ATT_HD;
+        uint16_t *dst = gn < ATT_QD + ATT_KD ? kc : vc;
+        dst[(((size_t)b * ATT_KV + kvh) * max_len + t) * ATT_HD + d] = vb;
+    }
+};
+
+template <int NB, int XT>
+__global__ __launch_bounds__(AttnQkvShape<NB>::NT, 1) void k_attn_qkv(W4 Wq, W4 Wk, W4 Wv, const void *__restrict__ x,
+                                                                  const uint16_t *__restrict__ nw, float eps,
+                                                                  EpiAttnQKV epi)
+{
+    using S = AttnQkvShape<NB>;
+    constexpr int NT = S::NT, R = S::R;
+    extern __shared__ __attribute__((aligned(16))) uint32_t act_lds[];
+    __shared__ float red[NB][NT / 64];
+    PreNorm<NB, XT, NT> pn;
+    pn.issue(x, nw);
+    __builtin_amdgcn_sched_barrier(0);
+    // this wave's block: one contiguous range of blocks per XCD, as in_proj
+    const int xcd = blockIdx.x & 7;
+    const int wave = __builtin_amdgcn_readfirstlane((int)((threadIdx.x >> 6) * (gridDim.x >> 3) + (blockIdx.x >> 3)));
+    constexpr int NBLK = (ATT_QD + 2 * ATT_KD) / S::RW;
+    const int bx = (NBLK + 7) / 8, blk = xcd * bx + wave;
+    const bool active = wave < bx && blk < NBLK;
+    const int row = min(blk, NBLK - 1) * S::RW;  // the three matrices' sizes are multiples of RW
+    const int which = row < ATT_QD ? 0 : row < ATT_QD + ATT_KD ? 1 : 2;
+    const int base = which == 0 ? 0 : which == 1 ? ATT_QD : ATT_QD + ATT_KD;
+    EpiAttnQKV e = epi;
+    e.base = base;
+    InProjBlock<NB, EpiAttnQKV, S> run(which == 0 ? Wq : which == 1 ? Wk : Wv, e, row - base, active);
+    pn.finish(eps, act_lds, red);
+    ActChunk am[NB][2], at[NB];
+    act_hidden<NB, R>(am, at, act_lds);
+    run.run(am, at);
+}
+
+hipError_t launch_attn_qkv(const W4 &Wq, const W4 &Wk, const W4 &Wv, const void *x, int x_t, const uint16_t *norm_w,
+                           float eps, int batch, uint16_t *q, uint16_t *kc, uint16_t *vc, const int *pos, int max_len,
+                           hipStream_t st)
+{
+    EpiAttnQKV e{q, kc, vc, pos, max_len, 0};
+    const size_t lds = (size_t)batch * (HIDDEN / 32) * ACT_WORDS * 4;
+#define NH_LAUNCH(NB)                                                                                           \
+    {                                                                                                           \
+        using S = AttnQkvShape<NB>;                                                                             \
+        constexpr int NBLK = (ATT_QD + 2 * ATT_KD) / S::RW, WPG = S::NT / 64;                                  \
+        const int bx = (NBLK + 7) / 8, grid = 8 * ((bx + WPG - 1) / WPG);                                      \
+        if (x_t == BF16)                                                                                        \
+            launch_k(k_attn_qkv<NB, BF16>, dim3(grid), dim3(S::NT), lds, st, Wq, Wk, Wv, x, norm_w, eps, e);      \
+        else                                                                                                    \
+            launch_k(k_attn_qkv<NB, F32>, dim3(grid), dim3(S::NT), lds, st, Wq, Wk, Wv, x, norm_w, eps, e);       \
+    }
+    switch (batch) {
+    case 1: NH_LAUNCH(1); break;
+    case 2: NH_LAUNCH(2); break;
+    case 3: NH_LAUNCH(3); break;
+    default: NH_LAUNCH(4); break;
+    }
+#undef NH_LAUNCH
+    return hipGetLastError();
 }
 
 // Pre-norm + MLP up projection (K = hidden) + squared ReLU: the in_proj kernel's structure

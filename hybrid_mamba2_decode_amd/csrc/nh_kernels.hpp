@@ -82,6 +82,18 @@ hipError_t launch_conv_step(const uint16_t *xbc, long ld, uint16_t *state, const
                             const uint16_t *b, uint16_t *out, int batch, int channels,
                             hipStream_t st);
 
+// ---- attention layers (gemv.hip, attn.hip)
+// Pre-norm + q/k/v projections: q into q ([batch][5120] bf16), k and v appended to the
+// caches ([batch][8][max_len][128] bf16) at pos[b] (device int32 [batch]).
+hipError_t launch_attn_qkv(const W4 &Wq, const W4 &Wk, const W4 &Wv, const void *x, int x_t, const uint16_t *norm_w,
+                           float eps, int batch, uint16_t *q, uint16_t *kc, uint16_t *vc, const int *pos, int max_len,
+                           hipStream_t st);
+// Attention of each sequence's new position over its cache positions 0 .. pos[b] (the new k, v
+// already appended): o ([batch][5120] bf16); part holds attn_part_bytes(batch) bytes.
+size_t attn_part_bytes(int batch);
+hipError_t launch_attn_decode(const uint16_t *q, const uint16_t *kc, const uint16_t *vc, const int *pos, int max_len,
+                              int batch, float *part, uint16_t *o, hipStream_t st);
+
 // ---- row kernels (rows.hip)
 // u = bf16(RMSNorm(x) * w); out_kind 0: bf16 bits, 1: fp16 bits of the same value (the
 // matrix-core operand format); su (nullable): per-64-group sums of u, [d/64][rows].

@@ -252,12 +252,72 @@ nh_status nh_fused_embedding(const nh_w4_matrix *E, const int32_t *text_ids,
                              nh_dtype audio_dtype, float function_weight, int batch,
                              float *out, void *stream);
 
+/* One attention layer of the hybrid stack, per position, for `batch`
+ * sequences (issue page, section "config.json": the '*' layers of
+ * hybrid_override_pattern, num_attention_heads 40, num_key_value_heads 8,
+ * head_dim 128, attention_bias false; the projections are 4-bit group-64 like
+ * the mixer's; no positional encoding is named, so none is applied).  The
+ * docs page "Nemotron VoiceChat", section "Online session", keeps the
+ * attention key/value caches across positions.  With fp32 sums:
+ *   u = bf16(RMSNorm(x) * norm_w),
+ *   q = bf16(q_proj u), k = bf16(k_proj u), v = bf16(v_proj u),
+ *   k and v are written into the cache at index positions[b],
+ *   o[h] = bf16(softmax_t(q[h] . K[h/5][t] / sqrt(128)) V[h/5]) over cache
+ *          indices t = 0 .. positions[b] (query head h reads key/value head
+ *          h / 5),
+ *   out = x + o_proj o.
+ * positions: int32 [batch] DEVICE array, the cache index of this position per
+ * sequence (the caller advances it; indices below it must hold the earlier
+ * positions' k and v).  A position outside 0 .. max_len-1 writes nothing to
+ * the cache and gives a row of NaN in out.  x: [batch][4480] of x_dtype; out:
+ * [batch][4480] of out_dtype (may not alias x).  ws: at least
+ * nh_attention_workspace_bytes(batch) bytes, contents on return unspecified.
+ * batch 1..4; every pointer 16-byte aligned.  Five kernels on `stream`.
+ * Errors before any launch: NH_ERR_UNSUPPORTED_SHAPE (projection shapes,
+ * max_len outside 1 .. 2^22, batch), NH_ERR_WORKSPACE_TOO_SMALL,
+ * NH_ERR_MISALIGNED, NH_ERR_INVALID_ARGUMENT (NULL pointer, dtype, eps <= 0,
+ * out == x). */
+typedef struct {
+    const uint16_t *norm_w;   /* bf16 [hidden]: pre-norm weight */
+    nh_w4_matrix q_proj;      /* [40*128][hidden] = [5120][4480] */
+    nh_w4_matrix k_proj;      /* [8*128][hidden] = [1024][4480] */
+    nh_w4_matrix v_proj;      /* [1024][4480] */
+    nh_w4_matrix o_proj;      /* [hidden][5120] = [4480][5120] */
+} nh_attention_weights;
+
+/* Key/value cache of one attention layer; k and v: bf16
+ * [batch][8][max_len][128] each (key/value head, then cache index, then the
+ * head dimension), owned by the caller. */
+typedef struct {
+    uint16_t *k, *v;
+    int max_len;
+} nh_kv_cache;
+
+size_t nh_attention_workspace_bytes(int batch);
+nh_status nh_attention_step(const nh_attention_weights *w, const nh_kv_cache *cache,
+                            const int32_t *positions, const void *x, nh_dtype x_dtype, void *out,
+                            nh_dtype out_dtype, int batch, float eps, void *ws, size_t ws_bytes,
+                            void *stream);
+
+/* The attention core of nh_attention_step on its own (same kernels): for
+ * every sequence b and query head h,
+ *   o[b][h] = bf16(softmax_t(q[b][h] . K[b][h/5][t] / sqrt(128)) V[b][h/5])
+ * over cache indices t = 0 .. positions[b], with fp32 scores and sums.
+ * q, o: bf16 [batch][40][128]; cache and positions as in nh_attention_step
+ * (the cache already holds index positions[b]; nothing is written to it).  A
+ * position outside 0 .. max_len-1 gives a row of NaN.  ws: at least
+ * nh_attention_decode_workspace_bytes(batch) bytes.  batch 1..64; errors
+ * before any launch as for nh_attention_step. */
+size_t nh_attention_decode_workspace_bytes(int batch);
+nh_status nh_attention_decode(const uint16_t *q, const nh_kv_cache *cache, const int32_t *positions,
+                              uint16_t *o, int batch, void *ws, size_t ws_bytes, void *stream);
+
 /* One position of the language model (issue page, section "Network 2"): the
- * fused input row, the layers of hybrid_override_pattern in order, norm_f,
+ * fused input row, the 56 layers of hybrid_override_pattern in order, norm_f,
  * both heads and their greedy ids.  'M' layers run nh_mamba_block_step
- * (state updated in place), '-' layers nh_mlp_step; the 4 attention layers
- * ('*') are not part of this library and pass the stream through unchanged.
- * The residual stream between layers is fp32. */
+ * (state updated in place), '-' layers nh_mlp_step, '*' layers
+ * nh_attention_step (cache written at positions[b]).  The residual stream
+ * between layers is fp32. */
 typedef struct {
     const uint16_t *norm_w;   /* bf16 [hidden] */
     nh_w4_matrix up;          /* [inter][hidden] */
@@ -268,6 +328,7 @@ typedef struct {
     nh_w4_matrix embed;                 /* [vocab][hidden]: embed_tokens */
     const nh_mamba_weights *mamba;      /* host array, one per 'M' of the pattern (27) */
     const nh_mlp_weights *mlp;          /* host array, one per '-' of the pattern (25) */
+    const nh_attention_weights *attn;   /* host array, one per '*' of the pattern (4) */
     const uint16_t *norm_f;             /* bf16 [hidden] */
     nh_w4_matrix lm_head, function_head; /* [vocab][hidden] each */
     float function_weight;              /* function_channel_weight, 2.0 in the config */
@@ -276,12 +337,16 @@ typedef struct {
 /* Workspace bytes of nh_lm_step for MLP width `inter` at this batch (0 on bad
  * arguments). */
 size_t nh_lm_workspace_bytes(const nh_mamba_dims *d, int inter, int batch);
-/* states: host array, one per 'M' layer, updated in place.  text_ids,
+/* states: host array, one per 'M' layer, updated in place.  caches: host
+ * array, one per '*' layer; positions: int32 [batch] device array, the cache
+ * index of this position (shared by the 4 attention layers; the caller
+ * advances it).  text_ids,
  * function_ids: int32 [batch] (the previous ids); audio: [batch][hidden] of
  * audio_dtype; hidden_out: nullable f32 [batch][hidden] (the stream before
  * norm_f); text_out, function_out: int32 [batch] (greedy ids as in
  * nh_head_argmax).  batch 1..4; every pointer 16-byte aligned. */
 nh_status nh_lm_step(const nh_mamba_dims *d, const nh_lm_weights *w, nh_mamba_state *states,
+                     const nh_kv_cache *caches, const int32_t *positions,
                      const int32_t *text_ids, const int32_t *function_ids, const void *audio,
                      nh_dtype audio_dtype, int batch, float *hidden_out, int32_t *text_out,
                      int32_t *function_out, void *ws, size_t ws_bytes, void *stream);

@@ -143,17 +143,56 @@ def test_lm_step_rejects_bad_arguments(nh):
     emb = _fake_w4(n=131072, k=4480)
     m = nh.nh_mamba_weights(A, _fake_w4(n=22656, k=4480), A, A, A, A, A, A, _fake_w4(n=4480, k=10240))
     f = nh.nh_mlp_weights(A, _fake_w4(n=15680, k=4480), _fake_w4(n=4480, k=15680))
-    w = nh.lm_weights(emb, [m] * 27, [f] * 25, A, emb, emb, 2.0)
+    at = _fake_attention(nh, A)
+    assert need >= nh.nh_attention_workspace_bytes(1)
+    w = nh.lm_weights(emb, [m] * 27, [f] * 25, [at] * 4, A, emb, emb, 2.0)
     st = [nh.nh_mamba_state(A, A)] * 27
+    kv = [nh.nh_kv_cache(A, A, 512)] * 4
 
-    def call(w=w, batch=1, ws_bytes=need, t=A):
-        return _status(lambda: nh.nh_lm_step(d, w, st, t, A, A, 0, batch, None, A, A, A, ws_bytes, 0))
+    def call(w=w, batch=1, ws_bytes=need, t=A, kv=kv, pos=A):
+        return _status(lambda: nh.nh_lm_step(d, w, st, kv, pos, t, A, A, 0, batch, None, A, A, A, ws_bytes, 0))
     assert call(batch=5) == nh.NH_ERR_UNSUPPORTED_SHAPE
     assert call(ws_bytes=need - 1) == nh.NH_ERR_WORKSPACE_TOO_SMALL
     assert call(t=None) == nh.NH_ERR_INVALID_ARGUMENT
+    assert call(pos=None) == nh.NH_ERR_INVALID_ARGUMENT
+    assert call(kv=[nh.nh_kv_cache(A, A, 512)] * 3 + [nh.nh_kv_cache(A, A, 0)]) == nh.NH_ERR_UNSUPPORTED_SHAPE
+    assert call(kv=[nh.nh_kv_cache(A, A + 8, 512)] * 4) == nh.NH_ERR_MISALIGNED
     bad_f = nh.nh_mlp_weights(A, _fake_w4(n=15680, k=4480), _fake_w4(n=4480, k=15616))
-    assert call(w=nh.lm_weights(emb, [m] * 27, [f] * 24 + [bad_f], A, emb, emb, 2.0)) == nh.NH_ERR_UNSUPPORTED_SHAPE
-    assert call(w=nh.lm_weights(emb, [m] * 27, [f] * 25, A, emb, emb, float("inf"))) == nh.NH_ERR_INVALID_ARGUMENT
+    assert call(w=nh.lm_weights(emb, [m] * 27, [f] * 24 + [bad_f], [at] * 4, A, emb, emb, 2.0)) == \
+        nh.NH_ERR_UNSUPPORTED_SHAPE
+    bad_a = _fake_attention(nh, A, kv_rows=512)
+    assert call(w=nh.lm_weights(emb, [m] * 27, [f] * 25, [at] * 3 + [bad_a], A, emb, emb, 2.0)) == \
+        nh.NH_ERR_UNSUPPORTED_SHAPE
+    assert call(w=nh.lm_weights(emb, [m] * 27, [f] * 25, [at] * 4, A, emb, emb, float("inf"))) == \
+        nh.NH_ERR_INVALID_ARGUMENT
+
+
+def _fake_attention(nh, A, kv_rows=1024):
+    return nh.nh_attention_weights(A, _fake_w4(n=5120, k=4480), _fake_w4(n=kv_rows, k=4480),
+                                   _fake_w4(n=1024, k=4480), _fake_w4(n=4480, k=5120))
+
+
+def test_attention_step_rejects_bad_arguments(nh):
+    A = 0x40000
+    need = nh.nh_attention_workspace_bytes(2)
+    assert need >= 2 * 2 * 5120 * 2
+    assert nh.nh_attention_workspace_bytes(0) == 0 and nh.nh_attention_workspace_bytes(5) == 0
+    at = _fake_attention(nh, A)
+
+    def call(w=at, kv=nh.nh_kv_cache(A, A, 413), pos=A, x=A, out=A + 0x1000, batch=2, eps=1e-5, ws=need, xt=0):
+        return _status(lambda: nh.nh_attention_step(w, kv, pos, x, xt, out, 0, batch, eps, A, ws, 0))
+    assert call(w=_fake_attention(nh, A, kv_rows=512)) == nh.NH_ERR_UNSUPPORTED_SHAPE
+    assert call(kv=nh.nh_kv_cache(A, A, 0)) == nh.NH_ERR_UNSUPPORTED_SHAPE
+    assert call(kv=nh.nh_kv_cache(A, A, (1 << 22) + 1)) == nh.NH_ERR_UNSUPPORTED_SHAPE
+    assert call(kv=nh.nh_kv_cache(None, A, 16)) == nh.NH_ERR_INVALID_ARGUMENT
+    assert call(pos=None) == nh.NH_ERR_INVALID_ARGUMENT
+    assert call(pos=A + 4) == nh.NH_ERR_MISALIGNED
+    assert call(out=A) == nh.NH_ERR_INVALID_ARGUMENT   # out aliases x
+    assert call(batch=0) == nh.NH_ERR_UNSUPPORTED_SHAPE
+    assert call(batch=5) == nh.NH_ERR_UNSUPPORTED_SHAPE
+    assert call(eps=0.0) == nh.NH_ERR_INVALID_ARGUMENT
+    assert call(ws=need - 1) == nh.NH_ERR_WORKSPACE_TOO_SMALL
+    assert call(xt=3) == nh.NH_ERR_INVALID_ARGUMENT
 
 
 def test_gemm_workspace_check(nh):
