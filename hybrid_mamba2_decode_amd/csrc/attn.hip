@@ -49,31 +49,40 @@ __device__ __forceinline__ float dot8(uint4 a, uint4 b, float c)
     return dot2(a.w, b.w, c);
 }
 
+// One tile's loads for a lane: its k piece (score role) and its four value rows (value role),
+// positions clamped into the split's range so that every load stays in it.
+struct TileRegs {
+    uint4 k[4], v[4];
+};
+
+__device__ __forceinline__ void load_tile(TileRegs &r, const uint16_t *kp, const uint16_t *vp, int t0, int plast,
+                                          int t)
+{
+    const int pk = min(t0 + (t >> 2), plast);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r.k[j] = *reinterpret_cast<const uint4 *>(kp + (size_t)pk * HD + 8 * ((t & 3) + 4 * j));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int pv = min(t0 + (t >> 4) + 16 * i, plast);
+        r.v[i] = *reinterpret_cast<const uint4 *>(vp + (size_t)pv * HD + 8 * (t & 15));
+    }
+}
+
 // Thread roles inside a 256-thread work-group, per tile:
 //   scores:  position p = t / 4 of the tile, dims 8 (t % 4 + 4 j) .. + 7 for j < 4 (the quad
 //            reads the 256-byte k row as four 64-byte pieces); quad sums give q_h . k_p.
 //   weights: the quad's lane i computes 2^(s - m) for query head i (lane 0 also head 4).
-//   values:  dims 2 (t % 64), + 1 over positions 16 (t / 64) .. + 15 of the tile.
+//   values:  dims 8 (t % 16) .. + 7 over positions t / 16 + 16 i, i < 4 (16 lanes read one
+//            256-byte value row).
+// The next tile's loads are issued before the current tile is computed.
 __global__ __launch_bounds__(256) void k_attn_decode(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
                                                      const uint16_t *__restrict__ vc, const int *__restrict__ pos,
                                                      int max_len, float *__restrict__ part)
 {
     const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z, nsplit = gridDim.x;
     const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
-    const int P = pos[b];
-    if (P < 0 || P >= max_len) return;  // the combine writes NaN for this sequence
-    const int L = P + 1, c = split_len(L, nsplit);
-    const int p0 = s * c, p1 = min(L, p0 + c);
-    if (p0 >= p1) return;  // nothing here; the combine reads only the splits below L
-
-    __shared__ float wl[2][REP][TILE];       // softmax weights of a tile (double-buffered)
-    __shared__ float rm[2][4][REP];          // per-wave tile maxima of the scores
-    __shared__ float red[4][REP * HD + REP];  // final cross-wave sums of acc and l
-
-    const size_t kvbase = ((size_t)b * KVH + g) * max_len * HD;
-    const uint16_t *kp = kc + kvbase, *vp = vc + kvbase;
-
-    // the five query heads' dims of this lane (score role), bf16 pairs
+    // the five query heads' dims of this lane (score role), bf16 pairs; issued before the
+    // position is known
     const int dq = t & 3;
     uint4 qv[REP][4];
 #pragma unroll
@@ -81,38 +90,44 @@ __global__ __launch_bounds__(256) void k_attn_decode(const uint16_t *__restrict_
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             qv[h][j] = *reinterpret_cast<const uint4 *>(q + (size_t)b * HEADS * HD + (g * REP + h) * HD + 8 * (dq + 4 * j));
+    const int P = pos[b];
+    if (P < 0 || P >= max_len) return;  // the combine writes NaN for this sequence
+    const int L = P + 1, c = split_len(L, nsplit);
+    const int p0 = s * c, p1 = min(L, p0 + c);
+    if (p0 >= p1) return;  // nothing here; the combine reads only the splits below L
+
+    __shared__ float wl[2][REP][TILE];  // softmax weights of a tile (double-buffered)
+    __shared__ float rm[2][4][REP];     // per-wave tile maxima of the scores
+    __shared__ __attribute__((aligned(16))) float red[4][REP * HD];  // final cross-wave sums of acc
+    __shared__ float redl[4][REP];      // and of l
+
+    const size_t kvbase = ((size_t)b * KVH + g) * max_len * HD;
+    const uint16_t *kp = kc + kvbase, *vp = vc + kvbase;
 
     // log2(e) / sqrt(128): scores in base 2
     const float scale = 1.4426950408889634f * 0.08838834764831845f;
-    float m[REP], l[REP], acc[REP][2];
+    float m[REP], l[REP], acc[REP][8];
 #pragma unroll
     for (int h = 0; h < REP; ++h) {
         m[h] = -INFINITY;
         l[h] = 0.f;
-        acc[h][0] = acc[h][1] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
     }
 
+    TileRegs cur, nxt;
+    load_tile(nxt, kp, vp, p0, p1 - 1, t);
     int buf = 0;
     for (int t0 = p0; t0 < p1; t0 += TILE, buf ^= 1) {
-        // loads: the lane's k piece and its 16 value pairs (positions clamped into the range)
+        cur = nxt;
+        load_tile(nxt, kp, vp, t0 + TILE, p1 - 1, t);  // past the range: clamped re-reads of the last row
         const int pk = t0 + (t >> 2);
-        const int pkc = min(pk, p1 - 1);
-        uint4 kv[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) kv[j] = *reinterpret_cast<const uint4 *>(kp + (size_t)pkc * HD + 8 * (dq + 4 * j));
-        uint32_t vv[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int pv = min(t0 + 16 * wave + i, p1 - 1);
-            vv[i] = *reinterpret_cast<const uint32_t *>(vp + (size_t)pv * HD + 2 * lane);
-        }
-        // scores of position pk for the five heads
         float sc[REP];
 #pragma unroll
         for (int h = 0; h < REP; ++h) {
             float a = 0.f;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) a = dot8(qv[h][j], kv[j], a);
+            for (int j = 0; j < 4; ++j) a = dot8(qv[h][j], cur.k[j], a);
             a += __shfl_xor(a, 1, 64);
             a += __shfl_xor(a, 2, 64);
             sc[h] = pk < p1 ? a * scale : -INFINITY;
@@ -147,29 +162,45 @@ __global__ __launch_bounds__(256) void k_attn_decode(const uint16_t *__restrict_
         __syncthreads();
         // values
 #pragma unroll
-        for (int h = 0; h < REP; ++h) {
-            acc[h][0] *= alpha[h];
-            acc[h][1] *= alpha[h];
-        }
+        for (int h = 0; h < REP; ++h)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float v0 = bf16lo(vv[i]), v1 = bf16hi(vv[i]);
+            for (int e = 0; e < 8; ++e) acc[h][e] *= alpha[h];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint4 vr = cur.v[i];
+            const float v8[8] = {bf16lo(vr.x), bf16hi(vr.x), bf16lo(vr.y), bf16hi(vr.y),
+                                 bf16lo(vr.z), bf16hi(vr.z), bf16lo(vr.w), bf16hi(vr.w)};
 #pragma unroll
             for (int h = 0; h < REP; ++h) {
-                const float w = wl[buf][h][16 * wave + i];
-                acc[h][0] = fmaf(w, v0, acc[h][0]);
-                acc[h][1] = fmaf(w, v1, acc[h][1]);
+                const float w = wl[buf][h][(t >> 4) + 16 * i];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(w, v8[e], acc[h][e]);
             }
         }
     }
 
-    // cross-wave sums: acc over the four position quarters, l over all lanes
+    // acc over the 16 position groups: the wave's four (lanes 16 apart), then the four waves
+#pragma unroll
+    for (int h = 0; h < REP; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float v = acc[h][e];
+            v += __shfl_xor(v, 16, 64);
+            v += __shfl_xor(v, 32, 64);
+            acc[h][e] = v;
+        }
+    if (lane < 16) {
+#pragma unroll
+        for (int h = 0; h < REP; ++h) {
+            float4 *d4 = reinterpret_cast<float4 *>(&red[wave][h * HD + 8 * lane]);
+            d4[0] = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+            d4[1] = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+        }
+    }
 #pragma unroll
     for (int h = 0; h < REP; ++h) {
-        red[wave][h * HD + 2 * lane] = acc[h][0];
-        red[wave][h * HD + 2 * lane + 1] = acc[h][1];
         const float lw = wave_sum(l[h]);
-        if (lane == 0) red[wave][REP * HD + h] = lw;
+        if (lane == 0) redl[wave][h] = lw;
     }
     __syncthreads();
     float *dst = part + (((size_t)b * KVH + g) * nsplit + s) * PART;
@@ -178,41 +209,54 @@ __global__ __launch_bounds__(256) void k_attn_decode(const uint16_t *__restrict_
 #pragma unroll
         for (int h = 1; h < REP; ++h) mv = t == h ? m[h] : mv;
         dst[t] = mv;
-        dst[REP + t] = red[0][REP * HD + t] + red[1][REP * HD + t] + red[2][REP * HD + t] + red[3][REP * HD + t];
+        dst[REP + t] = redl[0][t] + redl[1][t] + redl[2][t] + redl[3][t];
     }
     for (int e = t; e < REP * HD; e += 256) dst[16 + e] = red[0][e] + red[1][e] + red[2][e] + red[3][e];
 }
 
 // o[b][h * 128 + d] = bf16(sum_s e_s acc_s[d] / sum_s e_s l_s) over the splits that hold
-// positions; NaN for a sequence whose position is outside the cache.
-__global__ __launch_bounds__(128) void k_attn_combine(const float *__restrict__ part, const int *__restrict__ pos,
-                                                      int max_len, int nsplit, uint16_t *__restrict__ o)
+// positions; NaN for a sequence whose position is outside the cache.  One wave per query head:
+// lane s holds split s's maximum and sum (the splits' loads all in flight at once), lane d
+// sums dims d and d + 64.
+__global__ __launch_bounds__(64) void k_attn_combine(const float *__restrict__ part, const int *__restrict__ pos,
+                                                     int max_len, int nsplit, uint16_t *__restrict__ o)
 {
-    const int hq = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+    const int hq = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
     const int g = hq / REP, h = hq % REP;
+    const float *src = part + ((size_t)b * KVH + g) * nsplit * PART;
     const int P = pos[b];
-    uint16_t *dst = o + (size_t)b * HEADS * HD + hq * HD + d;
+    uint16_t *dst = o + (size_t)b * HEADS * HD + hq * HD;
     if (P < 0 || P >= max_len) {
-        *dst = 0x7FC0;  // NaN
+        dst[lane] = dst[lane + 64] = 0x7FC0;  // NaN
         return;
     }
-    const int L = P + 1, c = split_len(L, nsplit), ns = (L + c - 1) / c;
-    const float *src = part + ((size_t)b * KVH + g) * nsplit * PART;
-    float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, src[(size_t)s * PART + h]);
-    float num = 0.f, den = 0.f;
-    for (int s = 0; s < ns; ++s) {
-        const float *p = src + (size_t)s * PART;
-        const float e = exp2f(p[h] - M);
-        den = fmaf(e, p[REP + h], den);
-        num = fmaf(e, p[16 + h * HD + d], num);
+    const int L = P + 1, c = split_len(L, nsplit), ns = (L + c - 1) / c;  // 1 .. 64
+    const bool have = lane < ns;
+    const float ms = have ? src[(size_t)lane * PART + h] : -INFINITY;
+    const float ls = have ? src[(size_t)lane * PART + REP + h] : 0.f;
+    float M = ms;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+    const float es = have ? exp2f(ms - M) : 0.f;
+    const float den = wave_sum(es * ls);
+    float n0 = 0.f, n1 = 0.f;
+    for (int s0 = 0; s0 < ns; s0 += 8) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int sj = min(s0 + j, ns - 1);  // past ns: weight 0, an in-range row re-read
+            const float e = s0 + j < ns ? __shfl(es, sj, 64) : 0.f;
+            const float *a = src + (size_t)sj * PART + 16 + h * HD;
+            n0 = fmaf(e, a[lane], n0);
+            n1 = fmaf(e, a[lane + 64], n1);
+        }
     }
-    *dst = f32_to_bf16(num / den);
+    dst[lane] = f32_to_bf16(n0 / den);
+    dst[lane + 64] = f32_to_bf16(n1 / den);
 }
 
-// Splits per (sequence, kv head): about 256 work-groups in all (one per CU), at most one
-// split per tile of the cache.
-int max_splits(int batch) { return std::max(1, std::min((256 + 8 * batch - 1) / (8 * batch), MAX_SPLIT)); }
+// Splits per (sequence, kv head): about 512 work-groups in all (two per CU), at most one split
+// per tile of the cache.
+int max_splits(int batch) { return std::max(1, std::min((512 + 8 * batch - 1) / (8 * batch), MAX_SPLIT)); }
 
 int attn_splits(int batch, int max_len)
 {
@@ -229,7 +273,7 @@ hipError_t launch_attn_decode(const uint16_t *q, const uint16_t *kc, const uint1
 {
     const int ns = attn_splits(batch, max_len);
     launch_k(k_attn_decode, dim3(ns, KVH, batch), dim3(256), 0, st, q, kc, vc, pos, max_len, part);
-    launch_k(k_attn_combine, dim3(HEADS, batch), dim3(HD), 0, st, (const float *)part, pos, max_len, ns, o);
+    launch_k(k_attn_combine, dim3(HEADS, batch), dim3(64), 0, st, (const float *)part, pos, max_len, ns, o);
     return hipGetLastError();
 }
 
