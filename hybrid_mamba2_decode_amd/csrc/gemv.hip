@@ -25,6 +25,8 @@
 #include "nh_device.hpp"
 #include "nh_kernels.hpp"
 
+#include <type_traits>
+
 namespace nh {
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -33,6 +35,20 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c)
 {
     uint32_t r;
     asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(c));
+    return r;
+}
+
+// The same operation in plain code, for results that feed a matrix-core instruction: a VALU
+// write of a register that an MFMA then reads as its A or B operand needs two wait states,
+// which the compiler inserts only for instructions it can see (not for inline assembly).
+__device__ __forceinline__ uint32_t and_or_mf(uint32_t a, uint32_t m, uint32_t c) { return (a & m) | c; }
+
+// A value the compiler keeps in a vector register without knowing it (so that and_or_mf of two
+// such masks is one v_and_or_b32: with constants it takes two instructions).
+__device__ __forceinline__ uint32_t opaque_v(uint32_t x)
+{
+    uint32_t r;
+    asm("v_mov_b32 %0, %1" : "=v"(r) : "v"(x));
     return r;
 }
 
@@ -658,6 +674,49 @@ struct PreNorm {
     }
 };
 
+// The activation source of the K = hidden kernels without a pre-norm: the bf16 rows of x go to
+// LDS in the activation format as they are, with PreNorm's interface (thread t < 140 owns
+// chunk t of every batch row).
+template <int NB, int NT>
+struct PlainAct {
+    static constexpr int NCH = HIDDEN / 32, NW = NT / 64;
+    bool own;
+    uint4 xr[NB][4];
+
+    __device__ __forceinline__ void issue(const void *x, const uint16_t *)
+    {
+        own = (int)threadIdx.x < NCH;
+        if (own) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const uint4 *src = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(x) +
+                                                                   (size_t)b * HIDDEN + 32 * threadIdx.x);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) xr[b][j] = src[j];
+            }
+        }
+    }
+
+    __device__ __forceinline__ void finish(float, uint32_t *act_lds, float (&)[NB][NW])
+    {
+        if (own) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                float v[32];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint4 r = xr[b][j];
+                    v[8 * j + 0] = bf16lo(r.x); v[8 * j + 1] = bf16hi(r.x); v[8 * j + 2] = bf16lo(r.y);
+                    v[8 * j + 3] = bf16hi(r.y); v[8 * j + 4] = bf16lo(r.z); v[8 * j + 5] = bf16hi(r.z);
+                    v[8 * j + 6] = bf16lo(r.w); v[8 * j + 7] = bf16hi(r.w);
+                }
+                make_chunk(v, act_lds + ((size_t)b * NCH + threadIdx.x) * ACT_WORDS);
+            }
+        }
+        __syncthreads();
+    }
+};
+
 // Activations of the lane's chunks in the K = 4480 layout: l and l + 64 of every row, and
 // its tail chunk 128 + l % 12 (zero for lanes beyond the R rows' tails).
 template <int NB, int R>
@@ -695,9 +754,11 @@ __device__ __forceinline__ void act_hidden(ActChunk (&am)[NB][2], ActChunk (&at)
 //
 // Per chunk: D gathers the even nibbles (1024 + q) and D' the odd ones (1024 + 16 q) as in
 // chunk_dot, and acc += s (D + D'/16).  The activation constants of the magic offset and of
-// the bias are per (chunk, batch row) and live in the A lanes, so they enter through two
-// v_mfma_f32_4x4x1_16b_f32: E += sum_x b and E += (-off) s.  After the 9 chunks the 16
-// blocks' partials are summed across lanes (DPP row rotations, then two shuffles).
+// the bias are per (chunk, batch row) and live in the A lanes, so they enter through
+// v_mfma_f32_4x4x1_16b_f32, which broadcasts them over the columns: D starts at -off, and
+// E += sum_x b.  After the 9 chunks the 16 blocks' partials are summed across lanes (DPP row
+// rotations, then two shuffles).  The same kernel serves the plain W4 GEMV of K = 4480 at
+// batch 3 and 4.
 constexpr int MF_CH = 9;    // chunks per lane and row
 constexpr int MF_WGS = 256;  // work-groups of the batched in_proj: one per CU, 32 per XCD
 
@@ -714,16 +775,18 @@ __device__ __forceinline__ h4v h4_of(uint32_t lo, uint32_t hi)
     return __builtin_bit_cast(h4v, make_uint2(lo, hi));
 }
 
-template <int NB, int XT>
-__global__ __launch_bounds__(256, 1) void k_inproj_step_mf(W4 W, const void *__restrict__ x,
-                                                          const uint16_t *__restrict__ nw, float eps,
-                                                          EpiInProjStep epi, uint32_t *zero_ptr, int nzero)
+// NORM: the activations are the pre-norm u = bf16(x / rms(x) * nw) of x (XT: its dtype);
+// otherwise x is bf16 and used as it is.  Epi: the row epilogue (in_proj's split and conv
+// step, or a plain store).
+template <int NB, int XT, bool NORM, class Epi>
+__global__ __launch_bounds__(256, 1) void k_w4_mf(W4 W, const void *__restrict__ x, const uint16_t *__restrict__ nw,
+                                                  float eps, Epi epi, uint32_t *zero_ptr, int nzero)
 {
     constexpr int NT = 256, NW = NT / 64, NCH = HIDDEN / 32;
     extern __shared__ __attribute__((aligned(16))) uint32_t act_lds[];
     __shared__ float red[NB][NW];
     if (blockIdx.x == 0 && (int)threadIdx.x < nzero) zero_ptr[threadIdx.x] = 0u;
-    PreNorm<NB, XT, NT> pn;
+    std::conditional_t<NORM, PreNorm<NB, XT, NT>, PlainAct<NB, NT>> pn;
     pn.issue(x, nw);
     __builtin_amdgcn_sched_barrier(0);
 
@@ -774,18 +837,21 @@ __global__ __launch_bounds__(256, 1) void k_inproj_step_mf(W4 W, const void *__r
             a[t].sum = 0.f;
         }
     }
+    const uint32_t mlo = opaque_v(0x000F000Fu), mhi = opaque_v(0x00F000F0u), magic = opaque_v(0x64006400u);
     auto step = [&](const MfStage &g, int st) {
-        const uint32_t mlo = 0x000F000Fu, mhi = 0x00F000F0u, magic = 0x64006400u;
         floatx4 acc = {0.f, 0.f, 0.f, 0.f}, E = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < MF_CH; ++t) {
-            floatx4 D = {0.f, 0.f, 0.f, 0.f}, D2 = {0.f, 0.f, 0.f, 0.f};
+            // D starts at -off (batch row i's offset in every column): D + D'/16 is then the
+            // chunk's sum of a q itself, so a one-hot x gives s q + b with one rounding
+            const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+            floatx4 D = __builtin_amdgcn_mfma_f32_4x4x1f32(a[t].off, 1.0f, zero, 0, 0, 0), D2 = zero;
             const uint32_t wq[4] = {g.q[t].x, g.q[t].y, g.q[t].z, g.q[t].w};
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
                 const uint32_t wd = wq[w], wh = wd >> 8;
-                const uint32_t d0 = and_or(wd, mlo, magic), d1 = and_or(wd, mhi, magic);
-                const uint32_t d2 = and_or(wh, mlo, magic), d3 = and_or(wh, mhi, magic);
+                const uint32_t d0 = and_or_mf(wd, mlo, magic), d1 = and_or_mf(wd, mhi, magic);
+                const uint32_t d2 = and_or_mf(wh, mlo, magic), d3 = and_or_mf(wh, mhi, magic);
                 D = __builtin_amdgcn_mfma_f32_4x4x4f16(h4_of(a[t].p[4 * w], a[t].p[4 * w + 2]), h4_of(d0, d2), D, 0, 0, 0);
                 D2 = __builtin_amdgcn_mfma_f32_4x4x4f16(h4_of(a[t].p[4 * w + 1], a[t].p[4 * w + 3]), h4_of(d1, d3), D2, 0, 0, 0);
             }
@@ -793,7 +859,6 @@ __global__ __launch_bounds__(256, 1) void k_inproj_step_mf(W4 W, const void *__r
 #pragma unroll
             for (int v = 0; v < 4; ++v) acc[v] = fmaf(sc, fmaf(D2[v], 0.0625f, D[v]), acc[v]);
             E = __builtin_amdgcn_mfma_f32_4x4x1f32(a[t].sum, bi, E, 0, 0, 0);
-            E = __builtin_amdgcn_mfma_f32_4x4x1f32(a[t].off, sc, E, 0, 0, 0);
         }
         float tot[4];
 #pragma unroll
@@ -1308,6 +1373,17 @@ hipError_t launch_gemv(const W4 &W, const uint16_t *x, int batch, const void *re
                        void *y, int y_t, hipStream_t st)
 {
     EpiStore e{y, res, y_t, res_t, W.n};
+    // K = hidden at batch 3 and 4: the matrix-core kernel of the batched in_proj
+    if (W.k == HIDDEN && batch >= 3) {
+        const size_t lds = (size_t)batch * (HIDDEN / 32) * ACT_WORDS * 4;
+        if (batch == 3)
+            launch_k(k_w4_mf<3, BF16, false, EpiStore>, dim3(MF_WGS), dim3(256), lds, st, W, (const void *)x,
+                     (const uint16_t *)nullptr, 0.f, e, (uint32_t *)nullptr, 0);
+        else
+            launch_k(k_w4_mf<4, BF16, false, EpiStore>, dim3(MF_WGS), dim3(256), lds, st, W, (const void *)x,
+                     (const uint16_t *)nullptr, 0.f, e, (uint32_t *)nullptr, 0);
+        return hipGetLastError();
+    }
     switch (batch) {
     case 1: return gemv_nb<1>(W, x, e, st);
     case 2: return gemv_nb<2>(W, x, e, st);
@@ -1353,9 +1429,11 @@ hipError_t launch_inproj_step(const W4 &W, const void *x, int x_t, const uint16_
 #define NH_LAUNCH_MF(NB)                                                                                   \
     {                                                                                                      \
         if (x_t == BF16)                                                                                   \
-            launch_k(k_inproj_step_mf<NB, BF16>, dim3(MF_WGS), dim3(256), lds, st, W, x, norm_w, eps, e, zero_ptr, nzero); \
+            launch_k(k_w4_mf<NB, BF16, true, EpiInProjStep>, dim3(MF_WGS), dim3(256), lds, st, W, x, norm_w, eps, e, \
+                     zero_ptr, nzero);                                                                     \
         else                                                                                               \
-            launch_k(k_inproj_step_mf<NB, F32>, dim3(MF_WGS), dim3(256), lds, st, W, x, norm_w, eps, e, zero_ptr, nzero);  \
+            launch_k(k_w4_mf<NB, F32, true, EpiInProjStep>, dim3(MF_WGS), dim3(256), lds, st, W, x, norm_w, eps, e, \
+                     zero_ptr, nzero);                                                                     \
     }
     // the matrix-core kernel from batch 3 on (at batch 2 the per-row kernel is 1 us faster)
     switch (batch) {

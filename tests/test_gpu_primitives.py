@@ -85,6 +85,32 @@ def test_gemv_matches_oracle(env, n, k, batch):
     assert gu.max_abs(got, ref) < 1e-4 * max(1.0, np.abs(ref).max())
 
 
+# K = 4480 at batch 3 and 4 runs the batched in_proj's matrix-core kernel: ceil(n / 4) four-row
+# stages split evenly over the 8 XCDs and then over 1024 waves, two stages per loop iteration
+# (loads past a wave's last stage re-read it; only the second compute is conditional).  These
+# n_out give waves of {0,1}, {1,2}, {2,3}, {3,4}, {4,5} and {5,6} stages (odd and even counts,
+# idle waves) and last stages with 1, 2, 3 and 4 rows inside the matrix.
+MF_TAILS = [1, 3, 66, 4100, 8594, 14339, 16385, 22656]
+
+
+@pytest.mark.parametrize("batch", [3, 4])
+def test_gemv_matrix_core_stage_tails(env, batch):
+    nh, oracle, gu, torch = env
+    rng = np.random.default_rng(40 + batch)
+    for n in MF_TAILS:
+        _say("gemv matrix-core tails", n, batch)
+        W = _asym(synth.w4_random(5, n, 1, 2, n, 4480), n)
+        x = _x(rng, batch, 4480)
+        res = rng.normal(size=(batch, n)).astype(np.float32)
+        y = gu.empty_f32(batch, n)
+        nh.nh_w4_gemv(gu.w4_dev(W), gu.to_dev(x), batch, gu.to_dev(res), nh.NH_F32, y, nh.NH_F32)
+        ref = oracle.w4_matvec(W, gu.bf16_bits_to_f64(x)) + res
+        got = y.cpu().numpy().astype(np.float64)
+        assert np.isfinite(got).all(), n
+        assert gu.rel_l2(got, ref) < 1e-5, n
+        assert gu.max_abs(got, ref) < 1e-4 * max(1.0, np.abs(ref).max()), n
+
+
 def test_gemv_residual_bf16_out(env):
     nh, oracle, gu, torch = env
     _say("gemv residual bf16")
