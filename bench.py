@@ -152,6 +152,23 @@ def traffic_from_profile(kernel: str, *sources: str):
     return None
 
 
+def counters_from_profile(kernel: str, *sources: str):
+    """MFMA busy fraction, matrix-core TFLOP/s and LDS bank-conflict share of one kernel from the
+    committed counter summary, or None when absent or when the kernel's source changed after
+    the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "scan_gemm_counters.md")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        f = line.split()
+        if len(f) >= 5 and f[0] == kernel:
+            if f[1] != _source_sha(*sources):
+                return None
+            return {"file": "profiles/scan_gemm_counters.md", "mfma_busy": float(f[2]),
+                    "matrix_core_tflops": float(f[3]), "lds_bank_conflict_share": float(f[4])}
+    return None
+
+
 # ------------------------------------------------------------------- main
 
 def main():
@@ -609,11 +626,46 @@ def main():
                          "achieved": round(pps * fl / 1e12, 1), "peak": MFMA_F16_PEAK / 1e12, "unit": "TFLOP/s",
                          "frac": round(pps * fl / MFMA_F16_PEAK, 4),
                          "traffic": traffic_from_profile("k_ssd_scan", "scan.hip", "nh_device.hpp"),
+                         "counters": counters_from_profile("k_ssd_scan", "scan.hip", "nh_device.hpp"),
                          "flops_per_position": round(fl), "bytes_per_position": by,
                          "achieved_GBps": round(pps * by / 1e9, 1), "hbm_peak_GBps": HBM_PEAK / 1e9},
         }
         log("scan:", out["scan"])
         del sets
+
+        # ------- the W4 GEMM alone: in_proj and out_proj of the full-history block at M = 7500
+        # rows (batch 2 x T 3750), rotating over the 27 layers' weights
+        M = pos
+        Xi = gu.to_dev(synth.f32_to_bf16(rng.normal(0, 1, (M, HID)).astype(np.float32)))
+        Xo = gu.to_dev(synth.f32_to_bf16(rng.normal(0, 1, (M, DI)).astype(np.float32)))
+        Yi, Yo = gu.empty_u16(M, NIN), gu.empty_u16(M, HID)
+        gws_n = max(nh.nh_w4_gemm_workspace_bytes(M, HID), nh.nh_w4_gemm_workspace_bytes(M, DI))
+        gws = gu.workspace(gws_n)
+        gemm_out = {}
+        for name, X, Y, n_out, k_in in (("in_proj", Xi, Yi, NIN, HID), ("out_proj", Xo, Yo, HID, DI)):
+            def gemm(l):
+                W = getattr(dev_layers[l % len(dev_layers)], name)
+                nh.nh_w4_gemm(W, X, M, None, 0, Y, nh.NH_BF16, gws, gws_n, stream)
+
+            for l in range(3):
+                gemm(l)
+            hip.record(e0, stream)
+            for l in range(n_layers):
+                gemm(l)
+            hip.record(e1, stream)
+            torch.cuda.synchronize()
+            ms_g = hip.ms(e0, e1) / n_layers
+            fl_g = 2.0 * M * n_out * k_in
+            gemm_out[name] = {"ms": round(ms_g, 3), "tflops": round(fl_g / (ms_g * 1e-3) / 1e12, 1),
+                              "mfma_frac": round(fl_g / (ms_g * 1e-3) / MFMA_F16_PEAK, 4)}
+        out["gemm"] = {
+            "workload": "W4 GEMM Y = X W^T of the full-history block, M = 7500 rows (batch 2 x T 3750): "
+                        "in_proj 4480->22656 and out_proj 10240->4480, bf16 output, 27 layers' weights",
+            **gemm_out,
+            "counters": counters_from_profile("k_w4_gemm", "gemm.hip", "nh_device.hpp"),
+        }
+        log("gemm:", out["gemm"])
+        del Xi, Xo, Yi, Yo, gws
 
         if not args.skip_stack:
             x4 = gu.to_dev(synth.block_input(4, B4, T4))
