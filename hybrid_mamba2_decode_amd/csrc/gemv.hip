@@ -78,10 +78,11 @@ __device__ __forceinline__ float row_sum(float v)
 }
 
 // Activations of one 16-byte chunk: 16 fp16 pairs (k, k+4) in extraction order, the offset
-// 1024 sum_even + 64 sum_odd, and the plain sum.
+// 1024 sum_even + 64 sum_odd, and the plain sum.  A scaled chunk (make_chunk_scaled) holds its
+// values times 2^-k and mul = 2^k, which the consumer applies to the chunk's dot product.
 struct ActChunk {
     uint32_t p[16];
-    float off, sum;
+    float off, sum, mul;
 };
 constexpr int ACT_WORDS = 20;  // 80-byte slots: 16-byte reads, conflict-free across lanes
 
@@ -102,7 +103,26 @@ __device__ __forceinline__ void make_chunk(const float *v, uint32_t *dst)
     uint4 *d4 = reinterpret_cast<uint4 *>(dst);
 #pragma unroll
     for (int j = 0; j < 4; ++j) d4[j] = make_uint4(w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]);
-    d4[4] = make_uint4(__float_as_uint(fmaf(1024.f, se, 64.f * so)), __float_as_uint(se + so), 0u, 0u);
+    d4[4] = make_uint4(__float_as_uint(fmaf(1024.f, se, 64.f * so)), __float_as_uint(se + so), 0x3F800000u, 0u);
+}
+
+// A chunk of any bf16 values: the 32 values are scaled by 2^-k so that the largest magnitude m
+// lies in [2^14, 2^15) (k = floor(log2 m) - 14, kept in [-100, 113]); the scaling is exact, every
+// bf16 value of the chunk down to 2^-31 m is exact in fp16, and mul = 2^k restores the scale in
+// fp32 after the dot products.  Relative rounding is the same as for an unscaled chunk.
+__device__ __forceinline__ void make_chunk_scaled(const float *v, uint32_t *dst)
+{
+    float m = 0.f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) m = fmaxf(m, fabsf(v[e]));
+    const int ex = (int)((__float_as_uint(m) >> 23) & 0xFFu) - 127;
+    const int k = min(max(ex - 14, -100), 113);
+    const float inv = __uint_as_float((uint32_t)(127 - k) << 23), mul = __uint_as_float((uint32_t)(127 + k) << 23);
+    float u[32];
+#pragma unroll
+    for (int e = 0; e < 32; ++e) u[e] = v[e] * inv;
+    make_chunk(u, dst);
+    dst[18] = __float_as_uint(mul);
 }
 
 template <int LPR>
@@ -233,6 +253,7 @@ __device__ __forceinline__ void load_stage(Stage<RG, CPL> &st, __amdgpu_buffer_r
 }
 
 // One 16-byte chunk of a row against its activations: acc + s * (q . a) + b * sum(a).
+template <bool SC = false>
 __device__ __forceinline__ float chunk_dot(uint4 q, uint32_t sbits, uint32_t bbits, const ActChunk &a, float acc,
                                            uint32_t mlo, uint32_t mhi, uint32_t magic)
 {
@@ -248,10 +269,13 @@ __device__ __forceinline__ float chunk_dot(uint4 q, uint32_t sbits, uint32_t bbi
     }
     const float t = fmaf(dB, 0.0625f, dA) - a.off;
     const float sc = __uint_as_float(sbits << 16), bi = __uint_as_float(bbits << 16);
-    return fmaf(sc, t, fmaf(bi, a.sum, acc));
+    if constexpr (SC)
+        return fmaf(fmaf(sc, t, bi * a.sum), a.mul, acc);
+    else
+        return fmaf(sc, t, fmaf(bi, a.sum, acc));
 }
 
-template <int LPR, int CPL, int NB, int RG, class Epi>
+template <int LPR, int CPL, int NB, int RG, class Epi, bool SC>
 __device__ __forceinline__ void compute_stage(const Stage<RG, CPL> &st, const ActChunk (&a)[NB][CPL],
                                               const Epi &epi, const EpiPre &pre, int row0, int n_out,
                                               int li, uint32_t mlo, uint32_t mhi, uint32_t magic)
@@ -265,7 +289,7 @@ __device__ __forceinline__ void compute_stage(const Stage<RG, CPL> &st, const Ac
             float s = 0.f;
 #pragma unroll
             for (int i = 0; i < CPL; ++i)
-                s = chunk_dot(st.q[r][i], st.s[r][i], st.b[r][i], a[b][i], s, mlo, mhi, magic);
+                s = chunk_dot<SC>(st.q[r][i], st.s[r][i], st.b[r][i], a[b][i], s, mlo, mhi, magic);
             acc[r][b] = row_sum<LPR>(s);
         }
     // lane li = r*NB + b of each row finishes (row, b); rows are row0 + r*RPG
@@ -295,6 +319,7 @@ __device__ __forceinline__ void chunk_from_lds(ActChunk &a, const uint32_t *src)
     const uint4 t = s4[4];
     a.off = __uint_as_float(t.x);
     a.sum = __uint_as_float(t.y);
+    a.mul = __uint_as_float(t.z);
 }
 
 // Activations staged in LDS: [NB][nch][ACT_WORDS] words.
@@ -313,13 +338,15 @@ __device__ __forceinline__ void act_from_lds(ActChunk (&a)[NB][CPL], const uint3
                 for (int j = 0; j < 16; ++j) a[b][i].p[j] = 0u;
                 a[b][i].off = 0.f;
                 a[b][i].sum = 0.f;
+                a[b][i].mul = 1.f;
             }
         }
 }
 
 // The streaming loop.  Construction issues the first stage's loads, so a kernel can build
 // its activations (LDS staging, pre-norm, gated norm) while those loads are in flight.
-template <int LPR, int CPL, int NB, int RG, class Epi>
+// SC: the activations are scaled chunks (make_chunk_scaled).
+template <int LPR, int CPL, int NB, int RG, class Epi, bool SC = false>
 struct GemvRunner {
     static constexpr int RPG = GemvShape<LPR>::RPG;
     static constexpr int ROWS = RG * RPG;  // rows per wave per stage
@@ -398,20 +425,20 @@ struct GemvRunner {
         for (; i + 2 < nst; i += 2, n += 2 * stride) {
             ld(B, pb, n + stride);
             __builtin_amdgcn_sched_barrier(0);
-            compute_stage<LPR, CPL, NB, RG>(A, a, epi, pa, n + sub, nlim, li, mlo, mhi, magic);
+            compute_stage<LPR, CPL, NB, RG, Epi, SC>(A, a, epi, pa, n + sub, nlim, li, mlo, mhi, magic);
             ld(A, pa, n + 2 * stride);
             __builtin_amdgcn_sched_barrier(0);
-            compute_stage<LPR, CPL, NB, RG>(B, a, epi, pb, n + stride + sub, nlim, li, mlo, mhi, magic);
+            compute_stage<LPR, CPL, NB, RG, Epi, SC>(B, a, epi, pb, n + stride + sub, nlim, li, mlo, mhi, magic);
             __builtin_amdgcn_sched_barrier(0);
         }
         if (i + 1 < nst) {
             ld(B, pb, n + stride);
             __builtin_amdgcn_sched_barrier(0);
-            compute_stage<LPR, CPL, NB, RG>(A, a, epi, pa, n + sub, nlim, li, mlo, mhi, magic);
+            compute_stage<LPR, CPL, NB, RG, Epi, SC>(A, a, epi, pa, n + sub, nlim, li, mlo, mhi, magic);
             __builtin_amdgcn_sched_barrier(0);
-            compute_stage<LPR, CPL, NB, RG>(B, a, epi, pb, n + stride + sub, nlim, li, mlo, mhi, magic);
+            compute_stage<LPR, CPL, NB, RG, Epi, SC>(B, a, epi, pb, n + stride + sub, nlim, li, mlo, mhi, magic);
         } else {
-            compute_stage<LPR, CPL, NB, RG>(A, a, epi, pa, n + sub, nlim, li, mlo, mhi, magic);
+            compute_stage<LPR, CPL, NB, RG, Epi, SC>(A, a, epi, pa, n + sub, nlim, li, mlo, mhi, magic);
         }
     }
 };
@@ -710,7 +737,7 @@ struct PlainAct {
                     v[8 * j + 3] = bf16hi(r.y); v[8 * j + 4] = bf16lo(r.z); v[8 * j + 5] = bf16hi(r.z);
                     v[8 * j + 6] = bf16lo(r.w); v[8 * j + 7] = bf16hi(r.w);
                 }
-                make_chunk(v, act_lds + ((size_t)b * NCH + threadIdx.x) * ACT_WORDS);
+                make_chunk_scaled(v, act_lds + ((size_t)b * NCH + threadIdx.x) * ACT_WORDS);
             }
         }
         __syncthreads();
@@ -737,6 +764,7 @@ __device__ __forceinline__ void act_hidden(ActChunk (&am)[NB][2], ActChunk (&at)
             for (int j = 0; j < 16; ++j) at[b].p[j] = 0u;
             at[b].off = 0.f;
             at[b].sum = 0.f;
+            at[b].mul = 1.f;
         }
     }
 }
@@ -830,11 +858,13 @@ __global__ __launch_bounds__(256, 1) void k_w4_mf(W4 W, const void *__restrict__
         if (q4 < NB && c < NCH) {
             chunk_from_lds(a[t], act_lds + ((size_t)q4 * NCH + c) * ACT_WORDS);
             a[t].off = -a[t].off;
+            if constexpr (!NORM) a[t].sum *= a[t].mul;  // scaled chunks: the bias term in true scale
         } else {
 #pragma unroll
             for (int j = 0; j < 16; ++j) a[t].p[j] = 0u;
             a[t].off = 0.f;
             a[t].sum = 0.f;
+            a[t].mul = 1.f;
         }
     }
     const uint32_t mlo = opaque_v(0x000F000Fu), mhi = opaque_v(0x00F000F0u), magic = opaque_v(0x64006400u);
@@ -856,8 +886,15 @@ __global__ __launch_bounds__(256, 1) void k_w4_mf(W4 W, const void *__restrict__
                 D2 = __builtin_amdgcn_mfma_f32_4x4x4f16(h4_of(a[t].p[4 * w + 1], a[t].p[4 * w + 3]), h4_of(d1, d3), D2, 0, 0, 0);
             }
             const float sc = __uint_as_float((uint32_t)g.s[t] << 16), bi = __uint_as_float((uint32_t)g.b[t] << 16);
+            if constexpr (NORM) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) acc[v] = fmaf(sc, fmaf(D2[v], 0.0625f, D[v]), acc[v]);
+                for (int v = 0; v < 4; ++v) acc[v] = fmaf(sc, fmaf(D2[v], 0.0625f, D[v]), acc[v]);
+            } else {
+                // scaled chunks: batch row v's 2^k, broadcast over the columns like the offset
+                const floatx4 Mb = __builtin_amdgcn_mfma_f32_4x4x1f32(a[t].mul, 1.0f, zero, 0, 0, 0);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[v] = fmaf(sc * Mb[v], fmaf(D2[v], 0.0625f, D[v]), acc[v]);
+            }
             E = __builtin_amdgcn_mfma_f32_4x4x1f32(a[t].sum, bi, E, 0, 0, 0);
         }
         float tot[4];
@@ -891,6 +928,273 @@ __global__ __launch_bounds__(256, 1) void k_w4_mf(W4 W, const void *__restrict__
     }
 }
 
+// ------------------------------------ batched rows on the matrix cores, activations in LDS
+//
+// The same 4x4x4 block layout as k_w4_mf for any K: the NB activation rows stay in LDS (the
+// work-group builds them once) and each lane reads its A operand chunk by chunk, so K is not
+// limited by registers.  LDS slot c NB + b holds chunk c of batch row b: the four lanes of a
+// block (batch rows 0..3 of one chunk) read consecutive 80-byte slots, which are
+// conflict-free.  A 4-row stage is cut into slices of CH chunk slots per lane-block
+// (block b takes chunks b + 16 t); the (stage, slice) units are streamed with the next unit's
+// loads in flight, and after a stage's last slice the 16 blocks' partials are summed across
+// lanes.  One work-group of 8 waves per CU.  SC: the chunks are scaled (make_chunk_scaled).
+constexpr int MFL_NT = 512;
+
+template <int CH>
+struct MflUnit {
+    uint4 q[CH];
+    uint16_t s[CH], b[CH];
+};
+
+// x [NB][k] bf16 as scaled chunks.  issue() loads a thread's chunks (chunk it = b nch + c
+// for it = thread, thread + NT, ...; at most MAXC per thread) before the caller's first weight
+// loads, so that they do not queue behind them; finish() builds the LDS slots.
+template <int NB, int NT, int MAXC>
+struct ActPlainK {
+    const uint16_t *x;
+    uint4 r[MAXC][4];
+    __device__ __forceinline__ void issue(int nch)
+    {
+        // unconditional (indices clamped): after a conditional load the compiler's wait for its
+        // registers would also wait for every load issued after it, the weight stream included
+#pragma unroll
+        for (int i = 0; i < MAXC; ++i) {
+            const int it = min((int)threadIdx.x + NT * i, NB * nch - 1);
+            const uint4 *src = reinterpret_cast<const uint4 *>(x + (size_t)it * 32);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) r[i][j] = src[j];
+        }
+    }
+    __device__ __forceinline__ void finish(uint32_t *act_lds, int nch)
+    {
+#pragma unroll
+        for (int i = 0; i < MAXC; ++i) {
+            const int it = threadIdx.x + NT * i;
+            if (it < NB * nch) {
+                float v[32];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint4 w = r[i][j];
+                    v[8 * j + 0] = bf16lo(w.x); v[8 * j + 1] = bf16hi(w.x); v[8 * j + 2] = bf16lo(w.y);
+                    v[8 * j + 3] = bf16hi(w.y); v[8 * j + 4] = bf16lo(w.z); v[8 * j + 5] = bf16hi(w.z);
+                    v[8 * j + 6] = bf16lo(w.w); v[8 * j + 7] = bf16hi(w.w);
+                }
+                const int b = it / nch, c = it - b * nch;
+                make_chunk_scaled(v, act_lds + (size_t)(c * NB + b) * ACT_WORDS);
+            }
+        }
+        __syncthreads();
+    }
+};
+
+// out_proj's gated norm: o = bf16(g w / rms_group(g)) from the SSM step's g w and per-(head,
+// half) sums of g^2 (K = d_inner), unscaled chunks (normalised values).  issue() loads the sums
+// and the thread's g w chunks before the caller's first weight loads.
+template <int NB, int NT>
+struct ActGatedNorm {
+    static constexpr int NCH = DINNER / 32, NPART = NHEADS * 2;
+    static constexpr int MAXC = (NB * NCH + NT - 1) / NT, MAXP = (NB * NPART + NT - 1) / NT;
+    const float *gate, *part;
+    float eps;
+    float pv[MAXP];
+    float4 gv[MAXC][8];
+    __device__ __forceinline__ void issue(int)
+    {
+        // unconditional loads (indices clamped), for the reason given in ActPlainK
+#pragma unroll
+        for (int i = 0; i < MAXP; ++i) pv[i] = part[min((int)threadIdx.x + NT * i, NB * NPART - 1)];
+#pragma unroll
+        for (int i = 0; i < MAXC; ++i) {
+            const int it = min((int)threadIdx.x + NT * i, NB * NCH - 1);
+            const int b = it / NCH, c = it - b * NCH;
+            const float4 *gp = reinterpret_cast<const float4 *>(gate + (size_t)b * DINNER + 32 * c);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) gv[i][j] = gp[j];
+        }
+    }
+    __device__ __forceinline__ void finish(uint32_t *act_lds, int)
+    {
+        __shared__ float rstd[NB][NGROUPS];
+#pragma unroll
+        for (int i = 0; i < MAXP; ++i) {
+            const int t = threadIdx.x + NT * i;  // whole waves: NB * NPART is a multiple of 64
+            const float tot = row_sum<32>(t < NB * NPART ? pv[i] : 0.f);
+            if (t < NB * NPART && (t & 31) == 0) rstd[t / NPART][(t % NPART) / 32] = 1.0f / sqrtf(tot / (float)GNORM + eps);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < MAXC; ++i) {
+            const int it = threadIdx.x + NT * i;
+            if (it < NB * NCH) {
+                const int b = it / NCH, c = it - b * NCH;
+                const float r = rstd[b][(32 * c) / GNORM];
+                float v[32];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    v[4 * j] = round_bf16(gv[i][j].x * r);
+                    v[4 * j + 1] = round_bf16(gv[i][j].y * r);
+                    v[4 * j + 2] = round_bf16(gv[i][j].z * r);
+                    v[4 * j + 3] = round_bf16(gv[i][j].w * r);
+                }
+                make_chunk(v, act_lds + (size_t)(c * NB + b) * ACT_WORDS);
+            }
+        }
+        __syncthreads();
+    }
+};
+
+template <int NB, int CH, bool SC, class Act, class Epi>
+__global__ __launch_bounds__(MFL_NT, 1) void k_w4_mfl(W4 W, Act act_in, Epi epi)
+{
+    Act act = act_in;
+    constexpr int NW = MFL_NT / 64;
+    extern __shared__ __attribute__((aligned(16))) uint32_t act_lds[];
+    const int lane = threadIdx.x & 63, kb = lane >> 2, q4 = lane & 3;
+    const int nch = W.k >> 5, nmax = W.n - 1;
+    const uint32_t rowbytes = (uint32_t)W.k / 2, kg2 = (uint32_t)(W.k >> 6) * 2;
+    const int nsl = ((nch + 15) / 16 + CH - 1) / CH;  // slices per stage
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void *)W.q, 0, (int)((uint32_t)W.n * rowbytes), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)W.s, 0, (int)((uint32_t)W.n * kg2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rbi = __builtin_amdgcn_make_buffer_rsrc((void *)W.b, 0, (int)((uint32_t)W.n * kg2), 0x00020000);
+    // this wave's 4-row stages [s0, s1): an even split per XCD, then per wave inside the XCD
+    const int nst = (W.n + 3) / 4;
+    const int xcd = blockIdx.x & 7, nwx = (int)(gridDim.x >> 3) * NW;
+    const int wx = __builtin_amdgcn_readfirstlane((int)((blockIdx.x >> 3) * NW + (threadIdx.x >> 6)));
+    const int xs = (int)((long)nst * xcd / 8), xn = (int)((long)nst * (xcd + 1) / 8) - xs;
+    const int s0 = xs + (int)((long)xn * wx / nwx), s1 = xs + (int)((long)xn * (wx + 1) / nwx);
+    const int eb = min(lane >> 2, NB - 1);
+    const int nu = (s1 - s0) * nsl;  // (stage, slice) units of this wave
+
+    // unit u = (stage s0 + u / nsl, slice u % nsl); loads past the wave's last unit re-read it
+    auto load = [&](MflUnit<CH> &g, int u) {
+        u = min(u, max(nu - 1, 0));
+        const int st = s0 + u / nsl, sl = u % nsl;
+        const uint32_t row = (uint32_t)min(4 * st + q4, nmax);
+#pragma unroll
+        for (int t = 0; t < CH; ++t) {
+            const uint32_t c = (uint32_t)min(kb + 16 * (CH * sl + t), nch - 1);
+            g.q[t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, row * rowbytes + 16u * c, 0, NT_LOAD));
+            g.s[t] = __builtin_amdgcn_raw_buffer_load_b16(rs, row * kg2 + 2u * (c >> 1), 0, 0);
+            g.b[t] = __builtin_amdgcn_raw_buffer_load_b16(rbi, row * kg2 + 2u * (c >> 1), 0, 0);
+        }
+    };
+    MflUnit<CH> A, B;
+    act.issue(nch);
+    EpiPre pe = epi.prefetch(min(4 * min(s0, nst - 1) + q4, nmax), eb);
+    load(A, 0);
+    // slot NB nch: a zero chunk, read by the lanes with no activation (batch rows beyond NB,
+    // chunks past the row), so that every lane's LDS read is unconditional
+    uint32_t *zslot = act_lds + (size_t)NB * nch * ACT_WORDS;
+    if (threadIdx.x < ACT_WORDS) zslot[threadIdx.x] = threadIdx.x == 18 ? 0x3F800000u : 0u;
+    act.finish(act_lds, nch);
+    if (nu == 0) return;
+
+    const uint32_t mlo = opaque_v(0x000F000Fu), mhi = opaque_v(0x00F000F0u), magic = opaque_v(0x64006400u);
+    const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+    floatx4 acc = zero, E = zero;
+    auto unit = [&](const MflUnit<CH> &g, int u) {
+        const int st = s0 + u / nsl, sl = u % nsl;
+#pragma unroll
+        for (int t = 0; t < CH; ++t) {
+            // the A operand: batch row q4's chunk (zero beyond NB and past the row)
+            const int c = kb + 16 * (CH * sl + t);
+            ActChunk a;
+            chunk_from_lds(a, q4 < NB && c < nch ? act_lds + ((size_t)c * NB + q4) * ACT_WORDS : zslot);
+            floatx4 D = __builtin_amdgcn_mfma_f32_4x4x1f32(-a.off, 1.0f, zero, 0, 0, 0), D2 = zero;
+            const uint32_t wq[4] = {g.q[t].x, g.q[t].y, g.q[t].z, g.q[t].w};
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t wd = wq[w], wh = wd >> 8;
+                const uint32_t d0 = and_or_mf(wd, mlo, magic), d1 = and_or_mf(wd, mhi, magic);
+                const uint32_t d2 = and_or_mf(wh, mlo, magic), d3 = and_or_mf(wh, mhi, magic);
+                D = __builtin_amdgcn_mfma_f32_4x4x4f16(h4_of(a.p[4 * w], a.p[4 * w + 2]), h4_of(d0, d2), D, 0, 0, 0);
+                D2 = __builtin_amdgcn_mfma_f32_4x4x4f16(h4_of(a.p[4 * w + 1], a.p[4 * w + 3]), h4_of(d1, d3), D2, 0, 0, 0);
+            }
+            const float sc = __uint_as_float((uint32_t)g.s[t] << 16), bi = __uint_as_float((uint32_t)g.b[t] << 16);
+            if constexpr (SC) {
+                const floatx4 Mb = __builtin_amdgcn_mfma_f32_4x4x1f32(a.mul, 1.0f, zero, 0, 0, 0);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[v] = fmaf(sc * Mb[v], fmaf(D2[v], 0.0625f, D[v]), acc[v]);
+                E = __builtin_amdgcn_mfma_f32_4x4x1f32(a.sum * a.mul, bi, E, 0, 0, 0);
+            } else {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[v] = fmaf(sc, fmaf(D2[v], 0.0625f, D[v]), acc[v]);
+                E = __builtin_amdgcn_mfma_f32_4x4x1f32(a.sum, bi, E, 0, 0, 0);
+            }
+        }
+        if (sl == nsl - 1) {
+            float tot[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                float x = acc[v] + E[v];
+                x += dpp_mov<0x124>(x);  // row_ror:4
+                x += dpp_mov<0x128>(x);  // row_ror:8
+                x += __shfl_xor(x, 16, 64);
+                x += __shfl_xor(x, 32, 64);
+                tot[v] = x;
+            }
+            const int bsel = lane >> 2;
+            const float mine = bsel == 0 ? tot[0] : bsel == 1 ? tot[1] : bsel == 2 ? tot[2] : tot[3];
+            const int row = 4 * st + q4;
+            if (lane < 4 * NB && row <= nmax) epi(row, bsel, mine, pe);
+            pe = epi.prefetch(min(4 * min(st + 1, nst - 1) + q4, nmax), eb);
+            acc = zero;
+            E = zero;
+        }
+    };
+    // two units per iteration with no conditional load; only the second compute is conditional
+    for (int u = 0; u < nu; u += 2) {
+        load(B, u + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        unit(A, u);
+        load(A, u + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        if (u + 1 < nu) unit(B, u + 1);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+size_t mfl_lds_bytes(int batch, int k) { return ((size_t)batch * (k / 32) + 1) * ACT_WORDS * 4; }
+
+// chunk slots per lane-block and slice for K = 32 nch: the fewest slots, then the largest CH
+static inline int mfl_ch(int k)
+{
+    const int mch = (k / 32 + 15) / 16;
+    int best = 10, slots = 1 << 30;
+    for (int ch : {10, 9, 8, 4}) {
+        const int sl = (mch + ch - 1) / ch * ch;
+        if (sl < slots) { slots = sl; best = ch; }
+    }
+    return best;
+}
+
+// the kernel with its dynamic LDS limit raised once (above 64 KiB it must be set explicitly)
+template <int NB, int CH, bool SC, class Act, class Epi>
+static hipError_t launch_mfl_ch(const W4 &W, const Act &a, const Epi &e, size_t lds, hipStream_t st)
+{
+    static size_t allowed = 64 * 1024;  // raised to the largest size asked for so far
+    if (lds > allowed) {
+        const hipError_t r = hipFuncSetAttribute((const void *)k_w4_mfl<NB, CH, SC, Act, Epi>,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (r != hipSuccess) return r;
+        allowed = lds;
+    }
+    launch_k(k_w4_mfl<NB, CH, SC, Act, Epi>, dim3(MF_WGS), dim3(MFL_NT), lds, st, W, a, e);
+    return hipGetLastError();
+}
+
+template <int NB, bool SC, class Act, class Epi>
+static hipError_t launch_mfl(const W4 &W, const Act &a, const Epi &e, hipStream_t st)
+{
+    const size_t lds = mfl_lds_bytes(NB, W.k);
+    switch (mfl_ch(W.k)) {
+    case 10: return launch_mfl_ch<NB, 10, SC>(W, a, e, lds, st);
+    case 9: return launch_mfl_ch<NB, 9, SC>(W, a, e, lds, st);
+    case 8: return launch_mfl_ch<NB, 8, SC>(W, a, e, lds, st);
+    default: return launch_mfl_ch<NB, 4, SC>(W, a, e, lds, st);
+    }
+}
+
 // Work-groups of four waves per CU for the generic GEMV: three or two at batch 1 while the
 // activations (CPL chunks of 18 registers per lane) leave room, one above: with 8 chunks per
 // lane (K above 10240, e.g. an MLP down projection of K = 15680) two per CU spilled.
@@ -901,7 +1205,7 @@ constexpr int gemv_wgs_per_cu(int nb, int cpl) { return nb == 1 ? (cpl <= 3 ? 3 
 template <int LPR, int CPL, int NB, int RG>
 __global__ __launch_bounds__(256, gemv_wgs_per_cu(NB, CPL)) void k_gemv(W4 W, const uint16_t *__restrict__ x, EpiStore epi)
 {
-    GemvRunner<LPR, CPL, NB, RG, EpiStore> run(W, epi, 256);
+    GemvRunner<LPR, CPL, NB, RG, EpiStore, true> run(W, epi, 256);
     extern __shared__ __attribute__((aligned(16))) uint32_t act_lds[];
     const int nch = W.k >> 5;
     for (int it = threadIdx.x; it < NB * nch; it += 256) {
@@ -914,7 +1218,7 @@ __global__ __launch_bounds__(256, gemv_wgs_per_cu(NB, CPL)) void k_gemv(W4 W, co
             v[8 * j + 3] = bf16hi(w.y); v[8 * j + 4] = bf16lo(w.z); v[8 * j + 5] = bf16hi(w.z);
             v[8 * j + 6] = bf16lo(w.w); v[8 * j + 7] = bf16hi(w.w);
         }
-        make_chunk(v, act_lds + (size_t)it * ACT_WORDS);
+        make_chunk_scaled(v, act_lds + (size_t)it * ACT_WORDS);
     }
     __syncthreads();
     ActChunk a[NB][CPL];
@@ -1365,8 +1669,11 @@ static hipError_t gemv_nb(const W4 &W, const uint16_t *x, EpiStore e, hipStream_
     if (nch <= 128) return run_gemv<64, 2, NB, 2>(W, x, e, st);
     if (nch <= 192) return run_gemv<64, 3, NB, (NB == 1 ? 2 : 1)>(W, x, e, st);
     if (nch <= 256) return run_gemv<64, 4, NB, 1>(W, x, e, st);
-    if (nch <= 320) return run_gemv<64, 5, NB, 1>(W, x, e, st);
-    return run_gemv<64, 8, NB, 1>(W, x, e, st);
+    // batch 4 above K = 5120 and batch 2-3 above K = 10240 go to the matrix-core kernel
+    if constexpr (NB <= 3)
+        if (nch <= 320) return run_gemv<64, 5, NB, 1>(W, x, e, st);
+    if constexpr (NB == 1) return run_gemv<64, 8, NB, 1>(W, x, e, st);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemv(const W4 &W, const uint16_t *x, int batch, const void *res, int res_t,
@@ -1383,6 +1690,18 @@ hipError_t launch_gemv(const W4 &W, const uint16_t *x, int batch, const void *re
             launch_k(k_w4_mf<4, BF16, false, EpiStore>, dim3(MF_WGS), dim3(256), lds, st, W, (const void *)x,
                      (const uint16_t *)nullptr, 0.f, e, (uint32_t *)nullptr, 0);
         return hipGetLastError();
+    }
+    // The matrix-core kernel with the activations in LDS where the per-row kernel's registers
+    // run out: K above 10240 at batch 2 to 4 (per-row: 28 / 90 / 164 us at K = 15680 against
+    // 18-19 us) and K above 5120 at batch 4 (K = 10240: 27.5 against 15.5 us).  Elsewhere the
+    // per-row kernel is faster (the matrix-core kernel's activation build takes about 7 us).
+    // K up to 16384, i.e. 512 chunks per row: at most NB chunks per thread.
+    if (batch >= 2 && (W.k > 10240 || (batch == 4 && W.k > 5120))) {
+        switch (batch) {
+        case 2: return launch_mfl<2, true>(W, ActPlainK<2, MFL_NT, 2>{x}, e, st);
+        case 3: return launch_mfl<3, true>(W, ActPlainK<3, MFL_NT, 3>{x}, e, st);
+        default: return launch_mfl<4, true>(W, ActPlainK<4, MFL_NT, 4>{x}, e, st);
+        }
     }
     switch (batch) {
     case 1: return gemv_nb<1>(W, x, e, st);
@@ -1404,7 +1723,8 @@ hipError_t launch_outproj_step(const W4 &W, const float *gate, const float *part
     case 1: launch_k(k_outproj_step<1>, dim3(grid), dim3(512), lds, st, W, gate, part, eps, e); break;
     case 2: launch_k(k_outproj_step<2>, dim3(grid), dim3(256), lds, st, W, gate, part, eps, e); break;
     case 3: launch_k(k_outproj_step<3>, dim3(grid), dim3(256), lds, st, W, gate, part, eps, e); break;
-    default: launch_k(k_outproj_step<4>, dim3(grid), dim3(256), lds, st, W, gate, part, eps, e); break;
+    // batch 4: the matrix-core kernel (19.3 us against 22.1 for the per-row kernel)
+    default: return launch_mfl<4, false>(W, ActGatedNorm<4, MFL_NT>{gate, part, eps}, e, st);
     }
     return hipGetLastError();
 }

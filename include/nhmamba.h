@@ -34,11 +34,17 @@
  *    run at the same time.
  *  - Results are deterministic for fixed inputs on a fixed device (no
  *    floating-point atomics).
- *  - Internal matrix-core operands are fp16: activations entering the
- *    chunked scan and the W4 GEMM must lie within the fp16 range
- *    (|v| < 65504); magnitudes below 2^-14 are carried with fp16 subnormal
- *    precision.  The block's own activations (normalised, SiLU-bounded) are
- *    far inside this range.
+ *  - Internal operands are fp16 where noted.  The chunked scan and the W4
+ *    GEMM need their activations within the fp16 range (|v| < 65504), and
+ *    magnitudes below 2^-14 keep only fp16 subnormal precision.  The W4 GEMM
+ *    dequantises exactly for scales 2^-17 <= |s| <= 8188 (or s = 0).
+ *  - W4 GEMV activations are staged in fp16 chunks of 32.  nh_w4_gemv (and
+ *    the MLP down and attention o_proj projections) scale each chunk by an
+ *    exact power of two, so every finite bf16 input is exact.  The pre-normed
+ *    projections stage u = x / rms(x) * w, with |u| <= sqrt(d) max|w|.  These
+ *    are in_proj, MLP up, attention q/k/v, the heads and out_proj.  They need
+ *    max|w| < 978 for the hidden-size norms and < 1830 for the gated norm.
+ *    None of these ranges is checked at run time.
  */
 #ifndef NHMAMBA_H
 #define NHMAMBA_H

@@ -111,6 +111,33 @@ def test_gemv_matrix_core_stage_tails(env, batch):
         assert gu.max_abs(got, ref) < 1e-4 * max(1.0, np.abs(ref).max()), n
 
 
+# Activations far outside the fp16 range: each 32-value chunk is staged in fp16 after an exact
+# power-of-two scaling, so bf16 inputs of any magnitude are multiplied exactly.  Rows mix
+# magnitudes 1e3..1e5 (the chunk maxima overflow fp16 unscaled), with some chunks of tiny values
+# (1e-3) and some exact zeros; every kernel of nh_w4_gemv is covered (per-row kernel, K = 4480
+# matrix-core kernel at batch 3-4, LDS matrix-core kernel above K = 10240 or at batch 4).
+@pytest.mark.parametrize("n,k,batch", [(300, 4480, 1), (300, 4480, 2), (1000, 4480, 3), (1000, 4480, 4),
+                                       (4480, 5120, 4), (4480, 10240, 1), (4480, 10240, 3), (4480, 10240, 4),
+                                       (4480, 15680, 1), (4480, 15680, 2), (4480, 15680, 4)])
+def test_gemv_large_activations(env, n, k, batch):
+    nh, oracle, gu, torch = env
+    _say("gemv large activations", n, k, batch)
+    rng = np.random.default_rng(7 * n + k + batch)
+    W = _asym(synth.w4_random(8, n, 1, 2, n, k), n + 1)
+    mag = 10.0 ** rng.uniform(3, 5, (batch, k))
+    xf = rng.normal(0, 1, (batch, k)) * mag
+    xf[:, 64:96] = rng.normal(0, 1e-3, (batch, 32))     # a chunk of tiny values
+    xf[:, 160:192] = 0.0                                  # an all-zero chunk
+    x = synth.f32_to_bf16(xf.astype(np.float32))
+    y = gu.empty_f32(batch, n)
+    nh.nh_w4_gemv(gu.w4_dev(W), gu.to_dev(x), batch, None, 0, y, nh.NH_F32)
+    ref = oracle.w4_matvec(W, gu.bf16_bits_to_f64(x))
+    got = y.cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    assert gu.rel_l2(got, ref) < 1e-5
+    assert gu.max_abs(got, ref) < 1e-4 * np.abs(ref).max()
+
+
 def test_gemv_residual_bf16_out(env):
     nh, oracle, gu, torch = env
     _say("gemv residual bf16")
