@@ -102,7 +102,7 @@ _sigs = {
     "nh_last_error": (C.c_char_p, []),
     "nh_version": (C.c_char_p, []),
     "nh_hybrid_pattern": (C.c_char_p, []),
-    "nh_w4_gemv": (_i, [_vp, _vp, _i, _vp, _i, _vp, _i, _vp]),
+    "nh_w4_gemv": (_i, [_vp, _vp, _i, _i, _vp, _i, _vp, _i, _vp]),
     "nh_w4_gemm_workspace_bytes": (_sz, [_i, _i]),
     "nh_w4_gemm": (_i, [_vp, _vp, _i, _vp, _i, _vp, _i, _vp, _sz, _vp]),
     "nh_rmsnorm": (_i, [_vp, _i, _vp, _vp, _i, _i, C.c_float, _vp]),
@@ -112,7 +112,7 @@ _sigs = {
     "nh_ssm_step": (_i, [_vp, _vp, _vp, _l, _vp, _vp, _vp, _vp, _vp, _i, _i, _vp]),
     "nh_ssd_scan_workspace_bytes": (_sz, [_vp, _i, _i]),
     "nh_ssd_chunk_scan": (_i, [_vp, _vp, _vp, _l, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _sz, _vp]),
-    "nh_rmsnorm_gated": (_i, [_vp, _vp, _l, _vp, _vp, _i, _i, _i, C.c_float, _vp]),
+    "nh_rmsnorm_gated": (_i, [_vp, _i, _vp, _l, _vp, _vp, _i, _i, _i, C.c_float, _vp]),
     "nh_block_workspace_bytes": (_sz, [_vp, _i, _i, _i]),
     "nh_mamba_block_step": (_i, [_vp, _vp, _vp, _vp, _i, _vp, _i, _i, _vp, _sz, _vp]),
     "nh_mamba_block_step_noalloc": (_i, [_vp, _vp, _vp, _vp, _i, _vp, _i, _i, _vp]),
@@ -201,8 +201,8 @@ def hybrid_pattern() -> str:
 
 # ------------------------------------------------------------------ entry points
 
-def nh_w4_gemv(W, x, batch, residual, res_dtype, y, y_dtype, stream=None):
-    _check(lib.nh_w4_gemv(C.byref(W), _ptr(x), batch, _ptr(residual), res_dtype, _ptr(y), y_dtype,
+def nh_w4_gemv(W, x, x_dtype, batch, residual, res_dtype, y, y_dtype, stream=None):
+    _check(lib.nh_w4_gemv(C.byref(W), _ptr(x), x_dtype, batch, _ptr(residual), res_dtype, _ptr(y), y_dtype,
                           _stream(stream)))
 
 
@@ -322,8 +322,8 @@ def nh_ssd_chunk_scan(d, xc, dt_raw, ld_dt, T, dt_bias, A_log, D, h0, h_final, y
                                  batch, _ptr(ws), ws_bytes, _stream(stream)))
 
 
-def nh_rmsnorm_gated(y, z, ld_z, w, out, rows, d, group, eps, stream=None):
-    _check(lib.nh_rmsnorm_gated(_ptr(y), _ptr(z), ld_z, _ptr(w), _ptr(out), rows, d, group, eps,
+def nh_rmsnorm_gated(y, y_dtype, z, ld_z, w, out, rows, d, group, eps, stream=None):
+    _check(lib.nh_rmsnorm_gated(_ptr(y), y_dtype, _ptr(z), ld_z, _ptr(w), _ptr(out), rows, d, group, eps,
                                 _stream(stream)))
 
 

@@ -267,7 +267,7 @@ nh_status block_seq(const nh_mamba_dims *d, const nh_mamba_weights *w, const nh_
                            init ? init->ssm_state : nullptr, fin ? fin->ssm_state : nullptr, k.y, BF16, B,
                            k.u, s),
            "scan");
-    NH_HIP(launch_rmsnorm_gated(k.y, k.zx, NIN, w->gnorm_w, k.o, 1, k.su_o, M, DINNER, GNORM, d->eps, s),
+    NH_HIP(launch_rmsnorm_gated(k.y, BF16, k.zx, NIN, w->gnorm_w, k.o, 1, k.su_o, M, DINNER, GNORM, d->eps, s),
            "gated norm");
     NH_HIP(launch_w4_gemm(view(&w->out_proj), k.o, k.su_o, M, x, x_t, out, out_t, s), "out_proj");
     return ok();
@@ -349,7 +349,7 @@ nh_status attention_step(const nh_attention_weights *w, const nh_kv_cache *c, co
                            c->k, c->v, pos, c->max_len, s),
            "attention q/k/v");
     NH_HIP(launch_attn_decode(a.q, c->k, c->v, pos, c->max_len, B, a.part, a.o, s), "attention");
-    NH_HIP(launch_gemv(view(&w->o_proj), a.o, B, x, x_t, out, out_t, s), "attention o_proj");
+    NH_HIP(launch_gemv(view(&w->o_proj), a.o, BF16, B, x, x_t, out, out_t, s), "attention o_proj");
     return NH_OK;
 }
 
@@ -382,17 +382,18 @@ const char *nh_hybrid_pattern(void)
     return "M-M-M-MM-M-M-M*-M-M-M*-M-M-M-M*-M-M-M-M*-M-MM-M-M-M-M-M-";
 }
 
-nh_status nh_w4_gemv(const nh_w4_matrix *W, const uint16_t *x, int batch, const void *residual,
+nh_status nh_w4_gemv(const nh_w4_matrix *W, const void *x, nh_dtype x_dtype, int batch, const void *residual,
                      nh_dtype res_dtype, void *y, nh_dtype y_dtype, void *stream)
 {
     NH_TRY(check_w4(W, "W"));
     NH_TRY(need_ptr(x, "x"));
+    NH_TRY(need_dtype(x_dtype, "x_dtype"));
     NH_TRY(need_ptr(y, "y"));
     NH_TRY(opt_ptr(residual, "residual"));
     NH_TRY(need_dtype(y_dtype, "y_dtype"));
     if (residual) NH_TRY(need_dtype(res_dtype, "res_dtype"));
     if (batch < 1 || batch > 4) return fail(NH_ERR_UNSUPPORTED_SHAPE, "batch %d outside 1..4", batch);
-    NH_HIP(launch_gemv(view(W), x, batch, residual, res_dtype, y, y_dtype, S(stream)), "gemv");
+    NH_HIP(launch_gemv(view(W), x, x_dtype, batch, residual, res_dtype, y, y_dtype, S(stream)), "gemv");
     return ok();
 }
 
@@ -423,7 +424,7 @@ nh_status nh_mlp_step(const uint16_t *norm_w, const nh_w4_matrix *up, const nh_w
     if (ws_bytes < need) return fail(NH_ERR_WORKSPACE_TOO_SMALL, "mlp workspace %zu < %zu bytes", ws_bytes, need);
     uint16_t *h = reinterpret_cast<uint16_t *>(ws);
     NH_HIP(launch_mlp_up_step(view(up), x, x_dtype, norm_w, eps, batch, h, S(stream)), "mlp up");
-    NH_HIP(launch_gemv(view(down), h, batch, x, x_dtype, out, out_dtype, S(stream)), "mlp down");
+    NH_HIP(launch_gemv(view(down), h, BF16, batch, x, x_dtype, out, out_dtype, S(stream)), "mlp down");
     return ok();
 }
 
@@ -604,17 +605,18 @@ nh_status nh_ssd_chunk_scan(const nh_mamba_dims *d, const uint16_t *xc, const ui
     return ok();
 }
 
-nh_status nh_rmsnorm_gated(const uint16_t *y, const uint16_t *z, long ld_z, const uint16_t *w, uint16_t *out,
-                           int rows, int d, int group, float eps, void *stream)
+nh_status nh_rmsnorm_gated(const void *y, nh_dtype y_dtype, const uint16_t *z, long ld_z, const uint16_t *w,
+                           uint16_t *out, int rows, int d, int group, float eps, void *stream)
 {
     NH_TRY(need_ptr(y, "y"));
+    NH_TRY(need_dtype(y_dtype, "y_dtype"));
     NH_TRY(need_ptr(z, "z"));
     NH_TRY(need_ptr(w, "w"));
     NH_TRY(need_ptr(out, "out"));
     if (rows < 1 || group < 8 || group % 8 || d % group || group > 8192 || ld_z < d || ld_z % 8)
         return fail(NH_ERR_UNSUPPORTED_SHAPE, "rows %d, d %d, group %d, ld_z %ld", rows, d, group, ld_z);
     if (!(eps > 0.f) || !std::isfinite(eps)) return fail(NH_ERR_INVALID_ARGUMENT, "eps must be positive");
-    NH_HIP(launch_rmsnorm_gated(y, z, ld_z, w, out, 0, nullptr, rows, d, group, eps, S(stream)), "gated norm");
+    NH_HIP(launch_rmsnorm_gated(y, y_dtype, z, ld_z, w, out, 0, nullptr, rows, d, group, eps, S(stream)), "gated norm");
     return ok();
 }
 
@@ -883,7 +885,7 @@ nh_status nh_lm_step(const nh_mamba_dims *d, const nh_lm_weights *w, nh_mamba_st
             const nh_mlp_weights &m = w->mlp[li++];
             uint16_t *h = reinterpret_cast<uint16_t *>(scratch);
             NH_HIP(launch_mlp_up_step(view(&m.up), cur, F32, m.norm_w, d->eps, batch, h, s), "mlp up");
-            NH_HIP(launch_gemv(view(&m.down), h, batch, cur, F32, nxt, F32, s), "mlp down");
+            NH_HIP(launch_gemv(view(&m.down), h, BF16, batch, cur, F32, nxt, F32, s), "mlp down");
         } else {
             NH_TRY(attention_step(&w->attn[ai], &caches[ai], positions, cur, F32, nxt, F32, batch, d->eps, scratch,
                                   s));

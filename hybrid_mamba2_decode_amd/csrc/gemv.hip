@@ -125,6 +125,38 @@ __device__ __forceinline__ void make_chunk_scaled(const float *v, uint32_t *dst)
     dst[18] = __float_as_uint(mul);
 }
 
+// The raw words of one 32-value chunk of x (bf16 bits or fp32), loaded as they are (so that a
+// caller can issue the loads early and unpack later); fp32 values are rounded to bf16 when
+// unpacked, the GEMV's activation precision.
+template <int XT>
+struct XChunk {
+    static constexpr int NW = XT == BF16 ? 4 : 8;
+    uint4 r[NW];
+    __device__ __forceinline__ void load(const void *x, size_t chunk)
+    {
+        const uint4 *src = XT == BF16
+            ? reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(x) + chunk * 32)
+            : reinterpret_cast<const uint4 *>(reinterpret_cast<const float *>(x) + chunk * 32);
+#pragma unroll
+        for (int j = 0; j < NW; ++j) r[j] = src[j];
+    }
+    __device__ __forceinline__ void unpack(float (&v)[32]) const
+    {
+#pragma unroll
+        for (int j = 0; j < NW; ++j) {
+            const uint4 w = r[j];
+            if constexpr (XT == BF16) {
+                v[8 * j + 0] = bf16lo(w.x); v[8 * j + 1] = bf16hi(w.x); v[8 * j + 2] = bf16lo(w.y);
+                v[8 * j + 3] = bf16hi(w.y); v[8 * j + 4] = bf16lo(w.z); v[8 * j + 5] = bf16hi(w.z);
+                v[8 * j + 6] = bf16lo(w.w); v[8 * j + 7] = bf16hi(w.w);
+            } else {
+                v[4 * j + 0] = round_bf16(__uint_as_float(w.x)); v[4 * j + 1] = round_bf16(__uint_as_float(w.y));
+                v[4 * j + 2] = round_bf16(__uint_as_float(w.z)); v[4 * j + 3] = round_bf16(__uint_as_float(w.w));
+            }
+        }
+    }
+};
+
 template <int LPR>
 struct GemvShape {
     static constexpr int RPG = 64 / LPR;  // rows per wave-instruction
@@ -704,23 +736,18 @@ struct PreNorm {
 // The activation source of the K = hidden kernels without a pre-norm: the bf16 rows of x go to
 // LDS in the activation format as they are, with PreNorm's interface (thread t < 140 owns
 // chunk t of every batch row).
-template <int NB, int NT>
+template <int NB, int NT, int XT>
 struct PlainAct {
     static constexpr int NCH = HIDDEN / 32, NW = NT / 64;
     bool own;
-    uint4 xr[NB][4];
+    XChunk<XT> xr[NB];
 
     __device__ __forceinline__ void issue(const void *x, const uint16_t *)
     {
         own = (int)threadIdx.x < NCH;
         if (own) {
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                const uint4 *src = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(x) +
-                                                                   (size_t)b * HIDDEN + 32 * threadIdx.x);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) xr[b][j] = src[j];
-            }
+            for (int b = 0; b < NB; ++b) xr[b].load(x, (size_t)b * NCH + threadIdx.x);
         }
     }
 
@@ -730,13 +757,7 @@ struct PlainAct {
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
                 float v[32];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint4 r = xr[b][j];
-                    v[8 * j + 0] = bf16lo(r.x); v[8 * j + 1] = bf16hi(r.x); v[8 * j + 2] = bf16lo(r.y);
-                    v[8 * j + 3] = bf16hi(r.y); v[8 * j + 4] = bf16lo(r.z); v[8 * j + 5] = bf16hi(r.z);
-                    v[8 * j + 6] = bf16lo(r.w); v[8 * j + 7] = bf16hi(r.w);
-                }
+                xr[b].unpack(v);
                 make_chunk_scaled(v, act_lds + ((size_t)b * NCH + threadIdx.x) * ACT_WORDS);
             }
         }
@@ -814,7 +835,7 @@ __global__ __launch_bounds__(256, 1) void k_w4_mf(W4 W, const void *__restrict__
     extern __shared__ __attribute__((aligned(16))) uint32_t act_lds[];
     __shared__ float red[NB][NW];
     if (blockIdx.x == 0 && (int)threadIdx.x < nzero) zero_ptr[threadIdx.x] = 0u;
-    std::conditional_t<NORM, PreNorm<NB, XT, NT>, PlainAct<NB, NT>> pn;
+    std::conditional_t<NORM, PreNorm<NB, XT, NT>, PlainAct<NB, NT, XT>> pn;
     pn.issue(x, nw);
     __builtin_amdgcn_sched_barrier(0);
 
@@ -949,21 +970,16 @@ struct MflUnit {
 // x [NB][k] bf16 as scaled chunks.  issue() loads a thread's chunks (chunk it = b nch + c
 // for it = thread, thread + NT, ...; at most MAXC per thread) before the caller's first weight
 // loads, so that they do not queue behind them; finish() builds the LDS slots.
-template <int NB, int NT, int MAXC>
+template <int NB, int NT, int MAXC, int XT>
 struct ActPlainK {
-    const uint16_t *x;
-    uint4 r[MAXC][4];
+    const void *x;
+    XChunk<XT> r[MAXC];
     __device__ __forceinline__ void issue(int nch)
     {
         // unconditional (indices clamped): after a conditional load the compiler's wait for its
         // registers would also wait for every load issued after it, the weight stream included
 #pragma unroll
-        for (int i = 0; i < MAXC; ++i) {
-            const int it = min((int)threadIdx.x + NT * i, NB * nch - 1);
-            const uint4 *src = reinterpret_cast<const uint4 *>(x + (size_t)it * 32);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) r[i][j] = src[j];
-        }
+        for (int i = 0; i < MAXC; ++i) r[i].load(x, (size_t)min((int)threadIdx.x + NT * i, NB * nch - 1));
     }
     __device__ __forceinline__ void finish(uint32_t *act_lds, int nch)
     {
@@ -972,13 +988,7 @@ struct ActPlainK {
             const int it = threadIdx.x + NT * i;
             if (it < NB * nch) {
                 float v[32];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint4 w = r[i][j];
-                    v[8 * j + 0] = bf16lo(w.x); v[8 * j + 1] = bf16hi(w.x); v[8 * j + 2] = bf16lo(w.y);
-                    v[8 * j + 3] = bf16hi(w.y); v[8 * j + 4] = bf16lo(w.z); v[8 * j + 5] = bf16hi(w.z);
-                    v[8 * j + 6] = bf16lo(w.w); v[8 * j + 7] = bf16hi(w.w);
-                }
+                r[i].unpack(v);
                 const int b = it / nch, c = it - b * nch;
                 make_chunk_scaled(v, act_lds + (size_t)(c * NB + b) * ACT_WORDS);
             }
@@ -1202,22 +1212,17 @@ constexpr int gemv_wgs_per_cu(int nb, int cpl) { return nb == 1 ? (cpl <= 3 ? 3 
 
 // ------------------------------------------------------------------ kernels
 
-template <int LPR, int CPL, int NB, int RG>
-__global__ __launch_bounds__(256, gemv_wgs_per_cu(NB, CPL)) void k_gemv(W4 W, const uint16_t *__restrict__ x, EpiStore epi)
+template <int LPR, int CPL, int NB, int RG, int XT>
+__global__ __launch_bounds__(256, gemv_wgs_per_cu(NB, CPL)) void k_gemv(W4 W, const void *__restrict__ x, EpiStore epi)
 {
     GemvRunner<LPR, CPL, NB, RG, EpiStore, true> run(W, epi, 256);
     extern __shared__ __attribute__((aligned(16))) uint32_t act_lds[];
     const int nch = W.k >> 5;
-    for (int it = threadIdx.x; it < NB * nch; it += 256) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(x + (size_t)it * 32);  // [b][c] = b*nch + c
+    for (int it = threadIdx.x; it < NB * nch; it += 256) {  // chunk it = b nch + c
+        XChunk<XT> xc;
+        xc.load(x, (size_t)it);
         float v[32];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint4 w = src[j];
-            v[8 * j + 0] = bf16lo(w.x); v[8 * j + 1] = bf16hi(w.x); v[8 * j + 2] = bf16lo(w.y);
-            v[8 * j + 3] = bf16hi(w.y); v[8 * j + 4] = bf16lo(w.z); v[8 * j + 5] = bf16hi(w.z);
-            v[8 * j + 6] = bf16lo(w.w); v[8 * j + 7] = bf16hi(w.w);
-        }
+        xc.unpack(v);
         make_chunk_scaled(v, act_lds + (size_t)it * ACT_WORDS);
     }
     __syncthreads();
@@ -1651,43 +1656,42 @@ static int gemv_grid(int n, int rows_per_stage, int wgs_per_cu)
     return g < cap ? g : cap;
 }
 
-template <int LPR, int CPL, int NB, int RG>
-static hipError_t run_gemv(const W4 &W, const uint16_t *x, EpiStore e, hipStream_t st)
+template <int LPR, int CPL, int NB, int RG, int XT>
+static hipError_t run_gemv(const W4 &W, const void *x, EpiStore e, hipStream_t st)
 {
     const size_t lds = (size_t)NB * (W.k >> 5) * ACT_WORDS * 4;
     const int grid = gemv_grid(W.n, RG * (64 / LPR), gemv_wgs_per_cu(NB, CPL));
-    k_gemv<LPR, CPL, NB, RG><<<dim3(grid), dim3(256), lds, st>>>(W, x, e);
+    k_gemv<LPR, CPL, NB, RG, XT><<<dim3(grid), dim3(256), lds, st>>>(W, x, e);
     return hipGetLastError();
 }
 
-template <int NB>
-static hipError_t gemv_nb(const W4 &W, const uint16_t *x, EpiStore e, hipStream_t st)
+template <int NB, int XT>
+static hipError_t gemv_nb(const W4 &W, const void *x, EpiStore e, hipStream_t st)
 {
     const int nch = W.k >> 5;
-    if (nch <= 32) return run_gemv<32, 1, NB, 2>(W, x, e, st);
-    if (nch <= 64) return run_gemv<64, 1, NB, 2>(W, x, e, st);
-    if (nch <= 128) return run_gemv<64, 2, NB, 2>(W, x, e, st);
-    if (nch <= 192) return run_gemv<64, 3, NB, (NB == 1 ? 2 : 1)>(W, x, e, st);
-    if (nch <= 256) return run_gemv<64, 4, NB, 1>(W, x, e, st);
+    if (nch <= 32) return run_gemv<32, 1, NB, 2, XT>(W, x, e, st);
+    if (nch <= 64) return run_gemv<64, 1, NB, 2, XT>(W, x, e, st);
+    if (nch <= 128) return run_gemv<64, 2, NB, 2, XT>(W, x, e, st);
+    if (nch <= 192) return run_gemv<64, 3, NB, (NB == 1 ? 2 : 1), XT>(W, x, e, st);
+    if (nch <= 256) return run_gemv<64, 4, NB, 1, XT>(W, x, e, st);
     // batch 4 above K = 5120 and batch 2-3 above K = 10240 go to the matrix-core kernel
     if constexpr (NB <= 3)
-        if (nch <= 320) return run_gemv<64, 5, NB, 1>(W, x, e, st);
-    if constexpr (NB == 1) return run_gemv<64, 8, NB, 1>(W, x, e, st);
+        if (nch <= 320) return run_gemv<64, 5, NB, 1, XT>(W, x, e, st);
+    if constexpr (NB == 1) return run_gemv<64, 8, NB, 1, XT>(W, x, e, st);
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_gemv(const W4 &W, const uint16_t *x, int batch, const void *res, int res_t,
-                       void *y, int y_t, hipStream_t st)
+template <int XT>
+static hipError_t launch_gemv_t(const W4 &W, const void *x, int batch, EpiStore e, hipStream_t st)
 {
-    EpiStore e{y, res, y_t, res_t, W.n};
     // K = hidden at batch 3 and 4: the matrix-core kernel of the batched in_proj
     if (W.k == HIDDEN && batch >= 3) {
         const size_t lds = (size_t)batch * (HIDDEN / 32) * ACT_WORDS * 4;
         if (batch == 3)
-            launch_k(k_w4_mf<3, BF16, false, EpiStore>, dim3(MF_WGS), dim3(256), lds, st, W, (const void *)x,
+            launch_k(k_w4_mf<3, XT, false, EpiStore>, dim3(MF_WGS), dim3(256), lds, st, W, x,
                      (const uint16_t *)nullptr, 0.f, e, (uint32_t *)nullptr, 0);
         else
-            launch_k(k_w4_mf<4, BF16, false, EpiStore>, dim3(MF_WGS), dim3(256), lds, st, W, (const void *)x,
+            launch_k(k_w4_mf<4, XT, false, EpiStore>, dim3(MF_WGS), dim3(256), lds, st, W, x,
                      (const uint16_t *)nullptr, 0.f, e, (uint32_t *)nullptr, 0);
         return hipGetLastError();
     }
@@ -1698,17 +1702,24 @@ hipError_t launch_gemv(const W4 &W, const uint16_t *x, int batch, const void *re
     // K up to 16384, i.e. 512 chunks per row: at most NB chunks per thread.
     if (batch >= 2 && (W.k > 10240 || (batch == 4 && W.k > 5120))) {
         switch (batch) {
-        case 2: return launch_mfl<2, true>(W, ActPlainK<2, MFL_NT, 2>{x}, e, st);
-        case 3: return launch_mfl<3, true>(W, ActPlainK<3, MFL_NT, 3>{x}, e, st);
-        default: return launch_mfl<4, true>(W, ActPlainK<4, MFL_NT, 4>{x}, e, st);
+        case 2: return launch_mfl<2, true>(W, ActPlainK<2, MFL_NT, 2, XT>{x}, e, st);
+        case 3: return launch_mfl<3, true>(W, ActPlainK<3, MFL_NT, 3, XT>{x}, e, st);
+        default: return launch_mfl<4, true>(W, ActPlainK<4, MFL_NT, 4, XT>{x}, e, st);
         }
     }
     switch (batch) {
-    case 1: return gemv_nb<1>(W, x, e, st);
-    case 2: return gemv_nb<2>(W, x, e, st);
-    case 3: return gemv_nb<3>(W, x, e, st);
-    default: return gemv_nb<4>(W, x, e, st);
+    case 1: return gemv_nb<1, XT>(W, x, e, st);
+    case 2: return gemv_nb<2, XT>(W, x, e, st);
+    case 3: return gemv_nb<3, XT>(W, x, e, st);
+    default: return gemv_nb<4, XT>(W, x, e, st);
     }
+}
+
+hipError_t launch_gemv(const W4 &W, const void *x, int x_t, int batch, const void *res, int res_t,
+                       void *y, int y_t, hipStream_t st)
+{
+    EpiStore e{y, res, y_t, res_t, W.n};
+    return x_t == BF16 ? launch_gemv_t<BF16>(W, x, batch, e, st) : launch_gemv_t<F32>(W, x, batch, e, st);
 }
 
 hipError_t launch_outproj_step(const W4 &W, const float *gate, const float *part,

@@ -44,7 +44,8 @@ struct W4 {
 // Device address and size of this device's allocation-free scratch array (looked up once per
 // device with hipGetSymbolAddress; the current device is the caller's).
 hipError_t noalloc_scratch(void **ptr, size_t *bytes);
-hipError_t launch_gemv(const W4 &W, const uint16_t *x, int batch, const void *res, int res_t,
+// y = W x (+ res): x [batch][W.k] bf16 or fp32 (x_t; fp32 values are rounded to bf16).
+hipError_t launch_gemv(const W4 &W, const void *x, int x_t, int batch, const void *res, int res_t,
                        void *y, int y_t, hipStream_t st);
 // Fused: RMSNorm(x) -> in_proj GEMV -> split; xBC rows go through the conv step (state
 // updated in place), z and dt_raw rows are stored.  Also zeroes `nzero` words at zero_ptr.
@@ -99,7 +100,7 @@ hipError_t launch_attn_decode(const uint16_t *q, const uint16_t *kc, const uint1
 // matrix-core operand format); su (nullable): per-64-group sums of u, [d/64][rows].
 hipError_t launch_rmsnorm(const void *x, int x_t, const uint16_t *w, uint16_t *u, int out_kind,
                           float *su, int rows, int d, float eps, hipStream_t st);
-hipError_t launch_rmsnorm_gated(const uint16_t *y, const uint16_t *z, long ld_z,
+hipError_t launch_rmsnorm_gated(const void *y, int y_t, const uint16_t *z, long ld_z,
                                 const uint16_t *w, uint16_t *out, int out_kind, float *su,
                                 int rows, int d, int group, float eps, hipStream_t st);
 hipError_t launch_conv_seq(const uint16_t *xbc, long ld, int T, const uint16_t *state_in,

@@ -15,6 +15,26 @@ __device__ __forceinline__ float group8_sum(float v)
     return v;
 }
 
+// Eight consecutive values of y (bf16 bits or fp32) at element offset i.
+template <int YT>
+__device__ __forceinline__ void load_y8(const void *y, size_t i, float (&v)[8])
+{
+    if constexpr (YT == BF16) {
+        const uint4 t = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(y) + i);
+        const uint32_t a[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v[2 * e] = bf16lo(a[e]);
+            v[2 * e + 1] = bf16hi(a[e]);
+        }
+    } else {
+        const float4 *p = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(y) + i);
+        const float4 a = p[0], b = p[1];
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+}
+
 __device__ __forceinline__ float block_sum256(float v, float *red)
 {
     v = wave_sum(v);
@@ -120,7 +140,8 @@ hipError_t launch_rmsnorm(const void *x, int x_t, const uint16_t *w, uint16_t *u
 
 // ---------------------------------------------------------- gated RMSNorm
 // One work-group per (row, group of channels).  g = y * silu(z); out = g / rms(g) * w.
-__global__ __launch_bounds__(256) void k_rmsnorm_gated(const uint16_t *__restrict__ y,
+template <int YT>
+__global__ __launch_bounds__(256) void k_rmsnorm_gated(const void *__restrict__ y,
                                                        const uint16_t *__restrict__ z, long ld_z,
                                                        const uint16_t *__restrict__ w,
                                                        uint16_t *__restrict__ out, int kind,
@@ -138,13 +159,14 @@ __global__ __launch_bounds__(256) void k_rmsnorm_gated(const uint16_t *__restric
     for (int i = 0; i < RN_MAXV; ++i) {
         const int vi = threadIdx.x + 256 * i;
         if (vi < nv) {
-            const uint4 yy = *reinterpret_cast<const uint4 *>(y + row * d + base + 8 * vi);
+            float yv[8];
+            load_y8<YT>(y, row * d + base + 8 * vi, yv);
             const uint4 zz = *reinterpret_cast<const uint4 *>(z + row * ld_z + base + 8 * vi);
-            const uint32_t ya[4] = {yy.x, yy.y, yy.z, yy.w}, za[4] = {zz.x, zz.y, zz.z, zz.w};
+            const uint32_t za[4] = {zz.x, zz.y, zz.z, zz.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                gv[i][2 * e] = bf16lo(ya[e]) * silu(bf16lo(za[e]));
-                gv[i][2 * e + 1] = bf16hi(ya[e]) * silu(bf16hi(za[e]));
+                gv[i][2 * e] = yv[2 * e] * silu(bf16lo(za[e]));
+                gv[i][2 * e + 1] = yv[2 * e + 1] * silu(bf16hi(za[e]));
             }
 #pragma unroll
             for (int e = 0; e < 8; ++e) ss += gv[i][e] * gv[i][e];
@@ -179,7 +201,8 @@ __global__ __launch_bounds__(256) void k_rmsnorm_gated(const uint16_t *__restric
 // sum of squares is accumulated in another order.
 constexpr int RG_MAXI = 4;  // 16-byte vectors per lane: group <= 64 * 8 * RG_MAXI
 
-__global__ __launch_bounds__(256) void k_rmsnorm_gated_w(const uint16_t *__restrict__ y,
+template <int YT>
+__global__ __launch_bounds__(256) void k_rmsnorm_gated_w(const void *__restrict__ y,
                                                          const uint16_t *__restrict__ z, long ld_z,
                                                          const uint16_t *__restrict__ w,
                                                          uint16_t *__restrict__ out, int kind,
@@ -198,13 +221,14 @@ __global__ __launch_bounds__(256) void k_rmsnorm_gated_w(const uint16_t *__restr
     for (int i = 0; i < RG_MAXI; ++i) {
         const int vi = lane + 64 * i;
         if (vi < nv) {
-            const uint4 yy = *reinterpret_cast<const uint4 *>(y + row * d + base + 8 * vi);
+            float yv[8];
+            load_y8<YT>(y, row * d + base + 8 * vi, yv);
             const uint4 zz = *reinterpret_cast<const uint4 *>(z + row * ld_z + base + 8 * vi);
-            const uint32_t ya[4] = {yy.x, yy.y, yy.z, yy.w}, za[4] = {zz.x, zz.y, zz.z, zz.w};
+            const uint32_t za[4] = {zz.x, zz.y, zz.z, zz.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                gv[i][2 * e] = bf16lo(ya[e]) * silu(bf16lo(za[e]));
-                gv[i][2 * e + 1] = bf16hi(ya[e]) * silu(bf16hi(za[e]));
+                gv[i][2 * e] = yv[2 * e] * silu(bf16lo(za[e]));
+                gv[i][2 * e + 1] = yv[2 * e + 1] * silu(bf16hi(za[e]));
             }
 #pragma unroll
             for (int e = 0; e < 8; ++e) ss += gv[i][e] * gv[i][e];
@@ -234,18 +258,23 @@ __global__ __launch_bounds__(256) void k_rmsnorm_gated_w(const uint16_t *__restr
     }
 }
 
-hipError_t launch_rmsnorm_gated(const uint16_t *y, const uint16_t *z, long ld_z,
+hipError_t launch_rmsnorm_gated(const void *y, int y_t, const uint16_t *z, long ld_z,
                                 const uint16_t *w, uint16_t *out, int out_kind, float *su,
                                 int rows, int d, int group, float eps, hipStream_t st)
 {
     if (rows <= 0) return hipSuccess;
     if (group <= 64 * 8 * RG_MAXI) {
-        const long units = (long)rows * (d / group);
-        k_rmsnorm_gated_w<<<dim3((unsigned)((units + 3) / 4)), dim3(256), 0, st>>>(y, z, ld_z, w, out, out_kind, su,
-                                                                                 rows, d, group, eps);
+        const dim3 grid((unsigned)(((long)rows * (d / group) + 3) / 4)), block(256);
+        if (y_t == BF16)
+            k_rmsnorm_gated_w<BF16><<<grid, block, 0, st>>>(y, z, ld_z, w, out, out_kind, su, rows, d, group, eps);
+        else
+            k_rmsnorm_gated_w<F32><<<grid, block, 0, st>>>(y, z, ld_z, w, out, out_kind, su, rows, d, group, eps);
     } else {
         dim3 grid(rows, d / group), block(256);
-        k_rmsnorm_gated<<<grid, block, 0, st>>>(y, z, ld_z, w, out, out_kind, su, d, group, eps);
+        if (y_t == BF16)
+            k_rmsnorm_gated<BF16><<<grid, block, 0, st>>>(y, z, ld_z, w, out, out_kind, su, d, group, eps);
+        else
+            k_rmsnorm_gated<F32><<<grid, block, 0, st>>>(y, z, ld_z, w, out, out_kind, su, d, group, eps);
     }
     return hipGetLastError();
 }

@@ -131,10 +131,15 @@ nh_status nh_profile_events(void *const *events, int n);
 /* ---------------------------------------------------------- primitives */
 
 /* y = W x (+ residual): the W4 dequantising matrix-vector product for small
- * batches (per-position decode).  x: bf16 [batch][k_in]; residual: nullable,
- * [batch][n_out] of res_dtype; y: [batch][n_out] of y_dtype (fp32
- * accumulation, one rounding at the end).  batch 1..4. */
-nh_status nh_w4_gemv(const nh_w4_matrix *W, const uint16_t *x, int batch,
+ * batches, the per-position decode of the in_proj / out_proj rows of the
+ * scope (issue page, section "config.json": 4-bit, group 64; docs page,
+ * "Online session": one position at a time).  x: [batch][k_in] of x_dtype
+ * (fp32 values are rounded to bf16, the activation precision of every
+ * projection here); residual: nullable, [batch][n_out] of res_dtype; y:
+ * [batch][n_out] of y_dtype (fp32 accumulation, one rounding at the end).
+ * Any finite x (each 32-value chunk is staged in fp16 after an exact
+ * power-of-two scaling).  batch 1..4. */
+nh_status nh_w4_gemv(const nh_w4_matrix *W, const void *x, nh_dtype x_dtype, int batch,
                      const void *residual, nh_dtype res_dtype,
                      void *y, nh_dtype y_dtype, void *stream);
 
@@ -215,12 +220,15 @@ nh_status nh_ssd_chunk_scan(const nh_mamba_dims *d, const uint16_t *xc, const ui
                             nh_dtype y_dtype, int batch, void *ws, size_t ws_bytes,
                             void *stream);
 
-/* Gated RMSNorm: g = y * silu(z); every block of `group` channels is
- * normalised by its own RMS (eps inside the root) and multiplied by its
- * slice of w.  y: bf16 [rows][d]; z: bf16, row r at z + r*ld_z; w: bf16 [d];
- * out: bf16 [rows][d].  d % group == 0, group % 8 == 0. */
-nh_status nh_rmsnorm_gated(const uint16_t *y, const uint16_t *z, long ld_z, const uint16_t *w,
-                           uint16_t *out, int rows, int d, int group, float eps, void *stream);
+/* Gated RMSNorm (issue page, section "config.json": n_groups 8,
+ * layer_norm_epsilon 1e-5; Mamba2's norm before out_proj): g = y * silu(z);
+ * every block of `group` channels is normalised by its own RMS (eps inside
+ * the root) and multiplied by its slice of w.  y: [rows][d] of y_dtype; z:
+ * bf16, row r at z + r*ld_z; w: bf16 [d]; out: bf16 [rows][d].
+ * d % group == 0, group % 8 == 0, group <= 8192. */
+nh_status nh_rmsnorm_gated(const void *y, nh_dtype y_dtype, const uint16_t *z, long ld_z,
+                           const uint16_t *w, uint16_t *out, int rows, int d, int group,
+                           float eps, void *stream);
 
 /* ----------------------------------------------------------- model top */
 

@@ -56,19 +56,20 @@ def _status(fn):
 
 def test_gemv_rejects_bad_arguments(nh):
     A = 0x20000  # aligned fake addresses: validation fails before any use
-    assert _status(lambda: nh.nh_w4_gemv(_fake_w4(gs=32), A, 1, None, 0, A, 0, 0)) == nh.NH_ERR_UNSUPPORTED_SHAPE
-    assert _status(lambda: nh.nh_w4_gemv(_fake_w4(k=96), A, 1, None, 0, A, 0, 0)) == nh.NH_ERR_UNSUPPORTED_SHAPE
-    assert _status(lambda: nh.nh_w4_gemv(_fake_w4(), None, 1, None, 0, A, 0, 0)) == nh.NH_ERR_INVALID_ARGUMENT
-    assert _status(lambda: nh.nh_w4_gemv(_fake_w4(), A + 2, 1, None, 0, A, 0, 0)) == nh.NH_ERR_MISALIGNED
-    assert _status(lambda: nh.nh_w4_gemv(_fake_w4(), A, 5, None, 0, A, 0, 0)) == nh.NH_ERR_UNSUPPORTED_SHAPE
-    assert _status(lambda: nh.nh_w4_gemv(_fake_w4(), A, 1, None, 0, A, 7, 0)) == nh.NH_ERR_INVALID_ARGUMENT
+    assert _status(lambda: nh.nh_w4_gemv(_fake_w4(gs=32), A, 0, 1, None, 0, A, 0, 0)) == nh.NH_ERR_UNSUPPORTED_SHAPE
+    assert _status(lambda: nh.nh_w4_gemv(_fake_w4(k=96), A, 0, 1, None, 0, A, 0, 0)) == nh.NH_ERR_UNSUPPORTED_SHAPE
+    assert _status(lambda: nh.nh_w4_gemv(_fake_w4(), None, 0, 1, None, 0, A, 0, 0)) == nh.NH_ERR_INVALID_ARGUMENT
+    assert _status(lambda: nh.nh_w4_gemv(_fake_w4(), A + 2, 0, 1, None, 0, A, 0, 0)) == nh.NH_ERR_MISALIGNED
+    assert _status(lambda: nh.nh_w4_gemv(_fake_w4(), A, 0, 5, None, 0, A, 0, 0)) == nh.NH_ERR_UNSUPPORTED_SHAPE
+    assert _status(lambda: nh.nh_w4_gemv(_fake_w4(), A, 0, 1, None, 0, A, 7, 0)) == nh.NH_ERR_INVALID_ARGUMENT
+    assert _status(lambda: nh.nh_w4_gemv(_fake_w4(), A, 2, 1, None, 0, A, 0, 0)) == nh.NH_ERR_INVALID_ARGUMENT
     assert "batch" in nh.lib.nh_last_error().decode() or "dtype" in nh.lib.nh_last_error().decode()
 
 
 def test_packed_matrix_over_2gib_rejected(nh):
     A = 0x20000
     big = nh_w4(A, A + 0x1000, A + 0x2000, 1 << 18, 16384, 64)   # 2 GiB of packed words
-    assert _status(lambda: nh.nh_w4_gemv(big, A, 1, None, 0, A, 0, 0)) == nh.NH_ERR_UNSUPPORTED_SHAPE
+    assert _status(lambda: nh.nh_w4_gemv(big, A, 0, 1, None, 0, A, 0, 0)) == nh.NH_ERR_UNSUPPORTED_SHAPE
     assert "2 GiB" in nh.lib.nh_last_error().decode()
 
 
@@ -259,7 +260,7 @@ def test_primitive_checks(nh):
     assert _status(lambda: nh.nh_ssm_step(d, A, A, 128, A, A, A, A, A, 0, 0, 0)) == nh.NH_ERR_UNSUPPORTED_SHAPE
     assert _status(lambda: nh.nh_ssd_chunk_scan(d, A, A, 22656, 0, A, A, A, None, None, A, 0, 1, A, 1 << 20, 0)) == \
         nh.NH_ERR_UNSUPPORTED_SHAPE
-    assert _status(lambda: nh.nh_rmsnorm_gated(A, A, 10240, A, A, 1, 10240, 1000, 1e-5, 0)) == \
+    assert _status(lambda: nh.nh_rmsnorm_gated(A, 0, A, 10240, A, A, 1, 10240, 1000, 1e-5, 0)) == \
         nh.NH_ERR_UNSUPPORTED_SHAPE
     assert _status(lambda: nh.nh_rmsnorm(A, 0, A, A, 1, 4480, 0.0, 0)) == nh.NH_ERR_INVALID_ARGUMENT
 

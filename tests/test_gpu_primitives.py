@@ -63,7 +63,7 @@ def test_gemv_one_hot_is_bit_exact(env, asym):
         for i, k in enumerate(kk):
             x[i, k] = 0x3F80  # 1.0
         y = gu.empty_f32(len(kk), 300)
-        nh.nh_w4_gemv(gu.w4_dev(W), gu.to_dev(x), len(kk), None, 0, y, nh.NH_F32)
+        nh.nh_w4_gemv(gu.w4_dev(W), gu.to_dev(x), nh.NH_BF16, len(kk), None, 0, y, nh.NH_F32)
         got = y.cpu().numpy()
         for i, k in enumerate(kk):
             assert np.array_equal(got[i], Wd[:, k].astype(np.float32)), k
@@ -78,7 +78,7 @@ def test_gemv_matches_oracle(env, n, k, batch):
     W = synth.w4_random(3, n, 1, 2, n, k)
     x = _x(rng, batch, k)
     y = gu.empty_f32(batch, n)
-    nh.nh_w4_gemv(gu.w4_dev(W), gu.to_dev(x), batch, None, 0, y, nh.NH_F32)
+    nh.nh_w4_gemv(gu.w4_dev(W), gu.to_dev(x), nh.NH_BF16, batch, None, 0, y, nh.NH_F32)
     ref = oracle.w4_matvec(W, gu.bf16_bits_to_f64(x))
     got = y.cpu().numpy()
     assert gu.rel_l2(got, ref) < 1e-5
@@ -103,7 +103,7 @@ def test_gemv_matrix_core_stage_tails(env, batch):
         x = _x(rng, batch, 4480)
         res = rng.normal(size=(batch, n)).astype(np.float32)
         y = gu.empty_f32(batch, n)
-        nh.nh_w4_gemv(gu.w4_dev(W), gu.to_dev(x), batch, gu.to_dev(res), nh.NH_F32, y, nh.NH_F32)
+        nh.nh_w4_gemv(gu.w4_dev(W), gu.to_dev(x), nh.NH_BF16, batch, gu.to_dev(res), nh.NH_F32, y, nh.NH_F32)
         ref = oracle.w4_matvec(W, gu.bf16_bits_to_f64(x)) + res
         got = y.cpu().numpy().astype(np.float64)
         assert np.isfinite(got).all(), n
@@ -130,12 +130,29 @@ def test_gemv_large_activations(env, n, k, batch):
     xf[:, 160:192] = 0.0                                  # an all-zero chunk
     x = synth.f32_to_bf16(xf.astype(np.float32))
     y = gu.empty_f32(batch, n)
-    nh.nh_w4_gemv(gu.w4_dev(W), gu.to_dev(x), batch, None, 0, y, nh.NH_F32)
+    nh.nh_w4_gemv(gu.w4_dev(W), gu.to_dev(x), nh.NH_BF16, batch, None, 0, y, nh.NH_F32)
     ref = oracle.w4_matvec(W, gu.bf16_bits_to_f64(x))
     got = y.cpu().numpy().astype(np.float64)
     assert np.isfinite(got).all()
     assert gu.rel_l2(got, ref) < 1e-5
     assert gu.max_abs(got, ref) < 1e-4 * np.abs(ref).max()
+
+
+@pytest.mark.parametrize("n,k,batch", [(300, 4480, 1), (300, 4480, 2), (1000, 4480, 3), (1000, 4480, 4),
+                                       (4480, 10240, 1), (4480, 15680, 2), (4480, 10240, 4)])
+def test_gemv_f32_input(env, n, k, batch):
+    # x given as fp32 (not bf16-exact): the GEMV rounds it to bf16, its activation precision
+    nh, oracle, gu, torch = env
+    _say("gemv f32 input", n, k, batch)
+    rng = np.random.default_rng(11 * n + k + batch)
+    W = _asym(synth.w4_random(10, n, 1, 2, n, k), n + 2)
+    xf = rng.normal(0, 1, (batch, k)).astype(np.float32)
+    y = gu.empty_f32(batch, n)
+    nh.nh_w4_gemv(gu.w4_dev(W), gu.to_dev(xf), nh.NH_F32, batch, None, 0, y, nh.NH_F32)
+    ref = oracle.w4_matvec(W, oracle.round_bf16(xf.astype(np.float64)))
+    got = y.cpu().numpy().astype(np.float64)
+    assert gu.rel_l2(got, ref) < 1e-5
+    assert gu.max_abs(got, ref) < 1e-4 * max(1.0, np.abs(ref).max())
 
 
 def test_gemv_residual_bf16_out(env):
@@ -146,7 +163,7 @@ def test_gemv_residual_bf16_out(env):
     x = _x(rng, 2, 10240)
     res = rng.normal(size=(2, 4480)).astype(np.float32)
     y = gu.empty_u16(2, 4480)
-    nh.nh_w4_gemv(gu.w4_dev(W), gu.to_dev(x), 2, gu.to_dev(res), nh.NH_F32, y, nh.NH_BF16)
+    nh.nh_w4_gemv(gu.w4_dev(W), gu.to_dev(x), nh.NH_BF16, 2, gu.to_dev(res), nh.NH_F32, y, nh.NH_BF16)
     ref = oracle.w4_matvec(W, gu.bf16_bits_to_f64(x)) + res
     got = gu.bf16_bits_to_f64(gu.from_dev_u16(y))
     # half a bf16 unit of the value plus the fp32 accumulation error (a rounding-boundary flip)
@@ -410,8 +427,24 @@ def test_rmsnorm_and_gated_norm(env):
     z = synth.f32_to_bf16(rng.normal(size=(rows, 22656)).astype(np.float32))
     gw = synth.f32_to_bf16((1 + 0.05 * rng.normal(size=10240)).astype(np.float32))
     o = gu.empty_u16(rows, 10240)
-    nh.nh_rmsnorm_gated(gu.to_dev(y), gu.to_dev(z), 22656, gu.to_dev(gw), o, rows, 10240, 1280, 1e-5)
+    nh.nh_rmsnorm_gated(gu.to_dev(y), nh.NH_BF16, gu.to_dev(z), 22656, gu.to_dev(gw), o, rows, 10240, 1280, 1e-5)
     ref = oracle.rmsnorm_gated(gu.bf16_bits_to_f64(y), gu.bf16_bits_to_f64(z)[:, :10240], gw, 1280, 1e-5)
+    got = gu.bf16_bits_to_f64(gu.from_dev_u16(o))
+    assert np.all(np.abs(got - ref) <= np.abs(ref) * 2 ** -8 + 1e-7)
+
+
+@pytest.mark.parametrize("rows,d,group,ld_z", [(33, 10240, 1280, 22656), (5, 8192, 4096, 8200)])
+def test_gated_norm_f32_y(env, rows, d, group, ld_z):
+    # y given as fp32 (the SSM's own precision): used as it is, with z bf16
+    nh, oracle, gu, torch = env
+    rng = np.random.default_rng(rows + group)
+    _say(f"gated norm f32 y rows={rows} d={d} group={group}")
+    y = rng.normal(size=(rows, d)).astype(np.float32)
+    z = synth.f32_to_bf16(rng.normal(size=(rows, ld_z)).astype(np.float32))
+    gw = synth.f32_to_bf16((1 + 0.05 * rng.normal(size=d)).astype(np.float32))
+    o = gu.empty_u16(rows, d)
+    nh.nh_rmsnorm_gated(gu.to_dev(y), nh.NH_F32, gu.to_dev(z), ld_z, gu.to_dev(gw), o, rows, d, group, 1e-5)
+    ref = oracle.rmsnorm_gated(y.astype(np.float64), gu.bf16_bits_to_f64(z)[:, :d], gw, group, 1e-5)
     got = gu.bf16_bits_to_f64(gu.from_dev_u16(o))
     assert np.all(np.abs(got - ref) <= np.abs(ref) * 2 ** -8 + 1e-7)
 
@@ -428,7 +461,7 @@ def test_gated_norm_other_groups(env, rows, d, group, ld_z):
     z = synth.f32_to_bf16(rng.normal(size=(rows, ld_z)).astype(np.float32))
     gw = synth.f32_to_bf16((1 + 0.05 * rng.normal(size=d)).astype(np.float32))
     o = gu.empty_u16(rows, d)
-    nh.nh_rmsnorm_gated(gu.to_dev(y), gu.to_dev(z), ld_z, gu.to_dev(gw), o, rows, d, group, 1e-5)
+    nh.nh_rmsnorm_gated(gu.to_dev(y), nh.NH_BF16, gu.to_dev(z), ld_z, gu.to_dev(gw), o, rows, d, group, 1e-5)
     ref = oracle.rmsnorm_gated(gu.bf16_bits_to_f64(y), gu.bf16_bits_to_f64(z)[:, :d], gw, group, 1e-5)
     got = gu.bf16_bits_to_f64(gu.from_dev_u16(o))
     assert np.all(np.abs(got - ref) <= np.abs(ref) * 2 ** -8 + 1e-7)
