@@ -113,12 +113,20 @@ typedef struct {
 
 /* ------------------------------------------------------------- library */
 
+/* The message of the calling thread's last failed call (thread-local; empty
+ * after a success).  Bad arguments are rejected at the boundary, before any
+ * work, as the session calls of the docs page "Nemotron VoiceChat", section
+ * "Online session", reject bad input. */
 const char *nh_last_error(void);
+/* Library name, version and target (gfx950). */
 const char *nh_version(void);
-/* The hybrid_override_pattern of text_config: 'M' Mamba2, '*' attention, '-' MLP. */
+/* The hybrid_override_pattern of text_config (issue page, section
+ * "config.json"): 'M' Mamba2, '*' attention, '-' MLP, 56 layers. */
 const char *nh_hybrid_pattern(void);
 
-/* Measurement hook.  events: NULL (off) or an array of n >= 6 hipEvent_t
+/* Measurement hook for the per-position step (docs page, section
+ * "Performance": the language stage's time per position is the figure of
+ * merit).  events: NULL (off) or an array of n >= 6 hipEvent_t
  * created by the caller.  While set, every nh_mamba_block_step call on this
  * thread records events[2i] on its stream right before kernel i (0: fused
  * pre-norm/in_proj/conv, 1: SSM step + gated-norm partial sums, 2: gated
@@ -143,17 +151,21 @@ nh_status nh_w4_gemv(const nh_w4_matrix *W, const void *x, nh_dtype x_dtype, int
                      const void *residual, nh_dtype res_dtype,
                      void *y, nh_dtype y_dtype, void *stream);
 
-/* Y = X W^T (+ residual): the W4 matrix product for whole sequences.
- * X: bf16 [M][k_in]; residual: nullable [M][n_out] of res_dtype;
- * Y: [M][n_out] of y_dtype.  M >= 1.  Needs nh_w4_gemm_workspace_bytes(M, k_in)
- * bytes of workspace.  Matrix-core arithmetic; W is dequantised exactly. */
+/* Y = X W^T (+ residual): the W4 matrix product for whole sequences, the
+ * full-history recompute's in_proj / out_proj (docs page "Nemotron
+ * VoiceChat", section "Offline timeline"; issue page, section "config.json":
+ * 4-bit, group 64).  X: bf16 [M][k_in] (|x| < 65504); residual: nullable
+ * [M][n_out] of res_dtype; Y: [M][n_out] of y_dtype.  M >= 1.  Needs
+ * nh_w4_gemm_workspace_bytes(M, k_in) bytes of workspace.  Matrix-core
+ * arithmetic; W is dequantised exactly for 2^-17 <= |scale| <= 8188. */
 size_t nh_w4_gemm_workspace_bytes(int M, int k_in);
 nh_status nh_w4_gemm(const nh_w4_matrix *W, const uint16_t *X, int M,
                      const void *residual, nh_dtype res_dtype,
                      void *Y, nh_dtype y_dtype, void *ws, size_t ws_bytes, void *stream);
 
-/* u = RMSNorm(x) * w, rounded to bf16.  x: [rows][d] of x_dtype; w, u: bf16.
- * RMS over the d values of a row, eps inside the square root. */
+/* u = RMSNorm(x) * w, rounded to bf16: the block's pre-norm (issue page,
+ * section "config.json": layer_norm_epsilon 1e-5).  x: [rows][d] of x_dtype;
+ * w, u: bf16.  RMS over the d values of a row, eps inside the square root. */
 nh_status nh_rmsnorm(const void *x, nh_dtype x_dtype, const uint16_t *w, uint16_t *u,
                      int rows, int d, float eps, void *stream);
 
@@ -170,7 +182,9 @@ nh_status nh_inproj_conv_step(const nh_mamba_dims *d, const nh_mamba_weights *w,
                               uint16_t *z, uint16_t *xc, uint16_t *dt_raw, int batch,
                               void *stream);
 
-/* One position of the causal depthwise conv1d (kernel k, with bias) + SiLU.
+/* One position of the causal depthwise conv1d (kernel k, with bias) + SiLU
+ * (issue page, section "config.json": conv_kernel 4, use_conv_bias true;
+ * section "Network 2": the [channels, 4, 1] weight layout).
  * xbc: bf16, row b at xbc + b*ld (channels values); conv_state: bf16
  * [batch][k-1][channels], row 0 oldest, updated in place (shifted by one,
  * the new input appended); w: bf16 [channels][k], tap k-1 newest; b: bf16
@@ -179,7 +193,8 @@ nh_status nh_conv1d_step(const uint16_t *xbc, long ld, uint16_t *conv_state,
                          const uint16_t *w, const uint16_t *b, uint16_t *out,
                          int batch, int channels, int k, void *stream);
 
-/* The same conv over T positions.  xbc row (b, t) at xbc + (b*T + t)*ld;
+/* The same conv over T positions (the full-history recompute, docs page,
+ * section "Offline timeline").  xbc row (b, t) at xbc + (b*T + t)*ld;
  * state_in: nullable bf16 [batch][k-1][channels] (NULL = zeros);
  * state_out: nullable, receives the last k-1 pre-conv rows (may not alias
  * state_in); out: bf16 [batch][T][channels]. */
@@ -187,7 +202,10 @@ nh_status nh_conv1d_seq(const uint16_t *xbc, long ld, int T, const uint16_t *sta
                         uint16_t *state_out, const uint16_t *w, const uint16_t *b,
                         uint16_t *out, int batch, int channels, int k, void *stream);
 
-/* One position of the selective SSM.  xc: bf16 [batch][conv_dim], the
+/* One position of the selective SSM (issue page, section "config.json":
+ * mamba_num_heads 128, mamba_head_dim 80, ssm_state_size 128, n_groups 8;
+ * docs page, "Online session": the state carried from position to
+ * position).  xc: bf16 [batch][conv_dim], the
  * post-conv x | B | C; dt_raw: bf16, row b at dt_raw + b*ld_dt (n_heads
  * values).  dt = softplus(dt_raw + dt_bias), A = -exp(A_log); for head h
  * (group g = h / (n_heads/n_groups)):
@@ -199,7 +217,9 @@ nh_status nh_ssm_step(const nh_mamba_dims *d, const uint16_t *xc, const uint16_t
                       long ld_dt, const float *dt_bias, const float *A_log, const float *D,
                       float *ssm_state, void *y, nh_dtype y_dtype, int batch, void *stream);
 
-/* The same recurrence over T positions, computed as a chunked SSD scan with
+/* The same recurrence over T positions (docs page, "Offline timeline": the
+ * full-history recompute gives the cached step's tokens), computed as a
+ * chunked SSD scan with
  * chunk length d->chunk (intra-chunk quadratic form, chunk states, sequential
  * state passing; Dao & Gu 2024).  Equals the per-position recurrence up to
  * rounding for every chunk length.
@@ -396,10 +416,14 @@ nh_status nh_head_argmax(const nh_w4_matrix *W, const void *x, nh_dtype x_dtype,
 #define NH_MODE_SEQ 1
 
 /* Workspace bytes for nh_mamba_block_step (mode NH_MODE_STEP, T ignored) or
- * nh_mamba_block_seq (NH_MODE_SEQ) at this batch and T; 0 on bad arguments. */
+ * nh_mamba_block_seq (NH_MODE_SEQ) at this batch and T; 0 on bad arguments.
+ * (Each entry point that needs scratch has its own size function: the sizes
+ * depend on different arguments.) */
 size_t nh_block_workspace_bytes(const nh_mamba_dims *d, int batch, int T, int mode);
 
-/* One position of the whole block for `batch` independent sequences:
+/* One position of the whole Mamba2 block for `batch` independent sequences
+ * (docs page, "Online session": the cached per-position step; issue page,
+ * "config.json": the block's dimensions):
  * out = x + mixer(RMSNorm(x)), state updated in place.
  * x: [batch][hidden] of x_dtype; out: [batch][hidden] of out_dtype (may not
  * alias x).  Storage points: the normalised input, the in_proj output, the
@@ -426,7 +450,8 @@ nh_status nh_mamba_block_step_noalloc(const nh_mamba_dims *d, const nh_mamba_wei
                                       nh_mamba_state *state, const void *x, nh_dtype x_dtype,
                                       void *out, nh_dtype out_dtype, int batch, void *stream);
 
-/* The whole block over T positions (full-history recompute) with the same
+/* The whole block over T positions (full-history recompute, docs page,
+ * section "Offline timeline") with the same
  * storage points.  init: nullable (NULL = zero conv and SSM state);
  * final_state: nullable, receives the state after position T-1 (its
  * buffers may be init's).  x: [batch][T][hidden]; out: [batch][T][hidden]. */
@@ -436,7 +461,8 @@ nh_status nh_mamba_block_seq(const nh_mamba_dims *d, const nh_mamba_weights *w,
                              nh_dtype out_dtype, int batch, void *ws, size_t ws_bytes,
                              void *stream);
 
-/* A stack of n_layers Mamba2 blocks applied in order (the M layers of the
+/* A stack of n_layers Mamba2 blocks applied in order (issue page,
+ * "config.json", hybrid_override_pattern: the M layers of the
  * hybrid pattern; attention and MLP layers are not part of this library and
  * act as identity between them).  The residual stream between blocks is
  * fp32: layer i reads layer i-1's output and writes

@@ -319,9 +319,9 @@ def head(W, x, norm_w, eps: float, mode: int = CONTRACT):
     """Final norm and one greedy output head of the language model.
 
     The issue page "feat(nemotron_voicechat): ... offline duplex inference #1374", section
-    "Network 2": after the last layer the hidden state goes through norm_f, then through
-    lm_head and function_head, both 4-bit [4480 -> 131072] matrices without a linear bias,
-    and the text and function ids are the argmax of the last position (no sampling).
+    "Network 2": the final hidden state is normalised by norm_f and fed to two 4-bit heads
+    of shape [4480 -> 131072] (lm_head, function_head) with no linear bias; each head's id
+    is chosen greedily from its logits at the newest position.
     h = x / rms(x) * norm_w (rounded to bf16 in CONTRACT mode, the point where the GPU
     kernel stores it); logits = dequant(W) h in fp64; ids = greedy_ids(logits).
     x: [m][k_in] doubles.  Returns (logits [m][n_out], ids [m])."""
