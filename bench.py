@@ -185,7 +185,7 @@ def main():
     ap.add_argument("--skip-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--skip-heads", action="store_true",
                     help="skip the legs outside the block: MLP layer, output heads, input row")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=8.0)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -705,20 +705,53 @@ def main():
     if not args.skip_cpu:
         import oracle
         oracle.build(force=False)
+        cores = oracle.lib().nho_max_threads()
+        cpu_model = "unknown"
+        try:
+            for line in open("/proc/cpuinfo"):
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+        except OSError:
+            pass
         xh = gu.bf16_bits_to_f64(synth.block_input(1, 1, 1))
         csh = gu.bf16_bits_to_f64(cs0)
         lw0 = host_layers[0]
-        reps, t_cpu = 0, 0.0
-        while t_cpu < args.cpu_seconds or reps < 2:
-            ts = time.perf_counter()
-            oracle.block(synth.REAL, lw0, xh, csh, ss0, mode=oracle.CONTRACT, stepwise=True)
-            t_cpu += time.perf_counter() - ts
-            reps += 1
+
+        def timed(fn, budget, min_reps=2):
+            reps, t = 0, 0.0
+            while t < budget or reps < min_reps:
+                ts = time.perf_counter()
+                fn()
+                t += time.perf_counter() - ts
+                reps += 1
+            return t / reps, reps, t
+
+        # C1: one batch-1 step with a pre-filled state, every host thread
+        c1, c1_reps, c1_t = timed(lambda: oracle.block(synth.REAL, lw0, xh, csh, ss0, mode=oracle.CONTRACT,
+                                                       stepwise=True, nthreads=cores), args.cpu_seconds)
+        # C2: the batch-1 full-history recompute, a 32-position prefix of its T = 413 input
+        x2 = gu.bf16_bits_to_f64(synth.block_input(2, 1, 32))
+        c2, _, c2_t = timed(lambda: oracle.block(synth.REAL, lw0, x2, nthreads=cores), 0.0, 1)
+        # C4: batch 2 full history, one layer over a 16-position prefix of its T = 3750 input
+        x4 = gu.bf16_bits_to_f64(synth.block_input(4, 2, 16))
+        c4, _, c4_t = timed(lambda: oracle.block(synth.REAL, lw0, x4, nthreads=cores), 0.0, 1)
+        # C1 on one thread
+        c1s, _, c1s_t = timed(lambda: oracle.block(synth.REAL, lw0, xh, csh, ss0, mode=oracle.CONTRACT,
+                                                   stepwise=True, nthreads=1), 0.0, 2)
+        oracle.block(synth.REAL, lw0, xh, csh, ss0, stepwise=True, nthreads=cores)  # restore the thread count
         out["cpu_baseline"] = {
-            "value": round(t_cpu / reps * 1e6, 1), "unit": "us/layer", "cores": oracle.lib().nho_max_threads(),
+            "value": round(c1 * 1e6, 1), "unit": "us/layer", "cores": cores, "cpu_model": cpu_model,
             "kind": "oracle",
-            "sample": f"one batch-1 block step with a pre-filled state, fp64 oracle, {reps} repeats, "
-                      f"{t_cpu:.1f} s of host time",
+            "sample": f"one batch-1 block step with a pre-filled state, fp64 oracle on {cores} threads, "
+                      f"{c1_reps} repeats, {c1_t:.1f} s of host time",
+            "single_thread_us_per_layer": round(c1s * 1e6, 1),
+            "c2_positions_per_s": round(32 / c2, 2),
+            "c4_position_layers_per_s": round(2 * 16 / c4, 2),
+            "legs": "C1 step on all threads (value) and on one thread; C2 full history over the first 32 of "
+                    "its 413 positions (batch 1); C4 full history over the first 16 of its 3750 positions "
+                    "(batch 2, one layer); positions/s are position-layers per second",
+            "host_seconds": round(c1_t + c2_t + c4_t + c1s_t, 1),
         }
         log("cpu baseline:", out["cpu_baseline"])
 
