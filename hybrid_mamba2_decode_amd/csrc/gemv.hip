@@ -57,23 +57,14 @@ __device__ __forceinline__ float dot2h(uint32_t a, uint32_t b, float c)
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
 }
 
-// Cross-lane sums with DPP inside rows of 16 lanes (quad swaps, half-row and row mirrors),
-// then LDS permutes for the 32- and 64-lane steps.
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float v)
-{
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
-}
-
+// Sum over aligned groups of LPR lanes (LPR = 16, 32 or 64), in every lane of the group.
 template <int LPR>
 __device__ __forceinline__ float row_sum(float v)
 {
-    v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
-    v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
-    v += dpp_mov<0x141>(v);  // row_half_mirror
-    v += dpp_mov<0x140>(v);  // row_mirror
-    if (LPR >= 32) v += __shfl_xor(v, 16, 64);
-    if (LPR >= 64) v += __shfl_xor(v, 32, 64);
+    static_assert(LPR == 16 || LPR == 32 || LPR == 64, "row_sum: 16, 32 or 64 lanes");
+    v = row16_sum(v);
+    if (LPR >= 32) v = xor16_sum(v);
+    if (LPR >= 64) v = xor32_sum(v);
     return v;
 }
 
@@ -649,84 +640,103 @@ struct InProjBlock {
     }
 };
 
-// Pre-norm of the per-position kernels whose K is the hidden size.  Thread t < 140 owns the
-// 32-value chunk t of x (every batch row) and of the norm weight.  issue() sends the raw loads
-// (a wave's loads complete in issue order, so issued before the caller's first weight stage
-// they are all the pre-norm waits for); finish() widens them, sums the squares over the
-// work-group and writes u = bf16(x / rms(x) * w) to LDS in the activation format.
+// Pre-norm of the per-position kernels whose K is the hidden size.  Four threads build each
+// 32-value chunk: item i = 4 c + j (chunk c, quarter j) covers values 8 j .. 8 j + 7 of chunk c of
+// every batch row, i.e. the packed pairs p[4 j .. 4 j + 3], and the quarter's share of the chunk
+// sums, which the four consecutive lanes add up.  issue() sends the raw loads (a wave's loads
+// complete in issue order, so issued before the caller's weight stages they are all the
+// pre-norm waits for); finish() sums the squares over the work-group and writes
+// u = bf16(x / rms(x) * w) to LDS in the activation format.
 template <int NB, int XT, int NT>
 struct PreNorm {
-    static constexpr int NCH = HIDDEN / 32, NW = NT / 64;
-    static constexpr int XW = XT == BF16 ? 4 : 8;  // 16-byte words per 32 values
-    bool own;
-    uint4 xr[NB][XW], wq[4];
+    static constexpr int NCH = HIDDEN / 32, NI = 4 * NCH, NW = NT / 64;
+    static constexpr int M = (NI + NT - 1) / NT;     // items per thread
+    static constexpr int XW = XT == BF16 ? 1 : 2;    // 16-byte words per 8 values
+    uint4 xr[M][NB][XW], wq[M];
+
+    // item m of this thread (rows past the last item re-read it: unconditional loads)
+    __device__ __forceinline__ static int item(int m) { return min((int)threadIdx.x + NT * m, NI - 1); }
 
     __device__ __forceinline__ void issue(const void *x, const uint16_t *nw)
     {
-        own = (int)threadIdx.x < NCH;
-        if (own) {
-            const uint4 *wsrc = reinterpret_cast<const uint4 *>(nw + 32 * threadIdx.x);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) wq[j] = wsrc[j];
+        for (int m = 0; m < M; ++m) {
+            const int it = item(m);
+            wq[m] = *reinterpret_cast<const uint4 *>(nw + 8 * it);
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                const uint4 *src = XT == BF16
-                    ? reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(x) + (size_t)b * HIDDEN + 32 * threadIdx.x)
-                    : reinterpret_cast<const uint4 *>(reinterpret_cast<const float *>(x) + (size_t)b * HIDDEN + 32 * threadIdx.x);
+            for (int b = 0; b < NB; ++b)
 #pragma unroll
-                for (int j = 0; j < XW; ++j) xr[b][j] = src[j];
-            }
+                for (int w = 0; w < XW; ++w)
+                    xr[m][b][w] = XT == BF16
+                        ? *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(x) + (size_t)b * HIDDEN + 8 * it)
+                        : *reinterpret_cast<const uint4 *>(reinterpret_cast<const float *>(x) + (size_t)b * HIDDEN + 8 * it + 4 * w);
         }
+    }
+
+    // value e (0..7) of item m, batch row b
+    __device__ __forceinline__ float xval(int m, int b, int e) const
+    {
+        if (XT == BF16) {
+            const uint4 r = xr[m][b][0];
+            const uint32_t u = e < 2 ? r.x : e < 4 ? r.y : e < 6 ? r.z : r.w;
+            return (e % 2) == 0 ? bf16lo(u) : bf16hi(u);
+        } else {
+            const uint4 r = xr[m][b][e / 4];
+            return __uint_as_float((e % 4) == 0 ? r.x : (e % 4) == 1 ? r.y : (e % 4) == 2 ? r.z : r.w);
+        }
+    }
+    __device__ __forceinline__ float wval(int m, int e) const
+    {
+        const uint4 r = wq[m];
+        const uint32_t u = e < 2 ? r.x : e < 4 ? r.y : e < 6 ? r.z : r.w;
+        return (e % 2) == 0 ? bf16lo(u) : bf16hi(u);
     }
 
     __device__ __forceinline__ void finish(float eps, uint32_t *act_lds, float (&red)[NB][NW])
     {
-        float xv[NB][32], w[32];
-        if (own) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                w[8 * j + 0] = bf16lo(wq[j].x); w[8 * j + 1] = bf16hi(wq[j].x); w[8 * j + 2] = bf16lo(wq[j].y);
-                w[8 * j + 3] = bf16hi(wq[j].y); w[8 * j + 4] = bf16lo(wq[j].z); w[8 * j + 5] = bf16hi(wq[j].z);
-                w[8 * j + 6] = bf16lo(wq[j].w); w[8 * j + 7] = bf16hi(wq[j].w);
-            }
-#pragma unroll
-            for (int b = 0; b < NB; ++b)
-#pragma unroll
-                for (int j = 0; j < XW; ++j) {
-                    const uint4 r = xr[b][j];
-                    if (XT == BF16) {
-                        xv[b][8 * j + 0] = bf16lo(r.x); xv[b][8 * j + 1] = bf16hi(r.x); xv[b][8 * j + 2] = bf16lo(r.y);
-                        xv[b][8 * j + 3] = bf16hi(r.y); xv[b][8 * j + 4] = bf16lo(r.z); xv[b][8 * j + 5] = bf16hi(r.z);
-                        xv[b][8 * j + 6] = bf16lo(r.w); xv[b][8 * j + 7] = bf16hi(r.w);
-                    } else {
-                        xv[b][4 * j + 0] = __uint_as_float(r.x); xv[b][4 * j + 1] = __uint_as_float(r.y);
-                        xv[b][4 * j + 2] = __uint_as_float(r.z); xv[b][4 * j + 3] = __uint_as_float(r.w);
-                    }
-                }
-        }
         // sum of squares per batch row
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             float ss = 0.f;
-            if (own)
 #pragma unroll
-                for (int e = 0; e < 32; ++e) ss += xv[b][e] * xv[b][e];
+            for (int m = 0; m < M; ++m)
+                if ((int)threadIdx.x + NT * m < NI)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float v = xval(m, b, e);
+                        ss = fmaf(v, v, ss);
+                    }
             ss = wave_sum(ss);
             if ((threadIdx.x & 63) == 0) red[b][threadIdx.x >> 6] = ss;
         }
         __syncthreads();
-        // normalised, bf16-rounded chunks
-        if (own) {
+        // normalised, bf16-rounded quarters of chunks
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                float tot = 0.f;
+        for (int b = 0; b < NB; ++b) {
+            float tot = 0.f;
 #pragma unroll
-                for (int i = 0; i < NW; ++i) tot += red[b][i];
-                const float r = 1.0f / sqrtf(tot / (float)HIDDEN + eps);
-                float v[32];
+            for (int i = 0; i < NW; ++i) tot += red[b][i];
+            const float r = 1.0f / sqrtf(tot / (float)HIDDEN + eps);
 #pragma unroll
-                for (int e = 0; e < 32; ++e) v[e] = round_bf16(xv[b][e] * r * w[e]);
-                make_chunk(v, act_lds + ((size_t)b * NCH + threadIdx.x) * ACT_WORDS);
+            for (int m = 0; m < M; ++m) {
+                const int it = (int)threadIdx.x + NT * m, c = it >> 2, j = it & 3;
+                float v[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = round_bf16(xval(m, b, e) * r * wval(m, e));
+                // pairs (k, k + 4) of the quarter; even and odd sums of the quarter
+                float se = (v[0] + v[4]) + (v[2] + v[6]), so = (v[1] + v[5]) + (v[3] + v[7]);
+                se += dpp_mov<0xB1>(se);  // quad_perm [1,0,3,2]
+                so += dpp_mov<0xB1>(so);
+                se += dpp_mov<0x4E>(se);  // quad_perm [2,3,0,1]
+                so += dpp_mov<0x4E>(so);
+                if (it < NI) {
+                    uint32_t *dst = act_lds + ((size_t)b * NCH + c) * ACT_WORDS;
+                    reinterpret_cast<uint4 *>(dst)[j] =
+                        make_uint4(pack_f16x2(v[0], v[4]), pack_f16x2(v[1], v[5]), pack_f16x2(v[2], v[6]), pack_f16x2(v[3], v[7]));
+                    if (j == 0)
+                        reinterpret_cast<uint4 *>(dst)[4] =
+                            make_uint4(__float_as_uint(fmaf(1024.f, se, 64.f * so)), __float_as_uint(se + so), 0x3F800000u, 0u);
+                }
             }
         }
         __syncthreads();

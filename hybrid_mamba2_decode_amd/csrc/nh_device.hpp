@@ -79,20 +79,41 @@ __device__ __forceinline__ float softplus_fast(float v)
     return fmaxf(v, 0.0f) + (y < 0.015625f ? ser : __logf(1.0f + y));
 }
 
-__device__ __forceinline__ float wave_sum(float v)
+// Cross-lane moves: DPP inside rows of 16 lanes; across rows, the swap instructions of this
+// target, which exchange rows 0/2 with rows 1/3 (16-lane swap) or lanes 0-31 with 32-63
+// (32-lane swap) between two registers.  Given the same register twice, the two results hold
+// the value and its partner's, so their sum is v[i] + v[i ^ 16] (or ^ 32), equal in both lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v)
 {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float xor16_sum(float v)
+{
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float xor32_sum(float v)
+{
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+// Sum over the 16 lanes of each row (quad swaps, half-row and row mirrors), in every lane.
+__device__ __forceinline__ float row16_sum(float v)
+{
+    v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp_mov<0x141>(v);  // row_half_mirror
+    v += dpp_mov<0x140>(v);  // row_mirror
     return v;
 }
 
+// Sum over the 64 lanes, the same value in every lane.
+__device__ __forceinline__ float wave_sum(float v) { return xor32_sum(xor16_sum(row16_sum(v))); }
+
 // Sum over aligned groups of 32 lanes (lanes 0-31 and 32-63 separately).
-__device__ __forceinline__ float half_wave_sum(float v)
-{
-#pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
-}
+__device__ __forceinline__ float half_wave_sum(float v) { return xor16_sum(row16_sum(v)); }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
