@@ -128,16 +128,14 @@ __global__ __launch_bounds__(256) void k_attn_decode(const uint16_t *__restrict_
             float a = 0.f;
 #pragma unroll
             for (int j = 0; j < 4; ++j) a = dot8(qv[h][j], cur.k[j], a);
-            a += __shfl_xor(a, 1, 64);
-            a += __shfl_xor(a, 2, 64);
+            a += dpp_mov<0xB1>(a);  // quad_perm [1,0,3,2]
+            a += dpp_mov<0x4E>(a);  // quad_perm [2,3,0,1]
             sc[h] = pk < p1 ? a * scale : -INFINITY;
         }
         // tile maximum per head: over the wave, then over the four waves
 #pragma unroll
         for (int h = 0; h < REP; ++h) {
-            float v = sc[h];
-#pragma unroll
-            for (int o = 4; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+            const float v = wave_max(sc[h]);  // the quad's lanes hold equal values
             if (lane == 0) rm[buf][wave][h] = v;
         }
         __syncthreads();
@@ -185,8 +183,7 @@ __global__ __launch_bounds__(256) void k_attn_decode(const uint16_t *__restrict_
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             float v = acc[h][e];
-            v += __shfl_xor(v, 16, 64);
-            v += __shfl_xor(v, 32, 64);
+            v = xor32_sum(xor16_sum(v));
             acc[h][e] = v;
         }
     if (lane < 16) {
@@ -234,9 +231,7 @@ __global__ __launch_bounds__(64) void k_attn_combine(const float *__restrict__ p
     const bool have = lane < ns;
     const float ms = have ? src[(size_t)lane * PART + h] : -INFINITY;
     const float ls = have ? src[(size_t)lane * PART + REP + h] : 0.f;
-    float M = ms;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+    const float M = wave_max(ms);
     const float es = have ? exp2f(ms - M) : 0.f;
     const float den = wave_sum(es * ls);
     float n0 = 0.f, n1 = 0.f;

@@ -935,8 +935,7 @@ __global__ __launch_bounds__(256, 1) void k_w4_mf(W4 W, const void *__restrict__
             float u = acc[v] + E[v];
             u += dpp_mov<0x124>(u);  // row_ror:4
             u += dpp_mov<0x128>(u);  // row_ror:8
-            u += __shfl_xor(u, 16, 64);
-            u += __shfl_xor(u, 32, 64);
+            u = xor32_sum(xor16_sum(u));
             tot[v] = u;
         }
         const int bsel = lane >> 2;
@@ -1150,8 +1149,7 @@ __global__ __launch_bounds__(MFL_NT, 1) void k_w4_mfl(W4 W, Act act_in, Epi epi)
                 float x = acc[v] + E[v];
                 x += dpp_mov<0x124>(x);  // row_ror:4
                 x += dpp_mov<0x128>(x);  // row_ror:8
-                x += __shfl_xor(x, 16, 64);
-                x += __shfl_xor(x, 32, 64);
+                x = xor32_sum(xor16_sum(x));
                 tot[v] = x;
             }
             const int bsel = lane >> 2;

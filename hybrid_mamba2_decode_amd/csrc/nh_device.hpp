@@ -112,6 +112,26 @@ __device__ __forceinline__ float row16_sum(float v)
 // Sum over the 64 lanes, the same value in every lane.
 __device__ __forceinline__ float wave_sum(float v) { return xor32_sum(xor16_sum(row16_sum(v))); }
 
+// The same for the maximum.
+__device__ __forceinline__ float xor16_max(float v)
+{
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float xor32_max(float v)
+{
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float wave_max(float v)
+{
+    v = fmaxf(v, dpp_mov<0xB1>(v));   // quad_perm [1,0,3,2]
+    v = fmaxf(v, dpp_mov<0x4E>(v));   // quad_perm [2,3,0,1]
+    v = fmaxf(v, dpp_mov<0x141>(v));  // row_half_mirror
+    v = fmaxf(v, dpp_mov<0x140>(v));  // row_mirror
+    return xor32_max(xor16_max(v));
+}
+
 // Sum over aligned groups of 32 lanes (lanes 0-31 and 32-63 separately).
 __device__ __forceinline__ float half_wave_sum(float v) { return xor16_sum(row16_sum(v)); }
 

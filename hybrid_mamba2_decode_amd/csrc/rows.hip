@@ -9,9 +9,9 @@ namespace nh {
 // Sum over the 8 lanes that hold one 64-element quantisation group (8 values each).
 __device__ __forceinline__ float group8_sum(float v)
 {
-    v += __shfl_xor(v, 1, 64);
-    v += __shfl_xor(v, 2, 64);
-    v += __shfl_xor(v, 4, 64);
+    v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp_mov<0x141>(v);  // row_half_mirror: the other quad of the 8 lanes
     return v;
 }
 
