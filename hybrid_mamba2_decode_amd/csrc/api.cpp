@@ -259,13 +259,13 @@ nh_status block_seq(const nh_mamba_dims *d, const nh_mamba_weights *w, const nh_
     }
     NH_HIP(launch_conv_seq(k.zx + DINNER, NIN, T, cs_in, cs_out, w->conv_w, w->conv_b, k.xc, B, CONVDIM, s),
            "conv");
-    // the scan's C.B^T tiles (at most 8 KiB per position) reuse the normalised input, which
-    // in_proj has consumed
-    if (ssd_scan_ws_bytes(B, T, d->chunk) > (size_t)M * HIDDEN * sizeof(uint16_t))
-        return fail(NH_ERR_INVALID_ARGUMENT, "internal: scan tiles exceed their workspace region");
+    // the scan's workspace (C.B^T tiles, and for long chunks the B fragments and tables) takes
+    // the gated norm's output region, which is written only after the scan
+    if (ssd_scan_ws_bytes(B, T, d->chunk) > (size_t)M * DINNER * sizeof(uint16_t))
+        return fail(NH_ERR_INVALID_ARGUMENT, "internal: scan workspace exceeds its region");
     NH_HIP(launch_ssd_scan(k.xc, k.zx + DINNER + CONVDIM, NIN, T, d->chunk, w->dt_bias, w->A_log, w->D,
                            init ? init->ssm_state : nullptr, fin ? fin->ssm_state : nullptr, k.y, BF16, B,
-                           k.u, s),
+                           k.o, s),
            "scan");
     NH_HIP(launch_rmsnorm_gated(k.y, BF16, k.zx, NIN, w->gnorm_w, k.o, 1, k.su_o, M, DINNER, GNORM, d->eps, s),
            "gated norm");

@@ -230,9 +230,13 @@ nh_status nh_ssm_step(const nh_mamba_dims *d, const uint16_t *xc, const uint16_t
  * ws: caller-owned device workspace of at least
  * nh_ssd_scan_workspace_bytes(d, batch, T) bytes (16-byte aligned), which
  * receives the per-group C.B^T tiles of every chunk (at most 8 KiB per
- * position, for chunks of at most 16 rows; about 2.3 KiB at chunk 256); its
- * contents on return are unspecified.  A smaller ws fails with
- * NH_ERR_WORKSPACE_TOO_SMALL before any launch. */
+ * position, for chunks of at most 16 rows); for chunks of at least 128 rows
+ * in sequences of at least 64 positions also B and C in the matrix-core
+ * operand order and each head's per-chunk decay tables (about 8 KiB per
+ * position in all at chunk 256; never above 10 KiB per position).  Its
+ * contents on return are
+ * unspecified.  A smaller ws fails with NH_ERR_WORKSPACE_TOO_SMALL before
+ * any launch. */
 size_t nh_ssd_scan_workspace_bytes(const nh_mamba_dims *d, int batch, int T);
 nh_status nh_ssd_chunk_scan(const nh_mamba_dims *d, const uint16_t *xc, const uint16_t *dt_raw,
                             long ld_dt, int T, const float *dt_bias, const float *A_log,

@@ -271,11 +271,22 @@ def test_scan_workspace_size_and_checks(nh):
     # 2 x 512 B; row block I holds ceil((I+1)/2) pairs, 72 for 16 row blocks; a partial last
     # chunk of 166 rows has 11 row blocks, 36 pairs
     d256 = nh.dims(chunk=256)
-    assert nh.nh_ssd_scan_workspace_bytes(d256, 2, 3750) == 2 * 8 * 1024 * (14 * 72 + 36)
-    assert nh.nh_ssd_scan_workspace_bytes(d256, 1, 1) == 8 * 1024
-    for B, T, Q in [(1, 1, 1), (2, 413, 128), (3, 17, 16), (1, 300, 7), (2, 3750, 256)]:
+    tiles = 2 * 8 * 1024 * (14 * 72 + 36)
+    # chunks of at least 128 rows in sequences of at least 64 positions add, per (chunk,
+    # sequence, group), B as ceil(L/32) steps x 8 state blocks of 1 KiB and C as ceil(L/16) row
+    # blocks x 4 steps of 1 KiB, and per (chunk, sequence, head) the decay tables, 14 bytes per
+    # position over 32 ceil(L/32) positions (rounded up to 64 bytes): 3584 at 256 rows, 2688 at 166
+    bfr = 2 * 8 * (14 * 64 + 6 * 8) * 1024
+    cfr = 2 * 8 * (14 * 64 + 11 * 4) * 1024
+    tab = 2 * 128 * (14 * 3584 + 2688)
+    assert nh.nh_ssd_scan_workspace_bytes(d256, 2, 3750) == tiles + bfr + cfr + tab
+    assert nh.nh_ssd_scan_workspace_bytes(d256, 1, 1) == 8 * 1024          # short: tiles only
+    # 63 positions (short): 4 row blocks of 1 + 1 + 2 + 2 pairs of 1 KiB per group
+    assert nh.nh_ssd_scan_workspace_bytes(d256, 1, 63) == 8 * 1024 * 6
+    for B, T, Q in [(1, 1, 1), (2, 413, 128), (3, 17, 16), (1, 300, 7), (2, 3750, 256), (1, 130, 129)]:
         n = nh.nh_ssd_scan_workspace_bytes(nh.dims(chunk=Q), B, T)
-        assert 0 < n <= 8192 * B * T        # the block reuses 8960 B per position for it
+        # the block gives the scan its gated-norm output region, 20 KiB per position
+        assert 0 < n <= (10240 if Q >= 128 and T >= 64 else 8192) * B * T
     assert nh.nh_ssd_scan_workspace_bytes(nh.dims(chunk=0), 1, 10) == 0
     assert nh.nh_ssd_scan_workspace_bytes(nh.dims(chunk=257), 1, 10) == 0
     assert nh.nh_ssd_scan_workspace_bytes(d256, 0, 10) == 0

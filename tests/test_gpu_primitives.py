@@ -336,13 +336,21 @@ def _rows(gu, got, ref, what, bf16=False):
 
 def _scan_ws(nh, gu, Q, B, T):
     n = nh.nh_ssd_scan_workspace_bytes(nh.dims(chunk=Q), B, T)
-    assert 0 < n <= 8192 * B * T  # at most 8 KiB per position (chunks under 17 rows)
+    # at most 8 KiB per position for short chunks (C.B^T tiles; chunks under 17 rows at worst),
+    # 10 KiB for long ones (tiles, B and C fragments, decay tables)
+    assert 0 < n <= (10240 if Q >= 128 and T >= 64 else 8192) * B * T
     return gu.workspace(n), n
 
 
 @pytest.mark.parametrize("T,Q,h0,B", [(1, 128, False, 1), (5, 4, True, 1), (16, 128, False, 1), (17, 16, True, 2),
                                       (40, 7, False, 1), (129, 128, True, 1), (300, 256, False, 1),
-                                      (413, 128, False, 1), (413, 256, True, 2), (64, 1, False, 1)])
+                                      (413, 128, False, 1), (413, 256, True, 2), (64, 1, False, 1),
+                                      # chunks of at least 128 rows in sequences of at least 64
+                                      # positions take the long-chunk kernel: its threshold (one
+                                      # 64-row chunk), chunk lengths that are not powers of two, and
+                                      # a last chunk of one row
+                                      (64, 128, True, 1), (200, 160, True, 2), (300, 200, False, 1),
+                                      (257, 256, False, 1), (511, 255, True, 1)])
 def test_scan_matches_recurrence(env, T, Q, h0, B):
     nh, oracle, gu, torch = env
     _say("scan", T, Q, h0, B)
@@ -364,18 +372,18 @@ def test_scan_matches_recurrence(env, T, Q, h0, B):
         _rows(gu, yg[b], ry, f"scan T={T} Q={Q} b{b}")
 
 
-def test_scan_bf16_output_and_alias(env):
+@pytest.mark.parametrize("T,Q", [(100, 32), (300, 256)])
+def test_scan_bf16_output_and_alias(env, T, Q):
     nh, oracle, gu, torch = env
-    _say("scan bf16 + aliased state")
-    rng = np.random.default_rng(77)
+    _say("scan bf16 + aliased state", T, Q)
+    rng = np.random.default_rng(77 + T)
     lw = synth.layer_weights(2)
-    T = 100
     xc, dtr = _scan_inputs(rng, 1, T)
     S0 = (0.1 * rng.normal(size=(1, 128, 80, 128))).astype(np.float32)
     Sd = gu.to_dev(S0)
     y = gu.empty_u16(1, T, 10240)
-    nh.nh_ssd_chunk_scan(nh.dims(chunk=32), gu.to_dev(xc), gu.to_dev(dtr), 128, T, gu.to_dev(lw.dt_bias),
-                         gu.to_dev(lw.A_log), gu.to_dev(lw.D), Sd, Sd, y, nh.NH_BF16, 1, *_scan_ws(nh, gu, 32, 1, T))
+    nh.nh_ssd_chunk_scan(nh.dims(chunk=Q), gu.to_dev(xc), gu.to_dev(dtr), 128, T, gu.to_dev(lw.dt_bias),
+                         gu.to_dev(lw.A_log), gu.to_dev(lw.D), Sd, Sd, y, nh.NH_BF16, 1, *_scan_ws(nh, gu, Q, 1, T))
     ry, rS = _oracle_scan(oracle, gu, lw, xc[0], dtr[0], S0[0].astype(np.float64))
     yb = gu.bf16_bits_to_f64(gu.from_dev_u16(y)[0])
     assert gu.rel_l2(yb, ry) < 4e-3
@@ -383,7 +391,7 @@ def test_scan_bf16_output_and_alias(env):
     assert gu.rel_l2(Sd.cpu().numpy()[0], rS) < 1e-3
 
 
-@pytest.mark.parametrize("T,Q", [(413, 128), (29, 256), (7, 4)])
+@pytest.mark.parametrize("T,Q", [(413, 128), (29, 256), (7, 4), (257, 256), (190, 160)])
 def test_scan_stores_stay_inside_the_sequence(env, T, Q):
     """Rows past T in the last, partial chunk are computed as padding and must never be stored:
     the memory right after y (and before it) keeps its contents."""
