@@ -174,6 +174,72 @@ __device__ __forceinline__ size_t cb_base(int ck, int Q, int L, int batch, int b
 // computes the tile D = B_J C_I^T (D lane layout: rows j = 16J + 4q + r, column
 // i = 16I + l16), which is the G layout the scan reads.  Diagonal tiles hold 0 above the
 // diagonal (j > i): the causal mask.
+// Tables of one (chunk, sequence, group) for its 16 heads: wave w takes heads 2w and 2w + 1, lane
+// l positions 4l .. 4l + 3 of the chunk's P = 32 NJ(L) (dt = 0 past L).
+__device__ __forceinline__ void ssd_tables(const uint16_t *__restrict__ dtr, long ld_dt,
+                                           const float *__restrict__ dt_bias, const float *__restrict__ A_log,
+                                           char *__restrict__ Tw, int T, int Q, int c, int g, int b, int batch,
+                                           int L, int wave, int lane)
+{
+    const int t0 = c * Q, P = 32 * nj_of(L);
+    // tables of heads 2 wave and 2 wave + 1: lane l covers positions j = 4 l + r, r = 0..3
+    const float LOG2E = 1.4426950408889634f;
+    const uint16_t *dseq = dtr + ((size_t)b * T + t0) * ld_dt;
+    // the raw dt of both heads, all loads issued first (positions past L clamped, then zeroed)
+    uint16_t raw[2][4];
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            raw[k][r] = dseq[(size_t)min(4 * lane + r, L - 1) * ld_dt + g * HPG + 2 * wave + k];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int h = g * HPG + 2 * wave + k;
+        const float A2 = -expf(A_log[h]) * LOG2E;  // dt*A in log2 units
+        const float dtb = dt_bias[h];
+        float dt[4], s[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int j = 4 * lane + r;
+            dt[r] = j < L ? softplus_fast(bf16_to_f32(raw[k][r]) + dtb) : 0.f;
+            s[r] = (r ? s[r - 1] : 0.f) + dt[r] * A2;
+        }
+        // inclusive sum of the lane totals over the wave (row shifts, then the row ends
+        // broadcast into the following rows); the exclusive sum is the previous lane's
+        float v = s[3];
+        v += dpp_f<0x111, 0xF>(v);  // row_shr:1
+        v += dpp_f<0x112, 0xF>(v);  // row_shr:2
+        v += dpp_f<0x114, 0xF>(v);  // row_shr:4
+        v += dpp_f<0x118, 0xF>(v);  // row_shr:8
+        v += dpp_f<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+        v += dpp_f<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+        float ex = __shfl(v, (lane + 63) & 63, 64);
+        if (lane == 0) ex = 0.f;
+        float cum[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) cum[r] = ex + s[r];
+        // cumulative value at the end of the position's 16-row block (position 16 m + 15 is
+        // lane 4 m + 3, r = 3) and at the chunk end (a_j = 0 for j >= L)
+        const float cend = __shfl(cum[3], lane | 3, 64);
+        const float cl = __shfl(cum[3], P / 4 - 1, 64);
+        if (4 * lane < P) {
+            char *tb = Tw + (size_t)c * batch * NHEADS * tab_bytes(Q) + (size_t)(b * NHEADS + h) * tab_bytes(L);
+            float F[4];
+            _Float16 W[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                F[r] = __builtin_amdgcn_exp2f(cend - cum[r]) * dt[r];
+                W[r] = (_Float16)(__builtin_amdgcn_exp2f(cl - cum[r]) * dt[r]);
+            }
+            reinterpret_cast<float4 *>(tb)[lane] = make_float4(cum[0], cum[1], cum[2], cum[3]);
+            reinterpret_cast<float4 *>(tb + 4 * P)[lane] = make_float4(dt[0], dt[1], dt[2], dt[3]);
+            reinterpret_cast<float4 *>(tb + 8 * P)[lane] = make_float4(F[0], F[1], F[2], F[3]);
+            reinterpret_cast<uint2 *>(tb + 12 * P)[lane] =
+                make_uint2(__builtin_bit_cast(uint32_t, half2v{W[0], W[1]}), __builtin_bit_cast(uint32_t, half2v{W[2], W[3]}));
+        }
+    }
+}
+
 // Long-chunk operands (EXT).  For k_ssd_scanx the pre-pass also writes, per (chunk, sequence,
 // group), B in the operand order of the state update, and per (chunk, sequence, head) the chunk's
 // discretisation tables; see k_ssd_scanx for their layouts.
@@ -185,7 +251,11 @@ __global__ __launch_bounds__(CB_THREADS) void k_ssd_cb(const uint16_t *__restric
                                                       char *__restrict__ Cfw, char *__restrict__ Tw)
 {
     __shared__ __attribute__((aligned(16))) uint16_t Bs[QMAX * CB_LD];
-    const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    // EXT: three work-groups per (chunk, group, sequence): role 0 the tiles and C fragments,
+    // role 1 the B fragments, role 2 the tables
+    const int role = EXT ? (int)blockIdx.z % 3 : 0;
+    const int c = blockIdx.x, g = blockIdx.y, b = EXT ? blockIdx.z / 3 : blockIdx.z;
+    const int batch = EXT ? gridDim.z / 3 : gridDim.z;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, q4 = lane >> 4;
@@ -194,22 +264,50 @@ __global__ __launch_bounds__(CB_THREADS) void k_ssd_cb(const uint16_t *__restric
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(xc + ((size_t)b * T + t0) * CONVDIM), 0, (int)((uint32_t)L * XROW), 0x00020000);
 
+    if (EXT && role == 2) {
+        ssd_tables(dtr, ld_dt, dt_bias, A_log, Tw, T, Q, c, g, b, batch, L, wave, lane);
+        return;
+    }
     const int Ib[2] = {wave, 15 - wave};
     uint4 cq[2][4];
+    if (role == 0)
 #pragma unroll
-    for (int bi = 0; bi < 2; ++bi)
+        for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            cq[bi][ks] = bload16(rx, (uint32_t)(16 * Ib[bi] + l16) * XROW + (OFF_C + g * DSTATE + 32 * ks + 8 * q4) * 2, 0);
-    const int nrows = EXT ? 32 * nj_of(L) : 16 * nb;  // rows past L read as zero
-    for (int v = tid; v < nrows * 16; v += CB_THREADS) {
-        const int row = v >> 4, pc = v & 15;
-        *reinterpret_cast<uint4 *>(&Bs[row * CB_LD + 8 * pc]) =
-            bload16(rx, (uint32_t)row * XROW + (OFF_B + g * DSTATE + 8 * pc) * 2, 0);
+            for (int ks = 0; ks < 4; ++ks)
+                cq[bi][ks] = bload16(rx, (uint32_t)(16 * Ib[bi] + l16) * XROW + (OFF_C + g * DSTATE + 32 * ks + 8 * q4) * 2, 0);
+    // B rows to LDS: every load issued before the first LDS write (rows past L read as zero)
+    {
+        const int nrows = role == 1 ? 32 * nj_of(L) : 16 * nb;
+        constexpr int NV = QMAX * 16 / CB_THREADS;
+        uint4 bv[NV];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int v = tid + CB_THREADS * i, row = v >> 4, pc = v & 15;
+            bv[i] = bload16(rx, (uint32_t)row * XROW + (OFF_B + g * DSTATE + 8 * pc) * 2, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int v = tid + CB_THREADS * i, row = v >> 4, pc = v & 15;
+            if (row < nrows) *reinterpret_cast<uint4 *>(&Bs[row * CB_LD + 8 * pc]) = bv[i];
+        }
     }
     __syncthreads();
 
-    uint16_t *Gc = Gw + cb_base(c, Q, L, gridDim.z, b, g) + lane * 8;
+    if (EXT && role == 1) {
+        // B fragment (jp, state block n = wave): lane (q, i) holds B[32 jp + 4 q + e][16 n + i] for
+        // e < 4 and B[32 jp + 16 + 4 q + e - 4][16 n + i] for e >= 4, as fp16 (exact in range)
+        char *bf = Bfw + (size_t)c * batch * NGROUPS * btf_bytes(Q) + (size_t)(b * NGROUPS + g) * btf_bytes(L);
+        for (int jp = 0; jp < nj_of(L); ++jp) {
+            const uint2 lo = ld_tr(Bs, CB_LD, 32 * jp + 4 * q4, 16 * wave);
+            const uint2 hi = ld_tr(Bs, CB_LD, 32 * jp + 16 + 4 * q4, 16 * wave);
+            *reinterpret_cast<uint4 *>(bf + ((size_t)(jp * 8 + wave) * 64 + lane) * 16) =
+                make_uint4(bf16x2_to_f16x2(lo.x), bf16x2_to_f16x2(lo.y), bf16x2_to_f16x2(hi.x), bf16x2_to_f16x2(hi.y));
+        }
+        return;
+    }
+
+    uint16_t *Gc = Gw + cb_base(c, Q, L, batch, b, g) + lane * 8;
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi) {
         const int I = Ib[bi];
@@ -244,7 +342,6 @@ __global__ __launch_bounds__(CB_THREADS) void k_ssd_cb(const uint16_t *__restric
         }
     }
     if constexpr (EXT) {
-        const int batch = gridDim.z, NJ = nj_of(L), P = 32 * NJ;
         // C fragment (row block I, step ks): lane (q, i) holds C[16 I + i][32 ks + 8 q .. + 7]
         char *cfw = Cfw + (size_t)c * batch * NGROUPS * cfr_bytes(Q) + (size_t)(b * NGROUPS + g) * cfr_bytes(L);
 #pragma unroll
@@ -253,63 +350,6 @@ __global__ __launch_bounds__(CB_THREADS) void k_ssd_cb(const uint16_t *__restric
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks)
                     *reinterpret_cast<uint4 *>(cfw + ((size_t)(Ib[bi] * 4 + ks) * 64 + lane) * 16) = bf16x8_to_f16x8(cq[bi][ks]);
-        // B fragment (jp, state block n = wave): lane (q, i) holds B[32 jp + 4 q + e][16 n + i] for
-        // e < 4 and B[32 jp + 16 + 4 q + e - 4][16 n + i] for e >= 4, as fp16 (exact in range)
-        char *bf = Bfw + (size_t)c * batch * NGROUPS * btf_bytes(Q) + (size_t)(b * NGROUPS + g) * btf_bytes(L);
-        for (int jp = 0; jp < NJ; ++jp) {
-            const uint2 lo = ld_tr(Bs, CB_LD, 32 * jp + 4 * q4, 16 * wave);
-            const uint2 hi = ld_tr(Bs, CB_LD, 32 * jp + 16 + 4 * q4, 16 * wave);
-            *reinterpret_cast<uint4 *>(bf + ((size_t)(jp * 8 + wave) * 64 + lane) * 16) =
-                make_uint4(bf16x2_to_f16x2(lo.x), bf16x2_to_f16x2(lo.y), bf16x2_to_f16x2(hi.x), bf16x2_to_f16x2(hi.y));
-        }
-        // tables of heads 2 wave and 2 wave + 1: lane l covers positions j = 4 l + r, r = 0..3
-        const float LOG2E = 1.4426950408889634f;
-        const uint16_t *dseq = dtr + ((size_t)b * T + t0) * ld_dt;
-        for (int k = 0; k < 2; ++k) {
-            const int h = g * HPG + 2 * wave + k;
-            const float A2 = -expf(A_log[h]) * LOG2E;  // dt*A in log2 units
-            const float dtb = dt_bias[h];
-            float dt[4], s[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int j = 4 * lane + r;
-                dt[r] = j < L ? softplus_fast(bf16_to_f32(dseq[(size_t)j * ld_dt + h]) + dtb) : 0.f;
-                s[r] = (r ? s[r - 1] : 0.f) + dt[r] * A2;
-            }
-            // inclusive sum of the lane totals over the wave (row shifts, then the row ends
-            // broadcast into the following rows); the exclusive sum is the previous lane's
-            float v = s[3];
-            v += dpp_f<0x111, 0xF>(v);  // row_shr:1
-            v += dpp_f<0x112, 0xF>(v);  // row_shr:2
-            v += dpp_f<0x114, 0xF>(v);  // row_shr:4
-            v += dpp_f<0x118, 0xF>(v);  // row_shr:8
-            v += dpp_f<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
-            v += dpp_f<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
-            float ex = __shfl(v, (lane + 63) & 63, 64);
-            if (lane == 0) ex = 0.f;
-            float cum[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) cum[r] = ex + s[r];
-            // cumulative value at the end of the position's 16-row block (position 16 m + 15 is
-            // lane 4 m + 3, r = 3) and at the chunk end (a_j = 0 for j >= L)
-            const float cend = __shfl(cum[3], lane | 3, 64);
-            const float cl = __shfl(cum[3], P / 4 - 1, 64);
-            if (4 * lane < P) {
-                char *tb = Tw + (size_t)c * batch * NHEADS * tab_bytes(Q) + (size_t)(b * NHEADS + h) * tab_bytes(L);
-                float F[4];
-                _Float16 W[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    F[r] = __builtin_amdgcn_exp2f(cend - cum[r]) * dt[r];
-                    W[r] = (_Float16)(__builtin_amdgcn_exp2f(cl - cum[r]) * dt[r]);
-                }
-                reinterpret_cast<float4 *>(tb)[lane] = make_float4(cum[0], cum[1], cum[2], cum[3]);
-                reinterpret_cast<float4 *>(tb + 4 * P)[lane] = make_float4(dt[0], dt[1], dt[2], dt[3]);
-                reinterpret_cast<float4 *>(tb + 8 * P)[lane] = make_float4(F[0], F[1], F[2], F[3]);
-                reinterpret_cast<uint2 *>(tb + 12 * P)[lane] =
-                    make_uint2(__builtin_bit_cast(uint32_t, half2v{W[0], W[1]}), __builtin_bit_cast(uint32_t, half2v{W[2], W[3]}));
-            }
-        }
     }
 }
 
@@ -746,15 +786,17 @@ __global__ __launch_bounds__(SC_THREADS, 1) void k_ssd_scanx(const uint16_t *__r
                                                  (uint32_t)((wave & 3) * 64 + lane) * 16, 0, 0, 0);
     };
 
-    // State: st[pb] holds S[16pb + 4q4 + r][16 wave + l16], r = 0..3.
+    // State, as the transposed accumulator of the state update: st[pb] holds
+    // S[16pb + l16][16 wave + 4q4 + r], r = 0..3 (four consecutive state columns of one row).
     floatx4 st[5];
     {
         const float *S0 = h0 ? h0 + ((size_t)b * NHEADS + h) * HDIM * DSTATE : nullptr;
 #pragma unroll
-        for (int pb = 0; pb < 5; ++pb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                st[pb][r] = S0 ? S0[(16 * pb + 4 * q4 + r) * DSTATE + 16 * wave + l16] : 0.f;
+        for (int pb = 0; pb < 5; ++pb) {
+            const float4 v = S0 ? *reinterpret_cast<const float4 *>(&S0[(16 * pb + l16) * DSTATE + 16 * wave + 4 * q4])
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+            st[pb] = floatx4{v.x, v.y, v.z, v.w};
+        }
     }
 
     // outputs of blocks I0 and I1 of a chunk (Y^T, lane: column 16 I + l16, rows 16 pb + 4 q4 + r)
@@ -762,8 +804,7 @@ __global__ __launch_bounds__(SC_THREADS, 1) void k_ssd_scanx(const uint16_t *__r
 
     // y of chunk ck (the skip term is in the diagonal tiles).  bf16 output goes through the
     // wave's LDS rows so that each 16-byte store covers 8 consecutive columns of one row.  Called
-    // at the start of the next chunk, before its DMA is issued: with a DMA into LDS in flight,
-    // the compiler makes these LDS writes wait for it.
+    // at the start of the next chunk, while no DMA into LDS is in flight.
     auto store_y = [&](int ck) {
         const int t0 = ck * Q, L = min(Q, T - t0), nb = (L + 15) >> 4;
         const __amdgpu_buffer_rsrc_t ry = rsrc(yseq + (size_t)t0 * YROW, (uint32_t)L * YROW);
@@ -802,9 +843,6 @@ __global__ __launch_bounds__(SC_THREADS, 1) void k_ssd_scanx(const uint16_t *__r
     auto chunk = [&](int ck, uint16_t *Xs, uint32_t *Tb, uint16_t *Xn, uint32_t *Tn) {
         const int t0 = ck * Q, L = min(Q, T - t0), nb = (L + 15) >> 4, NJ = nj_of(L), P = 32 * NJ;
         if (ck > 0) store_y(ck - 1);
-        __builtin_amdgcn_sched_barrier(0);
-        dma(ck + 1, Xn, Tn);
-        __builtin_amdgcn_sched_barrier(0);
         const Src nx = src(min(ck + 1, nch - 1));  // the last chunk re-loads its own operands, unused
 
         // ---- x to fp16 in place (rows < P; rows at or past L are zero), S_in, decay
@@ -817,14 +855,18 @@ __global__ __launch_bounds__(SC_THREADS, 1) void k_ssd_scanx(const uint16_t *__r
         const _Float16 *Wh = reinterpret_cast<const _Float16 *>(cum + 3 * P);
 #pragma unroll
         for (int pb = 0; pb < 5; ++pb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                Si[(16 * pb + 4 * q4 + r) * SI_LD + 16 * wave + l16] = __builtin_bit_cast(uint16_t, (_Float16)st[pb][r]);
+            *reinterpret_cast<uint2 *>(&Si[(16 * pb + l16) * SI_LD + 16 * wave + 4 * q4]) =
+                make_uint2(pack_rne(st[pb][0], st[pb][1]), pack_rne(st[pb][2], st[pb][3]));
         const float dec = __builtin_amdgcn_exp2f(cum[P - 1]);
 #pragma unroll
         for (int pb = 0; pb < 5; ++pb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) st[pb][r] *= dec;
+        // the next chunk's DMA, after this wave's LDS writes of the chunk (with a DMA into LDS in
+        // flight, the compiler would make them wait for it)
+        __builtin_amdgcn_sched_barrier(0);
+        dma(ck + 1, Xn, Tn);
+        __builtin_amdgcn_sched_barrier(0);
         lds_barrier();
 
         // ---- Y^T = S_in C^T for both blocks (S_in fragments shared), scaled by exp(cum_i)
@@ -904,8 +946,9 @@ __global__ __launch_bounds__(SC_THREADS, 1) void k_ssd_scanx(const uint16_t *__r
                 const uint2 wlo = *reinterpret_cast<const uint2 *>(&Wh[32 * jp + 4 * q4]);
                 const uint2 whi = *reinterpret_cast<const uint2 *>(&Wh[32 * jp + 16 + 4 * q4]);
                 const half8 bw = __builtin_bit_cast(half8, bt[jp]) * cat(wlo, whi);
+                // S^T += (w B)^T x: the B fragment is the A operand (rows: state columns), x the B
 #pragma unroll
-                for (int pb = 0; pb < 5; ++pb) st[pb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xf[pb], bw, st[pb], 0, 0, 0);
+                for (int pb = 0; pb < 5; ++pb) st[pb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bw, xf[pb], st[pb], 0, 0, 0);
                 if (jp < 4 && v0 && jp <= (I0 >> 1)) {
                     const half8 m = pair(ci0, I0, jp, gp0[jp < 4 ? jp : 0]);
 #pragma unroll
@@ -952,8 +995,8 @@ __global__ __launch_bounds__(SC_THREADS, 1) void k_ssd_scanx(const uint16_t *__r
         float *Sg = hT + ((size_t)b * NHEADS + h) * HDIM * DSTATE;
 #pragma unroll
         for (int pb = 0; pb < 5; ++pb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Sg[(16 * pb + 4 * q4 + r) * DSTATE + 16 * wave + l16] = st[pb][r];
+            *reinterpret_cast<float4 *>(&Sg[(16 * pb + l16) * DSTATE + 16 * wave + 4 * q4]) =
+                make_float4(st[pb][0], st[pb][1], st[pb][2], st[pb][3]);
     }
 }
 
@@ -1000,7 +1043,7 @@ hipError_t launch_ssd_scan(const uint16_t *xc, const uint16_t *dtr, long ld_dt, 
         const int full = T / Q, last = T - full * Q;
         char *Cf = Bf + (size_t)batch * NGROUPS * ((size_t)full * btf_bytes(Q) + (last ? btf_bytes(last) : 0));
         char *Tb = Cf + (size_t)batch * NGROUPS * ((size_t)full * cfr_bytes(Q) + (last ? cfr_bytes(last) : 0));
-        k_ssd_cb<true><<<dim3(nch, NGROUPS, batch), CB_THREADS, 0, st>>>(xc, T, Q, Gws, dtr, ld_dt, dt_bias, A_log,
+        k_ssd_cb<true><<<dim3(nch, NGROUPS, batch * 3), CB_THREADS, 0, st>>>(xc, T, Q, Gws, dtr, ld_dt, dt_bias, A_log,
                                                                           Bf, Cf, Tb);
         if (y_t == BF16)
             k_ssd_scanx<BF16><<<grid, block, 0, st>>>(xc, T, Q, D, h0, hT, y, Gws, Bf, Cf, Tb);
