@@ -166,7 +166,7 @@ struct Carve {
 
 struct StepWs {
     uint16_t *z, *xc, *dtr;
-    float *gate, *part;
+    float *gate, *part, *osum;
 };
 
 StepWs carve_step(void *ws, int B, size_t *bytes)
@@ -178,6 +178,7 @@ StepWs carve_step(void *ws, int B, size_t *bytes)
     s.dtr = c.take<uint16_t>((size_t)B * NHEADS);
     s.gate = c.take<float>((size_t)B * DINNER);
     s.part = c.take<float>((size_t)B * NHEADS * 2);
+    s.osum = c.take<float>(outproj_partial_floats(B));
     *bytes = c.off;
     return s;
 }
@@ -235,7 +236,7 @@ nh_status block_step(const nh_mamba_dims *d, const nh_mamba_weights *w, nh_mamba
                                 w->gnorm_w, k.part, B, s),
            "ssm step");
     prof_arm(2);
-    NH_HIP(launch_outproj_step(view(&w->out_proj), k.gate, k.part, d->eps, B, x, x_t, out, out_t, s),
+    NH_HIP(launch_outproj_step(view(&w->out_proj), k.gate, k.part, d->eps, B, x, x_t, out, out_t, k.osum, s),
            "out_proj step");
     prof_next() = ProfEvents{};
     return ok();

@@ -1173,6 +1173,158 @@ __global__ __launch_bounds__(MFL_NT, 1) void k_w4_mfl(W4 W, Act act_in, Epi epi)
     }
 }
 
+// ----------------------------- batched out_proj, split over K by the gated-norm groups
+//
+// At batch 2..4 the gated norm + out_proj (4480 x 10240) runs split over K by the eight
+// gated-norm groups of 1280 channels: work-group i takes group g = i mod 8 (so each XCD streams
+// one group's weight columns and holds one group's activations) and rows [140 (i / 8), +140).
+// It builds only its group's NB x 40 activation chunks, where a work-group over the whole of K
+// builds NB x 320 (at batch 4 that build, from every work-group's 160 KB of g w, took most of the
+// full-K kernel's time).  The group's rstd needs only its own 32 per-(head, half) sums of
+// squares.  Each 4-row stage runs on the 4x4x4 matrix-core blocks as in k_w4_mfl (block kb takes
+// chunks kb, kb + 16, kb + 32 of the group's 40; the third is zero for kb >= 8).  The eight
+// groups' partial sums go to the workspace ([group][batch row][row] fp32) and k_sk_reduce adds
+// them in group order, then the residual: the result does not depend on timing.
+constexpr int SK_ROWS = HIDDEN / 32, SK_NCH = GNORM / 32, SK_STAGES = SK_ROWS / 4, SK_NT = 512;
+
+struct SkUnit {
+    uint4 q[3];
+    uint16_t s[3], b[3];
+};
+
+template <int NB>
+__global__ __launch_bounds__(SK_NT, 1) void k_outproj_sk(W4 W, const float *__restrict__ gate,
+                                                         const float *__restrict__ part, float eps,
+                                                         float *__restrict__ partial)
+{
+    __shared__ __attribute__((aligned(16))) uint32_t act[(NB * SK_NCH + 1) * ACT_WORDS];
+    __shared__ float rstd[NB];
+    const int g = blockIdx.x & 7, row0 = SK_ROWS * (int)(blockIdx.x >> 3);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kb = lane >> 2, q4 = lane & 3;
+    const uint32_t rowbytes = (uint32_t)W.k / 2, kg2 = (uint32_t)(W.k >> 6) * 2;
+    const int s0 = SK_STAGES * wave / 8, s1 = SK_STAGES * (wave + 1) / 8;  // this wave's stages
+    const int nu = s1 - s0;
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void *)W.q, 0, (int)((uint32_t)W.n * rowbytes), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)W.s, 0, (int)((uint32_t)W.n * kg2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rbi = __builtin_amdgcn_make_buffer_rsrc((void *)W.b, 0, (int)((uint32_t)W.n * kg2), 0x00020000);
+
+    // stage u of this wave: lane (kb, q4) loads row row0 + 4 (s0 + u) + q4, chunks kb + 16 t of the
+    // group's 40 (the third clamped for kb >= 8 and unused); past the last stage: re-read it
+    auto load = [&](SkUnit &un, int u) {
+        const uint32_t row = (uint32_t)(row0 + 4 * (s0 + min(u, nu - 1)) + q4);
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+            const uint32_t c = (uint32_t)(SK_NCH * g + min(kb + 16 * t, SK_NCH - 1));
+            un.q[t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, row * rowbytes + 16u * c, 0, NT_LOAD));
+            un.s[t] = __builtin_amdgcn_raw_buffer_load_b16(rs, row * kg2 + 2u * (c >> 1), 0, 0);
+            un.b[t] = __builtin_amdgcn_raw_buffer_load_b16(rbi, row * kg2 + 2u * (c >> 1), 0, 0);
+        }
+    };
+
+    // prologue loads first: the group's sums of squares (thread t < 32 NB: batch row t / 32) and
+    // the g w values of one chunk per thread (t < 40 NB: batch row t / 40, chunk t % 40)
+    const int pb = min(tid >> 5, NB - 1), cb = min(tid / SK_NCH, NB - 1), cc = tid % SK_NCH;
+    const float pv = part[pb * NHEADS * 2 + 32 * g + (tid & 31)];
+    float4 gv[8];
+    {
+        const float4 *gp = reinterpret_cast<const float4 *>(gate + (size_t)cb * DINNER + GNORM * g + 32 * cc);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) gv[j] = gp[j];
+    }
+    SkUnit A, B;
+    load(A, 0);
+    // slot NB * 40: a zero chunk for the lanes with no activation (batch rows past NB, chunks
+    // past the group's 40), so that every LDS read is unconditional
+    uint32_t *zslot = act + NB * SK_NCH * ACT_WORDS;
+    if (tid < ACT_WORDS) zslot[tid] = tid == 18 ? 0x3F800000u : 0u;
+    if (tid < 32 * NB) {
+        const float tot = row_sum<32>(pv);
+        if ((tid & 31) == 0) rstd[tid >> 5] = 1.0f / sqrtf(tot / (float)GNORM + eps);
+    }
+    __syncthreads();
+    if (tid < SK_NCH * NB) {
+        const float r = rstd[cb];
+        float v[32];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            v[4 * j] = round_bf16(gv[j].x * r);
+            v[4 * j + 1] = round_bf16(gv[j].y * r);
+            v[4 * j + 2] = round_bf16(gv[j].z * r);
+            v[4 * j + 3] = round_bf16(gv[j].w * r);
+        }
+        make_chunk(v, act + (size_t)(cc * NB + cb) * ACT_WORDS);
+    }
+    __syncthreads();
+    if (nu == 0) return;
+
+    const uint32_t mlo = opaque_v(0x000F000Fu), mhi = opaque_v(0x00F000F0u), magic = opaque_v(0x64006400u);
+    const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+    auto unit = [&](const SkUnit &un, int u) {
+        floatx4 acc = zero, E = zero;
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+            // the A operand: batch row q4's chunk (zero beyond NB and past the group's chunks)
+            const int c = kb + 16 * t;
+            ActChunk a;
+            chunk_from_lds(a, q4 < NB && c < SK_NCH ? act + ((size_t)c * NB + q4) * ACT_WORDS : zslot);
+            floatx4 D = __builtin_amdgcn_mfma_f32_4x4x1f32(-a.off, 1.0f, zero, 0, 0, 0), D2 = zero;
+            const uint32_t wq[4] = {un.q[t].x, un.q[t].y, un.q[t].z, un.q[t].w};
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t wd = wq[w], wh = wd >> 8;
+                const uint32_t d0 = and_or_mf(wd, mlo, magic), d1 = and_or_mf(wd, mhi, magic);
+                const uint32_t d2 = and_or_mf(wh, mlo, magic), d3 = and_or_mf(wh, mhi, magic);
+                D = __builtin_amdgcn_mfma_f32_4x4x4f16(h4_of(a.p[4 * w], a.p[4 * w + 2]), h4_of(d0, d2), D, 0, 0, 0);
+                D2 = __builtin_amdgcn_mfma_f32_4x4x4f16(h4_of(a.p[4 * w + 1], a.p[4 * w + 3]), h4_of(d1, d3), D2, 0, 0, 0);
+            }
+            const float sc = __uint_as_float((uint32_t)un.s[t] << 16), bi = __uint_as_float((uint32_t)un.b[t] << 16);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[v] = fmaf(sc, fmaf(D2[v], 0.0625f, D[v]), acc[v]);
+            E = __builtin_amdgcn_mfma_f32_4x4x1f32(a.sum, bi, E, 0, 0, 0);
+        }
+        // the 16 blocks' partials: lane (kb, q4) ends with batch row kb's sum for row q4
+        float tot[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            float x = acc[v] + E[v];
+            x += dpp_mov<0x124>(x);  // row_ror:4
+            x += dpp_mov<0x128>(x);  // row_ror:8
+            x = xor32_sum(xor16_sum(x));
+            tot[v] = x;
+        }
+        const int bsel = lane >> 2;
+        const float mine = bsel == 0 ? tot[0] : bsel == 1 ? tot[1] : bsel == 2 ? tot[2] : tot[3];
+        if (lane < 4 * NB)
+            partial[(size_t)(g * NB + bsel) * HIDDEN + row0 + 4 * (s0 + u) + q4] = mine;
+    };
+    // two stages per iteration with no conditional load; only the second compute is conditional
+    for (int u = 0; u < nu; u += 2) {
+        load(B, u + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        unit(A, u);
+        load(A, u + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        if (u + 1 < nu) unit(B, u + 1);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// y[b][row] = sum over the eight groups of partial[g][b][row] (in group order) + res[b][row]
+template <int NB>
+__global__ __launch_bounds__(256) void k_sk_reduce(const float *__restrict__ partial, EpiStore epi)
+{
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= NB * HIDDEN) return;
+    const int b = i / HIDDEN, row = i - b * HIDDEN;
+    const EpiPre pe = epi.prefetch(row, b);
+    float v = 0.f;
+#pragma unroll
+    for (int g = 0; g < NGROUPS; ++g) v += partial[(size_t)(g * NB + b) * HIDDEN + row];
+    epi(row, b, v, pe);
+}
+
 size_t mfl_lds_bytes(int batch, int k) { return ((size_t)batch * (k / 32) + 1) * ACT_WORDS * 4; }
 
 // chunk slots per lane-block and slice for K = 32 nch: the fewest slots, then the largest CH
@@ -1731,20 +1883,35 @@ hipError_t launch_gemv(const W4 &W, const void *x, int x_t, int batch, const voi
     return x_t == BF16 ? launch_gemv_t<BF16>(W, x, batch, e, st) : launch_gemv_t<F32>(W, x, batch, e, st);
 }
 
+size_t outproj_partial_floats(int batch) { return batch > 1 ? (size_t)NGROUPS * batch * HIDDEN : 0; }
+
 hipError_t launch_outproj_step(const W4 &W, const float *gate, const float *part,
                                float eps, int batch, const void *res, int res_t, void *out, int out_t,
-                               hipStream_t st)
+                               float *partial, hipStream_t st)
 {
     EpiStore e{out, res, out_t, res_t, W.n};
-    const size_t lds = (size_t)batch * (DINNER / 32) * ACT_WORDS * 4;
-    // one work-group per CU: 8 waves at batch 1; 4 waves (more registers each) above
-    const int grid = min(cu_count(), (W.n + 7) / 8);
+    if (batch == 1) {
+        // one work-group of 8 waves per CU
+        const size_t lds = (size_t)(DINNER / 32) * ACT_WORDS * 4;
+        const int grid = min(cu_count(), (W.n + 7) / 8);
+        launch_k(k_outproj_step<1>, dim3(grid), dim3(512), lds, st, W, gate, part, eps, e);
+        return hipGetLastError();
+    }
+    // batch 2..4: split over the gated-norm groups, then the ordered sum
+    const dim3 grid(NGROUPS * (HIDDEN / SK_ROWS)), rgrid((batch * HIDDEN + 255) / 256);
     switch (batch) {
-    case 1: launch_k(k_outproj_step<1>, dim3(grid), dim3(512), lds, st, W, gate, part, eps, e); break;
-    case 2: launch_k(k_outproj_step<2>, dim3(grid), dim3(256), lds, st, W, gate, part, eps, e); break;
-    case 3: launch_k(k_outproj_step<3>, dim3(grid), dim3(256), lds, st, W, gate, part, eps, e); break;
-    // batch 4: the matrix-core kernel (19.3 us against 22.1 for the per-row kernel)
-    default: return launch_mfl<4, false>(W, ActGatedNorm<4, MFL_NT>{gate, part, eps}, e, st);
+    case 2:
+        launch_k(k_outproj_sk<2>, grid, dim3(SK_NT), 0, st, W, gate, part, eps, partial);
+        launch_k(k_sk_reduce<2>, rgrid, dim3(256), 0, st, (const float *)partial, e);
+        break;
+    case 3:
+        launch_k(k_outproj_sk<3>, grid, dim3(SK_NT), 0, st, W, gate, part, eps, partial);
+        launch_k(k_sk_reduce<3>, rgrid, dim3(256), 0, st, (const float *)partial, e);
+        break;
+    default:
+        launch_k(k_outproj_sk<4>, grid, dim3(SK_NT), 0, st, W, gate, part, eps, partial);
+        launch_k(k_sk_reduce<4>, rgrid, dim3(256), 0, st, (const float *)partial, e);
+        break;
     }
     return hipGetLastError();
 }

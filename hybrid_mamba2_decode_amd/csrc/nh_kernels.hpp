@@ -76,9 +76,12 @@ hipError_t launch_ssm_step_part(const uint16_t *xc, const uint16_t *dtr, long ld
                                 float *S, float *gate, const uint16_t *z, const uint16_t *gw, float *part, int batch,
                                 hipStream_t st);
 // Gated RMSNorm (from g w and the SSM step's partial sums of g) fused into out_proj + residual.
+// Above batch 1 it runs split over the gated-norm groups: partial receives the groups' sums
+// (outproj_partial_floats(batch) floats; unused at batch 1).
+size_t outproj_partial_floats(int batch);
 hipError_t launch_outproj_step(const W4 &W, const float *gate, const float *part,
                                float eps, int batch, const void *res, int res_t, void *out, int out_t,
-                               hipStream_t st);
+                               float *partial, hipStream_t st);
 hipError_t launch_conv_step(const uint16_t *xbc, long ld, uint16_t *state, const uint16_t *w,
                             const uint16_t *b, uint16_t *out, int batch, int channels,
                             hipStream_t st);

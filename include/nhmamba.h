@@ -442,7 +442,7 @@ nh_status nh_mamba_block_step(const nh_mamba_dims *d, const nh_mamba_weights *w,
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * allocation.  Same computation, kernels and results as nh_mamba_block_step,
  * but the step workspace is the library's own file-scope device array
- * (352 KiB per GPU, held until the process ends), so no workspace argument
+ * (1 MiB per GPU, held until the process ends), so no workspace argument
  * is taken and nothing is allocated or freed.  Every call on one GPU shares
  * that GPU's array: calls that can overlap on one GPU (two streams, two
  * threads) race and must be serialised by the caller.  The array keeps the
