@@ -152,6 +152,10 @@ def traffic_from_profile(kernel: str, *sources: str):
     return None
 
 
+def _sum_or_none(*v):
+    return None if any(x is None for x in v) else float(sum(v))
+
+
 def counters_from_profile(kernel: str, *sources: str):
     """MFMA busy fraction, matrix-core TFLOP/s and LDS bank-conflict share of one kernel from the
     committed counter summary, or None when absent or when the kernel's source changed after
@@ -616,17 +620,19 @@ def main():
         fl = scan_flops_per_position(Q4)
         by = scan_bytes_per_position()
         out["scan"] = {
-            "workload": "chunked SSD scan (C.B^T pre-pass + scan), batch 2, T=3750, chunk 256, 27 layers' "
+            "workload": "chunked SSD scan (pre-pass + scan), batch 2, T=3750, chunk 256, 27 layers' "
                         "parameters, 3 rotating input sets",
             "metric": "SSD scan positions/s", "value": round(pps, 1), "unit": "position-layers/s",
             "avg_launch_us": round(float(per.mean() * 1e3), 2),
             "mfma_frac": round(pps * fl / MFMA_F16_PEAK, 4),
             "hbm_frac": round(pps * by / HBM_PEAK, 4),
-            "roofline": {"kernel": "k_ssd_scan + k_ssd_cb", "bound": "mfma",
+            "roofline": {"kernel": "k_ssd_scanx + k_ssd_cb", "bound": "mfma",
                          "achieved": round(pps * fl / 1e12, 1), "peak": MFMA_F16_PEAK / 1e12, "unit": "TFLOP/s",
                          "frac": round(pps * fl / MFMA_F16_PEAK, 4),
-                         "traffic": traffic_from_profile("k_ssd_scan", "scan.hip", "nh_device.hpp"),
-                         "counters": counters_from_profile("k_ssd_scan", "scan.hip", "nh_device.hpp"),
+                         # HBM bytes of one scan call: the scan kernel and its pre-pass
+                         "traffic": _sum_or_none(traffic_from_profile("k_ssd_scanx", "scan.hip", "nh_device.hpp"),
+                                                 traffic_from_profile("k_ssd_cb", "scan.hip", "nh_device.hpp")),
+                         "counters": counters_from_profile("k_ssd_scanx", "scan.hip", "nh_device.hpp"),
                          "flops_per_position": round(fl), "bytes_per_position": by,
                          "achieved_GBps": round(pps * by / 1e9, 1), "hbm_peak_GBps": HBM_PEAK / 1e9},
         }
