@@ -175,23 +175,25 @@ __device__ __forceinline__ size_t cb_base(int ck, int Q, int L, int batch, int b
 // i = 16I + l16), which is the G layout the scan reads.  Diagonal tiles hold 0 above the
 // diagonal (j > i): the causal mask.
 // Tables of one (chunk, sequence, group) for its 16 heads: wave w takes heads 2w and 2w + 1, lane
-// l positions 4l .. 4l + 3 of the chunk's P = 32 NJ(L) (dt = 0 past L).
-__device__ __forceinline__ void ssd_tables(const uint16_t *__restrict__ dtr, long ld_dt,
-                                           const float *__restrict__ dt_bias, const float *__restrict__ A_log,
-                                           char *__restrict__ Tw, int T, int Q, int c, int g, int b, int batch,
-                                           int L, int wave, int lane)
+// l positions 4l .. 4l + 3 of the chunk's P = 32 NJ(L) (dt = 0 past L).  ssd_tables_load issues
+// the raw dt loads (positions past L clamped), ssd_tables computes and stores the tables.
+__device__ __forceinline__ void ssd_tables_load(const uint16_t *__restrict__ dtr, long ld_dt, int T, int Q, int c,
+                                                int g, int b, int L, int wave, int lane, uint16_t (&raw)[2][4])
 {
-    const int t0 = c * Q, P = 32 * nj_of(L);
-    // tables of heads 2 wave and 2 wave + 1: lane l covers positions j = 4 l + r, r = 0..3
-    const float LOG2E = 1.4426950408889634f;
-    const uint16_t *dseq = dtr + ((size_t)b * T + t0) * ld_dt;
-    // the raw dt of both heads, all loads issued first (positions past L clamped, then zeroed)
-    uint16_t raw[2][4];
+    const uint16_t *dseq = dtr + ((size_t)b * T + (size_t)c * Q) * ld_dt;
 #pragma unroll
     for (int k = 0; k < 2; ++k)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             raw[k][r] = dseq[(size_t)min(4 * lane + r, L - 1) * ld_dt + g * HPG + 2 * wave + k];
+}
+
+__device__ __forceinline__ void ssd_tables(const uint16_t (&raw)[2][4], const float *__restrict__ dt_bias,
+                                           const float *__restrict__ A_log, char *__restrict__ Tw, int Q, int c,
+                                           int g, int b, int batch, int L, int wave, int lane)
+{
+    const int P = 32 * nj_of(L);
+    const float LOG2E = 1.4426950408889634f;
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
         const int h = g * HPG + 2 * wave + k;
@@ -251,11 +253,12 @@ __global__ __launch_bounds__(CB_THREADS) void k_ssd_cb(const uint16_t *__restric
                                                       char *__restrict__ Cfw, char *__restrict__ Tw)
 {
     __shared__ __attribute__((aligned(16))) uint16_t Bs[QMAX * CB_LD];
-    // EXT: three work-groups per (chunk, group, sequence): role 0 the tiles and C fragments,
-    // role 1 the B fragments, role 2 the tables
-    const int role = EXT ? (int)blockIdx.z % 3 : 0;
-    const int c = blockIdx.x, g = blockIdx.y, b = EXT ? blockIdx.z / 3 : blockIdx.z;
-    const int batch = EXT ? gridDim.z / 3 : gridDim.z;
+    // EXT: two work-groups per (chunk, group, sequence): role 0 the tiles and C fragments, role 1
+    // the B fragments and the tables (whose dt loads go out first, so the table arithmetic runs
+    // while B is still arriving)
+    const int role = EXT ? (int)blockIdx.z & 1 : 0;
+    const int c = blockIdx.x, g = blockIdx.y, b = EXT ? blockIdx.z >> 1 : blockIdx.z;
+    const int batch = EXT ? gridDim.z >> 1 : gridDim.z;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, q4 = lane >> 4;
@@ -264,10 +267,8 @@ __global__ __launch_bounds__(CB_THREADS) void k_ssd_cb(const uint16_t *__restric
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(xc + ((size_t)b * T + t0) * CONVDIM), 0, (int)((uint32_t)L * XROW), 0x00020000);
 
-    if (EXT && role == 2) {
-        ssd_tables(dtr, ld_dt, dt_bias, A_log, Tw, T, Q, c, g, b, batch, L, wave, lane);
-        return;
-    }
+    uint16_t raw[2][4];
+    if (EXT && role == 1) ssd_tables_load(dtr, ld_dt, T, Q, c, g, b, L, wave, lane, raw);
     const int Ib[2] = {wave, 15 - wave};
     uint4 cq[2][4];
     if (role == 0)
@@ -286,6 +287,7 @@ __global__ __launch_bounds__(CB_THREADS) void k_ssd_cb(const uint16_t *__restric
             const int v = tid + CB_THREADS * i, row = v >> 4, pc = v & 15;
             bv[i] = bload16(rx, (uint32_t)row * XROW + (OFF_B + g * DSTATE + 8 * pc) * 2, 0);
         }
+        if (EXT && role == 1) ssd_tables(raw, dt_bias, A_log, Tw, Q, c, g, b, batch, L, wave, lane);
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int v = tid + CB_THREADS * i, row = v >> 4, pc = v & 15;
@@ -1043,7 +1045,7 @@ hipError_t launch_ssd_scan(const uint16_t *xc, const uint16_t *dtr, long ld_dt, 
         const int full = T / Q, last = T - full * Q;
         char *Cf = Bf + (size_t)batch * NGROUPS * ((size_t)full * btf_bytes(Q) + (last ? btf_bytes(last) : 0));
         char *Tb = Cf + (size_t)batch * NGROUPS * ((size_t)full * cfr_bytes(Q) + (last ? cfr_bytes(last) : 0));
-        k_ssd_cb<true><<<dim3(nch, NGROUPS, batch * 3), CB_THREADS, 0, st>>>(xc, T, Q, Gws, dtr, ld_dt, dt_bias, A_log,
+        k_ssd_cb<true><<<dim3(nch, NGROUPS, batch * 2), CB_THREADS, 0, st>>>(xc, T, Q, Gws, dtr, ld_dt, dt_bias, A_log,
                                                                           Bf, Cf, Tb);
         if (y_t == BF16)
             k_ssd_scanx<BF16><<<grid, block, 0, st>>>(xc, T, Q, D, h0, hT, y, Gws, Bf, Cf, Tb);
