@@ -1007,62 +1007,6 @@ struct ActPlainK {
     }
 };
 
-// out_proj's gated norm: o = bf16(g w / rms_group(g)) from the SSM step's g w and per-(head,
-// half) sums of g^2 (K = d_inner), unscaled chunks (normalised values).  issue() loads the sums
-// and the thread's g w chunks before the caller's first weight loads.
-template <int NB, int NT>
-struct ActGatedNorm {
-    static constexpr int NCH = DINNER / 32, NPART = NHEADS * 2;
-    static constexpr int MAXC = (NB * NCH + NT - 1) / NT, MAXP = (NB * NPART + NT - 1) / NT;
-    const float *gate, *part;
-    float eps;
-    float pv[MAXP];
-    float4 gv[MAXC][8];
-    __device__ __forceinline__ void issue(int)
-    {
-        // unconditional loads (indices clamped), for the reason given in ActPlainK
-#pragma unroll
-        for (int i = 0; i < MAXP; ++i) pv[i] = part[min((int)threadIdx.x + NT * i, NB * NPART - 1)];
-#pragma unroll
-        for (int i = 0; i < MAXC; ++i) {
-            const int it = min((int)threadIdx.x + NT * i, NB * NCH - 1);
-            const int b = it / NCH, c = it - b * NCH;
-            const float4 *gp = reinterpret_cast<const float4 *>(gate + (size_t)b * DINNER + 32 * c);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) gv[i][j] = gp[j];
-        }
-    }
-    __device__ __forceinline__ void finish(uint32_t *act_lds, int)
-    {
-        __shared__ float rstd[NB][NGROUPS];
-#pragma unroll
-        for (int i = 0; i < MAXP; ++i) {
-            const int t = threadIdx.x + NT * i;  // whole waves: NB * NPART is a multiple of 64
-            const float tot = row_sum<32>(t < NB * NPART ? pv[i] : 0.f);
-            if (t < NB * NPART && (t & 31) == 0) rstd[t / NPART][(t % NPART) / 32] = 1.0f / sqrtf(tot / (float)GNORM + eps);
-        }
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < MAXC; ++i) {
-            const int it = threadIdx.x + NT * i;
-            if (it < NB * NCH) {
-                const int b = it / NCH, c = it - b * NCH;
-                const float r = rstd[b][(32 * c) / GNORM];
-                float v[32];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    v[4 * j] = round_bf16(gv[i][j].x * r);
-                    v[4 * j + 1] = round_bf16(gv[i][j].y * r);
-                    v[4 * j + 2] = round_bf16(gv[i][j].z * r);
-                    v[4 * j + 3] = round_bf16(gv[i][j].w * r);
-                }
-                make_chunk(v, act_lds + (size_t)(c * NB + b) * ACT_WORDS);
-            }
-        }
-        __syncthreads();
-    }
-};
-
 template <int NB, int CH, bool SC, class Act, class Epi>
 __global__ __launch_bounds__(MFL_NT, 1) void k_w4_mfl(W4 W, Act act_in, Epi epi)
 {
@@ -1414,97 +1358,64 @@ __global__ __launch_bounds__(InProjShape<NB>::NT, 1) void k_inproj_step(W4 W, co
     run.run(am, at);
 }
 
-// Fused gated RMSNorm + out_proj + residual for the per-position block.  The work-group forms
+// Fused gated RMSNorm + out_proj + residual for the per-position block at batch 1 (batches
+// 2..4 take the split over norm groups above).  The work-group forms
 // o = bf16((g w) / rms_group(g)) straight into the LDS activation format from g w (the gate
 // product g = bf16(y) * silu(z) times the norm weight) and the per-(head, half) sums of squares
 // of g, both left by the SSM step, while the first stage of out_proj weights is already in
 // flight; o never goes to memory.
-template <int NB>
-__global__ __launch_bounds__(NB == 1 ? 512 : 256, 1) void k_outproj_step(W4 W, const float *__restrict__ gate,
+__global__ __launch_bounds__(512, 1) void k_outproj_step(W4 W, const float *__restrict__ gate,
                                                          const float *__restrict__ part, float eps,
                                                          EpiStore epi)
 {
-    constexpr int LPR = 64, NCH = DINNER / 32, CPL = NCH / LPR, RG = 1, NT = NB == 1 ? 512 : 256;
+    constexpr int NB = 1, LPR = 64, NCH = DINNER / 32, CPL = NCH / LPR, RG = 1, NT = 512;
     extern __shared__ __attribute__((aligned(16))) uint32_t act_lds[];
-    __shared__ float rstd[NB][NGROUPS];
-    auto load = [&](int it, float4 *gv) {
-        const int b = it / NCH, c = it % NCH;
-        const float4 *gp = reinterpret_cast<const float4 *>(gate + (size_t)b * DINNER + 32 * c);
+    __shared__ float rstd[NGROUPS];
+    // The prologue's loads go out alone on waves 0..3 (one per-(head, half) sum of squares per
+    // thread, 32 of which make a group, and the chunks' g w values: chunks t and t + 256);
+    // waves 4..7 issue their first weight stage at once, so their rows stream while the
+    // activations are built.  Waves 0..3 start streaming after the first barrier: issued
+    // together, the prologue loads would queue behind their weight loads.
+    constexpr int PW = 256, GC = (NCH + PW - 1) / PW;
+    const bool early = threadIdx.x >= PW;
+    GemvRunner<LPR, CPL, NB, RG, EpiStore> run(W, epi, NT, early);
+    float4 gv0[GC][8];
+    if (!early) {
+        const float pv = part[threadIdx.x];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) gv[j] = gp[j];
-    };
-    auto build = [&](int it, const float4 *gv) {
-        const int b = it / NCH, c = it % NCH;
-        const float r = rstd[b][(32 * c) / GNORM];
-        float v[32];
+        for (int k = 0; k < GC; ++k) {
+            const int c = min((int)threadIdx.x + PW * k, NCH - 1);
+            const float4 *gp = reinterpret_cast<const float4 *>(gate + 32 * c);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            v[4 * j] = round_bf16(gv[j].x * r);
-            v[4 * j + 1] = round_bf16(gv[j].y * r);
-            v[4 * j + 2] = round_bf16(gv[j].z * r);
-            v[4 * j + 3] = round_bf16(gv[j].w * r);
+            for (int j = 0; j < 8; ++j) gv0[k][j] = gp[j];
         }
-        make_chunk(v, act_lds + (size_t)it * ACT_WORDS);
-    };
-    constexpr int NPART = NHEADS * 2;  // per batch row
-    if constexpr (NB == 1) {
-        // The prologue's loads go out alone on waves 0..3 (one per-(head, half) sum of squares
-        // per thread, 32 of which make a group, and the chunks' g w values: chunks t and t + 256);
-        // waves 4..7 issue their first weight stage at once, so their rows stream while the
-        // activations are built.  Waves 0..3 start streaming after the first barrier: issued
-        // together, the prologue loads would queue behind their weight loads.
-        constexpr int PW = 256, GC = (NCH + PW - 1) / PW;
-        const bool early = threadIdx.x >= PW;
-        GemvRunner<LPR, CPL, NB, RG, EpiStore> run(W, epi, NT, early);
-        float4 gv0[GC][8];
-        if (!early) {
-            const float pv = part[threadIdx.x];
-#pragma unroll
-            for (int k = 0; k < GC; ++k) load(min((int)threadIdx.x + PW * k, NCH - 1), gv0[k]);
-            const float tot = row_sum<32>(pv);  // 32 consecutive entries = one group
-            if ((threadIdx.x & 31) == 0) rstd[0][threadIdx.x / 32] = 1.0f / sqrtf(tot / (float)GNORM + eps);
-        }
-        __syncthreads();
-        if (!early) {
-            run.issue_first();
-#pragma unroll
-            for (int k = 0; k < GC; ++k)
-                if ((int)threadIdx.x + PW * k < NCH) build(threadIdx.x + PW * k, gv0[k]);
-        }
-        __syncthreads();
-        ActChunk a[NB][CPL];
-        act_from_lds<LPR, CPL, NB>(a, act_lds, NCH, (threadIdx.x & 63) % LPR);
-        run.run(a);
-    } else {
-        // The prologue's loads go out alone, and the weight stream starts only once the
-        // work-group has them (after the first barrier; issued together, they would queue behind
-        // every wave's weight loads).
-        constexpr int NPI = (NB * NPART + NT - 1) / NT;
-        float pv[NPI];
-#pragma unroll
-        for (int i = 0; i < NPI; ++i) {
-            const int t = threadIdx.x + NT * i;
-            pv[i] = t < NB * NPART ? part[t] : 0.f;
-        }
-#pragma unroll
-        for (int i = 0; i < NPI; ++i) {
-            const int t = threadIdx.x + NT * i;  // 32 consecutive entries = one group of one row
-            const float tot = row_sum<32>(pv[i]);
-            if (t < NB * NPART && (t & 31) == 0) rstd[t / NPART][(t % NPART) / 32] = 1.0f / sqrtf(tot / (float)GNORM + eps);
-        }
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        GemvRunner<LPR, CPL, NB, RG, EpiStore> run(W, epi, NT);
-        for (int it = threadIdx.x; it < NB * NCH; it += NT) {
-            float4 gv[8];
-            load(it, gv);
-            build(it, gv);
-        }
-        __syncthreads();
-        ActChunk a[NB][CPL];
-        act_from_lds<LPR, CPL, NB>(a, act_lds, NCH, (threadIdx.x & 63) % LPR);
-        run.run(a);
+        const float tot = row_sum<32>(pv);  // 32 consecutive entries = one group
+        if ((threadIdx.x & 31) == 0) rstd[threadIdx.x / 32] = 1.0f / sqrtf(tot / (float)GNORM + eps);
     }
+    __syncthreads();
+    if (!early) {
+        run.issue_first();
+#pragma unroll
+        for (int k = 0; k < GC; ++k) {
+            const int c = (int)threadIdx.x + PW * k;
+            if (c < NCH) {
+                const float r = rstd[(32 * c) / GNORM];
+                float v[32];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    v[4 * j] = round_bf16(gv0[k][j].x * r);
+                    v[4 * j + 1] = round_bf16(gv0[k][j].y * r);
+                    v[4 * j + 2] = round_bf16(gv0[k][j].z * r);
+                    v[4 * j + 3] = round_bf16(gv0[k][j].w * r);
+                }
+                make_chunk(v, act_lds + (size_t)c * ACT_WORDS);
+            }
+        }
+    }
+    __syncthreads();
+    ActChunk a[NB][CPL];
+    act_from_lds<LPR, CPL, NB>(a, act_lds, NCH, (threadIdx.x & 63) % LPR);
+    run.run(a);
 }
 
 // ----------------------------------------------------------------- attention q / k / v
@@ -1894,7 +1805,7 @@ hipError_t launch_outproj_step(const W4 &W, const float *gate, const float *part
         // one work-group of 8 waves per CU
         const size_t lds = (size_t)(DINNER / 32) * ACT_WORDS * 4;
         const int grid = min(cu_count(), (W.n + 7) / 8);
-        launch_k(k_outproj_step<1>, dim3(grid), dim3(512), lds, st, W, gate, part, eps, e);
+        launch_k(k_outproj_step, dim3(grid), dim3(512), lds, st, W, gate, part, eps, e);
         return hipGetLastError();
     }
     // batch 2..4: split over the gated-norm groups, then the ordered sum

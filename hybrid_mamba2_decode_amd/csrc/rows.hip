@@ -46,7 +46,8 @@ __device__ __forceinline__ float block_sum256(float v, float *red)
 }
 
 // Store eight values that are already bf16-exact, as bf16 bits (kind 0) or as fp16 bits
-// (kind 1, the matrix-core operand format), plus their group sum.
+// (kind 1, the W4 matrix product's operand format: the eight values in pair order
+// (0,4) (1,5) (2,6) (3,7), the order in which that product dequantises a packed weight word).
 __device__ __forceinline__ void store8(uint16_t *dst, const float *v, int kind)
 {
     uint4 o;
@@ -56,10 +57,10 @@ __device__ __forceinline__ void store8(uint16_t *dst, const float *v, int kind)
         o.z = (uint32_t)f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16);
         o.w = (uint32_t)f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16);
     } else {
-        o.x = pack_f16x2(v[0], v[1]);
-        o.y = pack_f16x2(v[2], v[3]);
-        o.z = pack_f16x2(v[4], v[5]);
-        o.w = pack_f16x2(v[6], v[7]);
+        o.x = pack_f16x2(v[0], v[4]);
+        o.y = pack_f16x2(v[1], v[5]);
+        o.z = pack_f16x2(v[2], v[6]);
+        o.w = pack_f16x2(v[3], v[7]);
     }
     *reinterpret_cast<uint4 *>(dst) = o;
 }
@@ -425,6 +426,8 @@ hipError_t launch_conv_seq(const uint16_t *xbc, long ld, int T, const uint16_t *
 }
 
 // ------------------------------------------------------- bf16 -> fp16 bits
+// The W4 matrix product's operand format: fp16 bits, each 8-value chunk in pair order
+// (0,4) (1,5) (2,6) (3,7); plus the sum of each row's 64-value groups, [group][row].
 __global__ __launch_bounds__(256) void k_to_f16(const uint16_t *__restrict__ x,
                                                 uint16_t *__restrict__ xh, float *__restrict__ su,
                                                 size_t nvec, int kvec)
@@ -434,10 +437,10 @@ __global__ __launch_bounds__(256) void k_to_f16(const uint16_t *__restrict__ x,
     if (v < nvec) {
         const uint4 w = *reinterpret_cast<const uint4 *>(x + 8 * v);
         uint4 o;
-        o.x = bf16x2_to_f16x2(w.x);
-        o.y = bf16x2_to_f16x2(w.y);
-        o.z = bf16x2_to_f16x2(w.z);
-        o.w = bf16x2_to_f16x2(w.w);
+        o.x = pack_f16x2(bf16lo(w.x), bf16lo(w.z));
+        o.y = pack_f16x2(bf16hi(w.x), bf16hi(w.z));
+        o.z = pack_f16x2(bf16lo(w.y), bf16lo(w.w));
+        o.w = pack_f16x2(bf16hi(w.y), bf16hi(w.w));
         *reinterpret_cast<uint4 *>(xh + 8 * v) = o;
         s = sum_bf16x8(w);
     }
