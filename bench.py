@@ -265,7 +265,7 @@ def main():
             for x in e:
                 hip.destroy(x)
         kb = step_kernel_bytes(B)
-        names = ["k_inproj_step<1, 0>", "k_ssm_step<true, 1>", "k_outproj_step<1>"]  # batch 1, bf16 input
+        names = ["k_inproj_step<1, 0>", "k_ssm_step<true, 1>", "k_outproj_step"]  # batch 1, bf16 input
         kernels = [{"kernel": names[j], "avg_us": round(float(k_avg[j]), 3), "median_us": round(float(k_med[j]), 3),
                     "algorithmic_bytes": int(kb[j]), "GBps": round(kb[j] / (k_avg[j] * 1e-6) / 1e9, 1),
                     "hbm_frac": round(kb[j] / (k_avg[j] * 1e-6) / HBM_PEAK, 4)} for j in range(3)]
@@ -668,7 +668,7 @@ def main():
             "workload": "W4 GEMM Y = X W^T of the full-history block, M = 7500 rows (batch 2 x T 3750): "
                         "in_proj 4480->22656 and out_proj 10240->4480, bf16 output, 27 layers' weights",
             **gemm_out,
-            "counters": counters_from_profile("k_w4_gemm", "gemm.hip", "nh_device.hpp"),
+            "counters": counters_from_profile("k_w4_gemm_wide", "gemm.hip", "nh_device.hpp"),
         }
         log("gemm:", out["gemm"])
         del Xi, Xo, Yi, Yo, gws

@@ -11,18 +11,22 @@
 // Activations arrive as fp16 bits (bf16-exact values), so every product is exact and the
 // accumulation is fp32 inside v_mfma_f32_32x32x16_f16.
 //
-// Tiling: a 256 x 128 output tile per work-group of 8 waves with split roles, one quantisation
-// group (K = 64) per step, through a ring of four LDS slots.  Waves 4-7 load: X reaches its slot
-// by DMA (buffer loads that write LDS directly, issued three steps ahead of use, so X spends no
-// registers or instructions of theirs), and the packed W of the group, its scale, the offset
-// term and the rows' group sums go through registers four steps ahead and are written to the
-// slot as they are stored (W stays packed).  Waves 0-3 compute: each owns a 128 x 64 block of
-// the tile (4 x 2 MFMA 32x32 tiles), reads its operands from LDS, dequantises its W columns in
-// registers, between its MFMAs, and issues the MFMAs.  With W packed in LDS a step moves 100 KB
-// through LDS instead of 144 KB (fp16 W written once and read by two waves each).  One barrier
-// per step: at step k the compute waves read slot k mod 4 and the packed W and scales of slot
-// (k + 1) mod 4 (dequantising that step's first k-step under their last MFMAs), the DMA fills
-// slot (k + 3) mod 4 and the loaders store the register part of slot (k + 2) mod 4.
+// Two kernels.  With an even number of quantisation groups (K a multiple of 128, as in_proj and
+// out_proj) and enough rows to fill the chip, k_w4_gemm_wide: 256 x 256 tiles, all 8 waves
+// compute, every operand reaches LDS by DMA (described with the kernel).  Otherwise
+// k_w4_gemm: a 256 x 128 output tile per
+// work-group of 8 waves with split roles, one quantisation group (K = 64) per step, through a
+// ring of four LDS slots.  Waves 4-7 load: X (and, from loader wave 0, the rows' group sums)
+// reaches its slot by DMA (buffer loads that write LDS directly, issued three steps ahead of use,
+// so X spends no registers or instructions of theirs), and the packed W of the group, its scale
+// and offset go through registers four steps ahead and are written to the slot as they are
+// stored (W stays packed).  Waves 0-3 compute: each owns a 128 x 64 block of the tile (4 x 2
+// MFMA 32x32 tiles), reads its operands from LDS, dequantises its W columns in registers,
+// between its MFMAs, and issues the MFMAs.  With W packed in LDS a step moves 100 KB through LDS
+// instead of 144 KB (fp16 W written once and read by two waves each).  One barrier per step: at
+// step k the compute waves read slot k mod 4 and the packed W and scales of slot (k + 1) mod 4
+// (dequantising that step's first k-step under their last MFMAs), the DMA fills slot
+// (k + 3) mod 4 and the loaders store the register part of slot (k + 2) mod 4.
 //
 // X comes in the operand format of the producing kernels: fp16 bits, each 8-value chunk in pair
 // order (0,4) (1,5) (2,6) (3,7), the order in which a packed word dequantises.  K order inside
@@ -57,6 +61,43 @@ struct GemmEpi {
     int y_t, res_t;
 };
 
+// Epilogue of one 32x32 MFMA tile: rows mb + 8 (r / 4) + 4 kh + (r mod 4) of column n (the
+// lane's), plus the residual, stored in the output type.  The residual loads of the tile go out
+// together (addresses clamped into the matrix, values past the end unused), then one wait.
+__device__ __forceinline__ void gemm_store_block(const floatx16 &acc, int mb, int n, int kh, int M, int N,
+                                                 const GemmEpi &ep)
+{
+    const int nc = min(n, N - 1);
+    float v[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) v[r] = acc[r];
+    auto at = [&](int r) { return (size_t)min(mb + 8 * (r >> 2) + 4 * kh + (r & 3), M - 1) * N + nc; };
+    if (ep.res && ep.res_t == BF16) {
+        uint16_t rv[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) rv[r] = reinterpret_cast<const uint16_t *>(ep.res)[at(r)];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[r] += bf16_to_f32(rv[r]);
+    } else if (ep.res) {
+        float rv[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) rv[r] = reinterpret_cast<const float *>(ep.res)[at(r)];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[r] += rv[r];
+    }
+    if (n >= N) return;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int m = mb + 8 * (r >> 2) + 4 * kh + (r & 3);
+        if (m >= M) continue;
+        const size_t o = (size_t)m * N + n;
+        if (ep.y_t == BF16)
+            reinterpret_cast<uint16_t *>(ep.y)[o] = f32_to_bf16(v[r]);
+        else
+            reinterpret_cast<float *>(ep.y)[o] = v[r];
+    }
+}
+
 constexpr int WS_BM = 256, WS_BN = 128, WS_SLOTS = 4, WS_THREADS = 512;
 
 // The register-loaded part of an LDS slot (one quantisation group of the tile).
@@ -72,25 +113,16 @@ struct WsSlotW {
 __device__ __forceinline__ int ws_sw(int row, int c) { return row * 8 + (c ^ (row & 7) ^ ((row >> 3) & 1)); }
 
 // A loader lane's register loads for one step: 16 bytes of packed W (column lane / 2, half
-// lane mod 2) and the groups' scales or offsets: with an even group count, one 4-byte load
-// per lane every other step carries two groups of one column's scales (loader waves 0 and 1)
-// or offsets (waves 2 and 3); otherwise each step loads its group's scale and offset of
-// column lane / 2 (2 bytes each).
+// lane mod 2) and the group's scale and offset of that column (2 bytes each).
 struct WsRegs {
     uint4 w;
-    uint32_t p;
     uint16_t s, b;
 };
 
-// Vector-memory loads a loader wave issues in the step that is j mod 4 of the unrolled loop:
-// the DMA of X (8), of the row sums (loader wave 0), packed W (1), scales and offsets.
-__host__ __device__ constexpr int ws_nonx(bool pairs, int j) { return 1 + (pairs ? ((j & 1) == 0) : 2); }
-__host__ __device__ constexpr int ws_total(bool pairs, bool su, int j) { return 8 + (su ? 1 : 0) + ws_nonx(pairs, j); }
-// loads that follow, by the end of the step, the X DMA issued two steps earlier
-__host__ __device__ constexpr int ws_after(bool pairs, bool su, int j)
-{
-    return ws_nonx(pairs, j) + ws_total(pairs, su, j + 1) + ws_total(pairs, su, j);
-}
+// Vector-memory loads a loader wave issues per step: the DMA of X (8) and of the row sums
+// (loader wave 0), packed W, scale and offset (3); by the end of a step, the X DMA issued two
+// steps earlier is followed by 3 + 2 (11 + su) loads.
+__host__ __device__ constexpr int ws_after(bool su) { return 3 + 2 * (11 + (su ? 1 : 0)); }
 
 typedef __attribute__((address_space(3))) void ws_lds_void;
 
@@ -116,7 +148,6 @@ __device__ __forceinline__ void ws_barrier()
 
 // Work-group i runs on XCD i mod 8; each XCD takes a contiguous range of tiles in row-major
 // tile order, so the work-groups resident on one XCD share the X rows of their tiles in its L2.
-template <bool PAIRS>
 __global__ __launch_bounds__(WS_THREADS, 1) void k_w4_gemm(W4 W, const uint16_t *__restrict__ Xh,
                                                            const float *__restrict__ su, int M, GemmEpi ep)
 {
@@ -153,10 +184,6 @@ __global__ __launch_bounds__(WS_THREADS, 1) void k_w4_gemm(W4 W, const uint16_t 
         const __amdgpu_buffer_rsrc_t rs = rsrc(W.s + (size_t)n0 * kg, nrows * (uint32_t)kg * 2);
         const __amdgpu_buffer_rsrc_t rb = rsrc(W.b + (size_t)n0 * kg, nrows * (uint32_t)kg * 2);
         const uint32_t vw = ((uint32_t)n * kw + 4 * h) * 4, vs = (uint32_t)n * kg * 2;
-        // scale / offset pairs (even group count): column 64 (lw mod 2) + lane
-        const int pc = 64 * (lw & 1) + lane;
-        const __amdgpu_buffer_rsrc_t rsb = lw < 2 ? rs : rb;
-        const uint32_t vp = (uint32_t)pc * kg * 2;
         // X DMA: load i (0..7) of loader wave lw fills slot positions 64 q + lane, q = 8 lw + i,
         // i.e. row r = 8 q + lane / 8 at stored chunk position lane mod 8, which holds chunk
         // (lane mod 8) ^ (lane / 8) ^ (q mod 2) of the row (the swizzle, with r mod 8 = lane / 8
@@ -183,38 +210,20 @@ __global__ __launch_bounds__(WS_THREADS, 1) void k_w4_gemm(W4 W, const uint16_t 
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (ws_lds_void *)&xs[64 * (8 * lw + i)], 16,
                                                              ((i & 1) ? vx1 : vx0) + (uint32_t)(8 * i * K * 2) + go, 0, 0, 0);
             };
-            // even: the step is even (with PAIRS its load carries this step's and the next one's
-            // scales or offsets)
-            auto issue = [&](WsRegs &R, int st, bool even) {
+            auto issue = [&](WsRegs &R, int st) {
                 const int g = min(st, kg - 1);
                 R.w = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, vw + (uint32_t)(32 * g), 0, 0));
-                if (PAIRS) {
-                    if (even) R.p = __builtin_amdgcn_raw_buffer_load_b32(rsb, vp + (uint32_t)(2 * min(st, kg - 2)), 0, 0);
-                } else {
-                    R.s = __builtin_amdgcn_raw_buffer_load_b16(rs, vs + (uint32_t)(2 * g), 0, 0);
-                    R.b = __builtin_amdgcn_raw_buffer_load_b16(rb, vs + (uint32_t)(2 * g), 0, 0);
-                }
+                R.s = __builtin_amdgcn_raw_buffer_load_b16(rs, vs + (uint32_t)(2 * g), 0, 0);
+                R.b = __builtin_amdgcn_raw_buffer_load_b16(rb, vs + (uint32_t)(2 * g), 0, 0);
             };
             auto half_pair = [](uint16_t v) {
                 const float sc = bf16_to_f32(v);
                 const half2v s2 = {(_Float16)sc, (_Float16)sc};
                 return __builtin_bit_cast(uint32_t, s2);
             };
-            // sl: the step's slot; sn: the next step's (PAIRS, even steps only)
-            auto store = [&](const WsRegs &R, WsSlotW &sl, WsSlotW &sn, bool even) {
+            auto store = [&](const WsRegs &R, WsSlotW &sl) {
                 sl.wq[h * WS_BN + n] = R.w;
-                if (PAIRS) {
-                    if (even) {
-                        const uint16_t lo = (uint16_t)(R.p & 0xffffu), hi = (uint16_t)(R.p >> 16);
-                        if (lw < 2) {
-                            sl.s2[pc] = half_pair(lo);
-                            sn.s2[pc] = half_pair(hi);
-                        } else {
-                            sl.bv[pc] = bf16_to_f32(lo);
-                            sn.bv[pc] = bf16_to_f32(hi);
-                        }
-                    }
-                } else if (h == 0) {
+                if (h == 0) {
                     sl.s2[n] = half_pair(R.s);
                     sl.bv[n] = bf16_to_f32(R.b);
                 }
@@ -227,25 +236,22 @@ __global__ __launch_bounds__(WS_THREADS, 1) void k_w4_gemm(W4 W, const uint16_t 
             dma(1, ws_x[1], ws_su[1]);
             dma(2, ws_x[2], ws_su[2]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) issue(rr[j], j, (j & 1) == 0);
-            store(rr[0], ws_w[0], ws_w[1], true);
-            issue(rr[0], 4, true);
-            store(rr[1], ws_w[1], ws_w[2], false);
-            issue(rr[1], 5, false);
-            ws_wait_vm<ws_after(PAIRS, SU, 1)>();  // the DMA of step 0 (more loads follow it)
+            for (int j = 0; j < 4; ++j) issue(rr[j], j);
+            store(rr[0], ws_w[0]);
+            issue(rr[0], 4);
+            store(rr[1], ws_w[1]);
+            issue(rr[1], 5);
+            ws_wait_vm<ws_after(SU)>();  // the DMA of step 0 (more loads follow it)
             auto block = [&](int k) {  // steps k .. k + 3
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     ws_barrier();  // step k + j: its slot is complete
                     dma(k + j + 3, ws_x[(j + 3) & 3], ws_su[(j + 3) & 3]);
                     asm volatile("" ::: "memory");  // the DMA goes out before this step's other loads
-                    store(rr[(j + 2) & 3], ws_w[(j + 2) & 3], ws_w[(j + 3) & 3], (j & 1) == 0);
-                    issue(rr[(j + 2) & 3], k + j + 6, (j & 1) == 0);
+                    store(rr[(j + 2) & 3], ws_w[(j + 2) & 3]);
+                    issue(rr[(j + 2) & 3], k + j + 6);
                     // the DMA of step k + j + 1 (in the first two steps more loads follow it)
-                    if ((j & 1) == 0)  // j is a constant once unrolled
-                        ws_wait_vm<ws_after(PAIRS, SU, 0)>();
-                    else
-                        ws_wait_vm<ws_after(PAIRS, SU, 1)>();
+                    ws_wait_vm<ws_after(SU)>();
                 }
             };
             // the first block outside the loop, so that the loop is entered with the loads in
@@ -360,37 +366,229 @@ __global__ __launch_bounds__(WS_THREADS, 1) void k_w4_gemm(W4 W, const uint16_t 
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int n = n0 + 64 * wn + 32 * j + l32;
-            if (n >= W.n) continue;
+        for (int j = 0; j < 2; ++j)
+            gemm_store_block(acc[i][j], m0 + 128 * wm + 32 * i, n0 + 64 * wn + 32 * j + l32, kh, M, W.n, ep);
+}
+
+// ------------------------------------------------------------------ wide tiles
+// With an even number of quantisation groups: 256 x 256 output tiles, all 8 waves compute
+// (wave w owns rows 128 (w / 4) .. + 127 and columns 64 (w mod 4) .. + 63, 4 x 2 MFMA 32x32
+// tiles) and every operand reaches LDS by DMA, so no wave spends registers or instructions on
+// staging.  The X tile of a step (32 KB) is the same as for a 256 x 128 tile and now feeds
+// twice the matrix-core work; with 256 x 128 tiles the X fetch (about 22 B per clock per CU)
+// set the pace.  Per step each wave issues 6 loads into the slot of the step two ahead:
+//   X: 4 x 1 KB (rows 32 w .. 32 w + 31, swizzled as in the split-role kernel);
+//   W: 1 KB of packed nibbles (half w / 4, columns 64 (w mod 4) + lane);
+//   the scales (waves 0-3) or offsets (waves 4-7) of 64 columns, 4 bytes per column holding
+//   the group pair (g & ~1, g | 1) (aligned because the group count is even);
+// and wave 0 the rows' group sums (1 KB).  Three slots, one barrier per step: at step k the
+// waves read slot k mod 3 and fill slot (k + 2) mod 3, which everyone left at step k - 1.
+constexpr int WG_BM = 256, WG_BN = 256, WG_THREADS = 512;
+
+struct WgSlot {
+    uint4 x[WG_BM * 8];   // fp16 X tile, [row][chunk] swizzled (ws_sw), pair order inside a chunk
+    uint4 wq[2 * WG_BN];  // packed W, [half][column]
+    uint32_t sp[WG_BN];   // bf16 scale pair (group g & ~1 low, g | 1 high) per column
+    uint32_t bp[WG_BN];   // bf16 offset pair, the same groups
+    float su[WG_BM];      // group sum of each X row
+};
+
+__global__ __launch_bounds__(WG_THREADS, 1) void k_w4_gemm_wide(W4 W, const uint16_t *__restrict__ Xh,
+                                                                const float *__restrict__ su, int M, GemmEpi ep)
+{
+    // three separate objects, so that the compiler can tell the slot being read from the ones
+    // the DMA is filling and does not wait for the DMA before the reads
+    __shared__ WgSlot sa, sb, sc;
+
+    const int K = W.k, kw = K >> 3, kg = K >> 6;
+    const int ntiles = (W.n + WG_BN - 1) / WG_BN, mtiles = (M + WG_BM - 1) / WG_BM;
+    const int tiles = ntiles * mtiles, per = (tiles + 7) / 8;
+    const int tile = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    if (tile >= tiles) return;
+    const int m0 = (tile / ntiles) * WG_BM, n0 = (tile % ntiles) * WG_BN;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nsteps = kg;
+
+    // ---- DMA sources (buffer resources cover only the tile's rows: rows past the end read 0)
+    auto rsrc = [](const void *p, uint32_t bytes) {
+        return __builtin_amdgcn_make_buffer_rsrc((void *)p, 0, (int)bytes, 0x00020000);
+    };
+    const uint32_t mrows = (uint32_t)min(M - m0, WG_BM), nrows = (uint32_t)min(W.n - n0, WG_BN);
+    const __amdgpu_buffer_rsrc_t rx = rsrc(Xh + (size_t)m0 * K, mrows * (uint32_t)K * 2);
+    const __amdgpu_buffer_rsrc_t rw = rsrc(W.q + (size_t)n0 * kw, nrows * (uint32_t)kw * 4);
+    const __amdgpu_buffer_rsrc_t rsb = wave < 4 ? rsrc(W.s + (size_t)n0 * kg, nrows * (uint32_t)kg * 2)
+                                                : rsrc(W.b + (size_t)n0 * kg, nrows * (uint32_t)kg * 2);
+    const size_t su_n = (size_t)M * kg;
+    // X: load i (0..3) fills slot positions 64 q + lane, q = 4 w + i: row 8 q + lane / 8 at
+    // stored chunk position lane mod 8, i.e. chunk (lane mod 8) ^ (lane / 8) ^ (q mod 2)
+    const int r0 = 32 * wave + (lane >> 3), c0 = (lane & 7) ^ (lane >> 3);
+    const uint32_t vx0 = (uint32_t)r0 * K * 2 + 16 * c0, vx1 = (uint32_t)r0 * K * 2 + 16 * (c0 ^ 1);
+    // W: position 64 w + lane = half h, column n
+    const int wp = 64 * wave + lane, wh = wp >> 8, wcol = wp & 255;
+    const uint32_t vw = (uint32_t)wcol * kw * 4 + 16 * wh;
+    const int sbcol = 64 * (wave & 3) + lane;
+    const uint32_t vsb = (uint32_t)sbcol * kg * 2;
+    // the loads of step st into slot sl, in three parts (issued between the k-steps of the
+    // current step, so that a wave waiting for room in the memory queue still has MFMAs in flight)
+    auto dma = [&](int part, int st, WgSlot &sl) __attribute__((always_inline)) {
+        const int g = min(st, kg - 1);
+        const uint32_t go = 128u * (uint32_t)g;
+        if (part == 0) {
+            if (wave == 0) {
+                // rows past the tile read the next rows of su (or zero past its end): unused
+                const size_t o = (size_t)g * M + m0;
+                const __amdgpu_buffer_rsrc_t ru = rsrc(su + o, (uint32_t)((su_n - o) * 4));
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ru, (ws_lds_void *)sl.su, 16, (uint32_t)lane * 16, 0, 0, 0);
+            }
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (ws_lds_void *)&sl.wq[64 * wave], 16, vw + 32u * (uint32_t)g, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (ws_lds_void *)&sl.sp[64 * wave], 4,
+                                                     vsb + 2u * (uint32_t)(g & ~1), 0, 0, 0);
+        } else {
+            const int i0 = 2 * (part - 1);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int m = m0 + 128 * wm + 32 * i + 8 * (r >> 2) + 4 * kh + (r & 3);
-                if (m >= M) continue;
-                const size_t o = (size_t)m * W.n + n;
-                float v = acc[i][j][r];
-                if (ep.res)
-                    v += ep.res_t == BF16 ? bf16_to_f32(reinterpret_cast<const uint16_t *>(ep.res)[o])
-                                          : reinterpret_cast<const float *>(ep.res)[o];
-                if (ep.y_t == BF16)
-                    reinterpret_cast<uint16_t *>(ep.y)[o] = f32_to_bf16(v);
-                else
-                    reinterpret_cast<float *>(ep.y)[o] = v;
+            for (int i = i0; i < i0 + 2; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (ws_lds_void *)&sl.x[64 * (4 * wave + i)], 16,
+                                                         ((i & 1) ? vx1 : vx0) + (uint32_t)(8 * i * K * 2) + go, 0, 0, 0);
+        }
+    };
+
+    // ---- compute
+    const int l32 = lane & 31, kh = lane >> 5;
+    const int wm = wave >> 2, wn = wave & 3;  // rows 128 wm .., columns 64 wn ..
+    floatx16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    auto step = [&](int k, const WgSlot &sl, WgSlot &fill) __attribute__((always_inline)) {
+        uint4 wr[2];
+        half2v s2[2];
+        float bq[2];
+        const int hi = k & 1;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int c = 64 * wn + 32 * j + l32;
+            wr[j] = sl.wq[kh * WG_BN + c];
+            const uint32_t spv = sl.sp[c], bpv = sl.bp[c];
+            const float sv = bf16_to_f32((uint16_t)(hi ? spv >> 16 : spv & 0xffffu));
+            const float bv = bf16_to_f32((uint16_t)(hi ? bpv >> 16 : bpv & 0xffffu));
+            s2[j] = half2v{(_Float16)sv, (_Float16)sv};
+            bq[j] = fmaf(8.f, sv, bv);  // beta + 8 s
+        }
+        half8 af[2][4], bf[2][2];
+        auto rd = [&](int ks, half8 (&a)[4], half8 (&b)[2]) {
+            const int c = 4 * kh + ks;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = __builtin_bit_cast(half8, sl.x[ws_sw(128 * wm + 32 * i + l32, c)]);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const uint32_t w = ks == 0 ? wr[j].x : ks == 1 ? wr[j].y : ks == 2 ? wr[j].z : wr[j].w;
+                b[j] = dequant_word(w, s2[j]);
+            }
+        };
+        rd(0, af[0], bf[0]);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            if (ks + 1 < 4) rd(ks + 1, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ks & 1][i], bf[ks & 1][j], acc[i][j], 0, 0, 0);
+            if (ks + 1 < 4) {
+                // the next k-step's LDS reads first, then its dequantisation spread between the
+                // MFMAs: one MFMA, four VALU instructions, eight times
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (ks < 3) {
+                asm volatile("" ::: "memory");
+                dma(ks, k + 2, fill);  // part ks of the loads of step k + 2
+                asm volatile("" ::: "memory");
             }
         }
+        // asymmetric groups: add (beta + 8 s) * (group sum of the X row) as a rank-1 fp32
+        // matrix-core update (K = 2 with the second k zero)
+        if (__builtin_amdgcn_ballot_w64(bq[0] != 0.f || bq[1] != 0.f) != 0ull) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float a = kh ? 0.f : sl.su[128 * wm + 32 * i + l32];
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, kh ? 0.f : bq[j], acc[i][j], 0, 0, 0);
+            }
+        }
+    };
+
+    // step k: DMA at step k - 2 (wave 0 issues 7 loads a step, the others 6; each wave waits
+    // for its own loads of the next step, which 6 or 7 loads follow, before the barrier)
+    for (int p = 0; p < 3; ++p) dma(p, 0, sa);
+    for (int p = 0; p < 3; ++p) dma(p, 1, sb);
+    ws_wait_vm<6>();
+    auto one = [&](int k, const WgSlot &cur, WgSlot &fill) __attribute__((always_inline)) {
+        ws_barrier();  // step k: its slot is complete, the slot of step k - 1 is free
+        step(k, cur, fill);  // and the loads of step k + 2 into the slot of step k - 1
+        ws_wait_vm<6>();     // this wave's loads of step k + 1
+    };
+    // every step computes: the loop leaves after the last one (the loads of the two steps past
+    // the end re-read the last group into slots nobody reads)
+    for (int k = 0;; k += 3) {
+        one(k, sa, sc);
+        if (k + 1 >= nsteps) break;
+        one(k + 1, sb, sa);
+        if (k + 2 >= nsteps) break;
+        one(k + 2, sc, sb);
+        if (k + 3 >= nsteps) break;
+    }
+    ws_wait_vm<0>();  // no DMA into LDS outlives the work-group
+
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            gemm_store_block(acc[i][j], m0 + 128 * wm + 32 * i, n0 + 64 * wn + 32 * j + l32, kh, M, W.n, ep);
+}
+
+static int gemm_cu_count()
+{
+    static int cus = 0;
+    if (!cus) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+    }
+    return cus;
 }
 
 hipError_t launch_w4_gemm(const W4 &W, const uint16_t *Xh, const float *su, int M,
                           const void *res, int res_t, void *Y, int y_t, hipStream_t st)
 {
     if (M <= 0) return hipSuccess;
-    const int tiles = ((M + WS_BM - 1) / WS_BM) * ((W.n + WS_BN - 1) / WS_BN);
     GemmEpi ep{Y, res, y_t, res_t};
-    const dim3 grid(8 * ((tiles + 7) / 8)), block(WS_THREADS);
-    if ((W.k >> 6) % 2 == 0)
-        k_w4_gemm<true><<<grid, block, 0, st>>>(W, Xh, su, M, ep);
-    else
-        k_w4_gemm<false><<<grid, block, 0, st>>>(W, Xh, su, M, ep);
+    const int tiles = ((M + WS_BM - 1) / WS_BM) * ((W.n + WS_BN - 1) / WS_BN);
+    if ((W.k >> 6) % 2 == 0) {
+        // A wide tile takes about 1.88 times as long as a split-role tile (measured at the
+        // in_proj and out_proj shapes), so the wide kernel is taken when its rounds of one
+        // work-group per CU, times 1.88, are fewer than the split kernel's: e.g. in_proj at
+        // 7500 rows (11 rounds against 21), but not out_proj (3 against 5).
+        const int wtiles = ((M + WG_BM - 1) / WG_BM) * ((W.n + WG_BN - 1) / WG_BN);
+        const int cus = gemm_cu_count(), rw = (wtiles + cus - 1) / cus, rs = (tiles + cus - 1) / cus;
+        if (47 * rw < 25 * rs) {
+            k_w4_gemm_wide<<<dim3(8 * ((wtiles + 7) / 8)), dim3(WG_THREADS), 0, st>>>(W, Xh, su, M, ep);
+            return hipGetLastError();
+        }
+    }
+    k_w4_gemm<<<dim3(8 * ((tiles + 7) / 8)), dim3(WS_THREADS), 0, st>>>(W, Xh, su, M, ep);
     return hipGetLastError();
 }
 

@@ -35,10 +35,17 @@ def _say(*a):
     print("[case]", *a, flush=True)
 
 
-def _asym(W, seed):
-    """Same matrix with arbitrary (non-symmetric) bf16 biases."""
+def _asym(W, seed, exact_offset=False):
+    """Same matrix with arbitrary (non-symmetric) bf16 biases.  exact_offset: biases that are
+    tiny next to 8 s, so that beta + 8 s is not an fp32 number, are set to 0 (still not
+    symmetric): the matrix product adds the offset term (beta + 8 s) * sum x in fp32, so only
+    then is its result the single rounding of the exact value."""
     rng = np.random.default_rng(seed)
     b = synth.f32_to_bf16(rng.uniform(-0.05, 0.05, W.biases.shape).astype(np.float32))
+    if exact_offset:
+        s64 = synth.bf16_to_f32(W.scales).astype(np.float64)
+        b64 = synth.bf16_to_f32(b).astype(np.float64)
+        b = np.where(np.float32(8 * s64 + b64).astype(np.float64) == 8 * s64 + b64, b, np.uint16(0)).astype(np.uint16)
     return synth.W4Matrix(W.qweight, W.scales, b, W.n_out, W.k_in, W.group_size)
 
 
@@ -172,14 +179,17 @@ def test_gemv_residual_bf16_out(env):
 
 # ------------------------------------------------------------------------ GEMM
 
+# 200 columns run the split-role kernel, 17000 the wide-tile one (on 256 compute units: 266
+# split tiles, two rounds, against 134 wide tiles, one round)
+@pytest.mark.parametrize("N", [200, 17000])
 @pytest.mark.parametrize("asym", [False, True])
-def test_gemm_identity_probe_is_bit_exact(env, asym):
+def test_gemm_identity_probe_is_bit_exact(env, asym, N):
     nh, oracle, gu, torch = env
-    _say("gemm identity", asym)
-    K, N = 512, 200
+    _say("gemm identity", asym, N)
+    K = 512
     W = synth.w4_random(13, 0, 1, 2, N, K)
     if asym:
-        W = _asym(W, 6)
+        W = _asym(W, 6, exact_offset=True)
     X = np.zeros((K, K), dtype=np.uint16)
     X[np.arange(K), np.arange(K)] = 0x3F80
     Y = gu.empty_f32(K, N)
@@ -190,9 +200,17 @@ def test_gemm_identity_probe_is_bit_exact(env, asym):
 
 @pytest.mark.parametrize("M,n,k,asym", [(1, 300, 4480, False), (16, 300, 4480, True), (130, 260, 4480, False),
                                         (413, 4480, 10240, True), (257, 64, 128, False),
-                                        # one, three and five groups of 64 (fewer groups than the
-                                        # loaders' three-step lead), several tiles in both directions
-                                        (37, 129, 64, True), (300, 520, 192, False), (600, 1000, 320, True)])
+                                        # odd group counts (the split-role kernel): one, three and
+                                        # five groups of 64, fewer than the loaders' three-step lead,
+                                        # several tiles in both directions
+                                        (37, 129, 64, True), (300, 520, 192, False), (600, 1000, 320, True),
+                                        # even group counts, few tiles (the split-role kernel): two,
+                                        # four, six and sixteen groups, ragged rows and columns
+                                        (37, 129, 128, True), (300, 520, 256, False), (600, 1000, 384, True),
+                                        (513, 600, 1024, True),
+                                        # even group counts, many columns (the wide-tile kernel on 256
+                                        # compute units): ragged rows and columns, four and two groups
+                                        (300, 17000, 256, True), (520, 16500, 128, False)])
 def test_gemm_matches_oracle(env, M, n, k, asym):
     nh, oracle, gu, torch = env
     _say("gemm", M, n, k, asym)
