@@ -2,9 +2,9 @@
 //
 // Dequantisation is exact: with bf16 scales s, the value s*(q-8) has at most 11 significant
 // bits (|q-8| <= 8 and s carries 8 bits), so it is an fp16 number.  The B operand is built as
-// fp16 s*(q-8) straight from the packed word: (word & 0x000F000F) | 0x64006400 gives the fp16
-// pair (1024+q_e, 1024+q_{e+4}) (1024's unit in the last place is 1), a packed subtract of 1032
-// and a packed multiply by s finish it.  The rest of the affine map,
+// fp16 s*(q-8) straight from the packed word: the fp16 pair (1024+q_e, 1024+q_{e+4}) is the
+// nibbles under a 0x64 exponent byte (1024's unit in the last place is 1), a packed subtract of
+// 1032 and a packed multiply by s finish it.  The rest of the affine map,
 //     W = s*(q-8) + (beta + 8 s),
 // is zero for symmetric groups (beta = -8 s); otherwise its contribution
 // (beta + 8s) * sum_{k in group} X[m][k] is added in fp32 from precomputed group sums.
@@ -39,15 +39,21 @@
 
 namespace nh {
 
-// One packed word of 8 nibbles -> 8 fp16 values s*(q-8) in pair order.
+// One packed word of 8 nibbles -> 8 fp16 values s*(q-8) in pair order.  The low and high
+// nibbles of each byte are split into bytes (lo: nibbles 0 2 4 6, hi: 1 3 5 7), and one byte
+// permute per pair places two of them under a 0x64 exponent byte: the fp16 pair
+// (1024 + q_e, 1024 + q_{e+4}) in 7 ALU instructions per word instead of 11.
 __device__ __forceinline__ half8 dequant_word(uint32_t w, half2v s2)
 {
     const half2v off = {(_Float16)1032.0f, (_Float16)1032.0f};
+    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu, ex = 0x64646464u;
+    // v_perm_b32: selector bytes 0-3 pick the second operand's bytes, 4-7 the first's
+    const uint32_t m[4] = {__builtin_amdgcn_perm(ex, lo, 0x04020400u), __builtin_amdgcn_perm(ex, hi, 0x04020400u),
+                           __builtin_amdgcn_perm(ex, lo, 0x04030401u), __builtin_amdgcn_perm(ex, hi, 0x04030401u)};
     half8 r;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const uint32_t m = ((w >> (4 * e)) & 0x000F000Fu) | 0x64006400u;
-        half2v v = __builtin_bit_cast(half2v, m);
+        half2v v = __builtin_bit_cast(half2v, m[e]);
         v = (v - off) * s2;
         r[2 * e] = v[0];
         r[2 * e + 1] = v[1];
@@ -393,6 +399,7 @@ struct WgSlot {
     float su[WG_BM];      // group sum of each X row
 };
 
+template <int WI>
 __global__ __launch_bounds__(WG_THREADS, 1) void k_w4_gemm_wide(W4 W, const uint16_t *__restrict__ Xh,
                                                                 const float *__restrict__ su, int M, GemmEpi ep)
 {
@@ -455,23 +462,27 @@ __global__ __launch_bounds__(WG_THREADS, 1) void k_w4_gemm_wide(W4 W, const uint
 
     // ---- compute
     const int l32 = lane & 31, kh = lane >> 5;
-    const int wm = wave >> 2, wn = wave & 3;  // rows 128 wm .., columns 64 wn ..
-    floatx16 acc[4][2];
+    // wave w: WI x WJ MFMA tiles, rows 32 WI wm .., columns 32 WJ wn ..  WI = 4 (128 x 64 per
+    // wave); 64 x 128 (WI = 2) reads less of X from LDS but dequantises twice the W per wave,
+    // and measured 10% slower
+    constexpr int WJ = 8 / WI, NWN = 8 / (8 / WI);
+    const int wm = wave / NWN, wn = wave % NWN;
+    floatx16 acc[WI][WJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < WI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < WJ; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     auto step = [&](int k, const WgSlot &sl, WgSlot &fill) __attribute__((always_inline)) {
-        uint4 wr[2];
-        half2v s2[2];
-        float bq[2];
+        uint4 wr[WJ];
+        half2v s2[WJ];
+        float bq[WJ];
         const int hi = k & 1;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int c = 64 * wn + 32 * j + l32;
+        for (int j = 0; j < WJ; ++j) {
+            const int c = 32 * WJ * wn + 32 * j + l32;
             wr[j] = sl.wq[kh * WG_BN + c];
             const uint32_t spv = sl.sp[c], bpv = sl.bp[c];
             const float sv = bf16_to_f32((uint16_t)(hi ? spv >> 16 : spv & 0xffffu));
@@ -479,13 +490,13 @@ __global__ __launch_bounds__(WG_THREADS, 1) void k_w4_gemm_wide(W4 W, const uint
             s2[j] = half2v{(_Float16)sv, (_Float16)sv};
             bq[j] = fmaf(8.f, sv, bv);  // beta + 8 s
         }
-        half8 af[2][4], bf[2][2];
-        auto rd = [&](int ks, half8 (&a)[4], half8 (&b)[2]) {
+        half8 af[2][WI], bf[2][WJ];
+        auto rd = [&](int ks, half8 (&a)[WI], half8 (&b)[WJ]) {
             const int c = 4 * kh + ks;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = __builtin_bit_cast(half8, sl.x[ws_sw(128 * wm + 32 * i + l32, c)]);
+            for (int i = 0; i < WI; ++i) a[i] = __builtin_bit_cast(half8, sl.x[ws_sw(32 * WI * wm + 32 * i + l32, c)]);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
+            for (int j = 0; j < WJ; ++j) {
                 const uint32_t w = ks == 0 ? wr[j].x : ks == 1 ? wr[j].y : ks == 2 ? wr[j].z : wr[j].w;
                 b[j] = dequant_word(w, s2[j]);
             }
@@ -495,18 +506,18 @@ __global__ __launch_bounds__(WG_THREADS, 1) void k_w4_gemm_wide(W4 W, const uint
         for (int ks = 0; ks < 4; ++ks) {
             if (ks + 1 < 4) rd(ks + 1, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < WI; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+                for (int j = 0; j < WJ; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ks & 1][i], bf[ks & 1][j], acc[i][j], 0, 0, 0);
             if (ks + 1 < 4) {
                 // the next k-step's LDS reads first, then its dequantisation spread between the
-                // MFMAs: one MFMA, four VALU instructions, eight times
-                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+                // eight MFMAs
+                __builtin_amdgcn_sched_group_barrier(0x100, WI, 0);
 #pragma unroll
                 for (int t = 0; t < 8; ++t) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 2 * WJ, 0);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -518,12 +529,15 @@ __global__ __launch_bounds__(WG_THREADS, 1) void k_w4_gemm_wide(W4 W, const uint
         }
         // asymmetric groups: add (beta + 8 s) * (group sum of the X row) as a rank-1 fp32
         // matrix-core update (K = 2 with the second k zero)
-        if (__builtin_amdgcn_ballot_w64(bq[0] != 0.f || bq[1] != 0.f) != 0ull) {
+        bool asym = false;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float a = kh ? 0.f : sl.su[128 * wm + 32 * i + l32];
+        for (int j = 0; j < WJ; ++j) asym = asym || bq[j] != 0.f;
+        if (__builtin_amdgcn_ballot_w64(asym) != 0ull) {
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+            for (int i = 0; i < WI; ++i) {
+                const float a = kh ? 0.f : sl.su[32 * WI * wm + 32 * i + l32];
+#pragma unroll
+                for (int j = 0; j < WJ; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, kh ? 0.f : bq[j], acc[i][j], 0, 0, 0);
             }
         }
@@ -552,10 +566,10 @@ __global__ __launch_bounds__(WG_THREADS, 1) void k_w4_gemm_wide(W4 W, const uint
     ws_wait_vm<0>();  // no DMA into LDS outlives the work-group
 
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < WI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-            gemm_store_block(acc[i][j], m0 + 128 * wm + 32 * i, n0 + 64 * wn + 32 * j + l32, kh, M, W.n, ep);
+        for (int j = 0; j < WJ; ++j)
+            gemm_store_block(acc[i][j], m0 + 32 * WI * wm + 32 * i, n0 + 32 * WJ * wn + 32 * j + l32, kh, M, W.n, ep);
 }
 
 static int gemm_cu_count()
@@ -584,7 +598,7 @@ hipError_t launch_w4_gemm(const W4 &W, const uint16_t *Xh, const float *su, int 
         const int wtiles = ((M + WG_BM - 1) / WG_BM) * ((W.n + WG_BN - 1) / WG_BN);
         const int cus = gemm_cu_count(), rw = (wtiles + cus - 1) / cus, rs = (tiles + cus - 1) / cus;
         if (47 * rw < 25 * rs) {
-            k_w4_gemm_wide<<<dim3(8 * ((wtiles + 7) / 8)), dim3(WG_THREADS), 0, st>>>(W, Xh, su, M, ep);
+            k_w4_gemm_wide<4><<<dim3(8 * ((wtiles + 7) / 8)), dim3(WG_THREADS), 0, st>>>(W, Xh, su, M, ep);
             return hipGetLastError();
         }
     }
