@@ -207,7 +207,7 @@ __global__ __launch_bounds__(WS_THREADS, 1) void k_w4_gemm(W4 W, const uint16_t 
                 if constexpr (SU) {
                     // rows past the tile read the next rows of su (or zero past its end): unused
                     const size_t o = (size_t)g * M + m0;
-                    const __amdgpu_buffer_rsrc_t ru = rsrc(su + o, (uint32_t)((su_n - o) * 4));
+                    const __amdgpu_buffer_rsrc_t ru = rsrc(su + o, (uint32_t)min((su_n - o) * 4, (size_t)0xFFFFFFF0u));
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(ru, (ws_lds_void *)sus, 16, (uint32_t)lane * 16, 0, 0, 0);
                 }
                 const uint32_t go = 128u * (uint32_t)g;
@@ -445,7 +445,7 @@ __global__ __launch_bounds__(WG_THREADS, 1) void k_w4_gemm_wide(W4 W, const uint
             if (wave == 0) {
                 // rows past the tile read the next rows of su (or zero past its end): unused
                 const size_t o = (size_t)g * M + m0;
-                const __amdgpu_buffer_rsrc_t ru = rsrc(su + o, (uint32_t)((su_n - o) * 4));
+                const __amdgpu_buffer_rsrc_t ru = rsrc(su + o, (uint32_t)min((su_n - o) * 4, (size_t)0xFFFFFFF0u));
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(ru, (ws_lds_void *)sl.su, 16, (uint32_t)lane * 16, 0, 0, 0);
             }
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (ws_lds_void *)&sl.wq[64 * wave], 16, vw + 32u * (uint32_t)g, 0, 0, 0);

@@ -157,7 +157,10 @@ nh_status nh_w4_gemv(const nh_w4_matrix *W, const void *x, nh_dtype x_dtype, int
  * 4-bit, group 64).  X: bf16 [M][k_in] (|x| < 65504); residual: nullable
  * [M][n_out] of res_dtype; Y: [M][n_out] of y_dtype.  M >= 1.  Needs
  * nh_w4_gemm_workspace_bytes(M, k_in) bytes of workspace.  Matrix-core
- * arithmetic; W is dequantised exactly for 2^-17 <= |scale| <= 8188. */
+ * arithmetic; W is dequantised exactly for 2^-17 <= |scale| <= 8188, and
+ * the products are exact with fp32 accumulation; for asymmetric groups the
+ * offset term (beta + 8 s) * sum(x over the group) is formed and added in
+ * fp32. */
 size_t nh_w4_gemm_workspace_bytes(int M, int k_in);
 nh_status nh_w4_gemm(const nh_w4_matrix *W, const uint16_t *X, int M,
                      const void *residual, nh_dtype res_dtype,
