@@ -210,7 +210,10 @@ def test_gemm_identity_probe_is_bit_exact(env, asym, N):
                                         (513, 600, 1024, True),
                                         # even group counts, many columns (the wide-tile kernel on 256
                                         # compute units): ragged rows and columns, four and two groups
-                                        (300, 17000, 256, True), (520, 16500, 128, False)])
+                                        (300, 17000, 256, True), (520, 16500, 128, False),
+                                        # one row on the wide kernel (255 of the tile's rows past the
+                                        # end; 313 split tiles against 157 wide ones)
+                                        (1, 40000, 128, True)])
 def test_gemm_matches_oracle(env, M, n, k, asym):
     nh, oracle, gu, torch = env
     _say("gemm", M, n, k, asym)
