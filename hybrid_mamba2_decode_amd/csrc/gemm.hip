@@ -298,9 +298,39 @@ __global__ __launch_bounds__(WS_THREADS, 1) void k_w4_gemm(W4 W, const uint16_t 
             b0[j] = dequant_word(wr[j].x, s2[j]);
         }
     };
+    // Asymmetric groups: (beta + 8 s) * (group sum of the X row) as a rank-1 fp32 matrix-core
+    // update.  Its MFMA takes K = 2, so it carries two groups: an even step k ends by reading its
+    // group's row sums and offset terms from its slot (su_e, bq_e: registers held only across
+    // the barrier), and step k + 1 starts with the update of both, k = 0 the even group (lanes
+    // 0-31), k = 1 its own (lanes 32-63).  A last even step (odd group count) adds its group
+    // alone, the second k zero.
+    float su_e[4], bq_e[2];
+    auto offset_term = [&](const WsSlotW &sl, int j) __attribute__((always_inline)) {
+        const int c = 64 * wn + 32 * j + l32;
+        return fmaf(8.f, (float)__builtin_bit_cast(half2v, sl.s2[c])[0], sl.bv[c]);  // beta + 8 s
+    };
+    auto asym_update = [&](const float *sus, const WsSlotW &sl, bool pair) __attribute__((always_inline)) {
+        float bq[2];
+        bool asym = false;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            bq[j] = kh ? (pair ? offset_term(sl, j) : 0.f) : bq_e[j];
+            asym = asym || bq[j] != 0.f;
+        }
+        if (__builtin_amdgcn_ballot_w64(asym) != 0ull) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float a = kh ? (pair ? sus[128 * wm + 32 * i + l32] : 0.f) : su_e[i];
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, bq[j], acc[i][j], 0, 0, 0);
+            }
+        }
+    };
     auto step = [&](int k, const uint4 *xs, const float *sus, const WsSlotW &sl, const WsSlotW &sl_next) {
         ws_barrier();
         if (k >= nsteps) return;
+        if (k & 1) asym_update(sus, sl, true);
         if (k == 0) wload(sl);
         // operands of k-step ks + 1 are read and dequantised while the MFMAs of k-step ks run;
         // during the last k-step, the next step's packed W (the register part of its slot is
@@ -344,22 +374,14 @@ __global__ __launch_bounds__(WS_THREADS, 1) void k_w4_gemm(W4 W, const uint16_t 
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        // asymmetric groups: add (beta + 8 s) * (group sum of the X row) as a rank-1 fp32
-        // matrix-core update (K = 2 with the second k zero)
-        float bq[2];
+        // an even step hands its group's row sums and offset terms to the next step (or, as the
+        // last step, adds them alone)
+        if ((k & 1) == 0) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int c = 64 * wn + 32 * j + l32;
-            bq[j] = fmaf(8.f, (float)__builtin_bit_cast(half2v, sl.s2[c])[0], sl.bv[c]);  // beta + 8 s
-        }
-        if (__builtin_amdgcn_ballot_w64(bq[0] != 0.f || bq[1] != 0.f) != 0ull) {
+            for (int i = 0; i < 4; ++i) su_e[i] = sus[128 * wm + 32 * i + l32];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float a = kh ? 0.f : sus[128 * wm + 32 * i + l32];
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, kh ? 0.f : bq[j], acc[i][j], 0, 0, 0);
-            }
+            for (int j = 0; j < 2; ++j) bq_e[j] = offset_term(sl, j);
+            if (k + 1 >= nsteps) asym_update(sus, sl, false);
         }
     };
     for (int k = 0; k < nloop; k += 4) {
@@ -475,20 +497,49 @@ __global__ __launch_bounds__(WG_THREADS, 1) void k_w4_gemm_wide(W4 W, const uint
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+    // Asymmetric groups: (beta + 8 s) * (group sum of the X row) as a rank-1 fp32 matrix-core
+    // update.  Its MFMA takes K = 2, so it carries two groups (the group count is even): an even
+    // step k ends by reading its group's row sums and offset terms from its own slot (su_e,
+    // bq_e: registers held only across the barrier), and step k + 1 starts with the update of
+    // both groups, k = 0 the even one (lanes 0-31), k = 1 its own (lanes 32-63).  The slot of
+    // step k is not read after its barrier: the loads of step k + 3 go into it.
+    float su_e[WI], bq_e[WJ];
+    auto offset_term = [&](const WgSlot &sl, int hi, int j) __attribute__((always_inline)) {
+        const int c = 32 * WJ * wn + 32 * j + l32;
+        const uint32_t spv = sl.sp[c], bpv = sl.bp[c];
+        const float sv = bf16_to_f32((uint16_t)(hi ? spv >> 16 : spv & 0xffffu));
+        const float bv = bf16_to_f32((uint16_t)(hi ? bpv >> 16 : bpv & 0xffffu));
+        return fmaf(8.f, sv, bv);  // beta + 8 s
+    };
+    auto asym_pair = [&](const WgSlot &cu) __attribute__((always_inline)) {
+        float bq[WJ];
+        bool asym = false;
+#pragma unroll
+        for (int j = 0; j < WJ; ++j) {
+            bq[j] = kh ? offset_term(cu, 1, j) : bq_e[j];
+            asym = asym || bq[j] != 0.f;
+        }
+        if (__builtin_amdgcn_ballot_w64(asym) != 0ull) {
+#pragma unroll
+            for (int i = 0; i < WI; ++i) {
+                const float a = kh ? cu.su[32 * WI * wm + 32 * i + l32] : su_e[i];
+#pragma unroll
+                for (int j = 0; j < WJ; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, bq[j], acc[i][j], 0, 0, 0);
+            }
+        }
+    };
     auto step = [&](int k, const WgSlot &sl, WgSlot &fill) __attribute__((always_inline)) {
         uint4 wr[WJ];
         half2v s2[WJ];
-        float bq[WJ];
         const int hi = k & 1;
 #pragma unroll
         for (int j = 0; j < WJ; ++j) {
             const int c = 32 * WJ * wn + 32 * j + l32;
             wr[j] = sl.wq[kh * WG_BN + c];
-            const uint32_t spv = sl.sp[c], bpv = sl.bp[c];
+            const uint32_t spv = sl.sp[c];
             const float sv = bf16_to_f32((uint16_t)(hi ? spv >> 16 : spv & 0xffffu));
-            const float bv = bf16_to_f32((uint16_t)(hi ? bpv >> 16 : bpv & 0xffffu));
             s2[j] = half2v{(_Float16)sv, (_Float16)sv};
-            bq[j] = fmaf(8.f, sv, bv);  // beta + 8 s
         }
         half8 af[2][WI], bf[2][WJ];
         auto rd = [&](int ks, half8 (&a)[WI], half8 (&b)[WJ]) {
@@ -527,19 +578,11 @@ __global__ __launch_bounds__(WG_THREADS, 1) void k_w4_gemm_wide(W4 W, const uint
                 asm volatile("" ::: "memory");
             }
         }
-        // asymmetric groups: add (beta + 8 s) * (group sum of the X row) as a rank-1 fp32
-        // matrix-core update (K = 2 with the second k zero)
-        bool asym = false;
+        if ((k & 1) == 0) {
 #pragma unroll
-        for (int j = 0; j < WJ; ++j) asym = asym || bq[j] != 0.f;
-        if (__builtin_amdgcn_ballot_w64(asym) != 0ull) {
+            for (int i = 0; i < WI; ++i) su_e[i] = sl.su[32 * WI * wm + 32 * i + l32];
 #pragma unroll
-            for (int i = 0; i < WI; ++i) {
-                const float a = kh ? 0.f : sl.su[32 * WI * wm + 32 * i + l32];
-#pragma unroll
-                for (int j = 0; j < WJ; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, kh ? 0.f : bq[j], acc[i][j], 0, 0, 0);
-            }
+            for (int j = 0; j < WJ; ++j) bq_e[j] = offset_term(sl, 0, j);
         }
     };
 
@@ -548,10 +591,12 @@ __global__ __launch_bounds__(WG_THREADS, 1) void k_w4_gemm_wide(W4 W, const uint
     for (int p = 0; p < 3; ++p) dma(p, 0, sa);
     for (int p = 0; p < 3; ++p) dma(p, 1, sb);
     ws_wait_vm<6>();
+    // fill: the slot of step k - 1, which takes the loads of step k + 2
     auto one = [&](int k, const WgSlot &cur, WgSlot &fill) __attribute__((always_inline)) {
         ws_barrier();  // step k: its slot is complete, the slot of step k - 1 is free
-        step(k, cur, fill);  // and the loads of step k + 2 into the slot of step k - 1
-        ws_wait_vm<6>();     // this wave's loads of step k + 1
+        if (k & 1) asym_pair(cur);
+        step(k, cur, fill);
+        ws_wait_vm<6>();  // this wave's loads of step k + 1
     };
     // every step computes: the loop leaves after the last one (the loads of the two steps past
     // the end re-read the last group into slots nobody reads)
