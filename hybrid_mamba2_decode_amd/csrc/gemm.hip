@@ -377,10 +377,17 @@ __global__ __launch_bounds__(WS_THREADS, 1) void k_w4_gemm(W4 W, const uint16_t 
         // an even step hands its group's row sums and offset terms to the next step (or, as the
         // last step, adds them alone)
         if ((k & 1) == 0) {
+            bool asym = false;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) su_e[i] = sus[128 * wm + 32 * i + l32];
+            for (int j = 0; j < 2; ++j) {
+                bq_e[j] = offset_term(sl, j);
+                asym = asym || bq_e[j] != 0.f;
+            }
+            // the row sums only for an asymmetric group (zero otherwise: the pair's update may
+            // still run for the odd group, and multiplies them by a zero offset term)
+            const bool any = __builtin_amdgcn_ballot_w64(asym) != 0ull;
 #pragma unroll
-            for (int j = 0; j < 2; ++j) bq_e[j] = offset_term(sl, j);
+            for (int i = 0; i < 4; ++i) su_e[i] = any ? sus[128 * wm + 32 * i + l32] : 0.f;
             if (k + 1 >= nsteps) asym_update(sus, sl, false);
         }
     };
@@ -502,8 +509,12 @@ __global__ __launch_bounds__(WG_THREADS, 1) void k_w4_gemm_wide(W4 W, const uint
     // step k ends by reading its group's row sums and offset terms from its own slot (su_e,
     // bq_e: registers held only across the barrier), and step k + 1 starts with the update of
     // both groups, k = 0 the even one (lanes 0-31), k = 1 its own (lanes 32-63).  The slot of
-    // step k is not read after its barrier: the loads of step k + 3 go into it.
+    // step k is not read after its barrier: the loads of step k + 3 go into it.  The even
+    // slot's scale and offset pairs also hold the odd group's (high halves), so the even step
+    // decides for both whether the update runs (pair_asym, wave-uniform); for symmetric groups
+    // the odd step does nothing.
     float su_e[WI], bq_e[WJ];
+    bool pair_asym = false;
     auto offset_term = [&](const WgSlot &sl, int hi, int j) __attribute__((always_inline)) {
         const int c = 32 * WJ * wn + 32 * j + l32;
         const uint32_t spv = sl.sp[c], bpv = sl.bp[c];
@@ -513,20 +524,14 @@ __global__ __launch_bounds__(WG_THREADS, 1) void k_w4_gemm_wide(W4 W, const uint
     };
     auto asym_pair = [&](const WgSlot &cu) __attribute__((always_inline)) {
         float bq[WJ];
-        bool asym = false;
 #pragma unroll
-        for (int j = 0; j < WJ; ++j) {
-            bq[j] = kh ? offset_term(cu, 1, j) : bq_e[j];
-            asym = asym || bq[j] != 0.f;
-        }
-        if (__builtin_amdgcn_ballot_w64(asym) != 0ull) {
+        for (int j = 0; j < WJ; ++j) bq[j] = kh ? offset_term(cu, 1, j) : bq_e[j];
 #pragma unroll
-            for (int i = 0; i < WI; ++i) {
-                const float a = kh ? cu.su[32 * WI * wm + 32 * i + l32] : su_e[i];
+        for (int i = 0; i < WI; ++i) {
+            const float a = kh ? cu.su[32 * WI * wm + 32 * i + l32] : su_e[i];
 #pragma unroll
-                for (int j = 0; j < WJ; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, bq[j], acc[i][j], 0, 0, 0);
-            }
+            for (int j = 0; j < WJ; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, bq[j], acc[i][j], 0, 0, 0);
         }
     };
     auto step = [&](int k, const WgSlot &sl, WgSlot &fill) __attribute__((always_inline)) {
@@ -579,10 +584,17 @@ __global__ __launch_bounds__(WG_THREADS, 1) void k_w4_gemm_wide(W4 W, const uint
             }
         }
         if ((k & 1) == 0) {
+            bool asym = false;
 #pragma unroll
-            for (int i = 0; i < WI; ++i) su_e[i] = sl.su[32 * WI * wm + 32 * i + l32];
+            for (int j = 0; j < WJ; ++j) {
+                bq_e[j] = offset_term(sl, 0, j);
+                asym = asym || bq_e[j] != 0.f || offset_term(sl, 1, j) != 0.f;
+            }
+            pair_asym = __builtin_amdgcn_ballot_w64(asym) != 0ull;
+            if (pair_asym) {
 #pragma unroll
-            for (int j = 0; j < WJ; ++j) bq_e[j] = offset_term(sl, 0, j);
+                for (int i = 0; i < WI; ++i) su_e[i] = sl.su[32 * WI * wm + 32 * i + l32];
+            }
         }
     };
 
@@ -594,7 +606,7 @@ __global__ __launch_bounds__(WG_THREADS, 1) void k_w4_gemm_wide(W4 W, const uint
     // fill: the slot of step k - 1, which takes the loads of step k + 2
     auto one = [&](int k, const WgSlot &cur, WgSlot &fill) __attribute__((always_inline)) {
         ws_barrier();  // step k: its slot is complete, the slot of step k - 1 is free
-        if (k & 1) asym_pair(cur);
+        if ((k & 1) && pair_asym) asym_pair(cur);
         step(k, cur, fill);
         ws_wait_vm<6>();  // this wave's loads of step k + 1
     };
